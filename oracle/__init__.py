@@ -1,0 +1,37 @@
+"""CPU oracle for the rotated low-bit quantized linear -- TEST INFRASTRUCTURE.
+
+Only the test suite, the package's smoke entry and the benchmark's CPU
+baseline leg may import this package.  The library (HIP kernels behind the C
+ABI and its Python binding) never imports, links or calls anything here, and
+this package imports nothing from the library: the two share no code.  The
+seeded input generators live in their own module (``workloads``) and hold none
+of the method's arithmetic.
+
+The oracle is plain NumPy: bf16 inputs are widened exactly to float64, the
+rotation is an explicit matrix product with the closed-form 256x256 regular
+Hadamard matrix, the integer contraction is exact, and the epilogues run in
+float64 before one round-to-nearest-even cast to bfloat16.  The quantization
+decision (absmax -> scale -> code) is taken in float32, the precision the
+kernels take it in, from the exactly rotated value rounded once to float32.
+
+Sources (web pages; cited by title and section):
+  [OrbitQuant]  model card "Krea 2 Turbo OrbitQuant W4A4" -- sections
+                "Fused transformer (OrbitQuant 0.11)", "What is quantized",
+                "Latency and VRAM".
+  [INT4-mixed]  model card "Krea-2 Turbo -- INT4 tensorwise W4A4 (+ConvRot,
+                mixed int8 fallback)" -- introduction.
+  [SVDQ-Comfy]  README "Krea-2-SVDQuant-ComfyUI" -- sections "Why this
+                exists", "Low-rank refinement", "LoRA".
+  [NunchakuLite] model card "Krea 2 Turbo Nunchaku Lite INT4 r32" -- intro.
+  [lab]         research log "lab" -- Studies 1-4.
+
+Parity status of each function is pinned by the ``-m "not gpu"`` tests:
+closed forms and Kronecker construction (Hadamard), involution (rotation),
+error bounds and ties (quantizer), documented byte example (packing),
+brute-force integer loops (GEMM), grid-exact end-to-end reconstruction
+(whole linear), the low-rank identity, and textbook SiLU values.  No function
+here is "parity unpinned".
+"""
+
+from .qlinear_ref import *  # noqa: F401,F403
+from .qlinear_ref import __all__  # noqa: F401
