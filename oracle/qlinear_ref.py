@@ -285,18 +285,43 @@ def quantize_weights(w_bits, bits: int, mode: str, rotate_on: bool = True) -> Qu
     return quantize_activations(w_bits, bits, mode, rotate_on)
 
 
+def _scale_col(q: QuantResult) -> np.ndarray:
+    """Per-row scale as a float64 column [R, 1] (tensor or row mode)."""
+    R = q.codes.shape[0]
+    s = np.asarray(q.scales, np.float64).reshape(-1)
+    return (np.full(R, s[0]) if q.mode == "tensor" else s).reshape(R, 1)
+
+
 def linear_fp64(qa: QuantResult, qw: QuantResult, x_bits=None, l1_bits=None, l2_bits=None,
                 bias_bits=None) -> np.ndarray:
-    """Dequantized product y = deq(A) deq(W)^T (+ bias) (+ low-rank branch),
-    float64, before the epilogue.
+    """Dequantized product before the epilogue, float64.
 
-    For tensor / row scales this equals acc * s_a[m] * s_w[n] with acc the
-    exact integer product; for group-64 scales it equals the sum over groups
-    of acc_g * s_a[m, g] * s_w[n, g].  The low-rank branch adds (X L1) L2 with
-    the unrotated bf16 X ([SVDQ-Comfy] "Low-rank refinement": W is split into
-    a quantized part plus a small full-precision product; "LoRA": the branch
-    is applied as a parallel low-rank product, (W + BA)x = Wx + B(Ax))."""
-    y = qa.dequant() @ qw.dequant().T
+    The layer accumulates the codes exactly in integers and only then
+    dequantizes ([OrbitQuant] "Fused transformer": integer GEMMs with the
+    scaling and the rest of the output work in their epilogues), so y is
+    formed from the exact integer product:
+      tensor / row scales:  y = acc * s_a[m] * s_w[n]
+      group-64 scales:      y = sum_g acc_g * (s_a[m, g] * s_w[n, g])
+    which equals deq(A) deq(W)^T mathematically; an exactly-zero accumulator
+    gives an exactly-zero y.  Optional bias[n] is added, and the low-rank
+    branch adds (X L1) L2 with the unrotated bf16 X ([SVDQ-Comfy] "Low-rank
+    refinement": W is split into a quantized part plus a small
+    full-precision product; "LoRA": the branch is applied as a parallel
+    low-rank product, (W + BA)x = Wx + B(Ax))."""
+    if (qa.mode == "group64") != (qw.mode == "group64"):
+        raise ValueError("group-64 scales must be used on both operands")
+    if qa.mode == "group64":
+        K = qa.codes.shape[1]
+        sa = np.asarray(qa.scales, np.float64)
+        sw = np.asarray(qw.scales, np.float64)
+        y = np.zeros((qa.codes.shape[0], qw.codes.shape[0]))
+        for g in range(K // 64):
+            sl = slice(64 * g, 64 * g + 64)
+            acc_g = int_gemm(qa.codes[:, sl], qw.codes[:, sl]).astype(np.float64)
+            y += acc_g * (sa[:, g][:, None] * sw[:, g][None, :])
+    else:
+        acc = int_gemm(qa.codes, qw.codes).astype(np.float64)
+        y = acc * _scale_col(qa) * _scale_col(qw).T
     if bias_bits is not None:
         y = y + bf16_bits_to_f64(bias_bits)[None, :]
     if l1_bits is not None and l2_bits is not None and np.asarray(l1_bits).shape[1] > 0:

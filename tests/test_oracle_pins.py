@@ -235,6 +235,26 @@ def test_dequant_product_matches_scaled_accumulator():
     assert np.allclose(got, want, rtol=1e-14, atol=0)
 
 
+def test_zero_accumulator_gives_exact_zero():
+    # Codes whose integer product is 0 must dequantize to exactly 0, whatever
+    # the scales (the integer sum is exact; scaling happens afterwards).
+    qa = np.zeros((2, 256), np.int8)
+    qw = np.zeros((3, 256), np.int8)
+    qa[0, :4] = [3, -5, 7, 1]
+    qw[0, :4] = [5, 3, 0, 0]                 # 15 - 15 = 0
+    qw[1, :4] = [1, 1, 1, -3]                # 3 - 5 + 7 - 3 = 2
+    for mode, sa, sw in [("row", np.float32([0.1234567, 3.3]), np.float32([0.0771, 1.7, 2.9])),
+                         ("tensor", np.float32([0.1234567]), np.float32([0.0771]))]:
+        a = O.QuantResult(qa, sa, 4, mode, None)
+        w = O.QuantResult(qw, sw, 4, mode, None)
+        y = O.linear_fp64(a, w)
+        assert y[0, 0] == 0.0 and y[0, 2] == 0.0 and y[1].tolist() == [0.0, 0.0, 0.0]
+        assert y[0, 1] == 2 * float(sa[0]) * float(sw[1 if mode == "row" else 0])
+    g = O.QuantResult(qa, np.full((2, 4), 0.3, np.float32), 4, "group64", None)
+    gw = O.QuantResult(qw, np.full((3, 4), 0.7, np.float32), 4, "group64", None)
+    assert O.linear_fp64(g, gw)[0, 0] == 0.0
+
+
 def test_group64_dequant_matches_per_group_loop():
     rng = np.random.default_rng(10)
     x = _bf16_vals(rng, (3, 256))
