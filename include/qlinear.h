@@ -1,0 +1,205 @@
+/*
+ * qlinear.h -- C ABI of the rotated low-bit quantized linear for AMD MI355X
+ * (gfx950).
+ *
+ * The layer (model card "Krea-2 Turbo -- INT4 tensorwise W4A4 (+ConvRot,
+ * mixed int8 fallback)", introduction; model card "Krea 2 Turbo OrbitQuant
+ * W4A4", sections "Fused transformer (OrbitQuant 0.11)" and "What is
+ * quantized"; README "Krea-2-SVDQuant-ComfyUI", section "Why this exists"):
+ *
+ *   1. rotate every aligned 256-channel group of the bf16 activations by the
+ *      orthonormal regular Hadamard matrix H/16 (H = H4 (x) H4 (x) H4 (x) H4,
+ *      H4 = J - 2I), online;
+ *   2. quantize them dynamically to symmetric INT4 or INT8 codes
+ *      (scale = absmax / qmax per tensor, per token or per token x 64
+ *      channels; code = round-half-even(x * qmax / absmax), |code| <= qmax);
+ *   3. multiply the codes with weights that were rotated the same way and
+ *      quantized offline (packed signed INT4, or INT8), accumulating exactly
+ *      in int32;
+ *   4. dequantize (acc * s_a * s_w) and apply an epilogue: plain bf16, SwiGLU
+ *      over a gate|up product, or a gated residual update; optionally add a
+ *      bf16 low-rank branch (X L1) L2 (README "Krea-2-SVDQuant-ComfyUI",
+ *      sections "Low-rank refinement" and "LoRA"; model card "Krea 2 Turbo
+ *      Nunchaku Lite INT4 r32": INT4 with group size 64 and rank 32).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates nothing, frees nothing and keeps no mutable global state.
+ *  - bf16 values travel as uint16_t bit patterns.  Matrices are row-major
+ *    with the row stride given in elements.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *    enqueues work on that stream and returns; it never synchronizes.
+ *    Calls are reentrant; two calls that write the same buffers race unless
+ *    the caller orders them.
+ *  - Arguments are validated before anything is enqueued.  On any error the
+ *    call returns a negative status and has enqueued nothing.  A launch
+ *    failure reported by the runtime right after enqueueing maps to
+ *    QL_ERR_LAUNCH (work already enqueued for that call may then be partial).
+ *    Faults inside kernels surface at the caller's next synchronization.
+ *  - There is no fallback path: on a device other than gfx950 every compute
+ *    entry point returns QL_ERR_UNSUPPORTED.
+ *  - Pointers to code / packed / bf16 matrices must be 16-byte aligned and
+ *    their row strides must keep every row 16-byte aligned.  Scale, bias and
+ *    gate pointers must be 4-byte (float) or 2-byte (bf16) aligned.
+ *  - K must be a positive multiple of 256 (one rotation group) for every
+ *    call; M may be any value >= 0 (M == 0 enqueues nothing); N must be a
+ *    positive multiple of 16.
+ */
+#ifndef QLINEAR_H
+#define QLINEAR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+enum {
+  QL_OK = 0,
+  QL_ERR_NULL = -1,        /* a required pointer is NULL                  */
+  QL_ERR_SHAPE = -2,       /* a size or stride violates a precondition    */
+  QL_ERR_ALIGN = -3,       /* a pointer or stride is misaligned           */
+  QL_ERR_UNSUPPORTED = -4, /* mode combination or device not supported    */
+  QL_ERR_LAUNCH = -5,      /* the HIP runtime rejected a launch           */
+  QL_ERR_DEVICE = -6       /* the current device could not be queried     */
+};
+
+/* ---- quantization scale granularity ------------------------------------ */
+enum {
+  QL_SCALE_TENSOR = 0,  /* one scale for the whole matrix            -> [1]      */
+  QL_SCALE_ROW = 1,     /* one per row (token / output channel)      -> [R]      */
+  QL_SCALE_GROUP64 = 2  /* one per row x aligned 64-channel group    -> [R, K/64] */
+};
+
+/* ---- INT4 code layouts --------------------------------------------------
+ * QL_LAYOUT_I8     : one code per int8 byte, [R, K] (int4 codes -7..7 kept in
+ *                    int8 containers; int8 codes always use this layout).
+ * QL_LAYOUT_PACKED : two signed 4-bit codes per byte, [R, K/2].  Within every
+ *                    run of 8 consecutive channels 8c..8c+7, byte 4c+j
+ *                    (j = 0..3) holds channel 8c+j in its low nibble and
+ *                    channel 8c+j+4 in its high nibble (two's complement).   */
+enum { QL_LAYOUT_I8 = 0, QL_LAYOUT_PACKED = 1 };
+
+/* ---- GEMM epilogues ---------------------------------------------------- */
+enum {
+  QL_EPI_BF16 = 0,           /* out[m,n] = bf16(y)                               */
+  QL_EPI_SWIGLU = 1,         /* out[m,j] = bf16(silu(y[m,j]) * y[m,j+N/2]), j<N/2 */
+  QL_EPI_GATED_RESIDUAL = 2, /* out[m,n] = bf16(res[m,n] + gate[n] * y[m,n])     */
+  QL_EPI_F32 = 3,            /* out[m,n] = y as float32                          */
+  QL_EPI_I32 = 4             /* out[m,n] = exact int32 accumulator (no scales)   */
+};
+/* y[m,n] = sum_k deq(a)[m,k] * deq(w)[n,k] (+ bias[n]) (+ (lr L2)[m,n]),
+ * i.e. acc * s_a * s_w for tensor / row scales, and the sum over 64-channel
+ * groups of acc_g * s_a[m,g] * s_w[n,g] for group-64 scales.  bf16 outputs
+ * are rounded to nearest even. */
+
+/* ---- entry points ------------------------------------------------------ */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* ql_status_string(int status);
+
+/* 1 if `device` is a gfx950 GPU this library was built for, 0 otherwise
+ * (also 0 if the device cannot be queried).  Needs no model or data
+ * (README "Krea-2-SVDQuant-ComfyUI", section "The nodes": an availability
+ * check that needs no model). */
+int ql_device_supported(int device);
+
+/* Online activation prologue (model card "Krea-2 Turbo -- INT4 tensorwise
+ * W4A4 (+ConvRot, mixed int8 fallback)", introduction: activations are
+ * rotated online and quantized dynamically inside the kernel).
+ *
+ *   x      [M, K] bf16, row stride ldx (elements, >= K, multiple of 8)
+ *   bits   4 or 8
+ *   scale_mode  QL_SCALE_TENSOR | QL_SCALE_ROW | QL_SCALE_GROUP64
+ *   layout QL_LAYOUT_I8 or QL_LAYOUT_PACKED (PACKED only with bits == 4)
+ *   rotate 1: rotate each 256-group by H/16 first; 0: quantize x as is
+ *   codes  out: [M, K] int8 or [M, K/2] packed bytes, dense rows
+ *   scales out: float32 [1] | [M] | [M, K/64] (scale = absmax / qmax)
+ *   l1, rank, lr  optional SVDQuant down-projection: if l1 != NULL,
+ *          lr[M, rank] (bf16, dense rows) = bf16(x[M,K] @ l1[K, rank]) with the
+ *          UNROTATED x, l1 bf16 row-major; rank a multiple of 16, 16..128.
+ *          l1 == NULL requires rank == 0.
+ * QL_SCALE_TENSOR uses scales[0] as its grid-wide reduction cell; the library
+ * initializes it on the stream. */
+int rotate_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                        int bits, int scale_mode, int layout, int rotate,
+                        void* codes, float* scales,
+                        const uint16_t* l1, int rank, uint16_t* lr,
+                        void* stream);
+
+/* Offline weight preparation for INT4 (model card "Krea-2 Turbo -- INT4
+ * tensorwise W4A4 (+ConvRot, mixed int8 fallback)", introduction: packed
+ * signed INT4 weights carrying the same group-256 rotation).  Same
+ * arithmetic as rotate_quantize_act(w, N, K, ldw, 4, scale_mode,
+ * QL_LAYOUT_PACKED, rotate, ...).  INT8 per-row weights (model card "Krea 2
+ * Turbo OrbitQuant W4A4", section "What is quantized") are produced by
+ * rotate_quantize_act with bits = 8 and QL_SCALE_ROW.
+ *   w      [N, K] bf16 (torch Linear layout: out x in), row stride ldw
+ *   packed out: [N, K/2] bytes in the QL_LAYOUT_PACKED order
+ *   scales out: float32 [1] | [N] | [N, K/64]                              */
+int pack_weight_int4(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
+                     int scale_mode, int rotate, uint8_t* packed, float* scales,
+                     void* stream);
+
+/* W4A4 GEMM + dequant epilogue (model card "Krea 2 Turbo OrbitQuant W4A4",
+ * section "Fused transformer (OrbitQuant 0.11)": W4A4 GEMMs for attention
+ * and gate/up projections).
+ *   a        [M, K] activation codes in `a_layout`, dense rows
+ *   sa       activation scales per a_scale_mode (TENSOR | ROW)
+ *   w        [N, K/2] packed int4 weight codes, dense rows
+ *   sw       weight scales per w_scale_mode (TENSOR | ROW)
+ *   bias     NULL or bf16 [N]
+ *   epilogue QL_EPI_BF16 | QL_EPI_F32 | QL_EPI_I32 (I32 ignores scales and bias)
+ *   out      [M, N] bf16 / float32 / int32, row stride ldo (elements)
+ * Group-64 scales go through qgemm_w4a4_lowrank (with rank 0). */
+int qgemm_w4a4(const void* a, const float* sa, int a_scale_mode, int a_layout,
+               const uint8_t* w, const float* sw, int w_scale_mode,
+               int64_t M, int64_t N, int64_t K,
+               const uint16_t* bias, int epilogue, void* out, int64_t ldo,
+               void* stream);
+
+/* W8A8 GEMM + dequant epilogue for the protected ff.down projections (model
+ * card "Krea 2 Turbo OrbitQuant W4A4", sections "Fused transformer" and
+ * "What is quantized": per-row INT8 weights with INT8 activations, gated
+ * residual update in the GEMM epilogue).
+ *   a [M, K] int8, w [N, K] int8 (dense rows); sa, sw per their scale modes
+ *   (TENSOR | ROW)
+ *   residual  bf16 [M, N] with row stride ldo; may alias out (in-place
+ *             h += gate * y).  Required for QL_EPI_GATED_RESIDUAL.
+ *   gate      bf16 [N]; required for QL_EPI_GATED_RESIDUAL.
+ *   epilogue  QL_EPI_BF16 | QL_EPI_GATED_RESIDUAL | QL_EPI_F32 | QL_EPI_I32 */
+int qgemm_w8a8(const int8_t* a, const float* sa, int a_scale_mode,
+               const int8_t* w, const float* sw, int w_scale_mode,
+               int64_t M, int64_t N, int64_t K,
+               const uint16_t* bias, const uint16_t* residual, const uint16_t* gate,
+               int epilogue, void* out, int64_t ldo, void* stream);
+
+/* W4A4 GEMM with group-64 (or row / tensor) scales, optional SVDQuant
+ * low-rank branch and SwiGLU epilogue (model card "Krea 2 Turbo Nunchaku
+ * Lite INT4 r32": INT4, group size 64, rank 32; README
+ * "Krea-2-SVDQuant-ComfyUI", section "Why this exists": a low-rank
+ * correction branch on top of the W4A4 kernel; model card "Krea 2 Turbo
+ * OrbitQuant W4A4", section "Fused transformer": SwiGLU gate|up GEMM).
+ *   a, sa, a_scale_mode, a_layout, w, sw, w_scale_mode   as qgemm_w4a4, and
+ *             GROUP64 is allowed only on both sides at once
+ *   lr        bf16 [M, rank] (from rotate_quantize_act), dense rows
+ *   l2        bf16 [rank, N], dense rows
+ *   rank      0 (no branch; lr, l2 may be NULL) or a multiple of 16, <= 128
+ *   epilogue  QL_EPI_BF16 | QL_EPI_SWIGLU | QL_EPI_F32; SWIGLU pairs output
+ *             column j (gate) with column j + N/2 (up), needs N % 32 == 0
+ *             and writes out[M, N/2]
+ *   out       row stride ldo (elements) */
+int qgemm_w4a4_lowrank(const void* a, const float* sa, int a_scale_mode, int a_layout,
+                       const uint8_t* w, const float* sw, int w_scale_mode,
+                       const uint16_t* lr, const uint16_t* l2, int rank,
+                       int64_t M, int64_t N, int64_t K,
+                       const uint16_t* bias, int epilogue, void* out, int64_t ldo,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLINEAR_H */

@@ -1,0 +1,19 @@
+"""Rotated low-bit quantized linear for AMD MI355X (gfx950).
+
+The computation lives in libqlinear.so (hand-written HIP kernels behind the C
+ABI declared in include/qlinear.h); this package is its thin Python binding
+(``_lib``) plus the in-tree build script (``build``) and a small layer helper
+(``linear``).
+"""
+
+from ._lib import (  # noqa: F401
+    QLinearError,
+    device_supported,
+    lib,
+    pack_weight_int4,
+    qgemm_w4a4,
+    qgemm_w4a4_lowrank,
+    qgemm_w8a8,
+    rotate_quantize_act,
+    status_string,
+)

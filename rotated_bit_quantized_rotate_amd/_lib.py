@@ -1,0 +1,211 @@
+"""ctypes binding of libqlinear.so (the C ABI in include/qlinear.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI.  torch is used for device memory (output allocation) and to
+name the current HIP stream.  There is no fallback: if the library is
+missing or the device is not gfx950, calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads torch's HIP runtime first, so the library shares it
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libqlinear.so")
+
+# ---- constants mirrored from include/qlinear.h ------------------------------
+QL_OK = 0
+QL_ERR_NULL = -1
+QL_ERR_SHAPE = -2
+QL_ERR_ALIGN = -3
+QL_ERR_UNSUPPORTED = -4
+QL_ERR_LAUNCH = -5
+QL_ERR_DEVICE = -6
+
+QL_SCALE_TENSOR = 0
+QL_SCALE_ROW = 1
+QL_SCALE_GROUP64 = 2
+QL_LAYOUT_I8 = 0
+QL_LAYOUT_PACKED = 1
+QL_EPI_BF16 = 0
+QL_EPI_SWIGLU = 1
+QL_EPI_GATED_RESIDUAL = 2
+QL_EPI_F32 = 3
+QL_EPI_I32 = 4
+
+SCALE_MODES = {"tensor": QL_SCALE_TENSOR, "row": QL_SCALE_ROW, "group64": QL_SCALE_GROUP64}
+LAYOUTS = {"i8": QL_LAYOUT_I8, "packed": QL_LAYOUT_PACKED}
+EPILOGUES = {"bf16": QL_EPI_BF16, "swiglu": QL_EPI_SWIGLU, "gated_residual": QL_EPI_GATED_RESIDUAL,
+             "f32": QL_EPI_F32, "i32": QL_EPI_I32}
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i = ctypes.c_int
+
+_SIGNATURES = {
+    "ql_status_string": (ctypes.c_char_p, [_i]),
+    "ql_device_supported": (_i, [_i]),
+    "rotate_quantize_act": (_i, [_p, _i64, _i64, _i64, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p]),
+    "pack_weight_int4": (_i, [_p, _i64, _i64, _i64, _i, _i, _p, _p, _p]),
+    "qgemm_w4a4": (_i, [_p, _p, _i, _i, _p, _p, _i, _i64, _i64, _i64, _p, _i, _p, _i64, _p]),
+    "qgemm_w8a8": (_i, [_p, _p, _i, _p, _p, _i, _i64, _i64, _i64, _p, _p, _p, _i, _p, _i64, _p]),
+    "qgemm_w4a4_lowrank": (_i, [_p, _p, _i, _i, _p, _p, _i, _p, _p, _i, _i64, _i64, _i64, _p, _i, _p,
+                                _i64, _p]),
+}
+
+_LIB = None
+
+
+class QLinearError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if libqlinear.so has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m rotated_bit_quantized_rotate_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return lib().ql_status_string(status).decode()
+
+
+def device_supported(device: int = 0) -> bool:
+    return bool(lib().ql_device_supported(device))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn, st):
+    if st != QL_OK:
+        raise QLinearError(fn, st)
+
+
+def _mode(m):
+    return SCALE_MODES[m] if isinstance(m, str) else int(m)
+
+
+def _epi(e):
+    return EPILOGUES[e] if isinstance(e, str) else int(e)
+
+
+def _lay(l):
+    return LAYOUTS[l] if isinstance(l, str) else int(l)
+
+
+def _scale_shape(R, K, mode):
+    return {QL_SCALE_TENSOR: (1,), QL_SCALE_ROW: (R,), QL_SCALE_GROUP64: (R, K // 64)}[mode]
+
+
+# ---- entry points (same names as the C ABI) ---------------------------------
+
+def rotate_quantize_act(x, bits=4, scale_mode="row", layout="i8", rotate=True, codes=None, scales=None,
+                        l1=None, lr=None, stream=None):
+    """x: bf16 [M, K] (row stride x.stride(0)).  Returns (codes, scales, lr)."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    M, K = x.shape
+    mode = _mode(scale_mode)
+    lay = _lay(layout)
+    if codes is None:
+        codes = torch.empty((M, K // 2) if lay == QL_LAYOUT_PACKED else (M, K),
+                            dtype=torch.uint8 if lay == QL_LAYOUT_PACKED else torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty(_scale_shape(M, K, mode), dtype=torch.float32, device=x.device)
+    rank = 0
+    if l1 is not None:
+        rank = l1.shape[1]
+        if lr is None:
+            lr = torch.empty((M, rank), dtype=torch.bfloat16, device=x.device)
+    st = lib().rotate_quantize_act(_ptr(x), M, K, x.stride(0), bits, mode, lay, int(bool(rotate)),
+                                   _ptr(codes), _ptr(scales), _ptr(l1), rank, _ptr(lr), _stream(stream))
+    _check("rotate_quantize_act", st)
+    return codes, scales, lr
+
+
+def pack_weight_int4(w, scale_mode="row", rotate=True, packed=None, scales=None, stream=None):
+    """w: bf16 [N, K].  Returns (packed uint8 [N, K/2], scales)."""
+    assert w.dtype == torch.bfloat16 and w.dim() == 2 and w.stride(1) == 1
+    N, K = w.shape
+    mode = _mode(scale_mode)
+    if packed is None:
+        packed = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty(_scale_shape(N, K, mode), dtype=torch.float32, device=w.device)
+    st = lib().pack_weight_int4(_ptr(w), N, K, w.stride(0), mode, int(bool(rotate)), _ptr(packed),
+                                _ptr(scales), _stream(stream))
+    _check("pack_weight_int4", st)
+    return packed, scales
+
+
+def _out(out, M, cols, epi, device):
+    if out is not None:
+        return out
+    dt = {QL_EPI_F32: torch.float32, QL_EPI_I32: torch.int32}.get(epi, torch.bfloat16)
+    return torch.empty((M, cols), dtype=dt, device=device)
+
+
+def qgemm_w4a4(a, sa, w, sw, K, a_scale_mode="row", w_scale_mode="row", a_layout="i8", bias=None,
+               epilogue="bf16", out=None, stream=None):
+    """a: codes [M, K] int8 or [M, K/2] packed; w: packed [N, K/2]."""
+    M = a.shape[0]
+    N = w.shape[0]
+    epi = _epi(epilogue)
+    out = _out(out, M, N // 2 if epi == QL_EPI_SWIGLU else N, epi, a.device)
+    st = lib().qgemm_w4a4(_ptr(a), _ptr(sa), _mode(a_scale_mode), _lay(a_layout), _ptr(w), _ptr(sw),
+                          _mode(w_scale_mode), M, N, K, _ptr(bias), epi, _ptr(out), out.stride(0),
+                          _stream(stream))
+    _check("qgemm_w4a4", st)
+    return out
+
+
+def qgemm_w8a8(a, sa, w, sw, a_scale_mode="row", w_scale_mode="row", bias=None, residual=None, gate=None,
+               epilogue="bf16", out=None, stream=None):
+    """a: int8 [M, K]; w: int8 [N, K].  residual may be `out` itself."""
+    M, K = a.shape
+    N = w.shape[0]
+    epi = _epi(epilogue)
+    out = _out(out, M, N, epi, a.device)
+    st = lib().qgemm_w8a8(_ptr(a), _ptr(sa), _mode(a_scale_mode), _ptr(w), _ptr(sw), _mode(w_scale_mode),
+                          M, N, K, _ptr(bias), _ptr(residual), _ptr(gate), epi, _ptr(out), out.stride(0),
+                          _stream(stream))
+    _check("qgemm_w8a8", st)
+    return out
+
+
+def qgemm_w4a4_lowrank(a, sa, w, sw, K, lr=None, l2=None, a_scale_mode="group64",
+                       w_scale_mode="group64", a_layout="i8", bias=None, epilogue="swiglu", out=None,
+                       stream=None):
+    """Group-64 (or row) W4A4 GEMM + optional low-rank branch lr @ l2 + epilogue."""
+    M = a.shape[0]
+    N = w.shape[0]
+    epi = _epi(epilogue)
+    rank = 0 if l2 is None else l2.shape[0]
+    out = _out(out, M, N // 2 if epi == QL_EPI_SWIGLU else N, epi, a.device)
+    st = lib().qgemm_w4a4_lowrank(_ptr(a), _ptr(sa), _mode(a_scale_mode), _lay(a_layout), _ptr(w),
+                                  _ptr(sw), _mode(w_scale_mode), _ptr(lr), _ptr(l2), rank, M, N, K,
+                                  _ptr(bias), epi, _ptr(out), out.stride(0), _stream(stream))
+    _check("qgemm_w4a4_lowrank", st)
+    return out

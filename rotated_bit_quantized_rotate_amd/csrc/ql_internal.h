@@ -1,0 +1,87 @@
+// Internal declarations shared by the HIP translation units of libqlinear.
+// Not part of the public ABI (see include/qlinear.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ql {
+
+// ---------------------------------------------------------------- types ----
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// -------------------------------------------------------- bf16 helpers -----
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// float -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ------------------------------------------------------------ DPP -----------
+// Cross-lane reads within 16-lane rows.  CTRL values follow the GFX9 DPP
+// encoding: quad_perm = p0 | p1<<2 | p2<<4 | p3<<6, row_ror:n = 0x120 + n.
+enum : int {
+  DPP_QUAD_SWAP1 = 0xB1,  // quad_perm [1,0,3,2]
+  DPP_QUAD_SWAP2 = 0x4E,  // quad_perm [2,3,0,1]
+  DPP_ROR4 = 0x124,
+  DPP_ROR8 = 0x128,
+  DPP_ROR2 = 0x122,
+  DPP_ROR1 = 0x121,
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// ------------------------------------------------------- launch plumbing ---
+// Status codes mirror include/qlinear.h.
+enum { OK = 0, ERR_LAUNCH = -5 };
+
+struct RqArgs {
+  const uint16_t* x;
+  int64_t M;
+  int64_t K;
+  int64_t ldx;
+  int bits;        // 4 | 8
+  int mode;        // 0 tensor, 1 row, 2 group64
+  int packed;      // 1: two int4 codes per byte
+  int rotate;      // 1: apply H per 256-group
+  void* codes;
+  float* scales;
+};
+
+int launch_rotate_quantize(const RqArgs& a, hipStream_t s);
+int launch_lowrank_down(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                        const uint16_t* l1, int rank, uint16_t* lr, hipStream_t s);
+
+struct GemmArgs {
+  const void* a;        // activation codes (int8 [M,K] or packed [M,K/2])
+  const void* w;        // weight codes (int8 [N,K] or packed [N,K/2])
+  const float* sa;
+  const float* sw;
+  int64_t M, N, K;
+  int a_packed, w_packed;
+  int a_mode, w_mode;   // 0 tensor, 1 row, 2 group64
+  const uint16_t* bias;
+  const uint16_t* residual;
+  const uint16_t* gate;
+  const uint16_t* lr;   // [M, rank]
+  const uint16_t* l2;   // [rank, N]
+  int rank;
+  int epilogue;         // QL_EPI_*
+  void* out;
+  int64_t ldo;
+};
+
+int launch_qgemm(const GemmArgs& g, hipStream_t s);
+
+}  // namespace ql

@@ -1,0 +1,238 @@
+// C ABI of libqlinear: argument validation, device check and dispatch to the
+// HIP kernels.  Every precondition listed in include/qlinear.h is checked
+// here before anything is enqueued; nothing is allocated, nothing is
+// synchronized.
+
+#include <string.h>
+
+#include "../../include/qlinear.h"
+#include "ql_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// Per-device cache of "is gfx950": 0 unknown, 1 yes, 2 no.  Written only with
+// the value the runtime reports, so concurrent first calls agree.
+int g_dev_ok[kMaxDevices];
+
+int device_is_gfx950(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return 0;
+  const int c = __atomic_load_n(&g_dev_ok[dev], __ATOMIC_RELAXED);
+  if (c) return c == 1;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+  const int ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  __atomic_store_n(&g_dev_ok[dev], ok ? 1 : 2, __ATOMIC_RELAXED);
+  return ok;
+}
+
+int check_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return QL_ERR_DEVICE;
+  return device_is_gfx950(dev) ? QL_OK : QL_ERR_UNSUPPORTED;
+}
+
+inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+inline bool al2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
+
+inline bool valid_mode(int m) { return m == QL_SCALE_TENSOR || m == QL_SCALE_ROW || m == QL_SCALE_GROUP64; }
+
+}  // namespace
+
+extern "C" {
+
+const char* ql_status_string(int status) {
+  switch (status) {
+    case QL_OK: return "QL_OK: success";
+    case QL_ERR_NULL: return "QL_ERR_NULL: a required pointer is NULL";
+    case QL_ERR_SHAPE: return "QL_ERR_SHAPE: a size or stride violates a precondition";
+    case QL_ERR_ALIGN: return "QL_ERR_ALIGN: a pointer or stride is misaligned";
+    case QL_ERR_UNSUPPORTED: return "QL_ERR_UNSUPPORTED: mode combination or device not supported";
+    case QL_ERR_LAUNCH: return "QL_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+    case QL_ERR_DEVICE: return "QL_ERR_DEVICE: the current device could not be queried";
+    default: return "unknown qlinear status";
+  }
+}
+
+int ql_device_supported(int device) { return device_is_gfx950(device); }
+
+static int validate_rq(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int bits, int scale_mode,
+                       int layout, int rotate, const void* codes, const float* scales,
+                       const uint16_t* l1, int rank, const uint16_t* lr) {
+  if (bits != 4 && bits != 8) return QL_ERR_UNSUPPORTED;
+  if (!valid_mode(scale_mode)) return QL_ERR_UNSUPPORTED;
+  if (layout != QL_LAYOUT_I8 && layout != QL_LAYOUT_PACKED) return QL_ERR_UNSUPPORTED;
+  if (layout == QL_LAYOUT_PACKED && bits != 4) return QL_ERR_UNSUPPORTED;
+  if (rotate != 0 && rotate != 1) return QL_ERR_UNSUPPORTED;
+  if (M < 0 || K <= 0 || K % 256 != 0 || K > 32768) return QL_ERR_SHAPE;
+  if (ldx < K || ldx % 8 != 0) return QL_ERR_SHAPE;
+  if (M > 0 && (!x || !codes || !scales)) return QL_ERR_NULL;
+  if (!l1 && rank != 0) return QL_ERR_SHAPE;
+  if (l1) {
+    if (rank < 16 || rank > 128 || rank % 16 != 0) return QL_ERR_SHAPE;
+    if (M > 0 && !lr) return QL_ERR_NULL;
+    if (!al16(l1) || !al16(lr)) return QL_ERR_ALIGN;
+  }
+  if (!al16(x) || !al16(codes) || !al4(scales)) return QL_ERR_ALIGN;
+  return QL_OK;
+}
+
+int rotate_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int bits, int scale_mode,
+                        int layout, int rotate, void* codes, float* scales, const uint16_t* l1,
+                        int rank, uint16_t* lr, void* stream) {
+  int st = validate_rq(x, M, K, ldx, bits, scale_mode, layout, rotate, codes, scales, l1, rank, lr);
+  if (st != QL_OK) return st;
+  if ((st = check_current_device()) != QL_OK) return st;
+  if (M == 0) return QL_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ql::RqArgs a{x, M, K, ldx, bits, scale_mode, layout == QL_LAYOUT_PACKED ? 1 : 0, rotate, codes, scales};
+  st = ql::launch_rotate_quantize(a, s);
+  if (st != QL_OK) return QL_ERR_LAUNCH;
+  if (l1) {
+    st = ql::launch_lowrank_down(x, M, K, ldx, l1, rank, lr, s);
+    if (st != QL_OK) return QL_ERR_LAUNCH;
+  }
+  return QL_OK;
+}
+
+int pack_weight_int4(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, int scale_mode, int rotate,
+                     uint8_t* packed, float* scales, void* stream) {
+  if (N <= 0) return QL_ERR_SHAPE;
+  return rotate_quantize_act(w, N, K, ldw, 4, scale_mode, QL_LAYOUT_PACKED, rotate, packed, scales,
+                             nullptr, 0, nullptr, stream);
+}
+
+// Output element size per epilogue (SWIGLU / BF16 / GATED write bf16).
+inline int64_t out_elem_size(int epilogue) {
+  return (epilogue == QL_EPI_F32 || epilogue == QL_EPI_I32) ? 4 : 2;
+}
+
+static int validate_gemm_common(const void* a, const float* sa, const void* w, const float* sw,
+                                int64_t M, int64_t N, int64_t K, const uint16_t* bias, void* out,
+                                int64_t ldo, int epilogue) {
+  if (M < 0 || N <= 0 || N % 16 != 0 || K <= 0 || K % 256 != 0) return QL_ERR_SHAPE;
+  const int64_t out_cols = epilogue == QL_EPI_SWIGLU ? N / 2 : N;
+  if (ldo < out_cols) return QL_ERR_SHAPE;
+  if (M > 0 && (!a || !sa || !w || !sw || !out)) return QL_ERR_NULL;
+  if (!al16(a) || !al16(w) || !al4(sa) || !al4(sw) || !al16(out)) return QL_ERR_ALIGN;
+  if ((ldo * out_elem_size(epilogue)) % 16 != 0) return QL_ERR_ALIGN;
+  if (bias && !al2(bias)) return QL_ERR_ALIGN;
+  return QL_OK;
+}
+
+int qgemm_w4a4(const void* a, const float* sa, int a_scale_mode, int a_layout, const uint8_t* w,
+               const float* sw, int w_scale_mode, int64_t M, int64_t N, int64_t K, const uint16_t* bias,
+               int epilogue, void* out, int64_t ldo, void* stream) {
+  if (a_scale_mode == QL_SCALE_GROUP64 || w_scale_mode == QL_SCALE_GROUP64) {
+    if (a_scale_mode != QL_SCALE_GROUP64 || w_scale_mode != QL_SCALE_GROUP64) return QL_ERR_UNSUPPORTED;
+    if (epilogue == QL_EPI_I32) return QL_ERR_UNSUPPORTED;
+    return qgemm_w4a4_lowrank(a, sa, a_scale_mode, a_layout, w, sw, w_scale_mode, nullptr, nullptr, 0, M,
+                              N, K, bias, epilogue, out, ldo, stream);
+  }
+  if (!valid_mode(a_scale_mode) || !valid_mode(w_scale_mode)) return QL_ERR_UNSUPPORTED;
+  if (a_layout != QL_LAYOUT_I8 && a_layout != QL_LAYOUT_PACKED) return QL_ERR_UNSUPPORTED;
+  if (epilogue != QL_EPI_BF16 && epilogue != QL_EPI_F32 && epilogue != QL_EPI_I32) return QL_ERR_UNSUPPORTED;
+  int st = validate_gemm_common(a, sa, w, sw, M, N, K, bias, out, ldo, epilogue);
+  if (st != QL_OK) return st;
+  if ((st = check_current_device()) != QL_OK) return st;
+  if (M == 0) return QL_OK;
+  ql::GemmArgs g{};
+  g.a = a;
+  g.w = w;
+  g.sa = sa;
+  g.sw = sw;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.a_packed = a_layout == QL_LAYOUT_PACKED;
+  g.w_packed = 1;
+  g.a_mode = a_scale_mode;
+  g.w_mode = w_scale_mode;
+  g.bias = bias;
+  g.epilogue = epilogue;
+  g.out = out;
+  g.ldo = ldo;
+  return ql::launch_qgemm(g, static_cast<hipStream_t>(stream)) == QL_OK ? QL_OK : QL_ERR_LAUNCH;
+}
+
+int qgemm_w8a8(const int8_t* a, const float* sa, int a_scale_mode, const int8_t* w, const float* sw,
+               int w_scale_mode, int64_t M, int64_t N, int64_t K, const uint16_t* bias,
+               const uint16_t* residual, const uint16_t* gate, int epilogue, void* out, int64_t ldo,
+               void* stream) {
+  if ((a_scale_mode != QL_SCALE_TENSOR && a_scale_mode != QL_SCALE_ROW) ||
+      (w_scale_mode != QL_SCALE_TENSOR && w_scale_mode != QL_SCALE_ROW))
+    return QL_ERR_UNSUPPORTED;
+  if (epilogue != QL_EPI_BF16 && epilogue != QL_EPI_GATED_RESIDUAL && epilogue != QL_EPI_F32 &&
+      epilogue != QL_EPI_I32)
+    return QL_ERR_UNSUPPORTED;
+  int st = validate_gemm_common(a, sa, w, sw, M, N, K, bias, out, ldo, epilogue);
+  if (st != QL_OK) return st;
+  if (epilogue == QL_EPI_GATED_RESIDUAL) {
+    if (M > 0 && (!residual || !gate)) return QL_ERR_NULL;
+    if (!al16(residual) || !al2(gate)) return QL_ERR_ALIGN;
+  }
+  if ((st = check_current_device()) != QL_OK) return st;
+  if (M == 0) return QL_OK;
+  ql::GemmArgs g{};
+  g.a = a;
+  g.w = w;
+  g.sa = sa;
+  g.sw = sw;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.a_packed = 0;
+  g.w_packed = 0;
+  g.a_mode = a_scale_mode;
+  g.w_mode = w_scale_mode;
+  g.bias = bias;
+  g.residual = residual;
+  g.gate = gate;
+  g.epilogue = epilogue;
+  g.out = out;
+  g.ldo = ldo;
+  return ql::launch_qgemm(g, static_cast<hipStream_t>(stream)) == QL_OK ? QL_OK : QL_ERR_LAUNCH;
+}
+
+int qgemm_w4a4_lowrank(const void* a, const float* sa, int a_scale_mode, int a_layout, const uint8_t* w,
+                       const float* sw, int w_scale_mode, const uint16_t* lr, const uint16_t* l2, int rank,
+                       int64_t M, int64_t N, int64_t K, const uint16_t* bias, int epilogue, void* out,
+                       int64_t ldo, void* stream) {
+  if (!valid_mode(a_scale_mode) || !valid_mode(w_scale_mode)) return QL_ERR_UNSUPPORTED;
+  if ((a_scale_mode == QL_SCALE_GROUP64) != (w_scale_mode == QL_SCALE_GROUP64)) return QL_ERR_UNSUPPORTED;
+  if (a_layout != QL_LAYOUT_I8 && a_layout != QL_LAYOUT_PACKED) return QL_ERR_UNSUPPORTED;
+  if (epilogue != QL_EPI_BF16 && epilogue != QL_EPI_SWIGLU && epilogue != QL_EPI_F32) return QL_ERR_UNSUPPORTED;
+  if (epilogue == QL_EPI_SWIGLU && N % 32 != 0) return QL_ERR_SHAPE;
+  int st = validate_gemm_common(a, sa, w, sw, M, N, K, bias, out, ldo, epilogue);
+  if (st != QL_OK) return st;
+  if (rank < 0 || rank > 128 || rank % 16 != 0) return QL_ERR_SHAPE;
+  if (rank > 0) {
+    if (M > 0 && (!lr || !l2)) return QL_ERR_NULL;
+    if (!al16(lr) || !al2(l2)) return QL_ERR_ALIGN;
+  }
+  if ((st = check_current_device()) != QL_OK) return st;
+  if (M == 0) return QL_OK;
+  ql::GemmArgs g{};
+  g.a = a;
+  g.w = w;
+  g.sa = sa;
+  g.sw = sw;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.a_packed = a_layout == QL_LAYOUT_PACKED;
+  g.w_packed = 1;
+  g.a_mode = a_scale_mode;
+  g.w_mode = w_scale_mode;
+  g.bias = bias;
+  g.lr = lr;
+  g.l2 = l2;
+  g.rank = rank;
+  g.epilogue = epilogue;
+  g.out = out;
+  g.ldo = ldo;
+  return ql::launch_qgemm(g, static_cast<hipStream_t>(stream)) == QL_OK ? QL_OK : QL_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,361 @@
+// Online rotation + dynamic symmetric quantization (activations), offline
+// weight packing, and the SVDQuant low-rank down-projection, for gfx950.
+//
+// Method (model card "Krea-2 Turbo -- INT4 tensorwise W4A4 (+ConvRot, mixed
+// int8 fallback)", introduction): each aligned 256-channel group is rotated
+// by a regular Hadamard matrix and the result is quantized to signed INT4 or
+// INT8 with a scale computed at run time from the absolute maximum.
+//
+// Rotation.  H = H4 (x) H4 (x) H4 (x) H4 with H4 = J - 2I acts on the four
+// base-4 digits of the in-group channel index i = 64*d3 + 16*d2 + 4*d1 + d0.
+// Applying H4 along one digit is the butterfly y = (sum of the 4 values that
+// differ only in that digit) - 2*x.  A 16-lane DPP row owns one group; lane
+// t holds the 16 consecutive channels i = 16*t + e.  Digits d0, d1 come from
+// e and are transformed in registers; digits d2 = t % 4 and d3 = t / 4 come
+// from the lane and are transformed with DPP quad permutes and 16-lane row
+// rotations.  The kernel forms z = H x (no 1/16): the codes do not depend on
+// a power-of-two factor, and the 1/16 is folded into the stored scale
+// exactly.
+//
+// Quantization (per tensor, per row, or per row x 64-channel group):
+//   amax = max |z| over the unit,  inv = qmax / amax (correctly rounded fp32),
+//   code = clamp(rint(z * inv), -qmax, qmax),  scale = amax / qmax (/16 if rotated).
+// A 64-channel group inside a 256-group is one value of d3, i.e. one quad of
+// lanes.
+
+#include "ql_internal.h"
+
+namespace ql {
+namespace {
+
+constexpr int kThreads = 256;  // 16 slots of 16 lanes
+
+// H applied to one 256-group held as 16 floats per lane across a 16-lane row.
+__device__ __forceinline__ void hadamard256(float (&v)[16]) {
+  // digit d0: e % 4
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float s = (v[4 * q] + v[4 * q + 1]) + (v[4 * q + 2] + v[4 * q + 3]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[4 * q + i] = __builtin_fmaf(-2.0f, v[4 * q + i], s);
+  }
+  // digit d1: e / 4
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float s = (v[c] + v[c + 4]) + (v[c + 8] + v[c + 12]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[c + 4 * i] = __builtin_fmaf(-2.0f, v[c + 4 * i], s);
+  }
+  // digit d2: lane bits 0-1 (the 4 lanes of a quad)
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float s1 = v[e] + dpp_f<DPP_QUAD_SWAP1>(v[e]);
+    const float s = s1 + dpp_f<DPP_QUAD_SWAP2>(s1);
+    v[e] = __builtin_fmaf(-2.0f, v[e], s);
+  }
+  // digit d3: lane bits 2-3 (lanes t, t+4, t+8, t+12 of the 16-lane row)
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float s1 = v[e] + dpp_f<DPP_ROR8>(v[e]);
+    const float s = s1 + dpp_f<DPP_ROR4>(s1);
+    v[e] = __builtin_fmaf(-2.0f, v[e], s);
+  }
+}
+
+__device__ __forceinline__ float row16_max(float m) {
+  m = fmaxf(m, dpp_f<DPP_ROR8>(m));
+  m = fmaxf(m, dpp_f<DPP_ROR4>(m));
+  m = fmaxf(m, dpp_f<DPP_ROR2>(m));
+  m = fmaxf(m, dpp_f<DPP_ROR1>(m));
+  return m;
+}
+
+__device__ __forceinline__ float quad_max(float m) {
+  m = fmaxf(m, dpp_f<DPP_QUAD_SWAP1>(m));
+  m = fmaxf(m, dpp_f<DPP_QUAD_SWAP2>(m));
+  return m;
+}
+
+// Encode 16 codes (channel order) and store them.
+__device__ __forceinline__ void store_codes(void* codes, int64_t off_elems, bool packed,
+                                            const int (&q)[16]) {
+  if (!packed) {
+    uint4 w;
+    uint32_t* wp = reinterpret_cast<uint32_t*>(&w);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      wp[k] = (uint32_t)(q[4 * k] & 0xff) | ((uint32_t)(q[4 * k + 1] & 0xff) << 8) |
+              ((uint32_t)(q[4 * k + 2] & 0xff) << 16) | ((uint32_t)(q[4 * k + 3] & 0xff) << 24);
+    *reinterpret_cast<uint4*>(static_cast<int8_t*>(codes) + off_elems) = w;
+  } else {
+    // byte 4c+j: low nibble channel 8c+j, high nibble channel 8c+j+4
+    uint2 w;
+    uint32_t* wp = reinterpret_cast<uint32_t*>(&w);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t b = (uint32_t)(q[8 * c + j] & 0xf) | ((uint32_t)(q[8 * c + j + 4] & 0xf) << 4);
+        word |= b << (8 * j);
+      }
+      wp[c] = word;
+    }
+    *reinterpret_cast<uint2*>(static_cast<uint8_t*>(codes) + off_elems / 2) = w;
+  }
+}
+
+// phase 0: quantize (row / group64, or tensor mode reading the absmax cell)
+// phase 1: tensor mode, absmax only (atomicMax into the cell)
+template <int GPL>
+__global__ __launch_bounds__(kThreads) void rq_kernel(RqArgs a, int slots_per_row,
+                                                      int rows_per_wg, int phase) {
+  __shared__ float red[16];
+  const int tid = threadIdx.x;
+  const int slot = tid >> 4;
+  const int t = tid & 15;
+  const int row_in_wg = slot / slots_per_row;
+  const int sir = slot - row_in_wg * slots_per_row;
+  const int64_t row = (int64_t)blockIdx.x * rows_per_wg + row_in_wg;
+  const int ngroups = (int)(a.K >> 8);
+  const bool row_ok = (row_in_wg < rows_per_wg) && (row < a.M);
+
+  float v[GPL][16];
+#pragma unroll
+  for (int j = 0; j < GPL; ++j) {
+    const int g = sir + j * slots_per_row;
+    if (row_ok && g < ngroups) {
+      const uint4* p = reinterpret_cast<const uint4*>(a.x + row * a.ldx + (int64_t)g * 256 + t * 16);
+      const uint4 u0 = p[0];
+      const uint4 u1 = p[1];
+      const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        v[j][2 * k] = __uint_as_float(w[k] << 16);
+        v[j][2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[j][e] = 0.0f;
+    }
+  }
+
+  if (a.rotate) {
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) hadamard256(v[j]);
+  }
+
+  const float qmax = a.bits == 4 ? 7.0f : 127.0f;
+  const float post = a.rotate ? 0.0625f : 1.0f;  // z = 16 x' when rotated
+
+  // per-unit absmax
+  float amax[GPL];
+  if (a.mode == 2) {  // group64: one quad of lanes per 64-channel group
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) {
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[j][e]));
+      amax[j] = quad_max(m);
+    }
+  } else {  // row or tensor: reduce over the row's slots
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < GPL; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[j][e]));
+    m = row16_max(m);
+    if (t == 0) red[slot] = m;
+    __syncthreads();
+    if (phase == 1) {
+      if (tid == 0) {
+        float wm = 0.0f;
+        for (int s = 0; s < 16; ++s) wm = fmaxf(wm, red[s]);
+        atomicMax(reinterpret_cast<unsigned int*>(a.scales), __float_as_uint(wm));
+      }
+      return;
+    }
+    float rm;
+    if (a.mode == 0) {
+      rm = __uint_as_float(*reinterpret_cast<const volatile unsigned int*>(a.scales));
+    } else {
+      rm = 0.0f;
+      const int s0 = row_in_wg * slots_per_row;
+      for (int s = 0; s < slots_per_row; ++s) rm = fmaxf(rm, red[(s0 + s) & 15]);
+    }
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) amax[j] = rm;
+  }
+
+  if (!row_ok) return;
+
+  const int64_t code_row = row * a.K;
+#pragma unroll
+  for (int j = 0; j < GPL; ++j) {
+    const int g = sir + j * slots_per_row;
+    if (g >= ngroups) continue;
+    const float am = amax[j];
+    const float inv = am > 0.0f ? __fdiv_rn(qmax, am) : 0.0f;
+    int q[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float r = __builtin_rintf(v[j][e] * inv);
+      r = fminf(fmaxf(r, -qmax), qmax);
+      q[e] = (int)r;
+    }
+    store_codes(a.codes, code_row + (int64_t)g * 256 + t * 16, a.packed != 0, q);
+    if (a.mode == 2) {
+      if ((t & 3) == 0)
+        a.scales[row * (a.K >> 6) + g * 4 + (t >> 2)] = __fdiv_rn(am, qmax) * post;
+    } else if (a.mode == 1 && t == 0 && sir == 0 && j == 0) {
+      a.scales[row] = __fdiv_rn(am, qmax) * post;
+    }
+  }
+}
+
+__global__ void cell_clear_kernel(float* cell) { *reinterpret_cast<unsigned int*>(cell) = 0u; }
+
+__global__ void cell_finalize_kernel(float* cell, float qmax, float post) {
+  const float am = *cell;
+  *cell = __fdiv_rn(am, qmax) * post;
+}
+
+struct Plan {
+  int gpl, slots, rows;
+};
+
+Plan plan_rows(int ngroups) {
+  static const int cand[] = {1, 2, 3, 4, 5, 6, 8};
+  Plan best{0, 0, 0};
+  double best_eff = -1.0;
+  for (int g : cand) {
+    const int s = (ngroups + g - 1) / g;
+    if (s > 16) continue;
+    const int rows = 16 / s;
+    const double eff = (double)(rows * s) / 16.0 * (double)ngroups / (double)(s * g);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = Plan{g, s, rows};
+    }
+  }
+  return best;
+}
+
+template <int GPL>
+hipError_t launch_rq(const RqArgs& a, const Plan& p, int phase, hipStream_t s) {
+  const unsigned blocks = (unsigned)((a.M + p.rows - 1) / p.rows);
+  hipLaunchKernelGGL(rq_kernel<GPL>, dim3(blocks), dim3(kThreads), 0, s, a, p.slots, p.rows, phase);
+  return hipGetLastError();
+}
+
+hipError_t dispatch_rq(const RqArgs& a, const Plan& p, int phase, hipStream_t s) {
+  switch (p.gpl) {
+    case 1: return launch_rq<1>(a, p, phase, s);
+    case 2: return launch_rq<2>(a, p, phase, s);
+    case 3: return launch_rq<3>(a, p, phase, s);
+    case 4: return launch_rq<4>(a, p, phase, s);
+    case 5: return launch_rq<5>(a, p, phase, s);
+    case 6: return launch_rq<6>(a, p, phase, s);
+    case 8: return launch_rq<8>(a, p, phase, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// SVDQuant down-projection lr = bf16(X @ L1) with the unrotated bf16 X
+// (README "Krea-2-SVDQuant-ComfyUI", section "Low-rank refinement": the
+// branch is a small full-precision product next to the quantized weight).
+// bf16 MFMA 16x16x32, fp32 accumulation.  64 rows per workgroup, one wave per
+// 16 rows; L1 is staged through LDS transposed ([rank][k]) in 128-deep chunks.
+// ---------------------------------------------------------------------------
+constexpr int kLrKC = 128;
+constexpr int kLrPitch = kLrKC + 8;  // bf16 elements per transposed L1 row
+
+__global__ __launch_bounds__(256) void lowrank_down_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                           int64_t K, int64_t ldx,
+                                                           const uint16_t* __restrict__ l1, int rank,
+                                                           uint16_t* __restrict__ lr) {
+  __shared__ __attribute__((aligned(16))) uint16_t l1t[128 * kLrPitch];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int nb = rank >> 4;
+  const int64_t m0 = (int64_t)blockIdx.x * 64 + wave * 16;
+  int64_t arow = m0 + (lane & 15);
+  if (arow > M - 1) arow = M - 1;
+  const uint16_t* xrow = x + arow * ldx + (lane >> 4) * 8;
+
+  v4f acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t k0 = 0; k0 < K; k0 += kLrKC) {
+    __syncthreads();
+    // stage L1[k0 : k0+128, 0:rank] transposed into l1t[n][k]
+    const int chunks = kLrKC * (rank >> 3);
+    for (int c = tid; c < chunks; c += 256) {
+      const int kr = c / (rank >> 3);
+      const int n8 = (c - kr * (rank >> 3)) * 8;
+      const uint4 u = *reinterpret_cast<const uint4*>(l1 + (k0 + kr) * rank + n8);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        l1t[(n8 + 2 * e) * kLrPitch + kr] = (uint16_t)(w[e] & 0xffff);
+        l1t[(n8 + 2 * e + 1) * kLrPitch + kr] = (uint16_t)(w[e] >> 16);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kLrKC; kk += 32) {
+      const v8bf af = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(xrow + k0 + kk));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j < nb) {
+          const v8bf bfr = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(
+              &l1t[(j * 16 + (lane & 15)) * kLrPitch + kk + (lane >> 4) * 8]));
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, acc[j], 0, 0, 0);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= nb) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t m = m0 + (lane >> 4) * 4 + r;
+      if (m < M) lr[m * rank + j * 16 + (lane & 15)] = (uint16_t)f32_to_bf16(acc[j][r]);
+    }
+  }
+}
+
+}  // namespace
+
+int launch_rotate_quantize(const RqArgs& a, hipStream_t s) {
+  if (a.M == 0) return OK;
+  const Plan p = plan_rows((int)(a.K >> 8));
+  if (p.gpl == 0) return ERR_LAUNCH;
+  const float qmax = a.bits == 4 ? 7.0f : 127.0f;
+  hipError_t e;
+  if (a.mode == 0) {
+    hipLaunchKernelGGL(cell_clear_kernel, dim3(1), dim3(1), 0, s, a.scales);
+    if ((e = hipGetLastError()) != hipSuccess) return ERR_LAUNCH;
+    if ((e = dispatch_rq(a, p, 1, s)) != hipSuccess) return ERR_LAUNCH;
+    if ((e = dispatch_rq(a, p, 0, s)) != hipSuccess) return ERR_LAUNCH;
+    hipLaunchKernelGGL(cell_finalize_kernel, dim3(1), dim3(1), 0, s, a.scales, qmax,
+                       a.rotate ? 0.0625f : 1.0f);
+    if ((e = hipGetLastError()) != hipSuccess) return ERR_LAUNCH;
+    return OK;
+  }
+  return dispatch_rq(a, p, 0, s) == hipSuccess ? OK : ERR_LAUNCH;
+}
+
+int launch_lowrank_down(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* l1,
+                        int rank, uint16_t* lr, hipStream_t s) {
+  if (M == 0) return OK;
+  const unsigned blocks = (unsigned)((M + 63) / 64);
+  hipLaunchKernelGGL(lowrank_down_kernel, dim3(blocks), dim3(256), 0, s, x, M, K, ldx, l1, rank, lr);
+  return hipGetLastError() == hipSuccess ? OK : ERR_LAUNCH;
+}
+
+}  // namespace ql

@@ -1,0 +1,74 @@
+"""Shared helpers for the test suite (marshalling between numpy and torch)."""
+
+import os
+import re
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlinear.h")
+
+
+def ensure_built():
+    """Build libqlinear.so in-tree if it is not there yet; return its path."""
+    from rotated_bit_quantized_rotate_amd import build as B
+
+    if not os.path.exists(B.LIB_PATH):
+        B.build()
+    return B.LIB_PATH
+
+
+def header_functions():
+    """Names of the functions include/qlinear.h declares."""
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", txt, flags=re.M)))
+
+
+def header_constants():
+    txt = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"\b(QL_[A-Z0-9_]+)\s*=\s*(-?\d+)", txt)}
+
+
+def to_dev_bf16(bits, device="cuda"):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def bf16_bits(t):
+    import torch
+
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def to_dev(a, device="cuda"):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def rel_fro(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def f32_ulp_diff(a, b):
+    """|ulp distance| between float32 arrays (same sign assumed for nonzeros)."""
+    ai = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    bi = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    return np.abs(ai - bi)
+
+
+def bf16_ulp_diff(a_bits, b_bits):
+    def key(x):
+        x = np.asarray(x, np.uint16).astype(np.int64)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x)
+    return np.abs(key(a_bits) - key(b_bits))
+
+
+def code_flip_stats(got, want):
+    """(fraction of differing codes, max |difference|)."""
+    d = np.abs(got.astype(np.int32) - want.astype(np.int32))
+    return float((d != 0).mean()) if d.size else 0.0, int(d.max()) if d.size else 0

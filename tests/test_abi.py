@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+the header declares, its constants match the binding, and argument
+validation rejects bad calls before touching a device."""
+
+import ctypes
+
+import pytest
+
+from tests.helpers import ensure_built, header_constants, header_functions
+
+
+@pytest.fixture(scope="module")
+def L():
+    ensure_built()
+    from rotated_bit_quantized_rotate_amd import _lib
+
+    return _lib.lib()
+
+
+def test_header_declares_the_five_entry_points():
+    fns = header_functions()
+    for name in ["rotate_quantize_act", "pack_weight_int4", "qgemm_w4a4", "qgemm_w8a8",
+                 "qgemm_w4a4_lowrank", "ql_status_string", "ql_device_supported"]:
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in header_functions():
+        assert hasattr(L, name), name
+
+
+def test_binding_constants_match_header():
+    from rotated_bit_quantized_rotate_amd import _lib
+
+    consts = header_constants()
+    assert consts
+    for k, v in consts.items():
+        assert getattr(_lib, k) == v, k
+
+
+def test_status_strings(L):
+    from rotated_bit_quantized_rotate_amd import _lib
+
+    for k, v in header_constants().items():
+        if k.startswith("QL_ERR") or k == "QL_OK":
+            s = _lib.status_string(v)
+            assert s.startswith(k), (k, s)
+    assert "unknown" in _lib.status_string(-99)
+
+
+NULL = None
+ALIGNED = ctypes.c_void_p(0x10000)     # never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def rq(L, **kw):
+    a = dict(x=ALIGNED, M=4, K=256, ldx=256, bits=4, mode=1, layout=0, rotate=1, codes=ALIGNED,
+             scales=ALIGNED, l1=NULL, rank=0, lr=NULL)
+    a.update(kw)
+    return L.rotate_quantize_act(a["x"], a["M"], a["K"], a["ldx"], a["bits"], a["mode"], a["layout"],
+                                 a["rotate"], a["codes"], a["scales"], a["l1"], a["rank"], a["lr"], None)
+
+
+def test_rotate_quantize_validation(L):
+    assert rq(L, bits=5) == -4
+    assert rq(L, mode=7) == -4
+    assert rq(L, layout=1, bits=8) == -4          # packed layout is int4-only
+    assert rq(L, rotate=2) == -4
+    assert rq(L, K=320, ldx=320) == -2            # K % 256
+    assert rq(L, K=0, ldx=0) == -2
+    assert rq(L, ldx=128) == -2                   # ldx < K
+    assert rq(L, ldx=260) == -2                   # ldx % 8
+    assert rq(L, M=-1) == -2
+    assert rq(L, x=NULL) == -1
+    assert rq(L, codes=NULL) == -1
+    assert rq(L, scales=NULL) == -1
+    assert rq(L, x=MISALIGNED) == -3
+    assert rq(L, rank=32) == -2                   # rank without l1
+    assert rq(L, l1=ALIGNED, rank=24, lr=ALIGNED) == -2
+    assert rq(L, l1=ALIGNED, rank=32, lr=NULL) == -1
+
+
+def g44(L, **kw):
+    a = dict(a=ALIGNED, sa=ALIGNED, am=1, al=0, w=ALIGNED, sw=ALIGNED, wm=1, M=4, N=32, K=256, bias=NULL,
+             epi=0, out=ALIGNED, ldo=32)
+    a.update(kw)
+    return L.qgemm_w4a4(a["a"], a["sa"], a["am"], a["al"], a["w"], a["sw"], a["wm"], a["M"], a["N"], a["K"],
+                        a["bias"], a["epi"], a["out"], a["ldo"], None)
+
+
+def test_qgemm_w4a4_validation(L):
+    assert g44(L, N=24) == -2                     # N % 16
+    assert g44(L, K=128) == -2
+    assert g44(L, ldo=16) == -2
+    assert g44(L, ldo=36) == -3                   # bf16 row stride not 16-byte aligned
+    assert g44(L, epi=1) == -4                    # SWIGLU goes through the low-rank entry
+    assert g44(L, epi=2) == -4
+    assert g44(L, am=2) == -4                     # group64 only on both sides
+    assert g44(L, al=3) == -4
+    assert g44(L, a=NULL) == -1
+    assert g44(L, sw=NULL) == -1
+    assert g44(L, w=MISALIGNED) == -3
+    assert g44(L, am=2, wm=2, epi=4) == -4        # exact int32 output needs one scale per product
+
+
+def g88(L, **kw):
+    a = dict(a=ALIGNED, sa=ALIGNED, am=1, w=ALIGNED, sw=ALIGNED, wm=1, M=4, N=32, K=256, bias=NULL,
+             res=NULL, gate=NULL, epi=0, out=ALIGNED, ldo=32)
+    a.update(kw)
+    return L.qgemm_w8a8(a["a"], a["sa"], a["am"], a["w"], a["sw"], a["wm"], a["M"], a["N"], a["K"],
+                        a["bias"], a["res"], a["gate"], a["epi"], a["out"], a["ldo"], None)
+
+
+def test_qgemm_w8a8_validation(L):
+    assert g88(L, epi=2) == -1                    # gated residual needs residual and gate
+    assert g88(L, epi=2, res=ALIGNED) == -1
+    assert g88(L, am=2) == -4
+    assert g88(L, epi=1) == -4
+    assert g88(L, N=0) == -2
+    assert g88(L, epi=2, res=MISALIGNED, gate=ALIGNED) == -3
+
+
+def glr(L, **kw):
+    a = dict(a=ALIGNED, sa=ALIGNED, am=2, al=0, w=ALIGNED, sw=ALIGNED, wm=2, lr=ALIGNED, l2=ALIGNED, r=32,
+             M=4, N=64, K=256, bias=NULL, epi=1, out=ALIGNED, ldo=32)
+    a.update(kw)
+    return L.qgemm_w4a4_lowrank(a["a"], a["sa"], a["am"], a["al"], a["w"], a["sw"], a["wm"], a["lr"],
+                                a["l2"], a["r"], a["M"], a["N"], a["K"], a["bias"], a["epi"], a["out"],
+                                a["ldo"], None)
+
+
+def test_qgemm_lowrank_validation(L):
+    assert glr(L, r=20) == -2
+    assert glr(L, r=256) == -2
+    assert glr(L, lr=NULL) == -1
+    assert glr(L, N=48) == -2                     # SWIGLU needs N % 32
+    assert glr(L, ldo=16) == -2                   # out needs N/2 columns
+    assert glr(L, am=1) == -4                     # group64 on one side only
+    assert glr(L, epi=4) == -4
+    assert glr(L, epi=2) == -4
+
+
+def test_device_supported_without_gpu_is_false(L):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert L.ql_device_supported(0) == 0

@@ -1,0 +1,477 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Acceptance (the contract of the layer):
+  * activation / weight codes: mismatches are all +-1 and at most 1e-4 of
+    the codes (fp32 butterflies versus the exactly rotated value can land on
+    the other side of a rounding boundary only at near-ties); scales within
+    8 float32 ulp (the scale is absmax/qmax of the fp32-rotated unit: the
+    absmax element carries the rounding of four butterfly stages, a few
+    ulp, so the exact-rotation oracle can differ by that much);
+  * int32 accumulators bit-exact when both sides consume the same codes;
+  * final bf16 outputs within 1e-2 relative Frobenius error of the oracle.
+Inputs are the seeded synthetic workloads; sizes span several 128x128
+tiles plus ragged tails.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from tests.helpers import (bf16_bits, bf16_ulp_diff, code_flip_stats, ensure_built, f32_ulp_diff,
+                           rel_fro, to_dev, to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+FLIP_BUDGET = 1e-4
+REL_FRO = 1e-2
+SCALE_ULP = 8
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import torch
+
+    ensure_built()
+    import rotated_bit_quantized_rotate_amd as Q
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    assert Q.device_supported(0), "device is not gfx950"
+    return Q
+
+
+@pytest.fixture(scope="module")
+def Q(_lib):
+    return _lib
+
+
+def _rand_bf16(seed, shape, std=1.0, outliers=0, factor=30.0):
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal(shape, dtype=np.float32) * np.float32(std)
+    if outliers:
+        a, _ = W.with_outlier_channels(rng, a, outliers, factor)
+    return W.to_bf16_bits(a)
+
+
+def _check_codes(got_codes, got_scales, ref, budget=FLIP_BUDGET):
+    frac, dmax = code_flip_stats(got_codes, ref.codes)
+    assert dmax <= 1, f"code difference {dmax} > 1"
+    assert frac <= budget, f"flip fraction {frac:.2e} > {budget:.0e}"
+    ulp = f32_ulp_diff(got_scales.reshape(ref.scales.shape), ref.scales)
+    assert ulp.max() <= SCALE_ULP, f"scale ulp diff {ulp.max()}"
+    return frac
+
+
+# --------------------------------------------------------------- prologue --
+
+@pytest.mark.parametrize("M,K", [(1, 256), (37, 512), (300, 5120), (5, 20480), (16, 1536), (33, 6144)])
+@pytest.mark.parametrize("bits,mode", [(4, "row"), (8, "row"), (4, "group64"), (4, "tensor"),
+                                       (8, "tensor")])
+def test_rotate_quantize_matches_oracle(Q, M, K, bits, mode):
+    import torch
+
+    xb = _rand_bf16(M * 7 + K, (M, K), outliers=max(1, K // 100))
+    x = to_dev_bf16(xb)
+    codes, scales, _ = Q.rotate_quantize_act(x, bits=bits, scale_mode=mode, layout="i8", rotate=True)
+    torch.cuda.synchronize()
+    ref = O.quantize_activations(xb, bits, mode, True)
+    _check_codes(codes.cpu().numpy(), scales.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("mode", ["row", "group64", "tensor"])
+def test_packed_layout_and_no_rotation(Q, mode):
+    import torch
+
+    M, K = 70, 1024
+    xb = _rand_bf16(3, (M, K), outliers=8)
+    x = to_dev_bf16(xb)
+    for rot in (True, False):
+        packed, scales, _ = Q.rotate_quantize_act(x, bits=4, scale_mode=mode, layout="packed", rotate=rot)
+        torch.cuda.synchronize()
+        ref = O.quantize_activations(xb, 4, mode, rot)
+        got = O.unpack_int4(packed.cpu().numpy())
+        budget = FLIP_BUDGET if rot else 0.0   # no rotation: the decision is bit-identical
+        _check_codes(got, scales.cpu().numpy(), ref, budget)
+
+
+def test_prologue_degenerate_rows(Q):
+    import torch
+
+    M, K = 6, 512
+    xb = _rand_bf16(4, (M, K))
+    xb[1] = 0                                  # all-zero row: scale 0, codes 0
+    xb[2] = 0
+    xb[2, 17] = W.to_bf16_bits(np.array([1000.0], np.float32))[0]   # one huge outlier
+    xb[3, :256] = 0                            # all-zero 64-groups
+    x = to_dev_bf16(xb)
+    for bits, mode in [(4, "row"), (8, "row"), (4, "group64")]:
+        codes, scales, _ = Q.rotate_quantize_act(x, bits=bits, scale_mode=mode)
+        torch.cuda.synchronize()
+        ref = O.quantize_activations(xb, bits, mode, True)
+        _check_codes(codes.cpu().numpy(), scales.cpu().numpy(), ref, 0.0)
+        assert (codes.cpu().numpy()[1] == 0).all()
+
+
+def test_prologue_empty_input(Q):
+    import torch
+
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    codes, scales, _ = Q.rotate_quantize_act(x, bits=4, scale_mode="row")
+    torch.cuda.synchronize()
+    assert codes.shape == (0, 256)
+
+
+def test_prologue_strided_rows(Q):
+    import torch
+
+    M, K, ld = 9, 512, 768
+    xb = _rand_bf16(5, (M, ld))
+    x = to_dev_bf16(xb)[:, :K]
+    codes, scales, _ = Q.rotate_quantize_act(x, bits=4, scale_mode="row")
+    torch.cuda.synchronize()
+    ref = O.quantize_activations(np.ascontiguousarray(xb[:, :K]), 4, "row", True)
+    _check_codes(codes.cpu().numpy(), scales.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("rank", [16, 32, 64])
+def test_lowrank_down_projection(Q, rank):
+    import torch
+
+    M, K = 130, 1024
+    xb = _rand_bf16(6, (M, K))
+    l1b = _rand_bf16(7, (K, rank), 0.02)
+    _, _, lr = Q.rotate_quantize_act(to_dev_bf16(xb), bits=4, scale_mode="group64",
+                                     l1=to_dev_bf16(l1b))
+    torch.cuda.synchronize()
+    want = O.bf16_bits_to_f64(xb) @ O.bf16_bits_to_f64(l1b)
+    got = O.bf16_bits_to_f64(bf16_bits(lr))
+    assert rel_fro(got, want) < 4e-3
+    assert bf16_ulp_diff(bf16_bits(lr), O.f64_to_bf16_bits(want)).max() <= 1
+
+
+# ------------------------------------------------------------ weight pack --
+
+@pytest.mark.parametrize("mode", ["row", "tensor", "group64"])
+def test_pack_weight_int4_matches_oracle(Q, mode):
+    import torch
+
+    N, K = 272, 1024
+    wb = _rand_bf16(8, (N, K), 0.02)
+    packed, scales = Q.pack_weight_int4(to_dev_bf16(wb), scale_mode=mode)
+    torch.cuda.synchronize()
+    ref = O.quantize_weights(wb, 4, mode, True)
+    got = O.unpack_int4(packed.cpu().numpy())
+    _check_codes(got, scales.cpu().numpy(), ref)
+
+
+# -------------------------------------------------- exact integer product --
+
+GEMM_SHAPES = [(1, 16, 256), (130, 272, 512), (257, 400, 1024), (128, 128, 256), (300, 656, 768)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+@pytest.mark.parametrize("a_layout", ["i8", "packed"])
+def test_w4a4_int32_bit_exact(Q, M, N, K, a_layout):
+    import torch
+
+    rng = np.random.default_rng(M + N + K)
+    qa = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    a = to_dev(O.pack_int4(qa) if a_layout == "packed" else qa)
+    w = to_dev(O.pack_int4(qw))
+    one_a = torch.ones(M, dtype=torch.float32, device="cuda")
+    one_w = torch.ones(N, dtype=torch.float32, device="cuda")
+    out = Q.qgemm_w4a4(a, one_a, w, one_w, K, a_layout=a_layout, epilogue="i32")
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.int64), O.int_gemm(qa, qw))
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES + [(64, 64, 20480)])
+def test_w8a8_int32_bit_exact(Q, M, N, K):
+    import torch
+
+    rng = np.random.default_rng(M * N + K)
+    qa = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    one_a = torch.ones(M, dtype=torch.float32, device="cuda")
+    one_w = torch.ones(N, dtype=torch.float32, device="cuda")
+    out = Q.qgemm_w8a8(to_dev(qa), one_a, to_dev(qw), one_w, epilogue="i32")
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.int64), O.int_gemm(qa, qw))
+
+
+def test_int32_extremes(Q):
+    """All codes at +-qmax: the largest accumulators the layer can produce."""
+    import torch
+
+    M, N, K = 32, 32, 20480
+    qa = np.full((M, K), 127, np.int8)
+    qw = np.full((N, K), -127, np.int8)
+    qw[::2] = 127
+    ones = torch.ones(max(M, N), dtype=torch.float32, device="cuda")
+    out = Q.qgemm_w8a8(to_dev(qa), ones[:M], to_dev(qw), ones[:N], epilogue="i32")
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.int64), O.int_gemm(qa, qw))
+    qa4 = np.full((M, 5120), -7, np.int8)
+    qw4 = np.full((N, 5120), 7, np.int8)
+    out = Q.qgemm_w4a4(to_dev(O.pack_int4(qa4)), ones[:M], to_dev(O.pack_int4(qw4)), ones[:N], 5120,
+                       a_layout="packed", epilogue="i32")
+    torch.cuda.synchronize()
+    assert (out.cpu().numpy() == -49 * 5120).all()
+
+
+def test_group64_unit_scales_exact(Q):
+    """Group-64 with all scales 1: the per-group fp32 sum of exact int32
+    partials is exact (|sum| < 2^24), so the float output equals the
+    integer product bit for bit."""
+    import torch
+
+    M, N, K = 130, 144, 1024
+    rng = np.random.default_rng(9)
+    qa = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    sa = torch.ones((M, K // 64), dtype=torch.float32, device="cuda")
+    sw = torch.ones((N, K // 64), dtype=torch.float32, device="cuda")
+    out = Q.qgemm_w4a4_lowrank(to_dev(qa), sa, to_dev(O.pack_int4(qw)), sw, K, epilogue="f32")
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), O.int_gemm(qa, qw).astype(np.float64))
+
+
+# ---------------------------------------------- dequant epilogues (same codes) --
+
+def _assert_bf16_close(got_bits, want_f64, magnitude):
+    """got (bf16 bits) within one bf16 ulp of the rounded oracle value, plus
+    an absolute float32-arithmetic allowance of 1e-6 * magnitude (covers
+    cancellation, e.g. y + bias near zero)."""
+    got = O.bf16_bits_to_f64(got_bits)
+    want = O.bf16_round(want_f64)
+    ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(want), 1e-38))[1] - 8)
+    err = np.abs(got - want)
+    bad = err > ulp + 1e-6 * magnitude
+    assert not bad.any(), f"{int(bad.sum())} outputs off; worst {float((err - ulp).max()):.3e}"
+
+
+def _upload_quant(ref, packed):
+    codes = O.pack_int4(ref.codes) if packed else ref.codes
+    return to_dev(codes), to_dev(np.ascontiguousarray(ref.scales))
+
+
+@pytest.mark.parametrize("mode", ["row", "tensor"])
+def test_w4a4_bf16_epilogue_same_codes(Q, mode):
+    import torch
+
+    M, N, K = 257, 400, 1024
+    xb = _rand_bf16(10, (M, K), outliers=10)
+    wb = _rand_bf16(11, (N, K), 0.02)
+    bias = _rand_bf16(12, (N,), 0.1)
+    qa = O.quantize_activations(xb, 4, mode)
+    qw = O.quantize_weights(wb, 4, mode)
+    a, sa = _upload_quant(qa, False)
+    w, sw = _upload_quant(qw, True)
+    for bb in (None, bias):
+        out = Q.qgemm_w4a4(a, sa, w, sw, K, a_scale_mode=mode, w_scale_mode=mode,
+                           bias=None if bb is None else to_dev_bf16(bb))
+        torch.cuda.synchronize()
+        y = O.linear_fp64(qa, qw, bias_bits=bb)
+        want = O.f64_to_bf16_bits(y)
+        got = bf16_bits(out)
+        assert rel_fro(O.bf16_bits_to_f64(got), O.bf16_bits_to_f64(want)) < REL_FRO
+        _assert_bf16_close(got, y, np.abs(O.linear_fp64(qa, qw)) + (0 if bb is None else 1.0))
+
+
+def test_w8a8_gated_residual_same_codes(Q):
+    import torch
+
+    M, N, K = 200, 272, 2048
+    xb = _rand_bf16(13, (M, K))
+    wb = _rand_bf16(14, (N, K), 0.01)
+    res = _rand_bf16(15, (M, N))
+    gate = _rand_bf16(16, (N,))
+    qa = O.quantize_activations(xb, 8, "row")
+    qw = O.quantize_weights(wb, 8, "row")
+    a, sa = _upload_quant(qa, False)
+    w, sw = _upload_quant(qw, False)
+    y = O.linear_fp64(qa, qw)
+    # out-of-place
+    out = Q.qgemm_w8a8(a, sa, w, sw, residual=to_dev_bf16(res), gate=to_dev_bf16(gate),
+                       epilogue="gated_residual")
+    torch.cuda.synchronize()
+    ref = O.epilogue(y, "gated_residual", O.bf16_bits_to_f64(res), O.bf16_bits_to_f64(gate))
+    mag = np.abs(O.bf16_bits_to_f64(res)) + np.abs(y * O.bf16_bits_to_f64(gate)[None, :])
+    _assert_bf16_close(bf16_bits(out), ref, mag)
+    # in place: h += gate * y
+    h = to_dev_bf16(res)
+    Q.qgemm_w8a8(a, sa, w, sw, residual=h, gate=to_dev_bf16(gate), epilogue="gated_residual", out=h)
+    torch.cuda.synchronize()
+    _assert_bf16_close(bf16_bits(h), ref, mag)
+    # residual 0, gate 1: the plain epilogue, so the residual cannot mask the product
+    z = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    ones = to_dev_bf16(W.to_bf16_bits(np.ones(N, np.float32)))
+    out = Q.qgemm_w8a8(a, sa, w, sw, residual=z, gate=ones, epilogue="gated_residual")
+    plain = Q.qgemm_w8a8(a, sa, w, sw, epilogue="bf16")
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(out), bf16_bits(plain))
+    _assert_bf16_close(bf16_bits(plain), y, np.abs(y))
+
+
+@pytest.mark.parametrize("rank", [0, 32])
+@pytest.mark.parametrize("epi", ["swiglu", "bf16"])
+def test_group64_lowrank_same_codes(Q, rank, epi):
+    import torch
+
+    M, F, K = 130, 160, 1024
+    N = 2 * F
+    xb = _rand_bf16(17, (M, K))
+    wb = _rand_bf16(18, (N, K), 0.02)
+    l1 = _rand_bf16(19, (K, max(rank, 16)), 0.02)[:, :rank]
+    l2 = _rand_bf16(20, (max(rank, 16), N), 0.02)[:rank]
+    qa = O.quantize_activations(xb, 4, "group64")
+    qw = O.quantize_weights(wb, 4, "group64")
+    a, sa = _upload_quant(qa, False)
+    w, sw = _upload_quant(qw, True)
+    lr = None
+    l2d = None
+    if rank:
+        _, _, lr = Q.rotate_quantize_act(to_dev_bf16(xb), bits=4, scale_mode="group64",
+                                         l1=to_dev_bf16(np.ascontiguousarray(l1)))
+        l2d = to_dev_bf16(np.ascontiguousarray(l2))
+    out = Q.qgemm_w4a4_lowrank(a, sa, w, sw, K, lr=lr, l2=l2d, epilogue=epi)
+    torch.cuda.synchronize()
+    y = O.linear_fp64(qa, qw, xb, l1 if rank else None, l2 if rank else None)
+    want = O.f64_to_bf16_bits(O.epilogue(y, epi))
+    got = bf16_bits(out)
+    assert rel_fro(O.bf16_bits_to_f64(got), O.bf16_bits_to_f64(want)) < REL_FRO
+    if rank == 0:
+        assert bf16_ulp_diff(got, want).max() <= 2
+
+
+# ------------------------------------------------- end to end, per workload --
+
+def _e2e(Q, wl, rows=None, wrows=None):
+    """Run the whole GPU path (prologue, weight prep, GEMM + epilogue) on the
+    full workload; compare with the oracle on `rows` (all if None) and, for
+    row/group scales, only on weight rows `wrows` (all if None)."""
+    import torch
+
+    x = to_dev_bf16(wl.x)
+    w = to_dev_bf16(wl.w)
+    mode = wl.scale_mode
+    rank = 0 if wl.l1 is None else wl.l1.shape[1]
+    l1 = to_dev_bf16(wl.l1) if rank else None
+    a_codes, sa, lr = Q.rotate_quantize_act(x, bits=wl.a_bits, scale_mode=mode, l1=l1)
+    if wl.w_bits == 4:
+        wq, sw = Q.pack_weight_int4(w, scale_mode=mode)
+    else:
+        wq, sw, _ = Q.rotate_quantize_act(w, bits=8, scale_mode=mode)
+    if wl.epilogue == "gated_residual":
+        out = Q.qgemm_w8a8(a_codes, sa, wq, sw, residual=to_dev_bf16(wl.residual),
+                           gate=to_dev_bf16(wl.gate), epilogue="gated_residual")
+    elif wl.w_bits == 8:
+        out = Q.qgemm_w8a8(a_codes, sa, wq, sw, a_scale_mode=mode, w_scale_mode=mode)
+    elif mode == "group64" or rank:
+        out = Q.qgemm_w4a4_lowrank(a_codes, sa, wq, sw, wl.K, lr=lr,
+                                   l2=to_dev_bf16(wl.l2) if rank else None,
+                                   a_scale_mode=mode, w_scale_mode=mode, epilogue=wl.epilogue)
+    else:
+        out = Q.qgemm_w4a4(a_codes, sa, wq, sw, wl.K, a_scale_mode=mode, w_scale_mode=mode)
+    torch.cuda.synchronize()
+
+    rsel = np.arange(wl.M) if rows is None else np.asarray(rows)
+    xs = np.ascontiguousarray(wl.x[rsel])
+    qa = O.quantize_activations(xs if mode != "tensor" else wl.x, wl.a_bits, mode)
+    if mode == "tensor":
+        qa = O.QuantResult(qa.codes[rsel], qa.scales, qa.bits, mode, None)
+    got_codes = a_codes.cpu().numpy()[rsel]
+    frac = _check_codes(got_codes, sa.cpu().numpy()[rsel] if mode != "tensor" else sa.cpu().numpy(), qa)
+
+    if wl.epilogue == "swiglu":
+        F = wl.N // 2
+        fsel = np.arange(F) if wrows is None else np.asarray(wrows)
+        nsel = np.concatenate([fsel, F + fsel])
+    else:
+        nsel = np.arange(wl.N) if wrows is None else np.asarray(wrows)
+    qw = O.quantize_weights(np.ascontiguousarray(wl.w[nsel]) if mode != "tensor" else wl.w,
+                            wl.w_bits, mode)
+    if mode == "tensor":
+        qw = O.QuantResult(qw.codes[nsel], qw.scales, qw.bits, mode, None)
+    l2s = np.ascontiguousarray(wl.l2[:, nsel]) if rank else None
+    y = O.linear_fp64(qa, qw, xs, wl.l1 if rank else None, l2s)
+    if wl.epilogue == "gated_residual":
+        ref = O.epilogue(y, "gated_residual", O.bf16_bits_to_f64(wl.residual[np.ix_(rsel, nsel)]),
+                         O.bf16_bits_to_f64(wl.gate[nsel]))
+        got = bf16_bits(out)[np.ix_(rsel, nsel)]
+    elif wl.epilogue == "swiglu":
+        ref = O.epilogue(y, "swiglu")
+        got = bf16_bits(out)[np.ix_(rsel, nsel[:len(nsel) // 2])]
+    else:
+        ref = y
+        got = bf16_bits(out)[np.ix_(rsel, nsel)]
+    want = O.f64_to_bf16_bits(ref)
+    err = rel_fro(O.bf16_bits_to_f64(got), O.bf16_bits_to_f64(want))
+    assert err < REL_FRO, f"{wl.name}: rel Frobenius {err:.3e}"
+    return err, frac
+
+
+def test_e2e_tiny_tensorwise(Q):
+    err, frac = _e2e(Q, W.tiny_w4a4(0))
+    assert err < 2e-3
+
+
+def test_e2e_attention_projection_reduced(Q):
+    wl = W.attn_proj_w4a4(M=520, N=656)
+    _e2e(Q, wl)
+
+
+def test_e2e_attention_projection_full_size(Q):
+    """The benchmarked shape M=4096, K=N=5120: every output row the oracle
+    checks is one of 64 sampled rows (all 5120 columns)."""
+    wl = W.attn_proj_w4a4()
+    rows = np.random.default_rng(0).choice(wl.M, 64, replace=False)
+    _e2e(Q, wl, rows=rows)
+
+
+def test_e2e_ffdown_w8a8_reduced(Q):
+    wl = W.ffdown_w8a8(M=200, K=4096, N=272)
+    _e2e(Q, wl)
+
+
+def test_e2e_ffdown_w8a8_full_size(Q):
+    wl = W.ffdown_w8a8()
+    rng = np.random.default_rng(1)
+    _e2e(Q, wl, rows=rng.choice(wl.M, 16, replace=False), wrows=rng.choice(wl.N, 512, replace=False))
+
+
+def test_e2e_svdq_gateup_reduced(Q):
+    wl = W.svdq_gateup(M=130, K=1024, F=160)
+    _e2e(Q, wl)
+
+
+def test_e2e_svdq_gateup_full_size(Q):
+    wl = W.svdq_gateup()
+    rng = np.random.default_rng(2)
+    _e2e(Q, wl, rows=rng.choice(wl.M, 16, replace=False),
+         wrows=rng.choice(wl.N // 2, 256, replace=False))
+
+
+@pytest.mark.parametrize("index", [0, 1, 4, 5, 7, 7 + 8 * 15])
+def test_e2e_stack_layer_shapes(Q, index):
+    """One layer of each distinct shape/precision of the 224-linear stack at
+    16384 tokens (sampled rows)."""
+    wl = W.stack_layer(index)
+    rng = np.random.default_rng(index)
+    _e2e(Q, wl, rows=rng.choice(wl.M, 8, replace=False), wrows=rng.choice(wl.N, 384, replace=False))
+
+
+def test_deterministic_outputs(Q):
+    import torch
+
+    wl = W.attn_proj_w4a4(M=300, N=400)
+    x = to_dev_bf16(wl.x)
+    w = to_dev_bf16(wl.w)
+    outs = []
+    for _ in range(2):
+        a, sa, _ = Q.rotate_quantize_act(x, bits=4)
+        wq, sw = Q.pack_weight_int4(w)
+        outs.append(bf16_bits(Q.qgemm_w4a4(a, sa, wq, sw, wl.K)))
+        torch.cuda.synchronize()
+    assert np.array_equal(outs[0], outs[1])
