@@ -391,6 +391,7 @@ hipError_t launch_lr(const KArgs& k, int64_t tiles_n, hipStream_t s) {
 
 int launch_qgemm(const GemmArgs& g, hipStream_t s) {
   if (g.M == 0) return OK;
+  if (g.a_mode != 2 && g.rank == 0 && g.epilogue != EPI_SWIGLU) return launch_qgemm_pipe(g, s);
   KArgs k;
   k.a = static_cast<const uint8_t*>(g.a);
   k.w = static_cast<const uint8_t*>(g.w);

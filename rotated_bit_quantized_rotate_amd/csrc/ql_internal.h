@@ -83,5 +83,7 @@ struct GemmArgs {
 };
 
 int launch_qgemm(const GemmArgs& g, hipStream_t s);
+// Large-tile pipelined kernel: tensor / row scales; BF16, F32, I32, GATED.
+int launch_qgemm_pipe(const GemmArgs& g, hipStream_t s);
 
 }  // namespace ql
