@@ -34,7 +34,6 @@
 namespace ql {
 namespace {
 
-constexpr int NT = 512;      // threads per workgroup
 constexpr int BK = 128;      // channels per stage
 constexpr int kLdsBytes = 160 * 1024;
 
@@ -81,12 +80,15 @@ struct PArgs {
   int group_m;     // tile rows per L2 group
 };
 
-template <int BM_, int BN_, bool AP_, bool WP_>
+template <int BM_, int BN_, int WGM_, int WGN_, bool AP_, bool WP_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_;
+  static constexpr int WGM = WGM_, WGN = WGN_;   // wave grid
+  static constexpr int NW = WGM * WGN;           // waves per workgroup
+  static constexpr int NT = 64 * NW;
   static constexpr bool AP = AP_, WP = WP_;
-  static constexpr int WM = BM / 2;         // wave tile rows (2 wave rows)
-  static constexpr int WN = BN / 4;         // wave tile cols (4 wave cols)
+  static constexpr int WM = BM / WGM;       // wave tile rows
+  static constexpr int WN = BN / WGN;       // wave tile cols
   static constexpr int FI = WM / 16;
   static constexpr int FJ = WN / 16;
   static constexpr int ARB = AP ? BK / 2 : BK;  // bytes per A row per stage
@@ -97,19 +99,24 @@ struct Cfg {
   static constexpr int A_INSTR = SA / 1024;  // 1 KB per DMA instruction
   static constexpr int W_INSTR = SW / 1024;
   static_assert(SA % 1024 == 0 && SW % 1024 == 0, "stage must be whole KB");
-  static_assert(A_INSTR % 8 == 0, "A DMA must split evenly over 8 waves");
-  static constexpr int A_PER_WAVE = A_INSTR / 8;
-  static constexpr int W_HI = (W_INSTR + 7) / 8;  // waves < W_SPLIT issue W_HI
-  static constexpr int W_SPLIT = W_INSTR - (W_HI - 1) * 8;
+  static_assert(A_INSTR % NW == 0, "A DMA must split evenly over the waves");
+  static constexpr int A_PER_WAVE = A_INSTR / NW;
+  static constexpr int W_HI = (W_INSTR + NW - 1) / NW;  // waves < W_SPLIT issue W_HI
+  static constexpr int W_SPLIT = W_INSTR - (W_HI - 1) * NW;
   static constexpr int NSTAGE = (3 * STAGE <= kLdsBytes) ? 3 : 2;  // LDS ring depth
   static_assert(NSTAGE * STAGE <= kLdsBytes, "LDS ring too large");
   static_assert((NSTAGE - 2) * (A_PER_WAVE + W_HI) < 64, "vmcnt range");
 };
 
-// Chunk position inside an LDS row of RB bytes.
+// Chunk position inside an LDS row of RB bytes: chunk c of row r lives at
+// c ^ f(r).  A fragment read (ds_read_b128) has 16 lanes on 16 consecutive
+// rows at one chunk index per lane group; these XOR patterns were measured
+// on gfx950 (bank-conflict counter) to serve every such read, for 128-byte
+// rows with chunk 2g + kk and 64-byte rows with chunk g, without bank
+// conflicts.  f depends only on r & 15.
 template <int RB>
 __device__ __forceinline__ int swz(int r, int c) {
-  if (RB == 128) return c ^ (r & 7);
+  if (RB == 128) return c ^ (((r & 3) << 1) | ((r >> 2) & 1));
   return c ^ ((r >> 1) & 3);
 }
 
@@ -128,14 +135,14 @@ __device__ __forceinline__ const uint8_t* dma_src(const uint8_t* base, int64_t l
 }
 
 template <class C, int EPI>
-__global__ __launch_bounds__(NT, 1) void qgemm_pipe_kernel(PArgs p) {
+__global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
   constexpr int NS = C::NSTAGE;
   __shared__ __attribute__((aligned(16))) uint8_t smem[NS * C::STAGE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 2;   // 0..1
-  const int wn = wave & 3;    // 0..3
+  const int wm = wave / C::WGN;
+  const int wn = wave % C::WGN;
   const int l16 = lane & 15;
   const int lg = lane >> 4;
 
@@ -158,20 +165,23 @@ __global__ __launch_bounds__(NT, 1) void qgemm_pipe_kernel(PArgs p) {
   const int64_t ldw = C::WP ? p.K / 2 : p.K;
   const int KT = (int)(p.K / BK);
 
-  // ---- DMA issue for one stage ------------------------------------------
+  // ---- DMA issue -----------------------------------------------------------
+  // Instruction t (0 .. NDMA-1) of this wave's share of stage kt: the first
+  // A_PER_WAVE move A, the rest W.  A burst of these right after a barrier
+  // stalls the wave on VMEM issue while its MFMA pipe idles, so the main
+  // loop spreads them through the MFMA stream.
   const bool w_hi = wave < C::W_SPLIT;
-  auto issue = [&](int kt) {
+  constexpr int NDMA = C::A_PER_WAVE + C::W_HI;
+  auto issue_one = [&](int kt, int t) {
     uint8_t* st = smem + (kt % NS) * C::STAGE;
-#pragma unroll
-    for (int t = 0; t < C::A_PER_WAVE; ++t) {
-      const int q = wave + 8 * t;
+    if (t < C::A_PER_WAVE) {
+      const int q = wave + C::NW * t;
       const uint8_t* src = dma_src<C::ARB>(p.a, lda, m0, p.M, q, lane, (int64_t)kt * C::ARB);
       __builtin_amdgcn_global_load_lds(src, LDS_AS(st + q * 1024), 16, 0, 0);
-    }
-#pragma unroll
-    for (int t = 0; t < C::W_HI; ++t) {
-      if (t < C::W_HI - 1 || w_hi) {
-        const int q = wave + 8 * t;
+    } else {
+      const int tw = t - C::A_PER_WAVE;
+      if (tw < C::W_HI - 1 || w_hi) {
+        const int q = wave + C::NW * tw;
         const uint8_t* src = dma_src<C::WRB>(p.w, ldw, n0, p.N, q, lane, (int64_t)kt * C::WRB);
         __builtin_amdgcn_global_load_lds(src, LDS_AS(st + C::SA + q * 1024), 16, 0, 0);
       }
@@ -184,7 +194,9 @@ __global__ __launch_bounds__(NT, 1) void qgemm_pipe_kernel(PArgs p) {
 #pragma unroll
     for (int i = 0; i < C::FI; ++i) acc[j][i] = v4i{0, 0, 0, 0};
 
-  // lane-constant LDS offsets (row & 7 and (row >> 1) & 3 depend on l16 only)
+  // lane-constant LDS offsets: fragment rows differ by multiples of 16, so
+  // the swizzle term depends on l16 only.
+  static_assert(C::WM % 16 == 0 && C::WN % 16 == 0, "wave tile must be 16-aligned");
   const int a_row = wm * C::WM + l16;
   const int w_row = wn * C::WN + l16;
   int a_off[2];
@@ -203,23 +215,28 @@ __global__ __launch_bounds__(NT, 1) void qgemm_pipe_kernel(PArgs p) {
   // prologue: stages 0 .. NS-2 in flight
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; ++s0)
-    if (s0 < KT) issue(s0);
+    if (s0 < KT) {
+#pragma unroll
+      for (int t = 0; t < NDMA; ++t) issue_one(s0, t);
+    }
 
   for (int kt = 0; kt < KT; ++kt) {
     // Stage kt has landed once only the later stages (at most NS-2 of them)
     // are still in flight; the barrier then publishes every wave's part and
-    // guarantees all waves finished reading the buffer the next issue reuses.
+    // guarantees all waves finished reading the buffer the next DMA reuses.
     if (NS == 3 && kt + 1 < KT) {
-      if (w_hi) wait_vmcnt<(NS - 2) * (C::A_PER_WAVE + C::W_HI)>();
-      else wait_vmcnt<(NS - 2) * (C::A_PER_WAVE + C::W_HI - 1)>();
+      if (w_hi) wait_vmcnt<(NS - 2) * NDMA>();
+      else wait_vmcnt<(NS - 2) * (NDMA - 1)>();
     } else {
       wait_vmcnt<0>();
     }
     lds_barrier();
-    if (kt + NS - 1 < KT) issue(kt + NS - 1);
+    const bool dma = kt + NS - 1 < KT;
 
     const uint8_t* As = smem + (kt % NS) * C::STAGE;
     const uint8_t* Ws = As + C::SA;
+    // W fragments: packed -> one b128 per fragment carries both halves (kk);
+    // int8 -> one b128 per fragment and half.
     uint4 wraw[C::FJ];
     uint4 wraw1[C::WP ? 1 : C::FJ];
 #pragma unroll
@@ -227,63 +244,77 @@ __global__ __launch_bounds__(NT, 1) void qgemm_pipe_kernel(PArgs p) {
       wraw[j] = *reinterpret_cast<const uint4*>(Ws + w_off + j * 16 * C::WRB);
       if (!C::WP) wraw1[j] = *reinterpret_cast<const uint4*>(Ws + w_off1 + j * 16 * C::WRB);
     }
+    // A fragments: int8 -> streamed through a small window read PF ahead;
+    // packed -> one b128 per fragment carries both halves.
+    constexpr int PF = 3;
+    constexpr int NQ = 2 * C::FI;
+    v4i abuf[PF + 1];
     uint4 araw[C::AP ? C::FI : 1];
     if (C::AP) {
 #pragma unroll
-      for (int i = 0; i < C::FI; ++i)
-        araw[i] = *reinterpret_cast<const uint4*>(As + a_off[0] + i * 16 * C::ARB);
+      for (int i = 0; i < C::FI; ++i) araw[i] = *reinterpret_cast<const uint4*>(As + a_off[0] + i * 16 * C::ARB);
+    } else {
+#pragma unroll
+      for (int q = 0; q < PF; ++q)
+        abuf[q] = *reinterpret_cast<const v4i*>(As + a_off[q / C::FI] + (q % C::FI) * 16 * C::ARB);
     }
+    v4i bw0[C::FJ], bw1[C::FJ];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      v4i bw[C::FJ];
+    for (int j = 0; j < C::FJ; ++j)
+      bw0[j] = C::WP ? unpack_lo(wraw[j].x, wraw[j].y)
+                     : v4i{(int)wraw[j].x, (int)wraw[j].y, (int)wraw[j].z, (int)wraw[j].w};
 #pragma unroll
-      for (int j = 0; j < C::FJ; ++j) {
-        if (C::WP) {
-          bw[j] = kk == 0 ? unpack_lo(wraw[j].x, wraw[j].y) : unpack_lo(wraw[j].z, wraw[j].w);
-        } else {
-          const uint4 u = kk == 0 ? wraw[j] : wraw1[j];
-          bw[j] = v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w};
-        }
+    for (int q = 0; q < NQ; ++q) {
+      const int kk = q / C::FI, i = q % C::FI;
+      v4i af;
+      if (C::AP) {
+        af = kk == 0 ? unpack_lo(araw[i].x, araw[i].y) : unpack_lo(araw[i].z, araw[i].w);
+      } else {
+        if (q + PF < NQ)
+          abuf[(q + PF) % (PF + 1)] = *reinterpret_cast<const v4i*>(
+              As + a_off[(q + PF) / C::FI] + ((q + PF) % C::FI) * 16 * C::ARB);
+        af = abuf[q % (PF + 1)];
       }
+      if (dma && (q % 2) == 0 && q / 2 < NDMA) issue_one(kt + NS - 1, q / 2);
+      // second-half W fragments, spread over the first half's MFMA groups
+      if (kk == 0 && i < C::FJ)
+        bw1[i] = C::WP ? unpack_lo(wraw[i].z, wraw[i].w)
+                       : v4i{(int)wraw1[i].x, (int)wraw1[i].y, (int)wraw1[i].z, (int)wraw1[i].w};
+      if (kk == 0 && i == C::FI - 1) {
 #pragma unroll
-      for (int i = 0; i < C::FI; ++i) {
-        v4i af;
-        if (C::AP) {
-          af = kk == 0 ? unpack_lo(araw[i].x, araw[i].y) : unpack_lo(araw[i].z, araw[i].w);
-        } else {
-          af = *reinterpret_cast<const v4i*>(As + a_off[kk] + i * 16 * C::ARB);
-        }
-#pragma unroll
-        for (int j = 0; j < C::FJ; ++j)
-          acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bw[j], af, acc[j][i], 0, 0, 0);
+        for (int j = C::FI; j < C::FJ; ++j)
+          bw1[j] = C::WP ? unpack_lo(wraw[j].z, wraw[j].w)
+                         : v4i{(int)wraw1[j].x, (int)wraw1[j].y, (int)wraw1[j].z, (int)wraw1[j].w};
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < C::FJ; ++j)
+        acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kk == 0 ? bw0[j] : bw1[j], af, acc[j][i], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // any DMA instructions not yet issued (only if NDMA > NQ / 2)
+    if (dma) {
+#pragma unroll
+      for (int t = NQ / 2; t < NDMA; ++t) issue_one(kt + NS - 1, t);
     }
   }
 
   // ---- epilogue: lane holds out[m][n .. n+3] for each (i, j) --------------
-  float swv[C::FJ][4];
-  float addv[C::FJ][4];   // bias
-  float gatev[C::FJ][4];
 #pragma unroll
   for (int j = 0; j < C::FJ; ++j) {
-    int64_t n = n0 + wn * C::WN + j * 16 + lg * 4;
-    if (n > p.N - 4) n = p.N - 4;   // columns past N are never stored
+    const int64_t n = n0 + wn * C::WN + j * 16 + lg * 4;
+    if (n >= p.N) continue;
+    float swv[4], addv[4], gatev[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      swv[j][r] = EPI == EPI_I32 ? 0.f : p.sw[(n + r) * p.sw_stride];
-      addv[j][r] = p.bias ? bf16_to_f32(p.bias[n + r]) : 0.f;
-      gatev[j][r] = EPI == EPI_GATED ? bf16_to_f32(p.gate[n + r]) : 0.f;
+      swv[r] = EPI == EPI_I32 ? 0.f : p.sw[(n + r) * p.sw_stride];
+      addv[r] = p.bias ? bf16_to_f32(p.bias[n + r]) : 0.f;
+      gatev[r] = EPI == EPI_GATED ? bf16_to_f32(p.gate[n + r]) : 0.f;
     }
-  }
 #pragma unroll
-  for (int i = 0; i < C::FI; ++i) {
-    const int64_t m = m0 + wm * C::WM + i * 16 + l16;
-    if (m >= p.M) continue;
-    const float sam = (EPI == EPI_I32) ? 0.f : p.sa[m * p.sa_stride] * p.post;
-#pragma unroll
-    for (int j = 0; j < C::FJ; ++j) {
-      const int64_t n = n0 + wn * C::WN + j * 16 + lg * 4;
-      if (n >= p.N) continue;
+    for (int i = 0; i < C::FI; ++i) {
+      const int64_t m = m0 + wm * C::WM + i * 16 + l16;
+      if (m >= p.M) continue;
       const v4i a4 = acc[j][i];
       if (EPI == EPI_I32) {
         int4 o;
@@ -294,9 +325,10 @@ __global__ __launch_bounds__(NT, 1) void qgemm_pipe_kernel(PArgs p) {
         *reinterpret_cast<int4*>(static_cast<int32_t*>(p.out) + m * p.ldo + n) = o;
         continue;
       }
+      const float sam = p.sa[m * p.sa_stride] * p.post;
       float y[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) y[r] = (float)a4[r] * sam * swv[j][r] + addv[j][r];
+      for (int r = 0; r < 4; ++r) y[r] = (float)a4[r] * sam * swv[r] + addv[r];
       if (EPI == EPI_F32) {
         *reinterpret_cast<float4*>(static_cast<float*>(p.out) + m * p.ldo + n) =
             make_float4(y[0], y[1], y[2], y[3]);
@@ -304,10 +336,10 @@ __global__ __launch_bounds__(NT, 1) void qgemm_pipe_kernel(PArgs p) {
       }
       if (EPI == EPI_GATED) {
         const uint2 rr = *reinterpret_cast<const uint2*>(p.residual + m * p.ldo + n);
-        y[0] = __builtin_fmaf(gatev[j][0], y[0], bf16_to_f32(rr.x & 0xffff));
-        y[1] = __builtin_fmaf(gatev[j][1], y[1], bf16_to_f32(rr.x >> 16));
-        y[2] = __builtin_fmaf(gatev[j][2], y[2], bf16_to_f32(rr.y & 0xffff));
-        y[3] = __builtin_fmaf(gatev[j][3], y[3], bf16_to_f32(rr.y >> 16));
+        y[0] = __builtin_fmaf(gatev[0], y[0], bf16_to_f32(rr.x & 0xffff));
+        y[1] = __builtin_fmaf(gatev[1], y[1], bf16_to_f32(rr.x >> 16));
+        y[2] = __builtin_fmaf(gatev[2], y[2], bf16_to_f32(rr.y & 0xffff));
+        y[3] = __builtin_fmaf(gatev[3], y[3], bf16_to_f32(rr.y >> 16));
       }
       const bf2 h0 = __builtin_convertvector(f2{y[0], y[1]}, bf2);
       const bf2 h1 = __builtin_convertvector(f2{y[2], y[3]}, bf2);
@@ -323,7 +355,7 @@ hipError_t launch_pipe(PArgs p, hipStream_t s) {
   p.tiles_n = (int)((p.N + C::BN - 1) / C::BN);
   p.group_m = 4;
   const int nb = p.tiles_m * p.tiles_n;
-  hipLaunchKernelGGL((qgemm_pipe_kernel<C, EPI>), dim3(nb), dim3(NT), 0, s, p);
+  hipLaunchKernelGGL((qgemm_pipe_kernel<C, EPI>), dim3(nb), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
 
@@ -362,10 +394,10 @@ int launch_qgemm_pipe(const GemmArgs& g, hipStream_t s) {
   p.shift = 4 * npacked;
   hipError_t e;
   if (g.w_packed) {
-    if (g.a_packed) e = launch_epi<Cfg<256, 320, true, true>>(p, g.epilogue, s);
-    else e = launch_epi<Cfg<256, 320, false, true>>(p, g.epilogue, s);
+    if (g.a_packed) e = launch_epi<Cfg<256, 320, 2, 4, true, true>>(p, g.epilogue, s);
+    else e = launch_epi<Cfg<256, 320, 2, 4, false, true>>(p, g.epilogue, s);
   } else {
-    e = launch_epi<Cfg<256, 256, false, false>>(p, g.epilogue, s);
+    e = launch_epi<Cfg<256, 256, 2, 4, false, false>>(p, g.epilogue, s);
   }
   return e == hipSuccess ? OK : ERR_LAUNCH;
 }
