@@ -1,21 +1,33 @@
 """Benchmark of the rotated low-bit quantized linear on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--workload attn_proj_w4a4|ffdown_w8a8|svdq_gateup|stack]
 
-Workload: one DiT attention projection at 1024x1024 -- X bf16 [4096 x 5120]
-~ N(0,1) with 1% outlier channels x30, W [5120 x 5120] ~ N(0, 0.02) packed
-int4 with the group-256 rotation, per-token activation / per-output-channel
-weight scales, bf16 out.  Inputs and packed weights are resident in HBM
-before timing.  One step = the layer's online path: rotate + quantize the
-activations (rotate_quantize_act), then the W4A4 GEMM with its dequant
-epilogue (qgemm_w4a4).  Weight packing is offline and timed separately.
+Default workload (the headline line): one DiT attention projection at
+1024x1024 -- X bf16 [4096 x 5120] ~ N(0,1) with 1% outlier channels x30,
+W [5120 x 5120] ~ N(0, 0.02) packed int4 with the group-256 rotation,
+per-token activation / per-output-channel weight scales, bf16 out.
 
-Prints ONE JSON line.  `value` is the effective integer throughput of a
-whole step, 2*M*N*K / step time, in TOP/s (eager launches, K steps between
-two synchronizations).  `roofline` describes the GEMM kernel (the dominant
-kernel): its average duration is measured inside the timed region with HIP
-events that bracket each GEMM launch on the stream it runs on.
-`cpu_baseline` times the CPU oracle on a bounded row sample.
+Other workloads (separate runs, same JSON shape):
+  ffdown_w8a8   W8A8 ff.down, X [4096 x 20480] post-SwiGLU-like, W int8 per
+                row [5120 x 20480], gated residual onto bf16 [4096 x 5120]
+  svdq_gateup   group-64 W4A4 gate|up [40960 x 5120] + bf16 rank-32
+                low-rank branch, SwiGLU out [4096 x 20480]
+  stack         the 224 linears of a 28-block DiT at 2048x2048 (16384
+                tokens): 128 W4A4 + 96 W8A8, every activation resident
+
+Inputs and prepared weights are resident in HBM before timing.  One step is
+the layer's online path: rotate + quantize the activations
+(rotate_quantize_act, which also forms X @ L1 for the low-rank branch), then
+the quantized GEMM with its fused epilogue.  Weight preparation (rotation,
+quantization, int4 packing) is offline and timed separately.
+
+Prints ONE JSON line.  `value` is the effective integer throughput of a whole
+step, 2*M*N*K / step time, in TOP/s (eager launches, K steps between two
+synchronizations).  `roofline` describes the GEMM kernel (the dominant
+kernel): its average duration comes from HIP events that bracket each launch
+on the stream the kernels run on, inside the timed region.  `cpu_baseline`
+times the CPU oracle on a bounded sample of the same workload.
 
 Profiling helpers (used to make the summaries under profiles/):
     --calib-copy            also run a plain 256 MiB device copy (a kernel of
@@ -46,15 +58,28 @@ if ROOT not in sys.path:
 
 INT8_MFMA_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POP/s
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemm_w4a4_4096x5120x5120_traffic.json")
-GEMM_SOURCES = ["rotated_bit_quantized_rotate_amd/csrc/qgemm_pipe.hip"]
 CALIB_BYTES = 256 << 20
+CSRC = "rotated_bit_quantized_rotate_amd/csrc/"
+HEADLINE_METRIC = "effective int TOPS + % int8 MFMA peak, W4A4 rotated GEMM M=4096 K=N=5120"
+
+# workload -> (GEMM kernel label, shape tag, sources whose text defines that kernel)
+GEMM_KERNELS = {
+    "attn_proj_w4a4": ("qgemm_w4a4", "4096x5120x5120", ["qgemm_pipe.hip"]),
+    "ffdown_w8a8": ("qgemm_w8a8", "4096x20480x5120", ["qgemm_pipe.hip"]),
+    "svdq_gateup": ("qgemm_w4a4_lowrank", "4096x5120x40960", ["qgemm.hip"]),
+    "stack": ("qgemm_stack", "224x16384", ["qgemm_pipe.hip"]),
+}
 
 
-def gemm_source_hash() -> str:
+def traffic_file(workload):
+    label, shape, _ = GEMM_KERNELS[workload]
+    return os.path.join(ROOT, "profiles", f"{label}_{shape}_traffic.json")
+
+
+def gemm_source_hash(workload="attn_proj_w4a4") -> str:
     h = hashlib.sha256()
-    for f in GEMM_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
+    for f in GEMM_KERNELS[workload][2]:
+        with open(os.path.join(ROOT, CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -62,65 +87,92 @@ def gemm_source_hash() -> str:
 def _parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=None,
+                   help="timed steps (default 200; 3 for the stack)")
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed warm-up steps (default 20; 1 for the stack)")
+    p.add_argument("--workload", default="attn_proj_w4a4", choices=sorted(GEMM_KERNELS))
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time of the oracle baseline sample")
     p.add_argument("--calib-copy", action="store_true")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
-    return p.parse_args()
+    a = p.parse_args()
+    stack = a.workload == "stack"
+    if a.steps is None:
+        a.steps = 3 if stack else 200
+    if a.warmup is None:
+        a.warmup = 1 if stack else 20
+    return a
+
+
+# ---------------------------------------------------------------- CPU oracle --
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return os.cpu_count() or 1
 
 
 def cpu_baseline(wl, target_s=12.0):
     """The oracle as it stands, on a row sample of X against the full weights
     (weights quantized beforehand, like the GPU step): rotate + quantize the
-    rows, exact integer product via float64 BLAS, dequant, bf16 rounding.
-    A 64-row probe sizes the sample to about `target_s` seconds."""
+    rows, exact integer product via float64 BLAS (per 64-group for group-64
+    scales), dequant, low-rank branch, epilogue, bf16 rounding.  A 64-row
+    probe sizes the sample to about `target_s` seconds; when the whole
+    workload takes less, it is run repeatedly and the total time is used."""
     import oracle as O
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    threads = _blas_threads()
     qw = O.quantize_weights(wl.w, wl.w_bits, wl.scale_mode)
+    res = O.bf16_bits_to_f64(wl.residual) if wl.residual is not None else None
+    gate = O.bf16_bits_to_f64(wl.gate) if wl.gate is not None else None
 
     def run(rows):
         xs = np.ascontiguousarray(wl.x[:rows])
         t0 = time.perf_counter()
         qa = O.quantize_activations(xs, wl.a_bits, wl.scale_mode)
-        y = O.linear_fp64(qa, qw)
-        O.f64_to_bf16_bits(y)
+        y = O.linear_fp64(qa, qw, xs, wl.l1, wl.l2)
+        out = O.epilogue(y, wl.epilogue, None if res is None else res[:rows], gate)
+        O.f64_to_bf16_bits(out)
         return time.perf_counter() - t0
 
     probe = run(64)
     rows = int(min(wl.M, max(64, 64 * target_s / max(probe, 1e-3))))
-    dt = run(rows)
-    ops = 2.0 * rows * wl.N * wl.K
-    return {"value": round(ops / dt / 1e12, 4), "unit": "TOP/s", "cores": int(threads),
+    reps = 1
+    if rows == wl.M:
+        first = run(rows)
+        reps = max(1, int(round((target_s - first) / max(first, 1e-3))))
+    t = sum(run(rows) for _ in range(reps))
+    ops = 2.0 * rows * wl.N * wl.K * reps
+    what = f"{rows} of {wl.M} rows of X" + (f", whole workload x{reps}" if rows == wl.M else "")
+    return {"value": round(ops / t / 1e12, 4), "unit": "TOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{rows} of {wl.M} rows of X against all {wl.N} outputs (weights "
-                      f"pre-quantized): rotate+quantize, exact integer GEMM via float64 BLAS, "
-                      f"dequant, bf16 rounding; {dt:.2f} s wall on {threads} BLAS threads"}
+            "sample": f"{what} against all {wl.N} outputs (weights pre-quantized): "
+                      f"rotate+quantize, exact integer GEMM via float64 BLAS, dequant, "
+                      f"{wl.epilogue} epilogue, bf16 rounding; {t:.2f} s wall on {threads} "
+                      f"BLAS threads"}
 
 
+# ------------------------------------------------------------ PMC traffic --
 def _read_pmc(dirname, counter):
-    """{kernel short name: [values]} from a rocprofv3 counter_collection.csv."""
+    """{kernel class: [values]} from a rocprofv3 counter_collection.csv."""
     out = {}
     for f in glob.glob(os.path.join(dirname, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] != counter:
                 continue
             name = r["Kernel_Name"]
-            key = ("qgemm" if "qgemm_pipe_kernel" in name else
+            key = ("qgemm" if "qgemm" in name else
                    "copy" if ("copyBuffer" in name or "copy" in name.lower()) else
                    re.sub(r"\(.*", "", name)[:40])
             out.setdefault(key, []).append(float(r["Counter_Value"]))
     return out
 
 
-def summarize_pmc(fetch_dir, write_dir):
+def summarize_pmc(fetch_dir, write_dir, workload):
     f = _read_pmc(fetch_dir, "FETCH_SIZE")
     w = _read_pmc(write_dir, "WRITE_SIZE")
     kib = 1024.0
@@ -130,35 +182,238 @@ def summarize_pmc(fetch_dir, write_dir):
     w_scale = CALIB_BYTES / copy_w
     gf = np.mean(f["qgemm"]) * kib * f_scale
     gw = np.mean(w["qgemm"]) * kib * w_scale
-    rec = {"kernel": "qgemm_w4a4 (qgemm_pipe_kernel 256x320)", "workload": "M=4096 N=5120 K=5120",
+    label, shape, _ = GEMM_KERNELS[workload]
+    rec = {"kernel": label, "workload": shape,
            "fetch_bytes_per_launch": int(gf), "write_bytes_per_launch": int(gw),
            "bytes_per_launch": int(gf + gw),
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
            "copy_kib_fetch": round(copy_f / kib, 1), "copy_kib_write": round(copy_w / kib, 1),
-           "gemm_source_hash": gemm_source_hash(),
+           "gemm_source_hash": gemm_source_hash(workload),
            "n_dispatches": [len(f["qgemm"]), len(w["qgemm"])]}
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as fh:
+    path = traffic_file(workload)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec))
 
 
-def load_traffic():
-    if not os.path.exists(TRAFFIC_FILE):
+def load_traffic(workload):
+    path = traffic_file(workload)
+    if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(path))
     except Exception:
         return None
-    if rec.get("gemm_source_hash") != gemm_source_hash():
+    if rec.get("gemm_source_hash") != gemm_source_hash(workload):
         return None                      # the kernel changed since the counters were taken
     return rec.get("bytes_per_launch")
 
 
+# -------------------------------------------------------------- workloads --
+class Case:
+    """One benchmark workload: prepared device tensors and the launches of a
+    step, in order, each tagged "prologue" or "gemm"."""
+
+    def __init__(self):
+        self.launches = []        # [(tag, fn)]
+        self.ops = 0              # 2*M*N*K summed over the step's GEMMs
+        self.gemm_bytes = 0       # algorithmic HBM bytes of the step's GEMMs
+        self.pro_bytes = 0        # algorithmic HBM bytes of the step's prologues
+        self.gemm_launches = 0
+        self.prep_ms = 0.0
+        self.metric = ""
+        self.config = {}
+        self.dtype = ""
+        self.wl = None            # host workload for the CPU baseline
+
+
+def _bf16_dev(bits, dev):
+    import torch
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def _timed_prep(fn):
+    import torch
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def case_attn(Q, W, dev):
+    import torch
+    wl = W.attn_proj_w4a4()
+    M, N, K = wl.M, wl.N, wl.K
+    x, w = _bf16_dev(wl.x, dev), _bf16_dev(wl.w, dev)
+    codes = torch.empty((M, K), dtype=torch.int8, device=dev)
+    sa = torch.empty((M,), dtype=torch.float32, device=dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    wq = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    sw = torch.empty((N,), dtype=torch.float32, device=dev)
+    c = Case()
+    c.prep_ms = _timed_prep(lambda: Q.pack_weight_int4(w, packed=wq, scales=sw))
+    c.launches = [
+        ("prologue", lambda: Q.rotate_quantize_act(x, bits=4, scale_mode="row", codes=codes, scales=sa)),
+        ("gemm", lambda: Q.qgemm_w4a4(codes, sa, wq, sw, K, out=out)),
+    ]
+    c.ops = wl.int_ops
+    c.gemm_launches = 1
+    c.pro_bytes = M * K * 2 + M * K + M * 4
+    c.gemm_bytes = M * K + N * K // 2 + M * 4 + N * 4 + M * N * 2
+    c.metric = HEADLINE_METRIC
+    c.dtype = "int8 MFMA (int4 codes), int32 accumulate, bf16 out"
+    c.config = {"workload": "W4A4 rotated linear, DiT attention projection at 1024^2: "
+                            "X bf16 [4096x5120] N(0,1) + 1% outlier channels x30, "
+                            "W [5120x5120] packed int4, group-256 Hadamard, per-token / "
+                            "per-row scales, bf16 out",
+                "M": M, "N": N, "K": K, "global_batch": M, "parallelism": "single GPU"}
+    c.wl = wl
+    return c
+
+
+def case_ffdown(Q, W, dev):
+    import torch
+    wl = W.ffdown_w8a8()
+    M, N, K = wl.M, wl.N, wl.K
+    x, w = _bf16_dev(wl.x, dev), _bf16_dev(wl.w, dev)
+    res, gate = _bf16_dev(wl.residual, dev), _bf16_dev(wl.gate, dev)
+    codes = torch.empty((M, K), dtype=torch.int8, device=dev)
+    sa = torch.empty((M,), dtype=torch.float32, device=dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    wq = torch.empty((N, K), dtype=torch.int8, device=dev)
+    sw = torch.empty((N,), dtype=torch.float32, device=dev)
+    c = Case()
+    c.prep_ms = _timed_prep(lambda: Q.rotate_quantize_act(w, bits=8, scale_mode="row", codes=wq,
+                                                          scales=sw))
+    c.launches = [
+        ("prologue", lambda: Q.rotate_quantize_act(x, bits=8, scale_mode="row", codes=codes, scales=sa)),
+        ("gemm", lambda: Q.qgemm_w8a8(codes, sa, wq, sw, residual=res, gate=gate,
+                                      epilogue="gated_residual", out=out)),
+    ]
+    c.ops = wl.int_ops
+    c.gemm_launches = 1
+    c.pro_bytes = M * K * 2 + M * K + M * 4
+    c.gemm_bytes = M * K + N * K + M * 4 + N * 4 + N * 2 + 2 * M * N * 2
+    c.metric = ("effective int TOPS + % int8 MFMA peak, W8A8 rotated GEMM + gated residual "
+                "M=4096 K=20480 N=5120")
+    c.dtype = "int8 MFMA, int32 accumulate, bf16 out"
+    c.config = {"workload": "W8A8 protected ff.down: X bf16 [4096x20480] = silu(a)*b, W int8 per-row "
+                            "[5120x20480], group-256 Hadamard, per-token int8, gated residual onto "
+                            "bf16 [4096x5120]",
+                "M": M, "N": N, "K": K, "global_batch": M, "parallelism": "single GPU"}
+    c.wl = wl
+    return c
+
+
+def case_svdq(Q, W, dev):
+    import torch
+    wl = W.svdq_gateup()
+    M, N, K = wl.M, wl.N, wl.K
+    r = wl.l1.shape[1]
+    x, w = _bf16_dev(wl.x, dev), _bf16_dev(wl.w, dev)
+    l1, l2 = _bf16_dev(wl.l1, dev), _bf16_dev(wl.l2, dev)
+    codes = torch.empty((M, K), dtype=torch.int8, device=dev)
+    sa = torch.empty((M, K // 64), dtype=torch.float32, device=dev)
+    lr = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((M, N // 2), dtype=torch.bfloat16, device=dev)
+    wq = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    sw = torch.empty((N, K // 64), dtype=torch.float32, device=dev)
+    c = Case()
+    c.prep_ms = _timed_prep(lambda: Q.pack_weight_int4(w, scale_mode="group64", packed=wq, scales=sw))
+    c.launches = [
+        ("prologue", lambda: Q.rotate_quantize_act(x, bits=4, scale_mode="group64", codes=codes,
+                                                   scales=sa, l1=l1, lr=lr)),
+        ("gemm", lambda: Q.qgemm_w4a4_lowrank(codes, sa, wq, sw, K, lr=lr, l2=l2, epilogue="swiglu",
+                                              out=out)),
+    ]
+    c.ops = wl.int_ops
+    c.gemm_launches = 1
+    c.pro_bytes = M * K * 2 + K * r * 2 + M * K + M * (K // 64) * 4 + M * r * 2
+    c.gemm_bytes = (M * K + N * K // 2 + M * (K // 64) * 4 + N * (K // 64) * 4 + M * r * 2
+                    + r * N * 2 + M * (N // 2) * 2)
+    c.metric = ("effective int TOPS + % int8 MFMA peak, group-64 W4A4 GEMM + rank-32 low-rank + SwiGLU "
+                "M=4096 K=5120 N=40960")
+    c.dtype = "int8 MFMA (int4 codes), int32 per-64 partials, fp32 rescale, bf16 out"
+    c.config = {"workload": "SVDQuant fused gate|up: X bf16 [4096x5120], W int4 group-64 [40960x5120], "
+                            "bf16 rank-32 L1 [5120x32] / L2 [32x40960], SwiGLU -> bf16 [4096x20480]",
+                "M": M, "N": N, "K": K, "rank": r, "global_batch": M, "parallelism": "single GPU"}
+    c.wl = wl
+    return c
+
+
+def case_stack(Q, W, dev):
+    """224 linears of the 28-block stack at 2048^2.  Activations for every
+    layer are drawn on the device (torch generator seeded 2l+1, N(0,1)) and
+    kept resident; weights (seeded 2l, N(0,0.02)) are prepared offline and the
+    bf16 copies freed.  One codes buffer and one output buffer are reused."""
+    import torch
+    M = 16384
+    layers = W.stack_layers()
+    g = torch.Generator(device=dev)
+    maxk = max(k for _, _, _, k, _ in layers)
+    maxn = max(n for _, _, n, _, _ in layers)
+    codes = torch.empty((M * maxk,), dtype=torch.int8, device=dev)
+    sa = torch.empty((M,), dtype=torch.float32, device=dev)
+    out = torch.empty((M * maxn,), dtype=torch.bfloat16, device=dev)
+    c = Case()
+    prep = 0.0
+    n4 = 0
+    for li, (b, name, n, k, bits) in enumerate(layers):
+        g.manual_seed(2 * li)
+        w = (torch.randn((n, k), generator=g, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+        g.manual_seed(2 * li + 1)
+        x = torch.randn((M, k), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        sw = torch.empty((n,), dtype=torch.float32, device=dev)
+        cd = codes[: M * k].view(M, k)
+        o = out[: M * n].view(M, n)
+        if bits == 4:
+            wq = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+            prep += _timed_prep(lambda: Q.pack_weight_int4(w, packed=wq, scales=sw))
+            c.launches.append(("prologue", lambda x=x, cd=cd: Q.rotate_quantize_act(
+                x, bits=4, scale_mode="row", codes=cd, scales=sa)))
+            c.launches.append(("gemm", lambda cd=cd, wq=wq, sw=sw, o=o, k=k: Q.qgemm_w4a4(
+                cd, sa, wq, sw, k, out=o)))
+            c.gemm_bytes += M * k + n * k // 2
+            n4 += 1
+        else:
+            wq = torch.empty((n, k), dtype=torch.int8, device=dev)
+            prep += _timed_prep(lambda: Q.rotate_quantize_act(w, bits=8, scale_mode="row", codes=wq,
+                                                              scales=sw))
+            c.launches.append(("prologue", lambda x=x, cd=cd: Q.rotate_quantize_act(
+                x, bits=8, scale_mode="row", codes=cd, scales=sa)))
+            c.launches.append(("gemm", lambda cd=cd, wq=wq, sw=sw, o=o: Q.qgemm_w8a8(
+                cd, sa, wq, sw, out=o)))
+            c.gemm_bytes += M * k + n * k
+        del w
+        c.ops += 2 * M * n * k
+        c.pro_bytes += M * k * 2 + M * k + M * 4
+        c.gemm_bytes += M * 4 + n * 4 + M * n * 2
+        c.gemm_launches += 1
+    torch.cuda.synchronize()
+    c.prep_ms = prep
+    c.metric = ("effective int TOPS + % int8 MFMA peak, mixed 224-linear DiT stack at 2048^2 "
+                "(16384 tokens, 128 W4A4 + 96 W8A8)")
+    c.dtype = "int8 MFMA (int4/int8 codes), int32 accumulate, bf16 out"
+    c.config = {"workload": "28-block DiT linear stack at 2048^2: 16384 tokens, d=5120, ffn=20480, "
+                            f"{len(layers)} linears ({n4} W4A4, {len(layers) - n4} W8A8), per-token / "
+                            "per-row scales, group-256 Hadamard, bf16 out, every activation resident",
+                "M": M, "layers": len(layers), "global_batch": M, "parallelism": "single GPU"}
+    return c
+
+
+CASES = {"attn_proj_w4a4": case_attn, "ffdown_w8a8": case_ffdown, "svdq_gateup": case_svdq,
+         "stack": case_stack}
+
+
+# ------------------------------------------------------------------- main --
 def main():
     args = _parse()
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc)
+        summarize_pmc(*args.summarize_pmc, args.workload)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
@@ -175,87 +430,66 @@ def main():
     if not Q.device_supported(0):
         raise SystemExit("device 0 is not gfx950")
 
-    wl = W.attn_proj_w4a4()
-    M, N, K = wl.M, wl.N, wl.K
+    case = CASES[args.workload](Q, W, dev)
+    L = len(case.launches)
 
-    def to_dev_bf16(bits):
-        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
-
-    x = to_dev_bf16(wl.x)
-    w = to_dev_bf16(wl.w)
-    codes = torch.empty((M, K), dtype=torch.int8, device=dev)
-    sa = torch.empty((M,), dtype=torch.float32, device=dev)
-    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-
-    # offline weight preparation (not part of a step)
-    wq = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
-    sw = torch.empty((N,), dtype=torch.float32, device=dev)
-    Q.pack_weight_int4(w, packed=wq, scales=sw)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(10):
-        Q.pack_weight_int4(w, packed=wq, scales=sw)
-    e1.record()
-    torch.cuda.synchronize()
-    pack_ms = e0.elapsed_time(e1) / 10
-
-    def prologue():
-        Q.rotate_quantize_act(x, bits=4, scale_mode="row", codes=codes, scales=sa)
-
-    def gemm():
-        Q.qgemm_w4a4(codes, sa, wq, sw, K, out=out)
+    def step():
+        for _, fn in case.launches:
+            fn()
 
     for _ in range(args.warmup):
-        prologue()
-        gemm()
+        step()
     torch.cuda.synchronize()
 
     # ---- timed region: exactly `steps` steps, synchronized on both sides.
-    # Events bracket the prologue and the GEMM of every step on the stream
-    # the kernels run on (the current torch stream).
+    # An event follows every launch, on the stream the kernels run on (the
+    # current torch stream), so each kernel's duration is the gap between
+    # the event before it and the event after it.
     n = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * n + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(L * n + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev[0].record()
     for s in range(n):
-        prologue()
-        ev[3 * s + 1].record()
-        gemm()
-        ev[3 * s + 2].record()
-        ev[3 * s + 3].record()
+        for i, (_, fn) in enumerate(case.launches):
+            fn()
+            ev[s * L + i + 1].record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
-    step_ms = ev[0].elapsed_time(ev[3 * n]) / n
-    gemm_ms = float(np.mean([ev[3 * s + 1].elapsed_time(ev[3 * s + 2]) for s in range(n)]))
-    pro_ms = float(np.mean([(ev[3 * s].elapsed_time(ev[3 * s + 1])) for s in range(n)]))
+    step_ms = ev[0].elapsed_time(ev[L * n]) / n
+    t_tag = {"prologue": 0.0, "gemm": 0.0}
+    for s in range(n):
+        for i, (tag, _) in enumerate(case.launches):
+            t_tag[tag] += ev[s * L + i].elapsed_time(ev[s * L + i + 1])
+    gemm_ms = t_tag["gemm"] / n            # GEMM time per step
+    pro_ms = t_tag["prologue"] / n
+    gemm_launch_ms = gemm_ms / case.gemm_launches
 
     # ---- the same step replayed from a HIP graph (no host launch cost)
     graph_step_ms = None
-    try:
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            prologue()
-            gemm()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            prologue()
-            gemm()
-        for _ in range(5):
-            g.replay()
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(n):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        graph_step_ms = e0.elapsed_time(e1) / n
-    except Exception as exc:  # graph capture is an extra figure only
-        print(f"graph replay skipped: {exc}", file=sys.stderr)
+    if not args.no_graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                step()
+            for _ in range(2):
+                g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            graph_step_ms = e0.elapsed_time(e1) / n
+        except Exception as exc:  # graph capture is an extra figure only
+            print(f"graph replay skipped: {exc}", file=sys.stderr)
 
     if args.calib_copy:
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev).fill_(1)
@@ -264,14 +498,13 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    ops = 2.0 * M * N * K
+    ops = float(case.ops)
     value = ops / (step_ms * 1e-3) / 1e12
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
-    pro_bytes = M * K * 2 + M * K + M * 4          # bf16 in, int8 codes + scales out
-    gemm_bytes = M * K + N * K // 2 + M * 4 + N * 4 + M * N * 2
-
+    label = GEMM_KERNELS[args.workload][0]
+    traffic = load_traffic(args.workload)
     rec = {
-        "metric": "effective int TOPS + % int8 MFMA peak, W4A4 rotated GEMM M=4096 K=N=5120",
+        "metric": case.metric,
         "value": round(value, 2),
         "unit": "TOP/s",
         "n_gpus": 1,
@@ -281,30 +514,30 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8 MFMA (int4 codes), int32 accumulate, bf16 out",
+        "dtype": case.dtype,
         "data": "synthetic",
-        "config": {"workload": "W4A4 rotated linear, DiT attention projection at 1024^2: "
-                               "X bf16 [4096x5120] N(0,1) + 1% outlier channels x30, "
-                               "W [5120x5120] packed int4, group-256 Hadamard, per-token / "
-                               "per-row scales, bf16 out",
-                   "M": M, "N": N, "K": K, "global_batch": M, "parallelism": "single GPU"},
+        "config": case.config,
         "pct_int8_peak_step": round(100.0 * value / INT8_MFMA_PEAK_TOPS, 2),
-        "gemm_only": {"ms": round(gemm_ms, 5), "tops": round(gemm_tops, 2),
-                      "pct_int8_peak": round(100.0 * gemm_tops / INT8_MFMA_PEAK_TOPS, 2)},
+        "gemm_only": {"ms": round(gemm_ms, 5), "ms_per_launch": round(gemm_launch_ms, 5),
+                      "tops": round(gemm_tops, 2),
+                      "pct_int8_peak": round(100.0 * gemm_tops / INT8_MFMA_PEAK_TOPS, 2),
+                      "gbs": round(case.gemm_bytes / (gemm_ms * 1e-3) / 1e9, 1)},
         "prologue": {"ms": round(pro_ms, 5),
-                     "gbs": round(pro_bytes / (pro_ms * 1e-3) / 1e9, 1),
-                     "pct_hbm_peak": round(100.0 * pro_bytes / (pro_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)},
+                     "gbs": round(case.pro_bytes / (pro_ms * 1e-3) / 1e9, 1),
+                     "pct_hbm_peak": round(100.0 * case.pro_bytes / (pro_ms * 1e-3) / 1e9
+                                           / HBM_PEAK_GBS, 2)},
         "graph_step_ms": None if graph_step_ms is None else round(graph_step_ms, 5),
         "graph_step_tops": None if graph_step_ms is None else round(ops / (graph_step_ms * 1e-3) / 1e12, 2),
-        "weight_prep_ms": round(pack_ms, 5),
+        "weight_prep_ms": round(case.prep_ms, 5),
         "wall_ms_timed_region": round(wall_ms, 3),
-        "roofline": {"bound": "mfma", "kernel": "qgemm_w4a4",
+        "roofline": {"bound": "mfma", "kernel": label,
                      "achieved": round(gemm_tops, 2), "peak": INT8_MFMA_PEAK_TOPS,
                      "unit": "TOP/s", "frac": round(gemm_tops / INT8_MFMA_PEAK_TOPS, 4),
-                     "traffic": load_traffic(), "algorithmic_bytes": gemm_bytes},
+                     "traffic": traffic,
+                     "algorithmic_bytes": int(case.gemm_bytes // case.gemm_launches)},
     }
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    if not args.no_cpu_baseline and case.wl is not None:
+        rec["cpu_baseline"] = cpu_baseline(case.wl, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
 
 

@@ -2,8 +2,7 @@
 
 The computation lives in libqlinear.so (hand-written HIP kernels behind the C
 ABI declared in include/qlinear.h); this package is its thin Python binding
-(``_lib``) plus the in-tree build script (``build``) and a small layer helper
-(``linear``).
+(``_lib``) plus the in-tree build script (``build``).
 """
 
 from ._lib import (  # noqa: F401
