@@ -66,7 +66,7 @@ HEADLINE_METRIC = "effective int TOPS + % int8 MFMA peak, W4A4 rotated GEMM M=40
 GEMM_KERNELS = {
     "attn_proj_w4a4": ("qgemm_w4a4", "4096x5120x5120", ["qgemm_pipe.hip"]),
     "ffdown_w8a8": ("qgemm_w8a8", "4096x20480x5120", ["qgemm_pipe.hip"]),
-    "svdq_gateup": ("qgemm_w4a4_lowrank", "4096x5120x40960", ["qgemm.hip"]),
+    "svdq_gateup": ("qgemm_w4a4_lowrank", "4096x5120x40960", ["qgemm_pipe.hip"]),
     "stack": ("qgemm_stack", "224x16384", ["qgemm_pipe.hip"]),
 }
 

@@ -1,31 +1,53 @@
-// Large-tile integer GEMM for the rotated low-bit linear on gfx950:
-// exact int32 accumulation on int8 MFMA with tensor / row scales and the
-// plain, f32, int32 and gated-residual epilogues (model card "Krea 2 Turbo
-// OrbitQuant W4A4", section "Fused transformer (OrbitQuant 0.11)": W4A4
-// GEMMs, and W8A8 for ff.down with the gated residual in the epilogue).
+// Integer GEMM of the rotated low-bit linear on gfx950: exact int32
+// accumulation on int8 MFMA, then the dequantize epilogue.
+//
+//   acc[m, n] = sum_k qa[m, k] * qw[n, k]                 (exact, int32)
+//   y[m, n]   = acc * s_a * s_w                   (tensor / row scales)
+//             = sum_g acc_g * s_a[m,g] * s_w[n,g]   (group-64 scales: exact
+//                                     int32 partial per group, fp32 sum)
+//   (+ bias[n]) (+ sum_r lr[m,r] * L2[r,n])  -> epilogue -> out
+//
+// Epilogues: bf16, f32, int32 (debug), gated residual res + gate[n] * y,
+// SwiGLU silu(y_gate) * y_up over a gate|up weight.  (Model card "Krea 2
+// Turbo OrbitQuant W4A4", section "Fused transformer (OrbitQuant 0.11)":
+// W4A4 GEMMs with SwiGLU and gated residuals in their epilogues, W8A8 for
+// ff.down; README "Krea-2-SVDQuant-ComfyUI", sections "Why this exists" and
+// "Low-rank refinement": a low-rank branch on top of the W4A4 kernel; model
+// card "Krea 2 Turbo Nunchaku Lite INT4 r32": group size 64, rank 32.)
 //
 // Design (MI355X: 256 CUs in 8 XCDs, 160 KB LDS per CU):
 //  * one 512-thread workgroup (8 waves, 2 x 4) per BM x BN output tile; with
 //    256 x 320 tiles a 4096 x 5120 output is exactly 256 tiles, one per CU;
-//  * K is staged through LDS 128 channels at a time in a 3-deep ring filled
-//    by direct global->LDS loads (global_load_lds_dwordx4): no staging
-//    registers, and the loads of stage s+2 overlap the MFMAs of stage s;
-//    one barrier per stage;
+//  * K is staged through LDS 128 channels at a time in a ring of 2-3 stages
+//    filled by direct global->LDS loads (global_load_lds): no staging
+//    registers, and the loads of later stages overlap the MFMAs of the
+//    current one; one barrier per stage.  Group-64 scales of the stage's two
+//    groups ride in the same ring (4-byte loads, gathered into the order
+//    the lanes read them);
 //  * 16-byte chunks are XOR-swizzled by row so every fragment read
 //    (ds_read_b128) hits distinct banks;
 //  * the MFMA is v_mfma_i32_16x16x64_i8 with the weight fragment as the
 //    first operand, so the accumulator lane layout holds 4 consecutive
 //    output columns of one row (8-byte bf16 stores in the epilogue);
-//  * INT4 weights are unpacked in registers: for a packed dword p,
+//  * INT4 codes are unpacked in registers: for a packed dword p,
 //    (p << 4) & 0xF0F0F0F0 and p & 0xF0F0F0F0 are four int8 lanes holding
 //    16 * (low nibble) and 16 * (high nibble); with the library's packed
-//    order they come out in channel order.  The factor 16 is removed exactly
-//    in the epilogue.
-//  * K-slice map: lane group g = lane / 16 owns channels [32g, 32g + 32) of
-//    each 128-channel stage, split over two MFMAs (kk = 0, 1) of 16 channels.
-//    In the packed layout those 32 channels are the 16 contiguous bytes
-//    [16g, 16g + 16), so one b128 read feeds both MFMAs.  Both operands use
-//    the same map, so the channel pairing is exact.
+//    order they come out in channel order.  The factor 16 per packed operand
+//    is removed exactly in the epilogue;
+//  * K-slice map (tensor / row scales): lane group g = lane / 16 owns
+//    channels [32g, 32g + 32) of each 128-channel stage, split over two
+//    MFMAs (kk = 0, 1) of 16 channels each.  In the packed layout those 32
+//    channels are the 16 contiguous bytes [16g, 16g + 16), so one b128 read
+//    feeds both MFMAs.  Both operands use the same map, so the channel
+//    pairing is exact;
+//  * K-slice map (group-64 scales): MFMA kk must cover exactly the stage's
+//    64-channel group kk, so lane group g takes channels 64 kk + 16 g +
+//    [0, 16) (packed: 8 bytes, one b64 read per MFMA).  Every MFMA starts
+//    from zero, its int32 result is that group's exact partial, and it is
+//    converted and added into an fp32 accumulator with s_a[m,g] * s_w[n,g];
+//  * SwiGLU: the W tile of a workgroup holds, per wave column, 32 gate rows
+//    f and the 32 matching up rows F + f, so a lane holds gate and up of the
+//    same outputs;
 //  * workgroup ids are remapped so the tiles one XCD runs form a compact
 //    block of the tile grid (shared A / W panels hit that XCD's L2).
 
@@ -68,25 +90,30 @@ struct PArgs {
   const float* sa;
   const float* sw;
   int64_t M, N, K;
-  int sa_stride, sw_stride;
+  int sa_stride, sw_stride;  // tensor / row scales: 0 or 1
+  int kg;                    // group-64 scales: K / 64 per row
   const uint16_t* bias;
   const uint16_t* residual;
   const uint16_t* gate;
+  const uint16_t* lr;        // [M, rank]
+  const uint16_t* l2;        // [rank, N]
+  int rank;
   void* out;
   int64_t ldo;
-  float post;
-  int shift;
+  float post;      // 1/16 per packed operand
+  int shift;       // 4 per packed operand (int32 output)
   int tiles_m, tiles_n;
   int group_m;     // tile rows per L2 group
+  int64_t half_n;  // SwiGLU: F = N / 2
 };
 
-template <int BM_, int BN_, int WGM_, int WGN_, bool AP_, bool WP_>
+template <int BM_, int BN_, int WGM_, int WGN_, bool AP_, bool WP_, bool GROUP_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int WGM = WGM_, WGN = WGN_;   // wave grid
   static constexpr int NW = WGM * WGN;           // waves per workgroup
   static constexpr int NT = 64 * NW;
-  static constexpr bool AP = AP_, WP = WP_;
+  static constexpr bool AP = AP_, WP = WP_, GROUP = GROUP_;
   static constexpr int WM = BM / WGM;       // wave tile rows
   static constexpr int WN = BN / WGN;       // wave tile cols
   static constexpr int FI = WM / 16;
@@ -95,48 +122,62 @@ struct Cfg {
   static constexpr int WRB = WP ? BK / 2 : BK;
   static constexpr int SA = BM * ARB;
   static constexpr int SW = BN * WRB;
-  static constexpr int STAGE = SA + SW;
-  static constexpr int A_INSTR = SA / 1024;  // 1 KB per DMA instruction
+  // two groups of fp32 scales, padded so every wave issues the same number
+  // of 256-byte loads
+  static constexpr int SC = GROUP ? (8 * (BM + BN) + 256 * NW - 1) / (256 * NW) * (256 * NW) : 0;
+  static constexpr int STAGE = SA + SW + SC;
+  static constexpr int A_INSTR = SA / 1024;  // 1 KB per 16-byte-per-lane load
   static constexpr int W_INSTR = SW / 1024;
+  static constexpr int S_INSTR = SC / 256;   // 256 B per 4-byte-per-lane load
   static_assert(SA % 1024 == 0 && SW % 1024 == 0, "stage must be whole KB");
-  static_assert(A_INSTR % NW == 0, "A DMA must split evenly over the waves");
+  static_assert(A_INSTR % NW == 0, "A loads must split evenly over the waves");
+  static_assert(S_INSTR % NW == 0, "scale loads must split evenly over the waves");
   static constexpr int A_PER_WAVE = A_INSTR / NW;
+  static constexpr int S_PER_WAVE = S_INSTR / NW;
   static constexpr int W_HI = (W_INSTR + NW - 1) / NW;  // waves < W_SPLIT issue W_HI
   static constexpr int W_SPLIT = W_INSTR - (W_HI - 1) * NW;
+  static constexpr int NDMA = A_PER_WAVE + W_HI + S_PER_WAVE;
   static constexpr int NSTAGE = (3 * STAGE <= kLdsBytes) ? 3 : 2;  // LDS ring depth
   static_assert(NSTAGE * STAGE <= kLdsBytes, "LDS ring too large");
-  static_assert((NSTAGE - 2) * (A_PER_WAVE + W_HI) < 64, "vmcnt range");
+  static_assert((NSTAGE - 2) * NDMA < 64, "vmcnt range");
+  static_assert(!GROUP || FI % 4 == 0, "group scales are read 4 rows at a time");
 };
 
 // Chunk position inside an LDS row of RB bytes: chunk c of row r lives at
 // c ^ f(r).  A fragment read (ds_read_b128) has 16 lanes on 16 consecutive
 // rows at one chunk index per lane group; these XOR patterns were measured
-// on gfx950 (bank-conflict counter) to serve every such read, for 128-byte
-// rows with chunk 2g + kk and 64-byte rows with chunk g, without bank
-// conflicts.  f depends only on r & 15.
-template <int RB>
+// on gfx950 (bank-conflict counter) to serve every such read without bank
+// conflicts: 128-byte rows read at chunk 2g + kk (GK = false) or 4 kk + g
+// (GK = true, the group-64 map), 64-byte rows at chunk g.  f depends only
+// on r & 15.
+template <int RB, bool GK>
 __device__ __forceinline__ int swz(int r, int c) {
-  if (RB == 128) return c ^ (((r & 3) << 1) | ((r >> 2) & 1));
+  if (RB == 128) return GK ? c ^ (r & 7) : c ^ (((r & 3) << 1) | ((r >> 2) & 1));
   return c ^ ((r >> 1) & 3);
 }
 
-// One DMA instruction q (1 KB) of an operand: lane i fills LDS chunk i of
-// that KB; rows are RB bytes.  Returns the global source for this lane.
-template <int RB>
-__device__ __forceinline__ const uint8_t* dma_src(const uint8_t* base, int64_t ld, int64_t row0,
-                                                  int64_t rows_valid, int q, int lane, int64_t kbyte) {
-  constexpr int CPR = RB / 16;
-  const int rl = q * (1024 / RB) + lane / CPR;  // row inside the tile
-  const int pos = lane % CPR;
-  const int c = swz<RB>(rl, pos);               // inverse of the XOR is itself
-  int64_t gr = row0 + rl;
-  if (gr > rows_valid - 1) gr = rows_valid - 1;
-  return base + gr * ld + kbyte + c * 16;
+// Weight row (row of W, of its scales and of L2's columns) held by W-tile
+// row t.  Plain: n0 + t.  SwiGLU (n0 = first output column f0 of the tile):
+// each wave column's WN rows are WN/2 gate rows f then the WN/2 up rows
+// F + f of the same outputs.  Rows past the end are clamped to the last row
+// (their results are never stored).
+template <class C, bool SWIG>
+__device__ __forceinline__ int64_t w_row_of(const PArgs& p, int64_t n0, int t) {
+  if (!SWIG) {
+    const int64_t r = n0 + t;
+    return r > p.N - 1 ? p.N - 1 : r;
+  }
+  constexpr int HW = C::WN / 2;
+  const int wv = t / C::WN, u = t % C::WN;
+  int64_t f = n0 + wv * HW + (u % HW);
+  if (f > p.half_n - 1) f = p.half_n - 1;
+  return (u >= HW ? p.half_n : 0) + f;
 }
 
-template <class C, int EPI>
+template <class C, int EPI, bool LOWRANK>
 __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
   constexpr int NS = C::NSTAGE;
+  constexpr bool SWIG = EPI == EPI_SWIGLU;
   __shared__ __attribute__((aligned(16))) uint8_t smem[NS * C::STAGE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -159,58 +200,117 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
   const int tile_m = first_m + inb % gm;
   const int tile_n = inb / gm;
   const int64_t m0 = (int64_t)tile_m * C::BM;
-  const int64_t n0 = (int64_t)tile_n * C::BN;
+  const int64_t n0 = (int64_t)tile_n * (SWIG ? C::BN / 2 : C::BN);
 
   const int64_t lda = C::AP ? p.K / 2 : p.K;
   const int64_t ldw = C::WP ? p.K / 2 : p.K;
   const int KT = (int)(p.K / BK);
 
-  // ---- DMA issue -----------------------------------------------------------
-  // Instruction t (0 .. NDMA-1) of this wave's share of stage kt: the first
-  // A_PER_WAVE move A, the rest W.  A burst of these right after a barrier
-  // stalls the wave on VMEM issue while its MFMA pipe idles, so the main
-  // loop spreads them through the MFMA stream.
+  // ---- global -> LDS loads -------------------------------------------------
+  // Load t (0 .. NDMA-1) of this wave's share of stage kt: the first
+  // A_PER_WAVE move A, the next W_HI move W, the rest move group scales.  A
+  // burst of these right after a barrier stalls the wave on VMEM issue
+  // while its MFMA pipe idles, so the main loop spreads them through the
+  // MFMA stream.
   const bool w_hi = wave < C::W_SPLIT;
-  constexpr int NDMA = C::A_PER_WAVE + C::W_HI;
+  constexpr int NDMA = C::NDMA;
   auto issue_one = [&](int kt, int t) {
     uint8_t* st = smem + (kt % NS) * C::STAGE;
     if (t < C::A_PER_WAVE) {
+      constexpr int CPR = C::ARB / 16;
       const int q = wave + C::NW * t;
-      const uint8_t* src = dma_src<C::ARB>(p.a, lda, m0, p.M, q, lane, (int64_t)kt * C::ARB);
+      const int rl = q * (1024 / C::ARB) + lane / CPR;
+      int64_t gr = m0 + rl;
+      if (gr > p.M - 1) gr = p.M - 1;
+      const uint8_t* src = p.a + gr * lda + ((int64_t)kt * C::ARB + (swz<C::ARB, C::GROUP>(rl, lane % CPR) << 4));
       __builtin_amdgcn_global_load_lds(src, LDS_AS(st + q * 1024), 16, 0, 0);
-    } else {
+    } else if (t < C::A_PER_WAVE + C::W_HI) {
       const int tw = t - C::A_PER_WAVE;
       if (tw < C::W_HI - 1 || w_hi) {
+        constexpr int CPR = C::WRB / 16;
         const int q = wave + C::NW * tw;
-        const uint8_t* src = dma_src<C::WRB>(p.w, ldw, n0, p.N, q, lane, (int64_t)kt * C::WRB);
+        const int rl = q * (1024 / C::WRB) + lane / CPR;
+        const int64_t gr = w_row_of<C, SWIG>(p, n0, rl);
+        const uint8_t* src =
+            p.w + gr * ldw + ((int64_t)kt * C::WRB + (swz<C::WRB, C::GROUP>(rl, lane % CPR) << 4));
         __builtin_amdgcn_global_load_lds(src, LDS_AS(st + C::SA + q * 1024), 16, 0, 0);
       }
+    } else if (C::GROUP) {
+      // Scale float at LDS position pos (of 2*BM A then 2*BN W values).
+      // A part, per group kk: the FI rows a lane reads (i*16 + l16 of its
+      // wave row) are contiguous.  W part, per group kk: natural row order.
+      const int si = wave + C::NW * (t - C::A_PER_WAVE - C::W_HI);
+      const int pos = si * 64 + lane;
+      const float* src;
+      if (pos < 2 * C::BM) {
+        const int kk = pos / C::BM, rem = pos % C::BM;
+        const int wv = rem / C::WM, u = rem % C::WM;
+        const int row = wv * C::WM + (u % C::FI) * 16 + u / C::FI;
+        int64_t gr = m0 + row;
+        if (gr > p.M - 1) gr = p.M - 1;
+        src = p.sa + gr * p.kg + (2 * kt + kk);
+      } else if (pos < 2 * (C::BM + C::BN)) {
+        const int pw = pos - 2 * C::BM;
+        const int kk = pw / C::BN, trow = pw % C::BN;
+        src = p.sw + w_row_of<C, SWIG>(p, n0, trow) * p.kg + (2 * kt + kk);
+      } else {
+        src = p.sw;  // padding: any valid address, never read back
+      }
+      __builtin_amdgcn_global_load_lds(src, LDS_AS(st + C::SA + C::SW + si * 256), 4, 0, 0);
     }
   };
 
-  v4i acc[C::FJ][C::FI];
+  // int32 accumulators (tensor / row scales) or fp32 sums of rescaled
+  // group partials (group-64 scales).
+  v4i acc[C::GROUP ? 1 : C::FJ][C::GROUP ? 1 : C::FI];
+  v4f yf[C::GROUP ? C::FJ : 1][C::GROUP ? C::FI : 1];
 #pragma unroll
   for (int j = 0; j < C::FJ; ++j)
 #pragma unroll
-    for (int i = 0; i < C::FI; ++i) acc[j][i] = v4i{0, 0, 0, 0};
+    for (int i = 0; i < C::FI; ++i) {
+      if (C::GROUP) yf[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
+      else acc[j][i] = v4i{0, 0, 0, 0};
+    }
 
   // lane-constant LDS offsets: fragment rows differ by multiples of 16, so
   // the swizzle term depends on l16 only.
   static_assert(C::WM % 16 == 0 && C::WN % 16 == 0, "wave tile must be 16-aligned");
   const int a_row = wm * C::WM + l16;
   const int w_row = wn * C::WN + l16;
+  // a_off[kk] / w_off, w_off1: fragment reads of half kk (b128); in the
+  // group-64 map packed operands are read per half as b64 at a_off[kk] /
+  // w_off (kk = 0) and w_off1 (kk = 1).
+  static_assert(!C::GROUP || C::WP, "group-64 scales come with INT4 weights");
+  constexpr bool GK = C::GROUP;
   int a_off[2];
-  int w_off;
+  int w_off, w_off1;
   if (C::AP) {
-    a_off[0] = a_row * 64 + (swz<64>(a_row, lg) << 4);
-    a_off[1] = a_off[0];
+    if (GK) {
+      a_off[0] = a_row * 64 + (swz<64, GK>(a_row, lg >> 1) << 4) + 8 * (lg & 1);
+      a_off[1] = a_row * 64 + (swz<64, GK>(a_row, 2 + (lg >> 1)) << 4) + 8 * (lg & 1);
+    } else {
+      a_off[0] = a_row * 64 + (swz<64, GK>(a_row, lg) << 4);
+      a_off[1] = a_off[0];
+    }
   } else {
-    a_off[0] = a_row * 128 + (swz<128>(a_row, 2 * lg) << 4);
-    a_off[1] = a_row * 128 + (swz<128>(a_row, 2 * lg + 1) << 4);
+    a_off[0] = a_row * 128 + (swz<128, GK>(a_row, GK ? lg : 2 * lg) << 4);
+    a_off[1] = a_row * 128 + (swz<128, GK>(a_row, GK ? 4 + lg : 2 * lg + 1) << 4);
   }
-  if (C::WP) w_off = w_row * 64 + (swz<64>(w_row, lg) << 4);
-  else w_off = w_row * 128 + (swz<128>(w_row, 2 * lg) << 4);
-  const int w_off1 = C::WP ? w_off : w_row * 128 + (swz<128>(w_row, 2 * lg + 1) << 4);
+  if (C::WP) {
+    if (GK) {
+      w_off = w_row * 64 + (swz<64, GK>(w_row, lg >> 1) << 4) + 8 * (lg & 1);
+      w_off1 = w_row * 64 + (swz<64, GK>(w_row, 2 + (lg >> 1)) << 4) + 8 * (lg & 1);
+    } else {
+      w_off = w_row * 64 + (swz<64, GK>(w_row, lg) << 4);
+      w_off1 = w_off;
+    }
+  } else {
+    w_off = w_row * 128 + (swz<128, GK>(w_row, 2 * lg) << 4);
+    w_off1 = w_row * 128 + (swz<128, GK>(w_row, 2 * lg + 1) << 4);
+  }
+  // group scales: byte offsets inside the stage's scale block
+  const int sa_off = (wm * C::WM + l16 * C::FI) * 4;
+  const int sw_off = (2 * C::BM + wn * C::WN + 4 * lg) * 4;
 
   // prologue: stages 0 .. NS-2 in flight
 #pragma unroll
@@ -223,7 +323,7 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
   for (int kt = 0; kt < KT; ++kt) {
     // Stage kt has landed once only the later stages (at most NS-2 of them)
     // are still in flight; the barrier then publishes every wave's part and
-    // guarantees all waves finished reading the buffer the next DMA reuses.
+    // guarantees all waves finished reading the buffer the next load reuses.
     if (NS == 3 && kt + 1 < KT) {
       if (w_hi) wait_vmcnt<(NS - 2) * NDMA>();
       else wait_vmcnt<(NS - 2) * (NDMA - 1)>();
@@ -235,39 +335,60 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
 
     const uint8_t* As = smem + (kt % NS) * C::STAGE;
     const uint8_t* Ws = As + C::SA;
+    const uint8_t* Ss = Ws + C::SW;
     // W fragments: packed -> one b128 per fragment carries both halves (kk);
     // int8 -> one b128 per fragment and half.
-    uint4 wraw[C::FJ];
-    uint4 wraw1[C::WP ? 1 : C::FJ];
+    uint4 wraw[GK ? 1 : C::FJ];
+    uint4 wraw1[(C::WP || GK) ? 1 : C::FJ];
+    v4i bw0[C::FJ], bw1[C::FJ];
+    if (GK) {
 #pragma unroll
-    for (int j = 0; j < C::FJ; ++j) {
-      wraw[j] = *reinterpret_cast<const uint4*>(Ws + w_off + j * 16 * C::WRB);
-      if (!C::WP) wraw1[j] = *reinterpret_cast<const uint4*>(Ws + w_off1 + j * 16 * C::WRB);
+      for (int j = 0; j < C::FJ; ++j) {
+        const uint2 h0 = *reinterpret_cast<const uint2*>(Ws + w_off + j * 16 * C::WRB);
+        const uint2 h1 = *reinterpret_cast<const uint2*>(Ws + w_off1 + j * 16 * C::WRB);
+        bw0[j] = unpack_lo(h0.x, h0.y);
+        bw1[j] = unpack_lo(h1.x, h1.y);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::FJ; ++j) {
+        wraw[j] = *reinterpret_cast<const uint4*>(Ws + w_off + j * 16 * C::WRB);
+        if (!C::WP) wraw1[j] = *reinterpret_cast<const uint4*>(Ws + w_off1 + j * 16 * C::WRB);
+      }
     }
     // A fragments: int8 -> streamed through a small window read PF ahead;
     // packed -> one b128 per fragment carries both halves.
     constexpr int PF = 3;
     constexpr int NQ = 2 * C::FI;
     v4i abuf[PF + 1];
-    uint4 araw[C::AP ? C::FI : 1];
+    uint4 araw[(C::AP && !GK) ? C::FI : 1];
     if (C::AP) {
+      if (!GK) {
 #pragma unroll
-      for (int i = 0; i < C::FI; ++i) araw[i] = *reinterpret_cast<const uint4*>(As + a_off[0] + i * 16 * C::ARB);
+        for (int i = 0; i < C::FI; ++i)
+          araw[i] = *reinterpret_cast<const uint4*>(As + a_off[0] + i * 16 * C::ARB);
+      }
     } else {
 #pragma unroll
       for (int q = 0; q < PF; ++q)
         abuf[q] = *reinterpret_cast<const v4i*>(As + a_off[q / C::FI] + (q % C::FI) * 16 * C::ARB);
     }
-    v4i bw0[C::FJ], bw1[C::FJ];
+    if (!GK) {
 #pragma unroll
-    for (int j = 0; j < C::FJ; ++j)
-      bw0[j] = C::WP ? unpack_lo(wraw[j].x, wraw[j].y)
-                     : v4i{(int)wraw[j].x, (int)wraw[j].y, (int)wraw[j].z, (int)wraw[j].w};
+      for (int j = 0; j < C::FJ; ++j)
+        bw0[j] = C::WP ? unpack_lo(wraw[j].x, wraw[j].y)
+                       : v4i{(int)wraw[j].x, (int)wraw[j].y, (int)wraw[j].z, (int)wraw[j].w};
+    }
+    v4f sav[C::GROUP ? C::FI / 4 : 1];
+    v4f swv[C::GROUP ? C::FJ : 1];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int kk = q / C::FI, i = q % C::FI;
       v4i af;
-      if (C::AP) {
+      if (C::AP && GK) {
+        const uint2 h = *reinterpret_cast<const uint2*>(As + a_off[kk] + i * 16 * C::ARB);
+        af = unpack_lo(h.x, h.y);
+      } else if (C::AP) {
         af = kk == 0 ? unpack_lo(araw[i].x, araw[i].y) : unpack_lo(araw[i].z, araw[i].w);
       } else {
         if (q + PF < NQ)
@@ -277,22 +398,53 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
       }
       if (dma && (q % 2) == 0 && q / 2 < NDMA) issue_one(kt + NS - 1, q / 2);
       // second-half W fragments, spread over the first half's MFMA groups
-      if (kk == 0 && i < C::FJ)
+      if (!GK && kk == 0 && i < C::FJ)
         bw1[i] = C::WP ? unpack_lo(wraw[i].z, wraw[i].w)
                        : v4i{(int)wraw1[i].x, (int)wraw1[i].y, (int)wraw1[i].z, (int)wraw1[i].w};
-      if (kk == 0 && i == C::FI - 1) {
+      if (!GK && kk == 0 && i == C::FI - 1) {
 #pragma unroll
         for (int j = C::FI; j < C::FJ; ++j)
           bw1[j] = C::WP ? unpack_lo(wraw[j].z, wraw[j].w)
                          : v4i{(int)wraw1[j].x, (int)wraw1[j].y, (int)wraw1[j].z, (int)wraw1[j].w};
       }
-      __builtin_amdgcn_sched_barrier(0);
+      if (!C::GROUP) {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < C::FJ; ++j)
-        acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kk == 0 ? bw0[j] : bw1[j], af, acc[j][i], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < C::FJ; ++j)
+          acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kk == 0 ? bw0[j] : bw1[j], af, acc[j][i], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        if (i == 0) {
+          // scales of group kk: s_a of the lane's FI rows, s_w of its 4
+          // columns in each fragment
+#pragma unroll
+          for (int f = 0; f < C::FI / 4; ++f)
+            sav[f] = *reinterpret_cast<const v4f*>(Ss + sa_off + (kk * C::BM + 4 * f) * 4);
+#pragma unroll
+          for (int j = 0; j < C::FJ; ++j)
+            swv[j] = *reinterpret_cast<const v4f*>(Ss + sw_off + (kk * C::BN + j * 16) * 4);
+        }
+        const float s_i = sav[i / 4][i % 4];
+        v4i part[C::FJ];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < C::FJ; ++j)
+          part[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kk == 0 ? bw0[j] : bw1[j], af, v4i{0, 0, 0, 0},
+                                                          0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < C::FJ; ++j) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            yf[j][i][r] = __builtin_fmaf((float)part[j][r], s_i * swv[j][r], yf[j][i][r]);
+          // keep the rescale next to its MFMAs: without this the compiler
+          // sinks every rescale below all of the stage's MFMAs and must hold
+          // all their partials at once
+          asm volatile("" : "+v"(yf[j][i]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    // any DMA instructions not yet issued (only if NDMA > NQ / 2)
+    // any loads not yet issued (only if NDMA > NQ / 2)
     if (dma) {
 #pragma unroll
       for (int t = NQ / 2; t < NDMA; ++t) issue_one(kt + NS - 1, t);
@@ -300,23 +452,66 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
   }
 
   // ---- epilogue: lane holds out[m][n .. n+3] for each (i, j) --------------
+  // SwiGLU pairs fragment j (gate) with j + FJ/2 (up) of the same outputs.
+  constexpr int NJ = SWIG ? C::FJ / 2 : C::FJ;
+  static_assert(!SWIG || C::FJ % 2 == 0, "SwiGLU needs gate/up fragment pairs");
 #pragma unroll
-  for (int j = 0; j < C::FJ; ++j) {
-    const int64_t n = n0 + wn * C::WN + j * 16 + lg * 4;
-    if (n >= p.N) continue;
-    float swv[4], addv[4], gatev[4];
+  for (int j = 0; j < NJ; ++j) {
+    const int t0 = wn * C::WN + j * 16;          // first W-tile row of fragment j
+    const int64_t n = SWIG ? n0 + wn * (C::WN / 2) + j * 16 + lg * 4 : n0 + t0 + lg * 4;
+    if (n >= (SWIG ? p.half_n : p.N)) continue;  // 4 | 16 | N: all four columns valid
+    // weight-side values of the lane's 4 columns (gate side, and up side)
+    float swv[2][4], addv[2][4], gatev[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      swv[r] = EPI == EPI_I32 ? 0.f : p.sw[(n + r) * p.sw_stride];
-      addv[r] = p.bias ? bf16_to_f32(p.bias[n + r]) : 0.f;
-      gatev[r] = EPI == EPI_GATED ? bf16_to_f32(p.gate[n + r]) : 0.f;
-    }
+    for (int h = 0; h < (SWIG ? 2 : 1); ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t wr = SWIG ? (h ? p.half_n : 0) + n + r : n + r;
+        swv[h][r] = (C::GROUP || EPI == EPI_I32) ? 1.f : p.sw[wr * p.sw_stride];
+        addv[h][r] = p.bias ? bf16_to_f32(p.bias[wr]) : 0.f;
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) gatev[r] = EPI == EPI_GATED ? bf16_to_f32(p.gate[n + r]) : 0.f;
+    // L2 fragments (first MFMA operand): lane supplies weight column
+    // w_row_of(t0 + l16) (and its up partner) at ranks k0 + 8 lg .. + 7.
+    // The skip above is uniform over the wave (16 | N, 16 | F), so every
+    // lane reaches the MFMAs below.
+    int64_t l2col[2];
+    l2col[0] = w_row_of<C, SWIG>(p, n0, t0 + l16);
+    l2col[1] = SWIG ? w_row_of<C, SWIG>(p, n0, t0 + C::WN / 2 + l16) : 0;
+
 #pragma unroll
     for (int i = 0; i < C::FI; ++i) {
       const int64_t m = m0 + wm * C::WM + i * 16 + l16;
+      // Low-rank branch first, with every lane active: an MFMA mixes all
+      // 64 lanes' operands, so rows past M load row M-1 instead of skipping.
+      v4f lrv[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+      if (LOWRANK) {
+        // lr[m, :] . L2[:, cols]: bf16 MFMA 16x16x32 over the rank
+        const int64_t mc = m < p.M ? m : p.M - 1;
+#pragma unroll
+        for (int h = 0; h < (SWIG ? 2 : 1); ++h) {
+          for (int k0 = 0; k0 < p.rank; k0 += 32) {
+            const int kc = k0 + lg * 8;
+            const bool kin = kc < p.rank;
+            const uint4 ua = kin ? *reinterpret_cast<const uint4*>(p.lr + mc * p.rank + kc)
+                                 : make_uint4(0, 0, 0, 0);
+            uint32_t wv[4] = {0u, 0u, 0u, 0u};
+            if (kin) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                wv[e] = (uint32_t)p.l2[(int64_t)(kc + 2 * e) * p.N + l2col[h]] |
+                        ((uint32_t)p.l2[(int64_t)(kc + 2 * e + 1) * p.N + l2col[h]] << 16);
+            }
+            lrv[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(v8bf, make_uint4(wv[0], wv[1], wv[2], wv[3])),
+                __builtin_bit_cast(v8bf, ua), lrv[h], 0, 0, 0);
+          }
+        }
+      }
       if (m >= p.M) continue;
-      const v4i a4 = acc[j][i];
       if (EPI == EPI_I32) {
+        const v4i a4 = acc[C::GROUP ? 0 : j][C::GROUP ? 0 : i];
         int4 o;
         o.x = a4[0] >> p.shift;
         o.y = a4[1] >> p.shift;
@@ -325,55 +520,86 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
         *reinterpret_cast<int4*>(static_cast<int32_t*>(p.out) + m * p.ldo + n) = o;
         continue;
       }
-      const float sam = p.sa[m * p.sa_stride] * p.post;
-      float y[4];
+      float y[2][4];
+      const float sam = C::GROUP ? p.post : p.sa[m * p.sa_stride] * p.post;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) y[r] = (float)a4[r] * sam * swv[r] + addv[r];
+      for (int h = 0; h < (SWIG ? 2 : 1); ++h) {
+        const int jj = j + h * (C::FJ / 2);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = C::GROUP ? yf[C::GROUP ? jj : 0][C::GROUP ? i : 0][r]
+                                   : (float)acc[C::GROUP ? 0 : jj][C::GROUP ? 0 : i][r];
+          y[h][r] = v * sam * swv[h][r] + addv[h][r] + (LOWRANK ? lrv[h][r] : 0.f);
+        }
+      }
+      float o[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = y[0][r];
       if (EPI == EPI_F32) {
         *reinterpret_cast<float4*>(static_cast<float*>(p.out) + m * p.ldo + n) =
-            make_float4(y[0], y[1], y[2], y[3]);
+            make_float4(o[0], o[1], o[2], o[3]);
         continue;
+      }
+      if (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = y[0][r] / (1.0f + __expf(-y[0][r])) * y[1][r];
       }
       if (EPI == EPI_GATED) {
         const uint2 rr = *reinterpret_cast<const uint2*>(p.residual + m * p.ldo + n);
-        y[0] = __builtin_fmaf(gatev[0], y[0], bf16_to_f32(rr.x & 0xffff));
-        y[1] = __builtin_fmaf(gatev[1], y[1], bf16_to_f32(rr.x >> 16));
-        y[2] = __builtin_fmaf(gatev[2], y[2], bf16_to_f32(rr.y & 0xffff));
-        y[3] = __builtin_fmaf(gatev[3], y[3], bf16_to_f32(rr.y >> 16));
+        o[0] = __builtin_fmaf(gatev[0], o[0], bf16_to_f32(rr.x & 0xffff));
+        o[1] = __builtin_fmaf(gatev[1], o[1], bf16_to_f32(rr.x >> 16));
+        o[2] = __builtin_fmaf(gatev[2], o[2], bf16_to_f32(rr.y & 0xffff));
+        o[3] = __builtin_fmaf(gatev[3], o[3], bf16_to_f32(rr.y >> 16));
       }
-      const bf2 h0 = __builtin_convertvector(f2{y[0], y[1]}, bf2);
-      const bf2 h1 = __builtin_convertvector(f2{y[2], y[3]}, bf2);
+      const bf2 h0 = __builtin_convertvector(f2{o[0], o[1]}, bf2);
+      const bf2 h1 = __builtin_convertvector(f2{o[2], o[3]}, bf2);
       *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + m * p.ldo + n) =
           make_uint2(__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1));
     }
   }
 }
 
-template <class C, int EPI>
+template <class C, int EPI, bool LOWRANK>
 hipError_t launch_pipe(PArgs p, hipStream_t s) {
   p.tiles_m = (int)((p.M + C::BM - 1) / C::BM);
-  p.tiles_n = (int)((p.N + C::BN - 1) / C::BN);
+  p.tiles_n = EPI == EPI_SWIGLU ? (int)((p.half_n + C::BN / 2 - 1) / (C::BN / 2))
+                                : (int)((p.N + C::BN - 1) / C::BN);
   p.group_m = 4;
   const int nb = p.tiles_m * p.tiles_n;
-  hipLaunchKernelGGL((qgemm_pipe_kernel<C, EPI>), dim3(nb), dim3(C::NT), 0, s, p);
+  hipLaunchKernelGGL((qgemm_pipe_kernel<C, EPI, LOWRANK>), dim3(nb), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
 
+// Tensor / row scales without low-rank branch: BF16 | F32 | I32 | GATED.
 template <class C>
-hipError_t launch_epi(const PArgs& p, int epi, hipStream_t s) {
+hipError_t launch_plain(const PArgs& p, int epi, hipStream_t s) {
   switch (epi) {
-    case EPI_BF16: return launch_pipe<C, EPI_BF16>(p, s);
-    case EPI_F32: return launch_pipe<C, EPI_F32>(p, s);
-    case EPI_I32: return launch_pipe<C, EPI_I32>(p, s);
-    case EPI_GATED: return launch_pipe<C, EPI_GATED>(p, s);
+    case EPI_BF16: return launch_pipe<C, EPI_BF16, false>(p, s);
+    case EPI_F32: return launch_pipe<C, EPI_F32, false>(p, s);
+    case EPI_I32: return launch_pipe<C, EPI_I32, false>(p, s);
+    case EPI_GATED: return launch_pipe<C, EPI_GATED, false>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// INT4 weights with group-64 scales, SwiGLU and/or the low-rank branch:
+// BF16 | F32 | SWIGLU, each with or without the branch.
+template <class C>
+hipError_t launch_lowrank(const PArgs& p, int epi, hipStream_t s) {
+  const bool lr = p.rank > 0;
+  switch (epi) {
+    case EPI_BF16: return lr ? launch_pipe<C, EPI_BF16, true>(p, s) : launch_pipe<C, EPI_BF16, false>(p, s);
+    case EPI_F32: return lr ? launch_pipe<C, EPI_F32, true>(p, s) : launch_pipe<C, EPI_F32, false>(p, s);
+    case EPI_SWIGLU:
+      return lr ? launch_pipe<C, EPI_SWIGLU, true>(p, s) : launch_pipe<C, EPI_SWIGLU, false>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-// Tensor / row scales, epilogues BF16 | F32 | I32 | GATED.
-int launch_qgemm_pipe(const GemmArgs& g, hipStream_t s) {
+int launch_qgemm(const GemmArgs& g, hipStream_t s) {
+  if (g.M == 0) return OK;
   PArgs p{};
   p.a = static_cast<const uint8_t*>(g.a);
   p.w = static_cast<const uint8_t*>(g.w);
@@ -384,20 +610,50 @@ int launch_qgemm_pipe(const GemmArgs& g, hipStream_t s) {
   p.K = g.K;
   p.sa_stride = g.a_mode == 1 ? 1 : 0;
   p.sw_stride = g.w_mode == 1 ? 1 : 0;
+  p.kg = (int)(g.K >> 6);
   p.bias = g.bias;
   p.residual = g.residual;
   p.gate = g.gate;
+  p.lr = g.lr;
+  p.l2 = g.l2;
+  p.rank = g.rank;
   p.out = g.out;
   p.ldo = g.ldo;
+  p.half_n = g.N / 2;
   const int npacked = (g.a_packed ? 1 : 0) + (g.w_packed ? 1 : 0);
   p.post = npacked == 2 ? 1.0f / 256.0f : (npacked == 1 ? 1.0f / 16.0f : 1.0f);
   p.shift = 4 * npacked;
+  const bool group = g.a_mode == 2;
   hipError_t e;
+  if (group || g.rank > 0 || g.epilogue == EPI_SWIGLU) {
+    // INT4 weights only (the ABI routes nothing else here); 256 x 256
+    // tiles keep the gate/up fragment pairs and the scale block in LDS.
+    if (group) {
+      e = g.a_packed ? launch_lowrank<Cfg<128, 256, 2, 4, true, true, true>>(p, g.epilogue, s)
+                     : launch_lowrank<Cfg<128, 256, 2, 4, false, true, true>>(p, g.epilogue, s);
+    } else {
+      e = g.a_packed ? launch_lowrank<Cfg<256, 256, 2, 4, true, true>>(p, g.epilogue, s)
+                     : launch_lowrank<Cfg<256, 256, 2, 4, false, true>>(p, g.epilogue, s);
+    }
+    return e == hipSuccess ? OK : ERR_LAUNCH;
+  }
+  // 256 x 320 tiles unless 256 x 256 needs fewer tile-area waves on the
+  // 256 CUs (one workgroup per CU): time ~ waves * tile area.
+  auto cost = [&](int64_t bn) {
+    const int64_t tiles = ((g.M + 255) / 256) * ((g.N + bn - 1) / bn);
+    return ((tiles + 255) / 256) * 256 * bn;
+  };
+  const bool wide = cost(320) <= cost(256);
   if (g.w_packed) {
-    if (g.a_packed) e = launch_epi<Cfg<256, 320, 2, 4, true, true>>(p, g.epilogue, s);
-    else e = launch_epi<Cfg<256, 320, 2, 4, false, true>>(p, g.epilogue, s);
+    if (g.a_packed)
+      e = wide ? launch_plain<Cfg<256, 320, 2, 4, true, true>>(p, g.epilogue, s)
+               : launch_plain<Cfg<256, 256, 2, 4, true, true>>(p, g.epilogue, s);
+    else
+      e = wide ? launch_plain<Cfg<256, 320, 2, 4, false, true>>(p, g.epilogue, s)
+               : launch_plain<Cfg<256, 256, 2, 4, false, true>>(p, g.epilogue, s);
   } else {
-    e = launch_epi<Cfg<256, 256, 2, 4, false, false>>(p, g.epilogue, s);
+    e = wide ? launch_plain<Cfg<256, 320, 2, 4, false, false>>(p, g.epilogue, s)
+             : launch_plain<Cfg<256, 256, 2, 4, false, false>>(p, g.epilogue, s);
   }
   return e == hipSuccess ? OK : ERR_LAUNCH;
 }

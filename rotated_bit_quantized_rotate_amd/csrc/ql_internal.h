@@ -82,8 +82,8 @@ struct GemmArgs {
   int64_t ldo;
 };
 
+// Every GEMM entry point: tensor / row / group-64 scales, all epilogues,
+// optional low-rank branch.
 int launch_qgemm(const GemmArgs& g, hipStream_t s);
-// Large-tile pipelined kernel: tensor / row scales; BF16, F32, I32, GATED.
-int launch_qgemm_pipe(const GemmArgs& g, hipStream_t s);
 
 }  // namespace ql

@@ -9,8 +9,8 @@ Acceptance (the contract of the layer):
     ulp, so the exact-rotation oracle can differ by that much);
   * int32 accumulators bit-exact when both sides consume the same codes;
   * final bf16 outputs within 1e-2 relative Frobenius error of the oracle.
-Inputs are the seeded synthetic workloads; sizes span several 128x128
-tiles plus ragged tails.
+Inputs are the seeded synthetic workloads; sizes span several tiles of
+each kernel configuration plus ragged tails.
 """
 
 import numpy as np
@@ -166,7 +166,11 @@ def test_pack_weight_int4_matches_oracle(Q, mode):
 
 # -------------------------------------------------- exact integer product --
 
-GEMM_SHAPES = [(1, 16, 256), (130, 272, 512), (257, 400, 1024), (128, 128, 256), (300, 656, 768)]
+# The small shapes run the 256 x 256-tile kernels; (4059, 5104, 512) needs
+# more than 256 such tiles but only 256 of 256 x 320, so it runs the wide
+# kernels, with ragged tails in both M and N.
+GEMM_SHAPES = [(1, 16, 256), (130, 272, 512), (257, 400, 1024), (128, 128, 256), (300, 656, 768),
+               (4059, 5104, 512)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
@@ -235,6 +239,31 @@ def test_group64_unit_scales_exact(Q):
     out = Q.qgemm_w4a4_lowrank(to_dev(qa), sa, to_dev(O.pack_int4(qw)), sw, K, epilogue="f32")
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().astype(np.float64), O.int_gemm(qa, qw).astype(np.float64))
+
+
+@pytest.mark.parametrize("a_layout", ["i8", "packed"])
+def test_group64_pow2_scales_exact(Q, a_layout):
+    """Group-64 with power-of-two scales 2^-e that differ per row and group:
+    every term acc_g * s_a * s_w is a multiple of 2^-6 below 2^18 and the
+    sum stays below 2^24, so the fp32 result is exact in any order and must
+    equal the oracle's dequantized product bit for bit.  A scale applied to
+    the wrong row, column or group changes the result."""
+    import torch
+
+    M, N, K = 200, 272, 1024
+    rng = np.random.default_rng(11)
+    qa = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    sa_h = np.ldexp(1.0, -rng.integers(0, 4, size=(M, K // 64))).astype(np.float32)
+    sw_h = np.ldexp(1.0, -rng.integers(0, 4, size=(N, K // 64))).astype(np.float32)
+    a = to_dev(O.pack_int4(qa) if a_layout == "packed" else qa)
+    out = Q.qgemm_w4a4_lowrank(a, to_dev(sa_h), to_dev(O.pack_int4(qw)), to_dev(sw_h), K,
+                               a_layout=a_layout, epilogue="f32")
+    torch.cuda.synchronize()
+    ref_a = O.QuantResult(qa, sa_h, 4, "group64", None)
+    ref_w = O.QuantResult(qw, sw_h, 4, "group64", None)
+    want = O.linear_fp64(ref_a, ref_w)
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), want)
 
 
 # ---------------------------------------------- dequant epilogues (same codes) --
