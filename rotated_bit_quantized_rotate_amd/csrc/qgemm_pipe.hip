@@ -455,6 +455,15 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
   // SwiGLU pairs fragment j (gate) with j + FJ/2 (up) of the same outputs.
   constexpr int NJ = SWIG ? C::FJ / 2 : C::FJ;
   static_assert(!SWIG || C::FJ % 2 == 0, "SwiGLU needs gate/up fragment pairs");
+  // Loads are issued ahead of their use (rows past M read row M-1) so a
+  // wave keeps many in flight instead of waiting on one per output.
+  float sam[C::FI];
+#pragma unroll
+  for (int i = 0; i < C::FI; ++i) {
+    int64_t m = m0 + wm * C::WM + i * 16 + l16;
+    if (m > p.M - 1) m = p.M - 1;
+    sam[i] = (C::GROUP || EPI == EPI_I32) ? p.post : p.sa[m * p.sa_stride] * p.post;
+  }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int t0 = wn * C::WN + j * 16;          // first W-tile row of fragment j
@@ -479,6 +488,15 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
     int64_t l2col[2];
     l2col[0] = w_row_of<C, SWIG>(p, n0, t0 + l16);
     l2col[1] = SWIG ? w_row_of<C, SWIG>(p, n0, t0 + C::WN / 2 + l16) : 0;
+    uint2 res[EPI == EPI_GATED ? C::FI : 1];
+    if (EPI == EPI_GATED) {
+#pragma unroll
+      for (int i = 0; i < C::FI; ++i) {
+        int64_t m = m0 + wm * C::WM + i * 16 + l16;
+        if (m > p.M - 1) m = p.M - 1;
+        res[i] = *reinterpret_cast<const uint2*>(p.residual + m * p.ldo + n);
+      }
+    }
 
 #pragma unroll
     for (int i = 0; i < C::FI; ++i) {
@@ -521,7 +539,6 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
         continue;
       }
       float y[2][4];
-      const float sam = C::GROUP ? p.post : p.sa[m * p.sa_stride] * p.post;
 #pragma unroll
       for (int h = 0; h < (SWIG ? 2 : 1); ++h) {
         const int jj = j + h * (C::FJ / 2);
@@ -529,7 +546,7 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
         for (int r = 0; r < 4; ++r) {
           const float v = C::GROUP ? yf[C::GROUP ? jj : 0][C::GROUP ? i : 0][r]
                                    : (float)acc[C::GROUP ? 0 : jj][C::GROUP ? 0 : i][r];
-          y[h][r] = v * sam * swv[h][r] + addv[h][r] + (LOWRANK ? lrv[h][r] : 0.f);
+          y[h][r] = v * sam[i] * swv[h][r] + addv[h][r] + (LOWRANK ? lrv[h][r] : 0.f);
         }
       }
       float o[4];
@@ -545,7 +562,7 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
         for (int r = 0; r < 4; ++r) o[r] = y[0][r] / (1.0f + __expf(-y[0][r])) * y[1][r];
       }
       if (EPI == EPI_GATED) {
-        const uint2 rr = *reinterpret_cast<const uint2*>(p.residual + m * p.ldo + n);
+        const uint2 rr = res[EPI == EPI_GATED ? i : 0];
         o[0] = __builtin_fmaf(gatev[0], o[0], bf16_to_f32(rr.x & 0xffff));
         o[1] = __builtin_fmaf(gatev[1], o[1], bf16_to_f32(rr.x >> 16));
         o[2] = __builtin_fmaf(gatev[2], o[2], bf16_to_f32(rr.y & 0xffff));

@@ -265,67 +265,67 @@ hipError_t dispatch_rq(const RqArgs& a, const Plan& p, int phase, hipStream_t s)
 // SVDQuant down-projection lr = bf16(X @ L1) with the unrotated bf16 X
 // (README "Krea-2-SVDQuant-ComfyUI", section "Low-rank refinement": the
 // branch is a small full-precision product next to the quantized weight).
-// bf16 MFMA 16x16x32, fp32 accumulation.  64 rows per workgroup, one wave per
-// 16 rows; L1 is staged through LDS transposed ([rank][k]) in 128-deep chunks.
+//
+// The product is skinny (rank <= 128) and bound by reading X once.  One
+// workgroup per 16 rows; its 8 waves split K into eighths, so a 4096-row X
+// gives 256 workgroups x 8 waves.  bf16 MFMA 16x16x32, fp32 accumulation:
+// the first operand is a 16-rank block of L1^T (each lane gathers 8
+// consecutive k of one L1 column straight from global memory; L1 is small
+// and stays in L2), the second the 16 rows of X (one 16-byte load per lane
+// per 32 channels).  The eight partial sums meet in LDS.
 // ---------------------------------------------------------------------------
-constexpr int kLrKC = 128;
-constexpr int kLrPitch = kLrKC + 8;  // bf16 elements per transposed L1 row
+constexpr int kLrWaves = 8;
+constexpr int kLrMaxRank = 128;
 
-__global__ __launch_bounds__(256) void lowrank_down_kernel(const uint16_t* __restrict__ x, int64_t M,
-                                                           int64_t K, int64_t ldx,
-                                                           const uint16_t* __restrict__ l1, int rank,
-                                                           uint16_t* __restrict__ lr) {
-  __shared__ __attribute__((aligned(16))) uint16_t l1t[128 * kLrPitch];
+__global__ __launch_bounds__(64 * kLrWaves) void lowrank_down_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, const uint16_t* __restrict__ l1,
+    int rank, uint16_t* __restrict__ lr) {
+  __shared__ float part[kLrWaves][16 * kLrMaxRank];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int lg = lane >> 4;
   const int nb = rank >> 4;
-  const int64_t m0 = (int64_t)blockIdx.x * 64 + wave * 16;
-  int64_t arow = m0 + (lane & 15);
+  const int64_t m0 = (int64_t)blockIdx.x * 16;
+  int64_t arow = m0 + l16;
   if (arow > M - 1) arow = M - 1;
-  const uint16_t* xrow = x + arow * ldx + (lane >> 4) * 8;
+  const int64_t kw = K / kLrWaves;  // multiple of 32 (K is a multiple of 256)
+  const int64_t kbeg = wave * kw;
+  const uint16_t* xp = x + arow * ldx + kbeg + lg * 8;
+  const uint16_t* lp = l1 + (kbeg + lg * 8) * rank + l16;
 
-  v4f acc[8];
+  v4f acc[kLrMaxRank / 16];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < kLrMaxRank / 16; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t k0 = 0; k0 < K; k0 += kLrKC) {
-    __syncthreads();
-    // stage L1[k0 : k0+128, 0:rank] transposed into l1t[n][k]
-    const int chunks = kLrKC * (rank >> 3);
-    for (int c = tid; c < chunks; c += 256) {
-      const int kr = c / (rank >> 3);
-      const int n8 = (c - kr * (rank >> 3)) * 8;
-      const uint4 u = *reinterpret_cast<const uint4*>(l1 + (k0 + kr) * rank + n8);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  for (int64_t k0 = 0; k0 < kw; k0 += 32) {
+    const v8bf xf = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(xp + k0));
+    const uint16_t* lk = lp + k0 * rank;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        l1t[(n8 + 2 * e) * kLrPitch + kr] = (uint16_t)(w[e] & 0xffff);
-        l1t[(n8 + 2 * e + 1) * kLrPitch + kr] = (uint16_t)(w[e] >> 16);
-      }
-    }
-    __syncthreads();
+    for (int j = 0; j < kLrMaxRank / 16; ++j) {
+      if (j < nb) {
+        uint32_t w[4];
 #pragma unroll
-    for (int kk = 0; kk < kLrKC; kk += 32) {
-      const v8bf af = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(xrow + k0 + kk));
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j < nb) {
-          const v8bf bfr = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(
-              &l1t[(j * 16 + (lane & 15)) * kLrPitch + kk + (lane >> 4) * 8]));
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, acc[j], 0, 0, 0);
-        }
+        for (int e = 0; e < 4; ++e)
+          w[e] = (uint32_t)lk[(2 * e) * rank + j * 16] | ((uint32_t)lk[(2 * e + 1) * rank + j * 16] << 16);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(v8bf, make_uint4(w[0], w[1], w[2], w[3])), xf, acc[j], 0, 0, 0);
       }
     }
   }
+  // lane holds ranks 16 j + 4 lg + r of row m0 + l16
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= nb) continue;
+  for (int j = 0; j < kLrMaxRank / 16; ++j)
+    if (j < nb)
+      *reinterpret_cast<v4f*>(&part[wave][l16 * rank + j * 16 + lg * 4]) = acc[j];
+  __syncthreads();
+  for (int o = tid; o < 16 * rank; o += 64 * kLrWaves) {
+    float sum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t m = m0 + (lane >> 4) * 4 + r;
-      if (m < M) lr[m * rank + j * 16 + (lane & 15)] = (uint16_t)f32_to_bf16(acc[j][r]);
-    }
+    for (int w = 0; w < kLrWaves; ++w) sum += part[w][o];
+    const int64_t m = m0 + o / rank;
+    if (m < M) lr[m * rank + o % rank] = (uint16_t)f32_to_bf16(sum);
   }
 }
 
@@ -353,8 +353,9 @@ int launch_rotate_quantize(const RqArgs& a, hipStream_t s) {
 int launch_lowrank_down(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* l1,
                         int rank, uint16_t* lr, hipStream_t s) {
   if (M == 0) return OK;
-  const unsigned blocks = (unsigned)((M + 63) / 64);
-  hipLaunchKernelGGL(lowrank_down_kernel, dim3(blocks), dim3(256), 0, s, x, M, K, ldx, l1, rank, lr);
+  const unsigned blocks = (unsigned)((M + 15) / 16);
+  hipLaunchKernelGGL(lowrank_down_kernel, dim3(blocks), dim3(64 * kLrWaves), 0, s, x, M, K, ldx, l1, rank,
+                     lr);
   return hipGetLastError() == hipSuccess ? OK : ERR_LAUNCH;
 }
 
