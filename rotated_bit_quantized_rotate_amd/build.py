@@ -69,8 +69,21 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB_PATH + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    _check_stubs(tmp)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
+
+
+def _check_stubs(lib: str) -> None:
+    """Fail if a kernel's host launch stub is referenced but not defined:
+    the host compilation pass can drop a kernel template it fails to
+    instantiate without an error, which would only show up when the library
+    is loaded."""
+    nm = shutil.which("nm") or "/usr/bin/nm"
+    r = subprocess.run([nm, "-u", lib], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    missing = [ln.split()[-1] for ln in r.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        raise RuntimeError(f"{len(missing)} kernel launch stubs are undefined in {lib}, e.g. {missing[0]}")
 
 
 if __name__ == "__main__":

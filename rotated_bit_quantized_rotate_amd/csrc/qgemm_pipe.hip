@@ -178,10 +178,19 @@ template <class C, int EPI, bool LOWRANK>
 __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
   constexpr int NS = C::NSTAGE;
   constexpr bool SWIG = EPI == EPI_SWIGLU;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NS * C::STAGE];
+  // One LDS array per ring stage.  The main loop is unrolled by NS so every
+  // access names its array statically: the compiler then sees that the
+  // loads in flight into the other stages do not alias the stage being read
+  // and adds no wait for them before the fragment reads.  The explicit
+  // vmcnt wait plus barrier at the top of each stage is the synchronization.
+  __shared__ __attribute__((aligned(16))) uint8_t sm0[C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm1[C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm2[NS == 3 ? C::STAGE : 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform; readfirstlane keeps everything derived from it in SGPRs
+  // (load bases, LDS destinations, branch conditions)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WGN;
   const int wn = wave % C::WGN;
   const int l16 = lane & 15;
@@ -214,48 +223,70 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
   // MFMA stream.
   const bool w_hi = wave < C::W_SPLIT;
   constexpr int NDMA = C::NDMA;
-  auto issue_one = [&](int kt, int t) {
-    uint8_t* st = smem + (kt % NS) * C::STAGE;
+  // Per-lane byte offsets of every load slot, fixed for the whole K loop:
+  // a load is a wave-uniform base (advanced by the stage) plus a 32-bit lane
+  // offset, the global_load_lds saddr form, so issuing one costs no vector
+  // address arithmetic.  (The host checks that the offsets fit in 32 bits.)
+  // A slot t: 1 KB chunk q = wave + NW t of the A stage; W slot likewise;
+  // scale slot: 64 floats at LDS position si * 64 (2*BM A-scale positions,
+  // then 2*BN W-scale positions, then padding).  A-scale positions put the
+  // FI rows a lane reads (i*16 + l16 of its wave row) next to each other;
+  // W-scale positions are in tile-row order.
+  // (Each load address goes through a named pointer variable: written
+  // inline as a pointer-plus-offset expression in the builtin call, the host
+  // pass of this compiler silently fails to instantiate the kernel and drops
+  // its launch stub; the build checks the library for that.)
+  const int64_t a_row0 = m0 * lda;
+  uint32_t a_vo[C::A_PER_WAVE];
+#pragma unroll
+  for (int t = 0; t < C::A_PER_WAVE; ++t) {
+    constexpr int CPR = C::ARB / 16;
+    const int rl = (wave + C::NW * t) * (1024 / C::ARB) + lane / CPR;
+    const int64_t gr = m0 + rl > p.M - 1 ? p.M - 1 : m0 + rl;
+    a_vo[t] = (uint32_t)((gr - m0) * lda + (swz<C::ARB, C::GROUP>(rl, lane % CPR) << 4));
+  }
+  uint32_t w_vo[C::W_HI];
+#pragma unroll
+  for (int tw = 0; tw < C::W_HI; ++tw) {
+    constexpr int CPR = C::WRB / 16;
+    const int rl = (wave + C::NW * tw) * (1024 / C::WRB) + lane / CPR;
+    w_vo[tw] = (uint32_t)(w_row_of<C, SWIG>(p, n0, rl) * ldw + (swz<C::WRB, C::GROUP>(rl, lane % CPR) << 4));
+  }
+  uint32_t s_vo[C::GROUP ? C::S_PER_WAVE : 1];
+#pragma unroll
+  for (int ts = 0; ts < (C::GROUP ? C::S_PER_WAVE : 0); ++ts) {
+    const int pos = (wave + C::NW * ts) * 64 + lane;
+    int64_t e = 0;  // float index relative to p.sa (A part) or p.sw (W part)
+    if (pos < 2 * C::BM) {
+      const int kk = pos / C::BM, rem = pos % C::BM;
+      const int wv = rem / C::WM, u = rem % C::WM;
+      const int row = wv * C::WM + (u % C::FI) * 16 + u / C::FI;
+      const int64_t gr = m0 + row > p.M - 1 ? p.M - 1 : m0 + row;
+      e = gr * p.kg + kk;
+    } else if (pos < 2 * (C::BM + C::BN)) {
+      const int pw = pos - 2 * C::BM;
+      const int kk = pw / C::BN, trow = pw % C::BN;
+      e = w_row_of<C, SWIG>(p, n0, trow) * p.kg + kk;
+    }  // padding slots load the first W scale, never read back
+    s_vo[ts] = (uint32_t)(e * 4);
+  }
+  auto issue_one = [&](uint8_t* st, int kt, int t) {
     if (t < C::A_PER_WAVE) {
-      constexpr int CPR = C::ARB / 16;
       const int q = wave + C::NW * t;
-      const int rl = q * (1024 / C::ARB) + lane / CPR;
-      int64_t gr = m0 + rl;
-      if (gr > p.M - 1) gr = p.M - 1;
-      const uint8_t* src = p.a + gr * lda + ((int64_t)kt * C::ARB + (swz<C::ARB, C::GROUP>(rl, lane % CPR) << 4));
+      const uint8_t* src = p.a + (a_row0 + (int64_t)kt * C::ARB + (int64_t)a_vo[t]);
       __builtin_amdgcn_global_load_lds(src, LDS_AS(st + q * 1024), 16, 0, 0);
     } else if (t < C::A_PER_WAVE + C::W_HI) {
       const int tw = t - C::A_PER_WAVE;
       if (tw < C::W_HI - 1 || w_hi) {
-        constexpr int CPR = C::WRB / 16;
         const int q = wave + C::NW * tw;
-        const int rl = q * (1024 / C::WRB) + lane / CPR;
-        const int64_t gr = w_row_of<C, SWIG>(p, n0, rl);
-        const uint8_t* src =
-            p.w + gr * ldw + ((int64_t)kt * C::WRB + (swz<C::WRB, C::GROUP>(rl, lane % CPR) << 4));
+        const uint8_t* src = p.w + ((int64_t)kt * C::WRB + (int64_t)w_vo[tw]);
         __builtin_amdgcn_global_load_lds(src, LDS_AS(st + C::SA + q * 1024), 16, 0, 0);
       }
     } else if (C::GROUP) {
-      // Scale float at LDS position pos (of 2*BM A then 2*BN W values).
-      // A part, per group kk: the FI rows a lane reads (i*16 + l16 of its
-      // wave row) are contiguous.  W part, per group kk: natural row order.
-      const int si = wave + C::NW * (t - C::A_PER_WAVE - C::W_HI);
-      const int pos = si * 64 + lane;
-      const float* src;
-      if (pos < 2 * C::BM) {
-        const int kk = pos / C::BM, rem = pos % C::BM;
-        const int wv = rem / C::WM, u = rem % C::WM;
-        const int row = wv * C::WM + (u % C::FI) * 16 + u / C::FI;
-        int64_t gr = m0 + row;
-        if (gr > p.M - 1) gr = p.M - 1;
-        src = p.sa + gr * p.kg + (2 * kt + kk);
-      } else if (pos < 2 * (C::BM + C::BN)) {
-        const int pw = pos - 2 * C::BM;
-        const int kk = pw / C::BN, trow = pw % C::BN;
-        src = p.sw + w_row_of<C, SWIG>(p, n0, trow) * p.kg + (2 * kt + kk);
-      } else {
-        src = p.sw;  // padding: any valid address, never read back
-      }
+      const int ts = t - C::A_PER_WAVE - C::W_HI;
+      const int si = wave + C::NW * ts;
+      const int64_t off = (int64_t)kt * 2 + (int64_t)(s_vo[C::GROUP ? ts : 0] >> 2);  // floats
+      const float* src = (si * 64 < 2 * C::BM ? p.sa : p.sw) + off;
       __builtin_amdgcn_global_load_lds(src, LDS_AS(st + C::SA + C::SW + si * 256), 4, 0, 0);
     }
   };
@@ -317,10 +348,17 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
   for (int s0 = 0; s0 < NS - 1; ++s0)
     if (s0 < KT) {
 #pragma unroll
-      for (int t = 0; t < NDMA; ++t) issue_one(s0, t);
+      for (int t = 0; t < NDMA; ++t) issue_one(s0 == 0 ? sm0 : sm1, s0, t);
     }
 
-  for (int kt = 0; kt < KT; ++kt) {
+  for (int kb = 0; kb < KT; kb += NS) {
+#pragma unroll
+  for (int sc = 0; sc < NS; ++sc) {
+    const int kt = kb + sc;
+    if (kt >= KT) break;
+    uint8_t* const cur = sc == 0 ? sm0 : (sc == 1 ? sm1 : sm2);
+    const int sn = (sc + NS - 1) % NS;  // stage that kt + NS - 1 lands in
+    uint8_t* const nxt = sn == 0 ? sm0 : (sn == 1 ? sm1 : sm2);
     // Stage kt has landed once only the later stages (at most NS-2 of them)
     // are still in flight; the barrier then publishes every wave's part and
     // guarantees all waves finished reading the buffer the next load reuses.
@@ -333,7 +371,7 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
     lds_barrier();
     const bool dma = kt + NS - 1 < KT;
 
-    const uint8_t* As = smem + (kt % NS) * C::STAGE;
+    const uint8_t* As = cur;
     const uint8_t* Ws = As + C::SA;
     const uint8_t* Ss = Ws + C::SW;
     // W fragments: packed -> one b128 per fragment carries both halves (kk);
@@ -396,7 +434,7 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
               As + a_off[(q + PF) / C::FI] + ((q + PF) % C::FI) * 16 * C::ARB);
         af = abuf[q % (PF + 1)];
       }
-      if (dma && (q % 2) == 0 && q / 2 < NDMA) issue_one(kt + NS - 1, q / 2);
+      if (dma && (q % 2) == 0 && q / 2 < NDMA) issue_one(nxt, kt + NS - 1, q / 2);
       // second-half W fragments, spread over the first half's MFMA groups
       if (!GK && kk == 0 && i < C::FJ)
         bw1[i] = C::WP ? unpack_lo(wraw[i].z, wraw[i].w)
@@ -447,8 +485,74 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
     // any loads not yet issued (only if NDMA > NQ / 2)
     if (dma) {
 #pragma unroll
-      for (int t = NQ / 2; t < NDMA; ++t) issue_one(kt + NS - 1, t);
+      for (int t = NQ / 2; t < NDMA; ++t) issue_one(nxt, kt + NS - 1, t);
     }
+  }
+  }
+
+  // ---- staged bf16 epilogue ---------------------------------------------
+  // A lane holds 4 consecutive columns of one row per fragment, so direct
+  // stores write 32-byte row pieces, and the 128-byte lines that two wave
+  // columns share reach memory in parts.  For the plain bf16 output the tile
+  // is instead converted into LDS (the ring is free now), half the rows at a
+  // time, and written back as whole rows with 16-byte stores.
+  if constexpr (EPI == EPI_BF16 && !SWIG && !LOWRANK && C::WGM == 2) {
+    constexpr int RB = C::BN * 2;     // bytes of one tile row
+    constexpr int PITCH = RB + 16;    // LDS row pitch
+    constexpr int HR = C::WM;         // rows per pass: one wave row
+    constexpr int RPA = (HR + NS - 1) / NS;  // staging rows per ring array
+    static_assert(RPA * PITCH <= C::STAGE, "staging rows must fit the ring");
+    auto row_ptr = [&](int r) -> uint8_t* {
+      const int a = r / RPA, o = (r % RPA) * PITCH;
+      return a == 0 ? sm0 + o : (a == 1 ? sm1 + o : sm2 + o);
+    };
+    __syncthreads();  // every wave is done with the ring
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      if (wm == pass) {
+#pragma unroll
+        for (int j = 0; j < C::FJ; ++j) {
+          const int col = wn * C::WN + j * 16 + lg * 4;   // tile column
+          float swv[4], addv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            int64_t n = n0 + col + r;
+            if (n > p.N - 1) n = p.N - 1;
+            swv[r] = C::GROUP ? 1.f : p.sw[n * p.sw_stride];
+            addv[r] = p.bias ? bf16_to_f32(p.bias[n]) : 0.f;
+          }
+#pragma unroll
+          for (int i = 0; i < C::FI; ++i) {
+            int64_t m = m0 + wm * C::WM + i * 16 + l16;
+            if (m > p.M - 1) m = p.M - 1;
+            const float sam = C::GROUP ? p.post : p.sa[m * p.sa_stride] * p.post;
+            float y[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float v = C::GROUP ? yf[C::GROUP ? j : 0][C::GROUP ? i : 0][r]
+                                       : (float)acc[C::GROUP ? 0 : j][C::GROUP ? 0 : i][r];
+              y[r] = v * sam * swv[r] + addv[r];
+            }
+            const bf2 h0 = __builtin_convertvector(f2{y[0], y[1]}, bf2);
+            const bf2 h1 = __builtin_convertvector(f2{y[2], y[3]}, bf2);
+            *reinterpret_cast<uint2*>(row_ptr(i * 16 + l16) + col * 2) =
+                make_uint2(__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1));
+          }
+        }
+      }
+      __syncthreads();
+      constexpr int CH = RB / 16;  // 16-byte chunks per row (8 columns each)
+      for (int c = tid; c < HR * CH; c += C::NT) {
+        const int r = c / CH, ch = c % CH;
+        const int64_t m = m0 + pass * HR + r;
+        const int64_t n = n0 + ch * 8;  // 16 | N: a chunk is wholly in or out
+        const uint4 v = *reinterpret_cast<const uint4*>(row_ptr(r) + ch * 16);
+        if (m < p.M && n < p.N)
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + m * p.ldo + n) = v;
+      }
+      __syncthreads();
+    }
+    return;
   }
 
   // ---- epilogue: lane holds out[m][n .. n+3] for each (i, j) --------------
