@@ -19,7 +19,7 @@
 //
 // Quantization (per tensor, per row, or per row x 64-channel group):
 //   amax = max |z| over the unit,  inv = qmax / amax (correctly rounded fp32),
-//   code = clamp(rint(z * inv), -qmax, qmax),  scale = amax / qmax (/16 if rotated).
+//   code = rint(z * inv) (already within [-qmax, qmax]),  scale = amax / qmax (/16 if rotated).
 // A 64-channel group inside a 256-group is one value of d3, i.e. one quad of
 // lanes.
 
@@ -76,139 +76,162 @@ __device__ __forceinline__ float quad_max(float m) {
   return m;
 }
 
-// Encode 16 codes (channel order) and store them.
+// Round to nearest integer, ties to even, for |x| < 2^22: adding 1.5 * 2^23
+// leaves the rounded integer in the low mantissa bits, so the low byte of
+// the sum's bit pattern is the code in two's complement.  The product and
+// the sum are separate correctly rounded operations (no fusion).
+__device__ __forceinline__ uint32_t code_bits(float x, float inv) {
+#pragma clang fp contract(off)
+  const float prod = x * inv;
+  return __float_as_uint(prod + 12582912.0f);
+}
+
+// Bytes 0 of a, b, c, d -> one dword [a, b, c, d].
+__device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);  // a.b0 | b.b0 << 8
+  const uint32_t hi = __builtin_amdgcn_perm(d, c, 0x04000c0cu);  // c.b0 << 16 | d.b0 << 24
+  return lo | hi;
+}
+
+// Encode 16 codes (channel order, as code_bits) and store them.
 __device__ __forceinline__ void store_codes(void* codes, int64_t off_elems, bool packed,
-                                            const int (&q)[16]) {
+                                            const uint32_t (&u)[16]) {
   if (!packed) {
     uint4 w;
-    uint32_t* wp = reinterpret_cast<uint32_t*>(&w);
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      wp[k] = (uint32_t)(q[4 * k] & 0xff) | ((uint32_t)(q[4 * k + 1] & 0xff) << 8) |
-              ((uint32_t)(q[4 * k + 2] & 0xff) << 16) | ((uint32_t)(q[4 * k + 3] & 0xff) << 24);
+    w.x = pack4(u[0], u[1], u[2], u[3]);
+    w.y = pack4(u[4], u[5], u[6], u[7]);
+    w.z = pack4(u[8], u[9], u[10], u[11]);
+    w.w = pack4(u[12], u[13], u[14], u[15]);
     *reinterpret_cast<uint4*>(static_cast<int8_t*>(codes) + off_elems) = w;
   } else {
     // byte 4c+j: low nibble channel 8c+j, high nibble channel 8c+j+4
     uint2 w;
-    uint32_t* wp = reinterpret_cast<uint32_t*>(&w);
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t b = (uint32_t)(q[8 * c + j] & 0xf) | ((uint32_t)(q[8 * c + j + 4] & 0xf) << 4);
-        word |= b << (8 * j);
-      }
-      wp[c] = word;
-    }
+    const uint32_t l0 = pack4(u[0], u[1], u[2], u[3]), h0 = pack4(u[4], u[5], u[6], u[7]);
+    const uint32_t l1 = pack4(u[8], u[9], u[10], u[11]), h1 = pack4(u[12], u[13], u[14], u[15]);
+    w.x = (l0 & 0x0F0F0F0Fu) | ((h0 << 4) & 0xF0F0F0F0u);
+    w.y = (l1 & 0x0F0F0F0Fu) | ((h1 << 4) & 0xF0F0F0F0u);
     *reinterpret_cast<uint2*>(static_cast<uint8_t*>(codes) + off_elems / 2) = w;
   }
 }
 
+// One workgroup handles blocks of rows_per_wg rows, slots_per_row 16-lane
+// slots per row, GPL groups per slot; it loops over blocks blockIdx.x,
+// blockIdx.x + gridDim.x, ... (one block each unless the grid is capped).
 // phase 0: quantize (row / group64, or tensor mode reading the absmax cell)
 // phase 1: tensor mode, absmax only (atomicMax into the cell)
 template <int GPL>
-__global__ __launch_bounds__(kThreads) void rq_kernel(RqArgs a, int slots_per_row,
-                                                      int rows_per_wg, int phase) {
-  __shared__ float red[16];
+__global__ __launch_bounds__(kThreads) void rq_kernel(RqArgs a, int slots_per_row, int rows_per_wg,
+                                                      int phase, int64_t nblocks) {
+  __shared__ float red[2][16];
   const int tid = threadIdx.x;
   const int slot = tid >> 4;
   const int t = tid & 15;
   const int row_in_wg = slot / slots_per_row;
   const int sir = slot - row_in_wg * slots_per_row;
-  const int64_t row = (int64_t)blockIdx.x * rows_per_wg + row_in_wg;
   const int ngroups = (int)(a.K >> 8);
-  const bool row_ok = (row_in_wg < rows_per_wg) && (row < a.M);
+  const float qmax = a.bits == 4 ? 7.0f : 127.0f;
+  const float post = a.rotate ? 0.0625f : 1.0f;  // z = 16 x' when rotated
 
-  float v[GPL][16];
+  uint4 raw[GPL][2];
+  auto load = [&](int64_t blk) {
+    const int64_t row = blk * rows_per_wg + row_in_wg;
+    const bool row_ok = (row_in_wg < rows_per_wg) && (row < a.M);
 #pragma unroll
-  for (int j = 0; j < GPL; ++j) {
-    const int g = sir + j * slots_per_row;
-    if (row_ok && g < ngroups) {
-      const uint4* p = reinterpret_cast<const uint4*>(a.x + row * a.ldx + (int64_t)g * 256 + t * 16);
-      const uint4 u0 = p[0];
-      const uint4 u1 = p[1];
-      const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    for (int j = 0; j < GPL; ++j) {
+      const int g = sir + j * slots_per_row;
+      if (row_ok && g < ngroups) {
+        const uint4* p = reinterpret_cast<const uint4*>(a.x + row * a.ldx + (int64_t)g * 256 + t * 16);
+        raw[j][0] = p[0];
+        raw[j][1] = p[1];
+      } else {
+        raw[j][0] = make_uint4(0, 0, 0, 0);
+        raw[j][1] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  int it = 0;
+  for (int64_t blk = blockIdx.x; blk < nblocks; blk += gridDim.x, ++it) {
+    const int64_t row = blk * rows_per_wg + row_in_wg;
+    const bool row_ok = (row_in_wg < rows_per_wg) && (row < a.M);
+    load(blk);
+    float v[GPL][16];
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) {
+      const uint32_t w[8] = {raw[j][0].x, raw[j][0].y, raw[j][0].z, raw[j][0].w,
+                             raw[j][1].x, raw[j][1].y, raw[j][1].z, raw[j][1].w};
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         v[j][2 * k] = __uint_as_float(w[k] << 16);
         v[j][2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
       }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) v[j][e] = 0.0f;
     }
-  }
 
-  if (a.rotate) {
+    if (a.rotate) {
 #pragma unroll
-    for (int j = 0; j < GPL; ++j) hadamard256(v[j]);
-  }
+      for (int j = 0; j < GPL; ++j) hadamard256(v[j]);
+    }
 
-  const float qmax = a.bits == 4 ? 7.0f : 127.0f;
-  const float post = a.rotate ? 0.0625f : 1.0f;  // z = 16 x' when rotated
-
-  // per-unit absmax
-  float amax[GPL];
-  if (a.mode == 2) {  // group64: one quad of lanes per 64-channel group
+    // per-unit absmax
+    float amax[GPL];
+    if (a.mode == 2) {  // group64: one quad of lanes per 64-channel group
 #pragma unroll
-    for (int j = 0; j < GPL; ++j) {
+      for (int j = 0; j < GPL; ++j) {
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[j][e]));
+        amax[j] = quad_max(m);
+      }
+    } else {  // row or tensor: reduce over the row's slots
       float m = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[j][e]));
-      amax[j] = quad_max(m);
-    }
-  } else {  // row or tensor: reduce over the row's slots
-    float m = 0.0f;
+      for (int j = 0; j < GPL; ++j)
 #pragma unroll
-    for (int j = 0; j < GPL; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[j][e]));
-    m = row16_max(m);
-    if (t == 0) red[slot] = m;
-    __syncthreads();
-    if (phase == 1) {
-      if (tid == 0) {
-        float wm = 0.0f;
-        for (int s = 0; s < 16; ++s) wm = fmaxf(wm, red[s]);
-        atomicMax(reinterpret_cast<unsigned int*>(a.scales), __float_as_uint(wm));
+        for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[j][e]));
+      m = row16_max(m);
+      float* rb = red[it & 1];  // alternate buffers: one barrier per block
+      if (t == 0) rb[slot] = m;
+      __syncthreads();
+      if (phase == 1) {
+        if (tid == 0) {
+          float wm = 0.0f;
+          for (int s2 = 0; s2 < 16; ++s2) wm = fmaxf(wm, rb[s2]);
+          atomicMax(reinterpret_cast<unsigned int*>(a.scales), __float_as_uint(wm));
+        }
+        continue;
       }
-      return;
-    }
-    float rm;
-    if (a.mode == 0) {
-      rm = __uint_as_float(*reinterpret_cast<const volatile unsigned int*>(a.scales));
-    } else {
-      rm = 0.0f;
-      const int s0 = row_in_wg * slots_per_row;
-      for (int s = 0; s < slots_per_row; ++s) rm = fmaxf(rm, red[(s0 + s) & 15]);
-    }
+      float rm;
+      if (a.mode == 0) {
+        rm = __uint_as_float(*reinterpret_cast<const volatile unsigned int*>(a.scales));
+      } else {
+        rm = 0.0f;
+        const int s0 = row_in_wg * slots_per_row;
+        for (int s2 = 0; s2 < slots_per_row; ++s2) rm = fmaxf(rm, rb[(s0 + s2) & 15]);
+      }
 #pragma unroll
-    for (int j = 0; j < GPL; ++j) amax[j] = rm;
-  }
+      for (int j = 0; j < GPL; ++j) amax[j] = rm;
+    }
 
-  if (!row_ok) return;
+    if (!row_ok) continue;
 
-  const int64_t code_row = row * a.K;
+    // |z * inv| <= qmax (1 + 2^-23) since |z| <= amax, so the rounded code
+    // never leaves [-qmax, qmax] and needs no clamp.
+    const int64_t code_row = row * a.K;
 #pragma unroll
-  for (int j = 0; j < GPL; ++j) {
-    const int g = sir + j * slots_per_row;
-    if (g >= ngroups) continue;
-    const float am = amax[j];
-    const float inv = am > 0.0f ? __fdiv_rn(qmax, am) : 0.0f;
-    int q[16];
+    for (int j = 0; j < GPL; ++j) {
+      const int g = sir + j * slots_per_row;
+      if (g >= ngroups) continue;
+      const float am = amax[j];
+      const float inv = am > 0.0f ? __fdiv_rn(qmax, am) : 0.0f;
+      uint32_t u[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float r = __builtin_rintf(v[j][e] * inv);
-      r = fminf(fmaxf(r, -qmax), qmax);
-      q[e] = (int)r;
-    }
-    store_codes(a.codes, code_row + (int64_t)g * 256 + t * 16, a.packed != 0, q);
-    if (a.mode == 2) {
-      if ((t & 3) == 0)
-        a.scales[row * (a.K >> 6) + g * 4 + (t >> 2)] = __fdiv_rn(am, qmax) * post;
-    } else if (a.mode == 1 && t == 0 && sir == 0 && j == 0) {
-      a.scales[row] = __fdiv_rn(am, qmax) * post;
+      for (int e = 0; e < 16; ++e) u[e] = code_bits(v[j][e], inv);
+      store_codes(a.codes, code_row + (int64_t)g * 256 + t * 16, a.packed != 0, u);
+      if (a.mode == 2) {
+        if ((t & 3) == 0)
+          a.scales[row * (a.K >> 6) + g * 4 + (t >> 2)] = __fdiv_rn(am, qmax) * post;
+      } else if (a.mode == 1 && t == 0 && sir == 0 && j == 0) {
+        a.scales[row] = __fdiv_rn(am, qmax) * post;
+      }
     }
   }
 }
@@ -241,10 +264,14 @@ Plan plan_rows(int ngroups) {
   return best;
 }
 
+// Workgroups launched at most (16 per CU of MI355X); larger inputs loop.
+constexpr int64_t kRqMaxGrid = 4096;
+
 template <int GPL>
 hipError_t launch_rq(const RqArgs& a, const Plan& p, int phase, hipStream_t s) {
-  const unsigned blocks = (unsigned)((a.M + p.rows - 1) / p.rows);
-  hipLaunchKernelGGL(rq_kernel<GPL>, dim3(blocks), dim3(kThreads), 0, s, a, p.slots, p.rows, phase);
+  const int64_t nblocks = (a.M + p.rows - 1) / p.rows;
+  const unsigned grid = (unsigned)(nblocks < kRqMaxGrid ? nblocks : kRqMaxGrid);
+  hipLaunchKernelGGL(rq_kernel<GPL>, dim3(grid), dim3(kThreads), 0, s, a, p.slots, p.rows, phase, nblocks);
   return hipGetLastError();
 }
 
