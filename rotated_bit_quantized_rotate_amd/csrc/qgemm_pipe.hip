@@ -351,6 +351,15 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
       for (int t = 0; t < NDMA; ++t) issue_one(s0 == 0 ? sm0 : sm1, s0, t);
     }
 
+  // Tensor / row scales: the MFMA group of a stage's last A fragment is
+  // deferred into the next stage, right after its barrier and first
+  // fragment reads, so the MFMA pipe has work while those reads are in
+  // flight (both waves of a SIMD leave the barrier together and would
+  // otherwise wait on them at the same time).  Its operands (the stage's
+  // second-half W fragments and last A fragment) stay in registers.
+  constexpr bool DEFER = !C::GROUP && C::WP;  // int8 W: not enough registers
+  v4i bw1[C::FJ];
+  v4i af_def = v4i{0, 0, 0, 0};
   for (int kb = 0; kb < KT; kb += NS) {
 #pragma unroll
   for (int sc = 0; sc < NS; ++sc) {
@@ -378,7 +387,7 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
     // int8 -> one b128 per fragment and half.
     uint4 wraw[GK ? 1 : C::FJ];
     uint4 wraw1[(C::WP || GK) ? 1 : C::FJ];
-    v4i bw0[C::FJ], bw1[C::FJ];
+    v4i bw0[C::FJ];
     if (GK) {
 #pragma unroll
       for (int j = 0; j < C::FJ; ++j) {
@@ -396,7 +405,7 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
     }
     // A fragments: int8 -> streamed through a small window read PF ahead;
     // packed -> one b128 per fragment carries both halves.
-    constexpr int PF = 3;
+    constexpr int PF = 2;
     constexpr int NQ = 2 * C::FI;
     v4i abuf[PF + 1];
     uint4 araw[(C::AP && !GK) ? C::FI : 1];
@@ -410,6 +419,13 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
 #pragma unroll
       for (int q = 0; q < PF; ++q)
         abuf[q] = *reinterpret_cast<const v4i*>(As + a_off[q / C::FI] + (q % C::FI) * 16 * C::ARB);
+    }
+    if (DEFER && kt > 0) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < C::FJ; ++j)
+        acc[j][C::FI - 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bw1[j], af_def, acc[j][C::FI - 1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (!GK) {
 #pragma unroll
@@ -446,11 +462,15 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
                          : v4i{(int)wraw1[j].x, (int)wraw1[j].y, (int)wraw1[j].z, (int)wraw1[j].w};
       }
       if (!C::GROUP) {
-        __builtin_amdgcn_sched_barrier(0);
+        if (DEFER && q == NQ - 1) {
+          af_def = af;  // issued after the next barrier (or after the loop)
+        } else {
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < C::FJ; ++j)
-          acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kk == 0 ? bw0[j] : bw1[j], af, acc[j][i], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+          for (int j = 0; j < C::FJ; ++j)
+            acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kk == 0 ? bw0[j] : bw1[j], af, acc[j][i], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       } else {
         if (i == 0) {
           // scales of group kk: s_a of the lane's FI rows, s_w of its 4
@@ -489,18 +509,32 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
     }
   }
   }
+  if (DEFER && KT > 0) {
+#pragma unroll
+    for (int j = 0; j < C::FJ; ++j)
+      acc[j][C::FI - 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bw1[j], af_def, acc[j][C::FI - 1], 0, 0, 0);
+  }
 
-  // ---- staged bf16 epilogue ---------------------------------------------
+  // ---- staged epilogue (plain bf16 and gated residual) ---------------------
   // A lane holds 4 consecutive columns of one row per fragment, so direct
   // stores write 32-byte row pieces, and the 128-byte lines that two wave
-  // columns share reach memory in parts.  For the plain bf16 output the tile
-  // is instead converted into LDS (the ring is free now), half the rows at a
-  // time, and written back as whole rows with 16-byte stores.
-  if constexpr (EPI == EPI_BF16 && !SWIG && !LOWRANK && C::WGM == 2) {
-    constexpr int RB = C::BN * 2;     // bytes of one tile row
-    constexpr int PITCH = RB + 16;    // LDS row pitch
-    constexpr int HR = C::WM;         // rows per pass: one wave row
+  // columns share reach memory in parts.  Instead the tile goes through LDS
+  // (the ring is free now) a band of rows at a time and leaves as whole rows
+  // with 16-byte stores.  bf16 output: the band holds finished bf16 values
+  // (two bands of BM/2 rows).  Gated residual: the band holds y in fp32 (four
+  // bands of BM/4 rows), and the copy-out reads the residual with the same
+  // coalesced 16-byte accesses, so out = res + gate * y is still rounded
+  // once.
+  if constexpr ((EPI == EPI_BF16 || EPI == EPI_GATED) && !SWIG && !LOWRANK && C::WGM == 2) {
+    constexpr bool F32 = EPI == EPI_GATED;
+    constexpr int EB = F32 ? 4 : 2;          // staged bytes per value
+    constexpr int NB = F32 ? 4 : 2;          // bands
+    constexpr int HR = C::BM / NB;           // rows per band
+    constexpr int FPB = C::FI * 2 / NB;      // fragments of a wave per band (FI * 16 = BM / 2)
+    constexpr int RB = C::BN * EB;           // staged bytes of one tile row
+    constexpr int PITCH = RB + 16;           // LDS row pitch
     constexpr int RPA = (HR + NS - 1) / NS;  // staging rows per ring array
+    static_assert(C::FI * 16 * 2 == C::BM && (C::FI * 2) % NB == 0, "bands cover whole fragments");
     static_assert(RPA * PITCH <= C::STAGE, "staging rows must fit the ring");
     auto row_ptr = [&](int r) -> uint8_t* {
       const int a = r / RPA, o = (r % RPA) * PITCH;
@@ -508,8 +542,11 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
     };
     __syncthreads();  // every wave is done with the ring
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      if (wm == pass) {
+    for (int band = 0; band < NB; ++band) {
+      // the band's rows belong to wave row wm = band / (NB / 2), fragments
+      // i0 .. i0 + FPB - 1
+      if (wm == band / (NB / 2)) {
+        const int i0 = (band % (NB / 2)) * FPB;
 #pragma unroll
         for (int j = 0; j < C::FJ; ++j) {
           const int col = wn * C::WN + j * 16 + lg * 4;   // tile column
@@ -522,7 +559,8 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
             addv[r] = p.bias ? bf16_to_f32(p.bias[n]) : 0.f;
           }
 #pragma unroll
-          for (int i = 0; i < C::FI; ++i) {
+          for (int ii = 0; ii < FPB; ++ii) {
+            const int i = i0 + ii;
             int64_t m = m0 + wm * C::WM + i * 16 + l16;
             if (m > p.M - 1) m = p.M - 1;
             const float sam = C::GROUP ? p.post : p.sa[m * p.sa_stride] * p.post;
@@ -533,22 +571,43 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
                                        : (float)acc[C::GROUP ? 0 : j][C::GROUP ? 0 : i][r];
               y[r] = v * sam * swv[r] + addv[r];
             }
-            const bf2 h0 = __builtin_convertvector(f2{y[0], y[1]}, bf2);
-            const bf2 h1 = __builtin_convertvector(f2{y[2], y[3]}, bf2);
-            *reinterpret_cast<uint2*>(row_ptr(i * 16 + l16) + col * 2) =
-                make_uint2(__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1));
+            uint8_t* dst = row_ptr(ii * 16 + l16) + col * EB;
+            if (F32) {
+              *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+            } else {
+              const bf2 h0 = __builtin_convertvector(f2{y[0], y[1]}, bf2);
+              const bf2 h1 = __builtin_convertvector(f2{y[2], y[3]}, bf2);
+              *reinterpret_cast<uint2*>(dst) =
+                  make_uint2(__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1));
+            }
           }
         }
       }
       __syncthreads();
-      constexpr int CH = RB / 16;  // 16-byte chunks per row (8 columns each)
+      constexpr int CH = C::BN / 8;  // 8-column chunks per row (16 bf16 bytes out)
       for (int c = tid; c < HR * CH; c += C::NT) {
         const int r = c / CH, ch = c % CH;
-        const int64_t m = m0 + pass * HR + r;
+        const int64_t m = m0 + band * HR + r;
         const int64_t n = n0 + ch * 8;  // 16 | N: a chunk is wholly in or out
-        const uint4 v = *reinterpret_cast<const uint4*>(row_ptr(r) + ch * 16);
-        if (m < p.M && n < p.N)
-          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + m * p.ldo + n) = v;
+        if (m >= p.M || n >= p.N) continue;
+        uint16_t* o = static_cast<uint16_t*>(p.out) + m * p.ldo + n;
+        if (F32) {
+          const float4 y0 = *reinterpret_cast<const float4*>(row_ptr(r) + ch * 32);
+          const float4 y1 = *reinterpret_cast<const float4*>(row_ptr(r) + ch * 32 + 16);
+          const uint4 rr = *reinterpret_cast<const uint4*>(p.residual + m * p.ldo + n);
+          const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+          const uint32_t rw[4] = {rr.x, rr.y, rr.z, rr.w};
+          uint32_t ow[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {  // gate is only 2-byte aligned: element loads
+            const float a0 = __builtin_fmaf(bf16_to_f32(p.gate[n + 2 * e]), yv[2 * e], bf16_to_f32(rw[e] & 0xffff));
+            const float a1 = __builtin_fmaf(bf16_to_f32(p.gate[n + 2 * e + 1]), yv[2 * e + 1], bf16_to_f32(rw[e] >> 16));
+            ow[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a0, a1}, bf2));
+          }
+          *reinterpret_cast<uint4*>(o) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+        } else {
+          *reinterpret_cast<uint4*>(o) = *reinterpret_cast<const uint4*>(row_ptr(r) + ch * 16);
+        }
       }
       __syncthreads();
     }
