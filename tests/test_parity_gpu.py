@@ -343,6 +343,62 @@ def test_w8a8_gated_residual_same_codes(Q):
     _assert_bf16_close(bf16_bits(plain), y, np.abs(y))
 
 
+def _sample_rows(M, n=48):
+    rng = np.random.default_rng(M)
+    return np.unique(np.concatenate([np.arange(8), M - 1 - np.arange(8), rng.choice(M, n, replace=False)]))
+
+
+@pytest.mark.parametrize("w8", [False, True])
+def test_wide_tile_staged_epilogue_ragged(Q, w8):
+    """The 256 x 320 tiles (chosen once a shape needs more than 256 tiles of
+    256 x 256) with ragged M and N, a strided output (ldo > N) and the
+    LDS-staged bf16 and gated-residual epilogues, against the oracle's
+    dequantized product on sampled rows."""
+    import torch
+
+    M, N, K = 4059, 5104, 512
+    rng = np.random.default_rng(21)
+    qmax = 127 if w8 else 7
+    qa = rng.integers(-qmax, qmax + 1, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-qmax, qmax + 1, size=(N, K)).astype(np.int8)
+    sa_h = (rng.random(M, dtype=np.float32) * 0.02 + 0.01).astype(np.float32)
+    sw_h = (rng.random(N, dtype=np.float32) * 0.02 + 0.01).astype(np.float32)
+    rows = _sample_rows(M)
+    acc = O.int_gemm(qa[rows], qw).astype(np.float64)
+    y = acc * sa_h[rows].astype(np.float64)[:, None] * sw_h.astype(np.float64)[None, :]
+    big = torch.zeros((M, N + 16), dtype=torch.bfloat16, device="cuda")
+    out = big[:, :N]
+    a, w, sa, sw = to_dev(qa), to_dev(qw if w8 else O.pack_int4(qw)), to_dev(sa_h), to_dev(sw_h)
+    if w8:
+        Q.qgemm_w8a8(a, sa, w, sw, epilogue="bf16", out=out)
+    else:
+        Q.qgemm_w4a4(a, sa, w, sw, K, epilogue="bf16", out=out)
+    torch.cuda.synchronize()
+    _assert_bf16_close(bf16_bits(out)[rows], y, np.abs(y))
+    assert not big[:, N:].any().item(), "store past the row end"
+    if not w8:
+        return
+    res_h = _rand_bf16(22, (M, N))
+    gate_h = _rand_bf16(23, (N,))
+    res = to_dev_bf16(res_h)
+    Q.qgemm_w8a8(a, sa, w, sw, residual=res, gate=to_dev_bf16(gate_h), epilogue="gated_residual", out=res)
+    torch.cuda.synchronize()
+    r64 = O.bf16_bits_to_f64(res_h)[rows]
+    g64 = O.bf16_bits_to_f64(gate_h)
+    ref = r64 + g64[None, :] * y
+    _assert_bf16_close(bf16_bits(res)[rows], ref, np.abs(r64) + np.abs(y * g64[None, :]))
+    # gate 0 returns the residual bit for bit, except that a residual of -0
+    # comes back as +0 (IEEE: -0 + 0*y = +0 for y >= 0), as in the oracle
+    zero_gate = torch.zeros(N, dtype=torch.bfloat16, device="cuda")
+    out0 = Q.qgemm_w8a8(a, sa, w, sw, residual=to_dev_bf16(res_h), gate=zero_gate, epilogue="gated_residual")
+    torch.cuda.synchronize()
+    got0 = bf16_bits(out0)
+    both_zero = ((got0 & 0x7FFF) == 0) & ((res_h & 0x7FFF) == 0)
+    bad = np.argwhere((got0 != res_h) & ~both_zero)
+    assert bad.size == 0, (f"{len(bad)} outputs differ from the residual, first at {bad[:4].tolist()}: "
+                           f"{got0[tuple(bad[0])]:#06x} vs {res_h[tuple(bad[0])]:#06x}")
+
+
 @pytest.mark.parametrize("rank", [0, 32])
 @pytest.mark.parametrize("epi", ["swiglu", "bf16"])
 def test_group64_lowrank_same_codes(Q, rank, epi):
