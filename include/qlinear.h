@@ -25,7 +25,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
- *    allocates nothing, frees nothing and keeps no mutable global state.
+ *    allocates nothing and frees nothing.  Its only global state is a
+ *    per-device cache of the device-architecture check.
  *  - bf16 values travel as uint16_t bit patterns.  Matrices are row-major
  *    with the row stride given in elements.
  *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
@@ -45,6 +46,9 @@
  *  - K must be a positive multiple of 256 (one rotation group) for every
  *    call; M may be any value >= 0 (M == 0 enqueues nothing); N must be a
  *    positive multiple of 16.
+ *  - GEMM size limits (the kernels address operands with 32-bit offsets):
+ *    K < 2^23, N * K < 2^31 and M * K < 2^36.  Violations return
+ *    QL_ERR_SHAPE.
  */
 #ifndef QLINEAR_H
 #define QLINEAR_H

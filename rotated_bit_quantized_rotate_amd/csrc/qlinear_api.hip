@@ -112,6 +112,9 @@ static int validate_gemm_common(const void* a, const float* sa, const void* w, c
                                 int64_t M, int64_t N, int64_t K, const uint16_t* bias, void* out,
                                 int64_t ldo, int epilogue) {
   if (M < 0 || N <= 0 || N % 16 != 0 || K <= 0 || K % 256 != 0) return QL_ERR_SHAPE;
+  // the GEMM kernels address operands, scales included, with 32-bit offsets
+  if (K >= (int64_t(1) << 23) || N * K >= (int64_t(1) << 31) || M >= (int64_t(1) << 36) / K)
+    return QL_ERR_SHAPE;
   const int64_t out_cols = epilogue == QL_EPI_SWIGLU ? N / 2 : N;
   if (ldo < out_cols) return QL_ERR_SHAPE;
   if (M > 0 && (!a || !sa || !w || !sw || !out)) return QL_ERR_NULL;

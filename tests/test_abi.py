@@ -101,6 +101,10 @@ def test_qgemm_w4a4_validation(L):
     assert g44(L, sw=NULL) == -1
     assert g44(L, w=MISALIGNED) == -3
     assert g44(L, am=2, wm=2, epi=4) == -4        # exact int32 output needs one scale per product
+    # size limits of the 32-bit operand offsets
+    assert g44(L, K=1 << 23, ldo=32) == -2
+    assert g44(L, N=1 << 20, K=1 << 11, ldo=1 << 20) == -2   # N * K = 2^31
+    assert g44(L, M=1 << 25, K=1 << 11) == -2                # M * K = 2^36
 
 
 def g88(L, **kw):
