@@ -66,7 +66,52 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 
 #define LDS_AS(p) ((__attribute__((address_space(3))) void*)(p))
 
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// Wave priority for quarter `level` (0..3) of a stage's MFMA groups: it
+// falls from 3 to 0 as the wave works through the stage, so when both waves
+// of a SIMD contend for the matrix pipe, the one further behind issues
+// first.  With equal priorities the older wave takes every contested slot,
+// runs ahead and then idles at the stage barrier while its partner finishes
+// alone with its read and load latencies exposed (measured on gfx950:
+// waves reached the barrier up to a third of a stage apart).
+__device__ __forceinline__ void stage_prio(int level) {
+  if (level <= 0) __builtin_amdgcn_s_setprio(3);
+  else if (level == 1) __builtin_amdgcn_s_setprio(2);
+  else if (level == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
+// Stage barrier.  The wave's own LDS reads are complete first, so no read
+// of a ring stage can still be in flight when another wave, past the
+// barrier, starts loading into that stage.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Direct global -> LDS load (global_load_lds, saddr form): lane l moves 16
+// (dma_b128) or 4 (dma_b32) bytes from base + voff[l] to LDS address
+// lds + l * size; base is wave-uniform, lds goes through M0.  Written as asm
+// so the compiler does not track these loads: its wait-count pass cannot
+// tell which ring stage a load fills and would drain every load in flight
+// (the prefetch of later stages included) before a stage's first fragment
+// read.  The kernel orders them itself with wait_vmcnt + barrier.  No VGPR
+// is written, so nothing the compiler allocates is overwritten later.  The
+// compiler's hazard pass does not look into the asm either: s_nop 4 gives
+// the five wait states a VMEM read of an SGPR (the base, M0) needs after a
+// VALU write of it (the base may come from v_readfirstlane).
+// (The base is passed through readfirstlane: it is uniform, but the compiler
+// does not always keep it in SGPRs, which the saddr operand requires.)
+__device__ __forceinline__ uint64_t sgpr_u64(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ void dma_b128(const void* base, uint32_t voff, const void* lds) {
+  const uint32_t la = (uint32_t)(uintptr_t)LDS_AS(lds);
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sgpr_u64(base)), "{m0}"(la));
+}
+__device__ __forceinline__ void dma_b32(const void* base, uint32_t voff, const void* lds) {
+  const uint32_t la = (uint32_t)(uintptr_t)LDS_AS(lds);
+  asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(sgpr_u64(base)), "{m0}"(la));
+}
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding).
 template <int N>
@@ -232,10 +277,6 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
   // then 2*BN W-scale positions, then padding).  A-scale positions put the
   // FI rows a lane reads (i*16 + l16 of its wave row) next to each other;
   // W-scale positions are in tile-row order.
-  // (Each load address goes through a named pointer variable: written
-  // inline as a pointer-plus-offset expression in the builtin call, the host
-  // pass of this compiler silently fails to instantiate the kernel and drops
-  // its launch stub; the build checks the library for that.)
   const int64_t a_row0 = m0 * lda;
   uint32_t a_vo[C::A_PER_WAVE];
 #pragma unroll
@@ -270,24 +311,24 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
     }  // padding slots load the first W scale, never read back
     s_vo[ts] = (uint32_t)(e * 4);
   }
+  // The stage advance goes into the 32-bit lane offset (one VALU add), so
+  // the SGPR bases stay loop-invariant.
+  const uint8_t* const a_base = p.a + a_row0;
   auto issue_one = [&](uint8_t* st, int kt, int t) {
     if (t < C::A_PER_WAVE) {
       const int q = wave + C::NW * t;
-      const uint8_t* src = p.a + (a_row0 + (int64_t)kt * C::ARB + (int64_t)a_vo[t]);
-      __builtin_amdgcn_global_load_lds(src, LDS_AS(st + q * 1024), 16, 0, 0);
+      dma_b128(a_base, a_vo[t] + (uint32_t)(kt * C::ARB), st + q * 1024);
     } else if (t < C::A_PER_WAVE + C::W_HI) {
       const int tw = t - C::A_PER_WAVE;
       if (tw < C::W_HI - 1 || w_hi) {
         const int q = wave + C::NW * tw;
-        const uint8_t* src = p.w + ((int64_t)kt * C::WRB + (int64_t)w_vo[tw]);
-        __builtin_amdgcn_global_load_lds(src, LDS_AS(st + C::SA + q * 1024), 16, 0, 0);
+        dma_b128(p.w, w_vo[tw] + (uint32_t)(kt * C::WRB), st + C::SA + q * 1024);
       }
     } else if (C::GROUP) {
       const int ts = t - C::A_PER_WAVE - C::W_HI;
       const int si = wave + C::NW * ts;
-      const int64_t off = (int64_t)kt * 2 + (int64_t)(s_vo[C::GROUP ? ts : 0] >> 2);  // floats
-      const float* src = (si * 64 < 2 * C::BM ? p.sa : p.sw) + off;
-      __builtin_amdgcn_global_load_lds(src, LDS_AS(st + C::SA + C::SW + si * 256), 4, 0, 0);
+      dma_b32(si * 64 < 2 * C::BM ? p.sa : p.sw, s_vo[C::GROUP ? ts : 0] + (uint32_t)(kt * 8),
+              st + C::SA + C::SW + si * 256);
     }
   };
 
@@ -378,6 +419,7 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
       wait_vmcnt<0>();
     }
     lds_barrier();
+    stage_prio(0);
     const bool dma = kt + NS - 1 < KT;
 
     const uint8_t* As = cur;
@@ -438,6 +480,7 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int kk = q / C::FI, i = q % C::FI;
+      if (q > 0 && (4 * q) % NQ < 4) stage_prio((4 * q) / NQ);
       v4i af;
       if (C::AP && GK) {
         const uint2 h = *reinterpret_cast<const uint2*>(As + a_off[kk] + i * 16 * C::ARB);
@@ -509,6 +552,36 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
     }
   }
   }
+  stage_prio(3);  // back to the lowest priority for the epilogue
+
+  // Staged epilogue: the tile's row factors (s_a * post) and column factors
+  // (s_w, bias, gate) as one vector of NV floats, fetched cooperatively (NVT
+  // per thread) before the last MFMAs so a single memory latency covers
+  // them all; they reach the other lanes through LDS.  Row factors are kept
+  // in the order the lanes read them: tile row wm * WM + 16 i + l16 at
+  // wm * WM + FI * l16 + i, so a lane's FI rows are contiguous.
+  constexpr bool STAGED = (EPI == EPI_BF16 || EPI == EPI_GATED) && !SWIG && !LOWRANK && C::WGM == 2;
+  constexpr int NV = C::BM + (EPI == EPI_GATED ? 3 : 2) * C::BN;
+  constexpr int NVT = STAGED ? (NV + C::NT - 1) / C::NT : 1;
+  float vec[NVT];
+  if constexpr (STAGED) {
+#pragma unroll
+    for (int u = 0; u < NVT; ++u) {
+      const int e = tid + u * C::NT;
+      float v = 0.f;
+      if (e < C::BM) {
+        const int64_t m = m0 + e > p.M - 1 ? p.M - 1 : m0 + e;
+        v = C::GROUP ? p.post : p.sa[m * p.sa_stride] * p.post;
+      } else if (e < NV) {
+        const int f = (e - C::BM) / C::BN;
+        const int64_t n = n0 + (e - C::BM) % C::BN > p.N - 1 ? p.N - 1 : n0 + (e - C::BM) % C::BN;
+        if (f == 0) v = C::GROUP ? 1.f : p.sw[n * p.sw_stride];
+        else if (f == 1) v = p.bias ? bf16_to_f32(p.bias[n]) : 0.f;
+        else v = bf16_to_f32(p.gate[n]);
+      }
+      vec[u] = v;
+    }
+  }
   if (DEFER && KT > 0) {
 #pragma unroll
     for (int j = 0; j < C::FJ; ++j)
@@ -536,34 +609,57 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
     constexpr int RPA = (HR + NS - 1) / NS;  // staging rows per ring array
     static_assert(C::FI * 16 * 2 == C::BM && (C::FI * 2) % NB == 0, "bands cover whole fragments");
     static_assert(RPA * PITCH <= C::STAGE, "staging rows must fit the ring");
+    // the factor vector sits behind the staging rows of the last ring array
+    constexpr int SVOFF = (RPA * PITCH + 15) / 16 * 16;
+    static_assert(SVOFF + 4 * NV <= C::STAGE, "factor vector must fit the ring");
+    float* const sv = reinterpret_cast<float*>((NS == 3 ? sm2 : sm1) + SVOFF);
     auto row_ptr = [&](int r) -> uint8_t* {
       const int a = r / RPA, o = (r % RPA) * PITCH;
       return a == 0 ? sm0 + o : (a == 1 ? sm1 + o : sm2 + o);
     };
-    __syncthreads();  // every wave is done with the ring
+    // The band barriers below order LDS only (lds_barrier: the wave's LDS
+    // accesses complete, then s_barrier).  __syncthreads would also wait for
+    // every global store issued so far, stalling each band on the previous
+    // band's writes to memory.
+    lds_barrier();  // every wave is done with the ring (its loads all landed)
+#pragma unroll
+    for (int u = 0; u < NVT; ++u) {
+      const int e = tid + u * C::NT;
+      if (e < C::BM) {
+        const int w = e / C::WM, r = e % C::WM;
+        sv[w * C::WM + (r % 16) * C::FI + r / 16] = vec[u];
+      } else if (e < NV) {
+        sv[e] = vec[u];
+      }
+    }
+    lds_barrier();
 #pragma unroll
     for (int band = 0; band < NB; ++band) {
       // the band's rows belong to wave row wm = band / (NB / 2), fragments
       // i0 .. i0 + FPB - 1
       if (wm == band / (NB / 2)) {
         const int i0 = (band % (NB / 2)) * FPB;
+        static_assert(FPB % 4 == 0, "row factors are read four at a time");
+        float samv[FPB];
+#pragma unroll
+        for (int f = 0; f < FPB / 4; ++f) {
+          const float4 s4 = *reinterpret_cast<const float4*>(sv + wm * C::WM + l16 * C::FI + i0 + 4 * f);
+          samv[4 * f] = s4.x;
+          samv[4 * f + 1] = s4.y;
+          samv[4 * f + 2] = s4.z;
+          samv[4 * f + 3] = s4.w;
+        }
 #pragma unroll
         for (int j = 0; j < C::FJ; ++j) {
           const int col = wn * C::WN + j * 16 + lg * 4;   // tile column
-          float swv[4], addv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            int64_t n = n0 + col + r;
-            if (n > p.N - 1) n = p.N - 1;
-            swv[r] = C::GROUP ? 1.f : p.sw[n * p.sw_stride];
-            addv[r] = p.bias ? bf16_to_f32(p.bias[n]) : 0.f;
-          }
+          const float4 sw4 = *reinterpret_cast<const float4*>(sv + C::BM + col);
+          const float4 ad4 = *reinterpret_cast<const float4*>(sv + C::BM + C::BN + col);
+          const float swv[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
+          const float addv[4] = {ad4.x, ad4.y, ad4.z, ad4.w};
 #pragma unroll
           for (int ii = 0; ii < FPB; ++ii) {
             const int i = i0 + ii;
-            int64_t m = m0 + wm * C::WM + i * 16 + l16;
-            if (m > p.M - 1) m = p.M - 1;
-            const float sam = C::GROUP ? p.post : p.sa[m * p.sa_stride] * p.post;
+            const float sam = samv[ii];
             float y[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -583,7 +679,7 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
           }
         }
       }
-      __syncthreads();
+      lds_barrier();
       constexpr int CH = C::BN / 8;  // 8-column chunks per row (16 bf16 bytes out)
       for (int c = tid; c < HR * CH; c += C::NT) {
         const int r = c / CH, ch = c % CH;
@@ -595,13 +691,16 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
           const float4 y0 = *reinterpret_cast<const float4*>(row_ptr(r) + ch * 32);
           const float4 y1 = *reinterpret_cast<const float4*>(row_ptr(r) + ch * 32 + 16);
           const uint4 rr = *reinterpret_cast<const uint4*>(p.residual + m * p.ldo + n);
+          const float4 g0 = *reinterpret_cast<const float4*>(sv + C::BM + 2 * C::BN + ch * 8);
+          const float4 g1 = *reinterpret_cast<const float4*>(sv + C::BM + 2 * C::BN + ch * 8 + 4);
           const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+          const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
           const uint32_t rw[4] = {rr.x, rr.y, rr.z, rr.w};
           uint32_t ow[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {  // gate is only 2-byte aligned: element loads
-            const float a0 = __builtin_fmaf(bf16_to_f32(p.gate[n + 2 * e]), yv[2 * e], bf16_to_f32(rw[e] & 0xffff));
-            const float a1 = __builtin_fmaf(bf16_to_f32(p.gate[n + 2 * e + 1]), yv[2 * e + 1], bf16_to_f32(rw[e] >> 16));
+          for (int e = 0; e < 4; ++e) {
+            const float a0 = __builtin_fmaf(gv[2 * e], yv[2 * e], bf16_to_f32(rw[e] & 0xffff));
+            const float a1 = __builtin_fmaf(gv[2 * e + 1], yv[2 * e + 1], bf16_to_f32(rw[e] >> 16));
             ow[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a0, a1}, bf2));
           }
           *reinterpret_cast<uint4*>(o) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
@@ -609,7 +708,7 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
           *reinterpret_cast<uint4*>(o) = *reinterpret_cast<const uint4*>(row_ptr(r) + ch * 16);
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
     return;
   }
