@@ -84,13 +84,16 @@ def gemm_source_hash(workload="attn_proj_w4a4") -> str:
     return h.hexdigest()[:16]
 
 
+WARMUP_S = 0.5  # default warm-up duration, seconds of steps
+
 def _parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None,
                    help="timed steps (default 200; 3 for the stack)")
     p.add_argument("--warmup", type=int, default=None,
-                   help="untimed warm-up steps (default 20; 1 for the stack)")
+                   help="untimed warm-up steps (default: as many as fill 0.5 s, at least 20; "
+                        "at least 1 for the stack)")
     p.add_argument("--workload", default="attn_proj_w4a4", choices=sorted(GEMM_KERNELS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true")
@@ -102,8 +105,12 @@ def _parse():
     stack = a.workload == "stack"
     if a.steps is None:
         a.steps = 3 if stack else 200
+    a.warmup_min = None
     if a.warmup is None:
-        a.warmup = 1 if stack else 20
+        # The GPU's clocks settle only after a fraction of a second of
+        # sustained load (a GEMM measured right after start-up runs ~15 %
+        # slower), so by default warm-up lasts 0.5 s of steps.
+        a.warmup_min = 1 if stack else 20
     return a
 
 
@@ -437,8 +444,17 @@ def main():
         for _, fn in case.launches:
             fn()
 
-    for _ in range(args.warmup):
-        step()
+    if args.warmup_min is None:
+        for _ in range(args.warmup):
+            step()
+    else:
+        w, t_w = 0, time.perf_counter()
+        while w < args.warmup_min or time.perf_counter() - t_w < WARMUP_S:
+            step()
+            w += 1
+            if w % (1 if args.workload == "stack" else 16) == 0:
+                torch.cuda.synchronize()  # keep the host within a few steps of the GPU
+        args.warmup = w
     torch.cuda.synchronize()
 
     # ---- timed region: exactly `steps` steps, synchronized on both sides.
