@@ -384,6 +384,34 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
   const int sa_off = (wm * C::WM + l16 * C::FI) * 4;
   const int sw_off = (2 * C::BM + wn * C::WN + 4 * lg) * 4;
 
+  // Staged epilogue: the tile's row factors (s_a * post) and column factors
+  // (s_w, bias, gate) as one vector of NV floats, fetched cooperatively (NVT
+  // per thread) before the K loop, so their latency hides under it; they
+  // reach the other lanes through LDS.  Row factors are kept
+  // in the order the lanes read them: tile row wm * WM + 16 i + l16 at
+  // wm * WM + FI * l16 + i, so a lane's FI rows are contiguous.
+  constexpr bool STAGED = (EPI == EPI_BF16 || EPI == EPI_GATED) && !SWIG && !LOWRANK && C::WGM == 2;
+  constexpr int NV = C::BM + (EPI == EPI_GATED ? 3 : 2) * C::BN;
+  constexpr int NVT = STAGED ? (NV + C::NT - 1) / C::NT : 1;
+  float vec[NVT];
+  if constexpr (STAGED) {
+#pragma unroll
+    for (int u = 0; u < NVT; ++u) {
+      const int e = tid + u * C::NT;
+      float v = 0.f;
+      if (e < C::BM) {
+        const int64_t m = m0 + e > p.M - 1 ? p.M - 1 : m0 + e;
+        v = C::GROUP ? p.post : p.sa[m * p.sa_stride] * p.post;
+      } else if (e < NV) {
+        const int f = (e - C::BM) / C::BN;
+        const int64_t n = n0 + (e - C::BM) % C::BN > p.N - 1 ? p.N - 1 : n0 + (e - C::BM) % C::BN;
+        if (f == 0) v = C::GROUP ? 1.f : p.sw[n * p.sw_stride];
+        else if (f == 1) v = p.bias ? bf16_to_f32(p.bias[n]) : 0.f;
+        else v = bf16_to_f32(p.gate[n]);
+      }
+      vec[u] = v;
+    }
+  }
   // prologue: stages 0 .. NS-2 in flight
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; ++s0)
@@ -554,34 +582,6 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
   }
   stage_prio(3);  // back to the lowest priority for the epilogue
 
-  // Staged epilogue: the tile's row factors (s_a * post) and column factors
-  // (s_w, bias, gate) as one vector of NV floats, fetched cooperatively (NVT
-  // per thread) before the last MFMAs so a single memory latency covers
-  // them all; they reach the other lanes through LDS.  Row factors are kept
-  // in the order the lanes read them: tile row wm * WM + 16 i + l16 at
-  // wm * WM + FI * l16 + i, so a lane's FI rows are contiguous.
-  constexpr bool STAGED = (EPI == EPI_BF16 || EPI == EPI_GATED) && !SWIG && !LOWRANK && C::WGM == 2;
-  constexpr int NV = C::BM + (EPI == EPI_GATED ? 3 : 2) * C::BN;
-  constexpr int NVT = STAGED ? (NV + C::NT - 1) / C::NT : 1;
-  float vec[NVT];
-  if constexpr (STAGED) {
-#pragma unroll
-    for (int u = 0; u < NVT; ++u) {
-      const int e = tid + u * C::NT;
-      float v = 0.f;
-      if (e < C::BM) {
-        const int64_t m = m0 + e > p.M - 1 ? p.M - 1 : m0 + e;
-        v = C::GROUP ? p.post : p.sa[m * p.sa_stride] * p.post;
-      } else if (e < NV) {
-        const int f = (e - C::BM) / C::BN;
-        const int64_t n = n0 + (e - C::BM) % C::BN > p.N - 1 ? p.N - 1 : n0 + (e - C::BM) % C::BN;
-        if (f == 0) v = C::GROUP ? 1.f : p.sw[n * p.sw_stride];
-        else if (f == 1) v = p.bias ? bf16_to_f32(p.bias[n]) : 0.f;
-        else v = bf16_to_f32(p.gate[n]);
-      }
-      vec[u] = v;
-    }
-  }
   if (DEFER && KT > 0) {
 #pragma unroll
     for (int j = 0; j < C::FJ; ++j)
