@@ -29,7 +29,10 @@ Parity status of each function is pinned by the ``-m "not gpu"`` tests:
 closed forms and Kronecker construction (Hadamard), involution (rotation),
 error bounds and ties (quantizer), documented byte example (packing),
 brute-force integer loops (GEMM), grid-exact end-to-end reconstruction
-(whole linear), the low-rank identity, and textbook SiLU values.  No function
+(whole linear), the low-rank identity, textbook SiLU values, and for the
+fused RMSNorm + modulation prologue closed forms (unit mean square, eps
+inside the root), scale invariance, a worked modulation example, brute-force
+loops and the reduction to the plain prologue when the norm is the identity.  No function
 here is "parity unpinned".
 """
 

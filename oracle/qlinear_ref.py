@@ -22,6 +22,7 @@ __all__ = [
     "int_gemm", "int_gemm_grouped",
     "silu", "epilogue",
     "QuantResult", "quantize_activations", "quantize_weights",
+    "rmsnorm_modulate", "quantize_activations_norm",
     "linear_fp64", "linear",
 ]
 
@@ -277,6 +278,40 @@ def quantize_activations(x_bits, bits: int, mode: str, rotate_on: bool = True) -
     xr = rotate(x) if rotate_on else x
     q, s = quantize(xr, bits, mode)
     return QuantResult(q, s, bits, mode, xr)
+
+
+def rmsnorm_modulate(x_bits, gamma_bits=None, scale_bits=None, shift_bits=None, eps: float = 1e-6) -> np.ndarray:
+    """RMSNorm followed by the adaLN modulation of a DiT block input, float64.
+
+    [OrbitQuant] "Fused transformer (OrbitQuant 0.11)": the block's RMSNorm
+    and modulation run inside the activation quantization prologues.  The page
+    names the two steps, not their formula; the reading taken is the usual one
+    for a batch-1 block (per-channel modulation vectors):
+
+        r[m]    = 1 / sqrt(mean_k x[m, k]^2 + eps)
+        h[m, k] = x[m, k] * r[m] * gamma[k] * (1 + scale[k]) + shift[k]
+
+    x_bits: bf16 bits [M, K]; gamma, scale, shift: bf16 bits [K] or None
+    (meaning 1, 0 and 0).  eps > 0."""
+    x = bf16_bits_to_f64(x_bits)
+    M, K = x.shape
+    gamma = np.ones(K) if gamma_bits is None else bf16_bits_to_f64(gamma_bits).reshape(K)
+    scale = np.zeros(K) if scale_bits is None else bf16_bits_to_f64(scale_bits).reshape(K)
+    shift = np.zeros(K) if shift_bits is None else bf16_bits_to_f64(shift_bits).reshape(K)
+    ms = np.mean(x * x, axis=1)                       # mean square of each row
+    r = 1.0 / np.sqrt(ms + eps)
+    return x * r[:, None] * (gamma * (1.0 + scale))[None, :] + shift[None, :]
+
+
+def quantize_activations_norm(x_bits, gamma_bits, scale_bits, shift_bits, eps: float, bits: int, mode: str,
+                              rotate_on: bool = True) -> QuantResult:
+    """The prologue with the norm fused in front: h = rmsnorm_modulate(x, ...)
+    (never rounded to bf16), then rotate and quantize h exactly as
+    quantize_activations does for x."""
+    h = rmsnorm_modulate(x_bits, gamma_bits, scale_bits, shift_bits, eps)
+    hr = rotate(h) if rotate_on else h
+    q, s = quantize(hr, bits, mode)
+    return QuantResult(q, s, bits, mode, hr)
 
 
 def quantize_weights(w_bits, bits: int, mode: str, rotate_on: bool = True) -> QuantResult:

@@ -382,3 +382,71 @@ def test_bf16_widening_is_exact():
     v = O.bf16_bits_to_f64(bits)
     fin = np.isfinite(v)
     assert (O.f64_to_bf16_bits(v[fin]) == bits[fin]).all()
+
+
+# ------------------------------------------- RMSNorm + modulation prologue --
+
+def test_rmsnorm_gives_unit_mean_square_without_eps():
+    # with eps = 0 and no modulation every row of h has mean square exactly 1
+    rng = np.random.default_rng(21)
+    x = to_bf16_bits(rng.normal(size=(5, 512)) * rng.uniform(0.1, 30.0, size=(5, 1)))
+    h = O.rmsnorm_modulate(x, eps=0.0)
+    assert np.allclose(np.mean(h * h, axis=1), 1.0, rtol=0, atol=1e-12)
+
+
+def test_rmsnorm_eps_sits_inside_the_root_next_to_the_mean():
+    # a constant row c: mean square c^2, so h = c / sqrt(c^2 + eps); c = 3, eps = 7 -> 3/4 exactly
+    x = to_bf16_bits(np.full((2, 256), 3.0))
+    h = O.rmsnorm_modulate(x, eps=7.0)
+    assert np.array_equal(h, np.full((2, 256), 0.75))
+    # mean (not sum) of squares: K = 256 constant channels of 1 with eps = 3 -> 1/2
+    h1 = O.rmsnorm_modulate(to_bf16_bits(np.ones((1, 256))), eps=3.0)
+    assert np.array_equal(h1, np.full((1, 256), 0.5))
+
+
+def test_rmsnorm_is_scale_invariant_without_eps():
+    rng = np.random.default_rng(22)
+    xf = rng.normal(size=(3, 256))
+    a = O.rmsnorm_modulate(to_bf16_bits(xf), eps=0.0)
+    b = O.rmsnorm_modulate(to_bf16_bits(xf * 8.0), eps=0.0)   # power of two: the bf16 inputs scale exactly
+    assert np.allclose(a, b, rtol=1e-15, atol=0)
+
+
+def test_modulation_worked_example():
+    # x = (1, -1, 1, -1) has mean square 1, so with eps = 0 the norm is the identity and
+    # h = x * gamma * (1 + scale) + shift:
+    #   gamma = (2, 1, 1, 1), scale = (0, 1, -0.5, 0), shift = (0, 0, 0, 0.25) -> (2, -2, 0.5, -0.75)
+    x = to_bf16_bits(np.array([[1.0, -1.0, 1.0, -1.0]]))
+    g = to_bf16_bits(np.array([2.0, 1.0, 1.0, 1.0]))
+    s = to_bf16_bits(np.array([0.0, 1.0, -0.5, 0.0]))
+    t = to_bf16_bits(np.array([0.0, 0.0, 0.0, 0.25]))
+    assert np.array_equal(O.rmsnorm_modulate(x, g, s, t, eps=0.0), np.array([[2.0, -2.0, 0.5, -0.75]]))
+
+
+def test_rmsnorm_modulate_matches_brute_force_loops():
+    # per-row factor, per-channel vectors (a transposed broadcast fails: M != K and the vectors differ)
+    rng = np.random.default_rng(23)
+    M, K, eps = 3, 8, 0.25
+    xb = to_bf16_bits(rng.normal(size=(M, K)))
+    gb, sb, tb = (to_bf16_bits(rng.normal(size=K)) for _ in range(3))
+    x, g, s, t = (O.bf16_bits_to_f64(v) for v in (xb, gb, sb, tb))
+    want = np.zeros((M, K))
+    for m in range(M):
+        acc = 0.0
+        for k in range(K):
+            acc += x[m, k] * x[m, k]
+        r = 1.0 / np.sqrt(acc / K + eps)
+        for k in range(K):
+            want[m, k] = x[m, k] * r * g[k] * (1.0 + s[k]) + t[k]
+    assert np.allclose(O.rmsnorm_modulate(xb, gb, sb, tb, eps=eps), want, rtol=1e-14, atol=1e-14)
+
+
+@pytest.mark.parametrize("bits,mode", [(4, "row"), (8, "group64"), (4, "tensor")])
+def test_norm_prologue_reduces_to_the_plain_prologue_when_the_norm_is_identity(bits, mode):
+    # rows of +-1 have mean square 1: with eps = 0 and no modulation h == x, so the fused
+    # prologue must give the plain prologue's codes and scales bit for bit
+    rng = np.random.default_rng(24)
+    x = to_bf16_bits(np.where(rng.random((4, 512)) < 0.5, -1.0, 1.0))
+    a = O.quantize_activations_norm(x, None, None, None, 0.0, bits, mode)
+    b = O.quantize_activations(x, bits, mode)
+    assert np.array_equal(a.codes, b.codes) and np.array_equal(a.scales, b.scales)
