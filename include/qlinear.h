@@ -133,6 +133,33 @@ int rotate_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                         const uint16_t* l1, int rank, uint16_t* lr,
                         void* stream);
 
+/* Activation prologue with the block's RMSNorm and adaLN modulation fused in
+ * front (model card "Krea 2 Turbo OrbitQuant W4A4", section "Fused
+ * transformer (OrbitQuant 0.11)": the norm and the modulation run inside the
+ * activation quantization prologue, so the normalized activation is never
+ * written).  The page names the steps; the formula is the usual batch-1
+ * reading:
+ *
+ *   h[m,k] = x[m,k] * r[m] * gamma[k] * (1 + mod_scale[k]) + mod_shift[k],
+ *   r[m]   = 1 / sqrt(mean_k x[m,k]^2 + eps),
+ *
+ * in fp32 (h is not rounded to bf16); h is then rotated and quantized exactly
+ * as rotate_quantize_act does with x.  One prepared activation serves every
+ * projection that reads the same normalized input (Q|K|V|gate, gate|up): the
+ * caller passes the same codes and scales to each GEMM.
+ *
+ *   x, M, K, ldx, bits, scale_mode, layout, rotate, codes, scales
+ *          as rotate_quantize_act; K <= 8192 (the vectors are staged on chip)
+ *   gamma, mod_scale, mod_shift   bf16 [K] each, 16-byte aligned, or NULL
+ *          (meaning all ones, all zeros, all zeros)
+ *   eps    > 0 and finite, else QL_ERR_SHAPE
+ * There is no low-rank output here (the SVDQuant branch reads the unrotated
+ * layer input; use rotate_quantize_act for that layer). */
+int rmsnorm_rotate_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                const uint16_t* gamma, const uint16_t* mod_scale,
+                                const uint16_t* mod_shift, float eps, int bits, int scale_mode,
+                                int layout, int rotate, void* codes, float* scales, void* stream);
+
 /* Offline weight preparation for INT4 (model card "Krea-2 Turbo -- INT4
  * tensorwise W4A4 (+ConvRot, mixed int8 fallback)", introduction: packed
  * signed INT4 weights carrying the same group-256 rotation).  Same

@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     qgemm_w4a4,
     qgemm_w4a4_lowrank,
     qgemm_w8a8,
+    rmsnorm_rotate_quantize_act,
     rotate_quantize_act,
     status_string,
 )

@@ -49,6 +49,8 @@ _SIGNATURES = {
     "ql_status_string": (ctypes.c_char_p, [_i]),
     "ql_device_supported": (_i, [_i]),
     "rotate_quantize_act": (_i, [_p, _i64, _i64, _i64, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p]),
+    "rmsnorm_rotate_quantize_act": (_i, [_p, _i64, _i64, _i64, _p, _p, _p, ctypes.c_float, _i, _i, _i, _i,
+                                         _p, _p, _p]),
     "pack_weight_int4": (_i, [_p, _i64, _i64, _i64, _i, _i, _p, _p, _p]),
     "qgemm_w4a4": (_i, [_p, _p, _i, _i, _p, _p, _i, _i64, _i64, _i64, _p, _i, _p, _i64, _p]),
     "qgemm_w8a8": (_i, [_p, _p, _i, _p, _p, _i, _i64, _i64, _i64, _p, _p, _p, _i, _p, _i64, _p]),
@@ -143,6 +145,30 @@ def rotate_quantize_act(x, bits=4, scale_mode="row", layout="i8", rotate=True, c
                                    _ptr(codes), _ptr(scales), _ptr(l1), rank, _ptr(lr), _stream(stream))
     _check("rotate_quantize_act", st)
     return codes, scales, lr
+
+
+def rmsnorm_rotate_quantize_act(x, gamma=None, mod_scale=None, mod_shift=None, eps=1e-6, bits=4,
+                                scale_mode="row", layout="i8", rotate=True, codes=None, scales=None,
+                                stream=None):
+    """x: bf16 [M, K]; gamma, mod_scale, mod_shift: bf16 [K] or None.  The
+    block's RMSNorm + modulation fused in front of rotate + quantize.
+    Returns (codes, scales)."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    M, K = x.shape
+    for v in (gamma, mod_scale, mod_shift):
+        assert v is None or (v.dtype == torch.bfloat16 and v.numel() == K and v.is_contiguous())
+    mode = _mode(scale_mode)
+    lay = _lay(layout)
+    if codes is None:
+        codes = torch.empty((M, K // 2) if lay == QL_LAYOUT_PACKED else (M, K),
+                            dtype=torch.uint8 if lay == QL_LAYOUT_PACKED else torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty(_scale_shape(M, K, mode), dtype=torch.float32, device=x.device)
+    st = lib().rmsnorm_rotate_quantize_act(_ptr(x), M, K, x.stride(0), _ptr(gamma), _ptr(mod_scale),
+                                           _ptr(mod_shift), float(eps), bits, mode, lay, int(bool(rotate)),
+                                           _ptr(codes), _ptr(scales), _stream(stream))
+    _check("rmsnorm_rotate_quantize_act", st)
+    return codes, scales
 
 
 def pack_weight_int4(w, scale_mode="row", rotate=True, packed=None, scales=None, stream=None):

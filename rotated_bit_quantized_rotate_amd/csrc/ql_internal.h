@@ -57,6 +57,13 @@ struct RqArgs {
   int rotate;      // 1: apply H per 256-group
   void* codes;
   float* scales;
+  // RMSNorm + modulation in front (norm != 0): h = x * r * gamma * (1 + scale) + shift,
+  // r = 1 / sqrt(mean(x^2) + eps); null vectors mean 1, 0, 0
+  int norm;
+  const uint16_t* gamma;
+  const uint16_t* mscale;
+  const uint16_t* mshift;
+  float eps;
 };
 
 int launch_rotate_quantize(const RqArgs& a, hipStream_t s);

@@ -96,6 +96,27 @@ int rotate_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, in
   return QL_OK;
 }
 
+int rmsnorm_rotate_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* gamma,
+                                const uint16_t* mod_scale, const uint16_t* mod_shift, float eps, int bits,
+                                int scale_mode, int layout, int rotate, void* codes, float* scales,
+                                void* stream) {
+  int st = validate_rq(x, M, K, ldx, bits, scale_mode, layout, rotate, codes, scales, nullptr, 0, nullptr);
+  if (st != QL_OK) return st;
+  // the per-channel vectors are staged in LDS (8 bytes per channel)
+  if (K > 8192) return QL_ERR_SHAPE;
+  if (!(eps > 0.0f) || eps > 3.0e38f) return QL_ERR_SHAPE;  // positive and finite (NaN fails too)
+  if (!al16(gamma) || !al16(mod_scale) || !al16(mod_shift)) return QL_ERR_ALIGN;
+  if ((st = check_current_device()) != QL_OK) return st;
+  if (M == 0) return QL_OK;
+  ql::RqArgs a{x, M, K, ldx, bits, scale_mode, layout == QL_LAYOUT_PACKED ? 1 : 0, rotate, codes, scales};
+  a.norm = 1;
+  a.gamma = gamma;
+  a.mscale = mod_scale;
+  a.mshift = mod_shift;
+  a.eps = eps;
+  return ql::launch_rotate_quantize(a, static_cast<hipStream_t>(stream)) == QL_OK ? QL_OK : QL_ERR_LAUNCH;
+}
+
 int pack_weight_int4(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, int scale_mode, int rotate,
                      uint8_t* packed, float* scales, void* stream) {
   if (N <= 0) return QL_ERR_SHAPE;

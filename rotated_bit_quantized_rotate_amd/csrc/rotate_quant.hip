@@ -70,6 +70,23 @@ __device__ __forceinline__ float row16_max(float m) {
   return m;
 }
 
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<DPP_ROR8>(v);
+  v += dpp_f<DPP_ROR4>(v);
+  v += dpp_f<DPP_ROR2>(v);
+  v += dpp_f<DPP_ROR1>(v);
+  return v;
+}
+
+// Position of channel c in the LDS copy of a per-channel vector: lane t of a
+// 16-lane slot reads the 16 channels 16 t .. 16 t + 15 of a 256-group as four
+// 16-byte pieces, piece q stored at q ^ (t / 4) so one ds_read_b128 by the
+// 16 lanes touches every bank once.
+__device__ __forceinline__ int nvec_pos(int c) {
+  const int t = (c >> 4) & 15, q = (c >> 2) & 3;
+  return (c & ~15) + ((q ^ (t >> 2)) << 2) + (c & 3);
+}
+
 __device__ __forceinline__ float quad_max(float m) {
   m = fmaxf(m, dpp_f<DPP_QUAD_SWAP1>(m));
   m = fmaxf(m, dpp_f<DPP_QUAD_SWAP2>(m));
@@ -119,10 +136,19 @@ __device__ __forceinline__ void store_codes(void* codes, int64_t off_elems, bool
 // blockIdx.x + gridDim.x, ... (one block each unless the grid is capped).
 // phase 0: quantize (row / group64, or tensor mode reading the absmax cell)
 // phase 1: tensor mode, absmax only (atomicMax into the cell)
-template <int GPL>
+// NORM: the RMSNorm + modulation of model card "Krea 2 Turbo OrbitQuant
+// W4A4", section "Fused transformer (OrbitQuant 0.11)" (the block's norm and
+// modulation run inside the activation quantization prologue), read as
+//   h = x * r * gamma * (1 + scale) + shift,  r = 1 / sqrt(mean_k x^2 + eps)
+// per row, with per-channel bf16 vectors; h stays in fp32 and is rotated and
+// quantized in place of x.  The workgroup first stages g = gamma * (1 + scale)
+// and shift as fp32 in dynamic LDS (8 K bytes).
+template <int GPL, bool NORM>
 __global__ __launch_bounds__(kThreads) void rq_kernel(RqArgs a, int slots_per_row, int rows_per_wg,
                                                       int phase, int64_t nblocks) {
   __shared__ float red[2][16];
+  __shared__ float sred[NORM ? 2 : 1][16];
+  extern __shared__ float nvec[];  // NORM: g at [0, K), shift at [K, 2K), nvec_pos order
   const int tid = threadIdx.x;
   const int slot = tid >> 4;
   const int t = tid & 15;
@@ -131,6 +157,36 @@ __global__ __launch_bounds__(kThreads) void rq_kernel(RqArgs a, int slots_per_ro
   const int ngroups = (int)(a.K >> 8);
   const float qmax = a.bits == 4 ? 7.0f : 127.0f;
   const float post = a.rotate ? 0.0625f : 1.0f;  // z = 16 x' when rotated
+
+  if (NORM) {
+    const int K = (int)a.K;
+    for (int c8 = tid; c8 < K / 8; c8 += kThreads) {
+      const uint4 gw = a.gamma ? reinterpret_cast<const uint4*>(a.gamma)[c8] : make_uint4(0, 0, 0, 0);
+      const uint4 sw = a.mscale ? reinterpret_cast<const uint4*>(a.mscale)[c8] : make_uint4(0, 0, 0, 0);
+      const uint4 bw = a.mshift ? reinterpret_cast<const uint4*>(a.mshift)[c8] : make_uint4(0, 0, 0, 0);
+      const uint32_t g2[4] = {gw.x, gw.y, gw.z, gw.w}, s2[4] = {sw.x, sw.y, sw.z, sw.w},
+                     b2[4] = {bw.x, bw.y, bw.z, bw.w};
+      float gv[8], bv[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float g0 = a.gamma ? __uint_as_float(g2[k] << 16) : 1.0f;
+        const float g1 = a.gamma ? __uint_as_float(g2[k] & 0xffff0000u) : 1.0f;
+        gv[2 * k] = g0 * (1.0f + __uint_as_float(s2[k] << 16));
+        gv[2 * k + 1] = g1 * (1.0f + __uint_as_float(s2[k] & 0xffff0000u));
+        bv[2 * k] = __uint_as_float(b2[k] << 16);
+        bv[2 * k + 1] = __uint_as_float(b2[k] & 0xffff0000u);
+      }
+      // channels 8 c8 .. 8 c8 + 7: two 4-channel pieces
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int p = nvec_pos(8 * c8 + 4 * h);
+        *reinterpret_cast<float4*>(nvec + p) = make_float4(gv[4 * h], gv[4 * h + 1], gv[4 * h + 2], gv[4 * h + 3]);
+        *reinterpret_cast<float4*>(nvec + K + p) =
+            make_float4(bv[4 * h], bv[4 * h + 1], bv[4 * h + 2], bv[4 * h + 3]);
+      }
+    }
+    __syncthreads();
+  }
 
   uint4 raw[GPL][2];
   auto load = [&](int64_t blk) {
@@ -163,6 +219,40 @@ __global__ __launch_bounds__(kThreads) void rq_kernel(RqArgs a, int slots_per_ro
       for (int k = 0; k < 8; ++k) {
         v[j][2 * k] = __uint_as_float(w[k] << 16);
         v[j][2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+      }
+    }
+
+    if (NORM) {
+      // mean square of the row: lane partials, the 16-lane slot, then the
+      // row's slots through LDS (fixed order)
+      float ss = 0.0f;
+#pragma unroll
+      for (int j = 0; j < GPL; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ss = __builtin_fmaf(v[j][e], v[j][e], ss);
+      ss = row16_sum(ss);
+      float* sb = sred[NORM ? (it & 1) : 0];
+      if (t == 0) sb[slot] = ss;
+      __syncthreads();
+      float rs = 0.0f;
+      const int s0 = row_in_wg * slots_per_row;
+      for (int s2 = 0; s2 < slots_per_row; ++s2) rs += sb[(s0 + s2) & 15];
+      const float r = __fdiv_rn(1.0f, __fsqrt_rn(__fdiv_rn(rs, (float)a.K) + a.eps));
+#pragma unroll
+      for (int j = 0; j < GPL; ++j) {
+        const int g = sir + j * slots_per_row;
+        if (g >= ngroups) continue;  // those lanes hold zeros and are never stored
+        const float* gp = nvec + g * 256 + t * 16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int pq = (q ^ (t >> 2)) << 2;
+          const float4 gq = *reinterpret_cast<const float4*>(gp + pq);
+          const float4 bq = *reinterpret_cast<const float4*>(gp + a.K + pq);
+          v[j][4 * q] = __builtin_fmaf(v[j][4 * q] * r, gq.x, bq.x);
+          v[j][4 * q + 1] = __builtin_fmaf(v[j][4 * q + 1] * r, gq.y, bq.y);
+          v[j][4 * q + 2] = __builtin_fmaf(v[j][4 * q + 2] * r, gq.z, bq.z);
+          v[j][4 * q + 3] = __builtin_fmaf(v[j][4 * q + 3] * r, gq.w, bq.w);
+        }
       }
     }
 
@@ -267,11 +357,22 @@ Plan plan_rows(int ngroups) {
 // Workgroups launched at most (16 per CU of MI355X); larger inputs loop.
 constexpr int64_t kRqMaxGrid = 4096;
 
+// With the norm fused in, every workgroup first stages the per-channel
+// vectors, so fewer workgroups loop over more rows.
+constexpr int64_t kRqNormMaxGrid = 512;
+
 template <int GPL>
 hipError_t launch_rq(const RqArgs& a, const Plan& p, int phase, hipStream_t s) {
   const int64_t nblocks = (a.M + p.rows - 1) / p.rows;
-  const unsigned grid = (unsigned)(nblocks < kRqMaxGrid ? nblocks : kRqMaxGrid);
-  hipLaunchKernelGGL(rq_kernel<GPL>, dim3(grid), dim3(kThreads), 0, s, a, p.slots, p.rows, phase, nblocks);
+  const int64_t cap = a.norm ? kRqNormMaxGrid : kRqMaxGrid;
+  const unsigned grid = (unsigned)(nblocks < cap ? nblocks : cap);
+  if (a.norm) {
+    hipLaunchKernelGGL((rq_kernel<GPL, true>), dim3(grid), dim3(kThreads), (size_t)(8 * a.K), s, a, p.slots,
+                       p.rows, phase, nblocks);
+  } else {
+    hipLaunchKernelGGL((rq_kernel<GPL, false>), dim3(grid), dim3(kThreads), 0, s, a, p.slots, p.rows, phase,
+                       nblocks);
+  }
   return hipGetLastError();
 }
 

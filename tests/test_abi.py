@@ -17,9 +17,9 @@ def L():
     return _lib.lib()
 
 
-def test_header_declares_the_five_entry_points():
+def test_header_declares_the_entry_points():
     fns = header_functions()
-    for name in ["rotate_quantize_act", "pack_weight_int4", "qgemm_w4a4", "qgemm_w8a8",
+    for name in ["rotate_quantize_act", "rmsnorm_rotate_quantize_act", "pack_weight_int4", "qgemm_w4a4", "qgemm_w8a8",
                  "qgemm_w4a4_lowrank", "ql_status_string", "ql_device_supported"]:
         assert name in fns
 
@@ -79,6 +79,36 @@ def test_rotate_quantize_validation(L):
     assert rq(L, l1=ALIGNED, rank=24, lr=ALIGNED) == -2
     assert rq(L, l1=ALIGNED, rank=32, lr=NULL) == -1
 
+
+
+def rqn(L, **kw):
+    a = dict(x=ALIGNED, M=4, K=256, ldx=256, g=NULL, s=NULL, t=NULL, eps=1e-6, bits=4, mode=1, layout=0,
+             rotate=1, codes=ALIGNED, scales=ALIGNED)
+    a.update(kw)
+    return L.rmsnorm_rotate_quantize_act(a["x"], a["M"], a["K"], a["ldx"], a["g"], a["s"], a["t"], a["eps"],
+                                         a["bits"], a["mode"], a["layout"], a["rotate"], a["codes"],
+                                         a["scales"], None)
+
+
+def test_rmsnorm_rotate_quantize_validation(L):
+    # the checks of rotate_quantize_act ...
+    assert rqn(L, bits=5) == -4
+    assert rqn(L, layout=1, bits=8) == -4
+    assert rqn(L, K=320, ldx=320) == -2
+    assert rqn(L, ldx=260) == -2
+    assert rqn(L, x=NULL) == -1
+    assert rqn(L, x=MISALIGNED) == -3
+    # ... plus its own: K fits the on-chip vectors, eps positive and finite, vectors 16-byte aligned
+    assert rqn(L, K=8448, ldx=8448) == -2
+    assert rqn(L, eps=0.0) == -2
+    assert rqn(L, eps=-1.0) == -2
+    assert rqn(L, eps=float("inf")) == -2
+    assert rqn(L, eps=float("nan")) == -2
+    assert rqn(L, g=MISALIGNED) == -3
+    assert rqn(L, s=MISALIGNED) == -3
+    assert rqn(L, t=MISALIGNED) == -3
+    # a valid call gets past validation to the device check (no gfx950 here)
+    assert rqn(L, g=ALIGNED, s=ALIGNED, t=ALIGNED, K=8192, ldx=8192) in (-4, -6)
 
 def g44(L, **kw):
     a = dict(a=ALIGNED, sa=ALIGNED, am=1, al=0, w=ALIGNED, sw=ALIGNED, wm=1, M=4, N=32, K=256, bias=NULL,

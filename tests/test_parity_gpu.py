@@ -133,6 +133,130 @@ def test_prologue_strided_rows(Q):
     _check_codes(codes.cpu().numpy(), scales.cpu().numpy(), ref)
 
 
+
+# ------------------------------------ RMSNorm + modulation fused prologue --
+# Scale tolerance: h = x * r * g + b is formed in fp32.  r carries the fp32
+# sum of K squares (a chain of 80 per lane, then a 6-level tree: at most
+# ~86 * 2^-24 relative) plus four correctly rounded operations, so the scales
+# can differ from the float64 oracle by up to ~3e-6 relative (~50 ulp) beside
+# the rotation's few ulp; 64 ulp is allowed.  A missing term (eps, the shift,
+# 1 + scale) moves them by orders of magnitude more.
+NORM_SCALE_ULP = 64
+
+
+def _norm_inputs(seed, M, K, vectors=True, row_spread=True):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x, _ = W.with_outlier_channels(rng, x, max(1, K // 100), 30.0)
+    if row_spread:
+        x *= rng.uniform(0.05, 20.0, size=(M, 1)).astype(np.float32)
+    g = W.to_bf16_bits(1.0 + 0.1 * rng.standard_normal(K)) if vectors else None
+    sc = W.to_bf16_bits(0.2 * rng.standard_normal(K)) if vectors else None
+    sh = W.to_bf16_bits(0.1 * rng.standard_normal(K)) if vectors else None
+    return W.to_bf16_bits(x), g, sc, sh
+
+
+def _dev_vec(v):
+    return None if v is None else to_dev_bf16(v)
+
+
+def _check_norm(got_codes, got_scales, ref):
+    frac, dmax = code_flip_stats(got_codes, ref.codes)
+    assert dmax <= 1, f"code difference {dmax} > 1"
+    assert frac <= FLIP_BUDGET, f"flip fraction {frac:.2e} > {FLIP_BUDGET:.0e}"
+    ulp = f32_ulp_diff(got_scales.reshape(ref.scales.shape), ref.scales)
+    assert ulp.max() <= NORM_SCALE_ULP, f"scale ulp diff {ulp.max()}"
+
+
+@pytest.mark.parametrize("M,K", [(1, 256), (37, 1536), (300, 5120), (9, 8192)])
+@pytest.mark.parametrize("bits,mode", [(4, "row"), (8, "row"), (4, "group64"), (4, "tensor")])
+def test_rmsnorm_prologue_matches_oracle(Q, M, K, bits, mode):
+    import torch
+
+    eps = 1e-5
+    xb, g, sc, sh = _norm_inputs(M * 11 + K, M, K)
+    codes, scales = Q.rmsnorm_rotate_quantize_act(to_dev_bf16(xb), _dev_vec(g), _dev_vec(sc), _dev_vec(sh),
+                                                  eps=eps, bits=bits, scale_mode=mode)
+    torch.cuda.synchronize()
+    ref = O.quantize_activations_norm(xb, g, sc, sh, eps, bits, mode, True)
+    _check_norm(codes.cpu().numpy(), scales.cpu().numpy(), ref)
+
+
+def test_rmsnorm_prologue_eps_and_absent_vectors(Q):
+    import torch
+
+    # small rows next to a large eps: eps dominates r, so a misplaced eps would show
+    M, K, eps = 40, 1024, 4.0
+    xb, _, _, _ = _norm_inputs(31, M, K, vectors=False, row_spread=False)
+    xb = W.to_bf16_bits(O.bf16_bits_to_f64(xb) * 0.25)
+    for bits, mode in [(4, "row"), (8, "group64")]:
+        codes, scales = Q.rmsnorm_rotate_quantize_act(to_dev_bf16(xb), eps=eps, bits=bits, scale_mode=mode)
+        torch.cuda.synchronize()
+        ref = O.quantize_activations_norm(xb, None, None, None, eps, bits, mode, True)
+        _check_norm(codes.cpu().numpy(), scales.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("rot", [True, False])
+def test_rmsnorm_prologue_packed_layout(Q, rot):
+    import torch
+
+    M, K = 70, 2048
+    xb, g, sc, sh = _norm_inputs(32, M, K)
+    packed, scales = Q.rmsnorm_rotate_quantize_act(to_dev_bf16(xb), _dev_vec(g), _dev_vec(sc), _dev_vec(sh),
+                                                   eps=1e-6, bits=4, scale_mode="row", layout="packed",
+                                                   rotate=rot)
+    torch.cuda.synchronize()
+    ref = O.quantize_activations_norm(xb, g, sc, sh, 1e-6, 4, "row", rot)
+    _check_norm(O.unpack_int4(packed.cpu().numpy()), scales.cpu().numpy(), ref)
+
+
+def test_rmsnorm_prologue_zero_rows_strided_and_empty(Q):
+    import torch
+
+    M, K, ld = 12, 512, 768
+    rng = np.random.default_rng(33)
+    xfull = W.to_bf16_bits(rng.standard_normal((M, ld)).astype(np.float32))
+    xfull[2] = 0                     # zero row: h = shift (r = 1/sqrt(eps))
+    xfull[5] = 0
+    sh = W.to_bf16_bits(0.5 * rng.standard_normal(K))
+    x = to_dev_bf16(xfull)[:, :K]
+    xb = np.ascontiguousarray(xfull[:, :K])
+    for shift in (sh, None):
+        codes, scales = Q.rmsnorm_rotate_quantize_act(x, mod_shift=_dev_vec(shift), eps=1e-6, bits=4,
+                                                      scale_mode="row")
+        torch.cuda.synchronize()
+        ref = O.quantize_activations_norm(xb, None, None, shift, 1e-6, 4, "row", True)
+        _check_norm(codes.cpu().numpy(), scales.cpu().numpy(), ref)
+        if shift is None:            # zero rows stay zero: scale 0, codes 0
+            assert (codes.cpu().numpy()[[2, 5]] == 0).all() and (scales.cpu().numpy()[[2, 5]] == 0).all()
+    empty = torch.empty((0, K), dtype=torch.bfloat16, device="cuda")
+    c, s_ = Q.rmsnorm_rotate_quantize_act(empty, eps=1e-6)
+    torch.cuda.synchronize()
+    assert c.shape == (0, K)
+
+
+def test_rmsnorm_prologue_reused_by_two_gemms(Q):
+    """One prepared activation feeds two projections of the same input (as
+    Q|K|V|gate or gate|up share it): each GEMM output matches the oracle's
+    linear of the normalized input."""
+    import torch
+
+    M, K, N1, N2 = 200, 1536, 384, 1024
+    xb, g, sc, sh = _norm_inputs(34, M, K)
+    codes, scales = Q.rmsnorm_rotate_quantize_act(to_dev_bf16(xb), _dev_vec(g), _dev_vec(sc), _dev_vec(sh),
+                                                  eps=1e-6, bits=4, scale_mode="row")
+    qa = O.quantize_activations_norm(xb, g, sc, sh, 1e-6, 4, "row", True)
+    rng = np.random.default_rng(35)
+    for N in (N1, N2):
+        wb = W.to_bf16_bits((0.02 * rng.standard_normal((N, K))).astype(np.float32))
+        wp, sw = Q.pack_weight_int4(to_dev_bf16(wb), scale_mode="row")
+        out = Q.qgemm_w4a4(codes, scales, wp, sw, K)
+        torch.cuda.synchronize()
+        qw = O.quantize_weights(wb, 4, "row", True)
+        want = O.linear_fp64(qa, qw)
+        assert rel_fro(O.bf16_bits_to_f64(bf16_bits(out)), want) <= REL_FRO
+
+
 @pytest.mark.parametrize("rank", [16, 32, 64])
 def test_lowrank_down_projection(Q, rank):
     import torch
