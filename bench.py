@@ -1,7 +1,7 @@
 """Benchmark of the rotated low-bit quantized linear on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--workload attn_proj_w4a4|ffdown_w8a8|svdq_gateup|stack]
+                    [--workload attn_proj_w4a4|ffdown_w8a8|svdq_gateup|stack|stack_fused]
 
 Default workload (the headline line): one DiT attention projection at
 1024x1024 -- X bf16 [4096 x 5120] ~ N(0,1) with 1% outlier channels x30,
@@ -15,6 +15,10 @@ Other workloads (separate runs, same JSON shape):
                 low-rank branch, SwiGLU out [4096 x 20480]
   stack         the 224 linears of a 28-block DiT at 2048x2048 (16384
                 tokens): 128 W4A4 + 96 W8A8, every activation resident
+  stack_fused   the same 224 linears with each block's RMSNorm + modulation
+                fused into its prologues and one prepared activation per
+                shared input and precision (Q|gate int4, K|V int8, gate|up):
+                5 prologues per block instead of 8
 
 Inputs and prepared weights are resident in HBM before timing.  One step is
 the layer's online path: rotate + quantize the activations
@@ -68,6 +72,7 @@ GEMM_KERNELS = {
     "ffdown_w8a8": ("qgemm_w8a8", "4096x20480x5120", ["qgemm_pipe.hip"]),
     "svdq_gateup": ("qgemm_w4a4_lowrank", "4096x5120x40960", ["qgemm_pipe.hip"]),
     "stack": ("qgemm_stack", "224x16384", ["qgemm_pipe.hip"]),
+    "stack_fused": ("qgemm_stack_fused", "224x16384", ["qgemm_pipe.hip"]),
 }
 
 
@@ -102,7 +107,7 @@ def _parse():
     p.add_argument("--calib-copy", action="store_true")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     a = p.parse_args()
-    stack = a.workload == "stack"
+    stack = a.workload in ("stack", "stack_fused")
     if a.steps is None:
         a.steps = 3 if stack else 200
     a.warmup_min = None
@@ -412,8 +417,122 @@ def case_stack(Q, W, dev):
     return c
 
 
+def case_stack_fused(Q, W, dev):
+    """The stack's 224 linears (same weights) as a DiT block runs them when
+    the block's RMSNorm + modulation live in the quantization prologue and one
+    prepared activation serves every projection of the same input (model card
+    "Krea 2 Turbo OrbitQuant W4A4", section "Fused transformer (OrbitQuant
+    0.11)").  Per block, four resident inputs (torch generator, N(0,1)):
+    the attention input (seed of wq's input), the wo input, the MLP input and
+    the down input (seeds of wo's, mlp_gate's and mlp_down's inputs); the
+    attention and MLP inputs go through rmsnorm_rotate_quantize_act with
+    synthetic adaLN vectors (gamma ~ 1 + 0.1 N, scale ~ 0.2 N, shift ~ 0.1 N,
+    seeds 10^7 + 8 b + i).  The attention input is prepared once as int4
+    codes (wq, attn_gate) and once as int8 codes (wk, wv); the MLP input once
+    (mlp_gate, mlp_up)."""
+    import torch
+    M = 16384
+    layers = W.stack_layers()
+    g = torch.Generator(device=dev)
+    maxk = max(k for _, _, _, k, _ in layers)
+    maxn = max(n for _, _, n, _, _ in layers)
+    codes = {4: torch.empty((M * maxk,), dtype=torch.int8, device=dev),
+             8: torch.empty((M * maxk,), dtype=torch.int8, device=dev)}
+    sa = {4: torch.empty((M,), dtype=torch.float32, device=dev),
+          8: torch.empty((M,), dtype=torch.float32, device=dev)}
+    out = torch.empty((M * maxn,), dtype=torch.bfloat16, device=dev)
+    c = Case()
+    prep = 0.0
+    n4 = 0
+    names = [nm for nm, _, _ in W.STACK_BLOCK]
+
+    def rnd(seed, shape, std=1.0, mean=0.0):
+        g.manual_seed(seed)
+        return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * std + mean).to(torch.bfloat16)
+
+    def prologue(x, bits, norm):
+        cd = codes[bits][: M * x.shape[1]].view(M, x.shape[1])
+        if norm is None:
+            fn = lambda: Q.rotate_quantize_act(x, bits=bits, scale_mode="row", codes=cd, scales=sa[bits])
+        else:
+            fn = lambda: Q.rmsnorm_rotate_quantize_act(x, *norm, eps=1e-6, bits=bits, scale_mode="row",
+                                                       codes=cd, scales=sa[bits])
+        c.launches.append(("prologue", fn))
+        c.pro_bytes += M * x.shape[1] * 3 + M * 4
+
+    for b in range(W.STACK_BLOCKS):
+        base = 8 * b
+        x_attn = rnd(2 * (base + names.index("wq")) + 1, (M, 5120))
+        x_o = rnd(2 * (base + names.index("wo")) + 1, (M, 6144))
+        x_mlp = rnd(2 * (base + names.index("mlp_gate")) + 1, (M, 5120))
+        x_down = rnd(2 * (base + names.index("mlp_down")) + 1, (M, 20480))
+        norm_attn = (rnd(10 ** 7 + base, (5120,), 0.1, 1.0), rnd(10 ** 7 + base + 1, (5120,), 0.2),
+                     rnd(10 ** 7 + base + 2, (5120,), 0.1))
+        norm_mlp = (rnd(10 ** 7 + base + 3, (5120,), 0.1, 1.0), rnd(10 ** 7 + base + 4, (5120,), 0.2),
+                    rnd(10 ** 7 + base + 5, (5120,), 0.1))
+        # prepared weights of the block's 8 linears (the stack's seeds and preparation)
+        lw = {}
+        for i, (name, n, k) in enumerate(W.STACK_BLOCK):
+            li = base + i
+            bits = W.stack_precision(b, name)
+            w = rnd(2 * li, (n, k), 0.02)
+            sw = torch.empty((n,), dtype=torch.float32, device=dev)
+            if bits == 4:
+                wq = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+                prep += _timed_prep(lambda: Q.pack_weight_int4(w, packed=wq, scales=sw))
+                n4 += 1
+            else:
+                wq = torch.empty((n, k), dtype=torch.int8, device=dev)
+                prep += _timed_prep(lambda: Q.rotate_quantize_act(w, bits=8, scale_mode="row", codes=wq,
+                                                                  scales=sw))
+            del w
+            lw[name] = (wq, sw, n, k, bits)
+
+        def gemm(name):
+            wq, sw, n, k, bits = lw[name]
+            cd = codes[bits][: M * k].view(M, k)
+            o = out[: M * n].view(M, n)
+            if bits == 4:
+                fn = lambda: Q.qgemm_w4a4(cd, sa[4], wq, sw, k, out=o)
+                c.gemm_bytes += n * k // 2
+            else:
+                fn = lambda: Q.qgemm_w8a8(cd, sa[8], wq, sw, out=o)
+                c.gemm_bytes += n * k
+            c.launches.append(("gemm", fn))
+            c.ops += 2 * M * n * k
+            c.gemm_bytes += M * k + M * 4 + n * 4 + M * n * 2
+            c.gemm_launches += 1
+
+        prologue(x_attn, 4, norm_attn)
+        gemm("wq")
+        gemm("attn_gate")
+        prologue(x_attn, 8, norm_attn)
+        gemm("wk")
+        gemm("wv")
+        prologue(x_o, lw["wo"][4], None)
+        gemm("wo")
+        prologue(x_mlp, 4, norm_mlp)
+        gemm("mlp_gate")
+        gemm("mlp_up")
+        prologue(x_down, lw["mlp_down"][4], None)
+        gemm("mlp_down")
+    torch.cuda.synchronize()
+    c.prep_ms = prep
+    c.metric = ("effective int TOPS + % int8 MFMA peak, mixed 224-linear DiT stack at 2048^2 "
+                "(16384 tokens, 128 W4A4 + 96 W8A8), norm fused + prepared activations reused")
+    c.dtype = "int8 MFMA (int4/int8 codes), int32 accumulate, bf16 out"
+    c.config = {"workload": "28-block DiT linear stack at 2048^2: 16384 tokens, d=5120, ffn=20480, "
+                            f"{len(layers)} linears ({n4} W4A4, {len(layers) - n4} W8A8), per-token / "
+                            "per-row scales, group-256 Hadamard, bf16 out; RMSNorm + adaLN modulation fused "
+                            "into the attention and MLP prologues, one prepared activation per shared input "
+                            "and precision (5 prologues per block), every input resident",
+                "M": M, "layers": len(layers), "prologues": 5 * W.STACK_BLOCKS, "global_batch": M,
+                "parallelism": "single GPU"}
+    return c
+
+
 CASES = {"attn_proj_w4a4": case_attn, "ffdown_w8a8": case_ffdown, "svdq_gateup": case_svdq,
-         "stack": case_stack}
+         "stack": case_stack, "stack_fused": case_stack_fused}
 
 
 # ------------------------------------------------------------------- main --
@@ -452,7 +571,7 @@ def main():
         while w < args.warmup_min or time.perf_counter() - t_w < WARMUP_S:
             step()
             w += 1
-            if w % (1 if args.workload == "stack" else 16) == 0:
+            if w % (1 if args.workload in ("stack", "stack_fused") else 16) == 0:
                 torch.cuda.synchronize()  # keep the host within a few steps of the GPU
         args.warmup = w
     torch.cuda.synchronize()

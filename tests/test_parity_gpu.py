@@ -182,6 +182,31 @@ def test_rmsnorm_prologue_matches_oracle(Q, M, K, bits, mode):
     _check_norm(codes.cpu().numpy(), scales.cpu().numpy(), ref)
 
 
+
+@pytest.mark.parametrize("bits,mode", [(4, "row"), (8, "row"), (4, "group64")])
+def test_rmsnorm_prologue_full_size_sampled_rows(Q, bits, mode):
+    """The stack's normed prologue at its real size (16384 x 5120): the grid
+    is capped, so each workgroup loops over several row blocks (the
+    double-buffered row reductions); rows are independent, so the oracle
+    checks a sample of them."""
+    import torch
+
+    M, K = 16384, 5120
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    x = torch.randn((M, K), generator=g, device="cuda", dtype=torch.float32)
+    x *= torch.rand((M, 1), generator=g, device="cuda") * 10 + 0.1
+    x = x.to(torch.bfloat16)
+    gam = (1.0 + 0.1 * torch.randn((K,), generator=g, device="cuda")).to(torch.bfloat16)
+    sc = (0.2 * torch.randn((K,), generator=g, device="cuda")).to(torch.bfloat16)
+    sh = (0.1 * torch.randn((K,), generator=g, device="cuda")).to(torch.bfloat16)
+    codes, scales = Q.rmsnorm_rotate_quantize_act(x, gam, sc, sh, eps=1e-6, bits=bits, scale_mode=mode)
+    torch.cuda.synchronize()
+    ri = torch.as_tensor(_sample_rows(M, 64), device="cuda")
+    xb = bf16_bits(x[ri])
+    ref = O.quantize_activations_norm(xb, bf16_bits(gam), bf16_bits(sc), bf16_bits(sh), 1e-6, bits, mode, True)
+    _check_norm(codes[ri].cpu().numpy(), scales[ri].cpu().numpy(), ref)
+
 def test_rmsnorm_prologue_eps_and_absent_vectors(Q):
     import torch
 
