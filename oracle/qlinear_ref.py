@@ -20,7 +20,7 @@ __all__ = [
     "quantize", "dequantize",
     "pack_int4", "unpack_int4",
     "int_gemm", "int_gemm_grouped",
-    "silu", "epilogue",
+    "silu", "sigmoid", "epilogue",
     "QuantResult", "quantize_activations", "quantize_weights",
     "rmsnorm_modulate", "quantize_activations_norm",
     "linear_fp64", "linear",
@@ -237,15 +237,26 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
+def sigmoid(z: np.ndarray) -> np.ndarray:
+    """Logistic sigmoid 1 / (1 + exp(-z)), in float64: the attention gate of
+    [OrbitQuant] "Fused transformer (OrbitQuant 0.11)" (the grouped
+    Q|K|V|gate GEMM applies it in its epilogue)."""
+    z = np.asarray(z, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
 def epilogue(y: np.ndarray, kind: str, residual=None, gate=None) -> np.ndarray:
     """Apply the output epilogue to the float64 GEMM result y [M, N]:
       "bf16"           -> y
       "swiglu"         -> silu(y[:, :F]) * y[:, F:], F = N / 2 (first half of
                           the output columns is the gate, second half up)
       "gated_residual" -> residual + gate[n] * y
+      "sigmoid"        -> sigmoid(y) (the attention gate projection)
     Returns float64 (round with f64_to_bf16_bits)."""
     if kind == "bf16":
         return y
+    if kind == "sigmoid":
+        return sigmoid(y)
     if kind == "swiglu":
         F = y.shape[1] // 2
         return silu(y[:, :F]) * y[:, F:]

@@ -450,3 +450,21 @@ def test_norm_prologue_reduces_to_the_plain_prologue_when_the_norm_is_identity(b
     a = O.quantize_activations_norm(x, None, None, None, 0.0, bits, mode)
     b = O.quantize_activations(x, bits, mode)
     assert np.array_equal(a.codes, b.codes) and np.array_equal(a.scales, b.scales)
+
+
+# ------------------------------------------------------ sigmoid gate epilogue --
+
+def test_sigmoid_closed_form_values(golden):
+    for ln in golden("sigmoid_values.txt"):
+        z, want = (float(v) for v in ln.split())
+        assert abs(float(O.sigmoid(np.array([z]))[0]) - want) <= 1e-15
+
+
+def test_sigmoid_symmetry_range_and_silu_relation():
+    z = np.linspace(-30, 30, 1201)
+    s = O.sigmoid(z)
+    assert np.allclose(s + O.sigmoid(-z), 1.0, rtol=0, atol=1e-15)       # sigma(-z) = 1 - sigma(z)
+    assert ((s > 0) & (s < 1)).all() and (np.diff(s) > 0).all()           # increasing into (0, 1)
+    assert np.allclose(O.silu(z), z * s, rtol=1e-15, atol=1e-300)         # silu(z) = z sigma(z)
+    y = np.array([[0.0, 1.0986122886681098]])
+    assert np.allclose(O.epilogue(y, "sigmoid"), [[0.5, 0.75]], rtol=0, atol=1e-15)
