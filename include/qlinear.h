@@ -92,7 +92,8 @@ enum {
   QL_EPI_SWIGLU = 1,         /* out[m,j] = bf16(silu(y[m,j]) * y[m,j+N/2]), j<N/2 */
   QL_EPI_GATED_RESIDUAL = 2, /* out[m,n] = bf16(res[m,n] + gate[n] * y[m,n])     */
   QL_EPI_F32 = 3,            /* out[m,n] = y as float32                          */
-  QL_EPI_I32 = 4             /* out[m,n] = exact int32 accumulator (no scales)   */
+  QL_EPI_I32 = 4,            /* out[m,n] = exact int32 accumulator (no scales)   */
+  QL_EPI_SIGMOID = 5         /* out[m,n] = bf16(1 / (1 + exp(-y[m,n])))          */
 };
 /* y[m,n] = sum_k deq(a)[m,k] * deq(w)[n,k] (+ bias[n]) (+ (lr L2)[m,n]),
  * i.e. acc * s_a * s_w for tensor / row scales, and the sum over 64-channel
@@ -182,7 +183,8 @@ int pack_weight_int4(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
  *   w        [N, K/2] packed int4 weight codes, dense rows
  *   sw       weight scales per w_scale_mode (TENSOR | ROW)
  *   bias     NULL or bf16 [N]
- *   epilogue QL_EPI_BF16 | QL_EPI_F32 | QL_EPI_I32 (I32 ignores scales and bias)
+ *   epilogue QL_EPI_BF16 | QL_EPI_F32 | QL_EPI_I32 (I32 ignores scales and bias) |
+ *            QL_EPI_SIGMOID (tensor / row scales; the attention gate)
  *   out      [M, N] bf16 / float32 / int32, row stride ldo (elements)
  * Group-64 scales go through qgemm_w4a4_lowrank (with rank 0). */
 int qgemm_w4a4(const void* a, const float* sa, int a_scale_mode, int a_layout,
@@ -200,7 +202,8 @@ int qgemm_w4a4(const void* a, const float* sa, int a_scale_mode, int a_layout,
  *   residual  bf16 [M, N] with row stride ldo; may alias out (in-place
  *             h += gate * y).  Required for QL_EPI_GATED_RESIDUAL.
  *   gate      bf16 [N]; required for QL_EPI_GATED_RESIDUAL.
- *   epilogue  QL_EPI_BF16 | QL_EPI_GATED_RESIDUAL | QL_EPI_F32 | QL_EPI_I32 */
+ *   epilogue  QL_EPI_BF16 | QL_EPI_GATED_RESIDUAL | QL_EPI_F32 | QL_EPI_I32 |
+ *             QL_EPI_SIGMOID */
 int qgemm_w8a8(const int8_t* a, const float* sa, int a_scale_mode,
                const int8_t* w, const float* sw, int w_scale_mode,
                int64_t M, int64_t N, int64_t K,
@@ -228,6 +231,37 @@ int qgemm_w4a4_lowrank(const void* a, const float* sa, int a_scale_mode, int a_l
                        int64_t M, int64_t N, int64_t K,
                        const uint16_t* bias, int epilogue, void* out, int64_t ldo,
                        void* stream);
+
+/* One projection of a grouped GEMM. */
+typedef struct {
+  const void* w;    /* packed int4 [n, K/2] (w_bits 4) or int8 [n, K] (w_bits 8), dense rows */
+  const float* sw;  /* per-row weight scales [n] */
+  int64_t n;        /* output columns: a positive multiple of 16, n * K < 2^31 */
+  int w_bits;       /* 4: int4 weights with the INT4 activation codes a4;
+                       8: int8 weights with the INT8 activation codes a8 */
+  int epilogue;     /* QL_EPI_BF16 or QL_EPI_SIGMOID */
+  void* out;        /* bf16 [M, n], row stride ldo (elements, >= n, 16-byte rows) */
+  int64_t ldo;
+} ql_segment;
+
+enum { QL_MAX_SEGMENTS = 8 };
+
+/* Grouped GEMM: up to QL_MAX_SEGMENTS projections of the same activations
+ * in one launch (model card "Krea 2 Turbo OrbitQuant W4A4", section "Fused
+ * transformer (OrbitQuant 0.11)": one grouped Q|K|V|gate W4A4 GEMM per block
+ * with the sigmoid gate in its epilogue, while the K and V projections stay
+ * INT8).  Segment s computes out_s = epilogue_s(deq(a) deq(w_s)^T) with
+ * per-token activation and per-row weight scales, exactly as qgemm_w4a4 /
+ * qgemm_w8a8 would; the tiles of every segment share one grid.
+ *   a4, sa4   int8-container INT4 codes [M, K] (dense rows) and their per-row
+ *             scales [M]; required if any segment has w_bits 4, else may be NULL
+ *   a8, sa8   INT8 codes [M, K] and per-row scales [M]; required if any
+ *             segment has w_bits 8, else may be NULL
+ *   segments  HOST array of nseg descriptors, 1 <= nseg <= QL_MAX_SEGMENTS;
+ *             read during the call only
+ * Outputs must not overlap each other or the inputs. */
+int qgemm_grouped(const void* a4, const float* sa4, const void* a8, const float* sa8,
+                  int64_t M, int64_t K, const ql_segment* segments, int nseg, void* stream);
 
 #ifdef __cplusplus
 }

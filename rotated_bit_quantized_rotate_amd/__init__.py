@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     device_supported,
     lib,
     pack_weight_int4,
+    qgemm_grouped,
     qgemm_w4a4,
     qgemm_w4a4_lowrank,
     qgemm_w8a8,

@@ -35,15 +35,24 @@ QL_EPI_SWIGLU = 1
 QL_EPI_GATED_RESIDUAL = 2
 QL_EPI_F32 = 3
 QL_EPI_I32 = 4
+QL_EPI_SIGMOID = 5
+QL_MAX_SEGMENTS = 8
 
 SCALE_MODES = {"tensor": QL_SCALE_TENSOR, "row": QL_SCALE_ROW, "group64": QL_SCALE_GROUP64}
 LAYOUTS = {"i8": QL_LAYOUT_I8, "packed": QL_LAYOUT_PACKED}
 EPILOGUES = {"bf16": QL_EPI_BF16, "swiglu": QL_EPI_SWIGLU, "gated_residual": QL_EPI_GATED_RESIDUAL,
-             "f32": QL_EPI_F32, "i32": QL_EPI_I32}
+             "f32": QL_EPI_F32, "i32": QL_EPI_I32, "sigmoid": QL_EPI_SIGMOID}
 
 _p = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _i = ctypes.c_int
+
+class Segment(ctypes.Structure):
+    """ql_segment of include/qlinear.h."""
+    _fields_ = [("w", ctypes.c_void_p), ("sw", ctypes.c_void_p), ("n", ctypes.c_int64),
+                ("w_bits", ctypes.c_int), ("epilogue", ctypes.c_int), ("out", ctypes.c_void_p),
+                ("ldo", ctypes.c_int64)]
+
 
 _SIGNATURES = {
     "ql_status_string": (ctypes.c_char_p, [_i]),
@@ -56,6 +65,7 @@ _SIGNATURES = {
     "qgemm_w8a8": (_i, [_p, _p, _i, _p, _p, _i, _i64, _i64, _i64, _p, _p, _p, _i, _p, _i64, _p]),
     "qgemm_w4a4_lowrank": (_i, [_p, _p, _i, _i, _p, _p, _i, _p, _p, _i, _i64, _i64, _i64, _p, _i, _p,
                                 _i64, _p]),
+    "qgemm_grouped": (_i, [_p, _p, _p, _p, _i64, _i64, ctypes.POINTER(Segment), _i, _p]),
 }
 
 _LIB = None
@@ -235,3 +245,28 @@ def qgemm_w4a4_lowrank(a, sa, w, sw, K, lr=None, l2=None, a_scale_mode="group64"
                                   _ptr(bias), epi, _ptr(out), out.stride(0), _stream(stream))
     _check("qgemm_w4a4_lowrank", st)
     return out
+
+
+def qgemm_grouped(a4, sa4, a8, sa8, K, segments, stream=None):
+    """Several projections of the same activations in one launch.
+    a4/sa4: int8-container int4 codes [M, K] + row scales (or None);
+    a8/sa8: int8 codes [M, K] + row scales (or None).  segments: list of
+    dicts with w (packed int4 [n, K/2] or int8 [n, K]), sw [n], bits (4 | 8),
+    epilogue ("bf16" | "sigmoid") and optionally out (bf16 [M, n]).
+    Returns the list of outputs."""
+    ref = a4 if a4 is not None else a8
+    M = ref.shape[0]
+    arr = (Segment * len(segments))()
+    outs = []
+    for i, sg in enumerate(segments):
+        n = sg["w"].shape[0]
+        out = sg.get("out")
+        if out is None:
+            out = torch.empty((M, n), dtype=torch.bfloat16, device=ref.device)
+        outs.append(out)
+        arr[i] = Segment(_ptr(sg["w"]), _ptr(sg["sw"]), n, int(sg["bits"]), _epi(sg.get("epilogue", "bf16")),
+                         _ptr(out), out.stride(0))
+    st = lib().qgemm_grouped(_ptr(a4), _ptr(sa4), _ptr(a8), _ptr(sa8), M, K, arr, len(segments),
+                             _stream(stream))
+    _check("qgemm_grouped", st)
+    return outs

@@ -59,7 +59,7 @@ namespace {
 constexpr int BK = 128;      // channels per stage
 constexpr int kLdsBytes = 160 * 1024;
 
-enum { EPI_BF16 = 0, EPI_SWIGLU = 1, EPI_GATED = 2, EPI_F32 = 3, EPI_I32 = 4 };
+enum { EPI_BF16 = 0, EPI_SWIGLU = 1, EPI_GATED = 2, EPI_F32 = 3, EPI_I32 = 4, EPI_SIGMOID = 5 };
 
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 typedef float f2 __attribute__((ext_vector_type(2)));
@@ -219,18 +219,34 @@ __device__ __forceinline__ int64_t w_row_of(const PArgs& p, int64_t n0, int t) {
   return (u >= HW ? p.half_n : 0) + f;
 }
 
+// Linear position of workgroup b in an XCD-aware order: the hardware hands
+// workgroups to the 8 XCDs round-robin, so consecutive positions go to the
+// same XCD and the tiles one XCD runs form a compact block.
+__device__ __forceinline__ int xcd_linear(int b, int nb) {
+  const int xcd = b & 7, q8 = nb >> 3, r8 = nb & 7;
+  return (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + (b >> 3);
+}
+
+// Tile (tile_m, tile_n) of linear position bl: groups of group_m tile rows,
+// column-major inside a group, so neighbouring positions share A and W panels.
+__device__ __forceinline__ void grouped_tile(int bl, int tiles_m, int tiles_n, int group_m, int& tile_m,
+                                             int& tile_n) {
+  const int gsz = group_m * tiles_n;
+  const int grp = bl / gsz;
+  const int first_m = grp * group_m;
+  const int gm = min(tiles_m - first_m, group_m);
+  const int inb = bl - grp * gsz;
+  tile_m = first_m + inb % gm;
+  tile_n = inb / gm;
+}
+
+// One output tile of the GEMM on the workgroup's LDS ring (sm0, sm1, sm2:
+// C::STAGE bytes each; sm2 is used only with a 3-stage ring).
 template <class C, int EPI, bool LOWRANK>
-__global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
+__device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n, uint8_t* const sm0,
+                                          uint8_t* const sm1, uint8_t* const sm2) {
   constexpr int NS = C::NSTAGE;
   constexpr bool SWIG = EPI == EPI_SWIGLU;
-  // One LDS array per ring stage.  The main loop is unrolled by NS so every
-  // access names its array statically: the compiler then sees that the
-  // loads in flight into the other stages do not alias the stage being read
-  // and adds no wait for them before the fragment reads.  The explicit
-  // vmcnt wait plus barrier at the top of each stage is the synchronization.
-  __shared__ __attribute__((aligned(16))) uint8_t sm0[C::STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t sm1[C::STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t sm2[NS == 3 ? C::STAGE : 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // wave-uniform; readfirstlane keeps everything derived from it in SGPRs
@@ -240,19 +256,6 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
   const int wn = wave % C::WGN;
   const int l16 = lane & 15;
   const int lg = lane >> 4;
-
-  // ---- XCD-aware tile order -------------------------------------------
-  const int nb = p.tiles_m * p.tiles_n;
-  const int b = blockIdx.x;
-  const int xcd = b & 7, q8 = nb >> 3, r8 = nb & 7;
-  const int bl = (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + (b >> 3);
-  const int gsz = p.group_m * p.tiles_n;
-  const int grp = bl / gsz;
-  const int first_m = grp * p.group_m;
-  const int gm = min(p.tiles_m - first_m, p.group_m);
-  const int inb = bl - grp * gsz;
-  const int tile_m = first_m + inb % gm;
-  const int tile_n = inb / gm;
   const int64_t m0 = (int64_t)tile_m * C::BM;
   const int64_t n0 = (int64_t)tile_n * (SWIG ? C::BN / 2 : C::BN);
 
@@ -390,7 +393,8 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
   // reach the other lanes through LDS.  Row factors are kept
   // in the order the lanes read them: tile row wm * WM + 16 i + l16 at
   // wm * WM + FI * l16 + i, so a lane's FI rows are contiguous.
-  constexpr bool STAGED = (EPI == EPI_BF16 || EPI == EPI_GATED) && !SWIG && !LOWRANK && C::WGM == 2;
+  constexpr bool STAGED =
+      (EPI == EPI_BF16 || EPI == EPI_GATED || EPI == EPI_SIGMOID) && !SWIG && !LOWRANK && C::WGM == 2;
   constexpr int NV = C::BM + (EPI == EPI_GATED ? 3 : 2) * C::BN;
   constexpr int NVT = STAGED ? (NV + C::NT - 1) / C::NT : 1;
   float vec[NVT];
@@ -588,17 +592,18 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
       acc[j][C::FI - 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bw1[j], af_def, acc[j][C::FI - 1], 0, 0, 0);
   }
 
-  // ---- staged epilogue (plain bf16 and gated residual) ---------------------
+  // ---- staged epilogue (plain bf16, sigmoid gate, gated residual) ----------
   // A lane holds 4 consecutive columns of one row per fragment, so direct
   // stores write 32-byte row pieces, and the 128-byte lines that two wave
   // columns share reach memory in parts.  Instead the tile goes through LDS
   // (the ring is free now) a band of rows at a time and leaves as whole rows
-  // with 16-byte stores.  bf16 output: the band holds finished bf16 values
-  // (two bands of BM/2 rows).  Gated residual: the band holds y in fp32 (four
+  // with 16-byte stores.  bf16 output (plain or through the sigmoid of the
+  // attention gate): the band holds finished bf16 values (two bands of BM/2
+  // rows).  Gated residual: the band holds y in fp32 (four
   // bands of BM/4 rows), and the copy-out reads the residual with the same
   // coalesced 16-byte accesses, so out = res + gate * y is still rounded
   // once.
-  if constexpr ((EPI == EPI_BF16 || EPI == EPI_GATED) && !SWIG && !LOWRANK && C::WGM == 2) {
+  if constexpr (STAGED) {
     constexpr bool F32 = EPI == EPI_GATED;
     constexpr int EB = F32 ? 4 : 2;          // staged bytes per value
     constexpr int NB = F32 ? 4 : 2;          // bands
@@ -666,6 +671,7 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
               const float v = C::GROUP ? yf[C::GROUP ? j : 0][C::GROUP ? i : 0][r]
                                        : (float)acc[C::GROUP ? 0 : j][C::GROUP ? 0 : i][r];
               y[r] = v * sam * swv[r] + addv[r];
+              if (EPI == EPI_SIGMOID) y[r] = 1.0f / (1.0f + __expf(-y[r]));  // the attention gate
             }
             uint8_t* dst = row_ptr(ii * 16 + l16) + col * EB;
             if (F32) {
@@ -839,6 +845,17 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
 }
 
 template <class C, int EPI, bool LOWRANK>
+__global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
+  // the LDS ring: one array per stage
+  __shared__ __attribute__((aligned(16))) uint8_t sm0[C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm1[C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm2[C::NSTAGE == 3 ? C::STAGE : 16];
+  int tile_m, tile_n;
+  grouped_tile(xcd_linear(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, p.group_m, tile_m, tile_n);
+  pipe_tile<C, EPI, LOWRANK>(p, tile_m, tile_n, sm0, sm1, sm2);
+}
+
+template <class C, int EPI, bool LOWRANK>
 hipError_t launch_pipe(PArgs p, hipStream_t s) {
   p.tiles_m = (int)((p.M + C::BM - 1) / C::BM);
   p.tiles_n = EPI == EPI_SWIGLU ? (int)((p.half_n + C::BN / 2 - 1) / (C::BN / 2))
@@ -857,6 +874,7 @@ hipError_t launch_plain(const PArgs& p, int epi, hipStream_t s) {
     case EPI_F32: return launch_pipe<C, EPI_F32, false>(p, s);
     case EPI_I32: return launch_pipe<C, EPI_I32, false>(p, s);
     case EPI_GATED: return launch_pipe<C, EPI_GATED, false>(p, s);
+    case EPI_SIGMOID: return launch_pipe<C, EPI_SIGMOID, false>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -875,7 +893,118 @@ hipError_t launch_lowrank(const PArgs& p, int epi, hipStream_t s) {
   }
 }
 
+// ---- grouped GEMM: several projections of one input in one launch --------
+// (model card "Krea 2 Turbo OrbitQuant W4A4", section "Fused transformer
+// (OrbitQuant 0.11)": one grouped Q|K|V|gate W4A4 GEMM per block with the
+// sigmoid gate in its epilogue, the INT8 projections kept inside the group.)
+// Each segment is a [M x n] product with its own weights, per-row scales,
+// precision (packed INT4 or INT8 weights; int8-container INT4 or INT8
+// activation codes, per-token scales) and epilogue (bf16 or sigmoid).  The
+// tiles of all segments form one grid, so the small projections fill the
+// large ones' last wave instead of leaving their own tail.  Both weight
+// formats use 256 x 320 tiles; a workgroup runs the tile body of its
+// segment's format on one LDS buffer sized for the larger ring.
+using CfgG4 = Cfg<256, 320, 2, 4, false, true>;
+using CfgG8 = Cfg<256, 320, 2, 4, false, false>;
+constexpr int kGroupedLds = (CfgG4::NSTAGE * CfgG4::STAGE > CfgG8::NSTAGE * CfgG8::STAGE)
+                                ? CfgG4::NSTAGE * CfgG4::STAGE
+                                : CfgG8::NSTAGE * CfgG8::STAGE;
+static_assert(kGroupedLds <= kLdsBytes, "grouped LDS ring too large");
+
+struct GSeg {
+  const uint8_t* w;
+  const float* sw;
+  void* out;
+  int64_t ldo;
+  int64_t n;
+  int w8;        // 1: int8 weights and int8 activation codes
+  int sigmoid;   // 1: sigmoid epilogue
+  int tiles_n;
+  int tile0;     // first linear tile of the segment
+};
+
+struct GArgs {
+  PArgs base;    // M, K, the activation operands of segment 0, group_m, tiles_m
+  const uint8_t* a4;
+  const float* sa4;
+  const uint8_t* a8;
+  const float* sa8;
+  int nseg;
+  int ntiles;
+  GSeg seg[kMaxGroupSegments];
+};
+
+__global__ __launch_bounds__(512, 1) void qgemm_grouped_kernel(GArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kGroupedLds];
+  const int bl = xcd_linear(blockIdx.x, g.ntiles);
+  int si = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroupSegments; ++i)
+    if (i < g.nseg && bl >= g.seg[i].tile0) si = i;
+  const GSeg& sg = g.seg[si];
+  PArgs p = g.base;
+  p.a = sg.w8 ? g.a8 : g.a4;
+  p.sa = sg.w8 ? g.sa8 : g.sa4;
+  p.w = sg.w;
+  p.sw = sg.sw;
+  p.N = sg.n;
+  p.half_n = sg.n / 2;
+  p.out = sg.out;
+  p.ldo = sg.ldo;
+  p.tiles_n = sg.tiles_n;
+  p.post = sg.w8 ? 1.0f : 1.0f / 16.0f;
+  p.shift = sg.w8 ? 0 : 4;
+  int tile_m, tile_n;
+  grouped_tile(bl - sg.tile0, p.tiles_m, sg.tiles_n, p.group_m, tile_m, tile_n);
+  if (sg.w8) {
+    uint8_t* const r = lds;
+    if (sg.sigmoid) pipe_tile<CfgG8, EPI_SIGMOID, false>(p, tile_m, tile_n, r, r + CfgG8::STAGE, r);
+    else pipe_tile<CfgG8, EPI_BF16, false>(p, tile_m, tile_n, r, r + CfgG8::STAGE, r);
+  } else {
+    uint8_t* const r = lds;
+    if (sg.sigmoid)
+      pipe_tile<CfgG4, EPI_SIGMOID, false>(p, tile_m, tile_n, r, r + CfgG4::STAGE, r + 2 * CfgG4::STAGE);
+    else
+      pipe_tile<CfgG4, EPI_BF16, false>(p, tile_m, tile_n, r, r + CfgG4::STAGE, r + 2 * CfgG4::STAGE);
+  }
+}
+
 }  // namespace
+
+int launch_qgemm_grouped(const GroupedArgs& ga, hipStream_t s) {
+  if (ga.M == 0) return OK;
+  GArgs g{};
+  g.base.M = ga.M;
+  g.base.K = ga.K;
+  g.base.sa_stride = 1;
+  g.base.sw_stride = 1;
+  g.base.kg = (int)(ga.K >> 6);
+  g.base.tiles_m = (int)((ga.M + 255) / 256);
+  g.base.group_m = 4;
+  g.a4 = static_cast<const uint8_t*>(ga.a4);
+  g.sa4 = ga.sa4;
+  g.a8 = static_cast<const uint8_t*>(ga.a8);
+  g.sa8 = ga.sa8;
+  g.nseg = ga.nseg;
+  int t = 0;
+  for (int i = 0; i < ga.nseg; ++i) {
+    GSeg& d = g.seg[i];
+    const GroupSegment& src = ga.seg[i];
+    d.w = static_cast<const uint8_t*>(src.w);
+    d.sw = src.sw;
+    d.out = src.out;
+    d.ldo = src.ldo;
+    d.n = src.n;
+    d.w8 = src.w_bits == 8 ? 1 : 0;
+    d.sigmoid = src.epilogue == EPI_SIGMOID ? 1 : 0;
+    d.tiles_n = (int)((src.n + 319) / 320);
+    d.tile0 = t;
+    t += g.base.tiles_m * d.tiles_n;
+  }
+  g.ntiles = t;
+  hipLaunchKernelGGL(qgemm_grouped_kernel, dim3(t), dim3(512), 0, s, g);
+  return hipGetLastError() == hipSuccess ? OK : ERR_LAUNCH;
+}
 
 int launch_qgemm(const GemmArgs& g, hipStream_t s) {
   if (g.M == 0) return OK;

@@ -93,4 +93,28 @@ struct GemmArgs {
 // optional low-rank branch.
 int launch_qgemm(const GemmArgs& g, hipStream_t s);
 
+// Grouped GEMM: up to kMaxGroupSegments projections of the same activations
+// in one launch (packed int4 or int8 weights per segment, per-row scales,
+// bf16 or sigmoid epilogue).
+constexpr int kMaxGroupSegments = 8;
+struct GroupSegment {
+  const void* w;
+  const float* sw;
+  int64_t n;
+  int w_bits;    // 4: packed int4 weights with the int4 activations; 8: int8 with int8
+  int epilogue;  // 0 bf16, 5 sigmoid
+  void* out;
+  int64_t ldo;
+};
+struct GroupedArgs {
+  const void* a4;
+  const float* sa4;
+  const void* a8;
+  const float* sa8;
+  int64_t M, K;
+  int nseg;
+  GroupSegment seg[kMaxGroupSegments];
+};
+int launch_qgemm_grouped(const GroupedArgs& g, hipStream_t s);
+
 }  // namespace ql

@@ -8,6 +8,8 @@
 #include "../../include/qlinear.h"
 #include "ql_internal.h"
 
+static_assert(QL_MAX_SEGMENTS == ql::kMaxGroupSegments, "segment limit mismatch");
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -156,7 +158,8 @@ int qgemm_w4a4(const void* a, const float* sa, int a_scale_mode, int a_layout, c
   }
   if (!valid_mode(a_scale_mode) || !valid_mode(w_scale_mode)) return QL_ERR_UNSUPPORTED;
   if (a_layout != QL_LAYOUT_I8 && a_layout != QL_LAYOUT_PACKED) return QL_ERR_UNSUPPORTED;
-  if (epilogue != QL_EPI_BF16 && epilogue != QL_EPI_F32 && epilogue != QL_EPI_I32) return QL_ERR_UNSUPPORTED;
+  if (epilogue != QL_EPI_BF16 && epilogue != QL_EPI_F32 && epilogue != QL_EPI_I32 && epilogue != QL_EPI_SIGMOID)
+    return QL_ERR_UNSUPPORTED;
   int st = validate_gemm_common(a, sa, w, sw, M, N, K, bias, out, ldo, epilogue);
   if (st != QL_OK) return st;
   if ((st = check_current_device()) != QL_OK) return st;
@@ -188,7 +191,7 @@ int qgemm_w8a8(const int8_t* a, const float* sa, int a_scale_mode, const int8_t*
       (w_scale_mode != QL_SCALE_TENSOR && w_scale_mode != QL_SCALE_ROW))
     return QL_ERR_UNSUPPORTED;
   if (epilogue != QL_EPI_BF16 && epilogue != QL_EPI_GATED_RESIDUAL && epilogue != QL_EPI_F32 &&
-      epilogue != QL_EPI_I32)
+      epilogue != QL_EPI_I32 && epilogue != QL_EPI_SIGMOID)
     return QL_ERR_UNSUPPORTED;
   int st = validate_gemm_common(a, sa, w, sw, M, N, K, bias, out, ldo, epilogue);
   if (st != QL_OK) return st;
@@ -257,6 +260,43 @@ int qgemm_w4a4_lowrank(const void* a, const float* sa, int a_scale_mode, int a_l
   g.out = out;
   g.ldo = ldo;
   return ql::launch_qgemm(g, static_cast<hipStream_t>(stream)) == QL_OK ? QL_OK : QL_ERR_LAUNCH;
+}
+
+int qgemm_grouped(const void* a4, const float* sa4, const void* a8, const float* sa8, int64_t M, int64_t K,
+                  const ql_segment* segments, int nseg, void* stream) {
+  if (!segments) return QL_ERR_NULL;
+  if (nseg < 1 || nseg > QL_MAX_SEGMENTS) return QL_ERR_SHAPE;
+  if (M < 0 || K <= 0 || K % 256 != 0) return QL_ERR_SHAPE;
+  if (K >= (int64_t(1) << 23) || M >= (int64_t(1) << 36) / K) return QL_ERR_SHAPE;
+  bool need4 = false, need8 = false;
+  for (int i = 0; i < nseg; ++i) {
+    const ql_segment& sg = segments[i];
+    if (sg.w_bits != 4 && sg.w_bits != 8) return QL_ERR_UNSUPPORTED;
+    if (sg.epilogue != QL_EPI_BF16 && sg.epilogue != QL_EPI_SIGMOID) return QL_ERR_UNSUPPORTED;
+    if (sg.n <= 0 || sg.n % 16 != 0 || sg.n * K >= (int64_t(1) << 31)) return QL_ERR_SHAPE;
+    if (sg.ldo < sg.n) return QL_ERR_SHAPE;
+    if (M > 0 && (!sg.w || !sg.sw || !sg.out)) return QL_ERR_NULL;
+    if (!al16(sg.w) || !al4(sg.sw) || !al16(sg.out) || (sg.ldo * 2) % 16 != 0) return QL_ERR_ALIGN;
+    (sg.w_bits == 4 ? need4 : need8) = true;
+  }
+  if (M > 0 && ((need4 && (!a4 || !sa4)) || (need8 && (!a8 || !sa8)))) return QL_ERR_NULL;
+  if (!al16(a4) || !al16(a8) || !al4(sa4) || !al4(sa8)) return QL_ERR_ALIGN;
+  int st = check_current_device();
+  if (st != QL_OK) return st;
+  if (M == 0) return QL_OK;
+  ql::GroupedArgs g{};
+  g.a4 = a4;
+  g.sa4 = sa4;
+  g.a8 = a8;
+  g.sa8 = sa8;
+  g.M = M;
+  g.K = K;
+  g.nseg = nseg;
+  for (int i = 0; i < nseg; ++i) {
+    const ql_segment& src = segments[i];
+    g.seg[i] = ql::GroupSegment{src.w, src.sw, src.n, src.w_bits, src.epilogue, src.out, src.ldo};
+  }
+  return ql::launch_qgemm_grouped(g, static_cast<hipStream_t>(stream)) == QL_OK ? QL_OK : QL_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -20,7 +20,7 @@ def L():
 def test_header_declares_the_entry_points():
     fns = header_functions()
     for name in ["rotate_quantize_act", "rmsnorm_rotate_quantize_act", "pack_weight_int4", "qgemm_w4a4", "qgemm_w8a8",
-                 "qgemm_w4a4_lowrank", "ql_status_string", "ql_device_supported"]:
+                 "qgemm_w4a4_lowrank", "qgemm_grouped", "ql_status_string", "ql_device_supported"]:
         assert name in fns
 
 
@@ -173,6 +173,41 @@ def test_qgemm_lowrank_validation(L):
     assert glr(L, epi=4) == -4
     assert glr(L, epi=2) == -4
 
+
+
+def grp(L, segs, **kw):
+    from rotated_bit_quantized_rotate_amd import _lib
+
+    a = dict(a4=ALIGNED, sa4=ALIGNED, a8=ALIGNED, sa8=ALIGNED, M=4, K=256, nseg=None)
+    a.update(kw)
+    arr = (_lib.Segment * max(len(segs), 1))()
+    for i, sg in enumerate(segs):
+        d = dict(w=ALIGNED, sw=ALIGNED, n=32, w_bits=4, epilogue=0, out=ALIGNED, ldo=32)
+        d.update(sg)
+        arr[i] = _lib.Segment(*(d[k] if not isinstance(d[k], ctypes.c_void_p) else d[k].value
+                                for k in ("w", "sw", "n", "w_bits", "epilogue", "out", "ldo")))
+    nseg = len(segs) if a["nseg"] is None else a["nseg"]
+    return L.qgemm_grouped(a["a4"], a["sa4"], a["a8"], a["sa8"], a["M"], a["K"], arr, nseg, None)
+
+
+def test_qgemm_grouped_validation(L):
+    assert L.qgemm_grouped(ALIGNED, ALIGNED, NULL, NULL, 4, 256, None, 1, None) == -1   # no segment array
+    assert grp(L, [{}], nseg=0) == -2
+    assert grp(L, [{}] * 9) == -2                                  # more than QL_MAX_SEGMENTS
+    assert grp(L, [{}], K=320) == -2                               # K % 256
+    assert grp(L, [{"n": 24, "ldo": 24}]) == -2                    # n % 16
+    assert grp(L, [{"ldo": 16}]) == -2                             # ldo < n
+    assert grp(L, [{"w_bits": 6}]) == -4
+    assert grp(L, [{"epilogue": 2}]) == -4                         # only bf16 / sigmoid
+    assert grp(L, [{"w": NULL}]) == -1
+    assert grp(L, [{"out": NULL}]) == -1
+    assert grp(L, [{"w": MISALIGNED}]) == -3
+    assert grp(L, [{"ldo": 36, "n": 32}]) == -3                    # rows not 16-byte aligned
+    assert grp(L, [{"w_bits": 8}], a8=NULL) == -1                  # int8 segment without int8 codes
+    assert grp(L, [{"w_bits": 4}], a4=NULL, sa4=NULL) == -1
+    assert grp(L, [{"w_bits": 4}], a8=NULL, sa8=NULL) in (-4, -6)  # unused operand may be NULL
+    assert grp(L, [{}, {"w_bits": 8, "epilogue": 5}, {"n": 48, "ldo": 48}]) in (-4, -6)
+    assert grp(L, [{}], M=0) in (0, -4, -6)
 
 def test_device_supported_without_gpu_is_false(L):
     import torch

@@ -709,3 +709,118 @@ def test_deterministic_outputs(Q):
         outs.append(bf16_bits(Q.qgemm_w4a4(a, sa, wq, sw, wl.K)))
         torch.cuda.synchronize()
     assert np.array_equal(outs[0], outs[1])
+
+
+# ------------------------------------------- grouped Q|K|V|gate GEMM (F2) --
+
+def _prep_weight(Q, wb, bits):
+    import torch
+
+    w = to_dev_bf16(wb)
+    if bits == 4:
+        return Q.pack_weight_int4(w, scale_mode="row")
+    wq = torch.empty(wb.shape, dtype=torch.int8, device="cuda")
+    sw = torch.empty((wb.shape[0],), dtype=torch.float32, device="cuda")
+    Q.rotate_quantize_act(w, bits=8, scale_mode="row", codes=wq, scales=sw)
+    return wq, sw
+
+
+def _qkvg(M, K, dims, seed):
+    """Activations and the four projections (q int4, k int8, v int8, gate int4 + sigmoid)."""
+    rng = np.random.default_rng(seed)
+    xb = W.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    specs = [("q", dims[0], 4, "bf16"), ("k", dims[1], 8, "bf16"), ("v", dims[2], 8, "bf16"),
+             ("gate", dims[3], 4, "sigmoid")]
+    ws = {name: W.to_bf16_bits((0.02 * rng.standard_normal((n, K))).astype(np.float32))
+          for name, n, _, _ in specs}
+    return xb, specs, ws
+
+
+@pytest.mark.parametrize("M,K,dims", [(300, 1536, (384, 96, 96, 384)), (64, 256, (320, 16, 48, 640)),
+                                      (515, 1024, (640, 160, 160, 640))])
+def test_grouped_qkvg_matches_oracle_and_separate_launches(Q, M, K, dims):
+    import torch
+
+    xb, specs, ws = _qkvg(M, K, dims, seed=M + K)
+    x = to_dev_bf16(xb)
+    a4, sa4, _ = Q.rotate_quantize_act(x, bits=4, scale_mode="row")
+    a8, sa8, _ = Q.rotate_quantize_act(x, bits=8, scale_mode="row")
+    prep = {name: _prep_weight(Q, ws[name], bits) for name, _, bits, _ in specs}
+    segs = [dict(w=prep[name][0], sw=prep[name][1], bits=bits, epilogue=epi) for name, _, bits, epi in specs]
+    outs = Q.qgemm_grouped(a4, sa4, a8, sa8, K, segs)
+    torch.cuda.synchronize()
+    qa = {4: O.quantize_activations(xb, 4, "row", True), 8: O.quantize_activations(xb, 8, "row", True)}
+    for (name, n, bits, epi), out in zip(specs, outs):
+        wq, sw = prep[name]
+        # the same product through the single-projection entry point, on the same codes: bit-exact
+        if bits == 4:
+            sep = Q.qgemm_w4a4(a4, sa4, wq, sw, K, epilogue=epi)
+        else:
+            sep = Q.qgemm_w8a8(a8, sa8, wq, sw, epilogue=epi)
+        torch.cuda.synchronize()
+        assert torch.equal(out, sep), name
+        # and against the oracle
+        qw = O.quantize_weights(ws[name], bits, "row", True)
+        want = O.epilogue(O.linear_fp64(qa[bits], qw), epi)
+        assert rel_fro(O.bf16_bits_to_f64(bf16_bits(out)), want) <= REL_FRO, name
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_sigmoid_epilogue_same_codes(Q, bits):
+    """The sigmoid epilogue element by element, from the oracle's own codes."""
+    import torch
+
+    M, N, K = 130, 640, 1024
+    rng = np.random.default_rng(41 + bits)
+    xb = W.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    wb = W.to_bf16_bits((0.05 * rng.standard_normal((N, K))).astype(np.float32))
+    qa = O.quantize_activations(xb, bits, "row", True)
+    qw = O.quantize_weights(wb, bits, "row", True)
+    a = to_dev(qa.codes)
+    sa = to_dev(np.asarray(qa.scales, np.float32))
+    sw = to_dev(np.asarray(qw.scales, np.float32))
+    if bits == 4:
+        out = Q.qgemm_w4a4(a, sa, to_dev(O.pack_int4(qw.codes)), sw, K, epilogue="sigmoid")
+    else:
+        out = Q.qgemm_w8a8(a, sa, to_dev(qw.codes), sw, epilogue="sigmoid")
+    torch.cuda.synchronize()
+    want = O.epilogue(O.linear_fp64(qa, qw), "sigmoid")
+    _assert_bf16_close(bf16_bits(out), want, 1.0)
+
+
+def test_grouped_stack_block_full_size(Q):
+    """One block's attention projections of the 2048^2 stack (16384 tokens, K = 5120:
+    q and gate [6144] int4, k and v [1536] int8) in one grouped launch: every
+    output equals the separate launches, and sampled rows match the oracle."""
+    import torch
+
+    M, K = 16384, 5120
+    g = torch.Generator(device="cuda")
+    g.manual_seed(91)
+    x = torch.randn((M, K), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    a4, sa4, _ = Q.rotate_quantize_act(x, bits=4, scale_mode="row")
+    a8, sa8, _ = Q.rotate_quantize_act(x, bits=8, scale_mode="row")
+    specs = [("q", 6144, 4, "bf16"), ("k", 1536, 8, "bf16"), ("v", 1536, 8, "bf16"), ("gate", 6144, 4, "sigmoid")]
+    wsb, prep = {}, {}
+    for name, n, bits, _ in specs:
+        w = (0.02 * torch.randn((n, K), generator=g, device="cuda", dtype=torch.float32)).to(torch.bfloat16)
+        wsb[name] = bf16_bits(w)
+        prep[name] = _prep_weight(Q, wsb[name], bits)
+    segs = [dict(w=prep[nm][0], sw=prep[nm][1], bits=b, epilogue=e) for nm, _, b, e in specs]
+    outs = Q.qgemm_grouped(a4, sa4, a8, sa8, K, segs)
+    torch.cuda.synchronize()
+    ri = torch.as_tensor(_sample_rows(M, 32), device="cuda")
+    xs = bf16_bits(x[ri])
+    qa = {4: O.quantize_activations(xs, 4, "row", True), 8: O.quantize_activations(xs, 8, "row", True)}
+    for (name, n, bits, epi), out in zip(specs, outs):
+        wq, sw = prep[name]
+        sep = (Q.qgemm_w4a4(a4, sa4, wq, sw, K, epilogue=epi) if bits == 4
+               else Q.qgemm_w8a8(a8, sa8, wq, sw, epilogue=epi))
+        torch.cuda.synchronize()
+        assert torch.equal(out, sep), name
+        del sep
+        cols = np.sort(np.random.default_rng(n).choice(n, 192, replace=False))
+        qw = O.quantize_weights(wsb[name][cols], bits, "row", True)      # weight rows are independent
+        want = O.epilogue(O.linear_fp64(qa[bits], qw), epi)
+        got = bf16_bits(out[ri][:, torch.as_tensor(cols, device="cuda")])
+        assert rel_fro(O.bf16_bits_to_f64(got), want) <= REL_FRO, name
