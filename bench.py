@@ -1,7 +1,8 @@
 """Benchmark of the rotated low-bit quantized linear on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--workload attn_proj_w4a4|ffdown_w8a8|svdq_gateup|stack|stack_fused]
+                    [--workload attn_proj_w4a4|ffdown_w8a8|svdq_gateup|stack|stack_fused|
+                                stack_grouped]
 
 Default workload (the headline line): one DiT attention projection at
 1024x1024 -- X bf16 [4096 x 5120] ~ N(0,1) with 1% outlier channels x30,
@@ -19,6 +20,9 @@ Other workloads (separate runs, same JSON shape):
                 fused into its prologues and one prepared activation per
                 shared input and precision (Q|gate int4, K|V int8, gate|up):
                 5 prologues per block instead of 8
+  stack_grouped stack_fused with each block's Q|K|V|gate projections in one
+                grouped launch (sigmoid on the gate; K, V in INT8) and its
+                gate|up projections in another: 4 GEMM launches per block
 
 Inputs and prepared weights are resident in HBM before timing.  One step is
 the layer's online path: rotate + quantize the activations
@@ -73,6 +77,7 @@ GEMM_KERNELS = {
     "svdq_gateup": ("qgemm_w4a4_lowrank", "4096x5120x40960", ["qgemm_pipe.hip"]),
     "stack": ("qgemm_stack", "224x16384", ["qgemm_pipe.hip"]),
     "stack_fused": ("qgemm_stack_fused", "224x16384", ["qgemm_pipe.hip"]),
+    "stack_grouped": ("qgemm_stack_grouped", "224x16384", ["qgemm_pipe.hip"]),
 }
 
 
@@ -107,7 +112,7 @@ def _parse():
     p.add_argument("--calib-copy", action="store_true")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     a = p.parse_args()
-    stack = a.workload in ("stack", "stack_fused")
+    stack = a.workload.startswith("stack")
     if a.steps is None:
         a.steps = 3 if stack else 200
     a.warmup_min = None
@@ -417,7 +422,7 @@ def case_stack(Q, W, dev):
     return c
 
 
-def case_stack_fused(Q, W, dev):
+def case_stack_fused(Q, W, dev, grouped=False):
     """The stack's 224 linears (same weights) as a DiT block runs them when
     the block's RMSNorm + modulation live in the quantization prologue and one
     prepared activation serves every projection of the same input (model card
@@ -429,7 +434,8 @@ def case_stack_fused(Q, W, dev):
     synthetic adaLN vectors (gamma ~ 1 + 0.1 N, scale ~ 0.2 N, shift ~ 0.1 N,
     seeds 10^7 + 8 b + i).  The attention input is prepared once as int4
     codes (wq, attn_gate) and once as int8 codes (wk, wv); the MLP input once
-    (mlp_gate, mlp_up)."""
+    (mlp_gate, mlp_up).  grouped: the block's Q|K|V|gate projections run as
+    one grouped launch (sigmoid on the gate) and gate|up as another."""
     import torch
     M = 16384
     layers = W.stack_layers()
@@ -440,7 +446,8 @@ def case_stack_fused(Q, W, dev):
              8: torch.empty((M * maxk,), dtype=torch.int8, device=dev)}
     sa = {4: torch.empty((M,), dtype=torch.float32, device=dev),
           8: torch.empty((M,), dtype=torch.float32, device=dev)}
-    out = torch.empty((M * maxn,), dtype=torch.bfloat16, device=dev)
+    # grouped launches write every segment at once: room for gate|up side by side
+    out = torch.empty((M * maxn * (2 if grouped else 1),), dtype=torch.bfloat16, device=dev)
     c = Case()
     prep = 0.0
     n4 = 0
@@ -503,36 +510,66 @@ def case_stack_fused(Q, W, dev):
             c.gemm_bytes += M * k + M * 4 + n * 4 + M * n * 2
             c.gemm_launches += 1
 
-        prologue(x_attn, 4, norm_attn)
-        gemm("wq")
-        gemm("attn_gate")
-        prologue(x_attn, 8, norm_attn)
-        gemm("wk")
-        gemm("wv")
+        def grouped_gemm(parts):
+            segs, off = [], 0
+            for name, epi in parts:
+                wq, sw, n, k, bits = lw[name]
+                o = out[off: off + M * n].view(M, n)
+                off += M * n
+                segs.append(dict(w=wq, sw=sw, bits=bits, epilogue=epi, out=o))
+                c.ops += 2 * M * n * k
+                c.gemm_bytes += (n * k // 2 if bits == 4 else n * k) + n * 4 + M * n * 2
+            k = lw[parts[0][0]][3]
+            bits_used = {lw[nm][4] for nm, _ in parts}
+            c.gemm_bytes += sum(M * k + M * 4 for _ in bits_used)
+            a4 = codes[4][: M * k].view(M, k) if 4 in bits_used else None
+            a8 = codes[8][: M * k].view(M, k) if 8 in bits_used else None
+            c.launches.append(("gemm", lambda: Q.qgemm_grouped(a4, sa[4] if a4 is not None else None, a8,
+                                                               sa[8] if a8 is not None else None, k, segs)))
+            c.gemm_launches += 1
+
+        if grouped:
+            prologue(x_attn, 4, norm_attn)
+            prologue(x_attn, 8, norm_attn)
+            grouped_gemm([("wq", "bf16"), ("wk", "bf16"), ("wv", "bf16"), ("attn_gate", "sigmoid")])
+        else:
+            prologue(x_attn, 4, norm_attn)
+            gemm("wq")
+            gemm("attn_gate")
+            prologue(x_attn, 8, norm_attn)
+            gemm("wk")
+            gemm("wv")
         prologue(x_o, lw["wo"][4], None)
         gemm("wo")
         prologue(x_mlp, 4, norm_mlp)
-        gemm("mlp_gate")
-        gemm("mlp_up")
+        if grouped:
+            grouped_gemm([("mlp_gate", "bf16"), ("mlp_up", "bf16")])
+        else:
+            gemm("mlp_gate")
+            gemm("mlp_up")
         prologue(x_down, lw["mlp_down"][4], None)
         gemm("mlp_down")
     torch.cuda.synchronize()
     c.prep_ms = prep
     c.metric = ("effective int TOPS + % int8 MFMA peak, mixed 224-linear DiT stack at 2048^2 "
-                "(16384 tokens, 128 W4A4 + 96 W8A8), norm fused + prepared activations reused")
+                "(16384 tokens, 128 W4A4 + 96 W8A8), norm fused + prepared activations reused"
+                + (" + grouped Q|K|V|gate and gate|up GEMMs" if grouped else ""))
     c.dtype = "int8 MFMA (int4/int8 codes), int32 accumulate, bf16 out"
     c.config = {"workload": "28-block DiT linear stack at 2048^2: 16384 tokens, d=5120, ffn=20480, "
                             f"{len(layers)} linears ({n4} W4A4, {len(layers) - n4} W8A8), per-token / "
                             "per-row scales, group-256 Hadamard, bf16 out; RMSNorm + adaLN modulation fused "
                             "into the attention and MLP prologues, one prepared activation per shared input "
-                            "and precision (5 prologues per block), every input resident",
+                            "and precision (5 prologues per block)"
+                            + ("; Q|K|V|gate (sigmoid gate, K/V INT8) and gate|up as grouped launches "
+                               "(4 GEMM launches per block)" if grouped else "") + ", every input resident",
                 "M": M, "layers": len(layers), "prologues": 5 * W.STACK_BLOCKS, "global_batch": M,
                 "parallelism": "single GPU"}
     return c
 
 
 CASES = {"attn_proj_w4a4": case_attn, "ffdown_w8a8": case_ffdown, "svdq_gateup": case_svdq,
-         "stack": case_stack, "stack_fused": case_stack_fused}
+         "stack": case_stack, "stack_fused": case_stack_fused,
+         "stack_grouped": lambda Q, W, dev: case_stack_fused(Q, W, dev, grouped=True)}
 
 
 # ------------------------------------------------------------------- main --
@@ -571,7 +608,7 @@ def main():
         while w < args.warmup_min or time.perf_counter() - t_w < WARMUP_S:
             step()
             w += 1
-            if w % (1 if args.workload in ("stack", "stack_fused") else 16) == 0:
+            if w % (1 if args.workload.startswith("stack") else 16) == 0:
                 torch.cuda.synchronize()  # keep the host within a few steps of the GPU
         args.warmup = w
     torch.cuda.synchronize()

@@ -901,15 +901,29 @@ hipError_t launch_lowrank(const PArgs& p, int epi, hipStream_t s) {
 // precision (packed INT4 or INT8 weights; int8-container INT4 or INT8
 // activation codes, per-token scales) and epilogue (bf16 or sigmoid).  The
 // tiles of all segments form one grid, so the small projections fill the
-// large ones' last wave instead of leaving their own tail.  Both weight
-// formats use 256 x 320 tiles; a workgroup runs the tile body of its
-// segment's format on one LDS buffer sized for the larger ring.
-using CfgG4 = Cfg<256, 320, 2, 4, false, true>;
-using CfgG8 = Cfg<256, 320, 2, 4, false, false>;
-constexpr int kGroupedLds = (CfgG4::NSTAGE * CfgG4::STAGE > CfgG8::NSTAGE * CfgG8::STAGE)
-                                ? CfgG4::NSTAGE * CfgG4::STAGE
-                                : CfgG8::NSTAGE * CfgG8::STAGE;
+// large ones' last wave instead of leaving their own tail.  Each segment
+// uses 256 x 320 or 256 x 256 tiles, whichever pads its columns less (320 on
+// a tie), like a single launch; a workgroup runs the tile body of its
+// segment's format and width on one LDS buffer sized for the largest ring.
+using CfgG4W = Cfg<256, 320, 2, 4, false, true>;
+using CfgG4N = Cfg<256, 256, 2, 4, false, true>;
+using CfgG8W = Cfg<256, 320, 2, 4, false, false>;
+using CfgG8N = Cfg<256, 256, 2, 4, false, false>;
+template <class C>
+constexpr int ring_bytes() { return C::NSTAGE * C::STAGE; }
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int kGroupedLds = cmax(cmax(ring_bytes<CfgG4W>(), ring_bytes<CfgG4N>()),
+                                 cmax(ring_bytes<CfgG8W>(), ring_bytes<CfgG8N>()));
 static_assert(kGroupedLds <= kLdsBytes, "grouped LDS ring too large");
+
+// the segment's tile body on the shared ring
+template <class C>
+__device__ __forceinline__ void grouped_body(const PArgs& p, int tile_m, int tile_n, bool sigmoid,
+                                             uint8_t* const r) {
+  uint8_t* const r2 = C::NSTAGE == 3 ? r + 2 * C::STAGE : r;
+  if (sigmoid) pipe_tile<C, EPI_SIGMOID, false>(p, tile_m, tile_n, r, r + C::STAGE, r2);
+  else pipe_tile<C, EPI_BF16, false>(p, tile_m, tile_n, r, r + C::STAGE, r2);
+}
 
 struct GSeg {
   const uint8_t* w;
@@ -919,6 +933,7 @@ struct GSeg {
   int64_t n;
   int w8;        // 1: int8 weights and int8 activation codes
   int sigmoid;   // 1: sigmoid epilogue
+  int wide;      // 1: 256 x 320 tiles, 0: 256 x 256
   int tiles_n;
   int tile0;     // first linear tile of the segment
 };
@@ -956,16 +971,13 @@ __global__ __launch_bounds__(512, 1) void qgemm_grouped_kernel(GArgs g) {
   p.shift = sg.w8 ? 0 : 4;
   int tile_m, tile_n;
   grouped_tile(bl - sg.tile0, p.tiles_m, sg.tiles_n, p.group_m, tile_m, tile_n);
+  const bool sig = sg.sigmoid != 0;
   if (sg.w8) {
-    uint8_t* const r = lds;
-    if (sg.sigmoid) pipe_tile<CfgG8, EPI_SIGMOID, false>(p, tile_m, tile_n, r, r + CfgG8::STAGE, r);
-    else pipe_tile<CfgG8, EPI_BF16, false>(p, tile_m, tile_n, r, r + CfgG8::STAGE, r);
+    if (sg.wide) grouped_body<CfgG8W>(p, tile_m, tile_n, sig, lds);
+    else grouped_body<CfgG8N>(p, tile_m, tile_n, sig, lds);
   } else {
-    uint8_t* const r = lds;
-    if (sg.sigmoid)
-      pipe_tile<CfgG4, EPI_SIGMOID, false>(p, tile_m, tile_n, r, r + CfgG4::STAGE, r + 2 * CfgG4::STAGE);
-    else
-      pipe_tile<CfgG4, EPI_BF16, false>(p, tile_m, tile_n, r, r + CfgG4::STAGE, r + 2 * CfgG4::STAGE);
+    if (sg.wide) grouped_body<CfgG4W>(p, tile_m, tile_n, sig, lds);
+    else grouped_body<CfgG4N>(p, tile_m, tile_n, sig, lds);
   }
 }
 
@@ -997,7 +1009,9 @@ int launch_qgemm_grouped(const GroupedArgs& ga, hipStream_t s) {
     d.n = src.n;
     d.w8 = src.w_bits == 8 ? 1 : 0;
     d.sigmoid = src.epilogue == EPI_SIGMOID ? 1 : 0;
-    d.tiles_n = (int)((src.n + 319) / 320);
+    const int64_t pad320 = (src.n + 319) / 320 * 320 - src.n, pad256 = (src.n + 255) / 256 * 256 - src.n;
+    d.wide = pad320 <= pad256 ? 1 : 0;
+    d.tiles_n = (int)(d.wide ? (src.n + 319) / 320 : (src.n + 255) / 256);
     d.tile0 = t;
     t += g.base.tiles_m * d.tiles_n;
   }
