@@ -32,7 +32,9 @@ brute-force integer loops (GEMM), grid-exact end-to-end reconstruction
 (whole linear), the low-rank identity, textbook SiLU values, and for the
 fused RMSNorm + modulation prologue closed forms (unit mean square, eps
 inside the root), scale invariance, a worked modulation example, brute-force
-loops and the reduction to the plain prologue when the norm is the identity.  No function
+loops and the reduction to the plain prologue when the norm is the identity, and for the
+FP6 (e2m3) code layout the format's constants, hand-derived bit patterns, a
+worked packing example and exact float32 summation at the largest K.  No function
 here is "parity unpinned".
 """
 

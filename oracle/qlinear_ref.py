@@ -19,6 +19,7 @@ __all__ = [
     "regular_hadamard_256", "rotate",
     "quantize", "dequantize",
     "pack_int4", "unpack_int4",
+    "fp6_e2m3_value", "fp6_e2m3_encode", "pack_fp6", "unpack_fp6",
     "int_gemm", "int_gemm_grouped",
     "silu", "sigmoid", "epilogue",
     "QuantResult", "quantize_activations", "quantize_weights",
@@ -206,6 +207,82 @@ def unpack_int4(p: np.ndarray) -> np.ndarray:
 # from running the matmul on integer units with activations quantized too;
 # [lab] Study 2/3: the fused low-bit multiply is the lever).
 # --------------------------------------------------------------------------
+
+# --------------------------------------------------------------------------
+# FP6 (e2m3) code layout -- an alternative encoding of the same int4 codes
+# for gfx950's FP6 matrix instructions.  Every integer -7..7 is exactly an
+# e2m3 value (sign bit, 2 exponent bits with bias 1, 3 mantissa bits: the
+# FP6 E2M3 element of the OCP microscaling formats), so the encoding changes
+# no code and no product; products of two codes are integers of magnitude
+# <= 49 and their sums stay exact in float32 while 49 K < 2^24.
+# Layout (this library's own): a row of K codes is K/128 blocks of 96 bytes.
+# In block b, sub-block g (0..3) holds channels 128b + 32g + i (i = 0..31)
+# as the 192-bit little-endian integer v_g with channel i in bits 6i..6i+5;
+# bytes 16g..16g+15 of the block are the low 16 bytes of v_g and bytes
+# 64 + 8g .. 64 + 8g + 7 its high 8 bytes.
+# --------------------------------------------------------------------------
+
+def fp6_e2m3_value(bits) -> np.ndarray:
+    """Decode 6-bit e2m3 patterns to float64 from the format's definition:
+    sign = bit 5, exponent e = bits 4..3, mantissa m = bits 2..0;
+    e == 0: (-1)^s * m / 8 (subnormal); else (-1)^s * 2^(e-1) * (1 + m/8)."""
+    b = np.asarray(bits, dtype=np.int64)
+    s = np.where((b >> 5) & 1, -1.0, 1.0)
+    e = (b >> 3) & 3
+    m = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0, np.ldexp(1.0 + m / 8.0, (e - 1).astype(np.int64)))
+    return s * mag
+
+
+def fp6_e2m3_encode(q: np.ndarray) -> np.ndarray:
+    """int codes -7..7 -> their exact e2m3 bit patterns, found by searching
+    all 64 patterns with the decoder (zero takes the +0 pattern)."""
+    q = np.asarray(q, dtype=np.int64)
+    if np.abs(q).max(initial=0) > 7:
+        raise ValueError("FP6 codes hold -7..7")
+    vals = fp6_e2m3_value(np.arange(64))
+    out = np.zeros(q.shape, dtype=np.int64)
+    for code in range(-7, 8):
+        out[q == code] = np.nonzero(vals == code)[0].min()
+    return out
+
+
+def pack_fp6(q: np.ndarray) -> np.ndarray:
+    """int8 codes [R, K] (-7..7, K % 128 == 0) -> uint8 [R, 3K/4] in the FP6 layout."""
+    q = np.asarray(q)
+    R, K = q.shape
+    if K % 128:
+        raise ValueError("FP6 layout needs K % 128 == 0")
+    pat = fp6_e2m3_encode(q)
+    out = np.zeros((R, K // 128, 96), dtype=np.uint8)
+    for r in range(R):
+        for b in range(K // 128):
+            for g in range(4):
+                v = 0
+                for i in range(32):
+                    v |= int(pat[r, 128 * b + 32 * g + i]) << (6 * i)
+                raw = np.frombuffer(v.to_bytes(24, "little"), dtype=np.uint8)
+                out[r, b, 16 * g: 16 * g + 16] = raw[:16]
+                out[r, b, 64 + 8 * g: 64 + 8 * g + 8] = raw[16:]
+    return out.reshape(R, K // 128 * 96)
+
+
+def unpack_fp6(p: np.ndarray) -> np.ndarray:
+    """uint8 [R, 3K/4] in the FP6 layout -> int8 codes [R, K]."""
+    p = np.asarray(p, dtype=np.uint8)
+    R, nb = p.shape
+    K = nb // 96 * 128
+    out = np.zeros((R, K), dtype=np.int8)
+    for r in range(R):
+        for b in range(K // 128):
+            blk = p[r, 96 * b: 96 * b + 96]
+            for g in range(4):
+                raw = bytes(blk[16 * g: 16 * g + 16]) + bytes(blk[64 + 8 * g: 64 + 8 * g + 8])
+                v = int.from_bytes(raw, "little")
+                pats = np.array([(v >> (6 * i)) & 63 for i in range(32)])
+                out[r, 128 * b + 32 * g: 128 * b + 32 * g + 32] = fp6_e2m3_value(pats).astype(np.int8)
+    return out
+
 
 def int_gemm(qa: np.ndarray, qw: np.ndarray) -> np.ndarray:
     """acc[m, n] = sum_k qa[m, k] * qw[n, k], exactly, as int64.  Formed by a

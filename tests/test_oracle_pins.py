@@ -468,3 +468,76 @@ def test_sigmoid_symmetry_range_and_silu_relation():
     assert np.allclose(O.silu(z), z * s, rtol=1e-15, atol=1e-300)         # silu(z) = z sigma(z)
     y = np.array([[0.0, 1.0986122886681098]])
     assert np.allclose(O.epilogue(y, "sigmoid"), [[0.5, 0.75]], rtol=0, atol=1e-15)
+
+
+# ---- FP6 (e2m3) code layout -------------------------------------------------
+# The FP6 E2M3 element of the OCP microscaling formats: largest normal 7.5,
+# smallest normal 1.0, smallest subnormal 0.125, 0.875 the largest subnormal;
+# bit 5 is the sign.
+
+def test_fp6_decoder_format_constants():
+    v = O.fp6_e2m3_value(np.arange(64))
+    assert v[0] == 0.0 and v[1] == 0.125 and v[7] == 0.875 and v[8] == 1.0 and v[31] == 7.5
+    assert v[32] == 0.0 and np.signbit(v[32]) and v[63] == -7.5
+    assert np.array_equal(v[32:], -v[:32])
+    assert np.all(np.diff(v[:32]) > 0)                 # magnitudes strictly increase with the pattern
+    assert np.abs(v).max() == 7.5
+
+
+def test_fp6_codes_are_exact_and_hand_derived():
+    # patterns of |c| = 0..7 worked out by hand from the definition
+    hand = {0: 0, 1: 8, 2: 16, 3: 20, 4: 24, 5: 26, 6: 28, 7: 30}
+    q = np.arange(-7, 8).reshape(1, 15)
+    q = np.concatenate([q, np.zeros((1, 128 - 15), dtype=q.dtype)], axis=1).astype(np.int8)
+    packed = O.pack_fp6(q)
+    v0 = int.from_bytes(bytes(packed[0, 0:16]) + bytes(packed[0, 64:72]), "little")
+    for i, c in enumerate(range(-7, 8)):
+        pat = (v0 >> (6 * i)) & 63
+        assert pat == hand[abs(c)] + (32 if c < 0 else 0), c
+        assert O.fp6_e2m3_value(pat) == c
+
+
+def test_fp6_pack_golden_example(golden):
+    q = np.zeros((1, 128), dtype=np.int8)
+    q[0, 0], q[0, 1], q[0, 32], q[0, 63] = 1, -7, 3, 7
+    want = np.zeros(96, dtype=np.uint8)
+    for line in golden("fp6_pack_example.txt"):
+        i, v = map(int, line.split())
+        want[i] = v
+    got = O.pack_fp6(q)
+    assert got.shape == (1, 96)
+    assert np.array_equal(got[0], want)
+    assert np.array_equal(O.unpack_fp6(got), q)
+
+
+def test_fp6_round_trip_and_rejects():
+    rng = np.random.default_rng(11)
+    q = rng.integers(-7, 8, size=(5, 384)).astype(np.int8)
+    assert np.array_equal(O.unpack_fp6(O.pack_fp6(q)), q)
+    with pytest.raises(ValueError):
+        O.pack_fp6(np.full((1, 128), 8, dtype=np.int8))
+    with pytest.raises(ValueError):
+        O.pack_fp6(np.zeros((1, 96), dtype=np.int8))
+
+
+def test_fp6_products_sum_exactly_in_float32():
+    # decoded products are integers <= 49 in magnitude; a float32 running sum
+    # over K = 5120 stays below 2^24 and so equals the exact integer dot
+    # product, including the all-extreme row
+    rng = np.random.default_rng(12)
+    K = 5120
+    a = rng.integers(-7, 8, size=(3, K)).astype(np.int8)
+    w = rng.integers(-7, 8, size=(2, K)).astype(np.int8)
+    a[0] = 7
+    w[0] = 7
+    w[1, ::2] = -7
+    da = O.fp6_e2m3_value(O.fp6_e2m3_encode(a)).astype(np.float32)
+    dw = O.fp6_e2m3_value(O.fp6_e2m3_encode(w)).astype(np.float32)
+    exact = O.int_gemm(a, w)
+    for i in range(3):
+        for j in range(2):
+            s = np.float32(0)
+            for k in range(0, K, 128):             # one 128-channel block per step, as the matrix core does
+                s = np.float32(s + np.float32(np.dot(da[i, k:k + 128].astype(np.float64), dw[j, k:k + 128])))
+            assert int(s) == exact[i, j]
+    assert exact[0, 0] == 49 * K
