@@ -253,35 +253,25 @@ def pack_fp6(q: np.ndarray) -> np.ndarray:
     R, K = q.shape
     if K % 128:
         raise ValueError("FP6 layout needs K % 128 == 0")
-    pat = fp6_e2m3_encode(q)
-    out = np.zeros((R, K // 128, 96), dtype=np.uint8)
-    for r in range(R):
-        for b in range(K // 128):
-            for g in range(4):
-                v = 0
-                for i in range(32):
-                    v |= int(pat[r, 128 * b + 32 * g + i]) << (6 * i)
-                raw = np.frombuffer(v.to_bytes(24, "little"), dtype=np.uint8)
-                out[r, b, 16 * g: 16 * g + 16] = raw[:16]
-                out[r, b, 64 + 8 * g: 64 + 8 * g + 8] = raw[16:]
-    return out.reshape(R, K // 128 * 96)
+    pat = fp6_e2m3_encode(q).reshape(R, K // 128, 4, 32)
+    # bit 6i + b of v_g is bit b of channel i's pattern
+    bits = ((pat[..., None] >> np.arange(6)) & 1).astype(np.uint8).reshape(R, K // 128, 4, 192)
+    v = np.packbits(bits, axis=-1, bitorder="little")          # [R, K/128, 4, 24] little-endian bytes
+    blk = np.concatenate([v[..., :16].reshape(R, K // 128, 64),  # low 16 bytes of v_0..v_3
+                          v[..., 16:].reshape(R, K // 128, 32)], axis=-1)  # then their high 8 bytes
+    return blk.reshape(R, K // 128 * 96)
 
 
 def unpack_fp6(p: np.ndarray) -> np.ndarray:
     """uint8 [R, 3K/4] in the FP6 layout -> int8 codes [R, K]."""
     p = np.asarray(p, dtype=np.uint8)
     R, nb = p.shape
-    K = nb // 96 * 128
-    out = np.zeros((R, K), dtype=np.int8)
-    for r in range(R):
-        for b in range(K // 128):
-            blk = p[r, 96 * b: 96 * b + 96]
-            for g in range(4):
-                raw = bytes(blk[16 * g: 16 * g + 16]) + bytes(blk[64 + 8 * g: 64 + 8 * g + 8])
-                v = int.from_bytes(raw, "little")
-                pats = np.array([(v >> (6 * i)) & 63 for i in range(32)])
-                out[r, 128 * b + 32 * g: 128 * b + 32 * g + 32] = fp6_e2m3_value(pats).astype(np.int8)
-    return out
+    blk = p.reshape(R, nb // 96, 96)
+    v = np.concatenate([blk[..., :64].reshape(R, nb // 96, 4, 16),
+                        blk[..., 64:].reshape(R, nb // 96, 4, 8)], axis=-1)    # [R, K/128, 4, 24]
+    bits = np.unpackbits(v, axis=-1, bitorder="little").reshape(R, nb // 96, 4, 32, 6)
+    pat = (bits.astype(np.int64) << np.arange(6)).sum(axis=-1)
+    return fp6_e2m3_value(pat).astype(np.int8).reshape(R, nb // 96 * 128)
 
 
 def int_gemm(qa: np.ndarray, qw: np.ndarray) -> np.ndarray:
