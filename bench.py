@@ -65,6 +65,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 INT8_MFMA_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POP/s
+FP6_MFMA_PEAK_TOPS = 10100.0     # MI355X dense FP6 / FP4 MFMA, 10.1 PFLOP/s
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 CALIB_BYTES = 256 << 20
 CSRC = "rotated_bit_quantized_rotate_amd/csrc/"
@@ -73,6 +74,7 @@ HEADLINE_METRIC = "effective int TOPS + % int8 MFMA peak, W4A4 rotated GEMM M=40
 # workload -> (GEMM kernel label, shape tag, sources whose text defines that kernel)
 GEMM_KERNELS = {
     "attn_proj_w4a4": ("qgemm_w4a4", "4096x5120x5120", ["qgemm_pipe.hip"]),
+    "attn_proj_w4a4_fp6": ("qgemm_w4a4_fp6", "4096x5120x5120", ["qgemm_pipe.hip"]),
     "ffdown_w8a8": ("qgemm_w8a8", "4096x20480x5120", ["qgemm_pipe.hip"]),
     "svdq_gateup": ("qgemm_w4a4_lowrank", "4096x5120x40960", ["qgemm_pipe.hip"]),
     "stack": ("qgemm_stack", "224x16384", ["qgemm_pipe.hip"]),
@@ -243,6 +245,7 @@ class Case:
         self.config = {}
         self.dtype = ""
         self.wl = None            # host workload for the CPU baseline
+        self.peak = INT8_MFMA_PEAK_TOPS   # dense matrix peak of the GEMM's instruction
 
 
 def _bf16_dev(bits, dev):
@@ -287,6 +290,40 @@ def case_attn(Q, W, dev):
                             "X bf16 [4096x5120] N(0,1) + 1% outlier channels x30, "
                             "W [5120x5120] packed int4, group-256 Hadamard, per-token / "
                             "per-row scales, bf16 out",
+                "M": M, "N": N, "K": K, "global_batch": M, "parallelism": "single GPU"}
+    c.wl = wl
+    return c
+
+
+def case_attn_fp6(Q, W, dev):
+    """The attention projection with the int4 codes in the FP6 e2m3 layout,
+    multiplied on the FP6 matrix instruction (same codes, same output)."""
+    import torch
+    wl = W.attn_proj_w4a4()
+    M, N, K = wl.M, wl.N, wl.K
+    x, w = _bf16_dev(wl.x, dev), _bf16_dev(wl.w, dev)
+    codes = torch.empty((M, K // 4 * 3), dtype=torch.uint8, device=dev)
+    sa = torch.empty((M,), dtype=torch.float32, device=dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    wq = torch.empty((N, K // 4 * 3), dtype=torch.uint8, device=dev)
+    sw = torch.empty((N,), dtype=torch.float32, device=dev)
+    c = Case()
+    c.prep_ms = _timed_prep(lambda: Q.pack_weight_fp6(w, packed=wq, scales=sw))
+    c.launches = [
+        ("prologue", lambda: Q.rotate_quantize_act(x, bits=4, scale_mode="row", layout="fp6", codes=codes,
+                                                   scales=sa)),
+        ("gemm", lambda: Q.qgemm_w4a4_fp6(codes, sa, wq, sw, K, out=out)),
+    ]
+    c.ops = wl.int_ops
+    c.gemm_launches = 1
+    c.pro_bytes = M * K * 2 + M * K // 4 * 3 + M * 4
+    c.gemm_bytes = (M + N) * K // 4 * 3 + M * 4 + N * 4 + M * N * 2
+    c.metric = "effective int TOPS, W4A4 rotated GEMM M=4096 K=N=5120 on the FP6 matrix instruction (experiment)"
+    c.dtype = "fp6 e2m3 MFMA (exact int4 codes), fp32 accumulate (exact), bf16 out"
+    c.peak = FP6_MFMA_PEAK_TOPS
+    c.config = {"workload": "W4A4 rotated linear, DiT attention projection at 1024^2, int4 codes stored as "
+                            "FP6 e2m3: X bf16 [4096x5120] N(0,1) + 1% outlier channels x30, W [5120x5120], "
+                            "group-256 Hadamard, per-token / per-row scales, bf16 out",
                 "M": M, "N": N, "K": K, "global_batch": M, "parallelism": "single GPU"}
     c.wl = wl
     return c
@@ -567,7 +604,7 @@ def case_stack_fused(Q, W, dev, grouped=False):
     return c
 
 
-CASES = {"attn_proj_w4a4": case_attn, "ffdown_w8a8": case_ffdown, "svdq_gateup": case_svdq,
+CASES = {"attn_proj_w4a4": case_attn, "attn_proj_w4a4_fp6": case_attn_fp6, "ffdown_w8a8": case_ffdown, "svdq_gateup": case_svdq,
          "stack": case_stack, "stack_fused": case_stack_fused,
          "stack_grouped": lambda Q, W, dev: case_stack_fused(Q, W, dev, grouped=True)}
 
@@ -703,8 +740,8 @@ def main():
         "weight_prep_ms": round(case.prep_ms, 5),
         "wall_ms_timed_region": round(wall_ms, 3),
         "roofline": {"bound": "mfma", "kernel": label,
-                     "achieved": round(gemm_tops, 2), "peak": INT8_MFMA_PEAK_TOPS,
-                     "unit": "TOP/s", "frac": round(gemm_tops / INT8_MFMA_PEAK_TOPS, 4),
+                     "achieved": round(gemm_tops, 2), "peak": case.peak,
+                     "unit": "TOP/s", "frac": round(gemm_tops / case.peak, 4),
                      "traffic": traffic,
                      "algorithmic_bytes": int(case.gemm_bytes // case.gemm_launches)},
     }

@@ -83,8 +83,16 @@ enum {
  * QL_LAYOUT_PACKED : two signed 4-bit codes per byte, [R, K/2].  Within every
  *                    run of 8 consecutive channels 8c..8c+7, byte 4c+j
  *                    (j = 0..3) holds channel 8c+j in its low nibble and
- *                    channel 8c+j+4 in its high nibble (two's complement).   */
-enum { QL_LAYOUT_I8 = 0, QL_LAYOUT_PACKED = 1 };
+ *                    channel 8c+j+4 in its high nibble (two's complement).
+ * QL_LAYOUT_FP6    : each int4 code as its exact FP6 e2m3 value (sign bit, 2
+ *                    exponent bits with bias 1, 3 mantissa bits), [R, 3K/4]
+ *                    bytes; for the FP6 GEMM only.  A row is K/128 blocks of
+ *                    96 bytes.  In a block, 32-channel sub-block g (0..3) is
+ *                    the 192-bit little-endian value v_g holding its channel
+ *                    i in bits 6i..6i+5; block bytes 16g..16g+15 hold the
+ *                    low 16 bytes of v_g and bytes 64+8g..64+8g+7 its high
+ *                    8 bytes.                                               */
+enum { QL_LAYOUT_I8 = 0, QL_LAYOUT_PACKED = 1, QL_LAYOUT_FP6 = 2 };
 
 /* ---- GEMM epilogues ---------------------------------------------------- */
 enum {
@@ -118,9 +126,10 @@ int ql_device_supported(int device);
  *   x      [M, K] bf16, row stride ldx (elements, >= K, multiple of 8)
  *   bits   4 or 8
  *   scale_mode  QL_SCALE_TENSOR | QL_SCALE_ROW | QL_SCALE_GROUP64
- *   layout QL_LAYOUT_I8 or QL_LAYOUT_PACKED (PACKED only with bits == 4)
+ *   layout QL_LAYOUT_I8, QL_LAYOUT_PACKED or QL_LAYOUT_FP6 (the last two
+ *          only with bits == 4)
  *   rotate 1: rotate each 256-group by H/16 first; 0: quantize x as is
- *   codes  out: [M, K] int8 or [M, K/2] packed bytes, dense rows
+ *   codes  out: [M, K] int8, [M, K/2] packed or [M, 3K/4] FP6 bytes, dense rows
  *   scales out: float32 [1] | [M] | [M, K/64] (scale = absmax / qmax)
  *   l1, rank, lr  optional SVDQuant down-projection: if l1 != NULL,
  *          lr[M, rank] (bf16, dense rows) = bf16(x[M,K] @ l1[K, rank]) with the
@@ -175,6 +184,15 @@ int pack_weight_int4(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
                      int scale_mode, int rotate, uint8_t* packed, float* scales,
                      void* stream);
 
+/* Offline INT4 weight preparation for the FP6 GEMM (qgemm_w4a4_fp6): the
+ * same codes and scales as pack_weight_int4, stored in QL_LAYOUT_FP6;
+ * equal to rotate_quantize_act(w, N, K, ldw, 4, scale_mode, QL_LAYOUT_FP6,
+ * rotate, ...).  scale_mode TENSOR | ROW.
+ *   packed out: [N, 3K/4] bytes in the QL_LAYOUT_FP6 order                 */
+int pack_weight_fp6(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
+                    int scale_mode, int rotate, uint8_t* packed, float* scales,
+                    void* stream);
+
 /* W4A4 GEMM + dequant epilogue (model card "Krea 2 Turbo OrbitQuant W4A4",
  * section "Fused transformer (OrbitQuant 0.11)": W4A4 GEMMs for attention
  * and gate/up projections).
@@ -192,6 +210,27 @@ int qgemm_w4a4(const void* a, const float* sa, int a_scale_mode, int a_layout,
                int64_t M, int64_t N, int64_t K,
                const uint16_t* bias, int epilogue, void* out, int64_t ldo,
                void* stream);
+
+/* Experimental W4A4 GEMM on gfx950's FP6 matrix instructions.  The pages
+ * run the same checkpoint faster as an FP4 build on a GPU whose matrix units
+ * take that format natively (model card "Krea 2 Turbo Nunchaku Lite INT4
+ * r32", section "Benchmark"); the MI355X counterpart for INT4 codes is FP6
+ * e2m3, which holds every code -7..7 exactly and runs at twice the INT8
+ * matrix rate.  Products of two codes are integers of magnitude <= 49 and
+ * their float32 sums are exact while 49 K < 2^24, so for K < 342392 the
+ * result equals qgemm_w4a4's bit for bit.
+ *   a   [M, 3K/4] activation codes in QL_LAYOUT_FP6 (rotate_quantize_act or
+ *       rmsnorm_rotate_quantize_act with layout QL_LAYOUT_FP6), dense rows
+ *   w   [N, 3K/4] weight codes in QL_LAYOUT_FP6 (pack_weight_fp6), dense rows
+ *   sa, a_scale_mode, sw, w_scale_mode   TENSOR | ROW scales, as qgemm_w4a4
+ *   bias, epilogue, out, ldo             as qgemm_w4a4 (BF16 | F32 | I32 |
+ *       SIGMOID); QL_EPI_I32 returns the exact sum of code products
+ * K must also be < 342392 (else QL_ERR_SHAPE). */
+int qgemm_w4a4_fp6(const uint8_t* a, const float* sa, int a_scale_mode,
+                   const uint8_t* w, const float* sw, int w_scale_mode,
+                   int64_t M, int64_t N, int64_t K,
+                   const uint16_t* bias, int epilogue, void* out, int64_t ldo,
+                   void* stream);
 
 /* W8A8 GEMM + dequant epilogue for the protected ff.down projections (model
  * card "Krea 2 Turbo OrbitQuant W4A4", sections "Fused transformer" and

@@ -9,9 +9,11 @@ from ._lib import (  # noqa: F401
     QLinearError,
     device_supported,
     lib,
+    pack_weight_fp6,
     pack_weight_int4,
     qgemm_grouped,
     qgemm_w4a4,
+    qgemm_w4a4_fp6,
     qgemm_w4a4_lowrank,
     qgemm_w8a8,
     rmsnorm_rotate_quantize_act,

@@ -30,6 +30,7 @@ QL_SCALE_ROW = 1
 QL_SCALE_GROUP64 = 2
 QL_LAYOUT_I8 = 0
 QL_LAYOUT_PACKED = 1
+QL_LAYOUT_FP6 = 2
 QL_EPI_BF16 = 0
 QL_EPI_SWIGLU = 1
 QL_EPI_GATED_RESIDUAL = 2
@@ -39,7 +40,7 @@ QL_EPI_SIGMOID = 5
 QL_MAX_SEGMENTS = 8
 
 SCALE_MODES = {"tensor": QL_SCALE_TENSOR, "row": QL_SCALE_ROW, "group64": QL_SCALE_GROUP64}
-LAYOUTS = {"i8": QL_LAYOUT_I8, "packed": QL_LAYOUT_PACKED}
+LAYOUTS = {"i8": QL_LAYOUT_I8, "packed": QL_LAYOUT_PACKED, "fp6": QL_LAYOUT_FP6}
 EPILOGUES = {"bf16": QL_EPI_BF16, "swiglu": QL_EPI_SWIGLU, "gated_residual": QL_EPI_GATED_RESIDUAL,
              "f32": QL_EPI_F32, "i32": QL_EPI_I32, "sigmoid": QL_EPI_SIGMOID}
 
@@ -61,7 +62,9 @@ _SIGNATURES = {
     "rmsnorm_rotate_quantize_act": (_i, [_p, _i64, _i64, _i64, _p, _p, _p, ctypes.c_float, _i, _i, _i, _i,
                                          _p, _p, _p]),
     "pack_weight_int4": (_i, [_p, _i64, _i64, _i64, _i, _i, _p, _p, _p]),
+    "pack_weight_fp6": (_i, [_p, _i64, _i64, _i64, _i, _i, _p, _p, _p]),
     "qgemm_w4a4": (_i, [_p, _p, _i, _i, _p, _p, _i, _i64, _i64, _i64, _p, _i, _p, _i64, _p]),
+    "qgemm_w4a4_fp6": (_i, [_p, _p, _i, _p, _p, _i, _i64, _i64, _i64, _p, _i, _p, _i64, _p]),
     "qgemm_w8a8": (_i, [_p, _p, _i, _p, _p, _i, _i64, _i64, _i64, _p, _p, _p, _i, _p, _i64, _p]),
     "qgemm_w4a4_lowrank": (_i, [_p, _p, _i, _i, _p, _p, _i, _p, _p, _i, _i64, _i64, _i64, _p, _i, _p,
                                 _i64, _p]),
@@ -128,6 +131,14 @@ def _lay(l):
     return LAYOUTS[l] if isinstance(l, str) else int(l)
 
 
+def _codes(R, K, lay, device):
+    if lay == QL_LAYOUT_PACKED:
+        return torch.empty((R, K // 2), dtype=torch.uint8, device=device)
+    if lay == QL_LAYOUT_FP6:
+        return torch.empty((R, K // 4 * 3), dtype=torch.uint8, device=device)
+    return torch.empty((R, K), dtype=torch.int8, device=device)
+
+
 def _scale_shape(R, K, mode):
     return {QL_SCALE_TENSOR: (1,), QL_SCALE_ROW: (R,), QL_SCALE_GROUP64: (R, K // 64)}[mode]
 
@@ -142,8 +153,7 @@ def rotate_quantize_act(x, bits=4, scale_mode="row", layout="i8", rotate=True, c
     mode = _mode(scale_mode)
     lay = _lay(layout)
     if codes is None:
-        codes = torch.empty((M, K // 2) if lay == QL_LAYOUT_PACKED else (M, K),
-                            dtype=torch.uint8 if lay == QL_LAYOUT_PACKED else torch.int8, device=x.device)
+        codes = _codes(M, K, lay, x.device)
     if scales is None:
         scales = torch.empty(_scale_shape(M, K, mode), dtype=torch.float32, device=x.device)
     rank = 0
@@ -170,8 +180,7 @@ def rmsnorm_rotate_quantize_act(x, gamma=None, mod_scale=None, mod_shift=None, e
     mode = _mode(scale_mode)
     lay = _lay(layout)
     if codes is None:
-        codes = torch.empty((M, K // 2) if lay == QL_LAYOUT_PACKED else (M, K),
-                            dtype=torch.uint8 if lay == QL_LAYOUT_PACKED else torch.int8, device=x.device)
+        codes = _codes(M, K, lay, x.device)
     if scales is None:
         scales = torch.empty(_scale_shape(M, K, mode), dtype=torch.float32, device=x.device)
     st = lib().rmsnorm_rotate_quantize_act(_ptr(x), M, K, x.stride(0), _ptr(gamma), _ptr(mod_scale),
@@ -196,6 +205,21 @@ def pack_weight_int4(w, scale_mode="row", rotate=True, packed=None, scales=None,
     return packed, scales
 
 
+def pack_weight_fp6(w, scale_mode="row", rotate=True, packed=None, scales=None, stream=None):
+    """w: bf16 [N, K].  Returns (uint8 [N, 3K/4] in the FP6 layout, scales)."""
+    assert w.dtype == torch.bfloat16 and w.dim() == 2 and w.stride(1) == 1
+    N, K = w.shape
+    mode = _mode(scale_mode)
+    if packed is None:
+        packed = _codes(N, K, QL_LAYOUT_FP6, w.device)
+    if scales is None:
+        scales = torch.empty(_scale_shape(N, K, mode), dtype=torch.float32, device=w.device)
+    st = lib().pack_weight_fp6(_ptr(w), N, K, w.stride(0), mode, int(bool(rotate)), _ptr(packed),
+                               _ptr(scales), _stream(stream))
+    _check("pack_weight_fp6", st)
+    return packed, scales
+
+
 def _out(out, M, cols, epi, device):
     if out is not None:
         return out
@@ -214,6 +238,19 @@ def qgemm_w4a4(a, sa, w, sw, K, a_scale_mode="row", w_scale_mode="row", a_layout
                           _mode(w_scale_mode), M, N, K, _ptr(bias), epi, _ptr(out), out.stride(0),
                           _stream(stream))
     _check("qgemm_w4a4", st)
+    return out
+
+
+def qgemm_w4a4_fp6(a, sa, w, sw, K, a_scale_mode="row", w_scale_mode="row", bias=None, epilogue="bf16",
+                   out=None, stream=None):
+    """a: codes [M, 3K/4], w: codes [N, 3K/4], both in the FP6 layout."""
+    M = a.shape[0]
+    N = w.shape[0]
+    epi = _epi(epilogue)
+    out = _out(out, M, N, epi, a.device)
+    st = lib().qgemm_w4a4_fp6(_ptr(a), _ptr(sa), _mode(a_scale_mode), _ptr(w), _ptr(sw), _mode(w_scale_mode),
+                              M, N, K, _ptr(bias), epi, _ptr(out), out.stride(0), _stream(stream))
+    _check("qgemm_w4a4_fp6", st)
     return out
 
 

@@ -51,6 +51,8 @@
 //  * workgroup ids are remapped so the tiles one XCD runs form a compact
 //    block of the tile grid (shared A / W panels hit that XCD's L2).
 
+#include <type_traits>
+
 #include "ql_internal.h"
 
 namespace ql {
@@ -152,19 +154,22 @@ struct PArgs {
   int64_t half_n;  // SwiGLU: F = N / 2
 };
 
-template <int BM_, int BN_, int WGM_, int WGN_, bool AP_, bool WP_, bool GROUP_ = false>
+// F6: both operands in the FP6 e2m3 layout (96 bytes per row per stage),
+// multiplied on the FP6 matrix instruction with fp32 accumulation.
+template <int BM_, int BN_, int WGM_, int WGN_, bool AP_, bool WP_, bool GROUP_ = false, bool F6_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int WGM = WGM_, WGN = WGN_;   // wave grid
   static constexpr int NW = WGM * WGN;           // waves per workgroup
   static constexpr int NT = 64 * NW;
-  static constexpr bool AP = AP_, WP = WP_, GROUP = GROUP_;
+  static constexpr bool AP = AP_, WP = WP_, GROUP = GROUP_, F6 = F6_;
   static constexpr int WM = BM / WGM;       // wave tile rows
   static constexpr int WN = BN / WGN;       // wave tile cols
   static constexpr int FI = WM / 16;
   static constexpr int FJ = WN / 16;
-  static constexpr int ARB = AP ? BK / 2 : BK;  // bytes per A row per stage
-  static constexpr int WRB = WP ? BK / 2 : BK;
+  static constexpr int ARB = F6 ? BK * 3 / 4 : (AP ? BK / 2 : BK);  // bytes per A row per stage
+  static constexpr int WRB = F6 ? BK * 3 / 4 : (WP ? BK / 2 : BK);
+  static_assert(!F6 || (!GROUP && AP && WP), "FP6 operands: both sides, tensor / row scales");
   static constexpr int SA = BM * ARB;
   static constexpr int SW = BN * WRB;
   // two groups of fp32 scales, padded so every wave issues the same number
@@ -187,6 +192,16 @@ struct Cfg {
   static_assert((NSTAGE - 2) * NDMA < 64, "vmcnt range");
   static_assert(!GROUP || FI % 4 == 0, "group scales are read 4 rows at a time");
 };
+
+template <bool F>
+struct AccOf { typedef v4i type; };
+template <>
+struct AccOf<true> { typedef v4f type; };
+
+// FP6 stage rows: 6 chunks of 16 bytes; chunk c of row r lives at
+// c ^ ((r >> 3) & 1), so rows r and r + 8 of a fragment read (16
+// consecutive rows at one chunk index) use different 16-byte bank groups.
+__device__ __forceinline__ int swz6(int r, int c) { return c ^ ((r >> 3) & 1); }
 
 // Chunk position inside an LDS row of RB bytes: chunk c of row r lives at
 // c ^ f(r).  A fragment read (ds_read_b128) has 16 lanes on 16 consecutive
@@ -259,8 +274,8 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   const int64_t m0 = (int64_t)tile_m * C::BM;
   const int64_t n0 = (int64_t)tile_n * (SWIG ? C::BN / 2 : C::BN);
 
-  const int64_t lda = C::AP ? p.K / 2 : p.K;
-  const int64_t ldw = C::WP ? p.K / 2 : p.K;
+  const int64_t lda = C::F6 ? p.K / 4 * 3 : (C::AP ? p.K / 2 : p.K);
+  const int64_t ldw = C::F6 ? p.K / 4 * 3 : (C::WP ? p.K / 2 : p.K);
   const int KT = (int)(p.K / BK);
 
   // ---- global -> LDS loads -------------------------------------------------
@@ -285,16 +300,21 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
 #pragma unroll
   for (int t = 0; t < C::A_PER_WAVE; ++t) {
     constexpr int CPR = C::ARB / 16;
-    const int rl = (wave + C::NW * t) * (1024 / C::ARB) + lane / CPR;
+    // FP6 rows (6 chunks) straddle the 1 KB loads: lane chunk -> row, chunk
+    const int ci = (wave + C::NW * t) * 64 + lane;
+    const int rl = C::F6 ? ci / CPR : (wave + C::NW * t) * (1024 / C::ARB) + lane / CPR;
     const int64_t gr = m0 + rl > p.M - 1 ? p.M - 1 : m0 + rl;
-    a_vo[t] = (uint32_t)((gr - m0) * lda + (swz<C::ARB, C::GROUP>(rl, lane % CPR) << 4));
+    const int ch = C::F6 ? swz6(rl, ci % CPR) : swz<C::ARB, C::GROUP>(rl, lane % CPR);
+    a_vo[t] = (uint32_t)((gr - m0) * lda + (ch << 4));
   }
   uint32_t w_vo[C::W_HI];
 #pragma unroll
   for (int tw = 0; tw < C::W_HI; ++tw) {
     constexpr int CPR = C::WRB / 16;
-    const int rl = (wave + C::NW * tw) * (1024 / C::WRB) + lane / CPR;
-    w_vo[tw] = (uint32_t)(w_row_of<C, SWIG>(p, n0, rl) * ldw + (swz<C::WRB, C::GROUP>(rl, lane % CPR) << 4));
+    const int ci = (wave + C::NW * tw) * 64 + lane;
+    const int rl = C::F6 ? ci / CPR : (wave + C::NW * tw) * (1024 / C::WRB) + lane / CPR;
+    const int ch = C::F6 ? swz6(rl, ci % CPR) : swz<C::WRB, C::GROUP>(rl, lane % CPR);
+    w_vo[tw] = (uint32_t)(w_row_of<C, SWIG>(p, n0, rl) * ldw + (ch << 4));
   }
   uint32_t s_vo[C::GROUP ? C::S_PER_WAVE : 1];
 #pragma unroll
@@ -335,16 +355,18 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
     }
   };
 
-  // int32 accumulators (tensor / row scales) or fp32 sums of rescaled
-  // group partials (group-64 scales).
-  v4i acc[C::GROUP ? 1 : C::FJ][C::GROUP ? 1 : C::FI];
+  // int32 accumulators (tensor / row scales), fp32 sums of rescaled group
+  // partials (group-64 scales), or fp32 sums of FP6 code products (exact
+  // integers below 2^24).
+  typedef typename AccOf<C::F6>::type acc_t;
+  acc_t acc[C::GROUP ? 1 : C::FJ][C::GROUP ? 1 : C::FI];
   v4f yf[C::GROUP ? C::FJ : 1][C::GROUP ? C::FI : 1];
 #pragma unroll
   for (int j = 0; j < C::FJ; ++j)
 #pragma unroll
     for (int i = 0; i < C::FI; ++i) {
       if (C::GROUP) yf[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
-      else acc[j][i] = v4i{0, 0, 0, 0};
+      else acc[j][i] = acc_t{0, 0, 0, 0};
     }
 
   // lane-constant LDS offsets: fragment rows differ by multiples of 16, so
@@ -383,6 +405,13 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
     w_off = w_row * 128 + (swz<128, GK>(w_row, 2 * lg) << 4);
     w_off1 = w_row * 128 + (swz<128, GK>(w_row, 2 * lg + 1) << 4);
   }
+  // FP6: sub-block lg of a 96-byte row, low 16 bytes at chunk lg, high 8
+  // bytes in chunk 4 + lg / 2 (half lg % 2); fragment rows differ by
+  // multiples of 16, which leaves the swizzle bit (row bit 3) unchanged.
+  const int a6_hi = a_row * 96 + (swz6(a_row, lg) << 4);
+  const int a6_lo = a_row * 96 + (swz6(a_row, 4 + (lg >> 1)) << 4) + 8 * (lg & 1);
+  const int w6_hi = w_row * 96 + (swz6(w_row, lg) << 4);
+  const int w6_lo = w_row * 96 + (swz6(w_row, 4 + (lg >> 1)) << 4) + 8 * (lg & 1);
   // group scales: byte offsets inside the stage's scale block
   const int sa_off = (wm * C::WM + l16 * C::FI) * 4;
   const int sw_off = (2 * C::BM + wn * C::WN + 4 * lg) * 4;
@@ -430,7 +459,7 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   // flight (both waves of a SIMD leave the barrier together and would
   // otherwise wait on them at the same time).  Its operands (the stage's
   // second-half W fragments and last A fragment) stay in registers.
-  constexpr bool DEFER = !C::GROUP && C::WP;  // int8 W: not enough registers
+  constexpr bool DEFER = !C::GROUP && C::WP && !C::F6;  // int8 W: not enough registers
   v4i bw1[C::FJ];
   v4i af_def = v4i{0, 0, 0, 0};
   for (int kb = 0; kb < KT; kb += NS) {
@@ -454,142 +483,189 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
     stage_prio(0);
     const bool dma = kt + NS - 1 < KT;
 
-    const uint8_t* As = cur;
-    const uint8_t* Ws = As + C::SA;
-    const uint8_t* Ss = Ws + C::SW;
-    // W fragments: packed -> one b128 per fragment carries both halves (kk);
-    // int8 -> one b128 per fragment and half.
-    uint4 wraw[GK ? 1 : C::FJ];
-    uint4 wraw1[(C::WP || GK) ? 1 : C::FJ];
-    v4i bw0[C::FJ];
-    if (GK) {
+    if constexpr (C::F6) {
+      // FP6 stage: one 16x16x128 instruction per fragment pair covers the
+      // stage's 128 channels.  W fragments are read whole; A fragments
+      // stream through a window read PF ahead; the next stage's loads go
+      // one per A fragment.
+      const uint8_t* As = cur;
+      const uint8_t* Ws = As + C::SA;
+      v8i wf[C::FJ];
 #pragma unroll
       for (int j = 0; j < C::FJ; ++j) {
-        const uint2 h0 = *reinterpret_cast<const uint2*>(Ws + w_off + j * 16 * C::WRB);
-        const uint2 h1 = *reinterpret_cast<const uint2*>(Ws + w_off1 + j * 16 * C::WRB);
-        bw0[j] = unpack_lo(h0.x, h0.y);
-        bw1[j] = unpack_lo(h1.x, h1.y);
+        const uint4 h = *reinterpret_cast<const uint4*>(Ws + w6_hi + j * 16 * C::WRB);
+        const uint2 l = *reinterpret_cast<const uint2*>(Ws + w6_lo + j * 16 * C::WRB);
+        wf[j] = v8i{(int)h.x, (int)h.y, (int)h.z, (int)h.w, (int)l.x, (int)l.y, 0, 0};  // FP6 reads 6 dwords
+      }
+      constexpr int PF = 2;
+      auto read_a = [&](int i) {
+        const uint4 h = *reinterpret_cast<const uint4*>(As + a6_hi + i * 16 * C::ARB);
+        const uint2 l = *reinterpret_cast<const uint2*>(As + a6_lo + i * 16 * C::ARB);
+        return v8i{(int)h.x, (int)h.y, (int)h.z, (int)h.w, (int)l.x, (int)l.y, 0, 0};
+      };
+      v8i abuf[PF + 1];
+#pragma unroll
+      for (int q = 0; q < PF; ++q) abuf[q] = read_a(q);
+#pragma unroll
+      for (int i = 0; i < C::FI; ++i) {
+        if (i > 0 && (4 * i) % C::FI < 4) stage_prio((4 * i) / C::FI);
+        if (i + PF < C::FI) abuf[(i + PF) % (PF + 1)] = read_a(i + PF);
+        if (dma && i < NDMA) issue_one(nxt, kt + NS - 1, i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < C::FJ; ++j) {
+          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], abuf[i % (PF + 1)], acc[j][i],
+                                                                      2, 2, 0, 127, 0, 127);
+          // pin the group here: otherwise the compiler sinks every MFMA
+          // below the loads' branches and must hold all A fragments at once
+          asm volatile("" : "+v"(acc[j][i]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (dma) {
+#pragma unroll
+        for (int t = C::FI; t < NDMA; ++t) issue_one(nxt, kt + NS - 1, t);
       }
     } else {
+      const uint8_t* As = cur;
+      const uint8_t* Ws = As + C::SA;
+      const uint8_t* Ss = Ws + C::SW;
+      // W fragments: packed -> one b128 per fragment carries both halves (kk);
+      // int8 -> one b128 per fragment and half.
+      uint4 wraw[GK ? 1 : C::FJ];
+      uint4 wraw1[(C::WP || GK) ? 1 : C::FJ];
+      v4i bw0[C::FJ];
+      if (GK) {
 #pragma unroll
-      for (int j = 0; j < C::FJ; ++j) {
-        wraw[j] = *reinterpret_cast<const uint4*>(Ws + w_off + j * 16 * C::WRB);
-        if (!C::WP) wraw1[j] = *reinterpret_cast<const uint4*>(Ws + w_off1 + j * 16 * C::WRB);
-      }
-    }
-    // A fragments: int8 -> streamed through a small window read PF ahead;
-    // packed -> one b128 per fragment carries both halves.
-    constexpr int PF = 2;
-    constexpr int NQ = 2 * C::FI;
-    v4i abuf[PF + 1];
-    uint4 araw[(C::AP && !GK) ? C::FI : 1];
-    if (C::AP) {
-      if (!GK) {
-#pragma unroll
-        for (int i = 0; i < C::FI; ++i)
-          araw[i] = *reinterpret_cast<const uint4*>(As + a_off[0] + i * 16 * C::ARB);
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < PF; ++q)
-        abuf[q] = *reinterpret_cast<const v4i*>(As + a_off[q / C::FI] + (q % C::FI) * 16 * C::ARB);
-    }
-    if (DEFER && kt > 0) {
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < C::FJ; ++j)
-        acc[j][C::FI - 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bw1[j], af_def, acc[j][C::FI - 1], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (!GK) {
-#pragma unroll
-      for (int j = 0; j < C::FJ; ++j)
-        bw0[j] = C::WP ? unpack_lo(wraw[j].x, wraw[j].y)
-                       : v4i{(int)wraw[j].x, (int)wraw[j].y, (int)wraw[j].z, (int)wraw[j].w};
-    }
-    v4f sav[C::GROUP ? C::FI / 4 : 1];
-    v4f swv[C::GROUP ? C::FJ : 1];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int kk = q / C::FI, i = q % C::FI;
-      if (q > 0 && (4 * q) % NQ < 4) stage_prio((4 * q) / NQ);
-      v4i af;
-      if (C::AP && GK) {
-        const uint2 h = *reinterpret_cast<const uint2*>(As + a_off[kk] + i * 16 * C::ARB);
-        af = unpack_lo(h.x, h.y);
-      } else if (C::AP) {
-        af = kk == 0 ? unpack_lo(araw[i].x, araw[i].y) : unpack_lo(araw[i].z, araw[i].w);
-      } else {
-        if (q + PF < NQ)
-          abuf[(q + PF) % (PF + 1)] = *reinterpret_cast<const v4i*>(
-              As + a_off[(q + PF) / C::FI] + ((q + PF) % C::FI) * 16 * C::ARB);
-        af = abuf[q % (PF + 1)];
-      }
-      if (dma && (q % 2) == 0 && q / 2 < NDMA) issue_one(nxt, kt + NS - 1, q / 2);
-      // second-half W fragments, spread over the first half's MFMA groups
-      if (!GK && kk == 0 && i < C::FJ)
-        bw1[i] = C::WP ? unpack_lo(wraw[i].z, wraw[i].w)
-                       : v4i{(int)wraw1[i].x, (int)wraw1[i].y, (int)wraw1[i].z, (int)wraw1[i].w};
-      if (!GK && kk == 0 && i == C::FI - 1) {
-#pragma unroll
-        for (int j = C::FI; j < C::FJ; ++j)
-          bw1[j] = C::WP ? unpack_lo(wraw[j].z, wraw[j].w)
-                         : v4i{(int)wraw1[j].x, (int)wraw1[j].y, (int)wraw1[j].z, (int)wraw1[j].w};
-      }
-      if (!C::GROUP) {
-        if (DEFER && q == NQ - 1) {
-          af_def = af;  // issued after the next barrier (or after the loop)
-        } else {
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int j = 0; j < C::FJ; ++j)
-            acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kk == 0 ? bw0[j] : bw1[j], af, acc[j][i], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < C::FJ; ++j) {
+          const uint2 h0 = *reinterpret_cast<const uint2*>(Ws + w_off + j * 16 * C::WRB);
+          const uint2 h1 = *reinterpret_cast<const uint2*>(Ws + w_off1 + j * 16 * C::WRB);
+          bw0[j] = unpack_lo(h0.x, h0.y);
+          bw1[j] = unpack_lo(h1.x, h1.y);
         }
       } else {
-        if (i == 0) {
-          // scales of group kk: s_a of the lane's FI rows, s_w of its 4
-          // columns in each fragment
 #pragma unroll
-          for (int f = 0; f < C::FI / 4; ++f)
-            sav[f] = *reinterpret_cast<const v4f*>(Ss + sa_off + (kk * C::BM + 4 * f) * 4);
-#pragma unroll
-          for (int j = 0; j < C::FJ; ++j)
-            swv[j] = *reinterpret_cast<const v4f*>(Ss + sw_off + (kk * C::BN + j * 16) * 4);
+        for (int j = 0; j < C::FJ; ++j) {
+          wraw[j] = *reinterpret_cast<const uint4*>(Ws + w_off + j * 16 * C::WRB);
+          if (!C::WP) wraw1[j] = *reinterpret_cast<const uint4*>(Ws + w_off1 + j * 16 * C::WRB);
         }
-        const float s_i = sav[i / 4][i % 4];
-        v4i part[C::FJ];
+      }
+      // A fragments: int8 -> streamed through a small window read PF ahead;
+      // packed -> one b128 per fragment carries both halves.
+      constexpr int PF = 2;
+      constexpr int NQ = 2 * C::FI;
+      v4i abuf[PF + 1];
+      uint4 araw[(C::AP && !GK) ? C::FI : 1];
+      if (C::AP) {
+        if (!GK) {
+#pragma unroll
+          for (int i = 0; i < C::FI; ++i)
+            araw[i] = *reinterpret_cast<const uint4*>(As + a_off[0] + i * 16 * C::ARB);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < PF; ++q)
+          abuf[q] = *reinterpret_cast<const v4i*>(As + a_off[q / C::FI] + (q % C::FI) * 16 * C::ARB);
+      }
+      if (DEFER && kt > 0) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < C::FJ; ++j)
-          part[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kk == 0 ? bw0[j] : bw1[j], af, v4i{0, 0, 0, 0},
-                                                          0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < C::FJ; ++j) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            yf[j][i][r] = __builtin_fmaf((float)part[j][r], s_i * swv[j][r], yf[j][i][r]);
-          // keep the rescale next to its MFMAs: without this the compiler
-          // sinks every rescale below all of the stage's MFMAs and must hold
-          // all their partials at once
-          asm volatile("" : "+v"(yf[j][i]));
-        }
+          acc[j][C::FI - 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bw1[j], af_def, acc[j][C::FI - 1], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    // any loads not yet issued (only if NDMA > NQ / 2)
-    if (dma) {
+      if (!GK) {
 #pragma unroll
-      for (int t = NQ / 2; t < NDMA; ++t) issue_one(nxt, kt + NS - 1, t);
+        for (int j = 0; j < C::FJ; ++j)
+          bw0[j] = C::WP ? unpack_lo(wraw[j].x, wraw[j].y)
+                         : v4i{(int)wraw[j].x, (int)wraw[j].y, (int)wraw[j].z, (int)wraw[j].w};
+      }
+      v4f sav[C::GROUP ? C::FI / 4 : 1];
+      v4f swv[C::GROUP ? C::FJ : 1];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int kk = q / C::FI, i = q % C::FI;
+        if (q > 0 && (4 * q) % NQ < 4) stage_prio((4 * q) / NQ);
+        v4i af;
+        if (C::AP && GK) {
+          const uint2 h = *reinterpret_cast<const uint2*>(As + a_off[kk] + i * 16 * C::ARB);
+          af = unpack_lo(h.x, h.y);
+        } else if (C::AP) {
+          af = kk == 0 ? unpack_lo(araw[i].x, araw[i].y) : unpack_lo(araw[i].z, araw[i].w);
+        } else {
+          if (q + PF < NQ)
+            abuf[(q + PF) % (PF + 1)] = *reinterpret_cast<const v4i*>(
+                As + a_off[(q + PF) / C::FI] + ((q + PF) % C::FI) * 16 * C::ARB);
+          af = abuf[q % (PF + 1)];
+        }
+        if (dma && (q % 2) == 0 && q / 2 < NDMA) issue_one(nxt, kt + NS - 1, q / 2);
+        // second-half W fragments, spread over the first half's MFMA groups
+        if (!GK && kk == 0 && i < C::FJ)
+          bw1[i] = C::WP ? unpack_lo(wraw[i].z, wraw[i].w)
+                         : v4i{(int)wraw1[i].x, (int)wraw1[i].y, (int)wraw1[i].z, (int)wraw1[i].w};
+        if (!GK && kk == 0 && i == C::FI - 1) {
+#pragma unroll
+          for (int j = C::FI; j < C::FJ; ++j)
+            bw1[j] = C::WP ? unpack_lo(wraw[j].z, wraw[j].w)
+                           : v4i{(int)wraw1[j].x, (int)wraw1[j].y, (int)wraw1[j].z, (int)wraw1[j].w};
+        }
+        if (!C::GROUP) {
+          if (DEFER && q == NQ - 1) {
+            af_def = af;  // issued after the next barrier (or after the loop)
+          } else {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < C::FJ; ++j)
+              acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kk == 0 ? bw0[j] : bw1[j], af, acc[j][i], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+          if (i == 0) {
+            // scales of group kk: s_a of the lane's FI rows, s_w of its 4
+            // columns in each fragment
+#pragma unroll
+            for (int f = 0; f < C::FI / 4; ++f)
+              sav[f] = *reinterpret_cast<const v4f*>(Ss + sa_off + (kk * C::BM + 4 * f) * 4);
+#pragma unroll
+            for (int j = 0; j < C::FJ; ++j)
+              swv[j] = *reinterpret_cast<const v4f*>(Ss + sw_off + (kk * C::BN + j * 16) * 4);
+          }
+          const float s_i = sav[i / 4][i % 4];
+          v4i part[C::FJ];
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = 0; j < C::FJ; ++j)
+            part[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kk == 0 ? bw0[j] : bw1[j], af, v4i{0, 0, 0, 0},
+                                                            0, 0, 0);
+#pragma unroll
+          for (int j = 0; j < C::FJ; ++j) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              yf[j][i][r] = __builtin_fmaf((float)part[j][r], s_i * swv[j][r], yf[j][i][r]);
+            // keep the rescale next to its MFMAs: without this the compiler
+            // sinks every rescale below all of the stage's MFMAs and must hold
+            // all their partials at once
+            asm volatile("" : "+v"(yf[j][i]));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // any loads not yet issued (only if NDMA > NQ / 2)
+      if (dma) {
+#pragma unroll
+        for (int t = NQ / 2; t < NDMA; ++t) issue_one(nxt, kt + NS - 1, t);
+      }
     }
   }
   }
   stage_prio(3);  // back to the lowest priority for the epilogue
 
-  if (DEFER && KT > 0) {
+  if constexpr (DEFER) {
+    if (KT > 0) {
 #pragma unroll
-    for (int j = 0; j < C::FJ; ++j)
-      acc[j][C::FI - 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bw1[j], af_def, acc[j][C::FI - 1], 0, 0, 0);
+      for (int j = 0; j < C::FJ; ++j)
+        acc[j][C::FI - 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bw1[j], af_def, acc[j][C::FI - 1], 0, 0, 0);
+    }
   }
 
   // ---- staged epilogue (plain bf16, sigmoid gate, gated residual) ----------
@@ -797,12 +873,12 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
       }
       if (m >= p.M) continue;
       if (EPI == EPI_I32) {
-        const v4i a4 = acc[C::GROUP ? 0 : j][C::GROUP ? 0 : i];
+        const acc_t a4 = acc[C::GROUP ? 0 : j][C::GROUP ? 0 : i];  // FP6: exact integers in fp32
         int4 o;
-        o.x = a4[0] >> p.shift;
-        o.y = a4[1] >> p.shift;
-        o.z = a4[2] >> p.shift;
-        o.w = a4[3] >> p.shift;
+        o.x = (int)a4[0] >> p.shift;
+        o.y = (int)a4[1] >> p.shift;
+        o.z = (int)a4[2] >> p.shift;
+        o.w = (int)a4[3] >> p.shift;
         *reinterpret_cast<int4*>(static_cast<int32_t*>(p.out) + m * p.ldo + n) = o;
         continue;
       }
@@ -1047,6 +1123,11 @@ int launch_qgemm(const GemmArgs& g, hipStream_t s) {
   p.shift = 4 * npacked;
   const bool group = g.a_mode == 2;
   hipError_t e;
+  if (g.fp6) {
+    // the FP6 instruction sums the code products themselves (no nibble shift)
+    p.post = 1.0f;
+    p.shift = 0;
+  }
   if (group || g.rank > 0 || g.epilogue == EPI_SWIGLU) {
     // INT4 weights only (the ABI routes nothing else here); 256 x 256
     // tiles keep the gate/up fragment pairs and the scale block in LDS.
@@ -1066,7 +1147,10 @@ int launch_qgemm(const GemmArgs& g, hipStream_t s) {
     return ((tiles + 255) / 256) * 256 * bn;
   };
   const bool wide = cost(320) <= cost(256);
-  if (g.w_packed) {
+  if (g.fp6) {
+    e = wide ? launch_plain<Cfg<256, 320, 2, 4, true, true, false, true>>(p, g.epilogue, s)
+             : launch_plain<Cfg<256, 256, 2, 4, true, true, false, true>>(p, g.epilogue, s);
+  } else if (g.w_packed) {
     if (g.a_packed)
       e = wide ? launch_plain<Cfg<256, 320, 2, 4, true, true>>(p, g.epilogue, s)
                : launch_plain<Cfg<256, 256, 2, 4, true, true>>(p, g.epilogue, s);

@@ -9,6 +9,7 @@ namespace ql {
 
 // ---------------------------------------------------------------- types ----
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
@@ -53,7 +54,7 @@ struct RqArgs {
   int64_t ldx;
   int bits;        // 4 | 8
   int mode;        // 0 tensor, 1 row, 2 group64
-  int packed;      // 1: two int4 codes per byte
+  int packed;      // 0: int8 codes, 1: two int4 codes per byte, 2: FP6 e2m3 layout
   int rotate;      // 1: apply H per 256-group
   void* codes;
   float* scales;
@@ -77,6 +78,7 @@ struct GemmArgs {
   const float* sw;
   int64_t M, N, K;
   int a_packed, w_packed;
+  int fp6;              // 1: both operands in the FP6 e2m3 layout [rows, 3K/4]
   int a_mode, w_mode;   // 0 tensor, 1 row, 2 group64
   const uint16_t* bias;
   const uint16_t* residual;

@@ -64,8 +64,8 @@ static int validate_rq(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int
                        const uint16_t* l1, int rank, const uint16_t* lr) {
   if (bits != 4 && bits != 8) return QL_ERR_UNSUPPORTED;
   if (!valid_mode(scale_mode)) return QL_ERR_UNSUPPORTED;
-  if (layout != QL_LAYOUT_I8 && layout != QL_LAYOUT_PACKED) return QL_ERR_UNSUPPORTED;
-  if (layout == QL_LAYOUT_PACKED && bits != 4) return QL_ERR_UNSUPPORTED;
+  if (layout != QL_LAYOUT_I8 && layout != QL_LAYOUT_PACKED && layout != QL_LAYOUT_FP6) return QL_ERR_UNSUPPORTED;
+  if (layout != QL_LAYOUT_I8 && bits != 4) return QL_ERR_UNSUPPORTED;
   if (rotate != 0 && rotate != 1) return QL_ERR_UNSUPPORTED;
   if (M < 0 || K <= 0 || K % 256 != 0 || K > 32768) return QL_ERR_SHAPE;
   if (ldx < K || ldx % 8 != 0) return QL_ERR_SHAPE;
@@ -88,7 +88,7 @@ int rotate_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, in
   if ((st = check_current_device()) != QL_OK) return st;
   if (M == 0) return QL_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  ql::RqArgs a{x, M, K, ldx, bits, scale_mode, layout == QL_LAYOUT_PACKED ? 1 : 0, rotate, codes, scales};
+  ql::RqArgs a{x, M, K, ldx, bits, scale_mode, layout, rotate, codes, scales};
   st = ql::launch_rotate_quantize(a, s);
   if (st != QL_OK) return QL_ERR_LAUNCH;
   if (l1) {
@@ -110,7 +110,7 @@ int rmsnorm_rotate_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t
   if (!al16(gamma) || !al16(mod_scale) || !al16(mod_shift)) return QL_ERR_ALIGN;
   if ((st = check_current_device()) != QL_OK) return st;
   if (M == 0) return QL_OK;
-  ql::RqArgs a{x, M, K, ldx, bits, scale_mode, layout == QL_LAYOUT_PACKED ? 1 : 0, rotate, codes, scales};
+  ql::RqArgs a{x, M, K, ldx, bits, scale_mode, layout, rotate, codes, scales};
   a.norm = 1;
   a.gamma = gamma;
   a.mscale = mod_scale;
@@ -124,6 +124,14 @@ int pack_weight_int4(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, int s
   if (N <= 0) return QL_ERR_SHAPE;
   return rotate_quantize_act(w, N, K, ldw, 4, scale_mode, QL_LAYOUT_PACKED, rotate, packed, scales,
                              nullptr, 0, nullptr, stream);
+}
+
+int pack_weight_fp6(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, int scale_mode, int rotate,
+                    uint8_t* packed, float* scales, void* stream) {
+  if (N <= 0) return QL_ERR_SHAPE;
+  if (scale_mode != QL_SCALE_TENSOR && scale_mode != QL_SCALE_ROW) return QL_ERR_UNSUPPORTED;
+  return rotate_quantize_act(w, N, K, ldw, 4, scale_mode, QL_LAYOUT_FP6, rotate, packed, scales, nullptr, 0,
+                             nullptr, stream);
 }
 
 // Output element size per epilogue (SWIGLU / BF16 / GATED write bf16).
@@ -174,6 +182,37 @@ int qgemm_w4a4(const void* a, const float* sa, int a_scale_mode, int a_layout, c
   g.K = K;
   g.a_packed = a_layout == QL_LAYOUT_PACKED;
   g.w_packed = 1;
+  g.a_mode = a_scale_mode;
+  g.w_mode = w_scale_mode;
+  g.bias = bias;
+  g.epilogue = epilogue;
+  g.out = out;
+  g.ldo = ldo;
+  return ql::launch_qgemm(g, static_cast<hipStream_t>(stream)) == QL_OK ? QL_OK : QL_ERR_LAUNCH;
+}
+
+int qgemm_w4a4_fp6(const uint8_t* a, const float* sa, int a_scale_mode, const uint8_t* w, const float* sw,
+                   int w_scale_mode, int64_t M, int64_t N, int64_t K, const uint16_t* bias, int epilogue,
+                   void* out, int64_t ldo, void* stream) {
+  if ((a_scale_mode != QL_SCALE_TENSOR && a_scale_mode != QL_SCALE_ROW) ||
+      (w_scale_mode != QL_SCALE_TENSOR && w_scale_mode != QL_SCALE_ROW))
+    return QL_ERR_UNSUPPORTED;
+  if (epilogue != QL_EPI_BF16 && epilogue != QL_EPI_F32 && epilogue != QL_EPI_I32 && epilogue != QL_EPI_SIGMOID)
+    return QL_ERR_UNSUPPORTED;
+  int st = validate_gemm_common(a, sa, w, sw, M, N, K, bias, out, ldo, epilogue);
+  if (st != QL_OK) return st;
+  if (49 * K >= (int64_t(1) << 24)) return QL_ERR_SHAPE;  // float32 sums of code products stay exact
+  if ((st = check_current_device()) != QL_OK) return st;
+  if (M == 0) return QL_OK;
+  ql::GemmArgs g{};
+  g.a = a;
+  g.w = w;
+  g.sa = sa;
+  g.sw = sw;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.fp6 = 1;
   g.a_mode = a_scale_mode;
   g.w_mode = w_scale_mode;
   g.bias = bias;

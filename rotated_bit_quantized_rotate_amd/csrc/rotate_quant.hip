@@ -110,10 +110,45 @@ __device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, ui
   return lo | hi;
 }
 
-// Encode 16 codes (channel order, as code_bits) and store them.
-__device__ __forceinline__ void store_codes(void* codes, int64_t off_elems, bool packed,
-                                            const uint32_t (&u)[16]) {
-  if (!packed) {
+// Four int4 codes (bytes of x, two's complement, |c| <= 7) -> their FP6
+// e2m3 bit patterns, one per byte.  |c| indexes the 8 magnitude patterns
+// {0, 8, 16, 20, 24, 26, 28, 30} (1 = 1.0 * 2^0, 2..3 = 1.m * 2^1, 4..7 =
+// 1.m * 2^2 with exponent bias 1) through one byte permute; bit 5 is the sign.
+__device__ __forceinline__ uint32_t fp6_bytes(uint32_t x) {
+  const uint32_t neg = (x >> 7) & 0x01010101u;          // 1 in each negative byte
+  const uint32_t mag = (x ^ (neg * 0xFFu)) + neg;       // per-byte |c| (no carries: |c| <= 7)
+  return __builtin_amdgcn_perm(0x1E1C1A18u, 0x14100800u, mag) | (neg << 5);
+}
+
+// Four 6-bit patterns (one per byte) -> 24 contiguous bits, byte i at bits 6i.
+__device__ __forceinline__ uint32_t fp6_join4(uint32_t p) {
+  return (p & 0x3Fu) | ((p >> 2) & 0xFC0u) | ((p >> 4) & 0x3F000u) | ((p >> 6) & 0xFC0000u);
+}
+
+// Encode 16 codes (channel order, as code_bits) and store them: fmt 0 int8,
+// 1 packed int4, 2 FP6 e2m3 layout (every lane of the 16-lane slot active).
+__device__ __forceinline__ void store_codes(void* codes, int64_t off_elems, int fmt, const uint32_t (&u)[16]) {
+  if (fmt == 2) {
+    // FP6 layout: a row is 96-byte blocks of 128 channels; in a block,
+    // 32-channel sub-block g is the 192-bit value v_g (channel i at bits
+    // 6i), its low 16 bytes at 16 g and its high 8 bytes at 64 + 8 g.  A
+    // lane's 16 channels are bits 0..95 (even lane) or 96..191 (odd lane)
+    // of one v_g, so the even lane stores the low 16 bytes with the first
+    // dword of its odd neighbour and the odd lane the high 8 bytes.
+    const uint32_t w0 = fp6_join4(fp6_bytes(pack4(u[0], u[1], u[2], u[3])));
+    const uint32_t w1 = fp6_join4(fp6_bytes(pack4(u[4], u[5], u[6], u[7])));
+    const uint32_t w2 = fp6_join4(fp6_bytes(pack4(u[8], u[9], u[10], u[11])));
+    const uint32_t w3 = fp6_join4(fp6_bytes(pack4(u[12], u[13], u[14], u[15])));
+    const uint32_t d0 = w0 | (w1 << 24), d1 = (w1 >> 8) | (w2 << 16), d2 = (w2 >> 16) | (w3 << 8);
+    const uint32_t nd0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)d0, DPP_QUAD_SWAP1, 0xF, 0xF, false);
+    const int64_t c = off_elems & 127;                 // channel within the 128-channel block
+    uint8_t* blk = static_cast<uint8_t*>(codes) + (off_elems >> 7) * 96;
+    const int g = (int)(c >> 5);
+    if ((c & 16) == 0) *reinterpret_cast<uint4*>(blk + 16 * g) = make_uint4(d0, d1, d2, nd0);
+    else *reinterpret_cast<uint2*>(blk + 64 + 8 * g) = make_uint2(d1, d2);
+    return;
+  }
+  if (fmt == 0) {
     uint4 w;
     w.x = pack4(u[0], u[1], u[2], u[3]);
     w.y = pack4(u[4], u[5], u[6], u[7]);
@@ -315,7 +350,7 @@ __global__ __launch_bounds__(kThreads) void rq_kernel(RqArgs a, int slots_per_ro
       uint32_t u[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) u[e] = code_bits(v[j][e], inv);
-      store_codes(a.codes, code_row + (int64_t)g * 256 + t * 16, a.packed != 0, u);
+      store_codes(a.codes, code_row + (int64_t)g * 256 + t * 16, a.packed, u);
       if (a.mode == 2) {
         if ((t & 3) == 0)
           a.scales[row * (a.K >> 6) + g * 4 + (t >> 2)] = __fdiv_rn(am, qmax) * post;

@@ -19,8 +19,9 @@ def L():
 
 def test_header_declares_the_entry_points():
     fns = header_functions()
-    for name in ["rotate_quantize_act", "rmsnorm_rotate_quantize_act", "pack_weight_int4", "qgemm_w4a4", "qgemm_w8a8",
-                 "qgemm_w4a4_lowrank", "qgemm_grouped", "ql_status_string", "ql_device_supported"]:
+    for name in ["rotate_quantize_act", "rmsnorm_rotate_quantize_act", "pack_weight_int4", "pack_weight_fp6",
+                 "qgemm_w4a4", "qgemm_w4a4_fp6", "qgemm_w8a8", "qgemm_w4a4_lowrank", "qgemm_grouped",
+                 "ql_status_string", "ql_device_supported"]:
         assert name in fns
 
 
@@ -65,6 +66,8 @@ def test_rotate_quantize_validation(L):
     assert rq(L, bits=5) == -4
     assert rq(L, mode=7) == -4
     assert rq(L, layout=1, bits=8) == -4          # packed layout is int4-only
+    assert rq(L, layout=2, bits=8) == -4          # so is the FP6 layout
+    assert rq(L, layout=3) == -4
     assert rq(L, rotate=2) == -4
     assert rq(L, K=320, ldx=320) == -2            # K % 256
     assert rq(L, K=0, ldx=0) == -2
@@ -208,6 +211,47 @@ def test_qgemm_grouped_validation(L):
     assert grp(L, [{"w_bits": 4}], a8=NULL, sa8=NULL) in (-4, -6)  # unused operand may be NULL
     assert grp(L, [{}, {"w_bits": 8, "epilogue": 5}, {"n": 48, "ldo": 48}]) in (-4, -6)
     assert grp(L, [{}], M=0) in (0, -4, -6)
+
+def g6(L, **kw):
+    a = dict(a=ALIGNED, sa=ALIGNED, am=1, w=ALIGNED, sw=ALIGNED, wm=1, M=4, N=32, K=256, bias=NULL,
+             epi=0, out=ALIGNED, ldo=32)
+    a.update(kw)
+    return L.qgemm_w4a4_fp6(a["a"], a["sa"], a["am"], a["w"], a["sw"], a["wm"], a["M"], a["N"], a["K"],
+                            a["bias"], a["epi"], a["out"], a["ldo"], None)
+
+
+def test_qgemm_w4a4_fp6_validation(L):
+    assert g6(L, am=2) == -4                      # tensor / row scales only
+    assert g6(L, wm=2) == -4
+    assert g6(L, epi=1) == -4                     # no SwiGLU / gated residual here
+    assert g6(L, epi=2) == -4
+    assert g6(L, N=24) == -2
+    assert g6(L, K=384) == -2                     # K % 256
+    assert g6(L, ldo=16) == -2
+    assert g6(L, a=NULL) == -1
+    assert g6(L, w=MISALIGNED) == -3
+    assert g6(L, ldo=36) == -3
+    # float32 sums of code products stay exact only while 49 K < 2^24
+    assert g6(L, K=342528) == -2
+    assert g6(L, K=342272) in (-4, -6)            # largest valid K reaches the device check
+    assert g6(L, M=0) in (0, -4, -6)
+    for epi in (0, 3, 4, 5):
+        assert g6(L, epi=epi) in (-4, -6)
+
+
+def test_pack_weight_fp6_validation(L):
+    def pw(**kw):
+        a = dict(w=ALIGNED, N=16, K=256, ldw=256, mode=1, rot=1, out=ALIGNED, sc=ALIGNED)
+        a.update(kw)
+        return L.pack_weight_fp6(a["w"], a["N"], a["K"], a["ldw"], a["mode"], a["rot"], a["out"], a["sc"], None)
+
+    assert pw(mode=2) == -4                       # group-64 scales do not reach the FP6 GEMM
+    assert pw(N=0) == -2
+    assert pw(K=320, ldw=320) == -2
+    assert pw(out=NULL) == -1
+    assert pw(w=MISALIGNED) == -3
+    assert pw() in (-4, -6)
+
 
 def test_device_supported_without_gpu_is_false(L):
     import torch
