@@ -25,6 +25,11 @@ Sources (web pages; cited by title and section):
   [NunchakuLite] model card "Krea 2 Turbo Nunchaku Lite INT4 r32" -- intro.
   [lab]         research log "lab" -- Studies 1-4.
 
+The offline low-rank split (svdq_split_ref) follows [SVDQ-Comfy], sections on
+reproducible builds, "Activation-aware branch" and "Low-rank refinement, and
+what the objective actually is"; its randomized SVD is Halko, Martinsson and
+Tropp's randomized subspace iteration (2011).
+
 Parity status of each function is pinned by the ``-m "not gpu"`` tests:
 closed forms and Kronecker construction (Hadamard), involution (rotation),
 error bounds and ties (quantizer), documented byte example (packing),
@@ -34,9 +39,16 @@ fused RMSNorm + modulation prologue closed forms (unit mean square, eps
 inside the root), scale invariance, a worked modulation example, brute-force
 loops and the reduction to the plain prologue when the norm is the identity, and for the
 FP6 (e2m3) code layout the format's constants, hand-derived bit patterns, a
-worked packing example and exact float32 summation at the largest K.  No function
+worked packing example and exact float32 summation at the largest K; for the
+low-rank split the weight normalization in closed form, exact recovery of low-rank
+matrices, agreement with the full SVD under fast spectral decay, the plain split
+rebuilt from a full SVD, best-kept refinement, zero and scale-invariance cases.  No function
 here is "parity unpinned".
 """
 
 from .qlinear_ref import *  # noqa: F401,F403
-from .qlinear_ref import __all__  # noqa: F401
+from .qlinear_ref import __all__ as _q_all
+from .svdq_split_ref import *  # noqa: F401,F403
+from .svdq_split_ref import __all__ as _s_all
+
+__all__ = list(_q_all) + list(_s_all)

@@ -37,6 +37,9 @@ __all__ = [
     "svdq_gateup",
     "stack_layers",
     "stack_layer",
+    "gaussian_sketch",
+    "spectral_weight_bf16",
+    "act_rms",
 ]
 
 
@@ -202,3 +205,36 @@ def stack_layer(index: int, M: int = 16384, rows: int | None = None) -> Workload
     m = M if rows is None else rows
     x = normal_bf16(np.random.default_rng(2 * index + 1), (m, k))
     return Workload(f"stack_b{b}_{name}", x, w, bits, bits, "row", "bf16")
+
+
+# ---- inputs of the offline low-rank split ------------------------------------
+
+def gaussian_sketch(K: int, cols: int, seed: int = 0) -> np.ndarray:
+    """The randomized SVD's sketch: float32 [K, cols] ~ N(0, 1) (seed)."""
+    return np.random.default_rng(seed).standard_normal(size=(K, cols), dtype=np.float32)
+
+
+def spectral_weight_bf16(N: int, K: int, seed: int, rank: int, top: float = 0.5, decay: float = 0.93,
+                         noise: float = 0.002) -> np.ndarray:
+    """A weight with a decaying leading spectrum and a noise floor, as bf16
+    bits [N, K]: W = U diag(s) V^T + noise * G with U [N, rank], V [K, rank]
+    ~ N(0, 1/N), N(0, 1/K) (nearly orthonormal columns), s_j = top * decay^j,
+    G ~ N(0, 1); drawn in the order U, V, G from one generator (seed)."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(size=(N, rank), dtype=np.float32) / np.float32(np.sqrt(N))
+    v = rng.standard_normal(size=(K, rank), dtype=np.float32) / np.float32(np.sqrt(K))
+    g = rng.standard_normal(size=(N, K), dtype=np.float32)
+    s = (top * decay ** np.arange(rank)).astype(np.float32)
+    return to_bf16_bits((u * s[None, :]) @ v.T + np.float32(noise) * g)
+
+
+def act_rms(K: int, seed: int, outlier_frac: float = 0.01, factor: float = 30.0) -> np.ndarray:
+    """Synthetic per-input-channel activation RMS, float32 [K]: log-normal
+    exp(N(0, 0.5^2)) with floor(outlier_frac * K) channels (drawn without
+    replacement after the values) multiplied by `factor`."""
+    rng = np.random.default_rng(seed)
+    r = np.exp(0.5 * rng.standard_normal(size=K, dtype=np.float32)).astype(np.float32)
+    n = int(outlier_frac * K)
+    if n:
+        r[rng.choice(K, n, replace=False)] *= np.float32(factor)
+    return r
