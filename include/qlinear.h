@@ -302,6 +302,53 @@ enum { QL_MAX_SEGMENTS = 8 };
 int qgemm_grouped(const void* a4, const float* sa4, const void* a8, const float* sa8,
                   int64_t M, int64_t K, const ql_segment* segments, int nseg, void* stream);
 
+/* Offline SVDQuant split of a weight into a low-rank branch and an INT4
+ * residual, on the device (README "Krea-2-SVDQuant-ComfyUI": the split is a
+ * seeded randomized SVD, reproducible per device; "Activation-aware branch":
+ * the fit is weighted by per-input-channel activation RMS d, normalized to
+ * mean 1 and floored at 0.05; "Low-rank refinement, and what the objective
+ * actually is": the branch is refit to the current quantization error and
+ * the residual requantized, repeatedly, keeping the best, iteration 1 being
+ * the plain split).  With D = diag(d) (identity without statistics):
+ *   iteration t: fit target A = (W - E_{t-1}) D (E_0 = 0); randomized SVD of A
+ *     (subspace iteration with the sketch omega and power_iters power steps);
+ *     L1 = bf16(V_r S_r^1/2 / d), L2 = bf16((U_r S_r^1/2)^T) (singular values
+ *     below 1e-5 of the largest dropped); residual T = W - (L1 L2)^T,
+ *     quantized from bf16(T) exactly as pack_weight_int4 does (rotated INT4,
+ *     scale_mode); E_t = the residual's dequantized codes rotated back;
+ *     objective err_t = ||(T - E_t) D||_F.
+ *   The outputs hold the iteration with the smallest objective (ties: the
+ *   earlier one).  Deterministic: the same inputs give the same result on
+ *   the same device (no atomics; fixed-order reductions).
+ *   w        [N, K] bf16, row stride ldw (>= K, multiple of 8), 16-byte aligned;
+ *            N % 16 == 0, K % 256 == 0, K <= 32768, N * K < 2^31
+ *   act_rms  NULL or float32 [K] per-input-channel activation RMS
+ *   omega    float32 [K, rank + oversample], row-major: the Gaussian sketch
+ *            (draw it from a seeded generator for reproducible builds)
+ *   rank     16..128, multiple of 16; oversample 0..32; rank + oversample <= min(N, K)
+ *   power_iters 0..8; refine_iters 0..16 (iterations = refine_iters + 1)
+ *   scale_mode QL_SCALE_TENSOR | QL_SCALE_ROW | QL_SCALE_GROUP64 (the residual's scales)
+ *   l1 out: bf16 [K, rank]; l2 out: bf16 [rank, N] (the layout of the low-rank
+ *            GEMM entry points); packed out: [N, K/2] (QL_LAYOUT_PACKED);
+ *            scales out: float32 [1] | [N] | [N, K/64]; all 16-byte aligned
+ *   errors out: float32 [refine_iters + 1], err_t of every iteration
+ *   best_iter out: int32 [1], the iteration returned
+ *   sigma   NULL or out float32 [rank] (16-byte aligned): singular values of
+ *            the returned iteration's fit (0 where dropped)
+ *   workspace, workspace_bytes  device scratch of at least
+ *            svdq_split_workspace_bytes(N, K, rank, oversample, scale_mode)
+ *            bytes, 16-byte aligned, owned by the caller, not in use by
+ *            another call; about 10.5 N K bytes.
+ * All pointers are device pointers.  The call only enqueues work on `stream`. */
+int svdq_split(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, const float* act_rms,
+               const float* omega, int rank, int oversample, int power_iters, int refine_iters,
+               int scale_mode, uint16_t* l1, uint16_t* l2, uint8_t* packed, float* scales,
+               float* errors, int32_t* best_iter, float* sigma, void* workspace,
+               int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes svdq_split needs for these sizes; -1 for invalid sizes. */
+int64_t svdq_split_workspace_bytes(int64_t N, int64_t K, int rank, int oversample, int scale_mode);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,4 +19,6 @@ from ._lib import (  # noqa: F401
     rmsnorm_rotate_quantize_act,
     rotate_quantize_act,
     status_string,
+    svdq_split,
+    svdq_split_workspace_bytes,
 )

@@ -69,6 +69,9 @@ _SIGNATURES = {
     "qgemm_w4a4_lowrank": (_i, [_p, _p, _i, _i, _p, _p, _i, _p, _p, _i, _i64, _i64, _i64, _p, _i, _p,
                                 _i64, _p]),
     "qgemm_grouped": (_i, [_p, _p, _p, _p, _i64, _i64, ctypes.POINTER(Segment), _i, _p]),
+    "svdq_split": (_i, [_p, _i64, _i64, _i64, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _i64,
+                        _p]),
+    "svdq_split_workspace_bytes": (_i64, [_i64, _i64, _i, _i, _i]),
 }
 
 _LIB = None
@@ -307,3 +310,40 @@ def qgemm_grouped(a4, sa4, a8, sa8, K, segments, stream=None):
                              _stream(stream))
     _check("qgemm_grouped", st)
     return outs
+
+
+def svdq_split_workspace_bytes(N, K, rank, oversample=8, scale_mode="group64"):
+    return lib().svdq_split_workspace_bytes(N, K, rank, oversample, _mode(scale_mode))
+
+
+def svdq_split(w, omega, rank, oversample=8, power_iters=2, refine_iters=0, scale_mode="group64",
+               act_rms=None, workspace=None, stream=None):
+    """Offline SVDQuant split of w (bf16 [N, K]) with the Gaussian sketch
+    omega (float32 [K, rank + oversample]).  Returns a dict with l1 bf16
+    [K, rank], l2 bf16 [rank, N], packed uint8 [N, K/2], scales, errors float32
+    [refine_iters + 1], best_iter int32 [1] and sigma float32 [rank]."""
+    assert w.dtype == torch.bfloat16 and w.dim() == 2 and w.stride(1) == 1
+    N, K = w.shape
+    dev = w.device
+    mode = _mode(scale_mode)
+    assert omega.dtype == torch.float32 and tuple(omega.shape) == (K, rank + oversample) and omega.is_contiguous()
+    if act_rms is not None:
+        assert act_rms.dtype == torch.float32 and act_rms.numel() == K and act_rms.is_contiguous()
+    need = lib().svdq_split_workspace_bytes(N, K, rank, oversample, mode)
+    if need < 0:
+        raise QLinearError("svdq_split_workspace_bytes", QL_ERR_SHAPE)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    out = {"l1": torch.empty((K, rank), dtype=torch.bfloat16, device=dev),
+           "l2": torch.empty((rank, N), dtype=torch.bfloat16, device=dev),
+           "packed": torch.empty((N, K // 2), dtype=torch.uint8, device=dev),
+           "scales": torch.empty(_scale_shape(N, K, mode), dtype=torch.float32, device=dev),
+           "errors": torch.empty(refine_iters + 1, dtype=torch.float32, device=dev),
+           "best_iter": torch.empty(1, dtype=torch.int32, device=dev),
+           "sigma": torch.empty(rank, dtype=torch.float32, device=dev)}
+    st = lib().svdq_split(_ptr(w), N, K, w.stride(0), _ptr(act_rms), _ptr(omega), rank, oversample, power_iters,
+                          refine_iters, mode, _ptr(out["l1"]), _ptr(out["l2"]), _ptr(out["packed"]),
+                          _ptr(out["scales"]), _ptr(out["errors"]), _ptr(out["best_iter"]), _ptr(out["sigma"]),
+                          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("svdq_split", st)
+    return out

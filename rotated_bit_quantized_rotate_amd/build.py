@@ -22,7 +22,7 @@ LIB_NAME = "libqlinear.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["qlinear_api.hip", "rotate_quant.hip", "qgemm_pipe.hip"]
+SOURCES = ["qlinear_api.hip", "rotate_quant.hip", "qgemm_pipe.hip", "svdq_split.hip"]
 
 # Packed-FP32 VALU forms are disabled for device code; the host pass warns
 # that it does not know the feature, which is harmless.

@@ -43,6 +43,47 @@ __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
+// -------------------------------------------------- regular Hadamard -------
+// H = H4 (x) H4 (x) H4 (x) H4 with H4 = J - 2I acts on the four base-4
+// digits of the in-group channel index i = 64*d3 + 16*d2 + 4*d1 + d0.
+// Applying H4 along one digit is the butterfly y = (sum of the 4 values
+// that differ only in that digit) - 2*x.  A 16-lane DPP row owns one group;
+// lane t holds the 16 consecutive channels i = 16*t + e.  Digits d0, d1
+// come from e and are transformed in registers; digits d2 = t % 4 and
+// d3 = t / 4 come from the lane and are transformed with DPP quad permutes
+// and 16-lane row rotations.  Computes z = H x (no 1/16).  Every lane of the
+// 16-lane row must be active.
+__device__ __forceinline__ void hadamard256(float (&v)[16]) {
+  // digit d0: e % 4
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float s = (v[4 * q] + v[4 * q + 1]) + (v[4 * q + 2] + v[4 * q + 3]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[4 * q + i] = __builtin_fmaf(-2.0f, v[4 * q + i], s);
+  }
+  // digit d1: e / 4
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float s = (v[c] + v[c + 4]) + (v[c + 8] + v[c + 12]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[c + 4 * i] = __builtin_fmaf(-2.0f, v[c + 4 * i], s);
+  }
+  // digit d2: lane bits 0-1 (the 4 lanes of a quad)
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float s1 = v[e] + dpp_f<DPP_QUAD_SWAP1>(v[e]);
+    const float s = s1 + dpp_f<DPP_QUAD_SWAP2>(s1);
+    v[e] = __builtin_fmaf(-2.0f, v[e], s);
+  }
+  // digit d3: lane bits 2-3 (lanes t, t+4, t+8, t+12 of the 16-lane row)
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float s1 = v[e] + dpp_f<DPP_ROR8>(v[e]);
+    const float s = s1 + dpp_f<DPP_ROR4>(s1);
+    v[e] = __builtin_fmaf(-2.0f, v[e], s);
+  }
+}
+
 // ------------------------------------------------------- launch plumbing ---
 // Status codes mirror include/qlinear.h.
 enum { OK = 0, ERR_LAUNCH = -5 };
@@ -118,5 +159,24 @@ struct GroupedArgs {
   GroupSegment seg[kMaxGroupSegments];
 };
 int launch_qgemm_grouped(const GroupedArgs& g, hipStream_t s);
+
+// Offline SVDQuant split (see svdq_split.hip).
+struct SplitArgs {
+  const uint16_t* w;      // bf16 [N, K], row stride ldw
+  int64_t N, K, ldw;
+  const float* act_rms;   // [K] or NULL
+  const float* omega;     // [K, rank + oversample]
+  int rank, oversample, power_iters, refine_iters, scale_mode;
+  uint16_t* l1;           // [K, rank] bf16
+  uint16_t* l2;           // [rank, N] bf16
+  uint8_t* packed;        // [N, K/2]
+  float* scales;
+  float* errors;          // [refine_iters + 1]
+  int32_t* best_iter;     // [1]
+  float* sigma;           // [rank] or NULL
+  void* workspace;
+};
+int64_t svdq_split_workspace(int64_t N, int64_t K, int rank, int oversample, int scale_mode);
+int launch_svdq_split(const SplitArgs& a, hipStream_t s);
 
 }  // namespace ql

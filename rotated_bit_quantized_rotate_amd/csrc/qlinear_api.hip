@@ -338,4 +338,53 @@ int qgemm_grouped(const void* a4, const float* sa4, const void* a8, const float*
   return ql::launch_qgemm_grouped(g, static_cast<hipStream_t>(stream)) == QL_OK ? QL_OK : QL_ERR_LAUNCH;
 }
 
+int64_t svdq_split_workspace_bytes(int64_t N, int64_t K, int rank, int oversample, int scale_mode) {
+  if (N <= 0 || K <= 0 || K % 256 != 0 || rank <= 0 || oversample < 0 || !valid_mode(scale_mode)) return -1;
+  return ql::svdq_split_workspace(N, K, rank, oversample, scale_mode);
+}
+
+int svdq_split(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, const float* act_rms, const float* omega,
+               int rank, int oversample, int power_iters, int refine_iters, int scale_mode, uint16_t* l1,
+               uint16_t* l2, uint8_t* packed, float* scales, float* errors, int32_t* best_iter, float* sigma,
+               void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!valid_mode(scale_mode)) return QL_ERR_UNSUPPORTED;
+  if (N <= 0 || N % 16 != 0 || K <= 0 || K % 256 != 0 || K > 32768) return QL_ERR_SHAPE;
+  if (ldw < K || ldw % 8 != 0) return QL_ERR_SHAPE;
+  if (rank < 16 || rank > 128 || rank % 16 != 0) return QL_ERR_SHAPE;
+  if (oversample < 0 || oversample > 32) return QL_ERR_SHAPE;
+  const int64_t l = rank + oversample;
+  if (l > N || l > K) return QL_ERR_SHAPE;
+  if (power_iters < 0 || power_iters > 8 || refine_iters < 0 || refine_iters > 16) return QL_ERR_SHAPE;
+  // 32-bit-safe element counts for the one-thread-per-element kernels
+  if (N * K >= (int64_t(1) << 31)) return QL_ERR_SHAPE;
+  if (!w || !omega || !l1 || !l2 || !packed || !scales || !errors || !best_iter || !workspace) return QL_ERR_NULL;
+  if (!al16(w) || !al16(l1) || !al16(l2) || !al16(packed) || !al16(scales) || !al16(workspace) ||
+      !al4(omega) || !al4(errors) || !al4(best_iter) || (act_rms && !al4(act_rms)) || (sigma && !al16(sigma)))
+    return QL_ERR_ALIGN;
+  if (workspace_bytes < ql::svdq_split_workspace(N, K, rank, oversample, scale_mode)) return QL_ERR_SHAPE;
+  int st = check_current_device();
+  if (st != QL_OK) return st;
+  ql::SplitArgs a{};
+  a.w = w;
+  a.N = N;
+  a.K = K;
+  a.ldw = ldw;
+  a.act_rms = act_rms;
+  a.omega = omega;
+  a.rank = rank;
+  a.oversample = oversample;
+  a.power_iters = power_iters;
+  a.refine_iters = refine_iters;
+  a.scale_mode = scale_mode;
+  a.l1 = l1;
+  a.l2 = l2;
+  a.packed = packed;
+  a.scales = scales;
+  a.errors = errors;
+  a.best_iter = best_iter;
+  a.sigma = sigma;
+  a.workspace = workspace;
+  return ql::launch_svdq_split(a, static_cast<hipStream_t>(stream)) == QL_OK ? QL_OK : QL_ERR_LAUNCH;
+}
+
 }  // extern "C"

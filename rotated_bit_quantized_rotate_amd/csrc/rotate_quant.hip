@@ -30,38 +30,6 @@ namespace {
 
 constexpr int kThreads = 256;  // 16 slots of 16 lanes
 
-// H applied to one 256-group held as 16 floats per lane across a 16-lane row.
-__device__ __forceinline__ void hadamard256(float (&v)[16]) {
-  // digit d0: e % 4
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float s = (v[4 * q] + v[4 * q + 1]) + (v[4 * q + 2] + v[4 * q + 3]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[4 * q + i] = __builtin_fmaf(-2.0f, v[4 * q + i], s);
-  }
-  // digit d1: e / 4
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const float s = (v[c] + v[c + 4]) + (v[c + 8] + v[c + 12]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[c + 4 * i] = __builtin_fmaf(-2.0f, v[c + 4 * i], s);
-  }
-  // digit d2: lane bits 0-1 (the 4 lanes of a quad)
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const float s1 = v[e] + dpp_f<DPP_QUAD_SWAP1>(v[e]);
-    const float s = s1 + dpp_f<DPP_QUAD_SWAP2>(s1);
-    v[e] = __builtin_fmaf(-2.0f, v[e], s);
-  }
-  // digit d3: lane bits 2-3 (lanes t, t+4, t+8, t+12 of the 16-lane row)
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const float s1 = v[e] + dpp_f<DPP_ROR8>(v[e]);
-    const float s = s1 + dpp_f<DPP_ROR4>(s1);
-    v[e] = __builtin_fmaf(-2.0f, v[e], s);
-  }
-}
-
 __device__ __forceinline__ float row16_max(float m) {
   m = fmaxf(m, dpp_f<DPP_ROR8>(m));
   m = fmaxf(m, dpp_f<DPP_ROR4>(m));

@@ -21,7 +21,7 @@ def test_header_declares_the_entry_points():
     fns = header_functions()
     for name in ["rotate_quantize_act", "rmsnorm_rotate_quantize_act", "pack_weight_int4", "pack_weight_fp6",
                  "qgemm_w4a4", "qgemm_w4a4_fp6", "qgemm_w8a8", "qgemm_w4a4_lowrank", "qgemm_grouped",
-                 "ql_status_string", "ql_device_supported"]:
+                 "svdq_split", "svdq_split_workspace_bytes", "ql_status_string", "ql_device_supported"]:
         assert name in fns
 
 
@@ -251,6 +251,45 @@ def test_pack_weight_fp6_validation(L):
     assert pw(out=NULL) == -1
     assert pw(w=MISALIGNED) == -3
     assert pw() in (-4, -6)
+
+
+def test_svdq_split_workspace_bytes(L):
+    n1 = L.svdq_split_workspace_bytes(512, 1024, 32, 8, 2)
+    assert n1 >= int(10.5 * 512 * 1024)
+    assert L.svdq_split_workspace_bytes(1024, 1024, 32, 8, 2) > n1
+    assert L.svdq_split_workspace_bytes(512, 1000, 32, 8, 2) == -1      # K % 256
+    assert L.svdq_split_workspace_bytes(512, 1024, 32, 8, 7) == -1      # scale mode
+
+
+def sp(L, **kw):
+    a = dict(w=ALIGNED, N=512, K=1024, ldw=1024, rms=NULL, om=ALIGNED, rank=32, over=8, pi=2, ri=1, mode=2,
+             l1=ALIGNED, l2=ALIGNED, packed=ALIGNED, scales=ALIGNED, errors=ALIGNED, best=ALIGNED, sigma=NULL,
+             ws=ALIGNED, wsb=1 << 40)
+    a.update(kw)
+    return L.svdq_split(a["w"], a["N"], a["K"], a["ldw"], a["rms"], a["om"], a["rank"], a["over"], a["pi"], a["ri"],
+                        a["mode"], a["l1"], a["l2"], a["packed"], a["scales"], a["errors"], a["best"], a["sigma"],
+                        a["ws"], a["wsb"], None)
+
+
+def test_svdq_split_validation(L):
+    assert sp(L, mode=5) == -4
+    assert sp(L, N=500) == -2                     # N % 16
+    assert sp(L, K=1000, ldw=1000) == -2
+    assert sp(L, ldw=1020) == -2
+    assert sp(L, rank=24) == -2
+    assert sp(L, rank=144) == -2
+    assert sp(L, over=33) == -2
+    assert sp(L, N=32, rank=32, over=8) == -2     # rank + oversample > N
+    assert sp(L, pi=9) == -2
+    assert sp(L, ri=17) == -2
+    assert sp(L, wsb=1024) == -2                  # workspace too small
+    assert sp(L, w=NULL) == -1
+    assert sp(L, om=NULL) == -1
+    assert sp(L, ws=NULL) == -1
+    assert sp(L, l1=MISALIGNED) == -3
+    assert sp(L, sigma=MISALIGNED) == -3
+    assert sp(L) in (-4, -6)                      # valid: reaches the device check
+    assert sp(L, rms=ALIGNED, sigma=ALIGNED, mode=0, pi=0, ri=0, over=0) in (-4, -6)
 
 
 def test_device_supported_without_gpu_is_false(L):
