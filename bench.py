@@ -66,6 +66,7 @@ if ROOT not in sys.path:
 
 INT8_MFMA_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POP/s
 FP6_MFMA_PEAK_TOPS = 10100.0     # MI355X dense FP6 / FP4 MFMA, 10.1 PFLOP/s
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector FMA: 256 CUs x 128 lanes x 2 x 2.4 GHz
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 CALIB_BYTES = 256 << 20
 CSRC = "rotated_bit_quantized_rotate_amd/csrc/"
@@ -75,6 +76,7 @@ HEADLINE_METRIC = "effective int TOPS + % int8 MFMA peak, W4A4 rotated GEMM M=40
 GEMM_KERNELS = {
     "attn_proj_w4a4": ("qgemm_w4a4", "4096x5120x5120", ["qgemm_pipe.hip"]),
     "attn_proj_w4a4_fp6": ("qgemm_w4a4_fp6", "4096x5120x5120", ["qgemm_pipe.hip"]),
+    "svdq_split_gateup": ("svdq_split", "40960x5120_r32", ["svdq_split.hip"]),
     "ffdown_w8a8": ("qgemm_w8a8", "4096x20480x5120", ["qgemm_pipe.hip"]),
     "svdq_gateup": ("qgemm_w4a4_lowrank", "4096x5120x40960", ["qgemm_pipe.hip"]),
     "stack": ("qgemm_stack", "224x16384", ["qgemm_pipe.hip"]),
@@ -116,7 +118,7 @@ def _parse():
     a = p.parse_args()
     stack = a.workload.startswith("stack")
     if a.steps is None:
-        a.steps = 3 if stack else 200
+        a.steps = 3 if stack else (20 if a.workload.startswith("svdq_split") else 200)
     a.warmup_min = None
     if a.warmup is None:
         # The GPU's clocks settle only after a fraction of a second of
@@ -246,6 +248,9 @@ class Case:
         self.dtype = ""
         self.wl = None            # host workload for the CPU baseline
         self.peak = INT8_MFMA_PEAK_TOPS   # dense matrix peak of the GEMM's instruction
+        self.bound = "mfma"
+        self.cpu_fn = None        # custom CPU baseline (else the linear's oracle on case.wl)
+        self.unit = "TOP/s"
 
 
 def _bf16_dev(bits, dev):
@@ -326,6 +331,68 @@ def case_attn_fp6(Q, W, dev):
                             "group-256 Hadamard, per-token / per-row scales, bf16 out",
                 "M": M, "N": N, "K": K, "global_batch": M, "parallelism": "single GPU"}
     c.wl = wl
+    return c
+
+
+SPLIT_RANK, SPLIT_OVER, SPLIT_POWER, SPLIT_REFINE = 32, 8, 2, 2
+
+
+def _split_flops(N, K, r, l, q, iters):
+    """fp32 multiply-adds x 2 of the split's large products per call: the
+    sketch product, 2 per power iteration, the final B^T, and the residual."""
+    return 2.0 * N * K * (l * (2 + 2 * q) + r) * iters
+
+
+def case_svdq_split(Q, W, dev):
+    """The offline SVDQuant split of the gate|up weight [40960 x 5120]: rank 32,
+    oversampling 8, 2 power iterations, activation-aware with synthetic
+    channel RMS, 2 refinement iterations (3 fits), group-64 residual."""
+    import torch
+    wl = W.svdq_gateup()
+    N, K = wl.w.shape
+    r, l = SPLIT_RANK, SPLIT_RANK + SPLIT_OVER
+    w = _bf16_dev(wl.w, dev)
+    omega = torch.from_numpy(W.gaussian_sketch(K, l, 0)).to(dev)
+    rms_h = W.act_rms(K, 1)
+    rms = torch.from_numpy(rms_h).to(dev)
+    ws = torch.empty(Q.svdq_split_workspace_bytes(N, K, r, SPLIT_OVER, "group64"), dtype=torch.uint8, device=dev)
+    c = Case()
+    c.launches = [("gemm", lambda: Q.svdq_split(w, omega, r, SPLIT_OVER, SPLIT_POWER, SPLIT_REFINE, "group64",
+                                                act_rms=rms, workspace=ws))]
+    iters = SPLIT_REFINE + 1
+    c.ops = _split_flops(N, K, r, l, SPLIT_POWER, iters)
+    c.gemm_launches = 1
+    c.gemm_bytes = N * K * 2 + K * l * 4 + K * 4 + K * r * 2 + r * N * 2 + N * K // 2 + N * (K // 64) * 4
+    c.metric = ("offline SVDQuant split of the gate|up weight [40960x5120], rank 32, 3 fits: effective fp32 "
+                "TFLOP/s of its products (ms_per_step = one split)")
+    c.dtype = "fp32 (products, CholeskyQR2 and Jacobi in fp64), bf16 factors, int4 residual"
+    c.peak = FP32_VECTOR_PEAK_TFLOPS
+    c.bound = "alu"
+    c.unit = "TFLOP/s"
+    c.config = {"workload": "SVDQuant split: W bf16 [40960x5120] N(0, 0.02), Gaussian sketch [5120x40] (seed 0), "
+                            "synthetic log-normal channel RMS with 1% outlier channels x30 (seed 1); rank 32, "
+                            "oversample 8, 2 power iterations, 2 refinement iterations, group-64 INT4 residual",
+                "N": N, "K": K, "rank": r, "iterations": iters, "parallelism": "single GPU"}
+
+    def cpu(target_s):
+        import oracle as O
+        threads = _blas_threads()
+        om = W.gaussian_sketch(K, l, 0)
+
+        def run(rows):
+            t0 = time.perf_counter()
+            O.svdq_split(wl.w[:rows], om, r, SPLIT_POWER, SPLIT_REFINE, "group64", act_rms=rms_h)
+            return time.perf_counter() - t0
+
+        probe = run(512)
+        rows = int(min(N, max(512, 512 * target_s / max(probe, 1e-3))) // 16 * 16)
+        t = run(rows)
+        ops = _split_flops(rows, K, r, l, SPLIT_POWER, iters)
+        return {"value": round(ops / t / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+                "sample": f"the oracle's split of the first {rows} of {N} weight rows (same rank, sketch, "
+                          f"power and refinement iterations, act-aware, group-64): {t:.2f} s wall on {threads} "
+                          f"BLAS threads"}
+    c.cpu_fn = cpu
     return c
 
 
@@ -604,7 +671,8 @@ def case_stack_fused(Q, W, dev, grouped=False):
     return c
 
 
-CASES = {"attn_proj_w4a4": case_attn, "attn_proj_w4a4_fp6": case_attn_fp6, "ffdown_w8a8": case_ffdown, "svdq_gateup": case_svdq,
+CASES = {"attn_proj_w4a4": case_attn, "attn_proj_w4a4_fp6": case_attn_fp6, "svdq_split_gateup": case_svdq_split,
+         "ffdown_w8a8": case_ffdown, "svdq_gateup": case_svdq,
          "stack": case_stack, "stack_fused": case_stack_fused,
          "stack_grouped": lambda Q, W, dev: case_stack_fused(Q, W, dev, grouped=True)}
 
@@ -715,7 +783,7 @@ def main():
     rec = {
         "metric": case.metric,
         "value": round(value, 2),
-        "unit": "TOP/s",
+        "unit": case.unit,
         "n_gpus": 1,
         "steps": n,
         "warmup": args.warmup,
@@ -726,26 +794,29 @@ def main():
         "dtype": case.dtype,
         "data": "synthetic",
         "config": case.config,
-        "pct_int8_peak_step": round(100.0 * value / INT8_MFMA_PEAK_TOPS, 2),
+        "pct_int8_peak_step": round(100.0 * value / INT8_MFMA_PEAK_TOPS, 2) if case.bound == "mfma" else None,
         "gemm_only": {"ms": round(gemm_ms, 5), "ms_per_launch": round(gemm_launch_ms, 5),
                       "tops": round(gemm_tops, 2),
-                      "pct_int8_peak": round(100.0 * gemm_tops / INT8_MFMA_PEAK_TOPS, 2),
+                      "pct_int8_peak": (round(100.0 * gemm_tops / INT8_MFMA_PEAK_TOPS, 2)
+                                        if case.bound == "mfma" else None),
                       "gbs": round(case.gemm_bytes / (gemm_ms * 1e-3) / 1e9, 1)},
-        "prologue": {"ms": round(pro_ms, 5),
-                     "gbs": round(case.pro_bytes / (pro_ms * 1e-3) / 1e9, 1),
-                     "pct_hbm_peak": round(100.0 * case.pro_bytes / (pro_ms * 1e-3) / 1e9
-                                           / HBM_PEAK_GBS, 2)},
+        "prologue": None if pro_ms <= 0 else {
+            "ms": round(pro_ms, 5),
+            "gbs": round(case.pro_bytes / (pro_ms * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100.0 * case.pro_bytes / (pro_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)},
         "graph_step_ms": None if graph_step_ms is None else round(graph_step_ms, 5),
         "graph_step_tops": None if graph_step_ms is None else round(ops / (graph_step_ms * 1e-3) / 1e12, 2),
         "weight_prep_ms": round(case.prep_ms, 5),
         "wall_ms_timed_region": round(wall_ms, 3),
-        "roofline": {"bound": "mfma", "kernel": label,
+        "roofline": {"bound": case.bound, "kernel": label,
                      "achieved": round(gemm_tops, 2), "peak": case.peak,
-                     "unit": "TOP/s", "frac": round(gemm_tops / case.peak, 4),
+                     "unit": case.unit, "frac": round(gemm_tops / case.peak, 4),
                      "traffic": traffic,
                      "algorithmic_bytes": int(case.gemm_bytes // case.gemm_launches)},
     }
-    if not args.no_cpu_baseline and case.wl is not None:
+    if not args.no_cpu_baseline and case.cpu_fn is not None:
+        rec["cpu_baseline"] = case.cpu_fn(args.cpu_seconds)
+    elif not args.no_cpu_baseline and case.wl is not None:
         rec["cpu_baseline"] = cpu_baseline(case.wl, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
 
