@@ -32,9 +32,10 @@ quantization, int4 packing) is offline and timed separately.
 
 Prints ONE JSON line.  `value` is the effective integer throughput of a whole
 step, 2*M*N*K / step time, in TOP/s (eager launches, K steps between two
-synchronizations).  `roofline` describes the GEMM kernel (the dominant
-kernel): its average duration comes from HIP events that bracket each launch
-on the stream the kernels run on, inside the timed region.  `cpu_baseline`
+synchronizations, with one HIP event before and one after).  `roofline`
+describes the GEMM kernel (the dominant kernel): its average duration comes
+from a second run of the same K steps with a HIP event after every launch,
+on the stream the kernels run on.  `cpu_baseline`
 times the CPU oracle on a bounded sample of the same workload.
 
 Profiling helpers (used to make the summaries under profiles/):
@@ -718,22 +719,35 @@ def main():
         args.warmup = w
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly `steps` steps, synchronized on both sides.
-    # An event follows every launch, on the stream the kernels run on (the
-    # current torch stream), so each kernel's duration is the gap between
-    # the event before it and the event after it.
+    # ---- timed region: exactly `steps` steps, synchronized on both sides,
+    # one event before and one after on the stream the kernels run on (the
+    # current torch stream).  This is the step time `value` reports.
     n = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(L * n + 1)]
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e_start.record()
+    for s in range(n):
+        step()
+    e_end.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    step_ms = e_start.elapsed_time(e_end) / n
+
+    # ---- per-kernel breakdown: the same `steps` steps again with an event
+    # after every launch, so each kernel's duration is the gap between the
+    # event before it and the event after it.  (Recording an event between
+    # kernels adds a small gap, which is why the step time above is taken
+    # without them.)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(L * n + 1)]
+    torch.cuda.synchronize()
     ev[0].record()
     for s in range(n):
         for i, (_, fn) in enumerate(case.launches):
             fn()
             ev[s * L + i + 1].record()
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
-    step_ms = ev[0].elapsed_time(ev[L * n]) / n
+    step_events_ms = ev[0].elapsed_time(ev[L * n]) / n
     t_tag = {"prologue": 0.0, "gemm": 0.0}
     for s in range(n):
         for i, (tag, _) in enumerate(case.launches):
@@ -788,6 +802,7 @@ def main():
         "steps": n,
         "warmup": args.warmup,
         "ms_per_step": round(step_ms, 5),
+        "ms_per_step_with_kernel_events": round(step_events_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
