@@ -28,14 +28,17 @@ namespace ql {
 namespace {
 
 constexpr int kSplitThreads = 256;
+constexpr int64_t kSmallLds = 65536;  // dynamic LDS for the one-workgroup fp64 kernels (64 KB)
 constexpr float kDFloor = 0.05f;      // floor of the normalized activation weights
 constexpr double kSigmaDrop = 1e-5;   // singular values below this fraction of the largest are dropped
 
 // ---- fp32 tile GEMM with generic strides and split-K -----------------------
 // C[M x Nc] (+ z * M * Nc) = sum over k in split z of A(i, k) * B(k, j), with
 // A(i, k) = a[i * a_rs + k * a_cs] and B(k, j) = b[k * b_rs + j * b_cs].
-// 64 x 64 tiles, 16-deep k steps, 4 x 4 outputs per thread.  Tile loads run
-// along whichever index is contiguous, so transposed operands stay coalesced.
+// 64 x 64 tiles, 32-deep k steps, 4 x 4 outputs per thread.  Tile loads run
+// along whichever index is contiguous, so transposed operands stay
+// coalesced, and the next step's tiles are loaded into registers while the
+// current step computes from LDS.
 struct GemmDesc {
   const float* a;
   int64_t a_rs, a_cs;
@@ -45,9 +48,11 @@ struct GemmDesc {
   int64_t M, Nc, Kd, kchunk;
 };
 
+constexpr int kGemmBK = 32;
+
 __global__ __launch_bounds__(kSplitThreads) void sgemm_kernel(GemmDesc g) {
-  __shared__ float As[16][64 + 4];
-  __shared__ float Bs[16][64 + 4];
+  __shared__ float As[kGemmBK][64 + 4];
+  __shared__ float Bs[kGemmBK][64 + 4];
   const int tid = threadIdx.x;
   const int64_t i0 = (int64_t)blockIdx.y * 64, j0 = (int64_t)blockIdx.x * 64;
   const int64_t kbeg = (int64_t)blockIdx.z * g.kchunk;
@@ -55,27 +60,40 @@ __global__ __launch_bounds__(kSplitThreads) void sgemm_kernel(GemmDesc g) {
   const int tx = tid & 15, ty = tid >> 4;
   const bool a_along_i = g.a_rs == 1 && g.a_cs != 1;
   const bool b_along_j = g.b_cs == 1;
+  constexpr int PER = 64 * kGemmBK / kSplitThreads;  // tile elements per thread and operand
+  float ra[PER], rb[PER];
+  auto fetch = [&](int64_t k0) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + kSplitThreads * u;
+      const int ii = a_along_i ? (e & 63) : (e / kGemmBK);
+      const int ka = a_along_i ? (e >> 6) : (e % kGemmBK);
+      const int64_t gi = i0 + ii, gk = k0 + ka;
+      ra[u] = (gi < g.M && gk < kend) ? g.a[gi * g.a_rs + gk * g.a_cs] : 0.f;
+      const int jj = b_along_j ? (e & 63) : (e / kGemmBK);
+      const int kb = b_along_j ? (e >> 6) : (e % kGemmBK);
+      const int64_t gj = j0 + jj, gk2 = k0 + kb;
+      rb[u] = (gj < g.Nc && gk2 < kend) ? g.b[gk2 * g.b_rs + gj * g.b_cs] : 0.f;
+    }
+  };
   float acc[4][4];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
-  for (int64_t k0 = kbeg; k0 < kend; k0 += 16) {
+  if (kbeg < kend) fetch(kbeg);
+  for (int64_t k0 = kbeg; k0 < kend; k0 += kGemmBK) {
+    __syncthreads();  // the previous step's reads of As / Bs are done
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < PER; ++u) {
       const int e = tid + kSplitThreads * u;
-      const int ii = a_along_i ? (e & 63) : (e >> 4);
-      const int ka = a_along_i ? (e >> 6) : (e & 15);
-      const int64_t gi = i0 + ii, gk = k0 + ka;
-      As[ka][ii] = (gi < g.M && gk < kend) ? g.a[gi * g.a_rs + gk * g.a_cs] : 0.f;
-      const int jj = b_along_j ? (e & 63) : (e >> 4);
-      const int kb = b_along_j ? (e >> 6) : (e & 15);
-      const int64_t gj = j0 + jj, gk2 = k0 + kb;
-      Bs[kb][jj] = (gj < g.Nc && gk2 < kend) ? g.b[gk2 * g.b_rs + gj * g.b_cs] : 0.f;
+      As[a_along_i ? (e >> 6) : (e % kGemmBK)][a_along_i ? (e & 63) : (e / kGemmBK)] = ra[u];
+      Bs[b_along_j ? (e >> 6) : (e % kGemmBK)][b_along_j ? (e & 63) : (e / kGemmBK)] = rb[u];
     }
     __syncthreads();
+    if (k0 + kGemmBK < kend) fetch(k0 + kGemmBK);  // in flight during the step below
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
+    for (int kk = 0; kk < kGemmBK; ++kk) {
       float av[4], bv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) av[r] = As[kk][ty * 4 + r];
@@ -86,7 +104,6 @@ __global__ __launch_bounds__(kSplitThreads) void sgemm_kernel(GemmDesc g) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[r][c] = __builtin_fmaf(av[r], bv[c], acc[r][c]);
     }
-    __syncthreads();
   }
   float* const cz = g.c + (int64_t)blockIdx.z * g.M * g.Nc;
 #pragma unroll
@@ -143,12 +160,15 @@ __global__ __launch_bounds__(kSplitThreads) void act_weights_kernel(const float*
 // the mean diagonal (a tiny shift that keeps a rank-deficient Gram matrix
 // positive definite); rinv = R^-1 (fp32, row-major), so X R^-1 has
 // orthonormal columns when G = X^T X.  A zero Gram matrix (trace <= 1e-60)
-// gives rinv = 0.  One workgroup; W is an l x l fp64
-// scratch in global memory.
-__global__ __launch_bounds__(kSplitThreads) void chol_inv_kernel(const double* __restrict__ G, int l,
-                                                                 double* __restrict__ W, double* __restrict__ R,
-                                                                 float* __restrict__ rinv) {
+// gives rinv = 0.  One workgroup; its two l x l fp64 scratch matrices live in
+// dynamic LDS when the launch provides 2 l^2 doubles of it, else in Wg / Rg
+// (global memory).
+__global__ __launch_bounds__(kSplitThreads) void chol_inv_kernel(const double* __restrict__ G, int l, double* Wg,
+                                                                 double* Rg, float* __restrict__ rinv, int in_lds) {
+  extern __shared__ double dyn[];
   __shared__ double tr;
+  double* const W = in_lds ? dyn : Wg;
+  double* const R = in_lds ? dyn + l * l : Rg;
   const int tid = threadIdx.x;
   if (tid == 0) {
     double t = 0.0;
@@ -199,15 +219,16 @@ __global__ __launch_bounds__(kSplitThreads) void chol_inv_kernel(const double* _
 // ---- symmetric eigen-decomposition (parallel cyclic Jacobi, fp64) ----------
 // S (fp64 [l x l], symmetric) is diagonalized in place by rounds of disjoint
 // Givens rotations (round-robin pairing, n - 1 rounds per sweep for n = l
-// rounded up to even); V accumulates the rotations.  Sweeps stop once the
+// rounded up to even); V accumulates the rotations (both in LDS when they fit).  Sweeps stop once the
 // off-diagonal mass is below 1e-30 of the diagonal's (at most 40).  Then
 // the eigenvalues are sorted in decreasing order and the leading r give
 //   sigma_j = sqrt(lambda_j)  (0 when below 1e-5 sigma_0: dropped),
 //   M1[:, j] = v_j sigma_j^-1/2,  M2[:, j] = v_j sigma_j^1/2   (fp32 [l x r]).
 __global__ __launch_bounds__(kSplitThreads) void jacobi_eig_kernel(const double* __restrict__ S0, int l, int r,
-                                                                   double* __restrict__ S, double* __restrict__ V,
-                                                                   float* __restrict__ M1, float* __restrict__ M2,
-                                                                   float* __restrict__ sigma) {
+                                                                   double* Sg, double* Vg, float* __restrict__ M1,
+                                                                   float* __restrict__ M2, float* __restrict__ sigma,
+                                                                   int in_lds) {
+  extern __shared__ double dyn[];
   __shared__ int pp[96], pq[96];
   __shared__ double pc[96], ps[96];
   __shared__ double red[2][kSplitThreads];
@@ -216,6 +237,9 @@ __global__ __launch_bounds__(kSplitThreads) void jacobi_eig_kernel(const double*
   const int tid = threadIdx.x;
   const int n = l + (l & 1);
   const int npair = n / 2;
+  // S and V in dynamic LDS when the launch provides 2 n^2 doubles, else global
+  double* const S = in_lds ? dyn : Sg;
+  double* const V = in_lds ? dyn + n * n : Vg;
   for (int e = tid; e < n * n; e += kSplitThreads) {
     const int i = e / n, j = e % n;
     S[e] = (i < l && j < l) ? S0[i * l + j] : 0.0;
@@ -563,7 +587,7 @@ struct Runner {
             double* c64, int64_t M, int64_t Nc, int64_t Kd, int64_t S, float* parts) {
     GemmDesc g{a, a_rs, a_cs, b, b_rs, b_cs, nullptr, M, Nc, Kd, 0};
     if (S < 1) S = 1;
-    g.kchunk = ((Kd + S - 1) / S + 15) / 16 * 16;
+    g.kchunk = ((Kd + S - 1) / S + kGemmBK - 1) / kGemmBK * kGemmBK;
     S = (Kd + g.kchunk - 1) / g.kchunk;
     const bool direct = S == 1 && c32 && !c64;
     g.c = direct ? c32 : parts;
@@ -592,6 +616,10 @@ int launch_svdq_split(const SplitArgs& a, hipStream_t s) {
   Ws w = carve(static_cast<uint8_t*>(a.workspace), N, K, a.rank, a.oversample, a.scale_mode);
   Runner run{s};
   const int64_t groups = N * (K >> 8);
+  // the small fp64 matrices go to LDS when they fit (l <= 64), else they stay in the workspace
+  const int64_t npad = l + (l & 1);
+  const size_t chol_lds = 2 * l * l * 8 <= kSmallLds ? (size_t)(2 * l * l * 8) : 0;
+  const size_t eig_lds = 2 * npad * npad * 8 <= kSmallLds ? (size_t)(2 * npad * npad * 8) : 0;
   const unsigned deq_blocks = (unsigned)((groups + 15) / 16);
 
   // CholeskyQR2: X [R x l] (row-major) -> orthonormal columns, back in X
@@ -600,7 +628,8 @@ int launch_svdq_split(const SplitArgs& a, hipStream_t s) {
       float* src = pass == 0 ? X : X2;
       float* dst = pass == 0 ? X2 : X;
       run.gemm(src, 1, l, src, l, 1, nullptr, w.G, l, l, R, split_parts(R), w.parts);
-      hipLaunchKernelGGL(chol_inv_kernel, dim3(1), dim3(kSplitThreads), 0, s, w.G, (int)l, w.W, w.R, w.rinv);
+      hipLaunchKernelGGL(chol_inv_kernel, dim3(1), dim3(kSplitThreads), chol_lds, s, w.G, (int)l, w.W, w.R, w.rinv,
+                         chol_lds ? 1 : 0);
       run.check();
       run.gemm(src, l, 1, w.rinv, l, 1, dst, nullptr, R, l, l, 1, w.parts);
     }
@@ -625,8 +654,8 @@ int launch_svdq_split(const SplitArgs& a, hipStream_t s) {
     }
     run.gemm(w.A, 1, K, w.Y, l, 1, w.Z, nullptr, K, l, N, split_parts(N), w.parts);  // Z = B^T
     run.gemm(w.Z, 1, l, w.Z, l, 1, nullptr, w.G, l, l, K, split_parts(K), w.parts);  // B B^T
-    hipLaunchKernelGGL(jacobi_eig_kernel, dim3(1), dim3(kSplitThreads), 0, s, w.G, (int)l, r, w.S, w.V, w.M1, w.M2,
-                       w.sigma_c);
+    hipLaunchKernelGGL(jacobi_eig_kernel, dim3(1), dim3(kSplitThreads), eig_lds, s, w.G, (int)l, r, w.S, w.V, w.M1,
+                       w.M2, w.sigma_c, eig_lds ? 1 : 0);
     run.check();
     // branch factors
     run.gemm(w.Z, l, 1, w.M1, r, 1, w.F1, nullptr, K, r, l, 1, w.parts);
