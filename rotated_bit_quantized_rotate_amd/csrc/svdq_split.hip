@@ -35,7 +35,9 @@ constexpr double kSigmaDrop = 1e-5;   // singular values below this fraction of 
 // ---- fp32 tile GEMM with generic strides and split-K -----------------------
 // C[M x Nc] (+ z * M * Nc) = sum over k in split z of A(i, k) * B(k, j), with
 // A(i, k) = a[i * a_rs + k * a_cs] and B(k, j) = b[k * b_rs + j * b_cs].
-// 64 x 64 tiles, 32-deep k steps, 4 x 4 outputs per thread.  Tile loads run
+// 64 x 64 tiles, 32-deep k steps.  Each wave computes a 32 x 32 quadrant as
+// 2 x 2 fp32 MFMA 16x16x4 blocks (lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16] and holds C[4 (l / 16) + r][l % 16]).  Tile loads run
 // along whichever index is contiguous, so transposed operands stay
 // coalesced, and the next step's tiles are loaded into registers while the
 // current step computes from LDS.
@@ -57,7 +59,9 @@ __global__ __launch_bounds__(kSplitThreads) void sgemm_kernel(GemmDesc g) {
   const int64_t i0 = (int64_t)blockIdx.y * 64, j0 = (int64_t)blockIdx.x * 64;
   const int64_t kbeg = (int64_t)blockIdx.z * g.kchunk;
   const int64_t kend = kbeg + g.kchunk < g.Kd ? kbeg + g.kchunk : g.Kd;
-  const int tx = tid & 15, ty = tid >> 4;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;  // the wave's quadrant
   const bool a_along_i = g.a_rs == 1 && g.a_cs != 1;
   const bool b_along_j = g.b_cs == 1;
   constexpr int PER = 64 * kGemmBK / kSplitThreads;  // tile elements per thread and operand
@@ -76,11 +80,11 @@ __global__ __launch_bounds__(kSplitThreads) void sgemm_kernel(GemmDesc g) {
       rb[u] = (gj < g.Nc && gk2 < kend) ? g.b[gk2 * g.b_rs + gj * g.b_cs] : 0.f;
     }
   };
-  float acc[4][4];
+  v4f acc[2][2];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+    for (int b = 0; b < 2; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
   if (kbeg < kend) fetch(kbeg);
   for (int64_t k0 = kbeg; k0 < kend; k0 += kGemmBK) {
     __syncthreads();  // the previous step's reads of As / Bs are done
@@ -93,29 +97,26 @@ __global__ __launch_bounds__(kSplitThreads) void sgemm_kernel(GemmDesc g) {
     __syncthreads();
     if (k0 + kGemmBK < kend) fetch(k0 + kGemmBK);  // in flight during the step below
 #pragma unroll
-    for (int kk = 0; kk < kGemmBK; ++kk) {
-      float av[4], bv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) av[r] = As[kk][ty * 4 + r];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) bv[c] = Bs[kk][tx * 4 + c];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[r][c] = __builtin_fmaf(av[r], bv[c], acc[r][c]);
+    for (int kq = 0; kq < kGemmBK; kq += 4) {
+      const float a0 = As[kq + lg][wr + l16], a1 = As[kq + lg][wr + 16 + l16];
+      const float b0 = Bs[kq + lg][wc + l16], b1 = Bs[kq + lg][wc + 16 + l16];
+      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
     }
   }
   float* const cz = g.c + (int64_t)blockIdx.z * g.M * g.Nc;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int64_t i = i0 + ty * 4 + r;
-    if (i >= g.M) continue;
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int64_t j = j0 + tx * 4 + c;
-      if (j < g.Nc) cz[i * g.Nc + j] = acc[r][c];
-    }
-  }
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t i = i0 + wr + 16 * a + 4 * lg + r;
+        const int64_t j = j0 + wc + 16 * b + l16;
+        if (i < g.M && j < g.Nc) cz[i * g.Nc + j] = acc[a][b][r];
+      }
 }
 
 // out[e] = sum over s of parts[s * n + e], in order s = 0, 1, ... (fp64 sum);
