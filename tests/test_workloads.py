@@ -37,3 +37,17 @@ def test_stack_recipe_counts():
     names8 = {(blk, n) for blk, n, _, _, b in layers if b == 8}
     assert all((blk, "wk") in names8 and (blk, "wv") in names8 for blk in range(28))
     assert sum(1 for blk, n in names8 if n == "wo") == 27
+
+
+def test_split_inputs_are_deterministic_and_shaped():
+    om = W.gaussian_sketch(512, 40, 7)
+    assert om.dtype == np.float32 and om.shape == (512, 40)
+    assert np.array_equal(om, W.gaussian_sketch(512, 40, 7)) and not np.array_equal(om, W.gaussian_sketch(512, 40, 8))
+    rms = W.act_rms(1000, 3)
+    assert rms.dtype == np.float32 and rms.shape == (1000,) and (rms > 0).all()
+    # 1 % of the channels (10) x30 on a log-normal base: they stand well above the median
+    assert np.sort(rms)[-10:].min() > 5 * np.median(rms)
+    w = W.spectral_weight_bf16(128, 256, 4, 8, top=1.0, decay=0.5, noise=1e-3)
+    assert w.dtype == np.uint16 and w.shape == (128, 256)
+    s = np.linalg.svd((w.astype(np.uint32) << 16).view(np.float32).astype(np.float64), compute_uv=False)
+    assert s[0] > 0.5 and s[8] < 0.1 * s[0]          # a decaying leading spectrum above the noise floor
