@@ -33,9 +33,12 @@ quantization, int4 packing) is offline and timed separately.
 Prints ONE JSON line.  `value` is the effective integer throughput of a whole
 step, 2*M*N*K / step time, in TOP/s (eager launches, K steps between two
 synchronizations, with one HIP event before and one after).  `roofline`
-describes the GEMM kernel (the dominant kernel): its average duration comes
-from a second run of the same K steps with a HIP event after every launch,
-on the stream the kernels run on.  `cpu_baseline`
+describes the GEMM kernel (the dominant kernel): its time per step is that
+step time minus the time of the step's prologues run alone K times (events
+only at the ends, on the stream the kernels run on).  A second run of the K
+steps with a HIP event after every launch gives the per-kernel breakdown
+reported beside it (`*_with_kernel_events`); those events add a gap of a
+few microseconds at each kernel boundary.  `cpu_baseline`
 times the CPU oracle on a bounded sample of the same workload.
 
 Profiling helpers (used to make the summaries under profiles/):
@@ -752,8 +755,26 @@ def main():
     for s in range(n):
         for i, (tag, _) in enumerate(case.launches):
             t_tag[tag] += ev[s * L + i].elapsed_time(ev[s * L + i + 1])
-    gemm_ms = t_tag["gemm"] / n            # GEMM time per step
-    pro_ms = t_tag["prologue"] / n
+    gemm_ev_ms = t_tag["gemm"] / n          # per step, from the per-launch events
+    pro_ev_ms = t_tag["prologue"] / n
+
+    # ---- the step's prologues alone, `steps` times, with events only at the
+    # ends: the GEMM time per step is the clean step time minus this, which
+    # leaves out the gaps the per-launch events add (each costs a few us).
+    pro_fns = [fn for tag, fn in case.launches if tag == "prologue"]
+    if pro_fns:
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        p0.record()
+        for _ in range(n):
+            for fn in pro_fns:
+                fn()
+        p1.record()
+        torch.cuda.synchronize()
+        pro_ms = p0.elapsed_time(p1) / n
+    else:
+        pro_ms = 0.0
+    gemm_ms = step_ms - pro_ms
     gemm_launch_ms = gemm_ms / case.gemm_launches
 
     # ---- the same step replayed from a HIP graph (no host launch cost)
@@ -811,12 +832,14 @@ def main():
         "config": case.config,
         "pct_int8_peak_step": round(100.0 * value / INT8_MFMA_PEAK_TOPS, 2) if case.bound == "mfma" else None,
         "gemm_only": {"ms": round(gemm_ms, 5), "ms_per_launch": round(gemm_launch_ms, 5),
+                      "ms_per_launch_with_kernel_events": round(gemm_ev_ms / case.gemm_launches, 5),
                       "tops": round(gemm_tops, 2),
                       "pct_int8_peak": (round(100.0 * gemm_tops / INT8_MFMA_PEAK_TOPS, 2)
                                         if case.bound == "mfma" else None),
                       "gbs": round(case.gemm_bytes / (gemm_ms * 1e-3) / 1e9, 1)},
         "prologue": None if pro_ms <= 0 else {
             "ms": round(pro_ms, 5),
+            "ms_with_kernel_events": round(pro_ev_ms, 5),
             "gbs": round(case.pro_bytes / (pro_ms * 1e-3) / 1e9, 1),
             "pct_hbm_peak": round(100.0 * case.pro_bytes / (pro_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)},
         "graph_step_ms": None if graph_step_ms is None else round(graph_step_ms, 5),
