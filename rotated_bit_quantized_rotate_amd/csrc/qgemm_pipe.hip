@@ -682,12 +682,12 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   if constexpr (STAGED) {
     constexpr bool F32 = EPI == EPI_GATED;
     constexpr int EB = F32 ? 4 : 2;          // staged bytes per value
-    constexpr int NB = F32 ? 4 : 2;          // bands
+    constexpr int NB = F32 ? 8 : 4;          // bands; round p stages bands p and NB / 2 + p
     constexpr int HR = C::BM / NB;           // rows per band
     constexpr int FPB = C::FI * 2 / NB;      // fragments of a wave per band (FI * 16 = BM / 2)
     constexpr int RB = C::BN * EB;           // staged bytes of one tile row
     constexpr int PITCH = RB + 16;           // LDS row pitch
-    constexpr int RPA = (HR + NS - 1) / NS;  // staging rows per ring array
+    constexpr int RPA = (2 * HR + NS - 1) / NS;  // staging rows per ring array (two bands per round)
     static_assert(C::FI * 16 * 2 == C::BM && (C::FI * 2) % NB == 0, "bands cover whole fragments");
     static_assert(RPA * PITCH <= C::STAGE, "staging rows must fit the ring");
     // the factor vector sits behind the staging rows of the last ring array
@@ -715,21 +715,14 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
     }
     lds_barrier();
 #pragma unroll
-    for (int band = 0; band < NB; ++band) {
-      // the band's rows belong to wave row wm = band / (NB / 2), fragments
-      // i0 .. i0 + FPB - 1
-      if (wm == band / (NB / 2)) {
-        const int i0 = (band % (NB / 2)) * FPB;
-        static_assert(FPB % 4 == 0, "row factors are read four at a time");
+    for (int band = 0; band < NB / 2; ++band) {
+      // both wave rows stage at once: wave row wm its band wm * NB / 2 + band
+      // (fragments i0 .. i0 + FPB - 1) into staging rows wm * HR + ...
+      {
+        const int i0 = band * FPB;
         float samv[FPB];
 #pragma unroll
-        for (int f = 0; f < FPB / 4; ++f) {
-          const float4 s4 = *reinterpret_cast<const float4*>(sv + wm * C::WM + l16 * C::FI + i0 + 4 * f);
-          samv[4 * f] = s4.x;
-          samv[4 * f + 1] = s4.y;
-          samv[4 * f + 2] = s4.z;
-          samv[4 * f + 3] = s4.w;
-        }
+        for (int f = 0; f < FPB; ++f) samv[f] = sv[wm * C::WM + l16 * C::FI + i0 + f];
 #pragma unroll
         for (int j = 0; j < C::FJ; ++j) {
           const int col = wn * C::WN + j * 16 + lg * 4;   // tile column
@@ -749,7 +742,7 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
               y[r] = v * sam * swv[r] + addv[r];
               if (EPI == EPI_SIGMOID) y[r] = 1.0f / (1.0f + __expf(-y[r]));  // the attention gate
             }
-            uint8_t* dst = row_ptr(ii * 16 + l16) + col * EB;
+            uint8_t* dst = row_ptr(wm * HR + ii * 16 + l16) + col * EB;
             if (F32) {
               *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
             } else {
@@ -765,9 +758,9 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
       // Output rows leave with nontemporal stores: nothing reads them in this
       // kernel, and streaming them past L2 allocation measured 3-4 % faster.
       constexpr int CH = C::BN / 8;  // 8-column chunks per row (16 bf16 bytes out)
-      for (int c = tid; c < HR * CH; c += C::NT) {
+      for (int c = tid; c < 2 * HR * CH; c += C::NT) {
         const int r = c / CH, ch = c % CH;
-        const int64_t m = m0 + band * HR + r;
+        const int64_t m = m0 + (r < HR ? band * HR + r : C::BM / 2 + band * HR + (r - HR));
         const int64_t n = n0 + ch * 8;  // 16 | N: a chunk is wholly in or out
         if (m >= p.M || n >= p.N) continue;
         uint16_t* o = static_cast<uint16_t*>(p.out) + m * p.ldo + n;
