@@ -688,7 +688,7 @@ def main():
         summarize_pmc(*args.summarize_pmc, args.workload)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the library has no "
               "multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 

@@ -696,6 +696,32 @@ def test_e2e_stack_layer_shapes(Q, index):
     _e2e(Q, wl, rows=rng.choice(wl.M, 8, replace=False), wrows=rng.choice(wl.N, 384, replace=False))
 
 
+def test_gemm_empty_inputs(Q):
+    """M = 0: every GEMM entry point returns an empty output and launches nothing."""
+    import torch
+
+    N, K, r = 320, 512, 16
+    d = "cuda"
+    w4 = torch.zeros((N, K // 2), dtype=torch.uint8, device=d)
+    w8 = torch.zeros((N, K), dtype=torch.int8, device=d)
+    w6 = torch.zeros((N, K // 4 * 3), dtype=torch.uint8, device=d)
+    sw = torch.ones(N, dtype=torch.float32, device=d)
+    swg = torch.ones((N, K // 64), dtype=torch.float32, device=d)
+    a8 = torch.empty((0, K), dtype=torch.int8, device=d)
+    sa = torch.empty((0,), dtype=torch.float32, device=d)
+    outs = [
+        Q.qgemm_w4a4(a8, sa, w4, sw, K),
+        Q.qgemm_w8a8(a8, sa, w8, sw, residual=torch.empty((0, N), dtype=torch.bfloat16, device=d),
+                     gate=torch.ones(N, dtype=torch.bfloat16, device=d), epilogue="gated_residual"),
+        Q.qgemm_w4a4_lowrank(a8, torch.empty((0, K // 64), dtype=torch.float32, device=d), w4, swg, K,
+                             lr=torch.empty((0, r), dtype=torch.bfloat16, device=d),
+                             l2=torch.zeros((r, N), dtype=torch.bfloat16, device=d)),
+        Q.qgemm_w4a4_fp6(torch.empty((0, K // 4 * 3), dtype=torch.uint8, device=d), sa, w6, sw, K),
+    ]
+    torch.cuda.synchronize()
+    assert [tuple(o.shape) for o in outs] == [(0, N), (0, N), (0, N // 2), (0, N)]
+
+
 def test_deterministic_outputs(Q):
     import torch
 
