@@ -1,8 +1,8 @@
 """Benchmark of the rotated low-bit quantized linear on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--workload attn_proj_w4a4|ffdown_w8a8|svdq_gateup|stack|stack_fused|
-                                stack_grouped]
+                    [--workload attn_proj_w4a4|attn_proj_w4a4_fp6|ffdown_w8a8|svdq_gateup|
+                                svdq_gateup_fp6|svdq_split_gateup|stack|stack_fused|stack_grouped]
 
 Default workload (the headline line): one DiT attention projection at
 1024x1024 -- X bf16 [4096 x 5120] ~ N(0,1) with 1% outlier channels x30,
@@ -14,6 +14,9 @@ Other workloads (separate runs, same JSON shape):
                 row [5120 x 20480], gated residual onto bf16 [4096 x 5120]
   svdq_gateup   group-64 W4A4 gate|up [40960 x 5120] + bf16 rank-32
                 low-rank branch, SwiGLU out [4096 x 20480]
+  svdq_gateup_fp6  the same layer with the codes in the FP6 e2m3 layout on
+                the FP6 matrix instruction (bit-identical output)
+  attn_proj_w4a4_fp6  the headline projection on the FP6 instruction
   stack         the 224 linears of a 28-block DiT at 2048x2048 (16384
                 tokens): 128 W4A4 + 96 W8A8, every activation resident
   stack_fused   the same 224 linears with each block's RMSNorm + modulation
@@ -83,6 +86,7 @@ GEMM_KERNELS = {
     "svdq_split_gateup": ("svdq_split", "40960x5120_r32", ["svdq_split.hip"]),
     "ffdown_w8a8": ("qgemm_w8a8", "4096x20480x5120", ["qgemm_pipe.hip"]),
     "svdq_gateup": ("qgemm_w4a4_lowrank", "4096x5120x40960", ["qgemm_pipe.hip"]),
+    "svdq_gateup_fp6": ("qgemm_w4a4_lowrank_fp6", "4096x5120x40960", ["qgemm_pipe.hip"]),
     "stack": ("qgemm_stack", "224x16384", ["qgemm_pipe.hip"]),
     "stack_fused": ("qgemm_stack_fused", "224x16384", ["qgemm_pipe.hip"]),
     "stack_grouped": ("qgemm_stack_grouped", "224x16384", ["qgemm_pipe.hip"]),
@@ -434,37 +438,49 @@ def case_ffdown(Q, W, dev):
     return c
 
 
-def case_svdq(Q, W, dev):
+def case_svdq(Q, W, dev, fp6=False):
+    """The SVDQuant gate|up layer; fp6: the same codes in the FP6 e2m3 layout
+    on the FP6 matrix instruction, one instruction per 64-channel group."""
     import torch
     wl = W.svdq_gateup()
     M, N, K = wl.M, wl.N, wl.K
     r = wl.l1.shape[1]
     x, w = _bf16_dev(wl.x, dev), _bf16_dev(wl.w, dev)
     l1, l2 = _bf16_dev(wl.l1, dev), _bf16_dev(wl.l2, dev)
-    codes = torch.empty((M, K), dtype=torch.int8, device=dev)
+    acols, wcols = (K // 4 * 3, K // 4 * 3) if fp6 else (K, K // 2)
+    codes = torch.empty((M, acols), dtype=torch.uint8 if fp6 else torch.int8, device=dev)
     sa = torch.empty((M, K // 64), dtype=torch.float32, device=dev)
     lr = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
     out = torch.empty((M, N // 2), dtype=torch.bfloat16, device=dev)
-    wq = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    wq = torch.empty((N, wcols), dtype=torch.uint8, device=dev)
     sw = torch.empty((N, K // 64), dtype=torch.float32, device=dev)
+    layout = "fp6" if fp6 else "i8"
+    pack = Q.pack_weight_fp6 if fp6 else Q.pack_weight_int4
     c = Case()
-    c.prep_ms = _timed_prep(lambda: Q.pack_weight_int4(w, scale_mode="group64", packed=wq, scales=sw))
+    c.prep_ms = _timed_prep(lambda: pack(w, scale_mode="group64", packed=wq, scales=sw))
     c.launches = [
-        ("prologue", lambda: Q.rotate_quantize_act(x, bits=4, scale_mode="group64", codes=codes,
+        ("prologue", lambda: Q.rotate_quantize_act(x, bits=4, scale_mode="group64", layout=layout, codes=codes,
                                                    scales=sa, l1=l1, lr=lr)),
-        ("gemm", lambda: Q.qgemm_w4a4_lowrank(codes, sa, wq, sw, K, lr=lr, l2=l2, epilogue="swiglu",
-                                              out=out)),
+        ("gemm", lambda: Q.qgemm_w4a4_lowrank(codes, sa, wq, sw, K, lr=lr, l2=l2, a_layout=layout,
+                                              epilogue="swiglu", out=out)),
     ]
     c.ops = wl.int_ops
     c.gemm_launches = 1
-    c.pro_bytes = M * K * 2 + K * r * 2 + M * K + M * (K // 64) * 4 + M * r * 2
-    c.gemm_bytes = (M * K + N * K // 2 + M * (K // 64) * 4 + N * (K // 64) * 4 + M * r * 2
+    c.pro_bytes = M * K * 2 + K * r * 2 + M * acols + M * (K // 64) * 4 + M * r * 2
+    c.gemm_bytes = (M * acols + N * wcols + M * (K // 64) * 4 + N * (K // 64) * 4 + M * r * 2
                     + r * N * 2 + M * (N // 2) * 2)
-    c.metric = ("effective int TOPS + % int8 MFMA peak, group-64 W4A4 GEMM + rank-32 low-rank + SwiGLU "
-                "M=4096 K=5120 N=40960")
-    c.dtype = "int8 MFMA (int4 codes), int32 per-64 partials, fp32 rescale, bf16 out"
-    c.config = {"workload": "SVDQuant fused gate|up: X bf16 [4096x5120], W int4 group-64 [40960x5120], "
-                            "bf16 rank-32 L1 [5120x32] / L2 [32x40960], SwiGLU -> bf16 [4096x20480]",
+    if fp6:
+        c.metric = ("effective int TOPS, group-64 W4A4 GEMM + rank-32 low-rank + SwiGLU M=4096 K=5120 N=40960 "
+                    "on the FP6 matrix instruction (experiment)")
+        c.dtype = "fp6 e2m3 MFMA (exact int4 codes), exact fp32 per-64 partials, fp32 rescale, bf16 out"
+        c.peak = FP6_MFMA_PEAK_TOPS
+    else:
+        c.metric = ("effective int TOPS + % int8 MFMA peak, group-64 W4A4 GEMM + rank-32 low-rank + SwiGLU "
+                    "M=4096 K=5120 N=40960")
+        c.dtype = "int8 MFMA (int4 codes), int32 per-64 partials, fp32 rescale, bf16 out"
+    c.config = {"workload": "SVDQuant fused gate|up: X bf16 [4096x5120], W int4 group-64 [40960x5120]"
+                            + (" stored as FP6 e2m3" if fp6 else "")
+                            + ", bf16 rank-32 L1 [5120x32] / L2 [32x40960], SwiGLU -> bf16 [4096x20480]",
                 "M": M, "N": N, "K": K, "rank": r, "global_batch": M, "parallelism": "single GPU"}
     c.wl = wl
     return c
@@ -677,6 +693,7 @@ def case_stack_fused(Q, W, dev, grouped=False):
 
 CASES = {"attn_proj_w4a4": case_attn, "attn_proj_w4a4_fp6": case_attn_fp6, "svdq_split_gateup": case_svdq_split,
          "ffdown_w8a8": case_ffdown, "svdq_gateup": case_svdq,
+         "svdq_gateup_fp6": lambda Q, W, dev: case_svdq(Q, W, dev, fp6=True),
          "stack": case_stack, "stack_fused": case_stack_fused,
          "stack_grouped": lambda Q, W, dev: case_stack_fused(Q, W, dev, grouped=True)}
 

@@ -187,7 +187,8 @@ int pack_weight_int4(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
 /* Offline INT4 weight preparation for the FP6 GEMM (qgemm_w4a4_fp6): the
  * same codes and scales as pack_weight_int4, stored in QL_LAYOUT_FP6;
  * equal to rotate_quantize_act(w, N, K, ldw, 4, scale_mode, QL_LAYOUT_FP6,
- * rotate, ...).  scale_mode TENSOR | ROW.
+ * rotate, ...).  scale_mode TENSOR | ROW | GROUP64 (GROUP64 weights go to
+ * qgemm_w4a4_fp6 or qgemm_w4a4_lowrank with a_layout QL_LAYOUT_FP6).
  *   packed out: [N, 3K/4] bytes in the QL_LAYOUT_FP6 order                 */
 int pack_weight_fp6(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
                     int scale_mode, int rotate, uint8_t* packed, float* scales,
@@ -222,10 +223,16 @@ int qgemm_w4a4(const void* a, const float* sa, int a_scale_mode, int a_layout,
  *   a   [M, 3K/4] activation codes in QL_LAYOUT_FP6 (rotate_quantize_act or
  *       rmsnorm_rotate_quantize_act with layout QL_LAYOUT_FP6), dense rows
  *   w   [N, 3K/4] weight codes in QL_LAYOUT_FP6 (pack_weight_fp6), dense rows
- *   sa, a_scale_mode, sw, w_scale_mode   TENSOR | ROW scales, as qgemm_w4a4
+ *   sa, a_scale_mode, sw, w_scale_mode   TENSOR | ROW scales, as qgemm_w4a4,
+ *       or GROUP64 on both sides (README "Krea-2-SVDQuant-ComfyUI": INT4 with
+ *       group size 64); each instruction then runs once per 64-channel group
+ *       with the other group's weight lanes zeroed, and its fp32 result, the
+ *       group's exact partial, is rescaled as qgemm_w4a4_lowrank does, so the
+ *       output again equals the INT8 path's bit for bit
  *   bias, epilogue, out, ldo             as qgemm_w4a4 (BF16 | F32 | I32 |
- *       SIGMOID); QL_EPI_I32 returns the exact sum of code products
- * K must also be < 342392 (else QL_ERR_SHAPE). */
+ *       SIGMOID; GROUP64: BF16 | F32); QL_EPI_I32 returns the exact sum of
+ *       code products
+ * With tensor / row scales K must also be < 342392 (else QL_ERR_SHAPE). */
 int qgemm_w4a4_fp6(const uint8_t* a, const float* sa, int a_scale_mode,
                    const uint8_t* w, const float* sw, int w_scale_mode,
                    int64_t M, int64_t N, int64_t K,
@@ -256,7 +263,11 @@ int qgemm_w8a8(const int8_t* a, const float* sa, int a_scale_mode,
  * correction branch on top of the W4A4 kernel; model card "Krea 2 Turbo
  * OrbitQuant W4A4", section "Fused transformer": SwiGLU gate|up GEMM).
  *   a, sa, a_scale_mode, a_layout, w, sw, w_scale_mode   as qgemm_w4a4, and
- *             GROUP64 is allowed only on both sides at once
+ *             GROUP64 is allowed only on both sides at once; a_layout
+ *             QL_LAYOUT_FP6 (GROUP64 only) takes both a and w in the FP6
+ *             layout ([M, 3K/4] and [N, 3K/4], from pack_weight_fp6) and runs
+ *             the group-64 FP6 kernel of qgemm_w4a4_fp6, bit-identical to the
+ *             INT8 path
  *   lr        bf16 [M, rank] (from rotate_quantize_act), dense rows
  *   l2        bf16 [rank, N], dense rows
  *   rank      0 (no branch; lr, l2 may be NULL) or a multiple of 16, <= 128

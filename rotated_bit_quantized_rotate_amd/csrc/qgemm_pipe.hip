@@ -169,7 +169,7 @@ struct Cfg {
   static constexpr int FJ = WN / 16;
   static constexpr int ARB = F6 ? BK * 3 / 4 : (AP ? BK / 2 : BK);  // bytes per A row per stage
   static constexpr int WRB = F6 ? BK * 3 / 4 : (WP ? BK / 2 : BK);
-  static_assert(!F6 || (!GROUP && AP && WP), "FP6 operands: both sides, tensor / row scales");
+  static_assert(!F6 || (AP && WP), "FP6 operands: both sides");
   static constexpr int SA = BM * ARB;
   static constexpr int SW = BN * WRB;
   // two groups of fp32 scales, padded so every wave issues the same number
@@ -497,6 +497,32 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
         const uint2 l = *reinterpret_cast<const uint2*>(Ws + w6_lo + j * 16 * C::WRB);
         wf[j] = v8i{(int)h.x, (int)h.y, (int)h.z, (int)h.w, (int)l.x, (int)l.y, 0, 0};  // FP6 reads 6 dwords
       }
+      // Group-64 scales: an instruction spans the stage's two groups (lanes
+      // 0..31 carry channels 0..63, lanes 32..63 channels 64..127), so each
+      // group runs with the other group's W lanes zeroed; its fp32 result is
+      // the group's exact partial, rescaled like the INT8 path's.
+      v8i wg[C::GROUP ? 2 : 1][C::GROUP ? C::FJ : 1];
+      v4f sav6[C::GROUP ? 2 : 1][C::GROUP ? C::FI / 4 : 1];
+      v4f swv6[C::GROUP ? 2 : 1][C::GROUP ? C::FJ : 1];
+      if constexpr (C::GROUP) {
+        const uint8_t* Ss = Ws + C::SW;
+        const bool lo = lane < 32;
+        const v8i z = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < C::FJ; ++j) {
+          wg[0][j] = lo ? wf[j] : z;
+          wg[1][j] = lo ? z : wf[j];
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+          for (int f = 0; f < C::FI / 4; ++f)
+            sav6[kk][f] = *reinterpret_cast<const v4f*>(Ss + sa_off + (kk * C::BM + 4 * f) * 4);
+#pragma unroll
+          for (int j = 0; j < C::FJ; ++j)
+            swv6[kk][j] = *reinterpret_cast<const v4f*>(Ss + sw_off + (kk * C::BN + j * 16) * 4);
+        }
+      }
       constexpr int PF = 2;
       auto read_a = [&](int i) {
         const uint4 h = *reinterpret_cast<const uint4*>(As + a6_hi + i * 16 * C::ARB);
@@ -512,13 +538,33 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
         if (i + PF < C::FI) abuf[(i + PF) % (PF + 1)] = read_a(i + PF);
         if (dma && i < NDMA) issue_one(nxt, kt + NS - 1, i);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (C::GROUP) {
 #pragma unroll
-        for (int j = 0; j < C::FJ; ++j) {
-          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], abuf[i % (PF + 1)], acc[j][i],
-                                                                      2, 2, 0, 127, 0, 127);
-          // pin the group here: otherwise the compiler sinks every MFMA
-          // below the loads' branches and must hold all A fragments at once
-          asm volatile("" : "+v"(acc[j][i]));
+          for (int kk = 0; kk < 2; ++kk) {
+            const float s_i = sav6[kk][i / 4][i % 4];
+            v4f part[C::FJ];
+#pragma unroll
+            for (int j = 0; j < C::FJ; ++j)
+              part[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wg[kk][j], abuf[i % (PF + 1)],
+                                                                         v4f{0.f, 0.f, 0.f, 0.f}, 2, 2, 0, 127,
+                                                                         0, 127);
+#pragma unroll
+            for (int j = 0; j < C::FJ; ++j) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                yf[j][i][r] = __builtin_fmaf(part[j][r], s_i * swv6[kk][j][r], yf[j][i][r]);
+              asm volatile("" : "+v"(yf[j][i]));
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < C::FJ; ++j) {
+            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], abuf[i % (PF + 1)], acc[j][i],
+                                                                        2, 2, 0, 127, 0, 127);
+            // pin the group here: otherwise the compiler sinks every MFMA
+            // below the loads' branches and must hold all A fragments at once
+            asm volatile("" : "+v"(acc[j][i]));
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -672,11 +718,11 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   // A lane holds 4 consecutive columns of one row per fragment, so direct
   // stores write 32-byte row pieces, and the 128-byte lines that two wave
   // columns share reach memory in parts.  Instead the tile goes through LDS
-  // (the ring is free now) a band of rows at a time and leaves as whole rows
-  // with 16-byte stores.  bf16 output (plain or through the sigmoid of the
-  // attention gate): the band holds finished bf16 values (two bands of BM/2
-  // rows).  Gated residual: the band holds y in fp32 (four
-  // bands of BM/4 rows), and the copy-out reads the residual with the same
+  // (the ring is free now) two bands of rows at a time, one per wave row,
+  // and leaves as whole rows with 16-byte stores.  bf16 output (plain or
+  // through the sigmoid of the attention gate): the bands hold finished bf16
+  // values (four bands of BM/4 rows).  Gated residual: the bands hold y in
+  // fp32 (eight bands of BM/8 rows), and the copy-out reads the residual with the same
   // coalesced 16-byte accesses, so out = res + gate * y is still rounded
   // once.
   if constexpr (STAGED) {
@@ -1126,7 +1172,11 @@ int launch_qgemm(const GemmArgs& g, hipStream_t s) {
   if (group || g.rank > 0 || g.epilogue == EPI_SWIGLU) {
     // INT4 weights only (the ABI routes nothing else here); 256 x 256
     // tiles keep the gate/up fragment pairs and the scale block in LDS.
-    if (group) {
+    // Group-64 FP6: 256 x 128 tiles, whose 24 KB A stage splits evenly over
+    // the 8 waves' 1 KB loads (a 128-row FP6 stage would not).
+    if (group && g.fp6) {
+      e = launch_lowrank<Cfg<256, 128, 2, 4, true, true, true, true>>(p, g.epilogue, s);
+    } else if (group) {
       e = g.a_packed ? launch_lowrank<Cfg<128, 256, 2, 4, true, true, true>>(p, g.epilogue, s)
                      : launch_lowrank<Cfg<128, 256, 2, 4, false, true, true>>(p, g.epilogue, s);
     } else {

@@ -129,7 +129,6 @@ int pack_weight_int4(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, int s
 int pack_weight_fp6(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, int scale_mode, int rotate,
                     uint8_t* packed, float* scales, void* stream) {
   if (N <= 0) return QL_ERR_SHAPE;
-  if (scale_mode != QL_SCALE_TENSOR && scale_mode != QL_SCALE_ROW) return QL_ERR_UNSUPPORTED;
   return rotate_quantize_act(w, N, K, ldw, 4, scale_mode, QL_LAYOUT_FP6, rotate, packed, scales, nullptr, 0,
                              nullptr, stream);
 }
@@ -194,14 +193,18 @@ int qgemm_w4a4(const void* a, const float* sa, int a_scale_mode, int a_layout, c
 int qgemm_w4a4_fp6(const uint8_t* a, const float* sa, int a_scale_mode, const uint8_t* w, const float* sw,
                    int w_scale_mode, int64_t M, int64_t N, int64_t K, const uint16_t* bias, int epilogue,
                    void* out, int64_t ldo, void* stream) {
-  if ((a_scale_mode != QL_SCALE_TENSOR && a_scale_mode != QL_SCALE_ROW) ||
-      (w_scale_mode != QL_SCALE_TENSOR && w_scale_mode != QL_SCALE_ROW))
+  const bool grp = a_scale_mode == QL_SCALE_GROUP64 && w_scale_mode == QL_SCALE_GROUP64;
+  if (!grp && ((a_scale_mode != QL_SCALE_TENSOR && a_scale_mode != QL_SCALE_ROW) ||
+               (w_scale_mode != QL_SCALE_TENSOR && w_scale_mode != QL_SCALE_ROW)))
     return QL_ERR_UNSUPPORTED;
   if (epilogue != QL_EPI_BF16 && epilogue != QL_EPI_F32 && epilogue != QL_EPI_I32 && epilogue != QL_EPI_SIGMOID)
     return QL_ERR_UNSUPPORTED;
+  // group-64 partials are rescaled in fp32, so there is no exact sum to return
+  if (grp && epilogue != QL_EPI_BF16 && epilogue != QL_EPI_F32) return QL_ERR_UNSUPPORTED;
   int st = validate_gemm_common(a, sa, w, sw, M, N, K, bias, out, ldo, epilogue);
   if (st != QL_OK) return st;
-  if (49 * K >= (int64_t(1) << 24)) return QL_ERR_SHAPE;  // float32 sums of code products stay exact
+  // float32 sums of code products stay exact (a group-64 partial is at most 64 * 49)
+  if (!grp && 49 * K >= (int64_t(1) << 24)) return QL_ERR_SHAPE;
   if ((st = check_current_device()) != QL_OK) return st;
   if (M == 0) return QL_OK;
   ql::GemmArgs g{};
@@ -267,7 +270,10 @@ int qgemm_w4a4_lowrank(const void* a, const float* sa, int a_scale_mode, int a_l
                        int64_t ldo, void* stream) {
   if (!valid_mode(a_scale_mode) || !valid_mode(w_scale_mode)) return QL_ERR_UNSUPPORTED;
   if ((a_scale_mode == QL_SCALE_GROUP64) != (w_scale_mode == QL_SCALE_GROUP64)) return QL_ERR_UNSUPPORTED;
-  if (a_layout != QL_LAYOUT_I8 && a_layout != QL_LAYOUT_PACKED) return QL_ERR_UNSUPPORTED;
+  if (a_layout != QL_LAYOUT_I8 && a_layout != QL_LAYOUT_PACKED && a_layout != QL_LAYOUT_FP6)
+    return QL_ERR_UNSUPPORTED;
+  // FP6 operands (both sides) come with group-64 scales here
+  if (a_layout == QL_LAYOUT_FP6 && a_scale_mode != QL_SCALE_GROUP64) return QL_ERR_UNSUPPORTED;
   if (epilogue != QL_EPI_BF16 && epilogue != QL_EPI_SWIGLU && epilogue != QL_EPI_F32) return QL_ERR_UNSUPPORTED;
   if (epilogue == QL_EPI_SWIGLU && N % 32 != 0) return QL_ERR_SHAPE;
   int st = validate_gemm_common(a, sa, w, sw, M, N, K, bias, out, ldo, epilogue);
@@ -289,6 +295,7 @@ int qgemm_w4a4_lowrank(const void* a, const float* sa, int a_scale_mode, int a_l
   g.K = K;
   g.a_packed = a_layout == QL_LAYOUT_PACKED;
   g.w_packed = 1;
+  g.fp6 = a_layout == QL_LAYOUT_FP6;
   g.a_mode = a_scale_mode;
   g.w_mode = w_scale_mode;
   g.bias = bias;

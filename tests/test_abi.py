@@ -175,7 +175,9 @@ def test_qgemm_lowrank_validation(L):
     assert glr(L, am=1) == -4                     # group64 on one side only
     assert glr(L, epi=4) == -4
     assert glr(L, epi=2) == -4
-
+    assert glr(L, al=3) == -4                     # no such layout
+    assert glr(L, al=2, am=1, wm=1) == -4         # FP6 operands here only with group-64 scales
+    assert glr(L, al=2) in (-4, -6)               # FP6 + group-64 reaches the device check
 
 
 def grp(L, segs, **kw):
@@ -221,8 +223,13 @@ def g6(L, **kw):
 
 
 def test_qgemm_w4a4_fp6_validation(L):
-    assert g6(L, am=2) == -4                      # tensor / row scales only
+    assert g6(L, am=2) == -4                      # group-64 scales only on both sides
     assert g6(L, wm=2) == -4
+    assert g6(L, am=2, wm=2, epi=4) == -4         # group sums are rescaled: no exact I32 result
+    assert g6(L, am=2, wm=2, epi=5) == -4
+    assert g6(L, am=2, wm=2, K=342528) in (-4, -6)  # group partials are exact at any K
+    for epi in (0, 3):
+        assert g6(L, am=2, wm=2, epi=epi) in (-4, -6)
     assert g6(L, epi=1) == -4                     # no SwiGLU / gated residual here
     assert g6(L, epi=2) == -4
     assert g6(L, N=24) == -2
@@ -245,7 +252,8 @@ def test_pack_weight_fp6_validation(L):
         a.update(kw)
         return L.pack_weight_fp6(a["w"], a["N"], a["K"], a["ldw"], a["mode"], a["rot"], a["out"], a["sc"], None)
 
-    assert pw(mode=2) == -4                       # group-64 scales do not reach the FP6 GEMM
+    assert pw(mode=3) == -4                       # no such scale mode
+    assert pw(mode=2) in (-4, -6)                 # group-64 passes validation (no device here)
     assert pw(N=0) == -2
     assert pw(K=320, ldw=320) == -2
     assert pw(out=NULL) == -1

@@ -108,7 +108,7 @@ def test_rmsnorm_prologue_fp6_layout(Q):
     assert torch.equal(s6, s8)
 
 
-@pytest.mark.parametrize("mode", ["row", "tensor"])
+@pytest.mark.parametrize("mode", ["row", "tensor", "group64"])
 def test_pack_weight_fp6(Q, mode):
     import torch
 
@@ -120,8 +120,6 @@ def test_pack_weight_fp6(Q, mode):
     torch.cuda.synchronize()
     assert np.array_equal(p6.cpu().numpy(), O.pack_fp6(O.unpack_int4(p4.cpu().numpy())))
     assert torch.equal(s6, s4)
-    with pytest.raises(Q.QLinearError):
-        Q.pack_weight_fp6(w, scale_mode="group64")
 
 
 # ---------------------------------------------------------------- GEMM ------
@@ -244,3 +242,111 @@ def test_fp6_attention_projection_full_size(Q):
     qw = O.unpack_int4(w4.cpu().numpy())
     assert np.array_equal(acc[rows].cpu().numpy().astype(np.int64), O.int_gemm(qa, qw))
     assert bf16_bits(got).shape == (M, N)
+
+
+# ------------------------------------------------------- group-64 GEMM ------
+
+def _group_pair(M, N, K, seed):
+    """Codes in both layouts and group-64 scales [M, K/64], [N, K/64]."""
+    rng = np.random.default_rng(seed)
+    qa = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    sa = (rng.random((M, K // 64), dtype=np.float32) * 0.02 + 0.005).astype(np.float32)
+    sw = (rng.random((N, K // 64), dtype=np.float32) * 0.02 + 0.005).astype(np.float32)
+    return qa, qw, sa, sw
+
+
+# 256 x 128 tiles: one ragged tile, several with ragged M and N, and a long K
+@pytest.mark.parametrize("M,N,K", [(1, 16, 256), (257, 400, 1024), (300, 656, 768), (1000, 2080, 2048),
+                                   (64, 48, 20480)])
+def test_fp6_group64_equals_int4_path(Q, M, N, K):
+    import torch
+
+    qa, qw, sa_h, sw_h = _group_pair(M, N, K, M + 3 * N + K)
+    sa, sw = to_dev(sa_h), to_dev(sw_h)
+    a8, w4 = to_dev(qa), to_dev(O.pack_int4(qw))
+    a6, w6 = to_dev(O.pack_fp6(qa)), to_dev(O.pack_fp6(qw))
+    bias = to_dev_bf16(_rand_bf16(N, (N,), 0.1))
+    for epi in ("bf16", "f32"):
+        for bb in (None, bias):
+            ref = Q.qgemm_w4a4(a8, sa, w4, sw, K, a_scale_mode="group64", w_scale_mode="group64", bias=bb,
+                               epilogue=epi)
+            got = Q.qgemm_w4a4_fp6(a6, sa, w6, sw, K, a_scale_mode="group64", w_scale_mode="group64", bias=bb,
+                                   epilogue=epi)
+            torch.cuda.synchronize()
+            iv = torch.int32 if epi == "f32" else torch.int16
+            assert torch.equal(got.view(iv), ref.view(iv)), (epi, bb is None)
+    if M * N * K > 2e8:
+        return
+    # the float result itself against the oracle's rescaled group sums: G
+    # fp32 multiply-adds of exact partials err by at most (G + 3) u times the
+    # sum of the terms' magnitudes (u = 2^-24)
+    y = O.linear_fp64(O.QuantResult(qa, sa_h, 4, "group64", None), O.QuantResult(qw, sw_h, 4, "group64", None))
+    got = Q.qgemm_w4a4_fp6(a6, sa, w6, sw, K, a_scale_mode="group64", w_scale_mode="group64", epilogue="f32")
+    torch.cuda.synchronize()
+    G = K // 64
+    mag = np.zeros((M, N))
+    for g in range(G):
+        sl = slice(64 * g, 64 * g + 64)
+        part = np.abs(qa[:, sl]).astype(np.float64) @ np.abs(qw[:, sl]).astype(np.float64).T
+        mag += part * (sa_h[:, g].astype(np.float64)[:, None] * sw_h[:, g].astype(np.float64)[None, :])
+    err = np.abs(got.cpu().numpy().astype(np.float64) - y)
+    assert np.all(err <= (G + 3) * 2.0 ** -24 * mag)
+
+
+@pytest.mark.parametrize("rank", [0, 32])
+@pytest.mark.parametrize("epi", ["swiglu", "bf16"])
+def test_fp6_group64_lowrank_equals_int4_path(Q, rank, epi):
+    import torch
+
+    M, N, K = 300, 640, 1024
+    qa, qw, sa_h, sw_h = _group_pair(M, N, K, 5 + rank)
+    sa, sw = to_dev(sa_h), to_dev(sw_h)
+    lr = to_dev_bf16(_rand_bf16(6, (M, rank), 0.5)) if rank else None
+    l2 = to_dev_bf16(_rand_bf16(7, (rank, N), 0.05)) if rank else None
+    ref = Q.qgemm_w4a4_lowrank(to_dev(qa), sa, to_dev(O.pack_int4(qw)), sw, K, lr=lr, l2=l2, epilogue=epi)
+    got = Q.qgemm_w4a4_lowrank(to_dev(O.pack_fp6(qa)), sa, to_dev(O.pack_fp6(qw)), sw, K, lr=lr, l2=l2,
+                               a_layout="fp6", epilogue=epi)
+    torch.cuda.synchronize()
+    assert got.shape == ref.shape
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
+def test_fp6_group64_rejections(Q):
+    import torch
+
+    M, N, K = 32, 64, 256
+    qa, qw, sa_h, sw_h = _group_pair(M, N, K, 1)
+    a6, w6 = to_dev(O.pack_fp6(qa)), to_dev(O.pack_fp6(qw))
+    with pytest.raises(Q.QLinearError):   # group sums are rescaled: no exact I32 result
+        Q.qgemm_w4a4_fp6(a6, to_dev(sa_h), w6, to_dev(sw_h), K, a_scale_mode="group64",
+                         w_scale_mode="group64", epilogue="i32")
+    row_a = torch.ones(M, dtype=torch.float32, device="cuda")
+    row_w = torch.ones(N, dtype=torch.float32, device="cuda")
+    with pytest.raises(Q.QLinearError):   # FP6 in the low-rank GEMM is group-64 only
+        Q.qgemm_w4a4_lowrank(a6, row_a, w6, row_w, K, a_scale_mode="row", w_scale_mode="row",
+                             a_layout="fp6", epilogue="bf16")
+
+
+def test_fp6_group64_svdq_gateup_full_size(Q):
+    """The SVDQuant gate|up layer, 4096 x 40960 x 5120 with group-64 scales, a
+    rank-32 branch and SwiGLU, from bf16 through both prologues and weight
+    packers: the FP6 output equals the INT8 path's bit for bit."""
+    import torch
+
+    M, N, K, r = 4096, 40960, 5120, 32
+    torch.manual_seed(11)
+    x = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+    w = (torch.randn(N, K, device="cuda") * 0.02).to(torch.bfloat16)
+    l1 = (torch.randn(K, r, device="cuda") * 0.02).to(torch.bfloat16)
+    l2 = (torch.randn(r, N, device="cuda") * 0.02).to(torch.bfloat16)
+    a8, sa8, lr = Q.rotate_quantize_act(x, bits=4, scale_mode="group64", layout="i8", l1=l1)
+    a6, sa6, _ = Q.rotate_quantize_act(x, bits=4, scale_mode="group64", layout="fp6")
+    w4, sw4 = Q.pack_weight_int4(w, scale_mode="group64")
+    w6, sw6 = Q.pack_weight_fp6(w, scale_mode="group64")
+    ref = Q.qgemm_w4a4_lowrank(a8, sa8, w4, sw4, K, lr=lr, l2=l2, epilogue="swiglu")
+    got = Q.qgemm_w4a4_lowrank(a6, sa6, w6, sw6, K, lr=lr, l2=l2, a_layout="fp6", epilogue="swiglu")
+    torch.cuda.synchronize()
+    assert torch.equal(sa6, sa8) and torch.equal(sw6, sw4)
+    assert got.shape == (M, N // 2)
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
