@@ -246,7 +246,8 @@ def qgemm_w4a4(a, sa, w, sw, K, a_scale_mode="row", w_scale_mode="row", a_layout
 
 def qgemm_w4a4_fp6(a, sa, w, sw, K, a_scale_mode="row", w_scale_mode="row", bias=None, epilogue="bf16",
                    out=None, stream=None):
-    """a: codes [M, 3K/4], w: codes [N, 3K/4], both in the FP6 layout."""
+    """a: codes [M, 3K/4], w: codes [N, 3K/4], both in the FP6 layout; tensor /
+    row scales, or group-64 on both sides (BF16 / F32 epilogues)."""
     M = a.shape[0]
     N = w.shape[0]
     epi = _epi(epilogue)
@@ -274,7 +275,9 @@ def qgemm_w8a8(a, sa, w, sw, a_scale_mode="row", w_scale_mode="row", bias=None, 
 def qgemm_w4a4_lowrank(a, sa, w, sw, K, lr=None, l2=None, a_scale_mode="group64",
                        w_scale_mode="group64", a_layout="i8", bias=None, epilogue="swiglu", out=None,
                        stream=None):
-    """Group-64 (or row) W4A4 GEMM + optional low-rank branch lr @ l2 + epilogue."""
+    """Group-64 (or row) W4A4 GEMM + optional low-rank branch lr @ l2 + epilogue.
+    a_layout "fp6" (group-64 only): a and w both in the FP6 layout, run on the
+    FP6 matrix instruction with the same result."""
     M = a.shape[0]
     N = w.shape[0]
     epi = _epi(epilogue)

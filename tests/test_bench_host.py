@@ -59,7 +59,7 @@ def test_load_traffic_rejects_a_stale_source_hash(tmp_path, monkeypatch):
 
 
 def test_committed_traffic_records_match_the_sources():
-    for wl in ("attn_proj_w4a4", "attn_proj_w4a4_fp6", "ffdown_w8a8", "svdq_gateup"):
+    for wl in ("attn_proj_w4a4", "attn_proj_w4a4_fp6", "ffdown_w8a8", "svdq_gateup", "svdq_gateup_fp6"):
         assert bench.load_traffic(wl) is not None, wl
 
 
