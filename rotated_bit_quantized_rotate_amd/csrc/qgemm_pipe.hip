@@ -324,7 +324,8 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
     if (pos < 2 * C::BM) {
       const int kk = pos / C::BM, rem = pos % C::BM;
       const int wv = rem / C::WM, u = rem % C::WM;
-      const int row = wv * C::WM + (u % C::FI) * 16 + u / C::FI;
+      // u = 64 f + 4 l16 + q holds the scale of fragment 4 f + q, lane row l16
+      const int row = wv * C::WM + (4 * (u / 64) + u % 4) * 16 + (u % 64) / 4;
       const int64_t gr = m0 + row > p.M - 1 ? p.M - 1 : m0 + row;
       e = gr * p.kg + kk;
     } else if (pos < 2 * (C::BM + C::BN)) {
@@ -412,8 +413,10 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   const int a6_lo = a_row * 96 + (swz6(a_row, 4 + (lg >> 1)) << 4) + 8 * (lg & 1);
   const int w6_hi = w_row * 96 + (swz6(w_row, lg) << 4);
   const int w6_lo = w_row * 96 + (swz6(w_row, 4 + (lg >> 1)) << 4) + 8 * (lg & 1);
-  // group scales: byte offsets inside the stage's scale block
-  const int sa_off = (wm * C::WM + l16 * C::FI) * 4;
+  // group scales: byte offsets inside the stage's scale block.  A lane reads
+  // the scales of its fragments 4f .. 4f+3 as one b128 at 64 f + 4 l16, so
+  // the 16 lanes of a read sit at a 16-byte stride (no bank conflicts).
+  const int sa_off = (wm * C::WM + l16 * 4) * 4;
   const int sw_off = (2 * C::BM + wn * C::WN + 4 * lg) * 4;
 
   // Staged epilogue: the tile's row factors (s_a * post) and column factors
@@ -517,7 +520,7 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
           for (int f = 0; f < C::FI / 4; ++f)
-            sav6[kk][f] = *reinterpret_cast<const v4f*>(Ss + sa_off + (kk * C::BM + 4 * f) * 4);
+            sav6[kk][f] = *reinterpret_cast<const v4f*>(Ss + sa_off + (kk * C::BM + 64 * f) * 4);
 #pragma unroll
           for (int j = 0; j < C::FJ; ++j)
             swv6[kk][j] = *reinterpret_cast<const v4f*>(Ss + sw_off + (kk * C::BN + j * 16) * 4);
@@ -671,7 +674,7 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
             // columns in each fragment
 #pragma unroll
             for (int f = 0; f < C::FI / 4; ++f)
-              sav[f] = *reinterpret_cast<const v4f*>(Ss + sa_off + (kk * C::BM + 4 * f) * 4);
+              sav[f] = *reinterpret_cast<const v4f*>(Ss + sa_off + (kk * C::BM + 64 * f) * 4);
 #pragma unroll
             for (int j = 0; j < C::FJ; ++j)
               swv[j] = *reinterpret_cast<const v4f*>(Ss + sw_off + (kk * C::BN + j * 16) * 4);
