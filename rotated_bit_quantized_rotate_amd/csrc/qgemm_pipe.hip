@@ -1180,10 +1180,10 @@ int launch_qgemm(const GemmArgs& g, hipStream_t s) {
     if (group && g.fp6) {
       e = launch_lowrank<Cfg<256, 128, 2, 4, true, true, true, true>>(p, g.epilogue, s);
     } else if (group) {
-      // 192 x 256 tiles with 12 waves: 158 VGPRs leave room for three waves
-      // per SIMD, whose interleaving the MFMA -> rescale chains need
-      e = g.a_packed ? launch_lowrank<Cfg<192, 256, 3, 4, true, true, true>>(p, g.epilogue, s)
-                     : launch_lowrank<Cfg<192, 256, 3, 4, false, true, true>>(p, g.epilogue, s);
+      // 256 x 128 tiles with 16 waves (64 x 32 wave tiles, under 128 VGPRs):
+      // four waves per SIMD interleave the MFMA -> rescale chains
+      e = g.a_packed ? launch_lowrank<Cfg<256, 128, 4, 4, true, true, true>>(p, g.epilogue, s)
+                     : launch_lowrank<Cfg<256, 128, 4, 4, false, true, true>>(p, g.epilogue, s);
     } else {
       e = g.a_packed ? launch_lowrank<Cfg<256, 256, 2, 4, true, true>>(p, g.epilogue, s)
                      : launch_lowrank<Cfg<256, 256, 2, 4, false, true>>(p, g.epilogue, s);
