@@ -11,8 +11,9 @@ The oracle is plain NumPy: bf16 inputs are widened exactly to float64, the
 rotation is an explicit matrix product with the closed-form 256x256 regular
 Hadamard matrix, the integer contraction is exact, and the epilogues run in
 float64 before one round-to-nearest-even cast to bfloat16.  The quantization
-decision (absmax -> scale -> code) is taken in float32, the precision the
-kernels take it in, from the exactly rotated value rounded once to float32.
+follows its definition in float64: absmax of the exactly rotated values,
+scale = absmax / qmax rounded once to float32, code = round-half-even of
+x' * qmax / absmax.
 
 Sources (web pages; cited by title and section):
   [OrbitQuant]  model card "Krea 2 Turbo OrbitQuant W4A4" -- sections

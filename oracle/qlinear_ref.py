@@ -17,7 +17,7 @@ __all__ = [
     "GROUP", "QMAX", "SCALE_MODES",
     "bf16_bits_to_f64", "f64_to_bf16_bits", "bf16_round",
     "regular_hadamard_256", "rotate",
-    "quantize", "dequantize",
+    "quantize", "code_ratio", "dequantize",
     "pack_int4", "unpack_int4",
     "fp6_e2m3_value", "fp6_e2m3_encode", "pack_fp6", "unpack_fp6",
     "int_gemm", "int_gemm_grouped",
@@ -115,16 +115,16 @@ def rotate(x: np.ndarray) -> np.ndarray:
 # [NunchakuLite] introduction: INT4 with group size 64).
 # --------------------------------------------------------------------------
 
-def _units(x32: np.ndarray, mode: str) -> np.ndarray:
-    R, K = x32.shape
+def _units(x: np.ndarray, mode: str) -> np.ndarray:
+    R, K = x.shape
     if mode == "tensor":
-        return x32.reshape(1, R * K)
+        return x.reshape(1, R * K)
     if mode == "row":
-        return x32.reshape(R, K)
+        return x.reshape(R, K)
     if mode == "group64":
         if K % 64:
             raise ValueError("group64 needs K % 64 == 0")
-        return x32.reshape(R * (K // 64), 64)
+        return x.reshape(R * (K // 64), 64)
     raise ValueError(f"unknown scale mode {mode!r}")
 
 
@@ -132,32 +132,53 @@ def _scale_shape(R: int, K: int, mode: str):
     return {"tensor": (1,), "row": (R,), "group64": (R, K // 64)}[mode]
 
 
+def _f32_quotient(a: np.ndarray, qmax: int) -> np.ndarray:
+    """a / qmax rounded once to float32 (round half to even), for float64 a.
+
+    The float64 quotient, cast to float32, is that correctly rounded value:
+    double rounding could differ only if the float64 rounding moved an
+    inexact quotient onto a float32 midpoint.  It cannot: a is a multiple of
+    its float64 ulp u_a, a midpoint m is a multiple of a much larger power of
+    two, so a nonzero a - qmax m is at least u_a and the quotient misses m by
+    at least u_a / qmax, which (qmax = 7 or 127, just below a power of two)
+    exceeds half a float64 ulp of the quotient."""
+    return (np.asarray(a, dtype=np.float64) / qmax).astype(np.float32)
+
+
+def code_ratio(xr: np.ndarray, bits: int, mode: str) -> np.ndarray:
+    """The unrounded code t = x' * qmax / a of every element of xr [R, K]
+    (already rotated values), a = max |x'| over the element's unit (whole
+    tensor, one row, or one row x 64-channel group), in float64; 0 where the
+    unit is all zero.  The code is rne(t) (see quantize)."""
+    qmax = QMAX[bits]
+    R, K = xr.shape
+    x = np.asarray(xr, dtype=np.float64)
+    u = _units(x, mode)
+    a = np.abs(u).max(axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.where(a[:, None] > 0, u * qmax / a[:, None], 0.0)
+    return t.reshape(R, K)
+
+
 def quantize(xr: np.ndarray, bits: int, mode: str):
     """Dynamic symmetric quantization of (already rotated) values xr [R, K].
 
     Per unit (whole tensor, one row, or one row x 64-channel group):
-      a     = max |x|                          (absmax of the unit)
-      s     = a / qmax                         (scale, float32)
-      q     = clamp(rne(x * (qmax / a)), +-qmax)   (code; 0 when a == 0)
+      a     = max |x'|                              (absmax of the unit)
+      s     = a / qmax, rounded once to float32     (the stored scale)
+      q     = clamp(rne(x' * qmax / a), +-qmax)     (the code; 0 when a == 0)
     with qmax = 7 (int4) or 127 (int8), round-half-to-even, and -qmax-1 never
-    produced.  The decision -- absmax, reciprocal, product, rounding -- is
-    taken in float32 (the kernels' precision) from x rounded once to
-    float32; each float32 operation is formed exactly in float64 and rounded
-    once, i.e. correctly rounded float32 arithmetic.
+    produced.  Everything before the float32 scale is float64: the rotated
+    values are exact, a is exact, and x' * qmax / a is the float64 quotient.
 
     Returns (codes int8 [R, K], scales float32 of shape [1] | [R] | [R, K/64])."""
     qmax = QMAX[bits]
     R, K = xr.shape
-    x32 = np.asarray(xr, dtype=np.float64).astype(np.float32)
-    u = _units(x32, mode)
-    a = np.abs(u).max(axis=1)                                     # float32
-    a64 = a.astype(np.float64)
-    scale = (a64 / qmax).astype(np.float32)
-    with np.errstate(divide="ignore"):
-        inv = np.where(a > 0, (qmax / a64).astype(np.float32), np.float32(0.0))
-    prod = (u.astype(np.float64) * inv.astype(np.float64)[:, None]).astype(np.float32)
-    q = np.clip(np.rint(prod), -qmax, qmax).astype(np.int8)
-    return q.reshape(R, K), scale.reshape(_scale_shape(R, K, mode))
+    u = _units(np.asarray(xr, dtype=np.float64), mode)
+    a = np.abs(u).max(axis=1)
+    scale = _f32_quotient(a, qmax)
+    q = np.clip(np.rint(code_ratio(xr, bits, mode)), -qmax, qmax).astype(np.int8)
+    return q, scale.reshape(_scale_shape(R, K, mode))
 
 
 def _expand_scale(scale: np.ndarray, R: int, K: int, mode: str) -> np.ndarray:

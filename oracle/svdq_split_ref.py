@@ -86,13 +86,14 @@ class SplitResult:
     """Best split of svdq_split: branch factors as bf16 bits, the residual's
     quantization, the objective of every iteration and the best index."""
 
-    def __init__(self, l1_bits, l2_bits, quant, errors, best, sigma):
+    def __init__(self, l1_bits, l2_bits, quant, errors, best, sigma, history):
         self.l1_bits = l1_bits      # uint16 [K, r]
         self.l2_bits = l2_bits      # uint16 [r, N]
         self.quant = quant          # QuantResult of the residual (codes, scales)
         self.errors = errors        # float64 [iterations]
         self.best = best            # index of the returned iteration
         self.sigma = sigma          # float64 [r] singular values of the best iteration's fit
+        self.history = history      # per iteration: (l1_bits, l2_bits, QuantResult of its residual)
 
 
 def svdq_split(w_bits, omega, rank: int, power_iters: int = 2, refine_iters: int = 0,
@@ -105,6 +106,7 @@ def svdq_split(w_bits, omega, rank: int, power_iters: int = 2, refine_iters: int
     d = np.ones(K) if act_rms is None else act_weights(act_rms)
     E = np.zeros_like(W)                      # unrotate(deq(Q)) of the previous iteration
     errors = []
+    history = []
     best = None
     for t in range(refine_iters + 1):
         L1, L2, s = svdq_branch(W - E, d, omega, rank, power_iters)
@@ -113,7 +115,8 @@ def svdq_split(w_bits, omega, rank: int, power_iters: int = 2, refine_iters: int
         E = rotate(dequantize(q.codes, q.scales, scale_mode))   # Hn is its own inverse
         err = float(np.linalg.norm((T - E) * d[None, :]))
         errors.append(err)
+        history.append((f64_to_bf16_bits(L1), f64_to_bf16_bits(L2), q))
         if best is None or err < errors[best[0]]:
             best = (t, L1, L2, q, s)
     t, L1, L2, q, s = best
-    return SplitResult(f64_to_bf16_bits(L1), f64_to_bf16_bits(L2), q, np.array(errors), t, s)
+    return SplitResult(f64_to_bf16_bits(L1), f64_to_bf16_bits(L2), q, np.array(errors), t, s, history)

@@ -115,7 +115,7 @@ def test_quantizer_error_bound_range_and_sign(bits, mode):
     qmax = O.QMAX[bits]
     deq = O.dequantize(q, s, mode)
     smat = O.dequantize(np.ones_like(q), s, mode)
-    # |x - s q| <= s/2 up to float32 rounding of x and of the reciprocal.
+    # |x - s q| <= s/2 up to the float32 rounding of the scale.
     assert (np.abs(xr - deq) <= smat * (0.5 + 1e-5) + 1e-30).all()
     assert np.abs(q).max() <= qmax
     # Each unit's absmax maps to +-qmax exactly.
@@ -141,6 +141,52 @@ def test_quantizer_scale_is_float32_absmax_over_qmax():
     q, s = O.quantize(x, 8, "row")
     assert s.dtype == np.float32 and s[0] == np.float32(3.0 / 127)
     assert q[0, 3] == -127
+
+
+def test_code_is_float64_quotient_not_float32_reciprocal_product():
+    """The code is round-half-even of the quotient x' * qmax / a.  Here
+    x' * 7 / 1 = 3.5 - 2^-28 exactly up to float64 rounding, which lies
+    below the tie, so the code is 3.  Rounding x' to float32 first (it
+    becomes 0.5) and multiplying by a float32 reciprocal gives exactly 3.5,
+    which ties to the even 4: the two recipes part at this near-tie, and the
+    definition decides."""
+    t = (3.5 - 2.0 ** -28) / 7.0
+    x = np.array([[1.0, t, -t, 0.0] + [0.0] * 60])
+    q, s = O.quantize(x, 4, "row")
+    assert q[0, :4].tolist() == [7, 3, -3, 0]
+    assert s[0] == np.float32(1.0 / 7.0)
+    f32 = np.rint(np.float32(t) * np.float32(7.0))   # the float32 recipe lands on the tie
+    assert f32 == 4.0
+    assert np.allclose(O.code_ratio(x, 4, "row")[0, :3], [7.0, 3.5 - 2.0 ** -28, -(3.5 - 2.0 ** -28)],
+                       rtol=0, atol=1e-15)
+
+
+def test_scale_is_the_correctly_rounded_float32_quotient():
+    """s = a / qmax rounded once to float32, checked against exact rational
+    arithmetic (round half to even on the exact quotient), including an
+    exact float32 midpoint and random float64 absmax values."""
+    from fractions import Fraction
+
+    def exact_f32(a, qmax):
+        v = Fraction(a) / qmax
+        f = np.float32(float(v))
+        cands = sorted({f, np.nextafter(f, np.float32(-np.inf)), np.nextafter(f, np.float32(np.inf))},
+                       key=lambda c: (abs(Fraction(float(c)) - v), int(np.float32(c).view(np.uint32)) & 1))
+        return cands[0]
+
+    rng = np.random.default_rng(12)
+    vals = list(np.ldexp(rng.random(400) + 0.5, rng.integers(-30, 30, 400)))
+    vals += [7.0 * (1.0 + 2.0 ** -24), 127.0 * (1.0 + 3 * 2.0 ** -24), 7.0, 127.0 * 2.0 ** -20]
+    for qmax in (7, 127):
+        for a in vals:
+            x = np.zeros((1, 64))
+            x[0, 5] = a
+            _, s = O.quantize(x, 4 if qmax == 7 else 8, "row")
+            assert s[0] == exact_f32(a, qmax), (a, qmax)
+    # a / 7 = 1 + 2^-24 exactly: a float32 midpoint, which rounds to the even 1.0
+    x = np.zeros((1, 64))
+    x[0, 0] = 7.0 * (1.0 + 2.0 ** -24)
+    assert O.quantize(x, 4, "row")[1][0] == np.float32(1.0)
 
 
 def test_rotation_lowers_outlier_quantization_error():

@@ -110,6 +110,40 @@ def test_refinement_keeps_the_best_and_never_does_worse():
         assert np.array_equal(ref.quant.codes, plain.quant.codes)
 
 
+def test_refinement_refits_to_the_previous_iterate_not_the_best():
+    """Iteration t > 1 fits the branch to W - unrotate(deq(Q_{t-1})), the
+    iterate just before it, even when an earlier one was better.  On this
+    weight (tensor scales) iteration 4 is worse than iteration 3, so the
+    readings "from the previous iterate" and "from the best so far" part
+    ways from iteration 5 on (index 4).  The sketch has as many columns as W
+    has rows and no power steps are needed: its range is W's whole column
+    space, so every fit is the exact truncated SVD, rebuilt here with
+    numpy's full SVD."""
+    N, K, r = 64, 256, 4
+    wb = W.normal_bf16(np.random.default_rng(2), (N, K), 0.02)
+    res = O.svdq_split(wb, W.gaussian_sketch(K, N, 102), r, 0, 6, "tensor")
+    Wf = O.bf16_bits_to_f64(wb)
+
+    def fit_to(t):
+        q = res.history[t][2]
+        U, s, Vt = np.linalg.svd(Wf - O.rotate(O.dequantize(q.codes, q.scales, "tensor")), full_matrices=False)
+        return (U[:, :r] * s[:r]) @ Vt[:r]
+
+    parted = 0
+    for t in range(1, 7):
+        l1, l2, _ = res.history[t]
+        got = (O.bf16_bits_to_f64(l1) @ O.bf16_bits_to_f64(l2)).T
+        want = fit_to(t - 1)
+        scale = np.abs(want).max()
+        assert np.abs(got - want).max() <= 1e-2 * scale, t          # bf16 factors: ~0.5 %
+        best_before = int(np.argmin(res.errors[:t]))
+        if best_before != t - 1:
+            parted += 1
+            assert np.abs(got - fit_to(best_before)).max() > 3e-2 * scale, t
+    assert parted >= 2   # the case really separates the two readings
+    assert res.best == int(np.argmin(res.errors))
+
+
 def test_zero_weight_and_constant_act_stats():
     N, K, r = 32, 256, 16
     zero = np.zeros((N, K), dtype=np.uint16)
