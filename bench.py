@@ -461,8 +461,9 @@ def case_svdq(Q, W, dev, fp6=False):
     c.launches = [
         ("prologue", lambda: Q.rotate_quantize_act(x, bits=4, scale_mode="group64", layout=layout, codes=codes,
                                                    scales=sa, l1=l1, lr=lr)),
-        ("gemm", lambda: Q.qgemm_w4a4_lowrank(codes, sa, wq, sw, K, lr=lr, l2=l2, a_layout=layout,
-                                              epilogue="swiglu", out=out)),
+        ("gemm", (lambda: Q.qgemm_w4a4_fp6_lowrank(codes, sa, wq, sw, K, lr=lr, l2=l2, epilogue="swiglu",
+                                                   out=out)) if fp6 else
+                 (lambda: Q.qgemm_w4a4_lowrank(codes, sa, wq, sw, K, lr=lr, l2=l2, epilogue="swiglu", out=out))),
     ]
     c.ops = wl.int_ops
     c.gemm_launches = 1

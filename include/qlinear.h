@@ -49,6 +49,14 @@
  *  - GEMM size limits (the kernels address operands with 32-bit offsets):
  *    K < 2^23, N * K < 2^31 and M * K < 2^36.  Violations return
  *    QL_ERR_SHAPE.
+ *  - Exactness of the int32 accumulator (tensor / row scales): it sums K
+ *    products of codes, each at most qmax_a * qmax_w and 16 times larger per
+ *    packed INT4 operand (packed codes enter the int8 instruction as
+ *    16 * code).  Every call whose sum could reach 2^31 returns QL_ERR_SHAPE
+ *    before launching: W8A8 K > 133144 (127 * 127 * K), W4A4 with int8-
+ *    container activations K > 2739137 (7 * 112 * K), W4A4 with packed
+ *    activations K > 171196 (112 * 112 * K).  Group-64 partials span 64
+ *    channels and are never at risk.
  */
 #ifndef QLINEAR_H
 #define QLINEAR_H
@@ -184,11 +192,11 @@ int pack_weight_int4(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
                      int scale_mode, int rotate, uint8_t* packed, float* scales,
                      void* stream);
 
-/* Offline INT4 weight preparation for the FP6 GEMM (qgemm_w4a4_fp6): the
- * same codes and scales as pack_weight_int4, stored in QL_LAYOUT_FP6;
- * equal to rotate_quantize_act(w, N, K, ldw, 4, scale_mode, QL_LAYOUT_FP6,
- * rotate, ...).  scale_mode TENSOR | ROW | GROUP64 (GROUP64 weights go to
- * qgemm_w4a4_fp6 or qgemm_w4a4_lowrank with a_layout QL_LAYOUT_FP6).
+/* Offline INT4 weight preparation for the FP6 GEMMs (qgemm_w4a4_fp6,
+ * qgemm_w4a4_fp6_lowrank): the same codes and scales as pack_weight_int4,
+ * stored in QL_LAYOUT_FP6; equal to rotate_quantize_act(w, N, K, ldw, 4,
+ * scale_mode, QL_LAYOUT_FP6, rotate, ...).  scale_mode TENSOR | ROW |
+ * GROUP64.
  *   packed out: [N, 3K/4] bytes in the QL_LAYOUT_FP6 order                 */
 int pack_weight_fp6(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
                     int scale_mode, int rotate, uint8_t* packed, float* scales,
@@ -205,7 +213,9 @@ int pack_weight_fp6(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
  *   epilogue QL_EPI_BF16 | QL_EPI_F32 | QL_EPI_I32 (I32 ignores scales and bias) |
  *            QL_EPI_SIGMOID (tensor / row scales; the attention gate)
  *   out      [M, N] bf16 / float32 / int32, row stride ldo (elements)
- * Group-64 scales go through qgemm_w4a4_lowrank (with rank 0). */
+ *   a_layout QL_LAYOUT_I8 | QL_LAYOUT_PACKED (else QL_ERR_UNSUPPORTED)
+ * Group-64 scales (both sides, BF16 | F32 only) run qgemm_w4a4_lowrank with
+ * rank 0. */
 int qgemm_w4a4(const void* a, const float* sa, int a_scale_mode, int a_layout,
                const uint8_t* w, const float* sw, int w_scale_mode,
                int64_t M, int64_t N, int64_t K,
@@ -264,10 +274,8 @@ int qgemm_w8a8(const int8_t* a, const float* sa, int a_scale_mode,
  * OrbitQuant W4A4", section "Fused transformer": SwiGLU gate|up GEMM).
  *   a, sa, a_scale_mode, a_layout, w, sw, w_scale_mode   as qgemm_w4a4, and
  *             GROUP64 is allowed only on both sides at once; a_layout
- *             QL_LAYOUT_FP6 (GROUP64 only) takes both a and w in the FP6
- *             layout ([M, 3K/4] and [N, 3K/4], from pack_weight_fp6) and runs
- *             the group-64 FP6 kernel of qgemm_w4a4_fp6, bit-identical to the
- *             INT8 path
+ *             QL_LAYOUT_I8 | QL_LAYOUT_PACKED (the FP6 experiment has its
+ *             own entry point, qgemm_w4a4_fp6_lowrank)
  *   lr        bf16 [M, rank] (from rotate_quantize_act), dense rows
  *   l2        bf16 [rank, N], dense rows
  *   rank      0 (no branch; lr, l2 may be NULL) or a multiple of 16, <= 128
@@ -281,6 +289,25 @@ int qgemm_w4a4_lowrank(const void* a, const float* sa, int a_scale_mode, int a_l
                        int64_t M, int64_t N, int64_t K,
                        const uint16_t* bias, int epilogue, void* out, int64_t ldo,
                        void* stream);
+
+/* The group-64 low-rank GEMM of qgemm_w4a4_lowrank on the FP6 matrix
+ * instructions -- the experiment beside the int8 path (model card "Krea 2
+ * Turbo Nunchaku Lite INT4 r32", section "Benchmark": the same checkpoint as
+ * an FP4 build on a GPU whose matrix units take it natively).  Both operands
+ * hold the int4 codes in QL_LAYOUT_FP6 (a [M, 3K/4] from the prologues with
+ * layout QL_LAYOUT_FP6, w [N, 3K/4] from pack_weight_fp6), with group-64
+ * scales on both sides (sa [M, K/64], sw [N, K/64]).  Each FP6 instruction
+ * runs once per 64-channel group with the other group's weight lanes zeroed;
+ * its fp32 result is the group's exact partial and is rescaled exactly as
+ * the INT8 path does, so the output equals qgemm_w4a4_lowrank's with group-64
+ * scales bit for bit.
+ *   lr, l2, rank, bias, out, ldo   as qgemm_w4a4_lowrank
+ *   epilogue  QL_EPI_BF16 | QL_EPI_SWIGLU | QL_EPI_F32 */
+int qgemm_w4a4_fp6_lowrank(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
+                           const uint16_t* lr, const uint16_t* l2, int rank,
+                           int64_t M, int64_t N, int64_t K,
+                           const uint16_t* bias, int epilogue, void* out, int64_t ldo,
+                           void* stream);
 
 /* One projection of a grouped GEMM. */
 typedef struct {

@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     qgemm_grouped,
     qgemm_w4a4,
     qgemm_w4a4_fp6,
+    qgemm_w4a4_fp6_lowrank,
     qgemm_w4a4_lowrank,
     qgemm_w8a8,
     rmsnorm_rotate_quantize_act,

@@ -68,6 +68,7 @@ _SIGNATURES = {
     "qgemm_w8a8": (_i, [_p, _p, _i, _p, _p, _i, _i64, _i64, _i64, _p, _p, _p, _i, _p, _i64, _p]),
     "qgemm_w4a4_lowrank": (_i, [_p, _p, _i, _i, _p, _p, _i, _p, _p, _i, _i64, _i64, _i64, _p, _i, _p,
                                 _i64, _p]),
+    "qgemm_w4a4_fp6_lowrank": (_i, [_p, _p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _p, _i, _p, _i64, _p]),
     "qgemm_grouped": (_i, [_p, _p, _p, _p, _i64, _i64, ctypes.POINTER(Segment), _i, _p]),
     "svdq_split": (_i, [_p, _i64, _i64, _i64, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _i64,
                         _p]),
@@ -275,9 +276,8 @@ def qgemm_w8a8(a, sa, w, sw, a_scale_mode="row", w_scale_mode="row", bias=None, 
 def qgemm_w4a4_lowrank(a, sa, w, sw, K, lr=None, l2=None, a_scale_mode="group64",
                        w_scale_mode="group64", a_layout="i8", bias=None, epilogue="swiglu", out=None,
                        stream=None):
-    """Group-64 (or row) W4A4 GEMM + optional low-rank branch lr @ l2 + epilogue.
-    a_layout "fp6" (group-64 only): a and w both in the FP6 layout, run on the
-    FP6 matrix instruction with the same result."""
+    """Group-64 (or row / tensor) W4A4 GEMM + optional low-rank branch
+    lr @ l2 + epilogue; a_layout "i8" or "packed"."""
     M = a.shape[0]
     N = w.shape[0]
     epi = _epi(epilogue)
@@ -287,6 +287,22 @@ def qgemm_w4a4_lowrank(a, sa, w, sw, K, lr=None, l2=None, a_scale_mode="group64"
                                   _ptr(sw), _mode(w_scale_mode), _ptr(lr), _ptr(l2), rank, M, N, K,
                                   _ptr(bias), epi, _ptr(out), out.stride(0), _stream(stream))
     _check("qgemm_w4a4_lowrank", st)
+    return out
+
+
+def qgemm_w4a4_fp6_lowrank(a, sa, w, sw, K, lr=None, l2=None, bias=None, epilogue="swiglu", out=None,
+                           stream=None):
+    """The group-64 low-rank GEMM on the FP6 matrix instruction: a [M, 3K/4]
+    and w [N, 3K/4] in the FP6 layout, sa [M, K/64], sw [N, K/64]; same
+    result as qgemm_w4a4_lowrank on the same codes."""
+    M = a.shape[0]
+    N = w.shape[0]
+    epi = _epi(epilogue)
+    rank = 0 if l2 is None else l2.shape[0]
+    out = _out(out, M, N // 2 if epi == QL_EPI_SWIGLU else N, epi, a.device)
+    st = lib().qgemm_w4a4_fp6_lowrank(_ptr(a), _ptr(sa), _ptr(w), _ptr(sw), _ptr(lr), _ptr(l2), rank, M, N, K,
+                                      _ptr(bias), epi, _ptr(out), out.stride(0), _stream(stream))
+    _check("qgemm_w4a4_fp6_lowrank", st)
     return out
 
 

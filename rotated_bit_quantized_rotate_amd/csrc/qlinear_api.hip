@@ -40,6 +40,16 @@ inline bool al2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) ==
 
 inline bool valid_mode(int m) { return m == QL_SCALE_TENSOR || m == QL_SCALE_ROW || m == QL_SCALE_GROUP64; }
 
+// The int32 accumulator of a tensor / row-scale GEMM holds K products of
+// codes; the largest product is qmax_a * qmax_w times 16 per packed INT4
+// operand (its codes enter the int8 instruction as 16 * code).  The sum is
+// exact only while K times that stays below 2^31.  Group-64 partials cover 64
+// channels and never overflow.
+inline bool acc_fits(int64_t K, int64_t max_product) { return K * max_product <= INT32_MAX; }
+constexpr int64_t kProdW8A8 = 127 * 127;          // K <= 133144
+constexpr int64_t kProdW4A4I8 = 7 * (16 * 7);     // int8-container codes x packed W: K <= 2739137
+constexpr int64_t kProdW4A4P = (16 * 7) * (16 * 7);  // both packed: K <= 171196
+
 }  // namespace
 
 extern "C" {
@@ -157,18 +167,21 @@ static int validate_gemm_common(const void* a, const float* sa, const void* w, c
 int qgemm_w4a4(const void* a, const float* sa, int a_scale_mode, int a_layout, const uint8_t* w,
                const float* sw, int w_scale_mode, int64_t M, int64_t N, int64_t K, const uint16_t* bias,
                int epilogue, void* out, int64_t ldo, void* stream) {
+  if (!valid_mode(a_scale_mode) || !valid_mode(w_scale_mode)) return QL_ERR_UNSUPPORTED;
+  if (a_layout != QL_LAYOUT_I8 && a_layout != QL_LAYOUT_PACKED) return QL_ERR_UNSUPPORTED;
   if (a_scale_mode == QL_SCALE_GROUP64 || w_scale_mode == QL_SCALE_GROUP64) {
     if (a_scale_mode != QL_SCALE_GROUP64 || w_scale_mode != QL_SCALE_GROUP64) return QL_ERR_UNSUPPORTED;
-    if (epilogue == QL_EPI_I32) return QL_ERR_UNSUPPORTED;
+    // group partials are rescaled in fp32: no exact I32 result, and the
+    // sigmoid gate / SwiGLU are not offered here
+    if (epilogue != QL_EPI_BF16 && epilogue != QL_EPI_F32) return QL_ERR_UNSUPPORTED;
     return qgemm_w4a4_lowrank(a, sa, a_scale_mode, a_layout, w, sw, w_scale_mode, nullptr, nullptr, 0, M,
                               N, K, bias, epilogue, out, ldo, stream);
   }
-  if (!valid_mode(a_scale_mode) || !valid_mode(w_scale_mode)) return QL_ERR_UNSUPPORTED;
-  if (a_layout != QL_LAYOUT_I8 && a_layout != QL_LAYOUT_PACKED) return QL_ERR_UNSUPPORTED;
   if (epilogue != QL_EPI_BF16 && epilogue != QL_EPI_F32 && epilogue != QL_EPI_I32 && epilogue != QL_EPI_SIGMOID)
     return QL_ERR_UNSUPPORTED;
   int st = validate_gemm_common(a, sa, w, sw, M, N, K, bias, out, ldo, epilogue);
   if (st != QL_OK) return st;
+  if (!acc_fits(K, a_layout == QL_LAYOUT_PACKED ? kProdW4A4P : kProdW4A4I8)) return QL_ERR_SHAPE;
   if ((st = check_current_device()) != QL_OK) return st;
   if (M == 0) return QL_OK;
   ql::GemmArgs g{};
@@ -237,6 +250,7 @@ int qgemm_w8a8(const int8_t* a, const float* sa, int a_scale_mode, const int8_t*
     return QL_ERR_UNSUPPORTED;
   int st = validate_gemm_common(a, sa, w, sw, M, N, K, bias, out, ldo, epilogue);
   if (st != QL_OK) return st;
+  if (!acc_fits(K, kProdW8A8)) return QL_ERR_SHAPE;
   if (epilogue == QL_EPI_GATED_RESIDUAL) {
     if (M > 0 && (!residual || !gate)) return QL_ERR_NULL;
     if (!al16(residual) || !al2(gate)) return QL_ERR_ALIGN;
@@ -264,20 +278,19 @@ int qgemm_w8a8(const int8_t* a, const float* sa, int a_scale_mode, const int8_t*
   return ql::launch_qgemm(g, static_cast<hipStream_t>(stream)) == QL_OK ? QL_OK : QL_ERR_LAUNCH;
 }
 
-int qgemm_w4a4_lowrank(const void* a, const float* sa, int a_scale_mode, int a_layout, const uint8_t* w,
-                       const float* sw, int w_scale_mode, const uint16_t* lr, const uint16_t* l2, int rank,
-                       int64_t M, int64_t N, int64_t K, const uint16_t* bias, int epilogue, void* out,
-                       int64_t ldo, void* stream) {
-  if (!valid_mode(a_scale_mode) || !valid_mode(w_scale_mode)) return QL_ERR_UNSUPPORTED;
-  if ((a_scale_mode == QL_SCALE_GROUP64) != (w_scale_mode == QL_SCALE_GROUP64)) return QL_ERR_UNSUPPORTED;
-  if (a_layout != QL_LAYOUT_I8 && a_layout != QL_LAYOUT_PACKED && a_layout != QL_LAYOUT_FP6)
-    return QL_ERR_UNSUPPORTED;
-  // FP6 operands (both sides) come with group-64 scales here
-  if (a_layout == QL_LAYOUT_FP6 && a_scale_mode != QL_SCALE_GROUP64) return QL_ERR_UNSUPPORTED;
+// The low-rank GEMM on INT4 codes (fp6 == 0) or on FP6 codes with group-64
+// scales (fp6 == 1); both entry points below validate their own layouts.
+static int lowrank_gemm(const void* a, const float* sa, int a_scale_mode, int a_layout, const uint8_t* w,
+                        const float* sw, int w_scale_mode, const uint16_t* lr, const uint16_t* l2, int rank,
+                        int64_t M, int64_t N, int64_t K, const uint16_t* bias, int epilogue, void* out,
+                        int64_t ldo, void* stream, int fp6) {
   if (epilogue != QL_EPI_BF16 && epilogue != QL_EPI_SWIGLU && epilogue != QL_EPI_F32) return QL_ERR_UNSUPPORTED;
   if (epilogue == QL_EPI_SWIGLU && N % 32 != 0) return QL_ERR_SHAPE;
   int st = validate_gemm_common(a, sa, w, sw, M, N, K, bias, out, ldo, epilogue);
   if (st != QL_OK) return st;
+  // tensor / row scales keep one int32 accumulator over K
+  if (a_scale_mode != QL_SCALE_GROUP64 && !acc_fits(K, a_layout == QL_LAYOUT_PACKED ? kProdW4A4P : kProdW4A4I8))
+    return QL_ERR_SHAPE;
   if (rank < 0 || rank > 128 || rank % 16 != 0) return QL_ERR_SHAPE;
   if (rank > 0) {
     if (M > 0 && (!lr || !l2)) return QL_ERR_NULL;
@@ -295,7 +308,7 @@ int qgemm_w4a4_lowrank(const void* a, const float* sa, int a_scale_mode, int a_l
   g.K = K;
   g.a_packed = a_layout == QL_LAYOUT_PACKED;
   g.w_packed = 1;
-  g.fp6 = a_layout == QL_LAYOUT_FP6;
+  g.fp6 = fp6;
   g.a_mode = a_scale_mode;
   g.w_mode = w_scale_mode;
   g.bias = bias;
@@ -306,6 +319,24 @@ int qgemm_w4a4_lowrank(const void* a, const float* sa, int a_scale_mode, int a_l
   g.out = out;
   g.ldo = ldo;
   return ql::launch_qgemm(g, static_cast<hipStream_t>(stream)) == QL_OK ? QL_OK : QL_ERR_LAUNCH;
+}
+
+int qgemm_w4a4_lowrank(const void* a, const float* sa, int a_scale_mode, int a_layout, const uint8_t* w,
+                       const float* sw, int w_scale_mode, const uint16_t* lr, const uint16_t* l2, int rank,
+                       int64_t M, int64_t N, int64_t K, const uint16_t* bias, int epilogue, void* out,
+                       int64_t ldo, void* stream) {
+  if (!valid_mode(a_scale_mode) || !valid_mode(w_scale_mode)) return QL_ERR_UNSUPPORTED;
+  if ((a_scale_mode == QL_SCALE_GROUP64) != (w_scale_mode == QL_SCALE_GROUP64)) return QL_ERR_UNSUPPORTED;
+  if (a_layout != QL_LAYOUT_I8 && a_layout != QL_LAYOUT_PACKED) return QL_ERR_UNSUPPORTED;
+  return lowrank_gemm(a, sa, a_scale_mode, a_layout, w, sw, w_scale_mode, lr, l2, rank, M, N, K, bias, epilogue,
+                      out, ldo, stream, 0);
+}
+
+int qgemm_w4a4_fp6_lowrank(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
+                           const uint16_t* lr, const uint16_t* l2, int rank, int64_t M, int64_t N, int64_t K,
+                           const uint16_t* bias, int epilogue, void* out, int64_t ldo, void* stream) {
+  return lowrank_gemm(a, sa, QL_SCALE_GROUP64, QL_LAYOUT_FP6, w, sw, QL_SCALE_GROUP64, lr, l2, rank, M, N, K,
+                      bias, epilogue, out, ldo, stream, 1);
 }
 
 int qgemm_grouped(const void* a4, const float* sa4, const void* a8, const float* sa8, int64_t M, int64_t K,
@@ -320,6 +351,7 @@ int qgemm_grouped(const void* a4, const float* sa4, const void* a8, const float*
     if (sg.w_bits != 4 && sg.w_bits != 8) return QL_ERR_UNSUPPORTED;
     if (sg.epilogue != QL_EPI_BF16 && sg.epilogue != QL_EPI_SIGMOID) return QL_ERR_UNSUPPORTED;
     if (sg.n <= 0 || sg.n % 16 != 0 || sg.n * K >= (int64_t(1) << 31)) return QL_ERR_SHAPE;
+    if (!acc_fits(K, sg.w_bits == 8 ? kProdW8A8 : kProdW4A4I8)) return QL_ERR_SHAPE;
     if (sg.ldo < sg.n) return QL_ERR_SHAPE;
     if (M > 0 && (!sg.w || !sg.sw || !sg.out)) return QL_ERR_NULL;
     if (!al16(sg.w) || !al4(sg.sw) || !al16(sg.out) || (sg.ldo * 2) % 16 != 0) return QL_ERR_ALIGN;

@@ -19,7 +19,8 @@
 //
 // Quantization (per tensor, per row, or per row x 64-channel group):
 //   amax = max |z| over the unit,  inv = qmax / amax (correctly rounded fp32),
-//   code = rint(z * inv) (already within [-qmax, qmax]),  scale = amax / qmax (/16 if rotated).
+//   code = rint(z * inv) (already within [-qmax, qmax]),  scale = amax / qmax (/16 if rotated);
+//   unrotated bf16 inputs take the correctly rounded quotient rint((x * qmax) / amax).
 // A 64-channel group inside a 256-group is one value of d3, i.e. one quad of
 // lanes.
 
@@ -309,6 +310,14 @@ __global__ __launch_bounds__(kThreads) void rq_kernel(RqArgs a, int slots_per_ro
 
     // |z * inv| <= qmax (1 + 2^-23) since |z| <= amax, so the rounded code
     // never leaves [-qmax, qmax] and needs no clamp.
+    // Unrotated bf16 inputs: x * qmax is exact in fp32 (8 + 7 significant
+    // bits) and amax is a bf16 value, so the correctly rounded quotient
+    // (x * qmax) / amax rounds to the same code as the exact one: it is the
+    // exact k + 1/2 at a tie (which then goes to even), and otherwise lies more
+    // than 2^7 half-ulps from any tie.  A reciprocal product would break
+    // exact ties (x = 3, amax = 6) either way.  Rotated or normalized values
+    // carry the fp32 error of the butterflies anyway and keep the product.
+    const bool exact_in = !NORM && !a.rotate;
     const int64_t code_row = row * a.K;
 #pragma unroll
     for (int j = 0; j < GPL; ++j) {
@@ -317,8 +326,13 @@ __global__ __launch_bounds__(kThreads) void rq_kernel(RqArgs a, int slots_per_ro
       const float am = amax[j];
       const float inv = am > 0.0f ? __fdiv_rn(qmax, am) : 0.0f;
       uint32_t u[16];
+      if (exact_in) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) u[e] = code_bits(v[j][e], inv);
+        for (int e = 0; e < 16; ++e) u[e] = code_bits(am > 0.0f ? __fdiv_rn(v[j][e] * qmax, am) : 0.0f, 1.0f);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) u[e] = code_bits(v[j][e], inv);
+      }
       store_codes(a.codes, code_row + (int64_t)g * 256 + t * 16, a.packed, u);
       if (a.mode == 2) {
         if ((t & 3) == 0)

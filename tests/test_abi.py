@@ -20,7 +20,8 @@ def L():
 def test_header_declares_the_entry_points():
     fns = header_functions()
     for name in ["rotate_quantize_act", "rmsnorm_rotate_quantize_act", "pack_weight_int4", "pack_weight_fp6",
-                 "qgemm_w4a4", "qgemm_w4a4_fp6", "qgemm_w8a8", "qgemm_w4a4_lowrank", "qgemm_grouped",
+                 "qgemm_w4a4", "qgemm_w4a4_fp6", "qgemm_w8a8", "qgemm_w4a4_lowrank", "qgemm_w4a4_fp6_lowrank",
+                 "qgemm_grouped",
                  "svdq_split", "svdq_split_workspace_bytes", "ql_status_string", "ql_device_supported"]:
         assert name in fns
 
@@ -134,6 +135,17 @@ def test_qgemm_w4a4_validation(L):
     assert g44(L, sw=NULL) == -1
     assert g44(L, w=MISALIGNED) == -3
     assert g44(L, am=2, wm=2, epi=4) == -4        # exact int32 output needs one scale per product
+    # the layout and epilogue are checked before the group-64 scales forward
+    # to the low-rank GEMM: FP6 operands never reach the int4 kernels here
+    assert g44(L, am=2, wm=2, al=2) == -4
+    assert g44(L, am=2, wm=2, epi=1) == -4        # no SwiGLU through this entry
+    assert g44(L, am=2, wm=2, epi=5) == -4        # nor the sigmoid with group-64 scales
+    assert g44(L, am=2, wm=2) in (-4, -6)
+    # int32 accumulator overflow: K * max |product| must stay below 2^31
+    assert g44(L, K=2738944) in (-4, -6)          # int8-container codes: 7 * 112 * K
+    assert g44(L, K=2739200) == -2
+    assert g44(L, al=1, K=171008) in (-4, -6)     # packed activations: 112 * 112 * K
+    assert g44(L, al=1, K=171264) == -2
     # size limits of the 32-bit operand offsets
     assert g44(L, K=1 << 23, ldo=32) == -2
     assert g44(L, N=1 << 20, K=1 << 11, ldo=1 << 20) == -2   # N * K = 2^31
@@ -155,6 +167,8 @@ def test_qgemm_w8a8_validation(L):
     assert g88(L, epi=1) == -4
     assert g88(L, N=0) == -2
     assert g88(L, epi=2, res=MISALIGNED, gate=ALIGNED) == -3
+    assert g88(L, K=133120) in (-4, -6)           # 127 * 127 * K < 2^31
+    assert g88(L, K=133376) == -2
 
 
 def glr(L, **kw):
@@ -176,8 +190,34 @@ def test_qgemm_lowrank_validation(L):
     assert glr(L, epi=4) == -4
     assert glr(L, epi=2) == -4
     assert glr(L, al=3) == -4                     # no such layout
-    assert glr(L, al=2, am=1, wm=1) == -4         # FP6 operands here only with group-64 scales
-    assert glr(L, al=2) in (-4, -6)               # FP6 + group-64 reaches the device check
+    assert glr(L, al=2, am=1, wm=1) == -4         # no FP6 operands here ...
+    assert glr(L, al=2) == -4                     # ... with any scales (qgemm_w4a4_fp6_lowrank has them)
+    assert glr(L) in (-4, -6)
+    # row scales keep one int32 accumulator: the overflow bound applies
+    assert glr(L, am=1, wm=1, K=2738944, N=64) in (-4, -6)
+    assert glr(L, am=1, wm=1, K=2739200) == -2
+    assert glr(L, K=2739200) in (-4, -6)          # group-64 partials cannot overflow
+
+
+def g6lr(L, **kw):
+    a = dict(a=ALIGNED, sa=ALIGNED, w=ALIGNED, sw=ALIGNED, lr=ALIGNED, l2=ALIGNED, r=32, M=4, N=64, K=256,
+             bias=NULL, epi=1, out=ALIGNED, ldo=32)
+    a.update(kw)
+    return L.qgemm_w4a4_fp6_lowrank(a["a"], a["sa"], a["w"], a["sw"], a["lr"], a["l2"], a["r"], a["M"], a["N"],
+                                    a["K"], a["bias"], a["epi"], a["out"], a["ldo"], None)
+
+
+def test_qgemm_fp6_lowrank_validation(L):
+    assert g6lr(L, r=20) == -2
+    assert g6lr(L, lr=NULL) == -1
+    assert g6lr(L, N=48) == -2                    # SWIGLU needs N % 32
+    assert g6lr(L, epi=4) == -4                   # group sums are rescaled: no I32
+    assert g6lr(L, epi=5) == -4
+    assert g6lr(L, epi=2) == -4
+    assert g6lr(L, a=MISALIGNED) == -3
+    for epi in (0, 1, 3):
+        assert g6lr(L, epi=epi, ldo=64) in (-4, -6)
+    assert g6lr(L, r=0, lr=NULL, l2=NULL) in (-4, -6)
 
 
 def grp(L, segs, **kw):
@@ -213,6 +253,8 @@ def test_qgemm_grouped_validation(L):
     assert grp(L, [{"w_bits": 4}], a8=NULL, sa8=NULL) in (-4, -6)  # unused operand may be NULL
     assert grp(L, [{}, {"w_bits": 8, "epilogue": 5}, {"n": 48, "ldo": 48}]) in (-4, -6)
     assert grp(L, [{}], M=0) in (0, -4, -6)
+    assert grp(L, [{"w_bits": 8}], K=133376) == -2                 # int8 segment: 127 * 127 * K < 2^31
+    assert grp(L, [{"w_bits": 8, "n": 16, "ldo": 16}], K=133120) in (-4, -6)
 
 def g6(L, **kw):
     a = dict(a=ALIGNED, sa=ALIGNED, am=1, w=ALIGNED, sw=ALIGNED, wm=1, M=4, N=32, K=256, bias=NULL,

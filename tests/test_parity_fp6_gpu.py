@@ -9,7 +9,9 @@ them on another instruction, so the bar is exactness:
     the oracle's own quantization;
   * the exact-sum output (I32) equals the oracle's integer product;
   * every float epilogue equals the INT4 path's output on the same codes
-    bit for bit (the fp32 sums of the FP6 products are exact integers).
+    bit for bit (the fp32 sums of the FP6 products are exact integers), and
+    the oracle's dequantized product through the epilogue element by
+    element (tolerances from tests/parity_checks.py).
 Sizes span the 256 x 256 and 256 x 320 tile kernels with ragged tails, and
 the full 4096 x 5120 x 5120 attention projection.
 """
@@ -19,11 +21,10 @@ import pytest
 
 import oracle as O
 import workloads as W
-from tests.helpers import bf16_bits, code_flip_stats, ensure_built, to_dev, to_dev_bf16
+from tests import parity_checks as P
+from tests.helpers import bf16_bits, ensure_built, to_dev, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
-
-FLIP_BUDGET = 1e-4
 
 
 @pytest.fixture(scope="module")
@@ -62,9 +63,9 @@ def test_prologue_fp6_layout(Q, M, K, mode):
     codes = c8.cpu().numpy()
     assert np.array_equal(c6.cpu().numpy(), O.pack_fp6(codes))
     assert torch.equal(s6, s8)
-    ref = O.quantize_activations(xb, 4, mode, True)
-    frac, dmax = code_flip_stats(O.unpack_fp6(c6.cpu().numpy()), ref.codes)
-    assert dmax <= 1 and frac <= FLIP_BUDGET
+    xf = O.bf16_bits_to_f64(xb)
+    P.check_codes(O.unpack_fp6(c6.cpu().numpy()), s6.cpu().numpy(), O.rotate(xf), P.rotation_error_bound(xf),
+                  4, mode)
 
 
 def test_prologue_fp6_extreme_codes_and_strides(Q):
@@ -186,6 +187,10 @@ def test_fp6_epilogues_equal_int4_path(Q, M, N, K, mode):
     a8, w4 = to_dev(qa), to_dev(O.pack_int4(qw))
     a6, w6 = to_dev(O.pack_fp6(qa)), to_dev(O.pack_fp6(qw))
     bias = to_dev_bf16(_rand_bf16(M, (N,), 0.1))
+    rows = np.unique(np.concatenate([np.arange(4), M - 1 - np.arange(4),
+                                     np.random.default_rng(M).choice(M, 40, replace=False)]))
+    qa_o = O.QuantResult(qa[rows], sa_h if mode == "tensor" else sa_h[rows], 4, mode, None)
+    qw_o = O.QuantResult(qw, sw_h, 4, mode, None)
     for epi in ("bf16", "f32", "sigmoid"):
         for bb in (None, bias):
             ref = Q.qgemm_w4a4(a8, sa, w4, sw, K, a_scale_mode=mode, w_scale_mode=mode, bias=bb, epilogue=epi)
@@ -194,6 +199,12 @@ def test_fp6_epilogues_equal_int4_path(Q, M, N, K, mode):
             torch.cuda.synchronize()
             assert torch.equal(got.view(torch.int16) if epi != "f32" else got.view(torch.int32),
                                ref.view(torch.int16) if epi != "f32" else ref.view(torch.int32)), (epi, bb is None)
+            # and the oracle, on sampled rows
+            y, dy = P.linear_bound(qa_o, qw_o, bias_bits=None if bb is None else bf16_bits(bb))
+            want, dw = P.epilogue_with_bound(y, dy, "bf16" if epi == "f32" else epi)
+            g = got[torch.as_tensor(rows, device="cuda")]
+            gv = g.cpu().numpy().astype(np.float64) if epi == "f32" else O.bf16_bits_to_f64(bf16_bits(g))
+            P.assert_outputs_close(gv, want, dw, bf16=epi != "f32", what=f"fp6 {mode} {epi}")
 
 
 def test_fp6_strided_output_and_empty(Q):
@@ -305,11 +316,19 @@ def test_fp6_group64_lowrank_equals_int4_path(Q, rank, epi):
     lr = to_dev_bf16(_rand_bf16(6, (M, rank), 0.5)) if rank else None
     l2 = to_dev_bf16(_rand_bf16(7, (rank, N), 0.05)) if rank else None
     ref = Q.qgemm_w4a4_lowrank(to_dev(qa), sa, to_dev(O.pack_int4(qw)), sw, K, lr=lr, l2=l2, epilogue=epi)
-    got = Q.qgemm_w4a4_lowrank(to_dev(O.pack_fp6(qa)), sa, to_dev(O.pack_fp6(qw)), sw, K, lr=lr, l2=l2,
-                               a_layout="fp6", epilogue=epi)
+    got = Q.qgemm_w4a4_fp6_lowrank(to_dev(O.pack_fp6(qa)), sa, to_dev(O.pack_fp6(qw)), sw, K, lr=lr, l2=l2,
+                                   epilogue=epi)
     torch.cuda.synchronize()
     assert got.shape == ref.shape
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    # the oracle: dequantized group sums plus lr L2 (lr as given), through the epilogue
+    y, dy = P.linear_bound(O.QuantResult(qa, sa_h, 4, "group64", None), O.QuantResult(qw, sw_h, 4, "group64", None))
+    if rank:
+        lrf, l2f = O.bf16_bits_to_f64(bf16_bits(lr)), O.bf16_bits_to_f64(bf16_bits(l2))
+        y = y + lrf @ l2f
+        dy = dy + (rank + 4) * P.U * (np.abs(lrf) @ np.abs(l2f)) + 3 * P.U * np.abs(lrf @ l2f)
+    want, dw = P.epilogue_with_bound(y, dy, epi)
+    P.assert_outputs_close(O.bf16_bits_to_f64(bf16_bits(got)), want, dw, what=f"fp6 group64 r{rank} {epi}")
 
 
 def test_fp6_group64_rejections(Q):
@@ -323,9 +342,11 @@ def test_fp6_group64_rejections(Q):
                          w_scale_mode="group64", epilogue="i32")
     row_a = torch.ones(M, dtype=torch.float32, device="cuda")
     row_w = torch.ones(N, dtype=torch.float32, device="cuda")
-    with pytest.raises(Q.QLinearError):   # FP6 in the low-rank GEMM is group-64 only
-        Q.qgemm_w4a4_lowrank(a6, row_a, w6, row_w, K, a_scale_mode="row", w_scale_mode="row",
-                             a_layout="fp6", epilogue="bf16")
+    with pytest.raises(Q.QLinearError):   # the INT4 low-rank GEMM takes no FP6 operands
+        Q.qgemm_w4a4_lowrank(a6, to_dev(sa_h), w6, to_dev(sw_h), K, a_layout="fp6", epilogue="bf16")
+    with pytest.raises(Q.QLinearError):   # the FP6 low-rank GEMM has no I32 or sigmoid epilogue
+        Q.qgemm_w4a4_fp6_lowrank(a6, to_dev(sa_h), w6, to_dev(sw_h), K, epilogue="sigmoid")
+    del row_a, row_w
 
 
 def test_fp6_group64_svdq_gateup_full_size(Q):
@@ -345,8 +366,21 @@ def test_fp6_group64_svdq_gateup_full_size(Q):
     w4, sw4 = Q.pack_weight_int4(w, scale_mode="group64")
     w6, sw6 = Q.pack_weight_fp6(w, scale_mode="group64")
     ref = Q.qgemm_w4a4_lowrank(a8, sa8, w4, sw4, K, lr=lr, l2=l2, epilogue="swiglu")
-    got = Q.qgemm_w4a4_lowrank(a6, sa6, w6, sw6, K, lr=lr, l2=l2, a_layout="fp6", epilogue="swiglu")
+    got = Q.qgemm_w4a4_fp6_lowrank(a6, sa6, w6, sw6, K, lr=lr, l2=l2, epilogue="swiglu")
     torch.cuda.synchronize()
     assert torch.equal(sa6, sa8) and torch.equal(sw6, sw4)
     assert got.shape == (M, N // 2)
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    # sampled rows and gate|up pairs against the oracle on the device's codes
+    rng = np.random.default_rng(12)
+    rows = np.sort(rng.choice(M, 12, replace=False))
+    fs = np.sort(rng.choice(N // 2, 192, replace=False))
+    ns = np.concatenate([fs, N // 2 + fs])
+    ri = torch.as_tensor(rows, device="cuda")
+    qa = O.QuantResult(O.unpack_fp6(a6[ri].cpu().numpy()), sa6[ri].cpu().numpy(), 4, "group64", None)
+    qw = O.QuantResult(O.unpack_fp6(w6[torch.as_tensor(ns, device="cuda")].cpu().numpy()), sw6.cpu().numpy()[ns],
+                       4, "group64", None)
+    y, dy = P.linear_bound(qa, qw, bf16_bits(x[ri]), bf16_bits(l1), bf16_bits(l2)[:, ns])
+    want, dw = P.epilogue_with_bound(y, dy, "swiglu")
+    P.assert_outputs_close(O.bf16_bits_to_f64(bf16_bits(got[ri][:, torch.as_tensor(fs, device="cuda")])),
+                           want, dw, what="fp6 svdq gate|up")
