@@ -106,33 +106,36 @@ def gemm_source_hash(workload="attn_proj_w4a4") -> str:
     return h.hexdigest()[:16]
 
 
-WARMUP_S = 0.5  # default warm-up duration, seconds of steps
+WARMUP_S = 0.5       # warm-up floor, seconds of steps (clocks settle only under sustained load)
+GEMM_REPEATS = 5     # GEMM-only: median of this many repeats ...
+GEMM_LAUNCHES = 100  # ... of this many back-to-back launches (after 10 untimed ones)
+COLD_LAUNCHES = 20   # cold-cache variant: launches, each after a 512 MiB write
+FLUSH_BYTES = 512 << 20
 
-def _parse():
+
+def _parse(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None,
                    help="timed steps (default 200; 3 for the stack)")
     p.add_argument("--warmup", type=int, default=None,
-                   help="untimed warm-up steps (default: as many as fill 0.5 s, at least 20; "
-                        "at least 1 for the stack)")
+                   help="minimum untimed warm-up steps (default 20; 1 for the stack); warm-up always "
+                        "lasts at least 0.5 s of steps")
     p.add_argument("--workload", default="attn_proj_w4a4", choices=sorted(GEMM_KERNELS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--no-other-gemms", action="store_true",
+                   help="headline workload: skip the GEMM-only figures of the W8A8 and SVDQuant layers")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time of the oracle baseline sample")
     p.add_argument("--calib-copy", action="store_true")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
-    a = p.parse_args()
+    a = p.parse_args(argv)
     stack = a.workload.startswith("stack")
     if a.steps is None:
         a.steps = 3 if stack else (20 if a.workload.startswith("svdq_split") else 200)
-    a.warmup_min = None
     if a.warmup is None:
-        # The GPU's clocks settle only after a fraction of a second of
-        # sustained load (a GEMM measured right after start-up runs ~15 %
-        # slower), so by default warm-up lasts 0.5 s of steps.
-        a.warmup_min = 1 if stack else 20
+        a.warmup = 1 if stack else 20
     return a
 
 
@@ -145,13 +148,24 @@ def _blas_threads():
         return os.cpu_count() or 1
 
 
-def cpu_baseline(wl, target_s=12.0):
+def _cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(wl, target_s=12.0, one_thread_s=3.0):
     """The oracle as it stands, on a row sample of X against the full weights
     (weights quantized beforehand, like the GPU step): rotate + quantize the
     rows, exact integer product via float64 BLAS (per 64-group for group-64
     scales), dequant, low-rank branch, epilogue, bf16 rounding.  A 64-row
     probe sizes the sample to about `target_s` seconds; when the whole
-    workload takes less, it is run repeatedly and the total time is used."""
+    workload takes less, it is run repeatedly and the total time is used.
+    A second, smaller sample runs with BLAS limited to one thread."""
     import oracle as O
 
     threads = _blas_threads()
@@ -168,21 +182,34 @@ def cpu_baseline(wl, target_s=12.0):
         O.f64_to_bf16_bits(out)
         return time.perf_counter() - t0
 
-    probe = run(64)
-    rows = int(min(wl.M, max(64, 64 * target_s / max(probe, 1e-3))))
-    reps = 1
-    if rows == wl.M:
-        first = run(rows)
-        reps = max(1, int(round((target_s - first) / max(first, 1e-3))))
-    t = sum(run(rows) for _ in range(reps))
+    def sample(target):
+        probe = run(64)
+        rows = int(min(wl.M, max(64, 64 * target / max(probe, 1e-3))))
+        reps = 1
+        if rows == wl.M:
+            first = run(rows)
+            reps = max(1, int(round((target - first) / max(first, 1e-3))))
+        t = sum(run(rows) for _ in range(reps))
+        return rows, reps, t
+
+    rows, reps, t = sample(target_s)
     ops = 2.0 * rows * wl.N * wl.K * reps
     what = f"{rows} of {wl.M} rows of X" + (f", whole workload x{reps}" if rows == wl.M else "")
-    return {"value": round(ops / t / 1e12, 4), "unit": "TOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{what} against all {wl.N} outputs (weights pre-quantized): "
-                      f"rotate+quantize, exact integer GEMM via float64 BLAS, dequant, "
-                      f"{wl.epilogue} epilogue, bf16 rounding; {t:.2f} s wall on {threads} "
-                      f"BLAS threads"}
+    rec = {"value": round(ops / t / 1e12, 4), "unit": "TOP/s", "cores": int(threads),
+           "kind": "oracle", "cpu_model": _cpu_model(),
+           "sample": f"{what} against all {wl.N} outputs (weights pre-quantized): "
+                     f"rotate+quantize, exact integer GEMM via float64 BLAS, dequant, "
+                     f"{wl.epilogue} epilogue, bf16 rounding; {t:.2f} s wall on {threads} "
+                     f"BLAS threads"}
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            r1, n1, t1 = sample(one_thread_s)
+        rec["one_thread"] = {"value": round(2.0 * r1 * wl.N * wl.K * n1 / t1 / 1e12, 5), "unit": "TOP/s",
+                             "sample": f"{r1} rows x{n1}, {t1:.2f} s wall on 1 BLAS thread"}
+    except ImportError:
+        rec["one_thread"] = None
+    return rec
 
 
 # ------------------------------------------------------------ PMC traffic --
@@ -700,8 +727,95 @@ CASES = {"attn_proj_w4a4": case_attn, "attn_proj_w4a4_fp6": case_attn_fp6, "svdq
 
 
 # ------------------------------------------------------------------- main --
-def main():
-    args = _parse()
+def _events():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_back_to_back(fns, launches=GEMM_LAUNCHES, repeats=GEMM_REPEATS, warm=10):
+    """Median over `repeats` of the time per pass of `fns` (a list of
+    launches run in order), each repeat `launches` passes back to back
+    between two events on the current stream, after `warm` untimed passes.
+    Returns (median ms per pass, every repeat's ms per pass)."""
+    import torch
+    for _ in range(warm):
+        for fn in fns:
+            fn()
+    per = []
+    for _ in range(repeats):
+        e0, e1 = _events()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(launches):
+            for fn in fns:
+                fn()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / launches)
+    return float(np.median(per)), per
+
+
+def time_cold(fns, dev, launches=COLD_LAUNCHES):
+    """Median time of one pass of `fns` right after a 512 MiB device write
+    (more than L2 and the 256 MB MALL hold), events around the pass only."""
+    import torch
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    per = []
+    for _ in range(launches):
+        flush.fill_(1)
+        e0, e1 = _events()
+        e0.record()
+        for fn in fns:
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1))
+    del flush
+    return float(np.median(per))
+
+
+def launch_count(pass_ms, target_ms=50.0):
+    """Passes per repeat: GEMM_LAUNCHES, fewer for long passes (a repeat of
+    about target_ms, at least 2)."""
+    return int(max(2, min(GEMM_LAUNCHES, round(target_ms / max(pass_ms, 1e-6)))))
+
+
+def gemm_only_record(case, ops, dev, cold=True):
+    """GEMM-only figures of a case: back-to-back launches of its GEMMs on
+    the codes its prologues left in HBM (median of 5 repeats of 100 passes,
+    fewer passes when one pass is long; the stack's 224 GEMMs form one
+    pass), and a cold-cache variant for single-GEMM cases."""
+    import torch
+    fns = [fn for tag, fn in case.launches if tag == "gemm"]
+    for tag, fn in case.launches:      # leave valid codes in place
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    e0.record()
+    for fn in fns:
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    passes = launch_count(e0.elapsed_time(e1))
+    stack = len(fns) > 8
+    ms, reps = time_back_to_back(fns, launches=passes, warm=min(10, passes))
+    rec = {"ms": round(ms, 5), "ms_per_launch": round(ms / case.gemm_launches, 5),
+           "repeats_ms": [round(v, 5) for v in reps], "passes_per_repeat": passes,
+           "tops": round(ops / (ms * 1e-3) / 1e12, 2),
+           "gbs": round(case.gemm_bytes / (ms * 1e-3) / 1e9, 1)}
+    if case.bound == "mfma":
+        rec["pct_int8_peak"] = round(100.0 * ops / (ms * 1e-3) / 1e12 / INT8_MFMA_PEAK_TOPS, 2)
+        if case.peak != INT8_MFMA_PEAK_TOPS:
+            rec["pct_own_peak"] = round(100.0 * ops / (ms * 1e-3) / 1e12 / case.peak, 2)
+    if cold and not stack:
+        cms = time_cold(fns, dev)
+        rec["cold_ms"] = round(cms, 5)
+        rec["cold_tops"] = round(ops / (cms * 1e-3) / 1e12, 2)
+    return rec
+
+
+def main(argv=None):
+    args = _parse(argv)
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.workload)
         return
@@ -722,29 +836,27 @@ def main():
 
     case = CASES[args.workload](Q, W, dev)
     L = len(case.launches)
+    stack = args.workload.startswith("stack")
 
     def step():
         for _, fn in case.launches:
             fn()
 
-    if args.warmup_min is None:
-        for _ in range(args.warmup):
-            step()
-    else:
-        w, t_w = 0, time.perf_counter()
-        while w < args.warmup_min or time.perf_counter() - t_w < WARMUP_S:
-            step()
-            w += 1
-            if w % (1 if args.workload.startswith("stack") else 16) == 0:
-                torch.cuda.synchronize()  # keep the host within a few steps of the GPU
-        args.warmup = w
+    # ---- warm-up: at least `warmup` steps and at least WARMUP_S seconds
+    w, t_w = 0, time.perf_counter()
+    while w < args.warmup or time.perf_counter() - t_w < WARMUP_S:
+        step()
+        w += 1
+        if w % (1 if stack else 16) == 0:
+            torch.cuda.synchronize()  # keep the host within a few steps of the GPU
     torch.cuda.synchronize()
+    warmup_s = time.perf_counter() - t_w
 
     # ---- timed region: exactly `steps` steps, synchronized on both sides,
     # one event before and one after on the stream the kernels run on (the
     # current torch stream).  This is the step time `value` reports.
     n = args.steps
-    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e_start, e_end = _events()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e_start.record()
@@ -755,11 +867,14 @@ def main():
     wall_ms = (time.perf_counter() - t0) * 1e3
     step_ms = e_start.elapsed_time(e_end) / n
 
-    # ---- per-kernel breakdown: the same `steps` steps again with an event
-    # after every launch, so each kernel's duration is the gap between the
-    # event before it and the event after it.  (Recording an event between
-    # kernels adds a small gap, which is why the step time above is taken
-    # without them.)
+    # ---- GEMM-only: back-to-back launches on the prepared codes (the
+    # roofline's kernel time), and a cold-cache variant
+    ops = float(case.ops)
+    gemm = gemm_only_record(case, ops, dev)
+    gemm_ms = gemm["ms"]
+
+    # ---- per-kernel breakdown: the `steps` steps again with an event after
+    # every launch (each event adds a small gap at the kernel boundary)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(L * n + 1)]
     torch.cuda.synchronize()
     ev[0].record()
@@ -773,27 +888,16 @@ def main():
     for s in range(n):
         for i, (tag, _) in enumerate(case.launches):
             t_tag[tag] += ev[s * L + i].elapsed_time(ev[s * L + i + 1])
-    gemm_ev_ms = t_tag["gemm"] / n          # per step, from the per-launch events
+    gemm_ev_ms = t_tag["gemm"] / n
     pro_ev_ms = t_tag["prologue"] / n
 
-    # ---- the step's prologues alone, `steps` times, with events only at the
-    # ends: the GEMM time per step is the clean step time minus this, which
-    # leaves out the gaps the per-launch events add (each costs a few us).
+    # ---- the step's prologues alone, back to back (median of 5 repeats):
+    # their time per step, and the step minus it (the GEMM share of a step)
     pro_fns = [fn for tag, fn in case.launches if tag == "prologue"]
-    if pro_fns:
-        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        p0.record()
-        for _ in range(n):
-            for fn in pro_fns:
-                fn()
-        p1.record()
-        torch.cuda.synchronize()
-        pro_ms = p0.elapsed_time(p1) / n
-    else:
-        pro_ms = 0.0
-    gemm_ms = step_ms - pro_ms
-    gemm_launch_ms = gemm_ms / case.gemm_launches
+    pro_ms = time_back_to_back(pro_fns, launches=1 if stack else 50, warm=2)[0] if pro_fns else 0.0
+
+    # ---- the step, median of 5 repeats of the same K steps
+    step_med_ms = time_back_to_back([step], launches=n, warm=0)[0]
 
     # ---- the same step replayed from a HIP graph (no host launch cost)
     graph_step_ms = None
@@ -811,7 +915,7 @@ def main():
             for _ in range(2):
                 g.replay()
             torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = _events()
             e0.record()
             for _ in range(n):
                 g.replay()
@@ -821,6 +925,19 @@ def main():
         except Exception as exc:  # graph capture is an extra figure only
             print(f"graph replay skipped: {exc}", file=sys.stderr)
 
+    # ---- the other single-layer GEMMs, GEMM-only, in the same process
+    other = None
+    if args.workload == "attn_proj_w4a4" and not args.no_other_gemms:
+        other = {}
+        for name in ("ffdown_w8a8", "svdq_gateup"):
+            oc = CASES[name](Q, W, dev)
+            rec = gemm_only_record(oc, float(oc.ops), dev)
+            rec["workload"] = oc.config["workload"]
+            other[name] = rec
+            del oc
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+
     if args.calib_copy:
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -828,9 +945,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    ops = float(case.ops)
     value = ops / (step_ms * 1e-3) / 1e12
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
+    sub_ms = step_ms - pro_ms
     label = GEMM_KERNELS[args.workload][0]
     traffic = load_traffic(args.workload)
     rec = {
@@ -839,8 +956,10 @@ def main():
         "unit": case.unit,
         "n_gpus": 1,
         "steps": n,
-        "warmup": args.warmup,
+        "warmup": w,
+        "warmup_s": round(warmup_s, 3),
         "ms_per_step": round(step_ms, 5),
+        "ms_per_step_median5": round(step_med_ms, 5),
         "ms_per_step_with_kernel_events": round(step_events_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -849,12 +968,10 @@ def main():
         "data": "synthetic",
         "config": case.config,
         "pct_int8_peak_step": round(100.0 * value / INT8_MFMA_PEAK_TOPS, 2) if case.bound == "mfma" else None,
-        "gemm_only": {"ms": round(gemm_ms, 5), "ms_per_launch": round(gemm_launch_ms, 5),
-                      "ms_per_launch_with_kernel_events": round(gemm_ev_ms / case.gemm_launches, 5),
-                      "tops": round(gemm_tops, 2),
-                      "pct_int8_peak": (round(100.0 * gemm_tops / INT8_MFMA_PEAK_TOPS, 2)
-                                        if case.bound == "mfma" else None),
-                      "gbs": round(case.gemm_bytes / (gemm_ms * 1e-3) / 1e9, 1)},
+        "gemm_only": gemm,
+        "gemm_step_minus_prologue": {"ms": round(sub_ms, 5), "ms_per_launch": round(sub_ms / case.gemm_launches, 5),
+                                     "ms_per_launch_with_kernel_events": round(gemm_ev_ms / case.gemm_launches, 5),
+                                     "tops": round(ops / (sub_ms * 1e-3) / 1e12, 2) if sub_ms > 0 else None},
         "prologue": None if pro_ms <= 0 else {
             "ms": round(pro_ms, 5),
             "ms_with_kernel_events": round(pro_ev_ms, 5),
@@ -868,8 +985,12 @@ def main():
                      "achieved": round(gemm_tops, 2), "peak": case.peak,
                      "unit": case.unit, "frac": round(gemm_tops / case.peak, 4),
                      "traffic": traffic,
-                     "algorithmic_bytes": int(case.gemm_bytes // case.gemm_launches)},
+                     "algorithmic_bytes": int(case.gemm_bytes // case.gemm_launches),
+                     "timing": "GEMM-only: median of 5 repeats of back-to-back launches, HIP events on the "
+                               "launch stream"},
     }
+    if other is not None:
+        rec["other_gemms"] = other
     if not args.no_cpu_baseline and case.cpu_fn is not None:
         rec["cpu_baseline"] = case.cpu_fn(args.cpu_seconds)
     elif not args.no_cpu_baseline and case.wl is not None:

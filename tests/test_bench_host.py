@@ -69,3 +69,19 @@ def test_split_flops(q):
     # sketch product, 2 per power iteration, the final B^T, and the residual
     per_fit = 2 * N * K * l + q * 2 * (2 * N * K * l) + 2 * N * K * l + 2 * N * K * r
     assert bench._split_flops(N, K, r, l, q, 3) == 3 * per_fit
+
+
+def test_warmup_is_a_floor_and_steps_are_exact():
+    a = bench._parse(["--steps", "20", "--warmup", "5"])
+    assert a.steps == 20 and a.warmup == 5      # at least 5 steps, and at least WARMUP_S of them
+    assert bench.WARMUP_S >= 0.5
+    d = bench._parse([])
+    assert d.steps == 200 and d.warmup == 20
+    s = bench._parse(["--workload", "stack"])
+    assert s.steps == 3 and s.warmup == 1
+
+
+def test_gemm_only_launch_count():
+    assert bench.launch_count(0.07) == bench.GEMM_LAUNCHES    # headline GEMM: 100 launches a repeat
+    assert bench.launch_count(1.6) == 31                      # about 50 ms a repeat
+    assert bench.launch_count(150.0) == 2                     # the stack: at least 2
