@@ -75,7 +75,8 @@ enum {
   QL_ERR_ALIGN = -3,       /* a pointer or stride is misaligned           */
   QL_ERR_UNSUPPORTED = -4, /* mode combination or device not supported    */
   QL_ERR_LAUNCH = -5,      /* the HIP runtime rejected a launch           */
-  QL_ERR_DEVICE = -6       /* the current device could not be queried     */
+  QL_ERR_DEVICE = -6,      /* the current device could not be queried     */
+  QL_ERR_SCRATCH = -7      /* larger than the allocation-free entry's fixed workspace */
 };
 
 /* ---- quantization scale granularity ------------------------------------ */
@@ -386,6 +387,26 @@ int svdq_split(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, const float
 
 /* Workspace bytes svdq_split needs for these sizes; -1 for invalid sizes. */
 int64_t svdq_split_workspace_bytes(int64_t N, int64_t K, int rank, int oversample, int scale_mode);
+
+/* svdq_split for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments and results as svdq_split without the workspace, which
+ * lives in a fixed 128 MiB array inside the library (one copy per GPU, held
+ * until the process ends; its device address is looked up once per device).
+ * The call allocates nothing.  It returns QL_ERR_SCRATCH before enqueueing
+ * anything when svdq_split_workspace_bytes(N, K, rank, oversample,
+ * scale_mode) exceeds svdq_split_noalloc_max_bytes() (at rank 32: up to about
+ * 11.7 M weight elements, e.g. 1536 x 5120 or 2048 x 5120, not 5120 x 5120).
+ * Every call on a GPU uses that GPU's one array: calls that overlap on the
+ * same GPU (other streams, other threads) race and must be ordered by the
+ * caller.  No part of the array has to start at zero. */
+int svdq_split_noalloc(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, const float* act_rms,
+                       const float* omega, int rank, int oversample, int power_iters, int refine_iters,
+                       int scale_mode, uint16_t* l1, uint16_t* l2, uint8_t* packed, float* scales,
+                       float* errors, int32_t* best_iter, float* sigma, void* stream);
+
+/* Size in bytes of svdq_split_noalloc's fixed workspace. */
+int64_t svdq_split_noalloc_max_bytes(void);
 
 #ifdef __cplusplus
 }

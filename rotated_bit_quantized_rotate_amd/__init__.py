@@ -21,5 +21,7 @@ from ._lib import (  # noqa: F401
     rotate_quantize_act,
     status_string,
     svdq_split,
+    svdq_split_noalloc,
+    svdq_split_noalloc_max_bytes,
     svdq_split_workspace_bytes,
 )

@@ -24,6 +24,7 @@ QL_ERR_ALIGN = -3
 QL_ERR_UNSUPPORTED = -4
 QL_ERR_LAUNCH = -5
 QL_ERR_DEVICE = -6
+QL_ERR_SCRATCH = -7
 
 QL_SCALE_TENSOR = 0
 QL_SCALE_ROW = 1
@@ -73,6 +74,8 @@ _SIGNATURES = {
     "svdq_split": (_i, [_p, _i64, _i64, _i64, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _i64,
                         _p]),
     "svdq_split_workspace_bytes": (_i64, [_i64, _i64, _i, _i, _i]),
+    "svdq_split_noalloc": (_i, [_p, _i64, _i64, _i64, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "svdq_split_noalloc_max_bytes": (_i64, []),
 }
 
 _LIB = None
@@ -366,3 +369,37 @@ def svdq_split(w, omega, rank, oversample=8, power_iters=2, refine_iters=0, scal
                           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("svdq_split", st)
     return out
+
+
+def svdq_split_noalloc_max_bytes():
+    return lib().svdq_split_noalloc_max_bytes()
+
+
+def svdq_split_noalloc(w, omega, rank, oversample=8, power_iters=2, refine_iters=0, scale_mode="group64",
+                       act_rms=None, out=None, stream=None):
+    """svdq_split without a workspace: the library's fixed per-GPU array holds
+    it and the call allocates nothing.  `out` may pass the output dict of an
+    earlier call (same shapes) to reuse its tensors; otherwise they are
+    allocated here, before the call.  Returns the same dict as svdq_split."""
+    assert w.dtype == torch.bfloat16 and w.dim() == 2 and w.stride(1) == 1
+    N, K = w.shape
+    dev = w.device
+    mode = _mode(scale_mode)
+    assert omega.dtype == torch.float32 and tuple(omega.shape) == (K, rank + oversample) and omega.is_contiguous()
+    if act_rms is not None:
+        assert act_rms.dtype == torch.float32 and act_rms.numel() == K and act_rms.is_contiguous()
+    if out is None:
+        out = {"l1": torch.empty((K, rank), dtype=torch.bfloat16, device=dev),
+               "l2": torch.empty((rank, N), dtype=torch.bfloat16, device=dev),
+               "packed": torch.empty((N, K // 2), dtype=torch.uint8, device=dev),
+               "scales": torch.empty(_scale_shape(N, K, mode), dtype=torch.float32, device=dev),
+               "errors": torch.empty(refine_iters + 1, dtype=torch.float32, device=dev),
+               "best_iter": torch.empty(1, dtype=torch.int32, device=dev),
+               "sigma": torch.empty(rank, dtype=torch.float32, device=dev)}
+    st = lib().svdq_split_noalloc(_ptr(w), N, K, w.stride(0), _ptr(act_rms), _ptr(omega), rank, oversample,
+                                  power_iters, refine_iters, mode, _ptr(out["l1"]), _ptr(out["l2"]),
+                                  _ptr(out["packed"]), _ptr(out["scales"]), _ptr(out["errors"]),
+                                  _ptr(out["best_iter"]), _ptr(out["sigma"]), _stream(stream))
+    _check("svdq_split_noalloc", st)
+    return out
+

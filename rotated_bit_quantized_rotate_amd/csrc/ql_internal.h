@@ -180,4 +180,9 @@ struct SplitArgs {
 int64_t svdq_split_workspace(int64_t N, int64_t K, int rank, int oversample, int scale_mode);
 int launch_svdq_split(const SplitArgs& a, hipStream_t s);
 
+// Allocation-free split: the workspace is a 128 MiB file-scope device array
+// (one copy per GPU); split_scratch gives its address on the current device.
+constexpr int64_t kSplitScratchBytes = int64_t(128) << 20;
+int split_scratch(void** ptr);
+
 }  // namespace ql

@@ -63,6 +63,8 @@ const char* ql_status_string(int status) {
     case QL_ERR_UNSUPPORTED: return "QL_ERR_UNSUPPORTED: mode combination or device not supported";
     case QL_ERR_LAUNCH: return "QL_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
     case QL_ERR_DEVICE: return "QL_ERR_DEVICE: the current device could not be queried";
+    case QL_ERR_SCRATCH:
+      return "QL_ERR_SCRATCH: the problem needs more workspace than the allocation-free entry point holds";
     default: return "unknown qlinear status";
   }
 }
@@ -382,10 +384,10 @@ int64_t svdq_split_workspace_bytes(int64_t N, int64_t K, int rank, int oversampl
   return ql::svdq_split_workspace(N, K, rank, oversample, scale_mode);
 }
 
-int svdq_split(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, const float* act_rms, const float* omega,
-               int rank, int oversample, int power_iters, int refine_iters, int scale_mode, uint16_t* l1,
-               uint16_t* l2, uint8_t* packed, float* scales, float* errors, int32_t* best_iter, float* sigma,
-               void* workspace, int64_t workspace_bytes, void* stream) {
+static int validate_split(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, const float* act_rms,
+                          const float* omega, int rank, int oversample, int power_iters, int refine_iters,
+                          int scale_mode, uint16_t* l1, uint16_t* l2, uint8_t* packed, float* scales, float* errors,
+                          int32_t* best_iter, float* sigma) {
   if (!valid_mode(scale_mode)) return QL_ERR_UNSUPPORTED;
   if (N <= 0 || N % 16 != 0 || K <= 0 || K % 256 != 0 || K > 32768) return QL_ERR_SHAPE;
   if (ldw < K || ldw % 8 != 0) return QL_ERR_SHAPE;
@@ -396,13 +398,17 @@ int svdq_split(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, const float
   if (power_iters < 0 || power_iters > 8 || refine_iters < 0 || refine_iters > 16) return QL_ERR_SHAPE;
   // 32-bit-safe element counts for the one-thread-per-element kernels
   if (N * K >= (int64_t(1) << 31)) return QL_ERR_SHAPE;
-  if (!w || !omega || !l1 || !l2 || !packed || !scales || !errors || !best_iter || !workspace) return QL_ERR_NULL;
-  if (!al16(w) || !al16(l1) || !al16(l2) || !al16(packed) || !al16(scales) || !al16(workspace) ||
-      !al4(omega) || !al4(errors) || !al4(best_iter) || (act_rms && !al4(act_rms)) || (sigma && !al16(sigma)))
+  if (!w || !omega || !l1 || !l2 || !packed || !scales || !errors || !best_iter) return QL_ERR_NULL;
+  if (!al16(w) || !al16(l1) || !al16(l2) || !al16(packed) || !al16(scales) || !al4(omega) || !al4(errors) ||
+      !al4(best_iter) || (act_rms && !al4(act_rms)) || (sigma && !al16(sigma)))
     return QL_ERR_ALIGN;
-  if (workspace_bytes < ql::svdq_split_workspace(N, K, rank, oversample, scale_mode)) return QL_ERR_SHAPE;
-  int st = check_current_device();
-  if (st != QL_OK) return st;
+  return QL_OK;
+}
+
+static int run_split(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, const float* act_rms, const float* omega,
+                     int rank, int oversample, int power_iters, int refine_iters, int scale_mode, uint16_t* l1,
+                     uint16_t* l2, uint8_t* packed, float* scales, float* errors, int32_t* best_iter, float* sigma,
+                     void* workspace, void* stream) {
   ql::SplitArgs a{};
   a.w = w;
   a.N = N;
@@ -425,5 +431,37 @@ int svdq_split(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, const float
   a.workspace = workspace;
   return ql::launch_svdq_split(a, static_cast<hipStream_t>(stream)) == QL_OK ? QL_OK : QL_ERR_LAUNCH;
 }
+
+int svdq_split(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, const float* act_rms, const float* omega,
+               int rank, int oversample, int power_iters, int refine_iters, int scale_mode, uint16_t* l1,
+               uint16_t* l2, uint8_t* packed, float* scales, float* errors, int32_t* best_iter, float* sigma,
+               void* workspace, int64_t workspace_bytes, void* stream) {
+  int st = validate_split(w, N, K, ldw, act_rms, omega, rank, oversample, power_iters, refine_iters, scale_mode, l1,
+                          l2, packed, scales, errors, best_iter, sigma);
+  if (st != QL_OK) return st;
+  if (!workspace) return QL_ERR_NULL;
+  if (!al16(workspace)) return QL_ERR_ALIGN;
+  if (workspace_bytes < ql::svdq_split_workspace(N, K, rank, oversample, scale_mode)) return QL_ERR_SHAPE;
+  if ((st = check_current_device()) != QL_OK) return st;
+  return run_split(w, N, K, ldw, act_rms, omega, rank, oversample, power_iters, refine_iters, scale_mode, l1, l2,
+                   packed, scales, errors, best_iter, sigma, workspace, stream);
+}
+
+int svdq_split_noalloc(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, const float* act_rms,
+                       const float* omega, int rank, int oversample, int power_iters, int refine_iters,
+                       int scale_mode, uint16_t* l1, uint16_t* l2, uint8_t* packed, float* scales, float* errors,
+                       int32_t* best_iter, float* sigma, void* stream) {
+  int st = validate_split(w, N, K, ldw, act_rms, omega, rank, oversample, power_iters, refine_iters, scale_mode, l1,
+                          l2, packed, scales, errors, best_iter, sigma);
+  if (st != QL_OK) return st;
+  if (ql::svdq_split_workspace(N, K, rank, oversample, scale_mode) > ql::kSplitScratchBytes) return QL_ERR_SCRATCH;
+  if ((st = check_current_device()) != QL_OK) return st;
+  void* ws = nullptr;
+  if (ql::split_scratch(&ws) != QL_OK) return QL_ERR_DEVICE;
+  return run_split(w, N, K, ldw, act_rms, omega, rank, oversample, power_iters, refine_iters, scale_mode, l1, l2,
+                   packed, scales, errors, best_iter, sigma, ws, stream);
+}
+
+int64_t svdq_split_noalloc_max_bytes(void) { return ql::kSplitScratchBytes; }
 
 }  // extern "C"

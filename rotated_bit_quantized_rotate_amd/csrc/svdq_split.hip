@@ -700,3 +700,37 @@ int launch_svdq_split(const SplitArgs& a, hipStream_t s) {
 }
 
 }  // namespace ql
+
+// ---- allocation-free variant: the workspace in a library-owned array -------
+// For callers that cannot allocate (graph capture, serving loops): the
+// split's workspace lives in this file-scope device array instead of the
+// caller's buffer.  Each GPU the library runs on holds its own copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, never the
+// device memory: its device address on the current device comes from
+// hipGetSymbolAddress, looked up once per device and kept.  Every region of
+// the workspace is written before it is read, so nothing needs clearing
+// between calls; calls that overlap on one GPU share the array and race.
+static __device__ __align__(256) uint8_t scratch[ql::kSplitScratchBytes];
+
+namespace ql {
+namespace {
+constexpr int kMaxScratchDevices = 64;
+void* g_scratch_ptr[kMaxScratchDevices];  // device address of `scratch` per device; null until looked up
+}  // namespace
+
+int split_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return ERR_LAUNCH;
+  void* p = __atomic_load_n(&g_scratch_ptr[dev], __ATOMIC_ACQUIRE);
+  if (!p) {
+    // with `dev` current: that device's copy of the array
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return ERR_LAUNCH;
+    __atomic_store_n(&g_scratch_ptr[dev], q, __ATOMIC_RELEASE);  // concurrent first calls store the same value
+    p = q;
+  }
+  *ptr = p;
+  return OK;
+}
+
+}  // namespace ql

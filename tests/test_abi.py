@@ -22,7 +22,8 @@ def test_header_declares_the_entry_points():
     for name in ["rotate_quantize_act", "rmsnorm_rotate_quantize_act", "pack_weight_int4", "pack_weight_fp6",
                  "qgemm_w4a4", "qgemm_w4a4_fp6", "qgemm_w8a8", "qgemm_w4a4_lowrank", "qgemm_w4a4_fp6_lowrank",
                  "qgemm_grouped",
-                 "svdq_split", "svdq_split_workspace_bytes", "ql_status_string", "ql_device_supported"]:
+                 "svdq_split", "svdq_split_workspace_bytes", "svdq_split_noalloc", "svdq_split_noalloc_max_bytes",
+                 "ql_status_string", "ql_device_supported"]:
         assert name in fns
 
 
@@ -340,6 +341,32 @@ def test_svdq_split_validation(L):
     assert sp(L, sigma=MISALIGNED) == -3
     assert sp(L) in (-4, -6)                      # valid: reaches the device check
     assert sp(L, rms=ALIGNED, sigma=ALIGNED, mode=0, pi=0, ri=0, over=0) in (-4, -6)
+
+
+def spn(L, **kw):
+    a = dict(w=ALIGNED, N=512, K=1024, ldw=1024, rms=NULL, om=ALIGNED, rank=32, over=8, pi=2, ri=1, mode=2,
+             l1=ALIGNED, l2=ALIGNED, packed=ALIGNED, scales=ALIGNED, errors=ALIGNED, best=ALIGNED, sigma=NULL)
+    a.update(kw)
+    return L.svdq_split_noalloc(a["w"], a["N"], a["K"], a["ldw"], a["rms"], a["om"], a["rank"], a["over"], a["pi"],
+                                a["ri"], a["mode"], a["l1"], a["l2"], a["packed"], a["scales"], a["errors"], a["best"],
+                                a["sigma"], None)
+
+
+def test_svdq_split_noalloc_validation(L):
+    cap = L.svdq_split_noalloc_max_bytes()
+    assert cap == 128 << 20
+    # the same argument checks as svdq_split
+    assert spn(L, mode=5) == -4
+    assert spn(L, N=500) == -2
+    assert spn(L, rank=24) == -2
+    assert spn(L, w=NULL) == -1
+    assert spn(L, l1=MISALIGNED) == -3
+    # problems whose workspace exceeds the fixed array are refused before any launch
+    assert L.svdq_split_workspace_bytes(2048, 5120, 32, 8, 2) <= cap < L.svdq_split_workspace_bytes(2560, 5120, 32, 8, 2)
+    assert spn(L, N=2560, K=5120, ldw=5120) == -7
+    assert spn(L, N=40960, K=5120, ldw=5120) == -7
+    assert spn(L, N=2048, K=5120, ldw=5120) in (-4, -6)   # fits: reaches the device check
+    assert spn(L) in (-4, -6)
 
 
 def test_device_supported_without_gpu_is_false(L):
