@@ -232,8 +232,10 @@ def summarize_pmc(fetch_dir, write_dir, workload):
     f = _read_pmc(fetch_dir, "FETCH_SIZE")
     w = _read_pmc(write_dir, "WRITE_SIZE")
     kib = 1024.0
-    copy_f = np.mean(f["copy"]) * kib
-    copy_w = np.mean(w["copy"]) * kib
+    # the calibration copies are the run's largest device copies; smaller
+    # ones (input uploads) must not dilute the factor
+    copy_f = np.max(f["copy"]) * kib
+    copy_w = np.max(w["copy"]) * kib
     f_scale = CALIB_BYTES / copy_f
     w_scale = CALIB_BYTES / copy_w
     gf = np.mean(f["qgemm"]) * kib * f_scale

@@ -278,7 +278,7 @@ int qgemm_w8a8(const int8_t* a, const float* sa, int a_scale_mode,
  *             QL_LAYOUT_I8 | QL_LAYOUT_PACKED (the FP6 experiment has its
  *             own entry point, qgemm_w4a4_fp6_lowrank)
  *   lr        bf16 [M, rank] (from rotate_quantize_act), dense rows
- *   l2        bf16 [rank, N], dense rows
+ *   l2        bf16 [rank, N], dense rows, 16-byte aligned
  *   rank      0 (no branch; lr, l2 may be NULL) or a multiple of 16, <= 128
  *   epilogue  QL_EPI_BF16 | QL_EPI_SWIGLU | QL_EPI_F32; SWIGLU pairs output
  *             column j (gate) with column j + N/2 (up), needs N % 32 == 0

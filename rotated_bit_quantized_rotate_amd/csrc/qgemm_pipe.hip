@@ -840,6 +840,48 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   }
 
   // ---- epilogue: lane holds out[m][n .. n+3] for each (i, j) --------------
+  // Low-rank branch: the tile's L2 columns (one rank vector per W-tile row t,
+  // i.e. per weight row w_row_of(t)) go through the now-free LDS ring once,
+  // read from L2 [rank, N] with coalesced 16-byte loads (8 consecutive
+  // columns of one rank row; a chunk never straddles the gate|up halves or
+  // the end of N, since 8 | HW and 16 | N) and stored transposed, so a lane's
+  // 8 consecutive ranks of one column are one 16-byte LDS read.  The rows
+  // are spread over the ring arrays, L2R rows each; the row pitch
+  // rank * 2 + 16 bytes puts the 16 rows of a fragment read on distinct bank
+  // groups.
+  constexpr int L2R = (C::BN + NS - 1) / NS;
+  const int l2pitch = p.rank * 2 + 16;
+  auto l2s_row = [&](int t) -> uint8_t* {
+    const int a = t / L2R;
+    return (a == 0 ? sm0 : (a == 1 ? sm1 : sm2)) + (t - a * L2R) * l2pitch;
+  };
+  if constexpr (LOWRANK) {
+    static_assert(L2R * (128 * 2 + 16) <= C::STAGE, "staged L2 columns must fit the ring");
+    static_assert(!SWIG || (C::WN / 2) % 8 == 0, "L2 chunks must not straddle the gate|up halves");
+    lds_barrier();  // every wave is done with the ring
+    const int cpr = C::BN / 8;  // 8-column chunks per rank row
+    for (int c = tid; c < p.rank * cpr; c += C::NT) {
+      const int r = c / cpr, t0c = (c % cpr) * 8;
+      int64_t col;
+      bool ok;
+      if (SWIG) {
+        constexpr int HW = C::WN / 2;
+        const int wv = t0c / C::WN, u = t0c % C::WN;
+        const int64_t f = n0 + wv * HW + (u % HW);
+        ok = f < p.half_n;
+        col = (u >= HW ? p.half_n : 0) + f;
+      } else {
+        col = n0 + t0c;
+        ok = col < p.N;
+      }
+      const uint4 v = ok ? *reinterpret_cast<const uint4*>(p.l2 + (int64_t)r * p.N + col) : make_uint4(0, 0, 0, 0);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint16_t*>(l2s_row(t0c + e) + r * 2) = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+    }
+    lds_barrier();
+  }
   // SwiGLU pairs fragment j (gate) with j + FJ/2 (up) of the same outputs.
   constexpr int NJ = SWIG ? C::FJ / 2 : C::FJ;
   static_assert(!SWIG || C::FJ % 2 == 0, "SwiGLU needs gate/up fragment pairs");
@@ -869,13 +911,13 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
       }
 #pragma unroll
     for (int r = 0; r < 4; ++r) gatev[r] = EPI == EPI_GATED ? bf16_to_f32(p.gate[n + r]) : 0.f;
-    // L2 fragments (first MFMA operand): lane supplies weight column
-    // w_row_of(t0 + l16) (and its up partner) at ranks k0 + 8 lg .. + 7.
-    // The skip above is uniform over the wave (16 | N, 16 | F), so every
-    // lane reaches the MFMAs below.
-    int64_t l2col[2];
-    l2col[0] = w_row_of<C, SWIG>(p, n0, t0 + l16);
-    l2col[1] = SWIG ? w_row_of<C, SWIG>(p, n0, t0 + C::WN / 2 + l16) : 0;
+    // L2 fragments (first MFMA operand): lane supplies the staged rank
+    // vector of W-tile row t0 + l16 (and its up partner t0 + WN/2 + l16) at
+    // ranks k0 + 8 lg .. + 7.  The skip above is uniform over the wave
+    // (16 | N, 16 | F), so every lane reaches the MFMAs below.
+    const uint8_t* l2row[2];
+    l2row[0] = l2s_row(t0 + l16);
+    l2row[1] = l2s_row(SWIG ? t0 + C::WN / 2 + l16 : t0 + l16);
     uint2 res[EPI == EPI_GATED ? C::FI : 1];
     if (EPI == EPI_GATED) {
 #pragma unroll
@@ -902,16 +944,9 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
             const bool kin = kc < p.rank;
             const uint4 ua = kin ? *reinterpret_cast<const uint4*>(p.lr + mc * p.rank + kc)
                                  : make_uint4(0, 0, 0, 0);
-            uint32_t wv[4] = {0u, 0u, 0u, 0u};
-            if (kin) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                wv[e] = (uint32_t)p.l2[(int64_t)(kc + 2 * e) * p.N + l2col[h]] |
-                        ((uint32_t)p.l2[(int64_t)(kc + 2 * e + 1) * p.N + l2col[h]] << 16);
-            }
-            lrv[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(v8bf, make_uint4(wv[0], wv[1], wv[2], wv[3])),
-                __builtin_bit_cast(v8bf, ua), lrv[h], 0, 0, 0);
+            const uint4 wv = kin ? *reinterpret_cast<const uint4*>(l2row[h] + kc * 2) : make_uint4(0, 0, 0, 0);
+            lrv[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, wv),
+                                                             __builtin_bit_cast(v8bf, ua), lrv[h], 0, 0, 0);
           }
         }
       }
@@ -947,7 +982,8 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
       }
       if (EPI == EPI_SWIGLU) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = y[0][r] / (1.0f + __expf(-y[0][r])) * y[1][r];
+        for (int r = 0; r < 4; ++r)
+          o[r] = y[0][r] * __builtin_amdgcn_rcpf(1.0f + __expf(-y[0][r])) * y[1][r];  // silu(gate) * up
       }
       if (EPI == EPI_GATED) {
         const uint2 rr = res[EPI == EPI_GATED ? i : 0];

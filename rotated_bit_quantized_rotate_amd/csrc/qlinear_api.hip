@@ -296,7 +296,7 @@ static int lowrank_gemm(const void* a, const float* sa, int a_scale_mode, int a_
   if (rank < 0 || rank > 128 || rank % 16 != 0) return QL_ERR_SHAPE;
   if (rank > 0) {
     if (M > 0 && (!lr || !l2)) return QL_ERR_NULL;
-    if (!al16(lr) || !al2(l2)) return QL_ERR_ALIGN;
+    if (!al16(lr) || !al16(l2)) return QL_ERR_ALIGN;
   }
   if ((st = check_current_device()) != QL_OK) return st;
   if (M == 0) return QL_OK;
