@@ -31,6 +31,10 @@ reproducible builds, "Activation-aware branch" and "Low-rank refinement, and
 what the objective actually is"; its randomized SVD is Halko, Martinsson and
 Tropp's randomized subspace iteration (2011).
 
+The MX block-scaled variant (mx_ref) stands in for the NVFP4 build of
+[NunchakuLite] "Benchmark" and the mxfp8 build of [lab] Study 1; the block
+formats follow the OCP Microscaling Formats (MX) Specification v1.0.
+
 Parity status of each function is pinned by the ``-m "not gpu"`` tests:
 closed forms and Kronecker construction (Hadamard), involution (rotation),
 error bounds and ties (quantizer), documented byte example (packing),
@@ -43,7 +47,10 @@ FP6 (e2m3) code layout the format's constants, hand-derived bit patterns, a
 worked packing example and exact float32 summation at the largest K; for the
 low-rank split the weight normalization in closed form, exact recovery of low-rank
 matrices, agreement with the full SVD under fast spectral decay, the plain split
-rebuilt from a full SVD, best-kept refinement, zero and scale-invariance cases.  No function
+rebuilt from a full SVD, best-kept refinement, zero and scale-invariance cases; for the MX
+formats the element tables decoded from the bit fields, E4M3 rounding against torch's
+float8_e4m3fn cast, hand-worked blocks, the block error bound and exact rational
+products on tiny inputs.  No function
 here is "parity unpinned".
 """
 
@@ -51,5 +58,7 @@ from .qlinear_ref import *  # noqa: F401,F403
 from .qlinear_ref import __all__ as _q_all
 from .svdq_split_ref import *  # noqa: F401,F403
 from .svdq_split_ref import __all__ as _s_all
+from .mx_ref import *  # noqa: F401,F403
+from .mx_ref import __all__ as _m_all
 
-__all__ = list(_q_all) + list(_s_all)
+__all__ = list(_q_all) + list(_s_all) + list(_m_all)
