@@ -73,6 +73,8 @@ if ROOT not in sys.path:
 
 INT8_MFMA_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POP/s
 FP6_MFMA_PEAK_TOPS = 10100.0     # MI355X dense FP6 / FP4 MFMA, 10.1 PFLOP/s
+FP4_MFMA_PEAK_TOPS = 10100.0
+FP8_MFMA_PEAK_TOPS = 5000.0      # MI355X dense FP8 MFMA, 5.0 PFLOP/s
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector FMA: 256 CUs x 128 lanes x 2 x 2.4 GHz
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 CALIB_BYTES = 256 << 20
@@ -83,6 +85,8 @@ HEADLINE_METRIC = "effective int TOPS + % int8 MFMA peak, W4A4 rotated GEMM M=40
 GEMM_KERNELS = {
     "attn_proj_w4a4": ("qgemm_w4a4", "4096x5120x5120", ["qgemm_pipe.hip"]),
     "attn_proj_w4a4_fp6": ("qgemm_w4a4_fp6", "4096x5120x5120", ["qgemm_pipe.hip"]),
+    "attn_proj_mxfp4": ("qgemm_mx_fp4", "4096x5120x5120", ["qgemm_pipe.hip"]),
+    "attn_proj_mxfp8": ("qgemm_mx_fp8", "4096x5120x5120", ["qgemm_pipe.hip"]),
     "svdq_split_gateup": ("svdq_split", "40960x5120_r32", ["svdq_split.hip"]),
     "ffdown_w8a8": ("qgemm_w8a8", "4096x20480x5120", ["qgemm_pipe.hip"]),
     "svdq_gateup": ("qgemm_w4a4_lowrank", "4096x5120x40960", ["qgemm_pipe.hip"]),
@@ -368,6 +372,84 @@ def case_attn_fp6(Q, W, dev):
                             "group-256 Hadamard, per-token / per-row scales, bf16 out",
                 "M": M, "N": N, "K": K, "global_batch": M, "parallelism": "single GPU"}
     c.wl = wl
+    return c
+
+
+def mx_cpu_baseline(wl, fmt, target_s=12.0, one_thread_s=3.0):
+    """The MX oracle on a row sample of X against the pre-quantized weights:
+    rotate, block-quantize, the block-scaled product (float64 BLAS per
+    32-channel block), bf16 rounding."""
+    import oracle as O
+
+    threads = _blas_threads()
+    qw = O.quantize_mx(wl.w, fmt)
+
+    def run(rows):
+        xs = np.ascontiguousarray(wl.x[:rows])
+        t0 = time.perf_counter()
+        qa = O.quantize_mx(xs, fmt)
+        O.f64_to_bf16_bits(O.mx_gemm(qa, qw))
+        return time.perf_counter() - t0
+
+    def sample(target):
+        probe = run(16)
+        rows = int(min(wl.M, max(16, 16 * target / max(probe, 1e-3))))
+        return rows, run(rows)
+
+    rows, t = sample(target_s)
+    rec = {"value": round(2.0 * rows * wl.N * wl.K / t / 1e12, 5), "unit": "TOP/s", "cores": int(threads),
+           "kind": "oracle", "cpu_model": _cpu_model(),
+           "sample": f"{rows} of {wl.M} rows of X against all {wl.N} outputs (weights pre-quantized): rotate, "
+                     f"MX {fmt} block quantization, block-scaled product via float64 BLAS per 32-channel "
+                     f"block, bf16 rounding; {t:.2f} s wall on {threads} BLAS threads"}
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            r1, t1 = sample(one_thread_s)
+        rec["one_thread"] = {"value": round(2.0 * r1 * wl.N * wl.K / t1 / 1e12, 6), "unit": "TOP/s",
+                             "sample": f"{r1} rows, {t1:.2f} s wall on 1 BLAS thread"}
+    except ImportError:
+        rec["one_thread"] = None
+    return rec
+
+
+def case_attn_mx(Q, W, dev, fmt="fp4"):
+    """The attention projection in the OCP MX block formats on gfx950's
+    block-scaled matrix instruction: both operands rotated and quantized to
+    32-element blocks with an E8M0 scale (MXFP4: E2M1 elements, the
+    counterpart of the pages' NVFP4 build; MXFP8: E4M3, their mxfp8 build)."""
+    import torch
+    wl = W.attn_proj_w4a4()
+    M, N, K = wl.M, wl.N, wl.K
+    eb = K // 2 if fmt == "fp4" else K          # element bytes per row
+    x, w = _bf16_dev(wl.x, dev), _bf16_dev(wl.w, dev)
+    codes = torch.empty((M, eb), dtype=torch.uint8, device=dev)
+    sa = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    wq = torch.empty((N, eb), dtype=torch.uint8, device=dev)
+    sw = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    c = Case()
+    c.prep_ms = _timed_prep(lambda: Q.rotate_quantize_mx(w, fmt=fmt, codes=wq, scales=sw))
+    c.launches = [
+        ("prologue", lambda: Q.rotate_quantize_mx(x, fmt=fmt, codes=codes, scales=sa)),
+        ("gemm", lambda: Q.qgemm_mx(codes, sa, wq, sw, K, fmt=fmt, out=out)),
+    ]
+    c.ops = wl.int_ops
+    c.gemm_launches = 1
+    c.pro_bytes = M * K * 2 + M * eb + M * K // 32
+    c.gemm_bytes = (M + N) * (eb + K // 32) + M * N * 2
+    name = "MXFP4" if fmt == "fp4" else "MXFP8"
+    c.metric = (f"effective TOPS + % {'FP4' if fmt == 'fp4' else 'FP8'} MFMA peak, {name} rotated GEMM "
+                f"M=4096 K=N=5120 (block-scaled matrix instruction)")
+    c.dtype = (f"{'fp4 e2m1' if fmt == 'fp4' else 'fp8 e4m3'} elements x E8M0 block-32 scales (MX), "
+               "fp32 accumulate, bf16 out")
+    c.peak = FP4_MFMA_PEAK_TOPS if fmt == "fp4" else FP8_MFMA_PEAK_TOPS
+    c.config = {"workload": f"{name} rotated linear, DiT attention projection at 1024^2: X bf16 [4096x5120] "
+                            "N(0,1) + 1% outlier channels x30, W [5120x5120], group-256 Hadamard, OCP MX "
+                            "blocks of 32 with E8M0 scales on both operands, bf16 out",
+                "M": M, "N": N, "K": K, "global_batch": M, "parallelism": "single GPU"}
+    c.wl = wl
+    c.cpu_fn = lambda s: mx_cpu_baseline(wl, fmt, s)
     return c
 
 
@@ -722,6 +804,8 @@ def case_stack_fused(Q, W, dev, grouped=False):
 
 
 CASES = {"attn_proj_w4a4": case_attn, "attn_proj_w4a4_fp6": case_attn_fp6, "svdq_split_gateup": case_svdq_split,
+         "attn_proj_mxfp4": lambda Q, W, dev: case_attn_mx(Q, W, dev, "fp4"),
+         "attn_proj_mxfp8": lambda Q, W, dev: case_attn_mx(Q, W, dev, "fp8"),
          "ffdown_w8a8": case_ffdown, "svdq_gateup": case_svdq,
          "svdq_gateup_fp6": lambda Q, W, dev: case_svdq(Q, W, dev, fp6=True),
          "stack": case_stack, "stack_fused": case_stack_fused,
@@ -931,7 +1015,7 @@ def main(argv=None):
     other = None
     if args.workload == "attn_proj_w4a4" and not args.no_other_gemms:
         other = {}
-        for name in ("ffdown_w8a8", "svdq_gateup"):
+        for name in ("ffdown_w8a8", "svdq_gateup", "attn_proj_mxfp4"):
             oc = CASES[name](Q, W, dev)
             rec = gemm_only_record(oc, float(oc.ops), dev)
             rec["workload"] = oc.config["workload"]

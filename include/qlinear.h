@@ -103,6 +103,17 @@ enum {
  *                    8 bytes.                                               */
 enum { QL_LAYOUT_I8 = 0, QL_LAYOUT_PACKED = 1, QL_LAYOUT_FP6 = 2 };
 
+/* ---- MX block formats (OCP Microscaling Formats v1.0) -------------------
+ * Every 32 consecutive elements of a row along K share one E8M0 scale byte
+ * (the power of two 2^(byte - 127)); elements are
+ * QL_MX_FP4 : FP4 E2M1 (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; sign in bit
+ *             3), two per byte, element 2i in the low nibble of byte i:
+ *             [R, K/2] bytes;
+ * QL_MX_FP8 : FP8 E4M3 (bias 7, largest magnitude 448, no infinities), one
+ *             per byte: [R, K] bytes.
+ * Scales: [R, K/32] bytes, row-major.  Zero elements are stored as +0. */
+enum { QL_MX_FP4 = 4, QL_MX_FP8 = 8 };
+
 /* ---- GEMM epilogues ---------------------------------------------------- */
 enum {
   QL_EPI_BF16 = 0,           /* out[m,n] = bf16(y)                               */
@@ -249,6 +260,54 @@ int qgemm_w4a4_fp6(const uint8_t* a, const float* sa, int a_scale_mode,
                    int64_t M, int64_t N, int64_t K,
                    const uint16_t* bias, int epilogue, void* out, int64_t ldo,
                    void* stream);
+
+/* MX block quantization: the activation prologue and the offline weight
+ * preparation of qgemm_mx (both operands use the same quantizer).  The pages
+ * run the model as an NVFP4 build on a GPU with native FP4 matrix units
+ * (model card "Krea 2 Turbo Nunchaku Lite INT4 r32", section "Benchmark")
+ * and as an mxfp8 build (research log "lab", Study 1); gfx950's
+ * block-scaled matrix instruction takes OCP MX operands (32-element blocks,
+ * E8M0 scales), so MXFP4 stands in for NVFP4 and MXFP8 for mxfp8.  Per
+ * block, after the optional rotation (as rotate_quantize_act):
+ *   e = floor(log2 max|x|) - emax (emax 2 for FP4, 8 for FP8), clamped to
+ *       [-127, 127]; -127 for an all-zero block;
+ *   element = x / 2^e rounded to nearest, ties to even, saturating at the
+ *       largest magnitude (OCP MX v1.0, conversion from wider formats).
+ *   x      [M, K] bf16 (finite), row stride ldx (elements, >= K, multiple of 8)
+ *   fmt    QL_MX_FP4 | QL_MX_FP8 (else QL_ERR_UNSUPPORTED)
+ *   rotate 1: rotate each 256-group by H/16 first; 0: quantize x as is
+ *   codes  out: element bytes per fmt, dense rows (16-byte aligned)
+ *   scales out: [M, K/32] E8M0 bytes, dense rows                           */
+int rotate_quantize_mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                       int fmt, int rotate, void* codes, uint8_t* scales,
+                       void* stream);
+
+/* MX block-scaled GEMM + epilogue on gfx950's block-scaled matrix
+ * instruction (pages and formats as rotate_quantize_mx):
+ *   y[m,n] = sum_b 2^(ea[m,b] + ew[n,b]) * sum_{k in block b} a[m,k] w[n,k]
+ *            (+ bias[n]),
+ * accumulated in float32 over the K/32 blocks (block scale products below
+ * 2^-126 underflow).  FP4 block products are exact.  FP8 products are
+ * summed by the matrix instruction on a fixed-point grid (measured on
+ * gfx950): inside a small group of adjacent elements each product is
+ * truncated toward zero to a multiple of 2^-13 times the binade of the
+ * group's largest product, so an FP8 block product can differ from the
+ * exact one by up to about 2^-13 of that product per element.
+ *   a, sa    activation elements [M, K/2 | K] and scales [M, K/32]
+ *   w, sw    weight elements [N, K/2 | K] and scales [N, K/32]
+ *            (rotate_quantize_mx with the same fmt; scale pointers 4-byte
+ *            aligned)
+ *   fmt      QL_MX_FP4 | QL_MX_FP8
+ *   bias     NULL or bf16 [N]
+ *   residual, gate   as qgemm_w8a8, for QL_EPI_GATED_RESIDUAL
+ *   epilogue QL_EPI_BF16 | QL_EPI_F32 | QL_EPI_SIGMOID |
+ *            QL_EPI_GATED_RESIDUAL | QL_EPI_SWIGLU (N a multiple of 32;
+ *            gate rows first, as qgemm_w4a4_lowrank); not QL_EPI_I32
+ *   out      [M, N] (SWIGLU: [M, N/2]) bf16 / float32, row stride ldo    */
+int qgemm_mx(const void* a, const uint8_t* sa, const void* w, const uint8_t* sw,
+             int fmt, int64_t M, int64_t N, int64_t K,
+             const uint16_t* bias, const uint16_t* residual, const uint16_t* gate,
+             int epilogue, void* out, int64_t ldo, void* stream);
 
 /* W8A8 GEMM + dequant epilogue for the protected ff.down projections (model
  * card "Krea 2 Turbo OrbitQuant W4A4", sections "Fused transformer" and

@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     pack_weight_fp6,
     pack_weight_int4,
     qgemm_grouped,
+    qgemm_mx,
     qgemm_w4a4,
     qgemm_w4a4_fp6,
     qgemm_w4a4_fp6_lowrank,
@@ -19,6 +20,7 @@ from ._lib import (  # noqa: F401
     qgemm_w8a8,
     rmsnorm_rotate_quantize_act,
     rotate_quantize_act,
+    rotate_quantize_mx,
     status_string,
     svdq_split,
     svdq_split_noalloc,

@@ -32,6 +32,9 @@ QL_SCALE_GROUP64 = 2
 QL_LAYOUT_I8 = 0
 QL_LAYOUT_PACKED = 1
 QL_LAYOUT_FP6 = 2
+QL_MX_FP4 = 4
+QL_MX_FP8 = 8
+MX_FORMATS = {"fp4": QL_MX_FP4, "fp8": QL_MX_FP8}
 QL_EPI_BF16 = 0
 QL_EPI_SWIGLU = 1
 QL_EPI_GATED_RESIDUAL = 2
@@ -76,6 +79,8 @@ _SIGNATURES = {
     "svdq_split_workspace_bytes": (_i64, [_i64, _i64, _i, _i, _i]),
     "svdq_split_noalloc": (_i, [_p, _i64, _i64, _i64, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]),
     "svdq_split_noalloc_max_bytes": (_i64, []),
+    "rotate_quantize_mx": (_i, [_p, _i64, _i64, _i64, _i, _i, _p, _p, _p]),
+    "qgemm_mx": (_i, [_p, _p, _p, _p, _i, _i64, _i64, _i64, _p, _p, _p, _i, _p, _i64, _p]),
 }
 
 _LIB = None
@@ -227,6 +232,26 @@ def pack_weight_fp6(w, scale_mode="row", rotate=True, packed=None, scales=None, 
     return packed, scales
 
 
+def _mxfmt(f):
+    return MX_FORMATS[f] if isinstance(f, str) else int(f)
+
+
+def rotate_quantize_mx(x, fmt="fp4", rotate=True, codes=None, scales=None, stream=None):
+    """x: bf16 [R, K] -> (element bytes [R, K/2] (fp4) | [R, K] (fp8) uint8,
+    E8M0 scale bytes [R, K/32] uint8).  Serves activations and weights."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    R, K = x.shape
+    f = _mxfmt(fmt)
+    if codes is None:
+        codes = torch.empty((R, K // 2 if f == QL_MX_FP4 else K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((R, K // 32), dtype=torch.uint8, device=x.device)
+    st = lib().rotate_quantize_mx(_ptr(x), R, K, x.stride(0), f, int(bool(rotate)), _ptr(codes), _ptr(scales),
+                                  _stream(stream))
+    _check("rotate_quantize_mx", st)
+    return codes, scales
+
+
 def _out(out, M, cols, epi, device):
     if out is not None:
         return out
@@ -259,6 +284,20 @@ def qgemm_w4a4_fp6(a, sa, w, sw, K, a_scale_mode="row", w_scale_mode="row", bias
     st = lib().qgemm_w4a4_fp6(_ptr(a), _ptr(sa), _mode(a_scale_mode), _ptr(w), _ptr(sw), _mode(w_scale_mode),
                               M, N, K, _ptr(bias), epi, _ptr(out), out.stride(0), _stream(stream))
     _check("qgemm_w4a4_fp6", st)
+    return out
+
+
+def qgemm_mx(a, sa, w, sw, K, fmt="fp4", bias=None, residual=None, gate=None, epilogue="bf16", out=None,
+             stream=None):
+    """MX block-scaled GEMM: a, w element bytes and sa, sw E8M0 scale bytes
+    from rotate_quantize_mx with the same fmt."""
+    M = a.shape[0]
+    N = w.shape[0]
+    epi = _epi(epilogue)
+    out = _out(out, M, N // 2 if epi == QL_EPI_SWIGLU else N, epi, a.device)
+    st = lib().qgemm_mx(_ptr(a), _ptr(sa), _ptr(w), _ptr(sw), _mxfmt(fmt), M, N, K, _ptr(bias), _ptr(residual),
+                        _ptr(gate), epi, _ptr(out), out.stride(0), _stream(stream))
+    _check("qgemm_mx", st)
     return out
 
 

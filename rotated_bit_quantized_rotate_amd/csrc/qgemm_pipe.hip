@@ -136,6 +136,8 @@ struct PArgs {
   const uint8_t* w;
   const float* sa;
   const float* sw;
+  const uint8_t* xa;         // MX: E8M0 block scales [M, K/32], [N, K/32]
+  const uint8_t* xw;
   int64_t M, N, K;
   int sa_stride, sw_stride;  // tensor / row scales: 0 or 1
   int kg;                    // group-64 scales: K / 64 per row
@@ -156,25 +158,38 @@ struct PArgs {
 
 // F6: both operands in the FP6 e2m3 layout (96 bytes per row per stage),
 // multiplied on the FP6 matrix instruction with fp32 accumulation.
-template <int BM_, int BN_, int WGM_, int WGN_, bool AP_, bool WP_, bool GROUP_ = false, bool F6_ = false>
+// MX = 4 / 8: both operands MX block-scaled (OCP Microscaling v1.0): FP4
+// E2M1 (64 bytes per row per stage) or FP8 E4M3 (128 bytes) elements, one
+// E8M0 scale per 32 elements along K, applied by the block-scaled matrix
+// instruction itself; fp32 accumulation.
+template <int BM_, int BN_, int WGM_, int WGN_, bool AP_, bool WP_, bool GROUP_ = false, bool F6_ = false,
+          int MX_ = 0>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int WGM = WGM_, WGN = WGN_;   // wave grid
   static constexpr int NW = WGM * WGN;           // waves per workgroup
   static constexpr int NT = 64 * NW;
   static constexpr bool AP = AP_, WP = WP_, GROUP = GROUP_, F6 = F6_;
+  static constexpr int MX = MX_;
+  static constexpr bool FMMA = F6 || MX != 0;   // float matrix instruction, fp32 accumulators
+  static constexpr bool NOSC = GROUP || MX != 0;  // accumulators already carry both scales
+  static constexpr bool SCL = GROUP || MX != 0;   // scales ride in the LDS ring
   static constexpr int WM = BM / WGM;       // wave tile rows
   static constexpr int WN = BN / WGN;       // wave tile cols
   static constexpr int FI = WM / 16;
   static constexpr int FJ = WN / 16;
-  static constexpr int ARB = F6 ? BK * 3 / 4 : (AP ? BK / 2 : BK);  // bytes per A row per stage
-  static constexpr int WRB = F6 ? BK * 3 / 4 : (WP ? BK / 2 : BK);
+  static constexpr int ARB = F6 ? BK * 3 / 4 : (MX ? BK * MX / 8 : (AP ? BK / 2 : BK));  // bytes per A row per stage
+  static constexpr int WRB = F6 ? BK * 3 / 4 : (MX ? BK * MX / 8 : (WP ? BK / 2 : BK));
   static_assert(!F6 || (AP && WP), "FP6 operands: both sides");
+  static_assert(MX == 0 || MX == 4 || MX == 8, "MX element width");
+  static_assert(!MX || (!AP && !WP && !GROUP && !F6), "MX operands have their own layout");
   static constexpr int SA = BM * ARB;
   static constexpr int SW = BN * WRB;
-  // two groups of fp32 scales, padded so every wave issues the same number
-  // of 256-byte loads
-  static constexpr int SC = GROUP ? (8 * (BM + BN) + 256 * NW - 1) / (256 * NW) * (256 * NW) : 0;
+  // group-64: two groups of fp32 scales per row; MX: the 4 E8M0 bytes of
+  // the stage's 4 blocks per row.  Padded so every wave issues the same
+  // number of 256-byte loads.
+  static constexpr int SCB = GROUP ? 8 * (BM + BN) : (MX ? 4 * (BM + BN) : 0);
+  static constexpr int SC = (SCB + 256 * NW - 1) / (256 * NW) * (256 * NW);
   static constexpr int STAGE = SA + SW + SC;
   static constexpr int A_INSTR = SA / 1024;  // 1 KB per 16-byte-per-lane load
   static constexpr int W_INSTR = SW / 1024;
@@ -274,8 +289,9 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   const int64_t m0 = (int64_t)tile_m * C::BM;
   const int64_t n0 = (int64_t)tile_n * (SWIG ? C::BN / 2 : C::BN);
 
-  const int64_t lda = C::F6 ? p.K / 4 * 3 : (C::AP ? p.K / 2 : p.K);
-  const int64_t ldw = C::F6 ? p.K / 4 * 3 : (C::WP ? p.K / 2 : p.K);
+  // row strides in bytes: a stage holds BK channels of a row in ARB / WRB bytes
+  const int64_t lda = p.K / BK * C::ARB;
+  const int64_t ldw = p.K / BK * C::WRB;
   const int KT = (int)(p.K / BK);
 
   // ---- global -> LDS loads -------------------------------------------------
@@ -316,11 +332,23 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
     const int ch = C::F6 ? swz6(rl, ci % CPR) : swz<C::WRB, C::GROUP>(rl, lane % CPR);
     w_vo[tw] = (uint32_t)(w_row_of<C, SWIG>(p, n0, rl) * ldw + (ch << 4));
   }
-  uint32_t s_vo[C::GROUP ? C::S_PER_WAVE : 1];
+  uint32_t s_vo[C::SCL ? C::S_PER_WAVE : 1];
 #pragma unroll
-  for (int ts = 0; ts < (C::GROUP ? C::S_PER_WAVE : 0); ++ts) {
+  for (int ts = 0; ts < (C::SCL ? C::S_PER_WAVE : 0); ++ts) {
     const int pos = (wave + C::NW * ts) * 64 + lane;
     int64_t e = 0;  // float index relative to p.sa (A part) or p.sw (W part)
+    if (C::MX) {
+      // MX: position pos holds the 4 scale bytes of tile row pos (A rows,
+      // then W rows in tile-row order); e is a byte offset into p.xa / p.xw
+      if (pos < C::BM) {
+        const int64_t gr = m0 + pos > p.M - 1 ? p.M - 1 : m0 + pos;
+        e = gr * (p.K / 32);
+      } else if (pos < C::BM + C::BN) {
+        e = w_row_of<C, SWIG>(p, n0, pos - C::BM) * (p.K / 32);
+      }
+      s_vo[ts] = (uint32_t)e;
+      continue;
+    }
     if (pos < 2 * C::BM) {
       const int kk = pos / C::BM, rem = pos % C::BM;
       const int wv = rem / C::WM, u = rem % C::WM;
@@ -348,10 +376,15 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
         const int q = wave + C::NW * tw;
         dma_b128(p.w, w_vo[tw] + (uint32_t)(kt * C::WRB), st + C::SA + q * 1024);
       }
+    } else if (C::MX) {
+      const int ts = t - C::A_PER_WAVE - C::W_HI;
+      const int si = wave + C::NW * ts;
+      dma_b32(si * 64 < C::BM ? p.xa : p.xw, s_vo[C::SCL ? ts : 0] + (uint32_t)(kt * 4),
+              st + C::SA + C::SW + si * 256);
     } else if (C::GROUP) {
       const int ts = t - C::A_PER_WAVE - C::W_HI;
       const int si = wave + C::NW * ts;
-      dma_b32(si * 64 < 2 * C::BM ? p.sa : p.sw, s_vo[C::GROUP ? ts : 0] + (uint32_t)(kt * 8),
+      dma_b32(si * 64 < 2 * C::BM ? p.sa : p.sw, s_vo[C::SCL ? ts : 0] + (uint32_t)(kt * 8),
               st + C::SA + C::SW + si * 256);
     }
   };
@@ -359,7 +392,7 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   // int32 accumulators (tensor / row scales), fp32 sums of rescaled group
   // partials (group-64 scales), or fp32 sums of FP6 code products (exact
   // integers below 2^24).
-  typedef typename AccOf<C::F6>::type acc_t;
+  typedef typename AccOf<C::FMMA>::type acc_t;
   acc_t acc[C::GROUP ? 1 : C::FJ][C::GROUP ? 1 : C::FI];
   v4f yf[C::GROUP ? C::FJ : 1][C::GROUP ? C::FI : 1];
 #pragma unroll
@@ -413,6 +446,16 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   const int a6_lo = a_row * 96 + (swz6(a_row, 4 + (lg >> 1)) << 4) + 8 * (lg & 1);
   const int w6_hi = w_row * 96 + (swz6(w_row, lg) << 4);
   const int w6_lo = w_row * 96 + (swz6(w_row, 4 + (lg >> 1)) << 4) + 8 * (lg & 1);
+  // MX: lane group lg supplies K-block lg of the stage (32 elements) and
+  // its scale.  FP4: the block is the 16 bytes of chunk lg.  FP8: the
+  // instruction takes 16 elements of each of two blocks per lane -- K
+  // [16 lg, 16 lg + 16) in its first four dwords and [64 + 16 lg, ...) in
+  // the last four (measured on gfx950; the scale of lane group b still
+  // covers K [32 b, 32 b + 32)), so the lane reads chunks lg and 4 + lg.
+  const int ax0 = a_row * C::ARB + (swz<C::ARB, false>(a_row, lg) << 4);
+  const int ax1 = a_row * C::ARB + (swz<C::ARB, false>(a_row, 4 + lg) << 4);
+  const int wx0 = w_row * C::WRB + (swz<C::WRB, false>(w_row, lg) << 4);
+  const int wx1 = w_row * C::WRB + (swz<C::WRB, false>(w_row, 4 + lg) << 4);
   // group scales: byte offsets inside the stage's scale block.  A lane reads
   // the scales of its fragments 4f .. 4f+3 as one b128 at 64 f + 4 l16, so
   // the 16 lanes of a read sit at a 16-byte stride (no bank conflicts).
@@ -437,11 +480,11 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
       float v = 0.f;
       if (e < C::BM) {
         const int64_t m = m0 + e > p.M - 1 ? p.M - 1 : m0 + e;
-        v = C::GROUP ? p.post : p.sa[m * p.sa_stride] * p.post;
+        v = C::NOSC ? p.post : p.sa[m * p.sa_stride] * p.post;
       } else if (e < NV) {
         const int f = (e - C::BM) / C::BN;
         const int64_t n = n0 + (e - C::BM) % C::BN > p.N - 1 ? p.N - 1 : n0 + (e - C::BM) % C::BN;
-        if (f == 0) v = C::GROUP ? 1.f : p.sw[n * p.sw_stride];
+        if (f == 0) v = C::NOSC ? 1.f : p.sw[n * p.sw_stride];
         else if (f == 1) v = p.bias ? bf16_to_f32(p.bias[n]) : 0.f;
         else v = bf16_to_f32(p.gate[n]);
       }
@@ -486,7 +529,53 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
     stage_prio(0);
     const bool dma = kt + NS - 1 < KT;
 
-    if constexpr (C::F6) {
+    if constexpr (C::MX) {
+      // MX stage: one block-scaled 16x16x128 instruction per fragment pair
+      // covers the stage's 128 channels; each lane passes the E8M0 scale of
+      // its own row and block (byte lg of the row's 4 stage scales).
+      const uint8_t* As = cur;
+      const uint8_t* Ws = As + C::SA;
+      const uint8_t* Ss = Ws + C::SW;
+      constexpr int FMT = C::MX == 4 ? 4 : 0;  // instruction format: FP4 E2M1 | FP8 E4M3
+      auto frag = [&](const uint8_t* base, int o0, int o1) -> v8i {
+        const uint4 h = *reinterpret_cast<const uint4*>(base + o0);
+        if (C::MX == 4) return v8i{(int)h.x, (int)h.y, (int)h.z, (int)h.w, 0, 0, 0, 0};
+        const uint4 g = *reinterpret_cast<const uint4*>(base + o1);
+        return v8i{(int)h.x, (int)h.y, (int)h.z, (int)h.w, (int)g.x, (int)g.y, (int)g.z, (int)g.w};
+      };
+      v8i wf[C::FJ];
+      int wsc[C::FJ];
+#pragma unroll
+      for (int j = 0; j < C::FJ; ++j) {
+        wf[j] = frag(Ws + j * 16 * C::WRB, wx0, wx1);
+        wsc[j] = Ss[(C::BM + w_row + 16 * j) * 4 + lg];
+      }
+      int asc[C::FI];
+#pragma unroll
+      for (int i = 0; i < C::FI; ++i) asc[i] = Ss[(a_row + 16 * i) * 4 + lg];
+      constexpr int PF = 2;
+      v8i abuf[PF + 1];
+#pragma unroll
+      for (int q = 0; q < PF; ++q) abuf[q] = frag(As + q * 16 * C::ARB, ax0, ax1);
+#pragma unroll
+      for (int i = 0; i < C::FI; ++i) {
+        if (i > 0 && (4 * i) % C::FI < 4) stage_prio((4 * i) / C::FI);
+        if (i + PF < C::FI) abuf[(i + PF) % (PF + 1)] = frag(As + (i + PF) * 16 * C::ARB, ax0, ax1);
+        if (dma && i < NDMA) issue_one(nxt, kt + NS - 1, i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < C::FJ; ++j) {
+          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], abuf[i % (PF + 1)], acc[j][i], FMT,
+                                                                      FMT, 0, wsc[j], 0, asc[i]);
+          asm volatile("" : "+v"(acc[j][i]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (dma) {
+#pragma unroll
+        for (int t = C::FI; t < NDMA; ++t) issue_one(nxt, kt + NS - 1, t);
+      }
+    } else if constexpr (C::F6) {
       // FP6 stage: one 16x16x128 instruction per fragment pair covers the
       // stage's 128 channels.  W fragments are read whole; A fragments
       // stream through a window read PF ahead; the next stage's loads go
@@ -892,7 +981,7 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   for (int i = 0; i < C::FI; ++i) {
     int64_t m = m0 + wm * C::WM + i * 16 + l16;
     if (m > p.M - 1) m = p.M - 1;
-    sam[i] = (C::GROUP || EPI == EPI_I32) ? p.post : p.sa[m * p.sa_stride] * p.post;
+    sam[i] = (C::NOSC || EPI == EPI_I32) ? p.post : p.sa[m * p.sa_stride] * p.post;
   }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -906,7 +995,7 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t wr = SWIG ? (h ? p.half_n : 0) + n + r : n + r;
-        swv[h][r] = (C::GROUP || EPI == EPI_I32) ? 1.f : p.sw[wr * p.sw_stride];
+        swv[h][r] = (C::NOSC || EPI == EPI_I32) ? 1.f : p.sw[wr * p.sw_stride];
         addv[h][r] = p.bias ? bf16_to_f32(p.bias[wr]) : 0.f;
       }
 #pragma unroll
@@ -1045,6 +1134,20 @@ hipError_t launch_lowrank(const PArgs& p, int epi, hipStream_t s) {
     case EPI_F32: return lr ? launch_pipe<C, EPI_F32, true>(p, s) : launch_pipe<C, EPI_F32, false>(p, s);
     case EPI_SWIGLU:
       return lr ? launch_pipe<C, EPI_SWIGLU, true>(p, s) : launch_pipe<C, EPI_SWIGLU, false>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// MX operands: BF16 | F32 | GATED | SIGMOID on the given tile, SwiGLU on
+// 256 x 256 tiles (gate/up fragment pairs), never the low-rank branch.
+template <class C, class CS>
+hipError_t launch_mx(const PArgs& p, int epi, hipStream_t s) {
+  switch (epi) {
+    case EPI_BF16: return launch_pipe<C, EPI_BF16, false>(p, s);
+    case EPI_F32: return launch_pipe<C, EPI_F32, false>(p, s);
+    case EPI_GATED: return launch_pipe<C, EPI_GATED, false>(p, s);
+    case EPI_SIGMOID: return launch_pipe<C, EPI_SIGMOID, false>(p, s);
+    case EPI_SWIGLU: return launch_pipe<CS, EPI_SWIGLU, false>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1203,6 +1306,28 @@ int launch_qgemm(const GemmArgs& g, hipStream_t s) {
   p.shift = 4 * npacked;
   const bool group = g.a_mode == 2;
   hipError_t e;
+  // 256 x 320 tiles unless 256 x 256 needs fewer tile-area waves on the
+  // 256 CUs (one workgroup per CU): time ~ waves * tile area.
+  auto cost = [&](int64_t bn) {
+    const int64_t tiles = ((g.M + 255) / 256) * ((g.N + bn - 1) / bn);
+    return ((tiles + 255) / 256) * 256 * bn;
+  };
+  const bool wide = cost(320) <= cost(256);
+  if (g.mx) {
+    // the block-scaled instruction applies both scales itself
+    p.xa = static_cast<const uint8_t*>(g.xa);
+    p.xw = static_cast<const uint8_t*>(g.xw);
+    p.post = 1.0f;
+    p.shift = 0;
+    // FP8 operands (8 dwords a fragment) next to the 256 x 320 tile's 160
+    // accumulators would spill inside the K loop: FP8 always takes 256 x 256.
+    using M4W = Cfg<256, 320, 2, 4, false, false, false, false, 4>;
+    using M4N = Cfg<256, 256, 2, 4, false, false, false, false, 4>;
+    using M8N = Cfg<256, 256, 2, 4, false, false, false, false, 8>;
+    if (g.mx == 4) e = wide ? launch_mx<M4W, M4N>(p, g.epilogue, s) : launch_mx<M4N, M4N>(p, g.epilogue, s);
+    else e = launch_mx<M8N, M8N>(p, g.epilogue, s);
+    return e == hipSuccess ? OK : ERR_LAUNCH;
+  }
   if (g.fp6) {
     // the FP6 instruction sums the code products themselves (no nibble shift)
     p.post = 1.0f;
@@ -1226,13 +1351,6 @@ int launch_qgemm(const GemmArgs& g, hipStream_t s) {
     }
     return e == hipSuccess ? OK : ERR_LAUNCH;
   }
-  // 256 x 320 tiles unless 256 x 256 needs fewer tile-area waves on the
-  // 256 CUs (one workgroup per CU): time ~ waves * tile area.
-  auto cost = [&](int64_t bn) {
-    const int64_t tiles = ((g.M + 255) / 256) * ((g.N + bn - 1) / bn);
-    return ((tiles + 255) / 256) * 256 * bn;
-  };
-  const bool wide = cost(320) <= cost(256);
   if (g.fp6) {
     e = wide ? launch_plain<Cfg<256, 320, 2, 4, true, true, false, true>>(p, g.epilogue, s)
              : launch_plain<Cfg<256, 256, 2, 4, true, true, false, true>>(p, g.epilogue, s);

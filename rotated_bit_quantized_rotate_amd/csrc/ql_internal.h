@@ -110,6 +110,18 @@ struct RqArgs {
 };
 
 int launch_rotate_quantize(const RqArgs& a, hipStream_t s);
+
+// MX block quantization (mx_quant.hip): bf16 [M, K] -> optional group-256
+// rotation -> E8M0 scale per 32 elements + FP4 / FP8 elements.
+struct MxArgs {
+  const uint16_t* x;
+  int64_t M, K, ldx;
+  int fmt;         // 4: FP4 E2M1, 8: FP8 E4M3
+  int rotate;
+  void* codes;     // [M, K/2] | [M, K] bytes, dense rows
+  uint8_t* scales; // [M, K/32]
+};
+int launch_mx_quantize(const MxArgs& a, hipStream_t s);
 int launch_lowrank_down(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                         const uint16_t* l1, int rank, uint16_t* lr, hipStream_t s);
 
@@ -121,6 +133,9 @@ struct GemmArgs {
   int64_t M, N, K;
   int a_packed, w_packed;
   int fp6;              // 1: both operands in the FP6 e2m3 layout [rows, 3K/4]
+  int mx;               // 4 / 8: both operands MX FP4 [rows, K/2] / FP8 [rows, K]
+  const void* xa;       // MX: E8M0 scale bytes [M, K/32]
+  const void* xw;       //     and [N, K/32]
   int a_mode, w_mode;   // 0 tensor, 1 row, 2 group64
   const uint16_t* bias;
   const uint16_t* residual;

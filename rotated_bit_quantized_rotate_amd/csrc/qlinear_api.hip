@@ -240,6 +240,58 @@ int qgemm_w4a4_fp6(const uint8_t* a, const float* sa, int a_scale_mode, const ui
   return ql::launch_qgemm(g, static_cast<hipStream_t>(stream)) == QL_OK ? QL_OK : QL_ERR_LAUNCH;
 }
 
+int rotate_quantize_mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int fmt, int rotate, void* codes,
+                       uint8_t* scales, void* stream) {
+  if (fmt != QL_MX_FP4 && fmt != QL_MX_FP8) return QL_ERR_UNSUPPORTED;
+  if (rotate != 0 && rotate != 1) return QL_ERR_UNSUPPORTED;
+  if (M < 0 || K <= 0 || K % 256 != 0 || K >= (int64_t(1) << 23)) return QL_ERR_SHAPE;
+  if (ldx < K || ldx % 8 != 0) return QL_ERR_SHAPE;
+  if (M > 0 && (!x || !codes || !scales)) return QL_ERR_NULL;
+  if (!al16(x) || !al16(codes)) return QL_ERR_ALIGN;
+  int st = check_current_device();
+  if (st != QL_OK) return st;
+  if (M == 0) return QL_OK;
+  ql::MxArgs a{x, M, K, ldx, fmt, rotate, codes, scales};
+  return ql::launch_mx_quantize(a, static_cast<hipStream_t>(stream)) == QL_OK ? QL_OK : QL_ERR_LAUNCH;
+}
+
+int qgemm_mx(const void* a, const uint8_t* sa, const void* w, const uint8_t* sw, int fmt, int64_t M, int64_t N,
+             int64_t K, const uint16_t* bias, const uint16_t* residual, const uint16_t* gate, int epilogue,
+             void* out, int64_t ldo, void* stream) {
+  if (fmt != QL_MX_FP4 && fmt != QL_MX_FP8) return QL_ERR_UNSUPPORTED;
+  if (epilogue != QL_EPI_BF16 && epilogue != QL_EPI_F32 && epilogue != QL_EPI_SIGMOID &&
+      epilogue != QL_EPI_GATED_RESIDUAL && epilogue != QL_EPI_SWIGLU)
+    return QL_ERR_UNSUPPORTED;
+  if (epilogue == QL_EPI_SWIGLU && N % 32 != 0) return QL_ERR_SHAPE;
+  // scale bytes are checked like float scales: present and 4-byte aligned
+  // (the kernel moves a row's 4 stage scales as one dword)
+  int st = validate_gemm_common(a, reinterpret_cast<const float*>(sa), w, reinterpret_cast<const float*>(sw), M,
+                                N, K, bias, out, ldo, epilogue);
+  if (st != QL_OK) return st;
+  if (epilogue == QL_EPI_GATED_RESIDUAL) {
+    if (M > 0 && (!residual || !gate)) return QL_ERR_NULL;
+    if (!al16(residual) || !al2(gate)) return QL_ERR_ALIGN;
+  }
+  if ((st = check_current_device()) != QL_OK) return st;
+  if (M == 0) return QL_OK;
+  ql::GemmArgs g{};
+  g.a = a;
+  g.w = w;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.mx = fmt;
+  g.xa = sa;
+  g.xw = sw;
+  g.bias = bias;
+  g.residual = residual;
+  g.gate = gate;
+  g.epilogue = epilogue;
+  g.out = out;
+  g.ldo = ldo;
+  return ql::launch_qgemm(g, static_cast<hipStream_t>(stream)) == QL_OK ? QL_OK : QL_ERR_LAUNCH;
+}
+
 int qgemm_w8a8(const int8_t* a, const float* sa, int a_scale_mode, const int8_t* w, const float* sw,
                int w_scale_mode, int64_t M, int64_t N, int64_t K, const uint16_t* bias,
                const uint16_t* residual, const uint16_t* gate, int epilogue, void* out, int64_t ldo,

@@ -268,3 +268,123 @@ def assert_outputs_close(got, want, bound, bf16: bool = True, what: str = ""):
         raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outputs off; first at {i.tolist()}: "
                              f"got {got[tuple(i)]!r}, want {ref[tuple(i)]!r}, tol {tol[tuple(i)]:.3e}")
     return float((err / np.maximum(tol, 1e-300)).max(initial=0.0))
+
+
+# ------------------------------------------------------------ MX blocks ----
+#
+# MX block quantization (oracle.mx_ref).  The kernels take the block
+# exponent from their float32 block maximum and divide by it exactly, so with
+# B_i the bound on |x'_gpu - x'_i| and B the largest over the block:
+#   * the exponent can differ from the oracle's only if [a - B, a + B]
+#     straddles a power of two: e_gpu lies between the exponents of a - B
+#     and a + B;
+#   * given e_gpu, the element's pre-rounding value is within B_i / 2^e_gpu
+#     of x'_i / 2^e_gpu, and rounding is monotone, so the code lies between
+#     the roundings of the two ends of that interval.
+# Unrotated bf16 inputs have B = 0: both decisions are the oracle's exactly.
+
+def mx_values(codes, fmt):
+    """Signed element values of element bit patterns."""
+    f = O.MX_FORMATS[fmt]
+    codes = np.asarray(codes, np.int64)
+    mags = O.mx_element_magnitudes(fmt)[codes & (f.sign_bit - 1)]
+    return np.where(codes & f.sign_bit, -mags, mags)
+
+
+def check_mx(got_codes, got_exps, xr, bound, fmt: str, budget: float = FLIP_BUDGET, rows=None):
+    """Check GPU MX element codes [R', K] (unpacked) and block exponents
+    [R', K/32] against the oracle's definition on rotated values xr [R, K]
+    with per-element error bound `bound`.  Returns {"exp_flips",
+    "code_flips", "flip_frac"}: decisions that differ from the oracle's own
+    (all of them inside the near-tie windows above)."""
+    xr = np.asarray(xr, np.float64)
+    R, K = xr.shape
+    sel = np.arange(R) if rows is None else np.asarray(rows)
+    xs = xr[sel]
+    bs = np.asarray(bound, np.float64)[sel]
+    nb = K // O.MX_BLOCK
+    gc = np.asarray(got_codes)
+    ge = np.asarray(got_exps, np.int64)
+    assert gc.shape == xs.shape and ge.shape == (len(sel), nb), (gc.shape, ge.shape)
+    a = np.abs(xs).reshape(-1, nb, 32).max(axis=2)
+    bb = bs.reshape(-1, nb, 32).max(axis=2)
+    ref = O.mx_quantize(xs, fmt)
+    e_lo = O.mx_shared_exponent(np.maximum(a - bb, 0.0), fmt)
+    e_hi = O.mx_shared_exponent(a + bb, fmt)
+    bad = (ge < e_lo) | (ge > e_hi)
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{int(bad.sum())} block exponents outside the window: first {list(i)}: gpu {ge[i]}, "
+                             f"oracle {ref.exps[i]}, block max {a[i]!r} +- {bb[i]:.3e}")
+    sh = np.repeat(ge, 32, axis=1)
+    t = np.ldexp(xs, -sh)
+    d = np.ldexp(bs, -sh)
+    lo = mx_values(O.mx_round_element(t - d, fmt), fmt)
+    hi = mx_values(O.mx_round_element(t + d, fmt), fmt)
+    gv = mx_values(gc, fmt)
+    far = (gv < lo) | (gv > hi)
+    if far.any():
+        i = tuple(np.argwhere(far)[0])
+        raise AssertionError(f"{int(far.sum())} MX codes outside their rounding window: first {list(i)}: gpu "
+                             f"{int(gc[i]):#x} ({gv[i]}), value / scale {t[i]!r} +- {d[i]:.3e}")
+    f = O.MX_FORMATS[fmt]
+    zero_neg = (gc & (f.sign_bit - 1)) == 0
+    assert not (gc[zero_neg] & f.sign_bit).any(), "a zero element carries the sign bit"
+    code_flips = int((gc != ref.codes).sum())
+    frac = code_flips / gc.size if gc.size else 0.0
+    assert frac <= budget, f"MX code flip fraction {frac:.2e} > {budget:.0e}"
+    return {"exp_flips": int((ge != ref.exps).sum()), "code_flips": code_flips, "flip_frac": frac}
+
+
+MX_ALIGN_BITS = 13      # FP8 products kept down to 2^-13 of the group's largest (measured)
+
+
+def mx_product_bound(qa: "O.MXResult", qw: "O.MXResult"):
+    """(y = the oracle's MX product of these codes, bound on the kernel's
+    float32 result).
+
+    Measured on gfx950 (in-bounds probes of the block-scaled 16x16x128
+    instruction): inside a small group of adjacent elements (two neighbours
+    interact, elements 16 apart do not) each product is truncated toward
+    zero to a multiple of 2^(E - 13), E the binade of the group's largest
+    product; group sums, block scales and the sums over blocks and over the
+    K/128 chained instructions are exact to float32 or better.  FP4 products
+    are multiples of 1/4 no larger than 36, so nothing is truncated; FP8
+    products span 36 binades.  Bound: for FP8, per 16-element chunk (which
+    contains the group), 16 products times the grid step of the chunk's
+    largest possible product (max|a| * max|w| over the chunk), times the
+    block scales; plus (127 + K/128) u times the sum of the products'
+    magnitudes for the float32 additions in any order, plus the float32
+    underflow step per addition."""
+    y = O.mx_gemm(qa, qw)
+    f = O.MX_FORMATS[qa.fmt]
+    qa_abs = O.MXResult(np.asarray(qa.codes) & (f.sign_bit - 1), qa.exps, qa.fmt, None)
+    qw_abs = O.MXResult(np.asarray(qw.codes) & (f.sign_bit - 1), qw.exps, qw.fmt, None)
+    mag = O.mx_gemm(qa_abs, qw_abs)
+    K = np.asarray(qa.codes).shape[1]
+    n = 127 + K / 128
+    bound = n * U * mag + K * 2.0 ** -149
+    if qa.fmt == "fp8":
+        M, N = y.shape
+        am = np.abs(qa.elements()).reshape(M, K // 16, 16).max(axis=2)
+        wm = np.abs(qw.elements()).reshape(N, K // 16, 16).max(axis=2)
+        for c in range(K // 16):
+            top = am[:, c][:, None] * wm[:, c][None, :]
+            with np.errstate(divide="ignore"):
+                e = np.floor(np.log2(np.where(top > 0, top, 1.0)))
+            step = np.where(top > 0, np.ldexp(1.0, (e - MX_ALIGN_BITS).astype(np.int64)), 0.0)
+            sc = qa.exps[:, c // 2][:, None] + qw.exps[:, c // 2][None, :]
+            bound = bound + 16 * np.ldexp(step, sc)
+    return y, bound
+
+
+def mx_linear_bound(qa: "O.MXResult", qw: "O.MXResult", bias_bits=None):
+    """(y + bias, bound): the product's bound plus the bias addition's
+    rounding."""
+    y, dy = mx_product_bound(qa, qw)
+    mag = np.abs(y)
+    if bias_bits is not None:
+        b = O.bf16_bits_to_f64(bias_bits)[None, :]
+        y = y + b
+        mag = mag + np.abs(b)
+    return y, dy + 2 * U * mag

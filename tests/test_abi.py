@@ -23,6 +23,7 @@ def test_header_declares_the_entry_points():
                  "qgemm_w4a4", "qgemm_w4a4_fp6", "qgemm_w8a8", "qgemm_w4a4_lowrank", "qgemm_w4a4_fp6_lowrank",
                  "qgemm_grouped",
                  "svdq_split", "svdq_split_workspace_bytes", "svdq_split_noalloc", "svdq_split_noalloc_max_bytes",
+                 "rotate_quantize_mx", "qgemm_mx",
                  "ql_status_string", "ql_device_supported"]:
         assert name in fns
 
@@ -302,6 +303,59 @@ def test_pack_weight_fp6_validation(L):
     assert pw(out=NULL) == -1
     assert pw(w=MISALIGNED) == -3
     assert pw() in (-4, -6)
+
+
+def test_rotate_quantize_mx_validation(L):
+    def mq(**kw):
+        a = dict(x=ALIGNED, M=4, K=256, ldx=256, fmt=4, rot=1, codes=ALIGNED, sc=ALIGNED)
+        a.update(kw)
+        return L.rotate_quantize_mx(a["x"], a["M"], a["K"], a["ldx"], a["fmt"], a["rot"], a["codes"], a["sc"], None)
+
+    assert mq(fmt=6) == -4                        # FP4 or FP8 elements only
+    assert mq(rot=2) == -4
+    assert mq(K=384, ldx=384) == -2               # K % 256
+    assert mq(K=0) == -2
+    assert mq(M=-1) == -2
+    assert mq(ldx=248) == -2                      # ldx >= K
+    assert mq(ldx=260) == -2                      # ldx % 8
+    assert mq(x=NULL) == -1
+    assert mq(sc=NULL) == -1
+    assert mq(codes=MISALIGNED) == -3
+    assert mq(x=MISALIGNED) == -3
+    assert mq(sc=ctypes.c_void_p(0x10001)) in (-4, -6)   # byte scales: any alignment
+    assert mq(M=0, x=NULL, codes=NULL, sc=NULL) in (0, -4, -6)
+    for fmt in (4, 8):
+        for rot in (0, 1):
+            assert mq(fmt=fmt, rot=rot) in (-4, -6)
+
+
+def test_qgemm_mx_validation(L):
+    def gm(**kw):
+        a = dict(a=ALIGNED, sa=ALIGNED, w=ALIGNED, sw=ALIGNED, fmt=4, M=16, N=32, K=256, bias=NULL, res=NULL,
+                 gate=NULL, epi=0, out=ALIGNED, ldo=32)
+        a.update(kw)
+        return L.qgemm_mx(a["a"], a["sa"], a["w"], a["sw"], a["fmt"], a["M"], a["N"], a["K"], a["bias"], a["res"],
+                          a["gate"], a["epi"], a["out"], a["ldo"], None)
+
+    assert gm(fmt=0) == -4
+    assert gm(epi=4) == -4                        # no exact integer result: the sums are float32
+    assert gm(epi=9) == -4
+    assert gm(N=24) == -2
+    assert gm(K=384) == -2
+    assert gm(epi=1, N=48) == -2                  # SwiGLU pairs 16-row gate / up fragments: N % 32
+    assert gm(ldo=16) == -2
+    assert gm(a=NULL) == -1
+    assert gm(sw=NULL) == -1
+    assert gm(sa=ctypes.c_void_p(0x10002)) == -3  # a row's 4 stage scales move as one dword
+    assert gm(w=MISALIGNED) == -3
+    assert gm(epi=2) == -1                        # gated residual needs residual and gate
+    assert gm(epi=2, res=ALIGNED, gate=ALIGNED) in (-4, -6)
+    assert gm(epi=2, res=MISALIGNED, gate=ALIGNED) == -3
+    assert gm(K=1 << 23) == -2                    # 32-bit operand offsets
+    assert gm(M=0) in (0, -4, -6)
+    for fmt in (4, 8):
+        for epi in (0, 1, 3, 5):
+            assert gm(fmt=fmt, epi=epi) in (-4, -6)
 
 
 def test_svdq_split_workspace_bytes(L):
