@@ -424,9 +424,9 @@ def case_attn_mx(Q, W, dev, fmt="fp4"):
     eb = K // 2 if fmt == "fp4" else K          # element bytes per row
     x, w = _bf16_dev(wl.x, dev), _bf16_dev(wl.w, dev)
     codes = torch.empty((M, eb), dtype=torch.uint8, device=dev)
-    sa = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    sa = torch.empty((K // 128, M, 4), dtype=torch.uint8, device=dev)
     wq = torch.empty((N, eb), dtype=torch.uint8, device=dev)
-    sw = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+    sw = torch.empty((K // 128, N, 4), dtype=torch.uint8, device=dev)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     c = Case()
     c.prep_ms = _timed_prep(lambda: Q.rotate_quantize_mx(w, fmt=fmt, codes=wq, scales=sw))

@@ -111,7 +111,10 @@ enum { QL_LAYOUT_I8 = 0, QL_LAYOUT_PACKED = 1, QL_LAYOUT_FP6 = 2 };
  *             [R, K/2] bytes;
  * QL_MX_FP8 : FP8 E4M3 (bias 7, largest magnitude 448, no infinities), one
  *             per byte: [R, K] bytes.
- * Scales: [R, K/32] bytes, row-major.  Zero elements are stored as +0. */
+ * Scales: stage-major [K/128][R][4] bytes -- for each 128-channel slice s
+ * of K, the 4 scale bytes of row 0 (blocks 4s .. 4s+3), then of row 1, ...
+ * (a GEMM tile reads one slice's scales for consecutive rows as consecutive
+ * bytes).  Zero elements are stored as +0. */
 enum { QL_MX_FP4 = 4, QL_MX_FP8 = 8 };
 
 /* ---- GEMM epilogues ---------------------------------------------------- */
@@ -277,7 +280,8 @@ int qgemm_w4a4_fp6(const uint8_t* a, const float* sa, int a_scale_mode,
  *   fmt    QL_MX_FP4 | QL_MX_FP8 (else QL_ERR_UNSUPPORTED)
  *   rotate 1: rotate each 256-group by H/16 first; 0: quantize x as is
  *   codes  out: element bytes per fmt, dense rows (16-byte aligned)
- *   scales out: [M, K/32] E8M0 bytes, dense rows                           */
+ *   scales out: [K/128][M][4] E8M0 bytes (stage-major, see QL_MX_FP4),
+ *          4-byte aligned                                                   */
 int rotate_quantize_mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                        int fmt, int rotate, void* codes, uint8_t* scales,
                        void* stream);
@@ -293,8 +297,8 @@ int rotate_quantize_mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
  * truncated toward zero to a multiple of 2^-13 times the binade of the
  * group's largest product, so an FP8 block product can differ from the
  * exact one by up to about 2^-13 of that product per element.
- *   a, sa    activation elements [M, K/2 | K] and scales [M, K/32]
- *   w, sw    weight elements [N, K/2 | K] and scales [N, K/32]
+ *   a, sa    activation elements [M, K/2 | K] and scales [K/128][M][4]
+ *   w, sw    weight elements [N, K/2 | K] and scales [K/128][N][4]
  *            (rotate_quantize_mx with the same fmt; scale pointers 4-byte
  *            aligned)
  *   fmt      QL_MX_FP4 | QL_MX_FP8

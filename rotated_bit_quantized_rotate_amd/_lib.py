@@ -238,14 +238,15 @@ def _mxfmt(f):
 
 def rotate_quantize_mx(x, fmt="fp4", rotate=True, codes=None, scales=None, stream=None):
     """x: bf16 [R, K] -> (element bytes [R, K/2] (fp4) | [R, K] (fp8) uint8,
-    E8M0 scale bytes [R, K/32] uint8).  Serves activations and weights."""
+    E8M0 scale bytes uint8 [K/128, R, 4], stage-major).  Serves activations
+    and weights."""
     assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
     R, K = x.shape
     f = _mxfmt(fmt)
     if codes is None:
         codes = torch.empty((R, K // 2 if f == QL_MX_FP4 else K), dtype=torch.uint8, device=x.device)
     if scales is None:
-        scales = torch.empty((R, K // 32), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((K // 128, R, 4), dtype=torch.uint8, device=x.device)
     st = lib().rotate_quantize_mx(_ptr(x), R, K, x.stride(0), f, int(bool(rotate)), _ptr(codes), _ptr(scales),
                                   _stream(stream))
     _check("rotate_quantize_mx", st)

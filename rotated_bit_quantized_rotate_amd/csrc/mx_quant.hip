@@ -15,9 +15,16 @@
 //   element = x / 2^e rounded to the nearest element value, ties to even,
 //             saturating at the largest magnitude (6 | 448)
 //   stored  : element bit patterns (every zero as +0) and the byte e + 127.
+// Scale bytes are stored stage-major, [K/128][R][4]: for every 128-channel
+// slice of K, the 4 block scales of row 0, then of row 1, ...  A GEMM tile
+// then finds one slice's scales for consecutive rows in consecutive bytes.
 //
 // A 16-lane slot owns one 256-channel unit of a row; lane t holds channels
-// 16 t .. 16 t + 15, so a block is the lane pair (2b, 2b + 1).  With the
+// 16 t .. 16 t + 15, so a block is the lane pair (2b, 2b + 1).  Units are
+// visited row-fastest (unit u: row u % M, column group u / M), so the 16
+// slots of a workgroup write the scales of 16 consecutive rows of a slice
+// as 64 consecutive bytes; lanes 0 and 8 of a slot gather the 4 scales of
+// their slice and store them as one dword.  With the
 // rotation the slot first forms z = H x = 16 x' (hadamard256), so the block
 // exponent of x' is that of max|z| minus 4 and x' / 2^e = z * 2^-(e + 4).
 // The division by 2^e is an exact ldexp; the rounding is
@@ -61,7 +68,7 @@ __device__ __forceinline__ uint32_t fp8_pos_zero(uint32_t w) {
 }
 
 template <int FMT, bool ROT>
-__global__ __launch_bounds__(kMxThreads) void mx_quant_kernel(MxArgs a, int64_t units, int64_t upr) {
+__global__ __launch_bounds__(kMxThreads) void mx_quant_kernel(MxArgs a, int64_t units) {
   const int tid = threadIdx.x;
   const int slot = tid >> 4;
   const int t = tid & 15;
@@ -71,8 +78,9 @@ __global__ __launch_bounds__(kMxThreads) void mx_quant_kernel(MxArgs a, int64_t 
     // 16-lane rows); lanes past the data hold zeros and store nothing
     const int64_t u = base + slot;
     const bool uok = u < units;
-    const int64_t row = uok ? u / upr : 0;
-    const int64_t c0 = (uok ? u - row * upr : 0) * 256 + t * 16;  // the lane's first channel
+    const int64_t g = uok ? u / a.M : 0;
+    const int64_t row = uok ? u - g * a.M : 0;
+    const int64_t c0 = g * 256 + t * 16;  // the lane's first channel
     const bool ok = uok && c0 < a.K;
     uint4 r0 = make_uint4(0, 0, 0, 0), r1 = make_uint4(0, 0, 0, 0);
     if (ok) {
@@ -103,7 +111,13 @@ __global__ __launch_bounds__(kMxThreads) void mx_quant_kernel(MxArgs a, int64_t 
       s[k] = __builtin_amdgcn_ldexpf(v[k], sh);
       if (FMT == 8) s[k] = __builtin_amdgcn_fmed3f(s[k], -448.0f, 448.0f);
     }
+    // scale bytes of blocks 4 (t / 8) .. + 3 gathered into lanes 0 and 8
+    const int sb = e + 127;
+    const int sb1 = __shfl_down(sb, 2, 16), sb2 = __shfl_down(sb, 4, 16), sb3 = __shfl_down(sb, 6, 16);
     if (!ok) continue;
+    if ((t & 7) == 0)
+      *reinterpret_cast<uint32_t*>(a.scales + (c0 / 128) * (a.M * 4) + row * 4) =
+          (uint32_t)sb | ((uint32_t)sb1 << 8) | ((uint32_t)sb2 << 16) | ((uint32_t)sb3 << 24);
     if (FMT == 4) {
       uint32_t d0 = 0, d1 = 0;
       d0 = fp4_pair<0>(d0, s[0], s[1]);
@@ -127,17 +141,16 @@ __global__ __launch_bounds__(kMxThreads) void mx_quant_kernel(MxArgs a, int64_t 
       }
       *reinterpret_cast<uint4*>(static_cast<uint8_t*>(a.codes) + row * a.K + c0) = make_uint4(d[0], d[1], d[2], d[3]);
     }
-    if ((t & 1) == 0) a.scales[row * (a.K / 32) + c0 / 32] = (uint8_t)(e + 127);
   }
 }
 
 template <int FMT, bool ROT>
 int launch_fmt(const MxArgs& a, hipStream_t s) {
-  const int64_t upr = (a.K + 255) / 256;
+  const int64_t upr = a.K / 256;
   const int64_t units = a.M * upr;
   const int64_t blocks = (units + 15) / 16;
   const int grid = (int)(blocks < kMxMaxGrid ? blocks : kMxMaxGrid);
-  hipLaunchKernelGGL((mx_quant_kernel<FMT, ROT>), dim3(grid), dim3(kMxThreads), 0, s, a, units, upr);
+  hipLaunchKernelGGL((mx_quant_kernel<FMT, ROT>), dim3(grid), dim3(kMxThreads), 0, s, a, units);
   return hipGetLastError() == hipSuccess ? OK : ERR_LAUNCH;
 }
 

@@ -136,7 +136,7 @@ struct PArgs {
   const uint8_t* w;
   const float* sa;
   const float* sw;
-  const uint8_t* xa;         // MX: E8M0 block scales [M, K/32], [N, K/32]
+  const uint8_t* xa;         // MX: E8M0 block scales [K/128][M][4], [K/128][N][4]
   const uint8_t* xw;
   int64_t M, N, K;
   int sa_stride, sw_stride;  // tensor / row scales: 0 or 1
@@ -162,8 +162,12 @@ struct PArgs {
 // E2M1 (64 bytes per row per stage) or FP8 E4M3 (128 bytes) elements, one
 // E8M0 scale per 32 elements along K, applied by the block-scaled matrix
 // instruction itself; fp32 accumulation.
+// SUB = 2: each LDS stage holds 256 channels (two 128-channel sub-stages),
+// so 4-bit operand rows are 128 contiguous bytes a stage -- whole cache
+// lines, half the line requests per channel of 64-byte rows (the loads'
+// cost follows the number of lines they touch) and half the barriers.
 template <int BM_, int BN_, int WGM_, int WGN_, bool AP_, bool WP_, bool GROUP_ = false, bool F6_ = false,
-          int MX_ = 0>
+          int MX_ = 0, int MAXS_ = 3, int SUB_ = 1>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int WGM = WGM_, WGN = WGN_;   // wave grid
@@ -171,6 +175,8 @@ struct Cfg {
   static constexpr int NT = 64 * NW;
   static constexpr bool AP = AP_, WP = WP_, GROUP = GROUP_, F6 = F6_;
   static constexpr int MX = MX_;
+  static constexpr int SUB = SUB_;         // 128-channel sub-stages per LDS stage
+  static constexpr int BKS = BK * SUB;     // channels per LDS stage
   static constexpr bool FMMA = F6 || MX != 0;   // float matrix instruction, fp32 accumulators
   static constexpr bool NOSC = GROUP || MX != 0;  // accumulators already carry both scales
   static constexpr bool SCL = GROUP || MX != 0;   // scales ride in the LDS ring
@@ -178,17 +184,19 @@ struct Cfg {
   static constexpr int WN = BN / WGN;       // wave tile cols
   static constexpr int FI = WM / 16;
   static constexpr int FJ = WN / 16;
-  static constexpr int ARB = F6 ? BK * 3 / 4 : (MX ? BK * MX / 8 : (AP ? BK / 2 : BK));  // bytes per A row per stage
-  static constexpr int WRB = F6 ? BK * 3 / 4 : (MX ? BK * MX / 8 : (WP ? BK / 2 : BK));
+  static constexpr int ARB = F6 ? BKS * 3 / 4 : (MX ? BKS * MX / 8 : (AP ? BKS / 2 : BKS));  // bytes per A row per stage
+  static constexpr int WRB = F6 ? BKS * 3 / 4 : (MX ? BKS * MX / 8 : (WP ? BKS / 2 : BKS));
   static_assert(!F6 || (AP && WP), "FP6 operands: both sides");
   static_assert(MX == 0 || MX == 4 || MX == 8, "MX element width");
   static_assert(!MX || (!AP && !WP && !GROUP && !F6), "MX operands have their own layout");
+  static_assert(SUB == 1 || (SUB == 2 && !GROUP && !F6 && ((AP && WP) || MX == 4)),
+                "256-channel stages: packed INT4 on both sides or MXFP4");
   static constexpr int SA = BM * ARB;
   static constexpr int SW = BN * WRB;
   // group-64: two groups of fp32 scales per row; MX: the 4 E8M0 bytes of
   // the stage's 4 blocks per row.  Padded so every wave issues the same
   // number of 256-byte loads.
-  static constexpr int SCB = GROUP ? 8 * (BM + BN) : (MX ? 4 * (BM + BN) : 0);
+  static constexpr int SCB = GROUP ? 8 * (BM + BN) : (MX ? 4 * SUB * (BM + BN) : 0);
   static constexpr int SC = (SCB + 256 * NW - 1) / (256 * NW) * (256 * NW);
   static constexpr int STAGE = SA + SW + SC;
   static constexpr int A_INSTR = SA / 1024;  // 1 KB per 16-byte-per-lane load
@@ -202,7 +210,8 @@ struct Cfg {
   static constexpr int W_HI = (W_INSTR + NW - 1) / NW;  // waves < W_SPLIT issue W_HI
   static constexpr int W_SPLIT = W_INSTR - (W_HI - 1) * NW;
   static constexpr int NDMA = A_PER_WAVE + W_HI + S_PER_WAVE;
-  static constexpr int NSTAGE = (3 * STAGE <= kLdsBytes) ? 3 : 2;  // LDS ring depth
+  // LDS ring depth: the deepest of MAXS_, 3, 2 stages that fits
+  static constexpr int NSTAGE = (MAXS_ >= 4 && 4 * STAGE <= kLdsBytes) ? 4 : ((3 * STAGE <= kLdsBytes) ? 3 : 2);
   static_assert(NSTAGE * STAGE <= kLdsBytes, "LDS ring too large");
   static_assert((NSTAGE - 2) * NDMA < 64, "vmcnt range");
   static_assert(!GROUP || FI % 4 == 0, "group scales are read 4 rows at a time");
@@ -270,12 +279,13 @@ __device__ __forceinline__ void grouped_tile(int bl, int tiles_m, int tiles_n, i
   tile_n = inb / gm;
 }
 
-// One output tile of the GEMM on the workgroup's LDS ring (sm0, sm1, sm2:
-// C::STAGE bytes each; sm2 is used only with a 3-stage ring).
+// One output tile of the GEMM on the workgroup's LDS ring (sm0 .. sm3:
+// C::STAGE bytes each; the first C::NSTAGE of them are used).
 template <class C, int EPI, bool LOWRANK>
 __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n, uint8_t* const sm0,
-                                          uint8_t* const sm1, uint8_t* const sm2) {
+                                          uint8_t* const sm1, uint8_t* const sm2, uint8_t* const sm3) {
   constexpr int NS = C::NSTAGE;
+  auto ring = [&](int i) -> uint8_t* { return i == 0 ? sm0 : (i == 1 ? sm1 : (i == 2 ? sm2 : sm3)); };
   constexpr bool SWIG = EPI == EPI_SWIGLU;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -289,10 +299,10 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   const int64_t m0 = (int64_t)tile_m * C::BM;
   const int64_t n0 = (int64_t)tile_n * (SWIG ? C::BN / 2 : C::BN);
 
-  // row strides in bytes: a stage holds BK channels of a row in ARB / WRB bytes
-  const int64_t lda = p.K / BK * C::ARB;
-  const int64_t ldw = p.K / BK * C::WRB;
-  const int KT = (int)(p.K / BK);
+  // row strides in bytes: a stage holds BKS channels of a row in ARB / WRB bytes
+  const int64_t lda = p.K / C::BKS * C::ARB;
+  const int64_t ldw = p.K / C::BKS * C::WRB;
+  const int KT = (int)(p.K / C::BKS);
 
   // ---- global -> LDS loads -------------------------------------------------
   // Load t (0 .. NDMA-1) of this wave's share of stage kt: the first
@@ -338,13 +348,17 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
     const int pos = (wave + C::NW * ts) * 64 + lane;
     int64_t e = 0;  // float index relative to p.sa (A part) or p.sw (W part)
     if (C::MX) {
-      // MX: position pos holds the 4 scale bytes of tile row pos (A rows,
-      // then W rows in tile-row order); e is a byte offset into p.xa / p.xw
-      if (pos < C::BM) {
-        const int64_t gr = m0 + pos > p.M - 1 ? p.M - 1 : m0 + pos;
-        e = gr * (p.K / 32);
-      } else if (pos < C::BM + C::BN) {
-        e = w_row_of<C, SWIG>(p, n0, pos - C::BM) * (p.K / 32);
+      // MX: position h (BM + BN) + pos holds the 4 scale bytes of tile row
+      // pos (A rows, then W rows in tile-row order) for sub-stage h; e is
+      // the byte offset of that row in slice h of the stage's first slice
+      // of p.xa / p.xw (stage-major [K/128][rows][4]: the 64 rows of one
+      // load are 256 consecutive bytes)
+      const int h = pos / (C::BM + C::BN), pr = pos % (C::BM + C::BN);
+      if (h < C::SUB && pr < C::BM) {
+        const int64_t gr = m0 + pr > p.M - 1 ? p.M - 1 : m0 + pr;
+        e = h * p.M * 4 + gr * 4;
+      } else if (h < C::SUB) {
+        e = h * p.N * 4 + w_row_of<C, SWIG>(p, n0, pr - C::BM) * 4;
       }
       s_vo[ts] = (uint32_t)e;
       continue;
@@ -363,6 +377,8 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
     }  // padding slots load the first W scale, never read back
     s_vo[ts] = (uint32_t)(e * 4);
   }
+  // MX scale slices: bytes per stage (SUB 128-channel slices) of xa / xw
+  const uint32_t xsa = (uint32_t)(p.M * 4 * C::SUB), xsw = (uint32_t)(p.N * 4 * C::SUB);
   // The stage advance goes into the 32-bit lane offset (one VALU add), so
   // the SGPR bases stay loop-invariant.
   const uint8_t* const a_base = p.a + a_row0;
@@ -379,7 +395,9 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
     } else if (C::MX) {
       const int ts = t - C::A_PER_WAVE - C::W_HI;
       const int si = wave + C::NW * ts;
-      dma_b32(si * 64 < C::BM ? p.xa : p.xw, s_vo[C::SCL ? ts : 0] + (uint32_t)(kt * 4),
+      const int h0 = si * 64 / (C::BM + C::BN);
+      const bool sa_side = h0 < C::SUB && si * 64 % (C::BM + C::BN) < C::BM;
+      dma_b32(sa_side ? p.xa : p.xw, s_vo[C::SCL ? ts : 0] + (uint32_t)kt * (sa_side ? xsa : xsw),
               st + C::SA + C::SW + si * 256);
     } else if (C::GROUP) {
       const int ts = t - C::A_PER_WAVE - C::W_HI;
@@ -446,15 +464,27 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   const int a6_lo = a_row * 96 + (swz6(a_row, 4 + (lg >> 1)) << 4) + 8 * (lg & 1);
   const int w6_hi = w_row * 96 + (swz6(w_row, lg) << 4);
   const int w6_lo = w_row * 96 + (swz6(w_row, 4 + (lg >> 1)) << 4) + 8 * (lg & 1);
-  // MX: lane group lg supplies K-block lg of the stage (32 elements) and
-  // its scale.  FP4: the block is the 16 bytes of chunk lg.  FP8: the
-  // instruction takes 16 elements of each of two blocks per lane -- K
+  // MX: lane group lg supplies K-block lg of the sub-stage (32 elements)
+  // and its scale.  FP4: the block is the 16 bytes of chunk 4 h + lg.  FP8:
+  // the instruction takes 16 elements of each of two blocks per lane -- K
   // [16 lg, 16 lg + 16) in its first four dwords and [64 + 16 lg, ...) in
   // the last four (measured on gfx950; the scale of lane group b still
   // covers K [32 b, 32 b + 32)), so the lane reads chunks lg and 4 + lg.
-  const int ax0 = a_row * C::ARB + (swz<C::ARB, false>(a_row, lg) << 4);
+  // Packed INT4 (tensor / row scales): chunk 4 h + lg, both halves (kk).
+  // Two sub-stages (MXFP4, packed INT4): sub-stage h, lane group lg takes
+  // the 32 channels of chunk 2 lg + h of the 256-channel stage -- the chunk
+  // pattern of the int8 reads (kk, 2 + kk, ...) that the swizzle serves
+  // without bank conflicts; an MX lane's scale is byte (2 lg + h) % 4 of
+  // slice lg / 2.
+  constexpr bool MXI = (C::MX == 4 || (C::AP && C::WP && !C::GROUP)) && C::SUB == 2;
+  int axp[C::SUB], wxp[C::SUB];
+#pragma unroll
+  for (int h = 0; h < C::SUB; ++h) {
+    const int ch = MXI ? 2 * lg + h : 4 * h + lg;
+    axp[h] = a_row * C::ARB + (swz<C::ARB, false>(a_row, ch) << 4);
+    wxp[h] = w_row * C::WRB + (swz<C::WRB, false>(w_row, ch) << 4);
+  }
   const int ax1 = a_row * C::ARB + (swz<C::ARB, false>(a_row, 4 + lg) << 4);
-  const int wx0 = w_row * C::WRB + (swz<C::WRB, false>(w_row, lg) << 4);
   const int wx1 = w_row * C::WRB + (swz<C::WRB, false>(w_row, 4 + lg) << 4);
   // group scales: byte offsets inside the stage's scale block.  A lane reads
   // the scales of its fragments 4f .. 4f+3 as one b128 at 64 f + 4 l16, so
@@ -496,7 +526,7 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   for (int s0 = 0; s0 < NS - 1; ++s0)
     if (s0 < KT) {
 #pragma unroll
-      for (int t = 0; t < NDMA; ++t) issue_one(s0 == 0 ? sm0 : sm1, s0, t);
+      for (int t = 0; t < NDMA; ++t) issue_one(ring(s0), s0, t);
     }
 
   // Tensor / row scales: the MFMA group of a stage's last A fragment is
@@ -513,15 +543,19 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   for (int sc = 0; sc < NS; ++sc) {
     const int kt = kb + sc;
     if (kt >= KT) break;
-    uint8_t* const cur = sc == 0 ? sm0 : (sc == 1 ? sm1 : sm2);
+    uint8_t* const cur = ring(sc);
     const int sn = (sc + NS - 1) % NS;  // stage that kt + NS - 1 lands in
-    uint8_t* const nxt = sn == 0 ? sm0 : (sn == 1 ? sm1 : sm2);
-    // Stage kt has landed once only the later stages (at most NS-2 of them)
-    // are still in flight; the barrier then publishes every wave's part and
-    // guarantees all waves finished reading the buffer the next load reuses.
-    if (NS == 3 && kt + 1 < KT) {
+    uint8_t* const nxt = ring(sn);
+    // Stage kt has landed once only the later stages (at most NS-2 of them,
+    // fewer at the end of K) are still in flight; the barrier then
+    // publishes every wave's part and guarantees all waves finished reading
+    // the buffer the next load reuses.
+    if (NS >= 3 && kt + NS - 2 < KT) {
       if (w_hi) wait_vmcnt<(NS - 2) * NDMA>();
       else wait_vmcnt<(NS - 2) * (NDMA - 1)>();
+    } else if (NS == 4 && kt + 1 < KT) {
+      if (w_hi) wait_vmcnt<NDMA>();
+      else wait_vmcnt<NDMA - 1>();
     } else {
       wait_vmcnt<0>();
     }
@@ -543,37 +577,44 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
         const uint4 g = *reinterpret_cast<const uint4*>(base + o1);
         return v8i{(int)h.x, (int)h.y, (int)h.z, (int)h.w, (int)g.x, (int)g.y, (int)g.z, (int)g.w};
       };
-      v8i wf[C::FJ];
-      int wsc[C::FJ];
 #pragma unroll
-      for (int j = 0; j < C::FJ; ++j) {
-        wf[j] = frag(Ws + j * 16 * C::WRB, wx0, wx1);
-        wsc[j] = Ss[(C::BM + w_row + 16 * j) * 4 + lg];
-      }
-      int asc[C::FI];
-#pragma unroll
-      for (int i = 0; i < C::FI; ++i) asc[i] = Ss[(a_row + 16 * i) * 4 + lg];
-      constexpr int PF = 2;
-      v8i abuf[PF + 1];
-#pragma unroll
-      for (int q = 0; q < PF; ++q) abuf[q] = frag(As + q * 16 * C::ARB, ax0, ax1);
-#pragma unroll
-      for (int i = 0; i < C::FI; ++i) {
-        if (i > 0 && (4 * i) % C::FI < 4) stage_prio((4 * i) / C::FI);
-        if (i + PF < C::FI) abuf[(i + PF) % (PF + 1)] = frag(As + (i + PF) * 16 * C::ARB, ax0, ax1);
-        if (dma && i < NDMA) issue_one(nxt, kt + NS - 1, i);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int h = 0; h < C::SUB; ++h) {
+        // the lane's scale byte: slice and byte of its block in this sub-stage
+        const int sb = MXI ? (lg >> 1) * (C::BM + C::BN) * 4 + ((2 * lg + h) & 3)
+                           : h * (C::BM + C::BN) * 4 + lg;
+        v8i wf[C::FJ];
+        int wsc[C::FJ];
 #pragma unroll
         for (int j = 0; j < C::FJ; ++j) {
-          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], abuf[i % (PF + 1)], acc[j][i], FMT,
-                                                                      FMT, 0, wsc[j], 0, asc[i]);
-          asm volatile("" : "+v"(acc[j][i]));
+          wf[j] = frag(Ws + j * 16 * C::WRB, wxp[h], wx1);
+          wsc[j] = Ss[sb + (C::BM + w_row + 16 * j) * 4];
         }
-        __builtin_amdgcn_sched_barrier(0);
+        int asc[C::FI];
+#pragma unroll
+        for (int i = 0; i < C::FI; ++i) asc[i] = Ss[sb + (a_row + 16 * i) * 4];
+        constexpr int PF = 2;
+        v8i abuf[PF + 1];
+#pragma unroll
+        for (int q = 0; q < PF; ++q) abuf[q] = frag(As + q * 16 * C::ARB, axp[h], ax1);
+#pragma unroll
+        for (int i = 0; i < C::FI; ++i) {
+          const int step = h * C::FI + i;  // position in the stage's MFMA groups
+          if (step > 0 && (4 * step) % (C::SUB * C::FI) < 4) stage_prio((4 * step) / (C::SUB * C::FI));
+          if (i + PF < C::FI) abuf[(i + PF) % (PF + 1)] = frag(As + (i + PF) * 16 * C::ARB, axp[h], ax1);
+          if (dma && step < NDMA) issue_one(nxt, kt + NS - 1, step);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = 0; j < C::FJ; ++j) {
+            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], abuf[i % (PF + 1)], acc[j][i],
+                                                                        FMT, FMT, 0, wsc[j], 0, asc[i]);
+            asm volatile("" : "+v"(acc[j][i]));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       if (dma) {
 #pragma unroll
-        for (int t = C::FI; t < NDMA; ++t) issue_one(nxt, kt + NS - 1, t);
+        for (int t = C::SUB * C::FI; t < NDMA; ++t) issue_one(nxt, kt + NS - 1, t);
       }
     } else if constexpr (C::F6) {
       // FP6 stage: one 16x16x128 instruction per fragment pair covers the
@@ -668,6 +709,10 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
       const uint8_t* As = cur;
       const uint8_t* Ws = As + C::SA;
       const uint8_t* Ss = Ws + C::SW;
+      constexpr int PF = 2;
+      constexpr int NQ = 2 * C::FI;
+#pragma unroll
+      for (int h = 0; h < C::SUB; ++h) {
       // W fragments: packed -> one b128 per fragment carries both halves (kk);
       // int8 -> one b128 per fragment and half.
       uint4 wraw[GK ? 1 : C::FJ];
@@ -684,71 +729,81 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
       } else {
 #pragma unroll
         for (int j = 0; j < C::FJ; ++j) {
-          wraw[j] = *reinterpret_cast<const uint4*>(Ws + w_off + j * 16 * C::WRB);
+          wraw[j] = *reinterpret_cast<const uint4*>(Ws + (C::WP ? wxp[h] : w_off) + j * 16 * C::WRB);
           if (!C::WP) wraw1[j] = *reinterpret_cast<const uint4*>(Ws + w_off1 + j * 16 * C::WRB);
         }
       }
       // A fragments: int8 -> streamed through a small window read PF ahead;
       // packed -> one b128 per fragment carries both halves.
-      constexpr int PF = 2;
-      constexpr int NQ = 2 * C::FI;
       v4i abuf[PF + 1];
-      uint4 araw[(C::AP && !GK) ? C::FI : 1];
+      // packed A (tensor / row scales): the 8-byte half kk of fragment i's
+      // chunk, streamed through a window read PF ahead like int8 A
+      uint2 pbuf[PF + 1];
+      auto read_pa = [&](int qq) {
+        return *reinterpret_cast<const uint2*>(As + axp[h] + 8 * (qq / C::FI) + (qq % C::FI) * 16 * C::ARB);
+      };
       if (C::AP) {
         if (!GK) {
 #pragma unroll
-          for (int i = 0; i < C::FI; ++i)
-            araw[i] = *reinterpret_cast<const uint4*>(As + a_off[0] + i * 16 * C::ARB);
+          for (int q = 0; q < PF; ++q) pbuf[q] = read_pa(q);
         }
       } else {
 #pragma unroll
         for (int q = 0; q < PF; ++q)
           abuf[q] = *reinterpret_cast<const v4i*>(As + a_off[q / C::FI] + (q % C::FI) * 16 * C::ARB);
       }
-      if (DEFER && kt > 0) {
+      if (DEFER && kt > 0 && h == 0) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < C::FJ; ++j)
           acc[j][C::FI - 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bw1[j], af_def, acc[j][C::FI - 1], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
+      // Two sub-stages: both halves are unpacked at once (after the deferred
+      // group, which still reads the previous high half), so the packed
+      // words die here -- three copies of the W fragments do not fit.
+      constexpr bool EARLY_W = C::SUB == 2 && C::WP && !GK;
       if (!GK) {
 #pragma unroll
-        for (int j = 0; j < C::FJ; ++j)
+        for (int j = 0; j < C::FJ; ++j) {
           bw0[j] = C::WP ? unpack_lo(wraw[j].x, wraw[j].y)
                          : v4i{(int)wraw[j].x, (int)wraw[j].y, (int)wraw[j].z, (int)wraw[j].w};
+          if (EARLY_W) bw1[j] = unpack_lo(wraw[j].z, wraw[j].w);
+        }
       }
       v4f sav[C::GROUP ? C::FI / 4 : 1];
       v4f swv[C::GROUP ? C::FJ : 1];
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         const int kk = q / C::FI, i = q % C::FI;
-        if (q > 0 && (4 * q) % NQ < 4) stage_prio((4 * q) / NQ);
+        const int step = h * NQ + q;  // position in the stage's MFMA groups
+        if (step > 0 && (4 * step) % (C::SUB * NQ) < 4) stage_prio((4 * step) / (C::SUB * NQ));
         v4i af;
         if (C::AP && GK) {
           const uint2 h = *reinterpret_cast<const uint2*>(As + a_off[kk] + i * 16 * C::ARB);
           af = unpack_lo(h.x, h.y);
         } else if (C::AP) {
-          af = kk == 0 ? unpack_lo(araw[i].x, araw[i].y) : unpack_lo(araw[i].z, araw[i].w);
+          if (q + PF < NQ) pbuf[(q + PF) % (PF + 1)] = read_pa(q + PF);
+          af = unpack_lo(pbuf[q % (PF + 1)].x, pbuf[q % (PF + 1)].y);
         } else {
           if (q + PF < NQ)
             abuf[(q + PF) % (PF + 1)] = *reinterpret_cast<const v4i*>(
                 As + a_off[(q + PF) / C::FI] + ((q + PF) % C::FI) * 16 * C::ARB);
           af = abuf[q % (PF + 1)];
         }
-        if (dma && (q % 2) == 0 && q / 2 < NDMA) issue_one(nxt, kt + NS - 1, q / 2);
+        if (dma && (step % 2) == 0 && step / 2 < NDMA) issue_one(nxt, kt + NS - 1, step / 2);
         // second-half W fragments, spread over the first half's MFMA groups
-        if (!GK && kk == 0 && i < C::FJ)
+        if (!GK && !EARLY_W && kk == 0 && i < C::FJ)
           bw1[i] = C::WP ? unpack_lo(wraw[i].z, wraw[i].w)
                          : v4i{(int)wraw1[i].x, (int)wraw1[i].y, (int)wraw1[i].z, (int)wraw1[i].w};
-        if (!GK && kk == 0 && i == C::FI - 1) {
+        if (!GK && !EARLY_W && kk == 0 && i == C::FI - 1) {
 #pragma unroll
           for (int j = C::FI; j < C::FJ; ++j)
             bw1[j] = C::WP ? unpack_lo(wraw[j].z, wraw[j].w)
                            : v4i{(int)wraw1[j].x, (int)wraw1[j].y, (int)wraw1[j].z, (int)wraw1[j].w};
         }
         if (!C::GROUP) {
-          if (DEFER && q == NQ - 1) {
+          if (DEFER && q == NQ - 1 && h == C::SUB - 1) {
             af_def = af;  // issued after the next barrier (or after the loop)
           } else {
             __builtin_amdgcn_sched_barrier(0);
@@ -788,10 +843,11 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // any loads not yet issued (only if NDMA > NQ / 2)
+      }  // sub-stages
+      // any loads not yet issued (only if NDMA > SUB * NQ / 2)
       if (dma) {
 #pragma unroll
-        for (int t = NQ / 2; t < NDMA; ++t) issue_one(nxt, kt + NS - 1, t);
+        for (int t = C::SUB * NQ / 2; t < NDMA; ++t) issue_one(nxt, kt + NS - 1, t);
       }
     }
   }
@@ -831,10 +887,10 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
     // the factor vector sits behind the staging rows of the last ring array
     constexpr int SVOFF = (RPA * PITCH + 15) / 16 * 16;
     static_assert(SVOFF + 4 * NV <= C::STAGE, "factor vector must fit the ring");
-    float* const sv = reinterpret_cast<float*>((NS == 3 ? sm2 : sm1) + SVOFF);
+    float* const sv = reinterpret_cast<float*>(ring(NS - 1) + SVOFF);
     auto row_ptr = [&](int r) -> uint8_t* {
       const int a = r / RPA, o = (r % RPA) * PITCH;
-      return a == 0 ? sm0 + o : (a == 1 ? sm1 + o : sm2 + o);
+      return ring(a) + o;
     };
     // The band barriers below order LDS only (lds_barrier: the wave's LDS
     // accesses complete, then s_barrier).  __syncthreads would also wait for
@@ -942,7 +998,7 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   const int l2pitch = p.rank * 2 + 16;
   auto l2s_row = [&](int t) -> uint8_t* {
     const int a = t / L2R;
-    return (a == 0 ? sm0 : (a == 1 ? sm1 : sm2)) + (t - a * L2R) * l2pitch;
+    return ring(a) + (t - a * L2R) * l2pitch;
   };
   if constexpr (LOWRANK) {
     static_assert(L2R * (128 * 2 + 16) <= C::STAGE, "staged L2 columns must fit the ring");
@@ -1094,10 +1150,11 @@ __global__ __launch_bounds__(C::NT, 1) void qgemm_pipe_kernel(PArgs p) {
   // the LDS ring: one array per stage
   __shared__ __attribute__((aligned(16))) uint8_t sm0[C::STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sm1[C::STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t sm2[C::NSTAGE == 3 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sm2[C::NSTAGE >= 3 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sm3[C::NSTAGE == 4 ? C::STAGE : 16];
   int tile_m, tile_n;
   grouped_tile(xcd_linear(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, p.group_m, tile_m, tile_n);
-  pipe_tile<C, EPI, LOWRANK>(p, tile_m, tile_n, sm0, sm1, sm2);
+  pipe_tile<C, EPI, LOWRANK>(p, tile_m, tile_n, sm0, sm1, sm2, sm3);
 }
 
 template <class C, int EPI, bool LOWRANK>
@@ -1179,9 +1236,10 @@ static_assert(kGroupedLds <= kLdsBytes, "grouped LDS ring too large");
 template <class C>
 __device__ __forceinline__ void grouped_body(const PArgs& p, int tile_m, int tile_n, bool sigmoid,
                                              uint8_t* const r) {
-  uint8_t* const r2 = C::NSTAGE == 3 ? r + 2 * C::STAGE : r;
-  if (sigmoid) pipe_tile<C, EPI_SIGMOID, false>(p, tile_m, tile_n, r, r + C::STAGE, r2);
-  else pipe_tile<C, EPI_BF16, false>(p, tile_m, tile_n, r, r + C::STAGE, r2);
+  uint8_t* const r2 = C::NSTAGE >= 3 ? r + 2 * C::STAGE : r;
+  uint8_t* const r3 = C::NSTAGE == 4 ? r + 3 * C::STAGE : r;
+  if (sigmoid) pipe_tile<C, EPI_SIGMOID, false>(p, tile_m, tile_n, r, r + C::STAGE, r2, r3);
+  else pipe_tile<C, EPI_BF16, false>(p, tile_m, tile_n, r, r + C::STAGE, r2, r3);
 }
 
 struct GSeg {
@@ -1321,8 +1379,8 @@ int launch_qgemm(const GemmArgs& g, hipStream_t s) {
     p.shift = 0;
     // FP8 operands (8 dwords a fragment) next to the 256 x 320 tile's 160
     // accumulators would spill inside the K loop: FP8 always takes 256 x 256.
-    using M4W = Cfg<256, 320, 2, 4, false, false, false, false, 4>;
-    using M4N = Cfg<256, 256, 2, 4, false, false, false, false, 4>;
+    using M4W = Cfg<256, 320, 2, 4, false, false, false, false, 4, 3, 2>;
+    using M4N = Cfg<256, 256, 2, 4, false, false, false, false, 4, 3, 2>;
     using M8N = Cfg<256, 256, 2, 4, false, false, false, false, 8>;
     if (g.mx == 4) e = wide ? launch_mx<M4W, M4N>(p, g.epilogue, s) : launch_mx<M4N, M4N>(p, g.epilogue, s);
     else e = launch_mx<M8N, M8N>(p, g.epilogue, s);

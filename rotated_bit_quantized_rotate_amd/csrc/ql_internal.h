@@ -119,7 +119,7 @@ struct MxArgs {
   int fmt;         // 4: FP4 E2M1, 8: FP8 E4M3
   int rotate;
   void* codes;     // [M, K/2] | [M, K] bytes, dense rows
-  uint8_t* scales; // [M, K/32]
+  uint8_t* scales; // [K/128][M][4] (stage-major)
 };
 int launch_mx_quantize(const MxArgs& a, hipStream_t s);
 int launch_lowrank_down(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
@@ -134,8 +134,8 @@ struct GemmArgs {
   int a_packed, w_packed;
   int fp6;              // 1: both operands in the FP6 e2m3 layout [rows, 3K/4]
   int mx;               // 4 / 8: both operands MX FP4 [rows, K/2] / FP8 [rows, K]
-  const void* xa;       // MX: E8M0 scale bytes [M, K/32]
-  const void* xw;       //     and [N, K/32]
+  const void* xa;       // MX: E8M0 scale bytes [K/128][M][4]
+  const void* xw;       //     and [K/128][N][4]
   int a_mode, w_mode;   // 0 tensor, 1 row, 2 group64
   const uint16_t* bias;
   const uint16_t* residual;

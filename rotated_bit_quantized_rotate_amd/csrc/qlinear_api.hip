@@ -247,7 +247,7 @@ int rotate_quantize_mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int
   if (M < 0 || K <= 0 || K % 256 != 0 || K >= (int64_t(1) << 23)) return QL_ERR_SHAPE;
   if (ldx < K || ldx % 8 != 0) return QL_ERR_SHAPE;
   if (M > 0 && (!x || !codes || !scales)) return QL_ERR_NULL;
-  if (!al16(x) || !al16(codes)) return QL_ERR_ALIGN;
+  if (!al16(x) || !al16(codes) || !al4(scales)) return QL_ERR_ALIGN;
   int st = check_current_device();
   if (st != QL_OK) return st;
   if (M == 0) return QL_OK;

@@ -58,8 +58,14 @@ def _gpu_mx(Q, xb, fmt, rotate):
     return codes, scales
 
 
+def _rowmajor(scales):
+    """Stage-major scale bytes [K/128, R, 4] -> row-major [R, K/32]."""
+    s = np.asarray(scales.cpu().numpy() if hasattr(scales, "cpu") else scales)
+    return np.ascontiguousarray(s.transpose(1, 0, 2).reshape(s.shape[1], -1))
+
+
 def _unpack(codes, scales, fmt):
-    return O.mx_unpack(codes.cpu().numpy(), scales.cpu().numpy(), fmt)
+    return O.mx_unpack(codes.cpu().numpy(), _rowmajor(scales), fmt)
 
 
 def _check(codes, exps, xb, fmt, rotate, rows=None):
@@ -77,7 +83,7 @@ def _check(codes, exps, xb, fmt, rotate, rows=None):
 def test_mx_quantize_matches_oracle(Q, M, K, fmt, rotate):
     xb = _rand_bf16(M * 3 + K, (M, K), outliers=max(1, K // 100), row_spread=True)
     codes, scales = _gpu_mx(Q, xb, fmt, rotate)
-    assert codes.shape == (M, K // 2 if fmt == "fp4" else K) and scales.shape == (M, K // 32)
+    assert codes.shape == (M, K // 2 if fmt == "fp4" else K) and scales.shape == (K // 128, M, 4)
     c, e = _unpack(codes, scales, fmt)
     st = _check(c, e, xb, fmt, rotate)
     print(f"exp flips {st['exp_flips']}, code flips {st['code_flips']} ({st['flip_frac']:.2e})")
@@ -138,7 +144,9 @@ def test_mx_quantize_edge_values_exact(Q, fmt):
     np.testing.assert_array_equal(c, ref.codes)
     data, sb = O.mx_pack(ref)
     np.testing.assert_array_equal(codes.cpu().numpy(), data)       # the byte layout too
-    np.testing.assert_array_equal(scales.cpu().numpy(), sb)
+    np.testing.assert_array_equal(_rowmajor(scales), sb)
+    # stage-major: slice s holds row r's blocks 4s .. 4s+3 at [s, r, :]
+    np.testing.assert_array_equal(scales.cpu().numpy()[1, 3], sb[3, 4:8])
 
 
 @pytest.mark.parametrize("fmt", ["fp4", "fp8"])
@@ -154,7 +162,7 @@ def test_mx_quantize_strided_rows_and_empty(Q, fmt):
     _check(c, e, xb[:, :K].copy(), fmt, True)
     empty = torch.empty((0, K), dtype=torch.bfloat16, device="cuda")
     codes, scales = Q.rotate_quantize_mx(empty, fmt=fmt)
-    assert codes.shape[0] == 0 and scales.shape[0] == 0
+    assert codes.shape[0] == 0 and scales.shape[1] == 0
 
 
 # ------------------------------------------------------------------- GEMM --
@@ -267,7 +275,7 @@ def test_mx_full_size_sampled_rows(Q, fmt):
     torch.cuda.synchronize()
     rows = np.array([0, 1, 255, 256, 2047, 3000, 4094, 4095])
     xs = wl.x[rows]
-    a_c, a_e = O.mx_unpack(ca[rows].cpu().numpy(), sa[rows].cpu().numpy(), fmt)
+    a_c, a_e = O.mx_unpack(ca[rows].cpu().numpy(), _rowmajor(sa)[rows], fmt)
     st = _check(a_c, a_e, xs, fmt, True)
     w_c, w_e = _unpack(cw, sw, fmt)
     stw = _check(w_c, w_e, wl.w, fmt, True)
