@@ -87,6 +87,7 @@ GEMM_KERNELS = {
     "attn_proj_w4a4_fp6": ("qgemm_w4a4_fp6", "4096x5120x5120", ["qgemm_pipe.hip"]),
     "attn_proj_mxfp4": ("qgemm_mx_fp4", "4096x5120x5120", ["qgemm_pipe.hip"]),
     "attn_proj_mxfp8": ("qgemm_mx_fp8", "4096x5120x5120", ["qgemm_pipe.hip"]),
+    "svdq_gateup_mxfp4": ("qgemm_mx_lowrank_fp4", "4096x5120x40960", ["qgemm_pipe.hip"]),
     "svdq_split_gateup": ("svdq_split", "40960x5120_r32", ["svdq_split.hip"]),
     "ffdown_w8a8": ("qgemm_w8a8", "4096x20480x5120", ["qgemm_pipe.hip"]),
     "svdq_gateup": ("qgemm_w4a4_lowrank", "4096x5120x40960", ["qgemm_pipe.hip"]),
@@ -378,17 +379,23 @@ def case_attn_fp6(Q, W, dev):
 def mx_cpu_baseline(wl, fmt, target_s=12.0, one_thread_s=3.0):
     """The MX oracle on a row sample of X against the pre-quantized weights:
     rotate, block-quantize, the block-scaled product (float64 BLAS per
-    32-channel block), bf16 rounding."""
+    32-channel block), the low-rank branch and epilogue when the workload
+    has them, bf16 rounding."""
     import oracle as O
 
     threads = _blas_threads()
     qw = O.quantize_mx(wl.w, fmt)
+    l1 = None if wl.l1 is None else O.bf16_bits_to_f64(wl.l1)
+    l2 = None if wl.l2 is None else O.bf16_bits_to_f64(wl.l2)
 
     def run(rows):
         xs = np.ascontiguousarray(wl.x[:rows])
         t0 = time.perf_counter()
         qa = O.quantize_mx(xs, fmt)
-        O.f64_to_bf16_bits(O.mx_gemm(qa, qw))
+        y = O.mx_gemm(qa, qw)
+        if l1 is not None:
+            y = y + (O.bf16_bits_to_f64(xs) @ l1) @ l2
+        O.f64_to_bf16_bits(O.epilogue(y, wl.epilogue))
         return time.perf_counter() - t0
 
     def sample(target):
@@ -401,7 +408,8 @@ def mx_cpu_baseline(wl, fmt, target_s=12.0, one_thread_s=3.0):
            "kind": "oracle", "cpu_model": _cpu_model(),
            "sample": f"{rows} of {wl.M} rows of X against all {wl.N} outputs (weights pre-quantized): rotate, "
                      f"MX {fmt} block quantization, block-scaled product via float64 BLAS per 32-channel "
-                     f"block, bf16 rounding; {t:.2f} s wall on {threads} BLAS threads"}
+                     f"block{', rank-%d branch' % wl.l1.shape[1] if wl.l1 is not None else ''}, {wl.epilogue} "
+                     f"epilogue, bf16 rounding; {t:.2f} s wall on {threads} BLAS threads"}
     try:
         from threadpoolctl import threadpool_limits
         with threadpool_limits(1):
@@ -450,6 +458,46 @@ def case_attn_mx(Q, W, dev, fmt="fp4"):
                 "M": M, "N": N, "K": K, "global_batch": M, "parallelism": "single GPU"}
     c.wl = wl
     c.cpu_fn = lambda s: mx_cpu_baseline(wl, fmt, s)
+    return c
+
+
+def case_svdq_mx(Q, W, dev):
+    """The SVDQuant gate|up layer in MXFP4 -- the pages' NVFP4 r32 build on
+    gfx950's block-scaled FP4 instruction: the same X, W, rank-32 factors and
+    SwiGLU as the INT4 group-64 workload, W and X as MXFP4 blocks."""
+    import torch
+    wl = W.svdq_gateup()
+    M, N, K = wl.M, wl.N, wl.K
+    r = wl.l1.shape[1]
+    x, w = _bf16_dev(wl.x, dev), _bf16_dev(wl.w, dev)
+    l1, l2 = _bf16_dev(wl.l1, dev), _bf16_dev(wl.l2, dev)
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    sa = torch.empty((K // 128, M, 4), dtype=torch.uint8, device=dev)
+    lr = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+    wq = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    sw = torch.empty((K // 128, N, 4), dtype=torch.uint8, device=dev)
+    out = torch.empty((M, N // 2), dtype=torch.bfloat16, device=dev)
+    c = Case()
+    c.prep_ms = _timed_prep(lambda: Q.rotate_quantize_mx(w, fmt="fp4", codes=wq, scales=sw))
+    c.launches = [
+        ("prologue", lambda: Q.rotate_quantize_mx(x, fmt="fp4", codes=codes, scales=sa, l1=l1, lr=lr)),
+        ("gemm", lambda: Q.qgemm_mx_lowrank(codes, sa, wq, sw, K, fmt="fp4", lr=lr, l2=l2, epilogue="swiglu",
+                                            out=out)),
+    ]
+    c.ops = wl.int_ops
+    c.gemm_launches = 1
+    c.pro_bytes = M * K * 2 + K * r * 2 + M * K // 2 + M * K // 32 + M * r * 2
+    c.gemm_bytes = (M + N) * (K // 2 + K // 32) + M * r * 2 + r * N * 2 + M * (N // 2) * 2
+    c.metric = ("effective TOPS + % FP4 MFMA peak, MXFP4 SVDQuant gate|up GEMM + rank-32 low-rank + SwiGLU "
+                "M=4096 K=5120 N=40960 (block-scaled matrix instruction)")
+    c.dtype = "fp4 e2m1 elements x E8M0 block-32 scales (MX), fp32 accumulate, bf16 rank-32 branch, bf16 out"
+    c.peak = FP4_MFMA_PEAK_TOPS
+    c.config = {"workload": "SVDQuant fused gate|up in MXFP4 (the NVFP4 r32 build on gfx950): X bf16 [4096x5120], "
+                            "W [40960x5120] MXFP4 with group-256 Hadamard, bf16 rank-32 L1 [5120x32] / "
+                            "L2 [32x40960], SwiGLU -> bf16 [4096x20480]",
+                "M": M, "N": N, "K": K, "rank": r, "global_batch": M, "parallelism": "single GPU"}
+    c.wl = wl
+    c.cpu_fn = lambda s: mx_cpu_baseline(wl, "fp4", s)
     return c
 
 
@@ -806,6 +854,7 @@ def case_stack_fused(Q, W, dev, grouped=False):
 CASES = {"attn_proj_w4a4": case_attn, "attn_proj_w4a4_fp6": case_attn_fp6, "svdq_split_gateup": case_svdq_split,
          "attn_proj_mxfp4": lambda Q, W, dev: case_attn_mx(Q, W, dev, "fp4"),
          "attn_proj_mxfp8": lambda Q, W, dev: case_attn_mx(Q, W, dev, "fp8"),
+         "svdq_gateup_mxfp4": case_svdq_mx,
          "ffdown_w8a8": case_ffdown, "svdq_gateup": case_svdq,
          "svdq_gateup_fp6": lambda Q, W, dev: case_svdq(Q, W, dev, fp6=True),
          "stack": case_stack, "stack_fused": case_stack_fused,
@@ -1015,7 +1064,7 @@ def main(argv=None):
     other = None
     if args.workload == "attn_proj_w4a4" and not args.no_other_gemms:
         other = {}
-        for name in ("ffdown_w8a8", "svdq_gateup", "attn_proj_mxfp4"):
+        for name in ("ffdown_w8a8", "svdq_gateup", "attn_proj_mxfp4", "svdq_gateup_mxfp4"):
             oc = CASES[name](Q, W, dev)
             rec = gemm_only_record(oc, float(oc.ops), dev)
             rec["workload"] = oc.config["workload"]

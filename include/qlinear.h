@@ -281,9 +281,13 @@ int qgemm_w4a4_fp6(const uint8_t* a, const float* sa, int a_scale_mode,
  *   rotate 1: rotate each 256-group by H/16 first; 0: quantize x as is
  *   codes  out: element bytes per fmt, dense rows (16-byte aligned)
  *   scales out: [K/128][M][4] E8M0 bytes (stage-major, see QL_MX_FP4),
- *          4-byte aligned                                                   */
+ *          4-byte aligned
+ *   l1, rank, lr  optional SVDQuant down-projection, exactly as
+ *          rotate_quantize_act: lr[M, rank] = bf16(x @ l1) with the
+ *          UNROTATED x (l1 == NULL requires rank == 0)                      */
 int rotate_quantize_mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                        int fmt, int rotate, void* codes, uint8_t* scales,
+                       const uint16_t* l1, int rank, uint16_t* lr,
                        void* stream);
 
 /* MX block-scaled GEMM + epilogue on gfx950's block-scaled matrix
@@ -312,6 +316,25 @@ int qgemm_mx(const void* a, const uint8_t* sa, const void* w, const uint8_t* sw,
              int fmt, int64_t M, int64_t N, int64_t K,
              const uint16_t* bias, const uint16_t* residual, const uint16_t* gate,
              int epilogue, void* out, int64_t ldo, void* stream);
+
+/* The SVDQuant layer in MX form: qgemm_mx's product plus the bf16 low-rank
+ * branch, y = mx(a) mx(w)^T (+ bias) + lr @ l2, then the epilogue -- the
+ * pages' "NVFP4 r32" build, an FP4 SVDQuant checkpoint with a rank-32 branch
+ * (model card "Krea 2 Turbo Nunchaku Lite INT4 r32", section "Benchmark";
+ * README "Krea-2-SVDQuant-ComfyUI", sections "Low-rank refinement" and
+ * "LoRA").  On gfx950 its FP4 runs as MXFP4 (see rotate_quantize_mx).
+ *   a, sa, w, sw, fmt   as qgemm_mx
+ *   lr       bf16 [M, rank] (rotate_quantize_mx's down-projection), dense rows
+ *   l2       bf16 [rank, N], row-major, 16-byte aligned
+ *   rank     0..128, a multiple of 16 (0: no branch)
+ *   bias     NULL or bf16 [N]
+ *   epilogue QL_EPI_BF16 | QL_EPI_F32 | QL_EPI_SWIGLU (N a multiple of 32;
+ *            gate rows first)
+ *   out      [M, N] (SWIGLU: [M, N/2]), row stride ldo                      */
+int qgemm_mx_lowrank(const void* a, const uint8_t* sa, const void* w, const uint8_t* sw,
+                     int fmt, const uint16_t* lr, const uint16_t* l2, int rank,
+                     int64_t M, int64_t N, int64_t K, const uint16_t* bias,
+                     int epilogue, void* out, int64_t ldo, void* stream);
 
 /* W8A8 GEMM + dequant epilogue for the protected ff.down projections (model
  * card "Krea 2 Turbo OrbitQuant W4A4", sections "Fused transformer" and

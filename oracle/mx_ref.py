@@ -262,14 +262,24 @@ def quantize_mx(x_bits, fmt, rotate_on: bool = True) -> MXResult:
 
 
 def mx_linear(x_bits, w_bits, fmt, rotate_on: bool = True, bias_bits=None, epi: str = "bf16",
-              residual_bits=None, gate_bits=None):
+              residual_bits=None, gate_bits=None, l1_bits=None, l2_bits=None):
     """End-to-end MX linear.  Returns (out_bf16_bits, y_fp64, qa, qw), y the
-    product plus bias before the epilogue."""
+    product plus bias (plus the low-rank branch) before the epilogue.
+
+    With l1_bits [K, r] / l2_bits [r, N] this is the SVDQuant layer in MX
+    form -- the pages' "NVFP4 r32" build (model card "Krea 2 Turbo Nunchaku
+    Lite INT4 r32", section "Benchmark": an FP4 build with a rank-32 branch;
+    README "Krea-2-SVDQuant-ComfyUI", section "Low-rank refinement": W is a
+    quantized part plus a small full-precision product): the branch
+    (X L1) L2 is added with the unrotated bf16 X, as in the integer layer."""
     qa = quantize_mx(x_bits, fmt, rotate_on)
     qw = quantize_mx(w_bits, fmt, rotate_on)
     y = mx_gemm(qa, qw)
     if bias_bits is not None:
         y = y + bf16_bits_to_f64(bias_bits)[None, :]
+    if l1_bits is not None and l2_bits is not None and np.asarray(l1_bits).shape[1] > 0:
+        x = bf16_bits_to_f64(x_bits)
+        y = y + (x @ bf16_bits_to_f64(l1_bits)) @ bf16_bits_to_f64(l2_bits)
     res = bf16_bits_to_f64(residual_bits) if residual_bits is not None else None
     gate = bf16_bits_to_f64(gate_bits) if gate_bits is not None else None
     return f64_to_bf16_bits(epilogue(y, epi, res, gate)), y, qa, qw

@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     pack_weight_int4,
     qgemm_grouped,
     qgemm_mx,
+    qgemm_mx_lowrank,
     qgemm_w4a4,
     qgemm_w4a4_fp6,
     qgemm_w4a4_fp6_lowrank,

@@ -79,8 +79,9 @@ _SIGNATURES = {
     "svdq_split_workspace_bytes": (_i64, [_i64, _i64, _i, _i, _i]),
     "svdq_split_noalloc": (_i, [_p, _i64, _i64, _i64, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]),
     "svdq_split_noalloc_max_bytes": (_i64, []),
-    "rotate_quantize_mx": (_i, [_p, _i64, _i64, _i64, _i, _i, _p, _p, _p]),
+    "rotate_quantize_mx": (_i, [_p, _i64, _i64, _i64, _i, _i, _p, _p, _p, _i, _p, _p]),
     "qgemm_mx": (_i, [_p, _p, _p, _p, _i, _i64, _i64, _i64, _p, _p, _p, _i, _p, _i64, _p]),
+    "qgemm_mx_lowrank": (_i, [_p, _p, _p, _p, _i, _p, _p, _i, _i64, _i64, _i64, _p, _i, _p, _i64, _p]),
 }
 
 _LIB = None
@@ -236,10 +237,11 @@ def _mxfmt(f):
     return MX_FORMATS[f] if isinstance(f, str) else int(f)
 
 
-def rotate_quantize_mx(x, fmt="fp4", rotate=True, codes=None, scales=None, stream=None):
+def rotate_quantize_mx(x, fmt="fp4", rotate=True, codes=None, scales=None, l1=None, lr=None, stream=None):
     """x: bf16 [R, K] -> (element bytes [R, K/2] (fp4) | [R, K] (fp8) uint8,
     E8M0 scale bytes uint8 [K/128, R, 4], stage-major).  Serves activations
-    and weights."""
+    and weights.  With l1 (bf16 [K, rank]) also returns lr = x @ l1 (bf16
+    [R, rank], unrotated x) as a third value."""
     assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
     R, K = x.shape
     f = _mxfmt(fmt)
@@ -247,10 +249,13 @@ def rotate_quantize_mx(x, fmt="fp4", rotate=True, codes=None, scales=None, strea
         codes = torch.empty((R, K // 2 if f == QL_MX_FP4 else K), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((K // 128, R, 4), dtype=torch.uint8, device=x.device)
+    rank = 0 if l1 is None else l1.shape[1]
+    if l1 is not None and lr is None:
+        lr = torch.empty((R, rank), dtype=torch.bfloat16, device=x.device)
     st = lib().rotate_quantize_mx(_ptr(x), R, K, x.stride(0), f, int(bool(rotate)), _ptr(codes), _ptr(scales),
-                                  _stream(stream))
+                                  _ptr(l1), rank, _ptr(lr), _stream(stream))
     _check("rotate_quantize_mx", st)
-    return codes, scales
+    return (codes, scales) if l1 is None else (codes, scales, lr)
 
 
 def _out(out, M, cols, epi, device):
@@ -299,6 +304,20 @@ def qgemm_mx(a, sa, w, sw, K, fmt="fp4", bias=None, residual=None, gate=None, ep
     st = lib().qgemm_mx(_ptr(a), _ptr(sa), _ptr(w), _ptr(sw), _mxfmt(fmt), M, N, K, _ptr(bias), _ptr(residual),
                         _ptr(gate), epi, _ptr(out), out.stride(0), _stream(stream))
     _check("qgemm_mx", st)
+    return out
+
+
+def qgemm_mx_lowrank(a, sa, w, sw, K, fmt="fp4", lr=None, l2=None, bias=None, epilogue="swiglu", out=None,
+                     stream=None):
+    """The MX GEMM plus the low-rank branch lr @ l2 (SVDQuant in MX form)."""
+    M = a.shape[0]
+    N = w.shape[0]
+    epi = _epi(epilogue)
+    rank = 0 if lr is None else lr.shape[1]
+    out = _out(out, M, N // 2 if epi == QL_EPI_SWIGLU else N, epi, a.device)
+    st = lib().qgemm_mx_lowrank(_ptr(a), _ptr(sa), _ptr(w), _ptr(sw), _mxfmt(fmt), _ptr(lr), _ptr(l2), rank, M, N, K,
+                                _ptr(bias), epi, _ptr(out), out.stride(0), _stream(stream))
+    _check("qgemm_mx_lowrank", st)
     return out
 
 

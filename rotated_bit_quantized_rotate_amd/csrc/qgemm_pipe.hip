@@ -1196,9 +1196,18 @@ hipError_t launch_lowrank(const PArgs& p, int epi, hipStream_t s) {
 }
 
 // MX operands: BF16 | F32 | GATED | SIGMOID on the given tile, SwiGLU on
-// 256 x 256 tiles (gate/up fragment pairs), never the low-rank branch.
+// 256 x 256 tiles (gate/up fragment pairs); with the low-rank branch
+// (rank > 0) BF16 | F32 on the given tile and SwiGLU on 256 x 256.
 template <class C, class CS>
 hipError_t launch_mx(const PArgs& p, int epi, hipStream_t s) {
+  if (p.rank > 0) {
+    switch (epi) {
+      case EPI_BF16: return launch_pipe<C, EPI_BF16, true>(p, s);
+      case EPI_F32: return launch_pipe<C, EPI_F32, true>(p, s);
+      case EPI_SWIGLU: return launch_pipe<CS, EPI_SWIGLU, true>(p, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (epi) {
     case EPI_BF16: return launch_pipe<C, EPI_BF16, false>(p, s);
     case EPI_F32: return launch_pipe<C, EPI_F32, false>(p, s);

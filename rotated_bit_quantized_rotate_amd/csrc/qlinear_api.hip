@@ -241,18 +241,62 @@ int qgemm_w4a4_fp6(const uint8_t* a, const float* sa, int a_scale_mode, const ui
 }
 
 int rotate_quantize_mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int fmt, int rotate, void* codes,
-                       uint8_t* scales, void* stream) {
+                       uint8_t* scales, const uint16_t* l1, int rank, uint16_t* lr, void* stream) {
   if (fmt != QL_MX_FP4 && fmt != QL_MX_FP8) return QL_ERR_UNSUPPORTED;
   if (rotate != 0 && rotate != 1) return QL_ERR_UNSUPPORTED;
   if (M < 0 || K <= 0 || K % 256 != 0 || K >= (int64_t(1) << 23)) return QL_ERR_SHAPE;
   if (ldx < K || ldx % 8 != 0) return QL_ERR_SHAPE;
   if (M > 0 && (!x || !codes || !scales)) return QL_ERR_NULL;
+  if (!l1 && rank != 0) return QL_ERR_SHAPE;
+  if (l1) {
+    if (rank < 16 || rank > 128 || rank % 16 != 0) return QL_ERR_SHAPE;
+    if (M > 0 && !lr) return QL_ERR_NULL;
+    if (!al16(l1) || !al16(lr)) return QL_ERR_ALIGN;
+  }
   if (!al16(x) || !al16(codes) || !al4(scales)) return QL_ERR_ALIGN;
   int st = check_current_device();
   if (st != QL_OK) return st;
   if (M == 0) return QL_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
   ql::MxArgs a{x, M, K, ldx, fmt, rotate, codes, scales};
-  return ql::launch_mx_quantize(a, static_cast<hipStream_t>(stream)) == QL_OK ? QL_OK : QL_ERR_LAUNCH;
+  if (ql::launch_mx_quantize(a, s) != QL_OK) return QL_ERR_LAUNCH;
+  if (l1 && ql::launch_lowrank_down(x, M, K, ldx, l1, rank, lr, s) != QL_OK) return QL_ERR_LAUNCH;
+  return QL_OK;
+}
+
+int qgemm_mx_lowrank(const void* a, const uint8_t* sa, const void* w, const uint8_t* sw, int fmt,
+                     const uint16_t* lr, const uint16_t* l2, int rank, int64_t M, int64_t N, int64_t K,
+                     const uint16_t* bias, int epilogue, void* out, int64_t ldo, void* stream) {
+  if (fmt != QL_MX_FP4 && fmt != QL_MX_FP8) return QL_ERR_UNSUPPORTED;
+  if (epilogue != QL_EPI_BF16 && epilogue != QL_EPI_SWIGLU && epilogue != QL_EPI_F32) return QL_ERR_UNSUPPORTED;
+  if (epilogue == QL_EPI_SWIGLU && N % 32 != 0) return QL_ERR_SHAPE;
+  int st = validate_gemm_common(a, reinterpret_cast<const float*>(sa), w, reinterpret_cast<const float*>(sw), M,
+                                N, K, bias, out, ldo, epilogue);
+  if (st != QL_OK) return st;
+  if (rank < 0 || rank > 128 || rank % 16 != 0) return QL_ERR_SHAPE;
+  if (rank > 0) {
+    if (M > 0 && (!lr || !l2)) return QL_ERR_NULL;
+    if (!al16(lr) || !al16(l2)) return QL_ERR_ALIGN;
+  }
+  if ((st = check_current_device()) != QL_OK) return st;
+  if (M == 0) return QL_OK;
+  ql::GemmArgs g{};
+  g.a = a;
+  g.w = w;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.mx = fmt;
+  g.xa = sa;
+  g.xw = sw;
+  g.lr = lr;
+  g.l2 = l2;
+  g.rank = rank;
+  g.bias = bias;
+  g.epilogue = epilogue;
+  g.out = out;
+  g.ldo = ldo;
+  return ql::launch_qgemm(g, static_cast<hipStream_t>(stream)) == QL_OK ? QL_OK : QL_ERR_LAUNCH;
 }
 
 int qgemm_mx(const void* a, const uint8_t* sa, const void* w, const uint8_t* sw, int fmt, int64_t M, int64_t N,

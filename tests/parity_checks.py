@@ -43,7 +43,7 @@ import numpy as np
 import oracle as O
 
 U = 2.0 ** -24          # float32 unit roundoff
-BF16_U = 2.0 ** -9      # bf16 unit roundoff (8 significant bits)
+BF16_U = 2.0 ** -8      # bf16 unit roundoff: 8 significant bits, |fl(x) - x| <= 2^-8 |x|
 FLIP_BUDGET = 1e-4
 
 

@@ -23,7 +23,7 @@ def test_header_declares_the_entry_points():
                  "qgemm_w4a4", "qgemm_w4a4_fp6", "qgemm_w8a8", "qgemm_w4a4_lowrank", "qgemm_w4a4_fp6_lowrank",
                  "qgemm_grouped",
                  "svdq_split", "svdq_split_workspace_bytes", "svdq_split_noalloc", "svdq_split_noalloc_max_bytes",
-                 "rotate_quantize_mx", "qgemm_mx",
+                 "rotate_quantize_mx", "qgemm_mx", "qgemm_mx_lowrank",
                  "ql_status_string", "ql_device_supported"]:
         assert name in fns
 
@@ -307,9 +307,10 @@ def test_pack_weight_fp6_validation(L):
 
 def test_rotate_quantize_mx_validation(L):
     def mq(**kw):
-        a = dict(x=ALIGNED, M=4, K=256, ldx=256, fmt=4, rot=1, codes=ALIGNED, sc=ALIGNED)
+        a = dict(x=ALIGNED, M=4, K=256, ldx=256, fmt=4, rot=1, codes=ALIGNED, sc=ALIGNED, l1=NULL, rank=0, lr=NULL)
         a.update(kw)
-        return L.rotate_quantize_mx(a["x"], a["M"], a["K"], a["ldx"], a["fmt"], a["rot"], a["codes"], a["sc"], None)
+        return L.rotate_quantize_mx(a["x"], a["M"], a["K"], a["ldx"], a["fmt"], a["rot"], a["codes"], a["sc"],
+                                    a["l1"], a["rank"], a["lr"], None)
 
     assert mq(fmt=6) == -4                        # FP4 or FP8 elements only
     assert mq(rot=2) == -4
@@ -324,6 +325,12 @@ def test_rotate_quantize_mx_validation(L):
     assert mq(x=MISALIGNED) == -3
     assert mq(sc=ctypes.c_void_p(0x10001)) == -3  # a row's 4 slice scales leave as one dword
     assert mq(M=0, x=NULL, codes=NULL, sc=NULL) in (0, -4, -6)
+    assert mq(rank=16) == -2                      # rank without l1
+    assert mq(l1=ALIGNED, rank=8, lr=ALIGNED) == -2
+    assert mq(l1=ALIGNED, rank=144, lr=ALIGNED) == -2
+    assert mq(l1=ALIGNED, rank=32, lr=NULL) == -1
+    assert mq(l1=MISALIGNED, rank=32, lr=ALIGNED) == -3
+    assert mq(l1=ALIGNED, rank=32, lr=ALIGNED) in (-4, -6)
     for fmt in (4, 8):
         for rot in (0, 1):
             assert mq(fmt=fmt, rot=rot) in (-4, -6)
@@ -356,6 +363,32 @@ def test_qgemm_mx_validation(L):
     for fmt in (4, 8):
         for epi in (0, 1, 3, 5):
             assert gm(fmt=fmt, epi=epi) in (-4, -6)
+
+
+def test_qgemm_mx_lowrank_validation(L):
+    def gl(**kw):
+        a = dict(a=ALIGNED, sa=ALIGNED, w=ALIGNED, sw=ALIGNED, fmt=4, lr=ALIGNED, l2=ALIGNED, rank=32, M=16, N=64,
+                 K=256, bias=NULL, epi=1, out=ALIGNED, ldo=32)
+        a.update(kw)
+        return L.qgemm_mx_lowrank(a["a"], a["sa"], a["w"], a["sw"], a["fmt"], a["lr"], a["l2"], a["rank"], a["M"],
+                                  a["N"], a["K"], a["bias"], a["epi"], a["out"], a["ldo"], None)
+
+    assert gl(fmt=6) == -4
+    assert gl(epi=2) == -4                        # bf16 | f32 | swiglu only
+    assert gl(epi=5) == -4
+    assert gl(epi=4) == -4
+    assert gl(N=48) == -2                         # SwiGLU: N % 32
+    assert gl(rank=8) == -2
+    assert gl(rank=144) == -2
+    assert gl(lr=NULL) == -1
+    assert gl(l2=NULL) == -1
+    assert gl(l2=MISALIGNED) == -3
+    assert gl(rank=0, lr=NULL, l2=NULL) in (-4, -6)  # no branch: the pointers may be NULL
+    assert gl(K=384) == -2
+    assert gl(ldo=16) == -2                       # SwiGLU writes N/2 columns
+    for fmt in (4, 8):
+        for epi in (0, 1, 3):
+            assert gl(fmt=fmt, epi=epi, ldo=64) in (-4, -6)
 
 
 def test_svdq_split_workspace_bytes(L):

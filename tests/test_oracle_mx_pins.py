@@ -172,3 +172,25 @@ def test_linear_rotation_matches_rotating_first():
     bound = nrm(da) * nrm(wr, 2) + nrm(ar, 2) * nrm(dw) + nrm(da) * nrm(dw)
     assert nrm(y - exact) <= bound * (1 + 1e-9)
     assert np.allclose(ar @ wr.T, exact, rtol=0, atol=1e-12)
+
+
+def test_lowrank_branch_adds_the_exact_factor_product():
+    # the branch is (X L1) L2 on the unrotated input: brute-force sums on a tiny case
+    rng = np.random.default_rng(5)
+    xb = O.f64_to_bf16_bits(rng.standard_normal((3, 256)))
+    wb = O.f64_to_bf16_bits(rng.standard_normal((32, 256)) * 0.02)
+    l1 = O.f64_to_bf16_bits(rng.standard_normal((256, 16)) * 0.1)
+    l2 = O.f64_to_bf16_bits(rng.standard_normal((16, 32)) * 0.1)
+    _, y0, _, _ = O.mx_linear(xb, wb, "fp4")
+    _, y1, _, _ = O.mx_linear(xb, wb, "fp4", l1_bits=l1, l2_bits=l2)
+    x, a, b = O.bf16_bits_to_f64(xb), O.bf16_bits_to_f64(l1), O.bf16_bits_to_f64(l2)
+    for m in range(3):
+        for n in (0, 17, 31):
+            br = sum(sum(x[m, k] * a[k, r] for k in range(256)) * b[r, n] for r in range(16))
+            assert abs((y1 - y0)[m, n] - br) <= 1e-12 * (1 + abs(br))
+    # rank 0 is the plain layer; SwiGLU pairs the first half (gate) with the second (up)
+    _, y2, _, _ = O.mx_linear(xb, wb, "fp4", l1_bits=l1[:, :0], l2_bits=l2[:0])
+    assert np.array_equal(y2, y0)
+    out, y3, _, _ = O.mx_linear(xb, wb, "fp4", epi="swiglu", l1_bits=l1, l2_bits=l2)
+    g, u = y3[:, :16], y3[:, 16:]
+    assert np.array_equal(out, O.f64_to_bf16_bits(g / (1 + np.exp(-g)) * u))

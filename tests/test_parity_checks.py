@@ -307,3 +307,14 @@ def test_mx_fp8_group_truncation_within_bound():
     bad = got + 40 * dy
     with pytest.raises(AssertionError):
         P.assert_outputs_close(bad, y, dy, bf16=False, what="too coarse")
+
+
+def test_bf16_unit_roundoff_is_tight():
+    # |bf16(x) - x| <= BF16_U |x| for every x, and the worst case comes close
+    # to it (a value just above 1 + 2^-8 rounds down by almost 2^-8 of itself)
+    rng = np.random.default_rng(15)
+    x = np.concatenate([rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000)),
+                        [1 + 2.0 ** -8 - 2.0 ** -30, 0.5455]])
+    rel = np.abs(O.bf16_round(x) - x) / np.abs(x)
+    assert rel.max() <= P.BF16_U
+    assert rel.max() > 0.99 * P.BF16_U / (1 + 2.0 ** -8)

@@ -283,3 +283,89 @@ def test_mx_full_size_sampled_rows(Q, fmt):
     y, dy = P.mx_linear_bound(O.MXResult(a_c, a_e, fmt, None), O.MXResult(w_c, w_e, fmt, None))
     got = O.bf16_bits_to_f64(bf16_bits(out[rows]))
     P.assert_outputs_close(got, y, dy, what=f"{fmt} full size")
+
+
+# ------------------------------------------------------- low-rank branch --
+
+def _lowrank_case(Q, M, N, K, r, fmt, seed):
+    import torch
+
+    xb = _rand_bf16(seed, (M, K), outliers=max(1, K // 100))
+    wb = _rand_bf16(seed + 1, (N, K), std=0.02)
+    l1 = _rand_bf16(seed + 2, (K, r), std=0.02)
+    l2 = _rand_bf16(seed + 3, (r, N), std=0.02)
+    ca, sa, lr = Q.rotate_quantize_mx(to_dev_bf16(xb), fmt=fmt, l1=to_dev_bf16(l1))
+    cw, sw = Q.rotate_quantize_mx(to_dev_bf16(wb), fmt=fmt)
+    torch.cuda.synchronize()
+    return xb, wb, l1, l2, (ca, sa, cw, sw, lr)
+
+
+def _lowrank_want(xb, l1, l2, ca, sa, cw, sw, fmt, epi, rows=None):
+    a_c, a_e = O.mx_unpack(ca.cpu().numpy(), _rowmajor(sa), fmt)
+    w_c, w_e = _unpack(cw, sw, fmt)
+    if rows is not None:
+        a_c, a_e, xb = a_c[rows], a_e[rows], xb[rows]
+    y, dy = P.mx_linear_bound(O.MXResult(a_c, a_e, fmt, None), O.MXResult(w_c, w_e, fmt, None))
+    br, dbr = P.lowrank_bound(xb, l1, l2)
+    y2 = y + br
+    dy2 = dy + dbr + 3 * P.U * (np.abs(y) + np.abs(br))
+    return P.epilogue_with_bound(y2, dy2, epi)
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp8"])
+@pytest.mark.parametrize("r", [16, 32, 64, 128])
+@pytest.mark.parametrize("epi", ["bf16", "swiglu", "f32"])
+def test_mx_lowrank_gemm(Q, fmt, r, epi):
+    import torch
+
+    M, N, K = 300, 640, 1024
+    xb, wb, l1, l2, (ca, sa, cw, sw, lr) = _lowrank_case(Q, M, N, K, r, fmt, seed=61 + r)
+    # the down-projection is the unrotated x @ l1, rounded once to bf16
+    lr_want = O.bf16_bits_to_f64(xb) @ O.bf16_bits_to_f64(l1)
+    lr_bound = P.BF16_U * np.abs(lr_want) + (K / 8 + 4) * P.U * (np.abs(O.bf16_bits_to_f64(xb)) @
+                                                                  np.abs(O.bf16_bits_to_f64(l1)))
+    lr_got = O.bf16_bits_to_f64(bf16_bits(lr))
+    assert np.all(np.abs(lr_got - lr_want) <= lr_bound + 2.0 ** -133)
+    out = Q.qgemm_mx_lowrank(ca, sa, cw, sw, K, fmt=fmt, lr=lr, l2=to_dev_bf16(l2), epilogue=epi)
+    torch.cuda.synchronize()
+    want, bound = _lowrank_want(xb, l1, l2, ca, sa, cw, sw, fmt, epi)
+    got = out.cpu().numpy().astype(np.float64) if epi == "f32" else O.bf16_bits_to_f64(bf16_bits(out))
+    r_ = P.assert_outputs_close(got, want, bound, bf16=epi != "f32", what=f"{fmt} rank {r} {epi}")
+    print(f"worst error / tolerance {r_:.3f}")
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp8"])
+def test_mx_lowrank_rank0_equals_plain(Q, fmt):
+    import torch
+
+    M, N, K = 128, 256, 512
+    xb, wb, l1, l2, (ca, sa, cw, sw, lr) = _lowrank_case(Q, M, N, K, 16, fmt, seed=71)
+    a = Q.qgemm_mx_lowrank(ca, sa, cw, sw, K, fmt=fmt, epilogue="bf16")
+    b = Q.qgemm_mx(ca, sa, cw, sw, K, fmt=fmt)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_mx_svdq_gateup_full_size_sampled_rows(Q):
+    """The SVDQuant gate|up layer at its full size in MXFP4 (X [4096 x 5120],
+    W [40960 x 5120], rank-32 L1 / L2, SwiGLU -> [4096 x 20480]) in the
+    launch configuration the benchmark times; sampled rows against the
+    oracle's product of the GPU's codes, sampled weight rows against the
+    quantizer's definition."""
+    import torch
+
+    wl = W.svdq_gateup()
+    M, K = wl.x.shape
+    N = wl.w.shape[0]
+    ca, sa, lr = Q.rotate_quantize_mx(to_dev_bf16(wl.x), fmt="fp4", l1=to_dev_bf16(wl.l1))
+    cw, sw = Q.rotate_quantize_mx(to_dev_bf16(wl.w), fmt="fp4")
+    out = Q.qgemm_mx_lowrank(ca, sa, cw, sw, K, fmt="fp4", lr=lr, l2=to_dev_bf16(wl.l2), epilogue="swiglu")
+    torch.cuda.synchronize()
+    rows = np.array([0, 255, 2048, 4095])
+    want, bound = _lowrank_want(wl.x, wl.l1, wl.l2, ca, sa, cw, sw, "fp4", "swiglu", rows=rows)
+    got = O.bf16_bits_to_f64(bf16_bits(out[rows]))
+    P.assert_outputs_close(got, want, bound, what="MXFP4 SVDQuant gate|up")
+    wsel = np.random.default_rng(0).choice(N, 64, replace=False)
+    w_c, w_e = _unpack(cw, sw, "fp4")
+    st = _check(w_c[wsel], w_e[wsel], wl.w[wsel], "fp4", True)
+    print(f"weights (64 sampled rows): {st}")
