@@ -204,7 +204,8 @@ def cpu_baseline(wl, target_s=12.0, one_thread_s=3.0):
            "kind": "oracle", "cpu_model": _cpu_model(),
            "sample": f"{what} against all {wl.N} outputs (weights pre-quantized): "
                      f"rotate+quantize, exact integer GEMM via float64 BLAS, dequant, "
-                     f"{wl.epilogue} epilogue, bf16 rounding; {t:.2f} s wall on {threads} "
+                     + (f"rank-{wl.l1.shape[1]} branch, " if wl.l1 is not None else "")
+                     + f"{wl.epilogue} epilogue, bf16 rounding; {t:.2f} s wall on {threads} "
                      f"BLAS threads"}
     try:
         from threadpoolctl import threadpool_limits
