@@ -589,10 +589,9 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
           wf[j] = frag(Ws + j * 16 * C::WRB, wxp[h], wx1);
           wsc[j] = Ss[sb + (C::BM + w_row + 16 * j) * 4];
         }
-        int asc[C::FI];
-#pragma unroll
-        for (int i = 0; i < C::FI; ++i) asc[i] = Ss[sb + (a_row + 16 * i) * 4];
-        constexpr int PF = 2;
+        // FP8 fragments are 8 dwords: a one-fragment read-ahead window keeps
+        // the 256 x 320 tile's registers under the 256 a wave may hold
+        constexpr int PF = C::MX == 8 ? 1 : 2;
         v8i abuf[PF + 1];
 #pragma unroll
         for (int q = 0; q < PF; ++q) abuf[q] = frag(As + q * 16 * C::ARB, axp[h], ax1);
@@ -601,12 +600,13 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
           const int step = h * C::FI + i;  // position in the stage's MFMA groups
           if (step > 0 && (4 * step) % (C::SUB * C::FI) < 4) stage_prio((4 * step) / (C::SUB * C::FI));
           if (i + PF < C::FI) abuf[(i + PF) % (PF + 1)] = frag(As + (i + PF) * 16 * C::ARB, axp[h], ax1);
+          const int asc_i = Ss[sb + (a_row + 16 * i) * 4];
           if (dma && step < NDMA) issue_one(nxt, kt + NS - 1, step);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int j = 0; j < C::FJ; ++j) {
             acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], abuf[i % (PF + 1)], acc[j][i],
-                                                                        FMT, FMT, 0, wsc[j], 0, asc[i]);
+                                                                        FMT, FMT, 0, wsc[j], 0, asc_i);
             asm volatile("" : "+v"(acc[j][i]));
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -1386,13 +1386,14 @@ int launch_qgemm(const GemmArgs& g, hipStream_t s) {
     p.xw = static_cast<const uint8_t*>(g.xw);
     p.post = 1.0f;
     p.shift = 0;
-    // FP8 operands (8 dwords a fragment) next to the 256 x 320 tile's 160
-    // accumulators would spill inside the K loop: FP8 always takes 256 x 256.
+    // SwiGLU pairs gate and up fragments, which a 320-wide tile (5 per
+    // wave) cannot: it takes 256 x 256.
     using M4W = Cfg<256, 320, 2, 4, false, false, false, false, 4, 3, 2>;
     using M4N = Cfg<256, 256, 2, 4, false, false, false, false, 4, 3, 2>;
+    using M8W = Cfg<256, 320, 2, 4, false, false, false, false, 8>;
     using M8N = Cfg<256, 256, 2, 4, false, false, false, false, 8>;
     if (g.mx == 4) e = wide ? launch_mx<M4W, M4N>(p, g.epilogue, s) : launch_mx<M4N, M4N>(p, g.epilogue, s);
-    else e = launch_mx<M8N, M8N>(p, g.epilogue, s);
+    else e = wide ? launch_mx<M8W, M8N>(p, g.epilogue, s) : launch_mx<M8N, M8N>(p, g.epilogue, s);
     return e == hipSuccess ? OK : ERR_LAUNCH;
   }
   if (g.fp6) {

@@ -198,6 +198,26 @@ def test_mx_gemm_same_codes(Q, fmt, M, N, K, epi):
 
 
 @pytest.mark.parametrize("fmt", ["fp4", "fp8"])
+def test_mx_gemm_wide_tiles_ragged(Q, fmt):
+    """A grid where 256 x 320 tiles save a wave over 256 x 256 (16 x 16
+    against 16 x 20 tiles), so the wide configuration runs, with ragged M
+    and N tails; sampled rows (the last tile row included) against the
+    oracle's product of the GPU's codes, every column."""
+    import torch
+
+    M, N, K = 4000, 5104, 512
+    xb, wb, (ca, sa, cw, sw), qa, qw = _mx_pair(Q, M, N, K, fmt, seed=11)
+    out = Q.qgemm_mx(ca, sa, cw, sw, K, fmt=fmt)
+    torch.cuda.synchronize()
+    rows = np.array([0, 17, 255, 256, 2100, 3839, 3840, 3998, 3999])
+    qa_rows = O.MXResult(qa.codes[rows], qa.exps[rows], fmt, None)
+    y, dy = P.mx_linear_bound(qa_rows, qw)
+    got = O.bf16_bits_to_f64(bf16_bits(out[rows]))
+    r = P.assert_outputs_close(got, y, dy, what=f"{fmt} wide tiles")
+    print(f"worst error / tolerance {r:.3f}")
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp8"])
 @pytest.mark.parametrize("epi", ["sigmoid", "gated_residual", "swiglu"])
 def test_mx_gemm_epilogues(Q, fmt, epi):
     import torch
