@@ -49,7 +49,14 @@
 //    f and the 32 matching up rows F + f, so a lane holds gate and up of the
 //    same outputs;
 //  * workgroup ids are remapped so the tiles one XCD runs form a compact
-//    block of the tile grid (shared A / W panels hit that XCD's L2).
+//    block of the tile grid (shared A / W panels hit that XCD's L2);
+//  * int8 activations with tensor / row scales on 256 x 320 tiles (the
+//    attention projections and the W8A8 ff.down) run a ping-pong K loop:
+//    the two waves of each SIMD alternate, one phase apart, between reading
+//    fragments from LDS (and issuing global -> LDS loads) and a cluster of
+//    40 MFMAs from registers, so one of them always feeds the matrix pipe
+//    (measured on gfx950: -3 to -5 % at 4096 x 5120 x 5120, -8 % at K =
+//    20480; the same loop with packed activations gains nothing).
 
 #include <type_traits>
 
@@ -167,7 +174,7 @@ struct PArgs {
 // lines, half the line requests per channel of 64-byte rows (the loads'
 // cost follows the number of lines they touch) and half the barriers.
 template <int BM_, int BN_, int WGM_, int WGN_, bool AP_, bool WP_, bool GROUP_ = false, bool F6_ = false,
-          int MX_ = 0, int MAXS_ = 3, int SUB_ = 1>
+          int MX_ = 0, int MAXS_ = 3, int SUB_ = 1, bool PP_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int WGM = WGM_, WGN = WGN_;   // wave grid
@@ -176,6 +183,7 @@ struct Cfg {
   static constexpr bool AP = AP_, WP = WP_, GROUP = GROUP_, F6 = F6_;
   static constexpr int MX = MX_;
   static constexpr int SUB = SUB_;         // 128-channel sub-stages per LDS stage
+  static constexpr bool PP = PP_;          // ping-pong K loop (see pipe_tile)
   static constexpr int BKS = BK * SUB;     // channels per LDS stage
   static constexpr bool FMMA = F6 || MX != 0;   // float matrix instruction, fp32 accumulators
   static constexpr bool NOSC = GROUP || MX != 0;  // accumulators already carry both scales
@@ -215,6 +223,8 @@ struct Cfg {
   static_assert(NSTAGE * STAGE <= kLdsBytes, "LDS ring too large");
   static_assert((NSTAGE - 2) * NDMA < 64, "vmcnt range");
   static_assert(!GROUP || FI % 4 == 0, "group scales are read 4 rows at a time");
+  static_assert(!PP || (!AP && !GROUP && !F6 && MX == 0 && SUB == 1 && WGM == 2 && WGN == 4 && NSTAGE <= 3),
+                "ping-pong loop: int8 A, tensor / row scales, 2 x 4 waves, 2 or 3 stages");
 };
 
 template <bool F>
@@ -535,9 +545,109 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   // flight (both waves of a SIMD leave the barrier together and would
   // otherwise wait on them at the same time).  Its operands (the stage's
   // second-half W fragments and last A fragment) stay in registers.
-  constexpr bool DEFER = !C::GROUP && C::WP && !C::F6;  // int8 W: not enough registers
+  constexpr bool DEFER = !C::GROUP && C::WP && !C::F6 && !C::PP;  // int8 W: not enough registers
   v4i bw1[C::FJ];
   v4i af_def = v4i{0, 0, 0, 0};
+  if constexpr (C::PP) {
+    // Ping-pong K loop.  Waves w and w + 4 share a SIMD (measured: pairing
+    // waves 2i and 2i + 1 instead runs 40 % slower); they form groups
+    // gp = 0 (waves 0-3) and gp = 1 (waves 4-7) that run the same sequence
+    // of phases per stage -- L0 C0 L1 C1, where L(kk) reads the fragments of
+    // half kk from LDS (and issues some of the wave's global -> LDS loads of
+    // stage kt + 2) and C(kk) runs its 40 MFMAs from registers -- one phase
+    // apart: every phase ends at a workgroup barrier, and group 1 passes one
+    // extra barrier before its first phase, group 0 one after its last.  So
+    // while one wave of a SIMD issues MFMAs back to back, the other waits on
+    // LDS and memory, and the MFMA stream does not stall on its own
+    // fragment reads.
+    // Slot 4 kt + p (p = 0..3) is group 0's phase p of stage kt and group
+    // 1's phase p - 1.  Stage kt is read in slots 4 kt .. 4 kt + 4, the
+    // loads of stage kt + 2 (into stage kt - 1's buffer, last read in slot
+    // 4 kt - 1) are issued in slots 4 kt .. 4 kt + 3, and every wave waits
+    // for its own loads of stage kt + 1 before the barrier that opens slot
+    // 4 kt + 4 (group 0 after C1, group 1 after L1).
+    // With a 2-stage ring (int8 W) the loads of stage kt + 1 go into stage
+    // kt - 1's buffer during stage kt; all of them are issued in L0, so they
+    // have two slots to land before the waits.
+    const int gp = wave >> 2;
+    if (NS == 3 && KT > 1) {
+      if (w_hi) wait_vmcnt<NDMA>();
+      else wait_vmcnt<NDMA - 1>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+    if (gp == 1) __builtin_amdgcn_s_barrier();
+    auto wait_next = [&](int kt) {
+      if (NS == 3 && kt + 2 < KT) {
+        if (w_hi) wait_vmcnt<NDMA>();
+        else wait_vmcnt<NDMA - 1>();
+      } else {
+        wait_vmcnt<0>();
+      }
+    };
+    v4i af[C::FI];
+    v4i bw[C::FJ];
+    uint2 whi[C::FJ];
+    constexpr int H0 = NS == 3 ? (NDMA + 1) / 2 : NDMA;  // loads issued in L0; the rest in L1
+    for (int kb = 0; kb < KT; kb += NS) {
+#pragma unroll
+      for (int sc = 0; sc < NS; ++sc) {
+        const int kt = kb + sc;
+        if (kt >= KT) break;
+        const uint8_t* As = ring(sc);
+        const uint8_t* Ws = As + C::SA;
+        uint8_t* const nxt = ring((sc + NS - 1) % NS);
+        const bool dma = kt + NS - 1 < KT;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          // L(kk)
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < C::FI; ++i) af[i] = *reinterpret_cast<const v4i*>(As + a_off[kk] + i * 16 * C::ARB);
+          if (!C::WP) {
+            // int8 W: one 16-byte read per fragment and half
+#pragma unroll
+            for (int j = 0; j < C::FJ; ++j)
+              bw[j] = *reinterpret_cast<const v4i*>(Ws + (kk == 0 ? w_off : w_off1) + j * 16 * C::WRB);
+          } else if (kk == 0) {
+#pragma unroll
+            for (int j = 0; j < C::FJ; ++j) {
+              const uint4 r = *reinterpret_cast<const uint4*>(Ws + wxp[0] + j * 16 * C::WRB);
+              bw[j] = unpack_lo(r.x, r.y);
+              whi[j] = make_uint2(r.z, r.w);
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < C::FJ; ++j) bw[j] = unpack_lo(whi[j].x, whi[j].y);
+          }
+          if (dma) {
+#pragma unroll
+            for (int t = kk == 0 ? 0 : H0; t < (kk == 0 ? H0 : NDMA); ++t) issue_one(nxt, kt + NS - 1, t);
+          }
+#pragma unroll
+          for (int j = 0; j < C::FJ; ++j) asm volatile("" : "+v"(bw[j]));
+#pragma unroll
+          for (int i = 0; i < C::FI; ++i) asm volatile("" : "+v"(af[i]));
+          if (kk == 1 && gp == 1 && kt + 1 < KT) wait_next(kt);
+          lds_barrier();
+          // C(kk)
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < C::FI; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FJ; ++j) {
+              acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bw[j], af[i], acc[j][i], 0, 0, 0);
+              asm volatile("" : "+v"(acc[j][i]));
+            }
+          __builtin_amdgcn_sched_barrier(0);
+          if (kk == 1 && gp == 0 && kt + 1 < KT) wait_next(kt);
+          __builtin_amdgcn_s_barrier();
+        }
+      }
+    }
+    if (gp == 0) __builtin_amdgcn_s_barrier();
+  } else {
   for (int kb = 0; kb < KT; kb += NS) {
 #pragma unroll
   for (int sc = 0; sc < NS; ++sc) {
@@ -852,6 +962,7 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
     }
   }
   }
+  }  // ping-pong / pipelined K loop
   stage_prio(3);  // back to the lowest priority for the epilogue
 
   if constexpr (DEFER) {
@@ -1427,10 +1538,10 @@ int launch_qgemm(const GemmArgs& g, hipStream_t s) {
       e = wide ? launch_plain<Cfg<256, 320, 2, 4, true, true>>(p, g.epilogue, s)
                : launch_plain<Cfg<256, 256, 2, 4, true, true>>(p, g.epilogue, s);
     else
-      e = wide ? launch_plain<Cfg<256, 320, 2, 4, false, true>>(p, g.epilogue, s)
+      e = wide ? launch_plain<Cfg<256, 320, 2, 4, false, true, false, false, 0, 3, 1, true>>(p, g.epilogue, s)
                : launch_plain<Cfg<256, 256, 2, 4, false, true>>(p, g.epilogue, s);
   } else {
-    e = wide ? launch_plain<Cfg<256, 320, 2, 4, false, false>>(p, g.epilogue, s)
+    e = wide ? launch_plain<Cfg<256, 320, 2, 4, false, false, false, false, 0, 3, 1, true>>(p, g.epilogue, s)
              : launch_plain<Cfg<256, 256, 2, 4, false, false>>(p, g.epilogue, s);
   }
   return e == hipSuccess ? OK : ERR_LAUNCH;
