@@ -294,6 +294,9 @@ class Case:
         self.bound = "mfma"
         self.cpu_fn = None        # custom CPU baseline (else the linear's oracle on case.wl)
         self.unit = "TOP/s"
+        # low-rank layers: (the prologue without X @ L1, the GEMM without the
+        # branch), the same launches otherwise, to report the branch's cost
+        self.branch = None
 
 
 def _bf16_dev(bits, dev):
@@ -471,7 +474,7 @@ def case_svdq_mx(Q, W, dev):
     M, N, K = wl.M, wl.N, wl.K
     r = wl.l1.shape[1]
     x, w = _bf16_dev(wl.x, dev), _bf16_dev(wl.w, dev)
-    l1, l2 = _bf16_dev(wl.l1, dev), _bf16_dev(wl.l2, dev)
+    l1, l2 = _bf16_dev(wl.l1, dev), _bf16_dev(np.ascontiguousarray(wl.l2.T), dev)  # L2 transposed, [N, r]
     codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     sa = torch.empty((K // 128, M, 4), dtype=torch.uint8, device=dev)
     lr = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
@@ -485,6 +488,10 @@ def case_svdq_mx(Q, W, dev):
         ("gemm", lambda: Q.qgemm_mx_lowrank(codes, sa, wq, sw, K, fmt="fp4", lr=lr, l2=l2, epilogue="swiglu",
                                             out=out)),
     ]
+    out0 = torch.empty_like(out)
+    c.branch = (
+        lambda: Q.rotate_quantize_mx(x, fmt="fp4", codes=codes, scales=sa),
+        lambda: Q.qgemm_mx_lowrank(codes, sa, wq, sw, K, fmt="fp4", epilogue="swiglu", out=out0))
     c.ops = wl.int_ops
     c.gemm_launches = 1
     c.pro_bytes = M * K * 2 + K * r * 2 + M * K // 2 + M * K // 32 + M * r * 2
@@ -606,7 +613,7 @@ def case_svdq(Q, W, dev, fp6=False):
     M, N, K = wl.M, wl.N, wl.K
     r = wl.l1.shape[1]
     x, w = _bf16_dev(wl.x, dev), _bf16_dev(wl.w, dev)
-    l1, l2 = _bf16_dev(wl.l1, dev), _bf16_dev(wl.l2, dev)
+    l1, l2 = _bf16_dev(wl.l1, dev), _bf16_dev(np.ascontiguousarray(wl.l2.T), dev)  # L2 transposed, [N, r]
     acols, wcols = (K // 4 * 3, K // 4 * 3) if fp6 else (K, K // 2)
     codes = torch.empty((M, acols), dtype=torch.uint8 if fp6 else torch.int8, device=dev)
     sa = torch.empty((M, K // 64), dtype=torch.float32, device=dev)
@@ -625,6 +632,11 @@ def case_svdq(Q, W, dev, fp6=False):
                                                    out=out)) if fp6 else
                  (lambda: Q.qgemm_w4a4_lowrank(codes, sa, wq, sw, K, lr=lr, l2=l2, epilogue="swiglu", out=out))),
     ]
+    out0 = torch.empty_like(out)
+    c.branch = (
+        lambda: Q.rotate_quantize_act(x, bits=4, scale_mode="group64", layout=layout, codes=codes, scales=sa),
+        (lambda: Q.qgemm_w4a4_fp6_lowrank(codes, sa, wq, sw, K, epilogue="swiglu", out=out0)) if fp6 else
+        (lambda: Q.qgemm_w4a4_lowrank(codes, sa, wq, sw, K, epilogue="swiglu", out=out0)))
     c.ops = wl.int_ops
     c.gemm_launches = 1
     c.pro_bytes = M * K * 2 + K * r * 2 + M * acols + M * (K // 64) * 4 + M * r * 2
@@ -1125,6 +1137,19 @@ def main(argv=None):
                      "timing": "GEMM-only: median of 5 repeats of back-to-back launches, HIP events on the "
                                "launch stream"},
     }
+    if case.branch is not None:
+        # the low-rank branch's share: the prologue and the GEMM timed again
+        # without it (same codes, tiles and epilogue), back to back
+        pro0_ms = time_back_to_back([case.branch[0]], launches=50, warm=2)[0]
+        g0_ms = time_back_to_back([case.branch[1]], launches=gemm["passes_per_repeat"],
+                                  warm=min(10, gemm["passes_per_repeat"]))[0]
+        down, up = pro_ms - pro0_ms, gemm["ms"] - g0_ms
+        rec["lowrank_branch"] = {
+            "down_ms": round(down, 5), "up_ms": round(up, 5),
+            "prologue_without_ms": round(pro0_ms, 5), "gemm_without_ms": round(g0_ms, 5),
+            "pct_of_step": round(100.0 * (down + up) / step_ms, 2),
+            "method": "X @ L1: prologue with it minus without; lr @ L2: GEMM with it minus without "
+                      "(medians of back-to-back launches)"}
     if other is not None:
         rec["other_gemms"] = other
     if not args.no_cpu_baseline and case.cpu_fn is not None:

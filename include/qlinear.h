@@ -126,7 +126,8 @@ enum {
   QL_EPI_I32 = 4,            /* out[m,n] = exact int32 accumulator (no scales)   */
   QL_EPI_SIGMOID = 5         /* out[m,n] = bf16(1 / (1 + exp(-y[m,n])))          */
 };
-/* y[m,n] = sum_k deq(a)[m,k] * deq(w)[n,k] (+ bias[n]) (+ (lr L2)[m,n]),
+/* y[m,n] = sum_k deq(a)[m,k] * deq(w)[n,k] (+ bias[n]) (+ (lr L2)[m,n]; the
+ * entry points take L2 stored transposed, l2[n, j] = L2[j, n]),
  * i.e. acc * s_a * s_w for tensor / row scales, and the sum over 64-channel
  * groups of acc_g * s_a[m,g] * s_w[n,g] for group-64 scales.  bf16 outputs
  * are rounded to nearest even. */
@@ -325,7 +326,8 @@ int qgemm_mx(const void* a, const uint8_t* sa, const void* w, const uint8_t* sw,
  * "LoRA").  On gfx950 its FP4 runs as MXFP4 (see rotate_quantize_mx).
  *   a, sa, w, sw, fmt   as qgemm_mx
  *   lr       bf16 [M, rank] (rotate_quantize_mx's down-projection), dense rows
- *   l2       bf16 [rank, N], row-major, 16-byte aligned
+ *   l2       bf16 [N, rank]: row n is the rank vector of output column n
+ *            (the branch's L2 factor stored transposed), 16-byte aligned
  *   rank     0..128, a multiple of 16 (0: no branch)
  *   bias     NULL or bf16 [N]
  *   epilogue QL_EPI_BF16 | QL_EPI_F32 | QL_EPI_SWIGLU (N a multiple of 32;
@@ -364,7 +366,9 @@ int qgemm_w8a8(const int8_t* a, const float* sa, int a_scale_mode,
  *             QL_LAYOUT_I8 | QL_LAYOUT_PACKED (the FP6 experiment has its
  *             own entry point, qgemm_w4a4_fp6_lowrank)
  *   lr        bf16 [M, rank] (from rotate_quantize_act), dense rows
- *   l2        bf16 [rank, N], dense rows, 16-byte aligned
+ *   l2        bf16 [N, rank]: row n is the rank vector of output column n
+ *             (the branch's L2 factor stored transposed, so the epilogue
+ *             reads 8 consecutive ranks with one 16-byte load), 16-byte aligned
  *   rank      0 (no branch; lr, l2 may be NULL) or a multiple of 16, <= 128
  *   epilogue  QL_EPI_BF16 | QL_EPI_SWIGLU | QL_EPI_F32; SWIGLU pairs output
  *             column j (gate) with column j + N/2 (up), needs N % 32 == 0
@@ -453,7 +457,7 @@ int qgemm_grouped(const void* a4, const float* sa4, const void* a8, const float*
  *   rank     16..128, multiple of 16; oversample 0..32; rank + oversample <= min(N, K)
  *   power_iters 0..8; refine_iters 0..16 (iterations = refine_iters + 1)
  *   scale_mode QL_SCALE_TENSOR | QL_SCALE_ROW | QL_SCALE_GROUP64 (the residual's scales)
- *   l1 out: bf16 [K, rank]; l2 out: bf16 [rank, N] (the layout of the low-rank
+ *   l1 out: bf16 [K, rank]; l2 out: bf16 [N, rank], L2 transposed (the layout of the low-rank
  *            GEMM entry points); packed out: [N, K/2] (QL_LAYOUT_PACKED);
  *            scales out: float32 [1] | [N] | [N, K/64]; all 16-byte aligned
  *   errors out: float32 [refine_iters + 1], err_t of every iteration

@@ -309,7 +309,8 @@ def qgemm_mx(a, sa, w, sw, K, fmt="fp4", bias=None, residual=None, gate=None, ep
 
 def qgemm_mx_lowrank(a, sa, w, sw, K, fmt="fp4", lr=None, l2=None, bias=None, epilogue="swiglu", out=None,
                      stream=None):
-    """The MX GEMM plus the low-rank branch lr @ l2 (SVDQuant in MX form)."""
+    """The MX GEMM plus the low-rank branch lr @ L2 (SVDQuant in MX form);
+    l2 is L2 transposed, bf16 [N, rank]."""
     M = a.shape[0]
     N = w.shape[0]
     epi = _epi(epilogue)
@@ -339,11 +340,12 @@ def qgemm_w4a4_lowrank(a, sa, w, sw, K, lr=None, l2=None, a_scale_mode="group64"
                        w_scale_mode="group64", a_layout="i8", bias=None, epilogue="swiglu", out=None,
                        stream=None):
     """Group-64 (or row / tensor) W4A4 GEMM + optional low-rank branch
-    lr @ l2 + epilogue; a_layout "i8" or "packed"."""
+    lr @ L2 + epilogue (l2: L2 transposed, bf16 [N, rank]); a_layout "i8" or
+    "packed"."""
     M = a.shape[0]
     N = w.shape[0]
     epi = _epi(epilogue)
-    rank = 0 if l2 is None else l2.shape[0]
+    rank = 0 if l2 is None else l2.shape[1]
     out = _out(out, M, N // 2 if epi == QL_EPI_SWIGLU else N, epi, a.device)
     st = lib().qgemm_w4a4_lowrank(_ptr(a), _ptr(sa), _mode(a_scale_mode), _lay(a_layout), _ptr(w),
                                   _ptr(sw), _mode(w_scale_mode), _ptr(lr), _ptr(l2), rank, M, N, K,
@@ -360,7 +362,7 @@ def qgemm_w4a4_fp6_lowrank(a, sa, w, sw, K, lr=None, l2=None, bias=None, epilogu
     M = a.shape[0]
     N = w.shape[0]
     epi = _epi(epilogue)
-    rank = 0 if l2 is None else l2.shape[0]
+    rank = 0 if l2 is None else l2.shape[1]
     out = _out(out, M, N // 2 if epi == QL_EPI_SWIGLU else N, epi, a.device)
     st = lib().qgemm_w4a4_fp6_lowrank(_ptr(a), _ptr(sa), _ptr(w), _ptr(sw), _ptr(lr), _ptr(l2), rank, M, N, K,
                                       _ptr(bias), epi, _ptr(out), out.stride(0), _stream(stream))
@@ -401,7 +403,7 @@ def svdq_split(w, omega, rank, oversample=8, power_iters=2, refine_iters=0, scal
                act_rms=None, workspace=None, stream=None):
     """Offline SVDQuant split of w (bf16 [N, K]) with the Gaussian sketch
     omega (float32 [K, rank + oversample]).  Returns a dict with l1 bf16
-    [K, rank], l2 bf16 [rank, N], packed uint8 [N, K/2], scales, errors float32
+    [K, rank], l2 bf16 [N, rank] (L2 transposed), packed uint8 [N, K/2], scales, errors float32
     [refine_iters + 1], best_iter int32 [1] and sigma float32 [rank]."""
     assert w.dtype == torch.bfloat16 and w.dim() == 2 and w.stride(1) == 1
     N, K = w.shape
@@ -416,7 +418,7 @@ def svdq_split(w, omega, rank, oversample=8, power_iters=2, refine_iters=0, scal
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     out = {"l1": torch.empty((K, rank), dtype=torch.bfloat16, device=dev),
-           "l2": torch.empty((rank, N), dtype=torch.bfloat16, device=dev),
+           "l2": torch.empty((N, rank), dtype=torch.bfloat16, device=dev),
            "packed": torch.empty((N, K // 2), dtype=torch.uint8, device=dev),
            "scales": torch.empty(_scale_shape(N, K, mode), dtype=torch.float32, device=dev),
            "errors": torch.empty(refine_iters + 1, dtype=torch.float32, device=dev),
@@ -449,7 +451,7 @@ def svdq_split_noalloc(w, omega, rank, oversample=8, power_iters=2, refine_iters
         assert act_rms.dtype == torch.float32 and act_rms.numel() == K and act_rms.is_contiguous()
     if out is None:
         out = {"l1": torch.empty((K, rank), dtype=torch.bfloat16, device=dev),
-               "l2": torch.empty((rank, N), dtype=torch.bfloat16, device=dev),
+               "l2": torch.empty((N, rank), dtype=torch.bfloat16, device=dev),
                "packed": torch.empty((N, K // 2), dtype=torch.uint8, device=dev),
                "scales": torch.empty(_scale_shape(N, K, mode), dtype=torch.float32, device=dev),
                "errors": torch.empty(refine_iters + 1, dtype=torch.float32, device=dev),

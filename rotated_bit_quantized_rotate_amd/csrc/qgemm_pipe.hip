@@ -152,7 +152,7 @@ struct PArgs {
   const uint16_t* residual;
   const uint16_t* gate;
   const uint16_t* lr;        // [M, rank]
-  const uint16_t* l2;        // [rank, N]
+  const uint16_t* l2;        // [N, rank] (L2 transposed)
   int rank;
   void* out;
   int64_t ldo;
@@ -1099,47 +1099,24 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   }
 
   // ---- epilogue: lane holds out[m][n .. n+3] for each (i, j) --------------
-  // Low-rank branch: the tile's L2 columns (one rank vector per W-tile row t,
-  // i.e. per weight row w_row_of(t)) go through the now-free LDS ring once,
-  // read from L2 [rank, N] with coalesced 16-byte loads (8 consecutive
-  // columns of one rank row; a chunk never straddles the gate|up halves or
-  // the end of N, since 8 | HW and 16 | N) and stored transposed, so a lane's
-  // 8 consecutive ranks of one column are one 16-byte LDS read.  The rows
-  // are spread over the ring arrays, L2R rows each; the row pitch
-  // rank * 2 + 16 bytes puts the 16 rows of a fragment read on distinct bank
-  // groups.
-  constexpr int L2R = (C::BN + NS - 1) / NS;
-  const int l2pitch = p.rank * 2 + 16;
-  auto l2s_row = [&](int t) -> uint8_t* {
-    const int a = t / L2R;
-    return ring(a) + (t - a * L2R) * l2pitch;
-  };
-  if constexpr (LOWRANK) {
-    static_assert(L2R * (128 * 2 + 16) <= C::STAGE, "staged L2 columns must fit the ring");
-    static_assert(!SWIG || (C::WN / 2) % 8 == 0, "L2 chunks must not straddle the gate|up halves");
-    lds_barrier();  // every wave is done with the ring
-    const int cpr = C::BN / 8;  // 8-column chunks per rank row
-    for (int c = tid; c < p.rank * cpr; c += C::NT) {
-      const int r = c / cpr, t0c = (c % cpr) * 8;
-      int64_t col;
-      bool ok;
-      if (SWIG) {
-        constexpr int HW = C::WN / 2;
-        const int wv = t0c / C::WN, u = t0c % C::WN;
-        const int64_t f = n0 + wv * HW + (u % HW);
-        ok = f < p.half_n;
-        col = (u >= HW ? p.half_n : 0) + f;
-      } else {
-        col = n0 + t0c;
-        ok = col < p.N;
-      }
-      const uint4 v = ok ? *reinterpret_cast<const uint4*>(p.l2 + (int64_t)r * p.N + col) : make_uint4(0, 0, 0, 0);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+  // Low-rank branch: L2 is stored [N, rank] (row n: the rank vector of
+  // weight row / output column n), so a lane's 8 consecutive ranks of one
+  // weight row are one 16-byte load -- the first MFMA operand as it is.
+  // MX and group-64 tiles: the lr fragments of ranks 0 .. 31 for all FI
+  // rows are loaded here, ahead of the column loop (they do not depend on
+  // the output columns); later 32-rank chunks, and every chunk of the other
+  // tiles (whose epilogues have no registers to spare), are loaded per half
+  // of the rows.
+  constexpr bool PRE_LR = LOWRANK && (C::MX != 0 || C::GROUP);
+  uint4 ua0[PRE_LR ? C::FI : 1];
+  if constexpr (PRE_LR) {
+    const int kc = lg * 8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint16_t*>(l2s_row(t0c + e) + r * 2) = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+    for (int i = 0; i < C::FI; ++i) {
+      int64_t mc = m0 + wm * C::WM + i * 16 + l16;
+      if (mc > p.M - 1) mc = p.M - 1;
+      ua0[i] = kc < p.rank ? *reinterpret_cast<const uint4*>(p.lr + mc * p.rank + kc) : make_uint4(0, 0, 0, 0);
     }
-    lds_barrier();
   }
   // SwiGLU pairs fragment j (gate) with j + FJ/2 (up) of the same outputs.
   constexpr int NJ = SWIG ? C::FJ / 2 : C::FJ;
@@ -1170,13 +1147,20 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
       }
 #pragma unroll
     for (int r = 0; r < 4; ++r) gatev[r] = EPI == EPI_GATED ? bf16_to_f32(p.gate[n + r]) : 0.f;
-    // L2 fragments (first MFMA operand): lane supplies the staged rank
-    // vector of W-tile row t0 + l16 (and its up partner t0 + WN/2 + l16) at
-    // ranks k0 + 8 lg .. + 7.  The skip above is uniform over the wave
-    // (16 | N, 16 | F), so every lane reaches the MFMAs below.
-    const uint8_t* l2row[2];
-    l2row[0] = l2s_row(t0 + l16);
-    l2row[1] = l2s_row(SWIG ? t0 + C::WN / 2 + l16 : t0 + l16);
+    // L2 fragments (first MFMA operand): the lane supplies ranks k0 + 8 lg ..
+    // + 7 of the L2 row of W-tile row t0 + l16 (and of its up partner
+    // t0 + WN/2 + l16); ranks 0 .. 31 are loaded here.  The skip above is
+    // uniform over the wave (16 | N, 16 | F), so every lane reaches the MFMAs
+    // below.
+    const uint16_t* l2row[2];
+    l2row[0] = p.l2 + w_row_of<C, SWIG>(p, n0, t0 + l16) * p.rank;
+    l2row[1] = p.l2 + w_row_of<C, SWIG>(p, n0, SWIG ? t0 + C::WN / 2 + l16 : t0 + l16) * p.rank;
+    uint4 wv0[LOWRANK ? (SWIG ? 2 : 1) : 1];
+    if constexpr (LOWRANK) {
+#pragma unroll
+      for (int h = 0; h < (SWIG ? 2 : 1); ++h)
+        wv0[h] = lg * 8 < p.rank ? *reinterpret_cast<const uint4*>(l2row[h] + lg * 8) : make_uint4(0, 0, 0, 0);
+    }
     uint2 res[EPI == EPI_GATED ? C::FI : 1];
     if (EPI == EPI_GATED) {
 #pragma unroll
@@ -1187,28 +1171,52 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
       }
     }
 
+    // The rows in two halves (IB fragments each).  Low-rank branch first,
+    // with every lane active: an MFMA mixes all 64 lanes' operands, so rows
+    // past M load row M-1 instead of skipping.  lr[m, :] . L2[:, cols] with
+    // bf16 MFMA 16x16x32 over the rank; per 32-rank chunk the lr fragments
+    // of the half's rows are loaded together, so one memory latency covers
+    // them (loaded next to the output stores of the row loop below, each
+    // would wait for its own).
+    constexpr int IB = C::FI >= 2 ? C::FI / 2 : 1;
 #pragma unroll
-    for (int i = 0; i < C::FI; ++i) {
-      const int64_t m = m0 + wm * C::WM + i * 16 + l16;
-      // Low-rank branch first, with every lane active: an MFMA mixes all
-      // 64 lanes' operands, so rows past M load row M-1 instead of skipping.
-      v4f lrv[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-      if (LOWRANK) {
-        // lr[m, :] . L2[:, cols]: bf16 MFMA 16x16x32 over the rank
-        const int64_t mc = m < p.M ? m : p.M - 1;
+    for (int ib = 0; ib < C::FI; ib += IB) {
+    v4f lrv[LOWRANK ? IB : 1][SWIG ? 2 : 1];
 #pragma unroll
-        for (int h = 0; h < (SWIG ? 2 : 1); ++h) {
-          for (int k0 = 0; k0 < p.rank; k0 += 32) {
-            const int kc = k0 + lg * 8;
-            const bool kin = kc < p.rank;
-            const uint4 ua = kin ? *reinterpret_cast<const uint4*>(p.lr + mc * p.rank + kc)
-                                 : make_uint4(0, 0, 0, 0);
-            const uint4 wv = kin ? *reinterpret_cast<const uint4*>(l2row[h] + kc * 2) : make_uint4(0, 0, 0, 0);
-            lrv[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, wv),
-                                                             __builtin_bit_cast(v8bf, ua), lrv[h], 0, 0, 0);
+    for (int i = 0; i < (LOWRANK ? IB : 1); ++i)
+#pragma unroll
+      for (int h = 0; h < (SWIG ? 2 : 1); ++h) lrv[i][h] = v4f{0.f, 0.f, 0.f, 0.f};
+    if constexpr (LOWRANK) {
+      for (int k0 = 0; k0 < p.rank; k0 += 32) {
+        const int kc = k0 + lg * 8;
+        const bool kin = kc < p.rank;
+        uint4 ua[IB];
+#pragma unroll
+        for (int i = 0; i < IB; ++i) {
+          if (PRE_LR && k0 == 0) {
+            ua[i] = ua0[PRE_LR ? ib + i : 0];
+          } else {
+            int64_t mc = m0 + wm * C::WM + (ib + i) * 16 + l16;
+            if (mc > p.M - 1) mc = p.M - 1;
+            ua[i] = kin ? *reinterpret_cast<const uint4*>(p.lr + mc * p.rank + kc) : make_uint4(0, 0, 0, 0);
           }
         }
+        uint4 wv[SWIG ? 2 : 1];
+#pragma unroll
+        for (int h = 0; h < (SWIG ? 2 : 1); ++h)
+          wv[h] = k0 == 0 ? wv0[h] : (kin ? *reinterpret_cast<const uint4*>(l2row[h] + kc) : make_uint4(0, 0, 0, 0));
+#pragma unroll
+        for (int i = 0; i < IB; ++i)
+#pragma unroll
+          for (int h = 0; h < (SWIG ? 2 : 1); ++h)
+            lrv[i][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, wv[h]),
+                                                                __builtin_bit_cast(v8bf, ua[i]), lrv[i][h], 0, 0, 0);
       }
+    }
+
+#pragma unroll
+    for (int i = ib; i < ib + IB; ++i) {
+      const int64_t m = m0 + wm * C::WM + i * 16 + l16;
       if (m >= p.M) continue;
       if (EPI == EPI_I32) {
         const acc_t a4 = acc[C::GROUP ? 0 : j][C::GROUP ? 0 : i];  // FP6: exact integers in fp32
@@ -1228,7 +1236,7 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
         for (int r = 0; r < 4; ++r) {
           const float v = C::GROUP ? yf[C::GROUP ? jj : 0][C::GROUP ? i : 0][r]
                                    : (float)acc[C::GROUP ? 0 : jj][C::GROUP ? 0 : i][r];
-          y[h][r] = v * sam[i] * swv[h][r] + addv[h][r] + (LOWRANK ? lrv[h][r] : 0.f);
+          y[h][r] = v * sam[i] * swv[h][r] + addv[h][r] + (LOWRANK ? lrv[LOWRANK ? i - ib : 0][SWIG ? h : 0][r] : 0.f);
         }
       }
       float o[4];
@@ -1256,6 +1264,7 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
       *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + m * p.ldo + n) =
           make_uint2(__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1));
     }
+    }  // row halves
   }
 }
 

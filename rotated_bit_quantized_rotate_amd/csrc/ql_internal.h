@@ -141,7 +141,7 @@ struct GemmArgs {
   const uint16_t* residual;
   const uint16_t* gate;
   const uint16_t* lr;   // [M, rank]
-  const uint16_t* l2;   // [rank, N]
+  const uint16_t* l2;   // [N, rank] (L2 transposed)
   int rank;
   int epilogue;         // QL_EPI_*
   void* out;
@@ -184,7 +184,7 @@ struct SplitArgs {
   const float* omega;     // [K, rank + oversample]
   int rank, oversample, power_iters, refine_iters, scale_mode;
   uint16_t* l1;           // [K, rank] bf16
-  uint16_t* l2;           // [rank, N] bf16
+  uint16_t* l2;           // [N, rank] bf16 (L2 transposed)
   uint8_t* packed;        // [N, K/2]
   float* scales;
   float* errors;          // [refine_iters + 1]

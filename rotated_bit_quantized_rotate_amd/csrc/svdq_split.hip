@@ -356,16 +356,15 @@ __global__ void finish_l1_kernel(const float* __restrict__ F, const float* __res
   l1r[e] = bf16_to_f32(b);
 }
 
-// L2[j, n] = bf16(F[n, j]) (F = Q M2 = L2^T, [N x r]); l2r keeps the rounded
-// value in F's layout.
+// L2 = bf16(F) with F = Q M2 = L2^T, [N x r]: the factor is stored in the
+// [N, rank] layout the low-rank GEMM reads (row n: the rank vector of output
+// column n); l2r keeps the rounded values as fp32 in the same layout.
 __global__ void finish_l2_kernel(const float* __restrict__ F, int64_t N, int r, uint16_t* __restrict__ l2,
                                  float* __restrict__ l2r) {
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= N * r) return;
-  const int64_t nn = e / r;
-  const int j = (int)(e % r);
   const uint32_t b = f32_to_bf16(F[e]);
-  l2[(int64_t)j * N + nn] = (uint16_t)b;
+  l2[e] = (uint16_t)b;
   l2r[e] = bf16_to_f32(b);
 }
 

@@ -36,6 +36,12 @@ def to_dev_bf16(bits, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
 
 
+def to_dev_l2(l2_bits, device="cuda"):
+    """The low-rank GEMMs take L2 transposed: bf16 [N, rank] from the
+    oracle's [rank, N] bits."""
+    return to_dev_bf16(np.ascontiguousarray(np.asarray(l2_bits).T), device)
+
+
 def bf16_bits(t):
     import torch
 

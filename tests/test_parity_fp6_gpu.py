@@ -22,7 +22,7 @@ import pytest
 import oracle as O
 import workloads as W
 from tests import parity_checks as P
-from tests.helpers import bf16_bits, ensure_built, to_dev, to_dev_bf16
+from tests.helpers import bf16_bits, ensure_built, to_dev, to_dev_bf16, to_dev_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -314,7 +314,7 @@ def test_fp6_group64_lowrank_equals_int4_path(Q, rank, epi):
     qa, qw, sa_h, sw_h = _group_pair(M, N, K, 5 + rank)
     sa, sw = to_dev(sa_h), to_dev(sw_h)
     lr = to_dev_bf16(_rand_bf16(6, (M, rank), 0.5)) if rank else None
-    l2 = to_dev_bf16(_rand_bf16(7, (rank, N), 0.05)) if rank else None
+    l2 = to_dev_l2(_rand_bf16(7, (rank, N), 0.05)) if rank else None
     ref = Q.qgemm_w4a4_lowrank(to_dev(qa), sa, to_dev(O.pack_int4(qw)), sw, K, lr=lr, l2=l2, epilogue=epi)
     got = Q.qgemm_w4a4_fp6_lowrank(to_dev(O.pack_fp6(qa)), sa, to_dev(O.pack_fp6(qw)), sw, K, lr=lr, l2=l2,
                                    epilogue=epi)
@@ -324,7 +324,7 @@ def test_fp6_group64_lowrank_equals_int4_path(Q, rank, epi):
     # the oracle: dequantized group sums plus lr L2 (lr as given), through the epilogue
     y, dy = P.linear_bound(O.QuantResult(qa, sa_h, 4, "group64", None), O.QuantResult(qw, sw_h, 4, "group64", None))
     if rank:
-        lrf, l2f = O.bf16_bits_to_f64(bf16_bits(lr)), O.bf16_bits_to_f64(bf16_bits(l2))
+        lrf, l2f = O.bf16_bits_to_f64(bf16_bits(lr)), O.bf16_bits_to_f64(bf16_bits(l2).T)
         y = y + lrf @ l2f
         dy = dy + (rank + 4) * P.U * (np.abs(lrf) @ np.abs(l2f)) + 3 * P.U * np.abs(lrf @ l2f)
     want, dw = P.epilogue_with_bound(y, dy, epi)
@@ -360,7 +360,7 @@ def test_fp6_group64_svdq_gateup_full_size(Q):
     x = torch.randn(M, K, device="cuda").to(torch.bfloat16)
     w = (torch.randn(N, K, device="cuda") * 0.02).to(torch.bfloat16)
     l1 = (torch.randn(K, r, device="cuda") * 0.02).to(torch.bfloat16)
-    l2 = (torch.randn(r, N, device="cuda") * 0.02).to(torch.bfloat16)
+    l2 = (torch.randn(N, r, device="cuda") * 0.02).to(torch.bfloat16)  # L2 transposed
     a8, sa8, lr = Q.rotate_quantize_act(x, bits=4, scale_mode="group64", layout="i8", l1=l1)
     a6, sa6, _ = Q.rotate_quantize_act(x, bits=4, scale_mode="group64", layout="fp6")
     w4, sw4 = Q.pack_weight_int4(w, scale_mode="group64")
@@ -380,7 +380,7 @@ def test_fp6_group64_svdq_gateup_full_size(Q):
     qa = O.QuantResult(O.unpack_fp6(a6[ri].cpu().numpy()), sa6[ri].cpu().numpy(), 4, "group64", None)
     qw = O.QuantResult(O.unpack_fp6(w6[torch.as_tensor(ns, device="cuda")].cpu().numpy()), sw6.cpu().numpy()[ns],
                        4, "group64", None)
-    y, dy = P.linear_bound(qa, qw, bf16_bits(x[ri]), bf16_bits(l1), bf16_bits(l2)[:, ns])
+    y, dy = P.linear_bound(qa, qw, bf16_bits(x[ri]), bf16_bits(l1), np.ascontiguousarray(bf16_bits(l2)[ns].T))
     want, dw = P.epilogue_with_bound(y, dy, "swiglu")
     P.assert_outputs_close(O.bf16_bits_to_f64(bf16_bits(got[ri][:, torch.as_tensor(fs, device="cuda")])),
                            want, dw, what="fp6 svdq gate|up")

@@ -25,7 +25,7 @@ import pytest
 import oracle as O
 import workloads as W
 from tests import parity_checks as P
-from tests.helpers import bf16_bits, bf16_ulp_diff, ensure_built, rel_fro, to_dev, to_dev_bf16
+from tests.helpers import bf16_bits, bf16_ulp_diff, ensure_built, rel_fro, to_dev, to_dev_bf16, to_dev_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -326,14 +326,18 @@ def test_rmsnorm_prologue_reused_by_two_gemms(Q):
         assert rel_fro(O.bf16_bits_to_f64(bf16_bits(out)), want) <= REL_FRO
 
 
-@pytest.mark.parametrize("rank", [16, 32, 64])
-def test_lowrank_down_projection(Q, rank):
+@pytest.mark.parametrize("rank", [16, 32, 64, 128])
+@pytest.mark.parametrize("mode", ["group64", "row"])
+def test_lowrank_down_projection(Q, rank, mode):
+    """lr = X @ L1 next to the quantization pass (its own launch, which
+    re-reads X), with group-64 and row scales: 130 rows are nine 16-row
+    blocks, the last with 2 rows."""
     import torch
 
     M, K = 130, 1024
     xb = _rand_bf16(6, (M, K))
     l1b = _rand_bf16(7, (K, rank), 0.02)
-    _, _, lr = Q.rotate_quantize_act(to_dev_bf16(xb), bits=4, scale_mode="group64",
+    _, _, lr = Q.rotate_quantize_act(to_dev_bf16(xb), bits=4, scale_mode=mode,
                                      l1=to_dev_bf16(l1b))
     torch.cuda.synchronize()
     want = O.bf16_bits_to_f64(xb) @ O.bf16_bits_to_f64(l1b)
@@ -598,7 +602,7 @@ def _lowrank_same_codes(Q, M, F, K, rank, mode, epi, seed, a_layout="i8"):
     lrb = _rand_bf16(seed + 2, (M, max(rank, 16)), 0.5)[:, :rank]
     l2b = _rand_bf16(seed + 3, (max(rank, 16), N), 0.05)[:rank]
     lr = to_dev_bf16(np.ascontiguousarray(lrb)) if rank else None
-    l2 = to_dev_bf16(np.ascontiguousarray(l2b)) if rank else None
+    l2 = to_dev_l2(l2b) if rank else None
     out = Q.qgemm_w4a4_lowrank(a, sa, w, sw, K, lr=lr, l2=l2, a_scale_mode=mode, w_scale_mode=mode,
                                a_layout=a_layout, epilogue=epi)
     torch.cuda.synchronize()
@@ -646,7 +650,7 @@ def test_group64_lowrank_with_device_lr(Q):
     w, sw = _upload_quant(qw, True)
     _, _, lr = Q.rotate_quantize_act(to_dev_bf16(xb), bits=4, scale_mode="group64", l1=to_dev_bf16(l1))
     for epi in ("swiglu", "bf16"):
-        out = Q.qgemm_w4a4_lowrank(a, sa, w, sw, K, lr=lr, l2=to_dev_bf16(l2), epilogue=epi)
+        out = Q.qgemm_w4a4_lowrank(a, sa, w, sw, K, lr=lr, l2=to_dev_l2(l2), epilogue=epi)
         torch.cuda.synchronize()
         y, dy = P.linear_bound(qa, qw, xb, l1, l2)
         want, dw = P.epilogue_with_bound(y, dy, epi)
@@ -685,7 +689,7 @@ def _e2e(Q, wl, rows=None, wrows=None):
         out = Q.qgemm_w8a8(a_codes, sa, wq, sw, a_scale_mode=mode, w_scale_mode=mode)
     elif mode == "group64" or rank:
         out = Q.qgemm_w4a4_lowrank(a_codes, sa, wq, sw, wl.K, lr=lr,
-                                   l2=to_dev_bf16(wl.l2) if rank else None,
+                                   l2=to_dev_l2(wl.l2) if rank else None,
                                    a_scale_mode=mode, w_scale_mode=mode, epilogue=wl.epilogue)
     else:
         out = Q.qgemm_w4a4(a_codes, sa, wq, sw, wl.K, a_scale_mode=mode, w_scale_mode=mode)
@@ -822,7 +826,7 @@ def test_gemm_empty_inputs(Q):
                      gate=torch.ones(N, dtype=torch.bfloat16, device=d), epilogue="gated_residual"),
         Q.qgemm_w4a4_lowrank(a8, torch.empty((0, K // 64), dtype=torch.float32, device=d), w4, swg, K,
                              lr=torch.empty((0, r), dtype=torch.bfloat16, device=d),
-                             l2=torch.zeros((r, N), dtype=torch.bfloat16, device=d)),
+                             l2=torch.zeros((N, r), dtype=torch.bfloat16, device=d)),
         Q.qgemm_w4a4_fp6(torch.empty((0, K // 4 * 3), dtype=torch.uint8, device=d), sa, w6, sw, K),
     ]
     torch.cuda.synchronize()

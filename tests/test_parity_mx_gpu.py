@@ -21,7 +21,7 @@ import pytest
 import oracle as O
 import workloads as W
 from tests import parity_checks as P
-from tests.helpers import bf16_bits, ensure_built, rel_fro, to_dev, to_dev_bf16
+from tests.helpers import bf16_bits, ensure_built, rel_fro, to_dev, to_dev_bf16, to_dev_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -346,7 +346,7 @@ def test_mx_lowrank_gemm(Q, fmt, r, epi):
                                                                   np.abs(O.bf16_bits_to_f64(l1)))
     lr_got = O.bf16_bits_to_f64(bf16_bits(lr))
     assert np.all(np.abs(lr_got - lr_want) <= lr_bound + 2.0 ** -133)
-    out = Q.qgemm_mx_lowrank(ca, sa, cw, sw, K, fmt=fmt, lr=lr, l2=to_dev_bf16(l2), epilogue=epi)
+    out = Q.qgemm_mx_lowrank(ca, sa, cw, sw, K, fmt=fmt, lr=lr, l2=to_dev_l2(l2), epilogue=epi)
     torch.cuda.synchronize()
     want, bound = _lowrank_want(xb, l1, l2, ca, sa, cw, sw, fmt, epi)
     got = out.cpu().numpy().astype(np.float64) if epi == "f32" else O.bf16_bits_to_f64(bf16_bits(out))
@@ -379,7 +379,7 @@ def test_mx_svdq_gateup_full_size_sampled_rows(Q):
     N = wl.w.shape[0]
     ca, sa, lr = Q.rotate_quantize_mx(to_dev_bf16(wl.x), fmt="fp4", l1=to_dev_bf16(wl.l1))
     cw, sw = Q.rotate_quantize_mx(to_dev_bf16(wl.w), fmt="fp4")
-    out = Q.qgemm_mx_lowrank(ca, sa, cw, sw, K, fmt="fp4", lr=lr, l2=to_dev_bf16(wl.l2), epilogue="swiglu")
+    out = Q.qgemm_mx_lowrank(ca, sa, cw, sw, K, fmt="fp4", lr=lr, l2=to_dev_l2(wl.l2), epilogue="swiglu")
     torch.cuda.synchronize()
     rows = np.array([0, 255, 2048, 4095])
     want, bound = _lowrank_want(wl.x, wl.l1, wl.l2, ca, sa, cw, sw, "fp4", "swiglu", rows=rows)

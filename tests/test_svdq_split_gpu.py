@@ -38,7 +38,9 @@ def _run(Q, wb, omega, rank, over, pi, ri, mode, rms=None):
     out = Q.svdq_split(to_dev_bf16(wb), to_dev(omega), rank, over, pi, ri, mode,
                        act_rms=None if rms is None else to_dev(rms))
     torch.cuda.synchronize()
-    return {k: (bf16_bits(v) if v.dtype == torch.bfloat16 else v.cpu().numpy()) for k, v in out.items()}
+    g = {k: (bf16_bits(v) if v.dtype == torch.bfloat16 else v.cpu().numpy()) for k, v in out.items()}
+    g["l2"] = np.ascontiguousarray(g["l2"].T)  # the library stores L2 transposed, [N, rank]
+    return g
 
 
 def _check_split_quant(codes, scales, wb, l1_bits, l2_bits, mode, budget=P.FLIP_BUDGET):
@@ -174,6 +176,6 @@ def test_split_full_size_gateup(Q):
     ri = torch.as_tensor(rows, device="cuda")
     codes = O.unpack_int4(out["packed"][ri].cpu().numpy())
     _check_split_quant(codes, out["scales"][ri].cpu().numpy(), np.ascontiguousarray(wb[rows]), bf16_bits(out["l1"]),
-                       np.ascontiguousarray(bf16_bits(out["l2"])[:, rows]), "group64")
+                       np.ascontiguousarray(bf16_bits(out["l2"])[rows].T), "group64")
     # the objective is a few percent of the weight
     assert 0.0 < e[best] < 0.2 * float(np.linalg.norm(O.bf16_bits_to_f64(wb[:2048]))) * np.sqrt(N / 2048)
