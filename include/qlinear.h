@@ -93,6 +93,13 @@ enum {
  *                    run of 8 consecutive channels 8c..8c+7, byte 4c+j
  *                    (j = 0..3) holds channel 8c+j in its low nibble and
  *                    channel 8c+j+4 in its high nibble (two's complement).
+ *                    Packed INT4 WEIGHTS (pack_weight_int4, svdq_split, the
+ *                    w operand of the INT4 GEMMs) also pair their rows: for
+ *                    every 128-channel slice s of K, the 64 bytes of row 2p
+ *                    and then those of row 2p + 1 are adjacent, at byte
+ *                    p * K + 128 s (+ 64 for row 2p + 1), so one cache line
+ *                    holds a slice of two rows.  Packed activations keep
+ *                    plain rows.
  * QL_LAYOUT_FP6    : each int4 code as its exact FP6 e2m3 value (sign bit, 2
  *                    exponent bits with bias 1, 3 mantissa bits), [R, 3K/4]
  *                    bytes; for the FP6 GEMM only.  A row is K/128 blocks of
@@ -202,7 +209,8 @@ int rmsnorm_rotate_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t
  * Turbo OrbitQuant W4A4", section "What is quantized") are produced by
  * rotate_quantize_act with bits = 8 and QL_SCALE_ROW.
  *   w      [N, K] bf16 (torch Linear layout: out x in), row stride ldw
- *   packed out: [N, K/2] bytes in the QL_LAYOUT_PACKED order
+ *   packed out: [N, K/2] bytes in the QL_LAYOUT_PACKED weight order (row
+ *            pairs interleaved per 128-channel slice)
  *   scales out: float32 [1] | [N] | [N, K/64]                              */
 int pack_weight_int4(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
                      int scale_mode, int rotate, uint8_t* packed, float* scales,
@@ -223,7 +231,8 @@ int pack_weight_fp6(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
  * and gate/up projections).
  *   a        [M, K] activation codes in `a_layout`, dense rows
  *   sa       activation scales per a_scale_mode (TENSOR | ROW)
- *   w        [N, K/2] packed int4 weight codes, dense rows
+ *   w        [N, K/2] packed int4 weight codes in the weight order of
+ *            QL_LAYOUT_PACKED (row pairs interleaved per 128-channel slice)
  *   sw       weight scales per w_scale_mode (TENSOR | ROW)
  *   bias     NULL or bf16 [N]
  *   epilogue QL_EPI_BF16 | QL_EPI_F32 | QL_EPI_I32 (I32 ignores scales and bias) |

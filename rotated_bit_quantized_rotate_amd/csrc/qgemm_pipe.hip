@@ -325,6 +325,8 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   // MFMA stream.
   const bool w_hi = wave < C::W_SPLIT;
   constexpr int NDMA = C::NDMA;
+  constexpr bool WPAIR = C::WP && !C::F6;  // packed INT4 weights: paired rows
+  static_assert(!WPAIR || C::WRB == 64, "paired weight rows need 64-byte stage rows");
   // Per-lane byte offsets of every load slot, fixed for the whole K loop:
   // a load is a wave-uniform base (advanced by the stage) plus a 32-bit lane
   // offset, the global_load_lds saddr form, so issuing one costs no vector
@@ -353,7 +355,11 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
     const int ci = (wave + C::NW * tw) * 64 + lane;
     const int rl = C::F6 ? ci / CPR : (wave + C::NW * tw) * (1024 / C::WRB) + lane / CPR;
     const int ch = C::F6 ? swz6(rl, ci % CPR) : swz<C::WRB, C::GROUP, C::MX == 8>(rl, lane % CPR);
-    w_vo[tw] = (uint32_t)(w_row_of<C, SWIG>(p, n0, rl) * ldw + (ch << 4));
+    // packed INT4 weights: rows 2p, 2p + 1 interleaved per 128-channel stage
+    // (64 bytes each), so a stage of two rows is one cache line
+    const int64_t wr = w_row_of<C, SWIG>(p, n0, rl);
+    w_vo[tw] = WPAIR ? (uint32_t)((wr >> 1) * 2 * ldw + ((wr & 1) << 6) + (ch << 4))
+                     : (uint32_t)(wr * ldw + (ch << 4));
   }
   uint32_t s_vo[C::SCL ? C::S_PER_WAVE : 1];
 #pragma unroll
@@ -403,7 +409,7 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
       const int tw = t - C::A_PER_WAVE;
       if (tw < C::W_HI - 1 || w_hi) {
         const int q = wave + C::NW * tw;
-        dma_b128(p.w, w_vo[tw] + (uint32_t)(kt * C::WRB), st + C::SA + q * 1024);
+        dma_b128(p.w, w_vo[tw] + (uint32_t)(kt * (WPAIR ? 2 * C::WRB : C::WRB)), st + C::SA + q * 1024);
       }
     } else if (C::MX) {
       const int ts = t - C::A_PER_WAVE - C::W_HI;

@@ -107,6 +107,9 @@ struct RqArgs {
   const uint16_t* mscale;
   const uint16_t* mshift;
   float eps;
+  // packed weights (packed == 1): rows 2p and 2p + 1 interleaved per
+  // 128-channel slice (64 bytes each), the GEMM's weight order
+  int paired;
 };
 
 int launch_rotate_quantize(const RqArgs& a, hipStream_t s);

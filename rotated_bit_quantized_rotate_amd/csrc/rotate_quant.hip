@@ -102,7 +102,11 @@ __device__ __forceinline__ uint32_t fp6_join4(uint32_t p) {
 // FP6 layouts keep plain stores: an FP6 block is written by two instructions
 // (16- and 8-byte pieces), and as nontemporal partial lines those cost
 // 8.5 us per 4096 x 5120 step.
-__device__ __forceinline__ void store_codes(void* codes, int64_t off_elems, int fmt, const uint32_t (&u)[16]) {
+// pair_k != 0 (packed weights): rows 2p and 2p + 1 interleaved per 128-channel
+// slice -- channel c of row r at byte (r / 2) K + 128 (c / 128) + 64 (r % 2)
+// + (c % 128) / 2 (K = pair_k); a lane's 16 channels never cross a slice.
+__device__ __forceinline__ void store_codes(void* codes, int64_t off_elems, int fmt, const uint32_t (&u)[16],
+                                            int64_t pair_k = 0) {
   if (fmt == 2) {
     // FP6 layout: a row is 96-byte blocks of 128 channels; in a block,
     // 32-channel sub-block g is the 192-bit value v_g (channel i at bits
@@ -131,7 +135,12 @@ __device__ __forceinline__ void store_codes(void* codes, int64_t off_elems, int 
     // byte 4c+j: low nibble channel 8c+j, high nibble channel 8c+j+4
     const uint32_t l0 = pack4(u[0], u[1], u[2], u[3]), h0 = pack4(u[4], u[5], u[6], u[7]);
     const uint32_t l1 = pack4(u[8], u[9], u[10], u[11]), h1 = pack4(u[12], u[13], u[14], u[15]);
-    *reinterpret_cast<uint2*>(static_cast<uint8_t*>(codes) + off_elems / 2) =
+    int64_t byte = off_elems / 2;
+    if (pair_k) {
+      const int64_t r = off_elems / pair_k, c = off_elems - r * pair_k;
+      byte = (r >> 1) * pair_k + ((c >> 7) << 7) + ((r & 1) << 6) + ((c & 127) >> 1);
+    }
+    *reinterpret_cast<uint2*>(static_cast<uint8_t*>(codes) + byte) =
         make_uint2((l0 & 0x0F0F0F0Fu) | ((h0 << 4) & 0xF0F0F0F0u), (l1 & 0x0F0F0F0Fu) | ((h1 << 4) & 0xF0F0F0F0u));
   }
 }
@@ -333,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void rq_kernel(RqArgs a, int slots_per_ro
 #pragma unroll
         for (int e = 0; e < 16; ++e) u[e] = code_bits(v[j][e], inv);
       }
-      store_codes(a.codes, code_row + (int64_t)g * 256 + t * 16, a.packed, u);
+      store_codes(a.codes, code_row + (int64_t)g * 256 + t * 16, a.packed, u, a.paired ? a.K : 0);
       if (a.mode == 2) {
         if ((t & 3) == 0)
           a.scales[row * (a.K >> 6) + g * 4 + (t >> 2)] = __fdiv_rn(am, qmax) * post;

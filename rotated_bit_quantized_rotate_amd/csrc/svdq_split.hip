@@ -401,7 +401,9 @@ __global__ __launch_bounds__(kSplitThreads) void deq_target_kernel(
     const int64_t c0 = g * 256 + t * 16;
     float e[16];
     if (codes) {
-      const uint2 pk = *reinterpret_cast<const uint2*>(codes + row * (K >> 1) + (c0 >> 1));
+      // packed weight order: rows 2p, 2p + 1 interleaved per 128-channel slice
+      const uint2 pk = *reinterpret_cast<const uint2*>(codes + (row >> 1) * K + ((c0 >> 7) << 7) + ((row & 1) << 6) +
+                                                       ((c0 & 127) >> 1));
       const float sc = mode == 0 ? scales[0] : (mode == 1 ? scales[row] : scales[row * (K >> 6) + (c0 >> 6)]);
       const uint32_t wds[2] = {pk.x, pk.y};
 #pragma unroll
@@ -672,6 +674,7 @@ int launch_svdq_split(const SplitArgs& a, hipStream_t s) {
                        w.T, w.Rb);
     run.check();
     RqArgs q{w.Rb, N, K, K, 4, a.scale_mode, 1, 1, w.codes_c, w.scales_c};
+    q.paired = 1;  // the GEMM's packed weight order
     if (launch_rotate_quantize(q, s) != OK) return ERR_LAUNCH;
     // objective, and the next iteration's target from this iteration's Q
     hipLaunchKernelGGL(deq_target_kernel, dim3(deq_blocks), dim3(kSplitThreads), 0, s, a.w, a.ldw, N, K, w.d,

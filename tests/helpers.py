@@ -36,6 +36,21 @@ def to_dev_bf16(bits, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
 
 
+def pair_w4(packed):
+    """Row-major packed int4 weights [N, K/2] -> the library's weight order:
+    rows 2p and 2p + 1 interleaved per 128-channel slice (64 bytes each)."""
+    p = np.asarray(packed)
+    n, h = p.shape
+    return np.ascontiguousarray(p.reshape(n // 2, 2, h // 64, 64).transpose(0, 2, 1, 3).reshape(n, h))
+
+
+def unpair_w4(packed):
+    """The library's packed weight order -> row-major [N, K/2]."""
+    p = np.asarray(packed)
+    n, h = p.shape
+    return np.ascontiguousarray(p.reshape(n // 2, h // 64, 2, 64).transpose(0, 2, 1, 3).reshape(n, h))
+
+
 def to_dev_l2(l2_bits, device="cuda"):
     """The low-rank GEMMs take L2 transposed: bf16 [N, rank] from the
     oracle's [rank, N] bits."""

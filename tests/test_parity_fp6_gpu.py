@@ -22,7 +22,7 @@ import pytest
 import oracle as O
 import workloads as W
 from tests import parity_checks as P
-from tests.helpers import bf16_bits, ensure_built, to_dev, to_dev_bf16, to_dev_l2
+from tests.helpers import bf16_bits, ensure_built, pair_w4, to_dev, to_dev_bf16, to_dev_l2, unpair_w4
 
 pytestmark = pytest.mark.gpu
 
@@ -119,7 +119,7 @@ def test_pack_weight_fp6(Q, mode):
     p4, s4 = Q.pack_weight_int4(w, scale_mode=mode)
     p6, s6 = Q.pack_weight_fp6(w, scale_mode=mode)
     torch.cuda.synchronize()
-    assert np.array_equal(p6.cpu().numpy(), O.pack_fp6(O.unpack_int4(p4.cpu().numpy())))
+    assert np.array_equal(p6.cpu().numpy(), O.pack_fp6(O.unpack_int4(unpair_w4(p4.cpu().numpy()))))
     assert torch.equal(s6, s4)
 
 
@@ -184,7 +184,7 @@ def test_fp6_epilogues_equal_int4_path(Q, M, N, K, mode):
 
     qa, qw, sa_h, sw_h = _same_codes_pair(M, N, K, M + N, mode)
     sa, sw = to_dev(sa_h), to_dev(sw_h)
-    a8, w4 = to_dev(qa), to_dev(O.pack_int4(qw))
+    a8, w4 = to_dev(qa), to_dev(pair_w4(O.pack_int4(qw)))
     a6, w6 = to_dev(O.pack_fp6(qa)), to_dev(O.pack_fp6(qw))
     bias = to_dev_bf16(_rand_bf16(M, (N,), 0.1))
     rows = np.unique(np.concatenate([np.arange(4), M - 1 - np.arange(4),
@@ -216,7 +216,7 @@ def test_fp6_strided_output_and_empty(Q):
     a6, w6 = to_dev(O.pack_fp6(qa)), to_dev(O.pack_fp6(qw))
     big = torch.zeros((M, N + 16), dtype=torch.bfloat16, device="cuda")
     out = Q.qgemm_w4a4_fp6(a6, sa, w6, sw, K, out=big[:, :N])
-    ref = Q.qgemm_w4a4(to_dev(qa), sa, to_dev(O.pack_int4(qw)), sw, K)
+    ref = Q.qgemm_w4a4(to_dev(qa), sa, to_dev(pair_w4(O.pack_int4(qw))), sw, K)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
     assert not big[:, N:].any().item(), "store past the row end"
@@ -250,7 +250,7 @@ def test_fp6_attention_projection_full_size(Q):
     rows = np.unique(np.concatenate([np.arange(4), M - 1 - np.arange(4), rng.choice(M, 24, replace=False)]))
     qa = O.unpack_fp6(a6[rows].cpu().numpy())
     assert np.array_equal(qa, a8[rows].cpu().numpy())
-    qw = O.unpack_int4(w4.cpu().numpy())
+    qw = O.unpack_int4(unpair_w4(w4.cpu().numpy()))
     assert np.array_equal(acc[rows].cpu().numpy().astype(np.int64), O.int_gemm(qa, qw))
     assert bf16_bits(got).shape == (M, N)
 
@@ -275,7 +275,7 @@ def test_fp6_group64_equals_int4_path(Q, M, N, K):
 
     qa, qw, sa_h, sw_h = _group_pair(M, N, K, M + 3 * N + K)
     sa, sw = to_dev(sa_h), to_dev(sw_h)
-    a8, w4 = to_dev(qa), to_dev(O.pack_int4(qw))
+    a8, w4 = to_dev(qa), to_dev(pair_w4(O.pack_int4(qw)))
     a6, w6 = to_dev(O.pack_fp6(qa)), to_dev(O.pack_fp6(qw))
     bias = to_dev_bf16(_rand_bf16(N, (N,), 0.1))
     for epi in ("bf16", "f32"):
@@ -315,7 +315,7 @@ def test_fp6_group64_lowrank_equals_int4_path(Q, rank, epi):
     sa, sw = to_dev(sa_h), to_dev(sw_h)
     lr = to_dev_bf16(_rand_bf16(6, (M, rank), 0.5)) if rank else None
     l2 = to_dev_l2(_rand_bf16(7, (rank, N), 0.05)) if rank else None
-    ref = Q.qgemm_w4a4_lowrank(to_dev(qa), sa, to_dev(O.pack_int4(qw)), sw, K, lr=lr, l2=l2, epilogue=epi)
+    ref = Q.qgemm_w4a4_lowrank(to_dev(qa), sa, to_dev(pair_w4(O.pack_int4(qw))), sw, K, lr=lr, l2=l2, epilogue=epi)
     got = Q.qgemm_w4a4_fp6_lowrank(to_dev(O.pack_fp6(qa)), sa, to_dev(O.pack_fp6(qw)), sw, K, lr=lr, l2=l2,
                                    epilogue=epi)
     torch.cuda.synchronize()

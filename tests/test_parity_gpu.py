@@ -25,7 +25,8 @@ import pytest
 import oracle as O
 import workloads as W
 from tests import parity_checks as P
-from tests.helpers import bf16_bits, bf16_ulp_diff, ensure_built, rel_fro, to_dev, to_dev_bf16, to_dev_l2
+from tests.helpers import (bf16_bits, bf16_ulp_diff, ensure_built, pair_w4, rel_fro, to_dev, to_dev_bf16,
+                           to_dev_l2, unpair_w4)
 
 pytestmark = pytest.mark.gpu
 
@@ -356,7 +357,7 @@ def test_pack_weight_int4_matches_oracle(Q, mode):
     wb = _rand_bf16(8, (N, K), 0.02)
     packed, scales = Q.pack_weight_int4(to_dev_bf16(wb), scale_mode=mode)
     torch.cuda.synchronize()
-    got = O.unpack_int4(packed.cpu().numpy())
+    got = O.unpack_int4(unpair_w4(packed.cpu().numpy()))
     _check_prologue(got, scales.cpu().numpy(), wb, 4, mode)
 
 
@@ -378,7 +379,7 @@ def test_w4a4_int32_bit_exact(Q, M, N, K, a_layout):
     qa = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
     qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
     a = to_dev(O.pack_int4(qa) if a_layout == "packed" else qa)
-    w = to_dev(O.pack_int4(qw))
+    w = to_dev(pair_w4(O.pack_int4(qw)))
     one_a = torch.ones(M, dtype=torch.float32, device="cuda")
     one_w = torch.ones(N, dtype=torch.float32, device="cuda")
     out = Q.qgemm_w4a4(a, one_a, w, one_w, K, a_layout=a_layout, epilogue="i32")
@@ -414,7 +415,7 @@ def test_int32_extremes(Q):
     assert np.array_equal(out.cpu().numpy().astype(np.int64), O.int_gemm(qa, qw))
     qa4 = np.full((M, 5120), -7, np.int8)
     qw4 = np.full((N, 5120), 7, np.int8)
-    out = Q.qgemm_w4a4(to_dev(O.pack_int4(qa4)), ones[:M], to_dev(O.pack_int4(qw4)), ones[:N], 5120,
+    out = Q.qgemm_w4a4(to_dev(O.pack_int4(qa4)), ones[:M], to_dev(pair_w4(O.pack_int4(qw4))), ones[:N], 5120,
                        a_layout="packed", epilogue="i32")
     torch.cuda.synchronize()
     assert (out.cpu().numpy() == -49 * 5120).all()
@@ -432,7 +433,7 @@ def test_group64_unit_scales_exact(Q):
     qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
     sa = torch.ones((M, K // 64), dtype=torch.float32, device="cuda")
     sw = torch.ones((N, K // 64), dtype=torch.float32, device="cuda")
-    out = Q.qgemm_w4a4_lowrank(to_dev(qa), sa, to_dev(O.pack_int4(qw)), sw, K, epilogue="f32")
+    out = Q.qgemm_w4a4_lowrank(to_dev(qa), sa, to_dev(pair_w4(O.pack_int4(qw))), sw, K, epilogue="f32")
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().astype(np.float64), O.int_gemm(qa, qw).astype(np.float64))
 
@@ -453,7 +454,7 @@ def test_group64_pow2_scales_exact(Q, a_layout):
     sa_h = np.ldexp(1.0, -rng.integers(0, 4, size=(M, K // 64))).astype(np.float32)
     sw_h = np.ldexp(1.0, -rng.integers(0, 4, size=(N, K // 64))).astype(np.float32)
     a = to_dev(O.pack_int4(qa) if a_layout == "packed" else qa)
-    out = Q.qgemm_w4a4_lowrank(a, to_dev(sa_h), to_dev(O.pack_int4(qw)), to_dev(sw_h), K,
+    out = Q.qgemm_w4a4_lowrank(a, to_dev(sa_h), to_dev(pair_w4(O.pack_int4(qw))), to_dev(sw_h), K,
                                a_layout=a_layout, epilogue="f32")
     torch.cuda.synchronize()
     ref_a = O.QuantResult(qa, sa_h, 4, "group64", None)
@@ -470,8 +471,12 @@ def _assert_bf16_close(got_bits, want_f64, bound):
     P.assert_outputs_close(O.bf16_bits_to_f64(got_bits), want_f64, bound)
 
 
-def _upload_quant(ref, packed):
+def _upload_quant(ref, packed, weight=False):
+    """Codes (packed int4 or int8 containers) and scales on the device;
+    packed weights in the library's paired-row order."""
     codes = O.pack_int4(ref.codes) if packed else ref.codes
+    if packed and weight:
+        codes = pair_w4(codes)
     return to_dev(codes), to_dev(np.ascontiguousarray(ref.scales))
 
 
@@ -486,7 +491,7 @@ def test_w4a4_bf16_epilogue_same_codes(Q, mode):
     qa = O.quantize_activations(xb, 4, mode)
     qw = O.quantize_weights(wb, 4, mode)
     a, sa = _upload_quant(qa, False)
-    w, sw = _upload_quant(qw, True)
+    w, sw = _upload_quant(qw, True, weight=True)
     for bb in (None, bias):
         out = Q.qgemm_w4a4(a, sa, w, sw, K, a_scale_mode=mode, w_scale_mode=mode,
                            bias=None if bb is None else to_dev_bf16(bb))
@@ -556,7 +561,7 @@ def test_wide_tile_staged_epilogue_ragged(Q, w8):
                            O.QuantResult(qw, sw_h, 8 if w8 else 4, "row", None))
     big = torch.zeros((M, N + 16), dtype=torch.bfloat16, device="cuda")
     out = big[:, :N]
-    a, w, sa, sw = to_dev(qa), to_dev(qw if w8 else O.pack_int4(qw)), to_dev(sa_h), to_dev(sw_h)
+    a, w, sa, sw = to_dev(qa), to_dev(qw if w8 else pair_w4(O.pack_int4(qw))), to_dev(sa_h), to_dev(sw_h)
     if w8:
         Q.qgemm_w8a8(a, sa, w, sw, epilogue="bf16", out=out)
     else:
@@ -598,7 +603,7 @@ def _lowrank_same_codes(Q, M, F, K, rank, mode, epi, seed, a_layout="i8"):
     qa = O.quantize_activations(xb, 4, mode)
     qw = O.quantize_weights(wb, 4, mode)
     a, sa = _upload_quant(qa, a_layout == "packed")
-    w, sw = _upload_quant(qw, True)
+    w, sw = _upload_quant(qw, True, weight=True)
     lrb = _rand_bf16(seed + 2, (M, max(rank, 16)), 0.5)[:, :rank]
     l2b = _rand_bf16(seed + 3, (max(rank, 16), N), 0.05)[:rank]
     lr = to_dev_bf16(np.ascontiguousarray(lrb)) if rank else None
@@ -647,7 +652,7 @@ def test_group64_lowrank_with_device_lr(Q):
     qa = O.quantize_activations(xb, 4, "group64")
     qw = O.quantize_weights(wb, 4, "group64")
     a, sa = _upload_quant(qa, False)
-    w, sw = _upload_quant(qw, True)
+    w, sw = _upload_quant(qw, True, weight=True)
     _, _, lr = Q.rotate_quantize_act(to_dev_bf16(xb), bits=4, scale_mode="group64", l1=to_dev_bf16(l1))
     for epi in ("swiglu", "bf16"):
         out = Q.qgemm_w4a4_lowrank(a, sa, w, sw, K, lr=lr, l2=to_dev_l2(l2), epilogue=epi)
@@ -708,8 +713,10 @@ def _e2e(Q, wl, rows=None, wrows=None):
     # codes and scales, activations and weights (tensor units need every row)
     ga = a_codes.cpu().numpy()[rsel]
     gsa = sa.cpu().numpy()
-    wsel = wq[torch.as_tensor(nsel, device=wq.device)].cpu().numpy()
-    gw = O.unpack_int4(wsel) if wl.w_bits == 4 else wsel
+    if wl.w_bits == 4:
+        gw = O.unpack_int4(unpair_w4(wq.cpu().numpy())[nsel])
+    else:
+        gw = wq[torch.as_tensor(nsel, device=wq.device)].cpu().numpy()
     gsw = sw.cpu().numpy()
     if mode == "tensor":
         sta = _check_prologue(ga, gsa, wl.x, wl.a_bits, mode, rows=rsel)
@@ -917,7 +924,7 @@ def test_sigmoid_epilogue_same_codes(Q, bits):
     sa = to_dev(np.asarray(qa.scales, np.float32))
     sw = to_dev(np.asarray(qw.scales, np.float32))
     if bits == 4:
-        out = Q.qgemm_w4a4(a, sa, to_dev(O.pack_int4(qw.codes)), sw, K, epilogue="sigmoid")
+        out = Q.qgemm_w4a4(a, sa, to_dev(pair_w4(O.pack_int4(qw.codes))), sw, K, epilogue="sigmoid")
     else:
         out = Q.qgemm_w8a8(a, sa, to_dev(qw.codes), sw, epilogue="sigmoid")
     torch.cuda.synchronize()

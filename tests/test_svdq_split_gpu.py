@@ -15,7 +15,7 @@ import pytest
 import oracle as O
 import workloads as W
 from tests import parity_checks as P
-from tests.helpers import bf16_bits, ensure_built, to_dev, to_dev_bf16
+from tests.helpers import bf16_bits, ensure_built, to_dev, to_dev_bf16, unpair_w4
 
 pytestmark = pytest.mark.gpu
 
@@ -40,6 +40,7 @@ def _run(Q, wb, omega, rank, over, pi, ri, mode, rms=None):
     torch.cuda.synchronize()
     g = {k: (bf16_bits(v) if v.dtype == torch.bfloat16 else v.cpu().numpy()) for k, v in out.items()}
     g["l2"] = np.ascontiguousarray(g["l2"].T)  # the library stores L2 transposed, [N, rank]
+    g["packed"] = unpair_w4(g["packed"])  # and packed weights in paired-row order
     return g
 
 
@@ -174,7 +175,7 @@ def test_split_full_size_gateup(Q):
     rows = np.unique(np.concatenate([np.arange(4), N - 1 - np.arange(4),
                                      np.random.default_rng(5).choice(N, 24, replace=False)]))
     ri = torch.as_tensor(rows, device="cuda")
-    codes = O.unpack_int4(out["packed"][ri].cpu().numpy())
+    codes = O.unpack_int4(unpair_w4(out["packed"].cpu().numpy())[rows])
     _check_split_quant(codes, out["scales"][ri].cpu().numpy(), np.ascontiguousarray(wb[rows]), bf16_bits(out["l1"]),
                        np.ascontiguousarray(bf16_bits(out["l2"])[rows].T), "group64")
     # the objective is a few percent of the weight
