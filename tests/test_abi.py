@@ -290,6 +290,24 @@ def test_qgemm_w4a4_fp6_validation(L):
         assert g6(L, epi=epi) in (-4, -6)
 
 
+def test_pack_weight_int4_validation(L):
+    """Packed INT4 weights are stored in row pairs (rows 2p, 2p + 1 per
+    128-channel slice), so an odd row count is a shape error."""
+    def pw(**kw):
+        a = dict(w=ALIGNED, N=16, K=256, ldw=256, mode=1, rot=1, out=ALIGNED, sc=ALIGNED)
+        a.update(kw)
+        return L.pack_weight_int4(a["w"], a["N"], a["K"], a["ldw"], a["mode"], a["rot"], a["out"], a["sc"], None)
+
+    assert pw(N=15) == -2
+    assert pw(N=0) == -2
+    assert pw(mode=3) == -4
+    assert pw(K=320, ldw=320) == -2
+    assert pw(out=NULL) == -1
+    assert pw(w=MISALIGNED) == -3
+    assert pw(N=2) in (-4, -6)                    # one row pair reaches the device check
+    assert pw() in (-4, -6)
+
+
 def test_pack_weight_fp6_validation(L):
     def pw(**kw):
         a = dict(w=ALIGNED, N=16, K=256, ldw=256, mode=1, rot=1, out=ALIGNED, sc=ALIGNED)
