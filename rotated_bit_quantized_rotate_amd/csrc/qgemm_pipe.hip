@@ -50,8 +50,8 @@
 //    same outputs;
 //  * workgroup ids are remapped so the tiles one XCD runs form a compact
 //    block of the tile grid (shared A / W panels hit that XCD's L2);
-//  * int8 activations with tensor / row scales on 256 x 320 tiles (the
-//    attention projections and the W8A8 ff.down) run a ping-pong K loop:
+//  * int8 activations with tensor / row scales (plain epilogues: the
+//    attention projections, the W8A8 ff.down) run a ping-pong K loop:
 //    the two waves of each SIMD alternate, one phase apart, between reading
 //    fragments from LDS (and issuing global -> LDS loads) and a cluster of
 //    40 MFMAs from registers, so one of them always feeds the matrix pipe
@@ -1557,10 +1557,10 @@ int launch_qgemm(const GemmArgs& g, hipStream_t s) {
                : launch_plain<Cfg<256, 256, 2, 4, true, true>>(p, g.epilogue, s);
     else
       e = wide ? launch_plain<Cfg<256, 320, 2, 4, false, true, false, false, 0, 3, 1, true>>(p, g.epilogue, s)
-               : launch_plain<Cfg<256, 256, 2, 4, false, true>>(p, g.epilogue, s);
+               : launch_plain<Cfg<256, 256, 2, 4, false, true, false, false, 0, 3, 1, true>>(p, g.epilogue, s);
   } else {
     e = wide ? launch_plain<Cfg<256, 320, 2, 4, false, false, false, false, 0, 3, 1, true>>(p, g.epilogue, s)
-             : launch_plain<Cfg<256, 256, 2, 4, false, false>>(p, g.epilogue, s);
+             : launch_plain<Cfg<256, 256, 2, 4, false, false, false, false, 0, 3, 1, true>>(p, g.epilogue, s);
   }
   return e == hipSuccess ? OK : ERR_LAUNCH;
 }
