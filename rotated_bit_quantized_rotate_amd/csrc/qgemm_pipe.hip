@@ -54,7 +54,8 @@
 //    attention projections, the W8A8 ff.down) run a ping-pong K loop:
 //    the two waves of each SIMD alternate, one phase apart, between reading
 //    fragments from LDS (and issuing global -> LDS loads) and a cluster of
-//    40 MFMAs from registers, so one of them always feeds the matrix pipe
+//    MFMAs from registers (40 on a 256 x 320 tile), so one of them always
+//    feeds the matrix pipe
 //    (measured on gfx950: -3 to -5 % at 4096 x 5120 x 5120, -8 % at K =
 //    20480; the same loop with packed activations gains nothing).
 
@@ -1558,6 +1559,10 @@ int launch_qgemm(const GemmArgs& g, hipStream_t s) {
     else
       e = wide ? launch_plain<Cfg<256, 320, 2, 4, false, true, false, false, 0, 3, 1, true>>(p, g.epilogue, s)
                : launch_plain<Cfg<256, 256, 2, 4, false, true, false, false, 0, 3, 1, true>>(p, g.epilogue, s);
+  } else if (cost(192) < (wide ? cost(320) : cost(256))) {
+    // int8 W, N = 1536 at M = 16384: 512 tiles of 256 x 192 fill two waves
+    // exactly where 384 tiles of 256 x 256 leave half the second one idle
+    e = launch_plain<Cfg<256, 192, 2, 4, false, false, false, false, 0, 3, 1, true>>(p, g.epilogue, s);
   } else {
     e = wide ? launch_plain<Cfg<256, 320, 2, 4, false, false, false, false, 0, 3, 1, true>>(p, g.epilogue, s)
              : launch_plain<Cfg<256, 256, 2, 4, false, false, false, false, 0, 3, 1, true>>(p, g.epilogue, s);

@@ -541,15 +541,16 @@ def _sample_rows(M, n=48):
     return np.unique(np.concatenate([np.arange(8), M - 1 - np.arange(8), rng.choice(M, n, replace=False)]))
 
 
-@pytest.mark.parametrize("w8", [False, True])
-def test_wide_tile_staged_epilogue_ragged(Q, w8):
-    """The 256 x 320 tiles (chosen once a shape needs more than 256 tiles of
-    256 x 256) with ragged M and N, a strided output (ldo > N) and the
-    LDS-staged bf16 and gated-residual epilogues, against the oracle's
-    dequantized product on sampled rows."""
+@pytest.mark.parametrize("w8,N", [(False, 5104), (True, 5104), (True, 1520)])
+def test_wide_tile_staged_epilogue_ragged(Q, w8, N):
+    """The 256 x 320 tiles (N = 5104: chosen once a shape needs more than 256
+    tiles of 256 x 256) and the int8-weight 256 x 192 tiles (N = 1520: 8 tile
+    columns, the last 176 wide) with ragged M and N, a strided output (ldo >
+    N) and the LDS-staged bf16 and gated-residual epilogues, against the
+    oracle's dequantized product on sampled rows."""
     import torch
 
-    M, N, K = 4059, 5104, 512
+    M, K = 4059, 512
     rng = np.random.default_rng(21)
     qmax = 127 if w8 else 7
     qa = rng.integers(-qmax, qmax + 1, size=(M, K)).astype(np.int8)
