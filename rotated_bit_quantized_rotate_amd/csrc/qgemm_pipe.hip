@@ -174,8 +174,11 @@ struct PArgs {
 // so 4-bit operand rows are 128 contiguous bytes a stage -- whole cache
 // lines, half the line requests per channel of 64-byte rows (the loads'
 // cost follows the number of lines they touch) and half the barriers.
+// M32 (FP6 with group-64 scales): the 32x32x64 FP6 instruction, whose 64
+// channels are exactly one scale group, so each instruction's fp32 result is
+// one group's exact partial for a 32 x 32 block (16 per lane).
 template <int BM_, int BN_, int WGM_, int WGN_, bool AP_, bool WP_, bool GROUP_ = false, bool F6_ = false,
-          int MX_ = 0, int MAXS_ = 3, int SUB_ = 1, bool PP_ = false>
+          int MX_ = 0, int MAXS_ = 3, int SUB_ = 1, bool PP_ = false, bool M32_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int WGM = WGM_, WGN = WGN_;   // wave grid
@@ -185,6 +188,7 @@ struct Cfg {
   static constexpr int MX = MX_;
   static constexpr int SUB = SUB_;         // 128-channel sub-stages per LDS stage
   static constexpr bool PP = PP_;          // ping-pong K loop (see pipe_tile)
+  static constexpr bool M32 = M32_;        // 32x32x64 FP6 instruction per scale group
   static constexpr int BKS = BK * SUB;     // channels per LDS stage
   static constexpr bool FMMA = F6 || MX != 0;   // float matrix instruction, fp32 accumulators
   static constexpr bool NOSC = GROUP || MX != 0;  // accumulators already carry both scales
@@ -193,6 +197,10 @@ struct Cfg {
   static constexpr int WN = BN / WGN;       // wave tile cols
   static constexpr int FI = WM / 16;
   static constexpr int FJ = WN / 16;
+  static constexpr int FI32 = WM / 32;      // M32: 32-row fragments of the wave tile
+  static constexpr int FJ32 = WN / 32;
+  static_assert(!M32_ || (F6_ && GROUP_ && WM % 32 == 0 && WN % 32 == 0 && WM / 32 == 4),
+                "M32: FP6 operands with group-64 scales, four 32-row fragments per wave");
   static constexpr int ARB = F6 ? BKS * 3 / 4 : (MX ? BKS * MX / 8 : (AP ? BKS / 2 : BKS));  // bytes per A row per stage
   static constexpr int WRB = F6 ? BKS * 3 / 4 : (MX ? BKS * MX / 8 : (WP ? BKS / 2 : BKS));
   static_assert(!F6 || (AP && WP), "FP6 operands: both sides");
@@ -386,8 +394,10 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
     if (pos < 2 * C::BM) {
       const int kk = pos / C::BM, rem = pos % C::BM;
       const int wv = rem / C::WM, u = rem % C::WM;
-      // u = 64 f + 4 l16 + q holds the scale of fragment 4 f + q, lane row l16
-      const int row = wv * C::WM + (4 * (u / 64) + u % 4) * 16 + (u % 64) / 4;
+      // u = 64 f + 4 l16 + q holds the scale of fragment 4 f + q, lane row l16;
+      // M32: u = 4 l32 + i holds the scale of 32-row fragment i, lane row l32
+      const int row = C::M32 ? wv * C::WM + 32 * (u % 4) + u / 4
+                             : wv * C::WM + (4 * (u / 64) + u % 4) * 16 + (u % 64) / 4;
       const int64_t gr = m0 + row > p.M - 1 ? p.M - 1 : m0 + row;
       e = gr * p.kg + kk;
     } else if (pos < 2 * (C::BM + C::BN)) {
@@ -433,13 +443,25 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   typedef typename AccOf<C::FMMA>::type acc_t;
   acc_t acc[C::GROUP ? 1 : C::FJ][C::GROUP ? 1 : C::FI];
   v4f yf[C::GROUP ? C::FJ : 1][C::GROUP ? C::FI : 1];
+  // M32: the sums in the 32x32 instruction's layout (lane: one activation
+  // row l32, weight rows 8 b + 4 (lane / 32) + t for register 4 b + t),
+  // moved into yf's 16x16 layout after the K loop
+  v16f y32[C::M32 ? C::FI32 : 1][C::M32 ? C::FJ32 : 1];
 #pragma unroll
   for (int j = 0; j < C::FJ; ++j)
 #pragma unroll
     for (int i = 0; i < C::FI; ++i) {
-      if (C::GROUP) yf[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
-      else acc[j][i] = acc_t{0, 0, 0, 0};
+      if (C::GROUP && !C::M32) yf[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
+      else if (!C::GROUP) acc[j][i] = acc_t{0, 0, 0, 0};
     }
+  if constexpr (C::M32) {
+#pragma unroll
+    for (int i = 0; i < C::FI32; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FJ32; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) y32[i][j][r] = 0.f;
+  }
 
   // lane-constant LDS offsets: fragment rows differ by multiples of 16, so
   // the swizzle term depends on l16 only.
@@ -484,6 +506,24 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   const int a6_lo = a_row * 96 + (swz6(a_row, 4 + (lg >> 1)) << 4) + 8 * (lg & 1);
   const int w6_hi = w_row * 96 + (swz6(w_row, lg) << 4);
   const int w6_lo = w_row * 96 + (swz6(w_row, 4 + (lg >> 1)) << 4) + 8 * (lg & 1);
+  // M32: lane supplies row l32 (+ 32 per fragment) and the 32-channel
+  // sub-block 2 kk + lane / 32 of group kk: 16 bytes at that chunk, 8 bytes
+  // in chunk 4 + kk (half lane / 32).  Rows + 32 keep the swizzle bit.
+  const int l32 = lane & 31, h32 = lane >> 5;
+  const int a32_row = wm * C::WM + l32, w32_row = wn * C::WN + l32;
+  int a32_hi[2], a32_lo[2], w32_hi[2], w32_lo[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    a32_hi[kk] = a32_row * 96 + (swz6(a32_row, 2 * kk + h32) << 4);
+    a32_lo[kk] = a32_row * 96 + (swz6(a32_row, 4 + kk) << 4) + 8 * h32;
+    w32_hi[kk] = w32_row * 96 + (swz6(w32_row, 2 * kk + h32) << 4);
+    w32_lo[kk] = w32_row * 96 + (swz6(w32_row, 4 + kk) << 4) + 8 * h32;
+  }
+  // M32 scales: the lane's four 32-row fragments' s_a as one b128 at
+  // position wm WM + 4 l32; its 16 weight rows' s_w as four b128 at tile
+  // rows wn WN + 32 j + 8 b + 4 (lane / 32)
+  const int sa32_off = (wm * C::WM + 4 * l32) * 4;
+  const int sw32_off = (2 * C::BM + wn * C::WN + 4 * h32) * 4;
   // MX: lane group lg supplies K-block lg of the sub-stage (32 elements)
   // and its scale.  FP4: the block is the 16 bytes of chunk 4 h + lg.  FP8:
   // the instruction takes 16 elements of each of two blocks per lane -- K
@@ -736,6 +776,70 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
 #pragma unroll
         for (int t = C::SUB * C::FI; t < NDMA; ++t) issue_one(nxt, kt + NS - 1, t);
       }
+    } else if constexpr (C::M32) {
+      // FP6 stage with group-64 scales on the 32x32x64 instruction: step
+      // s = FI32 kk + i multiplies 32-row A fragment i with the wave's
+      // 32-row W fragments over group kk (sub-blocks 2 kk and 2 kk + 1, one
+      // per lane half), giving that group's exact partial of a 32 x 32 block
+      // in fp32.  Its rescale y += part * (s_a * s_w) runs one step later,
+      // beside the next step's instructions, so it does not wait on them.
+      const uint8_t* As = cur;
+      const uint8_t* Ws = As + C::SA;
+      const uint8_t* Ss = Ws + C::SW;
+      auto frag6 = [&](const uint8_t* base, int hi, int lo) -> v8i {
+        const uint4 h = *reinterpret_cast<const uint4*>(base + hi);
+        const uint2 l = *reinterpret_cast<const uint2*>(base + lo);
+        return v8i{(int)h.x, (int)h.y, (int)h.z, (int)h.w, (int)l.x, (int)l.y, 0, 0};  // FP6 reads 6 dwords
+      };
+      v8i wf[2][C::FJ32];
+      v4f sa4[2];
+      v4f sw4[2][C::FJ32][4];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int j = 0; j < C::FJ32; ++j) wf[kk][j] = frag6(Ws + j * 32 * C::WRB, w32_hi[kk], w32_lo[kk]);
+        sa4[kk] = *reinterpret_cast<const v4f*>(Ss + sa32_off + kk * C::BM * 4);
+#pragma unroll
+        for (int j = 0; j < C::FJ32; ++j)
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            sw4[kk][j][b] = *reinterpret_cast<const v4f*>(Ss + sw32_off + (kk * C::BN + 32 * j + 8 * b) * 4);
+      }
+      constexpr int NSTEP = 2 * C::FI32;
+      v8i abuf[2];
+      abuf[0] = frag6(As, a32_hi[0], a32_lo[0]);
+      v16f part[2][C::FJ32];
+      auto rescale = [&](int st) {
+        const int kk = st / C::FI32, i = st % C::FI32;
+        const float s_i = sa4[kk][i];
+#pragma unroll
+        for (int j = 0; j < C::FJ32; ++j) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            y32[i][j][r] = __builtin_fmaf(part[st & 1][j][r], s_i * sw4[kk][j][r / 4][r % 4], y32[i][j][r]);
+        }
+      };
+#pragma unroll
+      for (int st = 0; st < NSTEP; ++st) {
+        const int kk = st / C::FI32;
+        if (st > 0 && (4 * st) % NSTEP < 4) stage_prio((4 * st) / NSTEP);
+        if (st + 1 < NSTEP)
+          abuf[(st + 1) & 1] = frag6(As + ((st + 1) % C::FI32) * 32 * C::ARB, a32_hi[(st + 1) / C::FI32],
+                                     a32_lo[(st + 1) / C::FI32]);
+        if (dma && st < NDMA) issue_one(nxt, kt + NS - 1, st);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < C::FJ32; ++j)
+          part[st & 1][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              wf[kk][j], abuf[st & 1], v16f{}, 2, 2, 0, 127, 0, 127);
+        if (st > 0) rescale(st - 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      rescale(NSTEP - 1);
+      if (dma) {
+#pragma unroll
+        for (int t = NSTEP; t < NDMA; ++t) issue_one(nxt, kt + NS - 1, t);
+      }
     } else if constexpr (C::F6) {
       // FP6 stage: one 16x16x128 instruction per fragment pair covers the
       // stage's 128 channels.  W fragments are read whole; A fragments
@@ -974,6 +1078,36 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   }
   }  // ping-pong / pipelined K loop
   stage_prio(3);  // back to the lowest priority for the epilogue
+
+  // M32: move the sums from the 32x32 instruction's layout into yf's 16x16
+  // layout through LDS (the ring is free once every wave is past the
+  // barrier): each wave owns a 64 x 32 fp32 block (pitch 36 floats) in sm0
+  // (waves 0-3) or sm1 (waves 4-7) and converts its 128 rows in two passes.
+  if constexpr (C::M32) {
+    constexpr int P = 36;
+    static_assert(C::NW == 8 && C::FJ32 == 1 && C::FJ == 2 && C::FI == 8, "M32 epilogue: 8 waves of 128 x 32");
+    static_assert(4 * 64 * P * 4 <= C::STAGE, "M32 blocks must fit one ring stage");
+    lds_barrier();
+    float* const blk = reinterpret_cast<float*>((wave < 4 ? sm0 : sm1) + (wave & 3) * (64 * P * 4));
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const v16f& y = y32[2 * pass + ii][0];
+          *reinterpret_cast<v4f*>(blk + (32 * ii + l32) * P + 8 * b + 4 * h32) =
+              v4f{y[4 * b], y[4 * b + 1], y[4 * b + 2], y[4 * b + 3]};
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int i16 = 0; i16 < 4; ++i16)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          yf[j][4 * pass + i16] = *reinterpret_cast<const v4f*>(blk + (16 * i16 + l16) * P + 16 * j + 4 * lg);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+  }
 
   if constexpr (DEFER) {
     if (KT > 0) {
@@ -1540,7 +1674,7 @@ int launch_qgemm(const GemmArgs& g, hipStream_t s) {
     // Group-64 FP6: 256 x 128 tiles, whose 24 KB A stage splits evenly over
     // the 8 waves' 1 KB loads (a 128-row FP6 stage would not).
     if (group && g.fp6) {
-      e = launch_lowrank<Cfg<256, 128, 2, 4, true, true, true, true>>(p, g.epilogue, s);
+      e = launch_lowrank<Cfg<256, 128, 2, 4, true, true, true, true, 0, 3, 1, false, true>>(p, g.epilogue, s);
     } else if (group) {
       // 256 x 128 tiles with 16 waves (64 x 32 wave tiles, under 128 VGPRs):
       // four waves per SIMD interleave the MFMA -> rescale chains
