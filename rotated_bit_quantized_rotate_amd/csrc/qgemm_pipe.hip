@@ -698,6 +698,29 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
     }
     if (gp == 0) __builtin_amdgcn_s_barrier();
   } else {
+  // M32 state carried across stages: the last step's partial is rescaled at
+  // the next stage's first step, beside its first instruction, with group
+  // 1's scales, which that stage reads only at its middle step.
+  v4f sa4[C::M32 ? 2 : 1];
+  v4f sw4[C::M32 ? 2 : 1][C::M32 ? C::FJ32 : 1][4];
+  v16f part[C::M32 ? 2 : 1][C::M32 ? C::FJ32 : 1];
+  if constexpr (C::M32) {
+#pragma unroll
+    for (int j = 0; j < C::FJ32; ++j) part[1][j] = v16f{};  // passes the first step's pin unused
+  }
+  auto rescale32 = [&](int st) {
+    if constexpr (C::M32) {
+      const int kk = st / C::FI32, i = st % C::FI32;
+      const float s_i = sa4[kk][i];
+#pragma unroll
+      for (int j = 0; j < C::FJ32; ++j) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          y32[i][j][r] = __builtin_fmaf(part[st & 1][j][r], s_i * sw4[kk][j][r / 4][r % 4], y32[i][j][r]);
+        asm volatile("" : "+v"(y32[i][j]));
+      }
+    }
+  };
   for (int kb = 0; kb < KT; kb += NS) {
 #pragma unroll
   for (int sc = 0; sc < NS; ++sc) {
@@ -782,7 +805,14 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
       // 32-row W fragments over group kk (sub-blocks 2 kk and 2 kk + 1, one
       // per lane half), giving that group's exact partial of a 32 x 32 block
       // in fp32.  Its rescale y += part * (s_a * s_w) runs one step later,
-      // beside the next step's instructions, so it does not wait on them.
+      // beside the next step's instruction, so it does not wait on it.
+      // Operands are read from LDS one step before their use (group kk's
+      // W fragments and scales in the step before its first instruction):
+      // the empty asm statements with a memory clobber keep each step's
+      // reads in that step, and those on the partials and sums keep each
+      // instruction and its rescale in their steps (otherwise the compiler hoists every
+      // read of the stage above the first instruction, which then waits for
+      // all of them, and sinks every rescale below the last instruction).
       const uint8_t* As = cur;
       const uint8_t* Ws = As + C::SA;
       const uint8_t* Ss = Ws + C::SW;
@@ -792,50 +822,45 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
         return v8i{(int)h.x, (int)h.y, (int)h.z, (int)h.w, (int)l.x, (int)l.y, 0, 0};  // FP6 reads 6 dwords
       };
       v8i wf[2][C::FJ32];
-      v4f sa4[2];
-      v4f sw4[2][C::FJ32][4];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      auto read_w = [&](int kk) {
 #pragma unroll
         for (int j = 0; j < C::FJ32; ++j) wf[kk][j] = frag6(Ws + j * 32 * C::WRB, w32_hi[kk], w32_lo[kk]);
+      };
+      auto read_s = [&](int kk) {
         sa4[kk] = *reinterpret_cast<const v4f*>(Ss + sa32_off + kk * C::BM * 4);
 #pragma unroll
         for (int j = 0; j < C::FJ32; ++j)
 #pragma unroll
           for (int b = 0; b < 4; ++b)
             sw4[kk][j][b] = *reinterpret_cast<const v4f*>(Ss + sw32_off + (kk * C::BN + 32 * j + 8 * b) * 4);
-      }
+      };
       constexpr int NSTEP = 2 * C::FI32;
       v8i abuf[2];
+      read_w(0);
       abuf[0] = frag6(As, a32_hi[0], a32_lo[0]);
-      v16f part[2][C::FJ32];
-      auto rescale = [&](int st) {
-        const int kk = st / C::FI32, i = st % C::FI32;
-        const float s_i = sa4[kk][i];
-#pragma unroll
-        for (int j = 0; j < C::FJ32; ++j) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            y32[i][j][r] = __builtin_fmaf(part[st & 1][j][r], s_i * sw4[kk][j][r / 4][r % 4], y32[i][j][r]);
-        }
-      };
 #pragma unroll
       for (int st = 0; st < NSTEP; ++st) {
         const int kk = st / C::FI32;
+        asm volatile("" ::: "memory");
         if (st > 0 && (4 * st) % NSTEP < 4) stage_prio((4 * st) / NSTEP);
         if (st + 1 < NSTEP)
           abuf[(st + 1) & 1] = frag6(As + ((st + 1) % C::FI32) * 32 * C::ARB, a32_hi[(st + 1) / C::FI32],
                                      a32_lo[(st + 1) / C::FI32]);
+        if (st == 0) read_s(0);
+        if (st == C::FI32 - 1) read_w(1);
+        if (st == C::FI32) read_s(1);
         if (dma && st < NDMA) issue_one(nxt, kt + NS - 1, st);
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < C::FJ32; ++j)
+        for (int j = 0; j < C::FJ32; ++j) {
           part[st & 1][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               wf[kk][j], abuf[st & 1], v16f{}, 2, 2, 0, 127, 0, 127);
-        if (st > 0) rescale(st - 1);
-        __builtin_amdgcn_sched_barrier(0);
+          // the previous step's partial passes through here too, so its
+          // rescale comes after this instruction and overlaps it
+          asm volatile("" : "+v"(part[st & 1][j]), "+v"(part[(st + 1) & 1][j]));
+        }
+        if (st > 0) rescale32(st - 1);
+        else if (kt > 0) rescale32(NSTEP - 1);  // the previous stage's last step
       }
-      rescale(NSTEP - 1);
       if (dma) {
 #pragma unroll
         for (int t = NSTEP; t < NDMA; ++t) issue_one(nxt, kt + NS - 1, t);
@@ -1075,6 +1100,9 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
       }
     }
   }
+  }
+  if constexpr (C::M32) {
+    if (KT > 0) rescale32(2 * C::FI32 - 1);  // the last stage's last step
   }
   }  // ping-pong / pipelined K loop
   stage_prio(3);  // back to the lowest priority for the epilogue
