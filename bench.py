@@ -616,11 +616,11 @@ def case_svdq(Q, W, dev, fp6=False):
     l1, l2 = _bf16_dev(wl.l1, dev), _bf16_dev(np.ascontiguousarray(wl.l2.T), dev)  # L2 transposed, [N, r]
     acols, wcols = (K // 4 * 3, K // 4 * 3) if fp6 else (K, K // 2)
     codes = torch.empty((M, acols), dtype=torch.uint8 if fp6 else torch.int8, device=dev)
-    sa = torch.empty((M, K // 64), dtype=torch.float32, device=dev)
+    sa = torch.empty((K // 64, M), dtype=torch.float32, device=dev).t()  # group-major group-64 scales
     lr = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
     out = torch.empty((M, N // 2), dtype=torch.bfloat16, device=dev)
     wq = torch.empty((N, wcols), dtype=torch.uint8, device=dev)
-    sw = torch.empty((N, K // 64), dtype=torch.float32, device=dev)
+    sw = torch.empty((K // 64, N), dtype=torch.float32, device=dev).t()
     layout = "fp6" if fp6 else "i8"
     pack = Q.pack_weight_fp6 if fp6 else Q.pack_weight_int4
     c = Case()

@@ -83,8 +83,11 @@ enum {
 enum {
   QL_SCALE_TENSOR = 0,  /* one scale for the whole matrix            -> [1]      */
   QL_SCALE_ROW = 1,     /* one per row (token / output channel)      -> [R]      */
-  QL_SCALE_GROUP64 = 2  /* one per row x aligned 64-channel group    -> [R, K/64] */
+  QL_SCALE_GROUP64 = 2  /* one per row x aligned 64-channel group    -> [K/64, R] */
 };
+/* GROUP64 scales are stored group-major: float g * R + r is the scale of row
+ * r over channels 64 g .. 64 g + 63, so the R scales of one group are
+ * contiguous and the GEMM fetches a K step's scales as whole cache lines. */
 
 /* ---- INT4 code layouts --------------------------------------------------
  * QL_LAYOUT_I8     : one code per int8 byte, [R, K] (int4 codes -7..7 kept in
@@ -161,7 +164,7 @@ int ql_device_supported(int device);
  *          only with bits == 4)
  *   rotate 1: rotate each 256-group by H/16 first; 0: quantize x as is
  *   codes  out: [M, K] int8, [M, K/2] packed or [M, 3K/4] FP6 bytes, dense rows
- *   scales out: float32 [1] | [M] | [M, K/64] (scale = absmax / qmax)
+ *   scales out: float32 [1] | [M] | [K/64, M] (scale = absmax / qmax)
  *   l1, rank, lr  optional SVDQuant down-projection: if l1 != NULL,
  *          lr[M, rank] (bf16, dense rows) = bf16(x[M,K] @ l1[K, rank]) with the
  *          UNROTATED x, l1 bf16 row-major; rank a multiple of 16, 16..128.
@@ -211,7 +214,7 @@ int rmsnorm_rotate_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t
  *   w      [N, K] bf16 (torch Linear layout: out x in), row stride ldw
  *   packed out: [N, K/2] bytes in the QL_LAYOUT_PACKED weight order (row
  *            pairs interleaved per 128-channel slice)
- *   scales out: float32 [1] | [N] | [N, K/64]                              */
+ *   scales out: float32 [1] | [N] | [K/64, N]                              */
 int pack_weight_int4(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
                      int scale_mode, int rotate, uint8_t* packed, float* scales,
                      void* stream);
@@ -260,10 +263,10 @@ int qgemm_w4a4(const void* a, const float* sa, int a_scale_mode, int a_layout,
  *   w   [N, 3K/4] weight codes in QL_LAYOUT_FP6 (pack_weight_fp6), dense rows
  *   sa, a_scale_mode, sw, w_scale_mode   TENSOR | ROW scales, as qgemm_w4a4,
  *       or GROUP64 on both sides (README "Krea-2-SVDQuant-ComfyUI": INT4 with
- *       group size 64); each instruction then runs once per 64-channel group
- *       with the other group's weight lanes zeroed, and its fp32 result, the
- *       group's exact partial, is rescaled as qgemm_w4a4_lowrank does, so the
- *       output again equals the INT8 path's bit for bit
+ *       group size 64); the 32x32x64 FP6 instruction then covers exactly one
+ *       64-channel group, and its fp32 result, the group's exact partial, is
+ *       rescaled as qgemm_w4a4_lowrank does, so the output again equals the
+ *       INT8 path's bit for bit
  *   bias, epilogue, out, ldo             as qgemm_w4a4 (BF16 | F32 | I32 |
  *       SIGMOID; GROUP64: BF16 | F32); QL_EPI_I32 returns the exact sum of
  *       code products
@@ -396,9 +399,9 @@ int qgemm_w4a4_lowrank(const void* a, const float* sa, int a_scale_mode, int a_l
  * an FP4 build on a GPU whose matrix units take it natively).  Both operands
  * hold the int4 codes in QL_LAYOUT_FP6 (a [M, 3K/4] from the prologues with
  * layout QL_LAYOUT_FP6, w [N, 3K/4] from pack_weight_fp6), with group-64
- * scales on both sides (sa [M, K/64], sw [N, K/64]).  Each FP6 instruction
- * runs once per 64-channel group with the other group's weight lanes zeroed;
- * its fp32 result is the group's exact partial and is rescaled exactly as
+ * scales on both sides (sa [K/64, M], sw [K/64, N]).  Each 32x32x64 FP6
+ * instruction covers exactly one 64-channel group; its fp32 result is the
+ * group's exact partial and is rescaled exactly as
  * the INT8 path does, so the output equals qgemm_w4a4_lowrank's with group-64
  * scales bit for bit.
  *   lr, l2, rank, bias, out, ldo   as qgemm_w4a4_lowrank
@@ -468,7 +471,7 @@ int qgemm_grouped(const void* a4, const float* sa4, const void* a8, const float*
  *   scale_mode QL_SCALE_TENSOR | QL_SCALE_ROW | QL_SCALE_GROUP64 (the residual's scales)
  *   l1 out: bf16 [K, rank]; l2 out: bf16 [N, rank], L2 transposed (the layout of the low-rank
  *            GEMM entry points); packed out: [N, K/2] (QL_LAYOUT_PACKED);
- *            scales out: float32 [1] | [N] | [N, K/64]; all 16-byte aligned
+ *            scales out: float32 [1] | [N] | [K/64, N]; all 16-byte aligned
  *   errors out: float32 [refine_iters + 1], err_t of every iteration
  *   best_iter out: int32 [1], the iteration returned
  *   sigma   NULL or out float32 [rank] (16-byte aligned): singular values of

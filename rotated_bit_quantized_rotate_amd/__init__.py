@@ -8,6 +8,7 @@ ABI declared in include/qlinear.h); this package is its thin Python binding
 from ._lib import (  # noqa: F401
     QLinearError,
     device_supported,
+    group64_scales,
     lib,
     pack_weight_fp6,
     pack_weight_int4,

@@ -156,6 +156,36 @@ def _scale_shape(R, K, mode):
     return {QL_SCALE_TENSOR: (1,), QL_SCALE_ROW: (R,), QL_SCALE_GROUP64: (R, K // 64)}[mode]
 
 
+def _new_scales(R, K, mode, device):
+    """Scales of R rows.  Group-64 scales live group-major ([K/64, R] in
+    memory, the library's layout) and are handed out as the transposed
+    [R, K/64] view, so element [r, g] is still row r's scale of group g."""
+    if mode == QL_SCALE_GROUP64:
+        return torch.empty((K // 64, R), dtype=torch.float32, device=device).t()
+    return torch.empty(_scale_shape(R, K, mode), dtype=torch.float32, device=device)
+
+
+def group64_scales(s):
+    """A [R, K/64] scale tensor in the library's group-major memory layout
+    (the transposed view of a contiguous [K/64, R] tensor); returns s itself
+    when it already is one."""
+    return s if _group_major(s) else s.t().contiguous().t()
+
+
+def _group_major(s):
+    return s.dim() == 2 and (s.numel() == 0 or s.t().is_contiguous())
+
+
+def _sptr(s, R, K, mode, name):
+    """Pointer to scales after checking that group-64 scales are the [R, K/64]
+    view of group-major memory."""
+    if s is not None and _mode(mode) == QL_SCALE_GROUP64:
+        if tuple(s.shape) != (R, K // 64) or not _group_major(s):
+            raise ValueError(f"{name}: group-64 scales must be a [{R}, {K // 64}] view of group-major memory "
+                             "(see group64_scales)")
+    return _ptr(s)
+
+
 # ---- entry points (same names as the C ABI) ---------------------------------
 
 def rotate_quantize_act(x, bits=4, scale_mode="row", layout="i8", rotate=True, codes=None, scales=None,
@@ -168,14 +198,15 @@ def rotate_quantize_act(x, bits=4, scale_mode="row", layout="i8", rotate=True, c
     if codes is None:
         codes = _codes(M, K, lay, x.device)
     if scales is None:
-        scales = torch.empty(_scale_shape(M, K, mode), dtype=torch.float32, device=x.device)
+        scales = _new_scales(M, K, mode, x.device)
     rank = 0
     if l1 is not None:
         rank = l1.shape[1]
         if lr is None:
             lr = torch.empty((M, rank), dtype=torch.bfloat16, device=x.device)
     st = lib().rotate_quantize_act(_ptr(x), M, K, x.stride(0), bits, mode, lay, int(bool(rotate)),
-                                   _ptr(codes), _ptr(scales), _ptr(l1), rank, _ptr(lr), _stream(stream))
+                                   _ptr(codes), _sptr(scales, M, K, mode, "scales"), _ptr(l1), rank, _ptr(lr),
+                                   _stream(stream))
     _check("rotate_quantize_act", st)
     return codes, scales, lr
 
@@ -195,10 +226,10 @@ def rmsnorm_rotate_quantize_act(x, gamma=None, mod_scale=None, mod_shift=None, e
     if codes is None:
         codes = _codes(M, K, lay, x.device)
     if scales is None:
-        scales = torch.empty(_scale_shape(M, K, mode), dtype=torch.float32, device=x.device)
+        scales = _new_scales(M, K, mode, x.device)
     st = lib().rmsnorm_rotate_quantize_act(_ptr(x), M, K, x.stride(0), _ptr(gamma), _ptr(mod_scale),
                                            _ptr(mod_shift), float(eps), bits, mode, lay, int(bool(rotate)),
-                                           _ptr(codes), _ptr(scales), _stream(stream))
+                                           _ptr(codes), _sptr(scales, M, K, mode, "scales"), _stream(stream))
     _check("rmsnorm_rotate_quantize_act", st)
     return codes, scales
 
@@ -211,9 +242,9 @@ def pack_weight_int4(w, scale_mode="row", rotate=True, packed=None, scales=None,
     if packed is None:
         packed = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
     if scales is None:
-        scales = torch.empty(_scale_shape(N, K, mode), dtype=torch.float32, device=w.device)
+        scales = _new_scales(N, K, mode, w.device)
     st = lib().pack_weight_int4(_ptr(w), N, K, w.stride(0), mode, int(bool(rotate)), _ptr(packed),
-                                _ptr(scales), _stream(stream))
+                                _sptr(scales, N, K, mode, "scales"), _stream(stream))
     _check("pack_weight_int4", st)
     return packed, scales
 
@@ -226,9 +257,9 @@ def pack_weight_fp6(w, scale_mode="row", rotate=True, packed=None, scales=None, 
     if packed is None:
         packed = _codes(N, K, QL_LAYOUT_FP6, w.device)
     if scales is None:
-        scales = torch.empty(_scale_shape(N, K, mode), dtype=torch.float32, device=w.device)
+        scales = _new_scales(N, K, mode, w.device)
     st = lib().pack_weight_fp6(_ptr(w), N, K, w.stride(0), mode, int(bool(rotate)), _ptr(packed),
-                               _ptr(scales), _stream(stream))
+                               _sptr(scales, N, K, mode, "scales"), _stream(stream))
     _check("pack_weight_fp6", st)
     return packed, scales
 
@@ -272,7 +303,8 @@ def qgemm_w4a4(a, sa, w, sw, K, a_scale_mode="row", w_scale_mode="row", a_layout
     N = w.shape[0]
     epi = _epi(epilogue)
     out = _out(out, M, N // 2 if epi == QL_EPI_SWIGLU else N, epi, a.device)
-    st = lib().qgemm_w4a4(_ptr(a), _ptr(sa), _mode(a_scale_mode), _lay(a_layout), _ptr(w), _ptr(sw),
+    st = lib().qgemm_w4a4(_ptr(a), _sptr(sa, M, K, a_scale_mode, "sa"), _mode(a_scale_mode), _lay(a_layout),
+                          _ptr(w), _sptr(sw, N, K, w_scale_mode, "sw"),
                           _mode(w_scale_mode), M, N, K, _ptr(bias), epi, _ptr(out), out.stride(0),
                           _stream(stream))
     _check("qgemm_w4a4", st)
@@ -287,7 +319,8 @@ def qgemm_w4a4_fp6(a, sa, w, sw, K, a_scale_mode="row", w_scale_mode="row", bias
     N = w.shape[0]
     epi = _epi(epilogue)
     out = _out(out, M, N, epi, a.device)
-    st = lib().qgemm_w4a4_fp6(_ptr(a), _ptr(sa), _mode(a_scale_mode), _ptr(w), _ptr(sw), _mode(w_scale_mode),
+    st = lib().qgemm_w4a4_fp6(_ptr(a), _sptr(sa, M, K, a_scale_mode, "sa"), _mode(a_scale_mode), _ptr(w),
+                              _sptr(sw, N, K, w_scale_mode, "sw"), _mode(w_scale_mode),
                               M, N, K, _ptr(bias), epi, _ptr(out), out.stride(0), _stream(stream))
     _check("qgemm_w4a4_fp6", st)
     return out
@@ -329,7 +362,8 @@ def qgemm_w8a8(a, sa, w, sw, a_scale_mode="row", w_scale_mode="row", bias=None, 
     N = w.shape[0]
     epi = _epi(epilogue)
     out = _out(out, M, N, epi, a.device)
-    st = lib().qgemm_w8a8(_ptr(a), _ptr(sa), _mode(a_scale_mode), _ptr(w), _ptr(sw), _mode(w_scale_mode),
+    st = lib().qgemm_w8a8(_ptr(a), _sptr(sa, M, K, a_scale_mode, "sa"), _mode(a_scale_mode), _ptr(w),
+                          _sptr(sw, N, K, w_scale_mode, "sw"), _mode(w_scale_mode),
                           M, N, K, _ptr(bias), _ptr(residual), _ptr(gate), epi, _ptr(out), out.stride(0),
                           _stream(stream))
     _check("qgemm_w8a8", st)
@@ -347,8 +381,8 @@ def qgemm_w4a4_lowrank(a, sa, w, sw, K, lr=None, l2=None, a_scale_mode="group64"
     epi = _epi(epilogue)
     rank = 0 if l2 is None else l2.shape[1]
     out = _out(out, M, N // 2 if epi == QL_EPI_SWIGLU else N, epi, a.device)
-    st = lib().qgemm_w4a4_lowrank(_ptr(a), _ptr(sa), _mode(a_scale_mode), _lay(a_layout), _ptr(w),
-                                  _ptr(sw), _mode(w_scale_mode), _ptr(lr), _ptr(l2), rank, M, N, K,
+    st = lib().qgemm_w4a4_lowrank(_ptr(a), _sptr(sa, M, K, a_scale_mode, "sa"), _mode(a_scale_mode),
+                                  _lay(a_layout), _ptr(w), _sptr(sw, N, K, w_scale_mode, "sw"), _mode(w_scale_mode), _ptr(lr), _ptr(l2), rank, M, N, K,
                                   _ptr(bias), epi, _ptr(out), out.stride(0), _stream(stream))
     _check("qgemm_w4a4_lowrank", st)
     return out
@@ -357,14 +391,16 @@ def qgemm_w4a4_lowrank(a, sa, w, sw, K, lr=None, l2=None, a_scale_mode="group64"
 def qgemm_w4a4_fp6_lowrank(a, sa, w, sw, K, lr=None, l2=None, bias=None, epilogue="swiglu", out=None,
                            stream=None):
     """The group-64 low-rank GEMM on the FP6 matrix instruction: a [M, 3K/4]
-    and w [N, 3K/4] in the FP6 layout, sa [M, K/64], sw [N, K/64]; same
+    and w [N, 3K/4] in the FP6 layout, sa [M, K/64], sw [N, K/64] (group-
+    major views, see group64_scales); same
     result as qgemm_w4a4_lowrank on the same codes."""
     M = a.shape[0]
     N = w.shape[0]
     epi = _epi(epilogue)
     rank = 0 if l2 is None else l2.shape[1]
     out = _out(out, M, N // 2 if epi == QL_EPI_SWIGLU else N, epi, a.device)
-    st = lib().qgemm_w4a4_fp6_lowrank(_ptr(a), _ptr(sa), _ptr(w), _ptr(sw), _ptr(lr), _ptr(l2), rank, M, N, K,
+    st = lib().qgemm_w4a4_fp6_lowrank(_ptr(a), _sptr(sa, M, K, "group64", "sa"), _ptr(w),
+                                      _sptr(sw, N, K, "group64", "sw"), _ptr(lr), _ptr(l2), rank, M, N, K,
                                       _ptr(bias), epi, _ptr(out), out.stride(0), _stream(stream))
     _check("qgemm_w4a4_fp6_lowrank", st)
     return out
@@ -420,13 +456,14 @@ def svdq_split(w, omega, rank, oversample=8, power_iters=2, refine_iters=0, scal
     out = {"l1": torch.empty((K, rank), dtype=torch.bfloat16, device=dev),
            "l2": torch.empty((N, rank), dtype=torch.bfloat16, device=dev),
            "packed": torch.empty((N, K // 2), dtype=torch.uint8, device=dev),
-           "scales": torch.empty(_scale_shape(N, K, mode), dtype=torch.float32, device=dev),
+           "scales": _new_scales(N, K, mode, dev),
            "errors": torch.empty(refine_iters + 1, dtype=torch.float32, device=dev),
            "best_iter": torch.empty(1, dtype=torch.int32, device=dev),
            "sigma": torch.empty(rank, dtype=torch.float32, device=dev)}
     st = lib().svdq_split(_ptr(w), N, K, w.stride(0), _ptr(act_rms), _ptr(omega), rank, oversample, power_iters,
                           refine_iters, mode, _ptr(out["l1"]), _ptr(out["l2"]), _ptr(out["packed"]),
-                          _ptr(out["scales"]), _ptr(out["errors"]), _ptr(out["best_iter"]), _ptr(out["sigma"]),
+                          _sptr(out["scales"], N, K, mode, "scales"), _ptr(out["errors"]), _ptr(out["best_iter"]),
+                          _ptr(out["sigma"]),
                           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("svdq_split", st)
     return out
@@ -453,13 +490,13 @@ def svdq_split_noalloc(w, omega, rank, oversample=8, power_iters=2, refine_iters
         out = {"l1": torch.empty((K, rank), dtype=torch.bfloat16, device=dev),
                "l2": torch.empty((N, rank), dtype=torch.bfloat16, device=dev),
                "packed": torch.empty((N, K // 2), dtype=torch.uint8, device=dev),
-               "scales": torch.empty(_scale_shape(N, K, mode), dtype=torch.float32, device=dev),
+               "scales": _new_scales(N, K, mode, dev),
                "errors": torch.empty(refine_iters + 1, dtype=torch.float32, device=dev),
                "best_iter": torch.empty(1, dtype=torch.int32, device=dev),
                "sigma": torch.empty(rank, dtype=torch.float32, device=dev)}
     st = lib().svdq_split_noalloc(_ptr(w), N, K, w.stride(0), _ptr(act_rms), _ptr(omega), rank, oversample,
                                   power_iters, refine_iters, mode, _ptr(out["l1"]), _ptr(out["l2"]),
-                                  _ptr(out["packed"]), _ptr(out["scales"]), _ptr(out["errors"]),
+                                  _ptr(out["packed"]), _sptr(out["scales"], N, K, mode, "scales"), _ptr(out["errors"]),
                                   _ptr(out["best_iter"]), _ptr(out["sigma"]), _stream(stream))
     _check("svdq_split_noalloc", st)
     return out

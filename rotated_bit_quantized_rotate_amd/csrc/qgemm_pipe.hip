@@ -149,6 +149,7 @@ struct PArgs {
   int64_t M, N, K;
   int sa_stride, sw_stride;  // tensor / row scales: 0 or 1
   int kg;                    // group-64 scales: K / 64 per row
+  uint32_t sa_gs, sw_gs;     // group-64 scales ([K/64, M], [K/64, N]): bytes per stage (two groups)
   const uint16_t* bias;
   const uint16_t* residual;
   const uint16_t* gate;
@@ -399,11 +400,11 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
       const int row = C::M32 ? wv * C::WM + 32 * (u % 4) + u / 4
                              : wv * C::WM + (4 * (u / 64) + u % 4) * 16 + (u % 64) / 4;
       const int64_t gr = m0 + row > p.M - 1 ? p.M - 1 : m0 + row;
-      e = gr * p.kg + kk;
+      e = kk * p.M + gr;  // scales are group-major: a stage's are contiguous per group
     } else if (pos < 2 * (C::BM + C::BN)) {
       const int pw = pos - 2 * C::BM;
       const int kk = pw / C::BN, trow = pw % C::BN;
-      e = w_row_of<C, SWIG>(p, n0, trow) * p.kg + kk;
+      e = kk * p.N + w_row_of<C, SWIG>(p, n0, trow);
     }  // padding slots load the first W scale, never read back
     s_vo[ts] = (uint32_t)(e * 4);
   }
@@ -432,7 +433,8 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
     } else if (C::GROUP) {
       const int ts = t - C::A_PER_WAVE - C::W_HI;
       const int si = wave + C::NW * ts;
-      dma_b32(si * 64 < 2 * C::BM ? p.sa : p.sw, s_vo[C::SCL ? ts : 0] + (uint32_t)(kt * 8),
+      const bool sa_side = si * 64 < 2 * C::BM;
+      dma_b32(sa_side ? p.sa : p.sw, s_vo[C::SCL ? ts : 0] + (uint32_t)kt * (sa_side ? p.sa_gs : p.sw_gs),
               st + C::SA + C::SW + si * 256);
     }
   };
@@ -1654,6 +1656,8 @@ int launch_qgemm(const GemmArgs& g, hipStream_t s) {
   p.sa_stride = g.a_mode == 1 ? 1 : 0;
   p.sw_stride = g.w_mode == 1 ? 1 : 0;
   p.kg = (int)(g.K >> 6);
+  p.sa_gs = (uint32_t)(8 * g.M);
+  p.sw_gs = (uint32_t)(8 * g.N);
   p.bias = g.bias;
   p.residual = g.residual;
   p.gate = g.gate;

@@ -345,7 +345,7 @@ __global__ __launch_bounds__(kThreads) void rq_kernel(RqArgs a, int slots_per_ro
       store_codes(a.codes, code_row + (int64_t)g * 256 + t * 16, a.packed, u, a.paired ? a.K : 0);
       if (a.mode == 2) {
         if ((t & 3) == 0)
-          a.scales[row * (a.K >> 6) + g * 4 + (t >> 2)] = __fdiv_rn(am, qmax) * post;
+          a.scales[(int64_t)(g * 4 + (t >> 2)) * a.M + row] = __fdiv_rn(am, qmax) * post;  // [K/64, M]
       } else if (a.mode == 1 && t == 0 && sir == 0 && j == 0) {
         a.scales[row] = __fdiv_rn(am, qmax) * post;
       }

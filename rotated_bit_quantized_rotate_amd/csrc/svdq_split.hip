@@ -404,7 +404,7 @@ __global__ __launch_bounds__(kSplitThreads) void deq_target_kernel(
       // packed weight order: rows 2p, 2p + 1 interleaved per 128-channel slice
       const uint2 pk = *reinterpret_cast<const uint2*>(codes + (row >> 1) * K + ((c0 >> 7) << 7) + ((row & 1) << 6) +
                                                        ((c0 & 127) >> 1));
-      const float sc = mode == 0 ? scales[0] : (mode == 1 ? scales[row] : scales[row * (K >> 6) + (c0 >> 6)]);
+      const float sc = mode == 0 ? scales[0] : (mode == 1 ? scales[row] : scales[(c0 >> 6) * N + row]);
       const uint32_t wds[2] = {pk.x, pk.y};
 #pragma unroll
       for (int h = 0; h < 2; ++h)

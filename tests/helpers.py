@@ -69,6 +69,16 @@ def to_dev(a, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
+def to_dev_scales(s, device="cuda"):
+    """Scales on the device in the library's layout: tensor / row scales as
+    they are; group-64 scales [R, K/64] as the transposed view of group-major
+    memory ([K/64, R] contiguous)."""
+    s = np.asarray(s, np.float32)
+    if s.ndim == 2:
+        return to_dev(s.T, device).t()
+    return to_dev(s, device)
+
+
 def rel_fro(a, b):
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)

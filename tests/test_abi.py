@@ -480,3 +480,31 @@ def test_device_supported_without_gpu_is_false(L):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert L.ql_device_supported(0) == 0
+
+
+def test_group64_scales_are_group_major_views():
+    """The binding hands out and accepts group-64 scales as [R, K/64] views of
+    group-major memory ([K/64, R] contiguous: the layout the kernels read);
+    other layouts are refused before any call."""
+    import torch
+
+    from rotated_bit_quantized_rotate_amd import _lib as B
+
+    R, K = 6, 512
+    s = B._new_scales(R, K, B.QL_SCALE_GROUP64, "cpu")
+    assert tuple(s.shape) == (R, K // 64) and s.stride() == (1, R)
+    assert B._sptr(s, R, K, "group64", "s").value == s.data_ptr()
+    plain = torch.arange(R * (K // 64), dtype=torch.float32).reshape(R, K // 64)
+    with pytest.raises(ValueError):
+        B._sptr(plain, R, K, "group64", "s")          # row-major [R, K/64]
+    with pytest.raises(ValueError):
+        B._sptr(s[:, :4], R, K, "group64", "s")       # wrong shape
+    g = B.group64_scales(plain)
+    assert torch.equal(g, plain) and g.stride() == (1, R)
+    # memory order: element (r, grp) at grp * R + r
+    flat = g.t().contiguous().reshape(-1)
+    assert float(flat[3 * R + 2]) == float(plain[2, 3])
+    assert B.group64_scales(g) is g
+    # tensor / row scales pass unchanged; empty group-64 scales are accepted
+    assert B._sptr(torch.ones(R), R, K, "row", "s") is not None
+    assert B._sptr(torch.empty((0, K // 64)), 0, K, "group64", "s") is not None

@@ -22,7 +22,7 @@ import pytest
 import oracle as O
 import workloads as W
 from tests import parity_checks as P
-from tests.helpers import bf16_bits, ensure_built, pair_w4, to_dev, to_dev_bf16, to_dev_l2, unpair_w4
+from tests.helpers import bf16_bits, ensure_built, pair_w4, to_dev, to_dev_bf16, to_dev_l2, to_dev_scales, unpair_w4
 
 pytestmark = pytest.mark.gpu
 
@@ -183,7 +183,7 @@ def test_fp6_epilogues_equal_int4_path(Q, M, N, K, mode):
     import torch
 
     qa, qw, sa_h, sw_h = _same_codes_pair(M, N, K, M + N, mode)
-    sa, sw = to_dev(sa_h), to_dev(sw_h)
+    sa, sw = to_dev_scales(sa_h), to_dev_scales(sw_h)
     a8, w4 = to_dev(qa), to_dev(pair_w4(O.pack_int4(qw)))
     a6, w6 = to_dev(O.pack_fp6(qa)), to_dev(O.pack_fp6(qw))
     bias = to_dev_bf16(_rand_bf16(M, (N,), 0.1))
@@ -212,7 +212,7 @@ def test_fp6_strided_output_and_empty(Q):
 
     M, N, K = 4059, 5104, 512
     qa, qw, sa_h, sw_h = _same_codes_pair(M, N, K, 77, "row")
-    sa, sw = to_dev(sa_h), to_dev(sw_h)
+    sa, sw = to_dev_scales(sa_h), to_dev_scales(sw_h)
     a6, w6 = to_dev(O.pack_fp6(qa)), to_dev(O.pack_fp6(qw))
     big = torch.zeros((M, N + 16), dtype=torch.bfloat16, device="cuda")
     out = Q.qgemm_w4a4_fp6(a6, sa, w6, sw, K, out=big[:, :N])
@@ -274,7 +274,7 @@ def test_fp6_group64_equals_int4_path(Q, M, N, K):
     import torch
 
     qa, qw, sa_h, sw_h = _group_pair(M, N, K, M + 3 * N + K)
-    sa, sw = to_dev(sa_h), to_dev(sw_h)
+    sa, sw = to_dev_scales(sa_h), to_dev_scales(sw_h)
     a8, w4 = to_dev(qa), to_dev(pair_w4(O.pack_int4(qw)))
     a6, w6 = to_dev(O.pack_fp6(qa)), to_dev(O.pack_fp6(qw))
     bias = to_dev_bf16(_rand_bf16(N, (N,), 0.1))
@@ -312,7 +312,7 @@ def test_fp6_group64_lowrank_equals_int4_path(Q, rank, epi):
 
     M, N, K = 300, 640, 1024
     qa, qw, sa_h, sw_h = _group_pair(M, N, K, 5 + rank)
-    sa, sw = to_dev(sa_h), to_dev(sw_h)
+    sa, sw = to_dev_scales(sa_h), to_dev_scales(sw_h)
     lr = to_dev_bf16(_rand_bf16(6, (M, rank), 0.5)) if rank else None
     l2 = to_dev_l2(_rand_bf16(7, (rank, N), 0.05)) if rank else None
     ref = Q.qgemm_w4a4_lowrank(to_dev(qa), sa, to_dev(pair_w4(O.pack_int4(qw))), sw, K, lr=lr, l2=l2, epilogue=epi)
@@ -338,14 +338,14 @@ def test_fp6_group64_rejections(Q):
     qa, qw, sa_h, sw_h = _group_pair(M, N, K, 1)
     a6, w6 = to_dev(O.pack_fp6(qa)), to_dev(O.pack_fp6(qw))
     with pytest.raises(Q.QLinearError):   # group sums are rescaled: no exact I32 result
-        Q.qgemm_w4a4_fp6(a6, to_dev(sa_h), w6, to_dev(sw_h), K, a_scale_mode="group64",
+        Q.qgemm_w4a4_fp6(a6, to_dev_scales(sa_h), w6, to_dev_scales(sw_h), K, a_scale_mode="group64",
                          w_scale_mode="group64", epilogue="i32")
     row_a = torch.ones(M, dtype=torch.float32, device="cuda")
     row_w = torch.ones(N, dtype=torch.float32, device="cuda")
     with pytest.raises(Q.QLinearError):   # the INT4 low-rank GEMM takes no FP6 operands
-        Q.qgemm_w4a4_lowrank(a6, to_dev(sa_h), w6, to_dev(sw_h), K, a_layout="fp6", epilogue="bf16")
+        Q.qgemm_w4a4_lowrank(a6, to_dev_scales(sa_h), w6, to_dev_scales(sw_h), K, a_layout="fp6", epilogue="bf16")
     with pytest.raises(Q.QLinearError):   # the FP6 low-rank GEMM has no I32 or sigmoid epilogue
-        Q.qgemm_w4a4_fp6_lowrank(a6, to_dev(sa_h), w6, to_dev(sw_h), K, epilogue="sigmoid")
+        Q.qgemm_w4a4_fp6_lowrank(a6, to_dev_scales(sa_h), w6, to_dev_scales(sw_h), K, epilogue="sigmoid")
     del row_a, row_w
 
 

@@ -25,7 +25,7 @@ import pytest
 import oracle as O
 import workloads as W
 from tests import parity_checks as P
-from tests.helpers import (bf16_bits, bf16_ulp_diff, ensure_built, pair_w4, rel_fro, to_dev, to_dev_bf16,
+from tests.helpers import (bf16_bits, bf16_ulp_diff, ensure_built, pair_w4, rel_fro, to_dev, to_dev_bf16, to_dev_scales,
                            to_dev_l2, unpair_w4)
 
 pytestmark = pytest.mark.gpu
@@ -431,8 +431,8 @@ def test_group64_unit_scales_exact(Q):
     rng = np.random.default_rng(9)
     qa = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
     qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
-    sa = torch.ones((M, K // 64), dtype=torch.float32, device="cuda")
-    sw = torch.ones((N, K // 64), dtype=torch.float32, device="cuda")
+    sa = Q.group64_scales(torch.ones((M, K // 64), dtype=torch.float32, device="cuda"))
+    sw = Q.group64_scales(torch.ones((N, K // 64), dtype=torch.float32, device="cuda"))
     out = Q.qgemm_w4a4_lowrank(to_dev(qa), sa, to_dev(pair_w4(O.pack_int4(qw))), sw, K, epilogue="f32")
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().astype(np.float64), O.int_gemm(qa, qw).astype(np.float64))
@@ -454,7 +454,7 @@ def test_group64_pow2_scales_exact(Q, a_layout):
     sa_h = np.ldexp(1.0, -rng.integers(0, 4, size=(M, K // 64))).astype(np.float32)
     sw_h = np.ldexp(1.0, -rng.integers(0, 4, size=(N, K // 64))).astype(np.float32)
     a = to_dev(O.pack_int4(qa) if a_layout == "packed" else qa)
-    out = Q.qgemm_w4a4_lowrank(a, to_dev(sa_h), to_dev(pair_w4(O.pack_int4(qw))), to_dev(sw_h), K,
+    out = Q.qgemm_w4a4_lowrank(a, to_dev_scales(sa_h), to_dev(pair_w4(O.pack_int4(qw))), to_dev_scales(sw_h), K,
                                a_layout=a_layout, epilogue="f32")
     torch.cuda.synchronize()
     ref_a = O.QuantResult(qa, sa_h, 4, "group64", None)
@@ -477,7 +477,7 @@ def _upload_quant(ref, packed, weight=False):
     codes = O.pack_int4(ref.codes) if packed else ref.codes
     if packed and weight:
         codes = pair_w4(codes)
-    return to_dev(codes), to_dev(np.ascontiguousarray(ref.scales))
+    return to_dev(codes), to_dev_scales(ref.scales)
 
 
 @pytest.mark.parametrize("mode", ["row", "tensor"])
@@ -562,7 +562,7 @@ def test_wide_tile_staged_epilogue_ragged(Q, w8, N):
                            O.QuantResult(qw, sw_h, 8 if w8 else 4, "row", None))
     big = torch.zeros((M, N + 16), dtype=torch.bfloat16, device="cuda")
     out = big[:, :N]
-    a, w, sa, sw = to_dev(qa), to_dev(qw if w8 else pair_w4(O.pack_int4(qw))), to_dev(sa_h), to_dev(sw_h)
+    a, w, sa, sw = to_dev(qa), to_dev(qw if w8 else pair_w4(O.pack_int4(qw))), to_dev_scales(sa_h), to_dev_scales(sw_h)
     if w8:
         Q.qgemm_w8a8(a, sa, w, sw, epilogue="bf16", out=out)
     else:
@@ -825,7 +825,7 @@ def test_gemm_empty_inputs(Q):
     w8 = torch.zeros((N, K), dtype=torch.int8, device=d)
     w6 = torch.zeros((N, K // 4 * 3), dtype=torch.uint8, device=d)
     sw = torch.ones(N, dtype=torch.float32, device=d)
-    swg = torch.ones((N, K // 64), dtype=torch.float32, device=d)
+    swg = Q.group64_scales(torch.ones((N, K // 64), dtype=torch.float32, device=d))
     a8 = torch.empty((0, K), dtype=torch.int8, device=d)
     sa = torch.empty((0,), dtype=torch.float32, device=d)
     outs = [
@@ -922,8 +922,8 @@ def test_sigmoid_epilogue_same_codes(Q, bits):
     qa = O.quantize_activations(xb, bits, "row", True)
     qw = O.quantize_weights(wb, bits, "row", True)
     a = to_dev(qa.codes)
-    sa = to_dev(np.asarray(qa.scales, np.float32))
-    sw = to_dev(np.asarray(qw.scales, np.float32))
+    sa = to_dev_scales(qa.scales)
+    sw = to_dev_scales(qw.scales)
     if bits == 4:
         out = Q.qgemm_w4a4(a, sa, to_dev(pair_w4(O.pack_int4(qw.codes))), sw, K, epilogue="sigmoid")
     else:
