@@ -36,10 +36,14 @@ quantization, int4 packing) is offline and timed separately.
 Prints ONE JSON line.  `value` is the effective integer throughput of a whole
 step, 2*M*N*K / step time, in TOP/s (eager launches, K steps between two
 synchronizations, with one HIP event before and one after).  `roofline`
-describes the GEMM kernel (the dominant kernel): its time per step is that
-step time minus the time of the step's prologues run alone K times (events
-only at the ends, on the stream the kernels run on).  A second run of the K
-steps with a HIP event after every launch gives the per-kernel breakdown
+describes the GEMM kernel (the dominant kernel): its time is the median of 5
+repeats of back-to-back GEMM launches on codes already in HBM (HIP events on
+the launch stream); the step minus the prologues run alone is reported beside
+it.  The group-64 layers are bound by their per-group fp32 rescale, so their
+roofline is the VALU's (`bound` "alu": algorithmic rescale instructions
+against the fp32 issue rate), with the int8-MFMA fraction kept beside it.  A
+second run of the K steps with a HIP event after every launch gives the
+per-kernel breakdown
 reported beside it (`*_with_kernel_events`); those events add a gap of a
 few microseconds at each kernel boundary.  `cpu_baseline`
 times the CPU oracle on a bounded sample of the same workload.
@@ -76,6 +80,10 @@ FP6_MFMA_PEAK_TOPS = 10100.0     # MI355X dense FP6 / FP4 MFMA, 10.1 PFLOP/s
 FP4_MFMA_PEAK_TOPS = 10100.0
 FP8_MFMA_PEAK_TOPS = 5000.0      # MI355X dense FP8 MFMA, 5.0 PFLOP/s
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector FMA: 256 CUs x 128 lanes x 2 x 2.4 GHz
+# fp32 VALU instructions without packed fp32 (which this library never emits):
+# 256 CUs x 4 SIMDs x 16 lanes per clock x 2.4 GHz (a wave64 instruction
+# occupies its SIMD for 4 clocks), in lane-instructions per second
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 CALIB_BYTES = 256 << 20
 CSRC = "rotated_bit_quantized_rotate_amd/csrc/"
@@ -291,6 +299,9 @@ class Case:
         self.dtype = ""
         self.wl = None            # host workload for the CPU baseline
         self.peak = INT8_MFMA_PEAK_TOPS   # dense matrix peak of the GEMM's instruction
+        # VALU-bound GEMMs (group-64 rescale): algorithmic fp32 VALU lane-
+        # instructions per launch; the roofline is then the VALU's
+        self.valu_ops = 0
         self.bound = "mfma"
         self.cpu_fn = None        # custom CPU baseline (else the linear's oracle on case.wl)
         self.unit = "TOP/s"
@@ -639,6 +650,10 @@ def case_svdq(Q, W, dev, fp6=False):
         (lambda: Q.qgemm_w4a4_lowrank(codes, sa, wq, sw, K, epilogue="swiglu", out=out0)))
     c.ops = wl.int_ops
     c.gemm_launches = 1
+    # the rescale of every output and 64-channel group: convert the int32
+    # partial, form s_a * s_w, fma (3); the FP6 instruction's partial is
+    # already fp32 (2)
+    c.valu_ops = M * N * (K // 64) * (2 if fp6 else 3)
     c.pro_bytes = M * K * 2 + K * r * 2 + M * acols + M * (K // 64) * 4 + M * r * 2
     c.gemm_bytes = (M * acols + N * wcols + M * (K // 64) * 4 + N * (K // 64) * 4 + M * r * 2
                     + r * N * 2 + M * (N // 2) * 2)
@@ -1137,6 +1152,18 @@ def main(argv=None):
                      "timing": "GEMM-only: median of 5 repeats of back-to-back launches, HIP events on the "
                                "launch stream"},
     }
+    if case.valu_ops:
+        # the group-64 rescale bounds these kernels (VALU busy 94 % on INT8 by
+        # the counters): the roofline is the fp32 VALU's issue rate
+        achieved = case.valu_ops / case.gemm_launches / (gemm["ms_per_launch"] * 1e-3) / 1e12
+        rec["roofline"] = {"bound": "alu", "kernel": label,
+                           "achieved": round(achieved, 2), "peak": round(VALU_PEAK_TOPS, 2),
+                           "unit": "T VALU lane-instructions/s", "frac": round(achieved / VALU_PEAK_TOPS, 4),
+                           "valu_ops_per_launch": int(case.valu_ops // case.gemm_launches),
+                           "traffic": traffic,
+                           "algorithmic_bytes": int(case.gemm_bytes // case.gemm_launches),
+                           "timing": rec["roofline"]["timing"],
+                           "mfma_frac": rec["roofline"]["frac"]}
     if case.branch is not None:
         # the low-rank branch's share: the prologue and the GEMM timed again
         # without it (same codes, tiles and epilogue), back to back

@@ -45,6 +45,11 @@
 //    [0, 16) (packed: 8 bytes, one b64 read per MFMA).  Every MFMA starts
 //    from zero, its int32 result is that group's exact partial, and it is
 //    converted and added into an fp32 accumulator with s_a[m,g] * s_w[n,g];
+//    the scales are stored group-major ([K/64][rows]), so a stage's loads of
+//    one group's scales read consecutive rows (whole cache lines);
+//  * the same codes in the FP6 layout with group-64 scales run the
+//    32x32x64 FP6 instruction (64 channels: exactly one group), whose fp32
+//    result is the group's exact partial, rescaled without a conversion;
 //  * SwiGLU: the W tile of a workgroup holds, per wave column, 32 gate rows
 //    f and the 32 matching up rows F + f, so a lane holds gate and up of the
 //    same outputs;
@@ -881,32 +886,7 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
         const uint2 l = *reinterpret_cast<const uint2*>(Ws + w6_lo + j * 16 * C::WRB);
         wf[j] = v8i{(int)h.x, (int)h.y, (int)h.z, (int)h.w, (int)l.x, (int)l.y, 0, 0};  // FP6 reads 6 dwords
       }
-      // Group-64 scales: an instruction spans the stage's two groups (lanes
-      // 0..31 carry channels 0..63, lanes 32..63 channels 64..127), so each
-      // group runs with the other group's W lanes zeroed; its fp32 result is
-      // the group's exact partial, rescaled like the INT8 path's.
-      v8i wg[C::GROUP ? 2 : 1][C::GROUP ? C::FJ : 1];
-      v4f sav6[C::GROUP ? 2 : 1][C::GROUP ? C::FI / 4 : 1];
-      v4f swv6[C::GROUP ? 2 : 1][C::GROUP ? C::FJ : 1];
-      if constexpr (C::GROUP) {
-        const uint8_t* Ss = Ws + C::SW;
-        const bool lo = lane < 32;
-        const v8i z = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int j = 0; j < C::FJ; ++j) {
-          wg[0][j] = lo ? wf[j] : z;
-          wg[1][j] = lo ? z : wf[j];
-        }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-          for (int f = 0; f < C::FI / 4; ++f)
-            sav6[kk][f] = *reinterpret_cast<const v4f*>(Ss + sa_off + (kk * C::BM + 64 * f) * 4);
-#pragma unroll
-          for (int j = 0; j < C::FJ; ++j)
-            swv6[kk][j] = *reinterpret_cast<const v4f*>(Ss + sw_off + (kk * C::BN + j * 16) * 4);
-        }
-      }
+      static_assert(!C::GROUP, "FP6 with group-64 scales runs the 32x32x64 (M32) form");
       constexpr int PF = 2;
       auto read_a = [&](int i) {
         const uint4 h = *reinterpret_cast<const uint4*>(As + a6_hi + i * 16 * C::ARB);
@@ -922,33 +902,13 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
         if (i + PF < C::FI) abuf[(i + PF) % (PF + 1)] = read_a(i + PF);
         if (dma && i < NDMA) issue_one(nxt, kt + NS - 1, i);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (C::GROUP) {
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const float s_i = sav6[kk][i / 4][i % 4];
-            v4f part[C::FJ];
-#pragma unroll
-            for (int j = 0; j < C::FJ; ++j)
-              part[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wg[kk][j], abuf[i % (PF + 1)],
-                                                                         v4f{0.f, 0.f, 0.f, 0.f}, 2, 2, 0, 127,
-                                                                         0, 127);
-#pragma unroll
-            for (int j = 0; j < C::FJ; ++j) {
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                yf[j][i][r] = __builtin_fmaf(part[j][r], s_i * swv6[kk][j][r], yf[j][i][r]);
-              asm volatile("" : "+v"(yf[j][i]));
-            }
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < C::FJ; ++j) {
-            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], abuf[i % (PF + 1)], acc[j][i],
-                                                                        2, 2, 0, 127, 0, 127);
-            // pin the group here: otherwise the compiler sinks every MFMA
-            // below the loads' branches and must hold all A fragments at once
-            asm volatile("" : "+v"(acc[j][i]));
-          }
+        for (int j = 0; j < C::FJ; ++j) {
+          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], abuf[i % (PF + 1)], acc[j][i],
+                                                                      2, 2, 0, 127, 0, 127);
+          // pin the group here: otherwise the compiler sinks every MFMA
+          // below the loads' branches and must hold all A fragments at once
+          asm volatile("" : "+v"(acc[j][i]));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
