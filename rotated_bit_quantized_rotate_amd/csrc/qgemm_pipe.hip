@@ -373,8 +373,11 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
     // packed INT4 weights: rows 2p, 2p + 1 interleaved per 128-channel stage
     // (64 bytes each), so a stage of two rows is one cache line
     const int64_t wr = w_row_of<C, SWIG>(p, n0, rl);
-    w_vo[tw] = WPAIR ? (uint32_t)((wr >> 1) * 2 * ldw + ((wr & 1) << 6) + (ch << 4))
-                     : (uint32_t)(wr * ldw + (ch << 4));
+    // FP6 weights: rows 4q .. 4q + 3 interleaved per 128-channel stage (96
+    // bytes each), so a stage of four rows is three whole cache lines
+    w_vo[tw] = WPAIR  ? (uint32_t)((wr >> 1) * 2 * ldw + ((wr & 1) << 6) + (ch << 4))
+               : C::F6 ? (uint32_t)((wr >> 2) * 4 * ldw + (wr & 3) * 96 + (ch << 4))
+                       : (uint32_t)(wr * ldw + (ch << 4));
   }
   uint32_t s_vo[C::SCL ? C::S_PER_WAVE : 1];
 #pragma unroll
@@ -426,7 +429,8 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
       const int tw = t - C::A_PER_WAVE;
       if (tw < C::W_HI - 1 || w_hi) {
         const int q = wave + C::NW * tw;
-        dma_b128(p.w, w_vo[tw] + (uint32_t)(kt * (WPAIR ? 2 * C::WRB : C::WRB)), st + C::SA + q * 1024);
+        dma_b128(p.w, w_vo[tw] + (uint32_t)(kt * (WPAIR ? 2 * C::WRB : (C::F6 ? 4 * C::WRB : C::WRB))),
+                 st + C::SA + q * 1024);
       }
     } else if (C::MX) {
       const int ts = t - C::A_PER_WAVE - C::W_HI;

@@ -122,6 +122,12 @@ __device__ __forceinline__ void store_codes(void* codes, int64_t off_elems, int 
     const uint32_t nd0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)d0, DPP_QUAD_SWAP1, 0xF, 0xF, false);
     const int64_t c = off_elems & 127;                 // channel within the 128-channel block
     uint8_t* blk = static_cast<uint8_t*>(codes) + (off_elems >> 7) * 96;
+    if (pair_k) {
+      // FP6 weights: rows 4q .. 4q + 3 interleaved per 128-channel slice
+      // (96 bytes each, 384 bytes: three whole cache lines)
+      const int64_t r = off_elems / pair_k, cc = off_elems - r * pair_k;
+      blk = static_cast<uint8_t*>(codes) + (r >> 2) * (pair_k / 128 * 384) + (cc >> 7) * 384 + (r & 3) * 96;
+    }
     const int g = (int)(c >> 5);
     if ((c & 16) == 0) *reinterpret_cast<uint4*>(blk + 16 * g) = make_uint4(d0, d1, d2, nd0);
     else *reinterpret_cast<uint2*>(blk + 64 + 8 * g) = make_uint2(d1, d2);

@@ -51,6 +51,21 @@ def unpair_w4(packed):
     return np.ascontiguousarray(p.reshape(n // 2, h // 64, 2, 64).transpose(0, 2, 1, 3).reshape(n, h))
 
 
+def quad_fp6(codes):
+    """Row-major FP6 weight codes [N, 3K/4] -> the library's FP6 weight order:
+    rows 4q .. 4q + 3 interleaved per 128-channel block (96 bytes each)."""
+    p = np.asarray(codes)
+    n, h = p.shape
+    return np.ascontiguousarray(p.reshape(n // 4, 4, h // 96, 96).transpose(0, 2, 1, 3).reshape(n, h))
+
+
+def unquad_fp6(codes):
+    """Inverse of quad_fp6."""
+    p = np.asarray(codes)
+    n, h = p.shape
+    return np.ascontiguousarray(p.reshape(n // 4, h // 96, 4, 96).transpose(0, 2, 1, 3).reshape(n, h))
+
+
 def to_dev_l2(l2_bits, device="cuda"):
     """The low-rank GEMMs take L2 transposed: bf16 [N, rank] from the
     oracle's [rank, N] bits."""
