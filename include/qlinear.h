@@ -110,12 +110,13 @@ enum {
  *                    the 192-bit little-endian value v_g holding its channel
  *                    i in bits 6i..6i+5; block bytes 16g..16g+15 hold the
  *                    low 16 bytes of v_g and bytes 64+8g..64+8g+7 its high
- *                    8 bytes.  FP6 WEIGHTS (pack_weight_fp6, the w operand
- *                    of the FP6 GEMMs) interleave their rows in fours: for
- *                    every 128-channel block s, the 96-byte blocks of rows
- *                    4q, 4q+1, 4q+2, 4q+3 are adjacent, row 4q+j's at byte
+ *                    8 bytes.  Rows are interleaved in fours: for every
+ *                    128-channel block s, the 96-byte blocks of rows 4q,
+ *                    4q+1, 4q+2, 4q+3 are adjacent, row 4q+j's at byte
  *                    4q * 3K/4 + 384 s + 96 j (three whole cache lines per
- *                    block of four rows).  FP6 activations keep plain rows. */
+ *                    block of four rows); the last R % 4 rows of an R-row
+ *                    matrix keep plain rows (row r's block s at
+ *                    r * 3K/4 + 96 s).  The size stays R * 3K/4 bytes.      */
 enum { QL_LAYOUT_I8 = 0, QL_LAYOUT_PACKED = 1, QL_LAYOUT_FP6 = 2 };
 
 /* ---- MX block formats (OCP Microscaling Formats v1.0) -------------------
@@ -168,7 +169,7 @@ int ql_device_supported(int device);
  *   layout QL_LAYOUT_I8, QL_LAYOUT_PACKED or QL_LAYOUT_FP6 (the last two
  *          only with bits == 4)
  *   rotate 1: rotate each 256-group by H/16 first; 0: quantize x as is
- *   codes  out: [M, K] int8, [M, K/2] packed or [M, 3K/4] FP6 bytes, dense rows
+ *   codes  out: [M, K] int8, [M, K/2] packed or [M, 3K/4] FP6 bytes (QL_LAYOUT_FP6 row order), dense
  *   scales out: float32 [1] | [M] | [K/64, M] (scale = absmax / qmax)
  *   l1, rank, lr  optional SVDQuant down-projection: if l1 != NULL,
  *          lr[M, rank] (bf16, dense rows) = bf16(x[M,K] @ l1[K, rank]) with the
@@ -226,11 +227,10 @@ int pack_weight_int4(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
 
 /* Offline INT4 weight preparation for the FP6 GEMMs (qgemm_w4a4_fp6,
  * qgemm_w4a4_fp6_lowrank): the same codes and scales as pack_weight_int4,
- * stored in QL_LAYOUT_FP6 with the weight rows interleaved in fours (the
- * codes and scales of rotate_quantize_act(w, N, K, ldw, 4, scale_mode,
- * QL_LAYOUT_FP6, rotate, ...), rows in the weight order).  scale_mode
- * TENSOR | ROW | GROUP64.  N must be a multiple of 4 (else QL_ERR_SHAPE).
- *   packed out: [N, 3K/4] bytes in the QL_LAYOUT_FP6 weight order          */
+ * stored in QL_LAYOUT_FP6; equal to rotate_quantize_act(w, N, K, ldw, 4,
+ * scale_mode, QL_LAYOUT_FP6, rotate, ...).  scale_mode TENSOR | ROW |
+ * GROUP64.
+ *   packed out: [N, 3K/4] bytes in the QL_LAYOUT_FP6 order                 */
 int pack_weight_fp6(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
                     int scale_mode, int rotate, uint8_t* packed, float* scales,
                     void* stream);
@@ -266,8 +266,7 @@ int qgemm_w4a4(const void* a, const float* sa, int a_scale_mode, int a_layout,
  * result equals qgemm_w4a4's bit for bit.
  *   a   [M, 3K/4] activation codes in QL_LAYOUT_FP6 (rotate_quantize_act or
  *       rmsnorm_rotate_quantize_act with layout QL_LAYOUT_FP6), dense rows
- *   w   [N, 3K/4] weight codes in the QL_LAYOUT_FP6 weight order (rows in
- *       fours, as pack_weight_fp6 writes them)
+ *   w   [N, 3K/4] weight codes in QL_LAYOUT_FP6 (pack_weight_fp6)
  *   sa, a_scale_mode, sw, w_scale_mode   TENSOR | ROW scales, as qgemm_w4a4,
  *       or GROUP64 on both sides (README "Krea-2-SVDQuant-ComfyUI": INT4 with
  *       group size 64); the 32x32x64 FP6 instruction then covers exactly one

@@ -353,6 +353,10 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   // W-scale positions are in tile-row order.
   const int64_t a_row0 = m0 * lda;
   uint32_t a_vo[C::A_PER_WAVE];
+  // FP6 rows come in fours (rows 4q .. 4q + 3 interleaved per stage, 384
+  // bytes) below M & ~3 and plain after, so a lane's stage advance is 384
+  // or 96 bytes (m0 is a multiple of 4)
+  uint32_t a_adv[C::F6 ? C::A_PER_WAVE : 1];
 #pragma unroll
   for (int t = 0; t < C::A_PER_WAVE; ++t) {
     constexpr int CPR = C::ARB / 16;
@@ -362,6 +366,11 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
     const int64_t gr = m0 + rl > p.M - 1 ? p.M - 1 : m0 + rl;
     const int ch = C::F6 ? swz6(rl, ci % CPR) : swz<C::ARB, C::GROUP, C::MX == 8>(rl, lane % CPR);
     a_vo[t] = (uint32_t)((gr - m0) * lda + (ch << 4));
+    if constexpr (C::F6) {
+      const bool quad = gr < (p.M & ~int64_t(3));
+      if (quad) a_vo[t] = (uint32_t)(((gr - m0) >> 2) * 4 * lda + ((gr - m0) & 3) * 96 + (ch << 4));
+      a_adv[t] = quad ? 4 * C::ARB : C::ARB;
+    }
   }
   uint32_t w_vo[C::W_HI];
 #pragma unroll
@@ -374,7 +383,8 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
     // (64 bytes each), so a stage of two rows is one cache line
     const int64_t wr = w_row_of<C, SWIG>(p, n0, rl);
     // FP6 weights: rows 4q .. 4q + 3 interleaved per 128-channel stage (96
-    // bytes each), so a stage of four rows is three whole cache lines
+    // bytes each), so a stage of four rows is three whole cache lines (the
+    // GEMM's N is a multiple of 16: whole fours only)
     w_vo[tw] = WPAIR  ? (uint32_t)((wr >> 1) * 2 * ldw + ((wr & 1) << 6) + (ch << 4))
                : C::F6 ? (uint32_t)((wr >> 2) * 4 * ldw + (wr & 3) * 96 + (ch << 4))
                        : (uint32_t)(wr * ldw + (ch << 4));
@@ -424,7 +434,8 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   auto issue_one = [&](uint8_t* st, int kt, int t) {
     if (t < C::A_PER_WAVE) {
       const int q = wave + C::NW * t;
-      dma_b128(a_base, a_vo[t] + (uint32_t)(kt * C::ARB), st + q * 1024);
+      if constexpr (C::F6) dma_b128(a_base, a_vo[t] + (uint32_t)kt * a_adv[t], st + q * 1024);
+      else dma_b128(a_base, a_vo[t] + (uint32_t)(kt * C::ARB), st + q * 1024);
     } else if (t < C::A_PER_WAVE + C::W_HI) {
       const int tw = t - C::A_PER_WAVE;
       if (tw < C::W_HI - 1 || w_hi) {

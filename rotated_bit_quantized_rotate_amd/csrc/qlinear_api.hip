@@ -144,13 +144,9 @@ int pack_weight_int4(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, int s
 
 int pack_weight_fp6(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, int scale_mode, int rotate,
                     uint8_t* packed, float* scales, void* stream) {
-  if (N <= 0 || N % 4 != 0) return QL_ERR_SHAPE;  // rows are stored in fours
-  int st = validate_rq(w, N, K, ldw, 4, scale_mode, QL_LAYOUT_FP6, rotate, packed, scales, nullptr, 0, nullptr);
-  if (st != QL_OK) return st;
-  if ((st = check_current_device()) != QL_OK) return st;
-  ql::RqArgs a{w, N, K, ldw, 4, scale_mode, QL_LAYOUT_FP6, rotate, packed, scales};
-  a.paired = 1;
-  return ql::launch_rotate_quantize(a, static_cast<hipStream_t>(stream)) == QL_OK ? QL_OK : QL_ERR_LAUNCH;
+  if (N <= 0) return QL_ERR_SHAPE;
+  return rotate_quantize_act(w, N, K, ldw, 4, scale_mode, QL_LAYOUT_FP6, rotate, packed, scales, nullptr, 0,
+                             nullptr, stream);
 }
 
 // Output element size per epilogue (SWIGLU / BF16 / GATED write bf16).

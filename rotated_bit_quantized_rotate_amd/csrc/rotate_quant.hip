@@ -106,7 +106,7 @@ __device__ __forceinline__ uint32_t fp6_join4(uint32_t p) {
 // slice -- channel c of row r at byte (r / 2) K + 128 (c / 128) + 64 (r % 2)
 // + (c % 128) / 2 (K = pair_k); a lane's 16 channels never cross a slice.
 __device__ __forceinline__ void store_codes(void* codes, int64_t off_elems, int fmt, const uint32_t (&u)[16],
-                                            int64_t pair_k = 0) {
+                                            int64_t pair_k = 0, int64_t rows = 0) {
   if (fmt == 2) {
     // FP6 layout: a row is 96-byte blocks of 128 channels; in a block,
     // 32-channel sub-block g is the 192-bit value v_g (channel i at bits
@@ -122,12 +122,11 @@ __device__ __forceinline__ void store_codes(void* codes, int64_t off_elems, int 
     const uint32_t nd0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)d0, DPP_QUAD_SWAP1, 0xF, 0xF, false);
     const int64_t c = off_elems & 127;                 // channel within the 128-channel block
     uint8_t* blk = static_cast<uint8_t*>(codes) + (off_elems >> 7) * 96;
-    if (pair_k) {
-      // FP6 weights: rows 4q .. 4q + 3 interleaved per 128-channel slice
-      // (96 bytes each, 384 bytes: three whole cache lines)
-      const int64_t r = off_elems / pair_k, cc = off_elems - r * pair_k;
+    // rows 4q .. 4q + 3 interleaved per 128-channel slice (96 bytes each,
+    // 384 bytes: three whole cache lines); the last rows % 4 rows stay plain
+    const int64_t r = off_elems / pair_k, cc = off_elems - r * pair_k;
+    if (r < (rows & ~int64_t(3)))
       blk = static_cast<uint8_t*>(codes) + (r >> 2) * (pair_k / 128 * 384) + (cc >> 7) * 384 + (r & 3) * 96;
-    }
     const int g = (int)(c >> 5);
     if ((c & 16) == 0) *reinterpret_cast<uint4*>(blk + 16 * g) = make_uint4(d0, d1, d2, nd0);
     else *reinterpret_cast<uint2*>(blk + 64 + 8 * g) = make_uint2(d1, d2);
@@ -348,7 +347,8 @@ __global__ __launch_bounds__(kThreads) void rq_kernel(RqArgs a, int slots_per_ro
 #pragma unroll
         for (int e = 0; e < 16; ++e) u[e] = code_bits(v[j][e], inv);
       }
-      store_codes(a.codes, code_row + (int64_t)g * 256 + t * 16, a.packed, u, a.paired ? a.K : 0);
+      store_codes(a.codes, code_row + (int64_t)g * 256 + t * 16, a.packed, u,
+                  (a.paired || a.packed == 2) ? a.K : 0, a.M);
       if (a.mode == 2) {
         if ((t & 3) == 0)
           a.scales[(int64_t)(g * 4 + (t >> 2)) * a.M + row] = __fdiv_rn(am, qmax) * post;  // [K/64, M]

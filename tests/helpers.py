@@ -52,18 +52,25 @@ def unpair_w4(packed):
 
 
 def quad_fp6(codes):
-    """Row-major FP6 weight codes [N, 3K/4] -> the library's FP6 weight order:
-    rows 4q .. 4q + 3 interleaved per 128-channel block (96 bytes each)."""
-    p = np.asarray(codes)
+    """Row-major FP6 codes [R, 3K/4] -> the library's FP6 row order: rows
+    4q .. 4q + 3 interleaved per 128-channel block (96 bytes each) for every
+    whole four of rows; the last R % 4 rows stay plain."""
+    p = np.ascontiguousarray(np.asarray(codes))
     n, h = p.shape
-    return np.ascontiguousarray(p.reshape(n // 4, 4, h // 96, 96).transpose(0, 2, 1, 3).reshape(n, h))
+    n4 = n // 4 * 4
+    out = p.copy()
+    out[:n4] = p[:n4].reshape(n4 // 4, 4, h // 96, 96).transpose(0, 2, 1, 3).reshape(n4, h)
+    return out
 
 
 def unquad_fp6(codes):
     """Inverse of quad_fp6."""
-    p = np.asarray(codes)
+    p = np.ascontiguousarray(np.asarray(codes))
     n, h = p.shape
-    return np.ascontiguousarray(p.reshape(n // 4, h // 96, 4, 96).transpose(0, 2, 1, 3).reshape(n, h))
+    n4 = n // 4 * 4
+    out = p.copy()
+    out[:n4] = p[:n4].reshape(n4 // 4, h // 96, 4, 96).transpose(0, 2, 1, 3).reshape(n4, h)
+    return out
 
 
 def to_dev_l2(l2_bits, device="cuda"):

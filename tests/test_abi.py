@@ -318,25 +318,30 @@ def test_pack_weight_fp6_validation(L):
     assert pw(mode=3) == -4                       # no such scale mode
     assert pw(mode=2) in (-4, -6)                 # group-64 passes validation (no device here)
     assert pw(N=0) == -2
-    assert pw(N=18) == -2                         # weight rows are stored in fours
-    assert pw(N=20) in (-4, -6)
+    assert pw(N=18) in (-4, -6)                   # any row count: full fours interleaved, the rest plain
     assert pw(K=320, ldw=320) == -2
     assert pw(out=NULL) == -1
     assert pw(w=MISALIGNED) == -3
     assert pw() in (-4, -6)
 
 
-def test_fp6_weight_row_order_round_trips():
+@pytest.mark.parametrize("rows", [8, 11, 3, 0])
+def test_fp6_row_order_round_trips(rows):
     from tests.helpers import quad_fp6, unquad_fp6
 
     rng = np.random.default_rng(3)
-    p = rng.integers(0, 256, size=(8, 3 * 96), dtype=np.uint8)
+    p = rng.integers(0, 256, size=(rows, 3 * 96), dtype=np.uint8)
     q = quad_fp6(p)
-    # row 4q + j's block s at 4q * 288 + 384 s + 96 j of the flat buffer
+    assert q.shape == p.shape
+    # row 4q + j < 4 floor(rows / 4): block s at 4q * 288 + 384 s + 96 j of
+    # the flat buffer; the last rows % 4 rows plain at r * 288 + 96 s
     flat = q.reshape(-1)
-    for r in range(8):
+    for r in range(rows):
         for blk in range(3):
-            off = (r // 4) * 4 * 288 + 384 * blk + 96 * (r % 4)
+            if r < rows // 4 * 4:
+                off = (r // 4) * 4 * 288 + 384 * blk + 96 * (r % 4)
+            else:
+                off = r * 288 + 96 * blk
             assert np.array_equal(flat[off:off + 96], p[r, 96 * blk:96 * blk + 96])
     assert np.array_equal(unquad_fp6(q), p)
 

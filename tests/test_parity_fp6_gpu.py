@@ -62,10 +62,10 @@ def test_prologue_fp6_layout(Q, M, K, mode):
     torch.cuda.synchronize()
     assert tuple(c6.shape) == (M, K // 4 * 3)
     codes = c8.cpu().numpy()
-    assert np.array_equal(c6.cpu().numpy(), O.pack_fp6(codes))
+    assert np.array_equal(unquad_fp6(c6.cpu().numpy()), O.pack_fp6(codes))
     assert torch.equal(s6, s8)
     xf = O.bf16_bits_to_f64(xb)
-    P.check_codes(O.unpack_fp6(c6.cpu().numpy()), s6.cpu().numpy(), O.rotate(xf), P.rotation_error_bound(xf),
+    P.check_codes(O.unpack_fp6(unquad_fp6(c6.cpu().numpy())), s6.cpu().numpy(), O.rotate(xf), P.rotation_error_bound(xf),
                   4, mode)
 
 
@@ -87,7 +87,7 @@ def test_prologue_fp6_extreme_codes_and_strides(Q):
         c6, s6, _ = Q.rotate_quantize_act(x, bits=4, scale_mode="row", layout="fp6", rotate=rot)
         torch.cuda.synchronize()
         codes = c8.cpu().numpy()
-        assert np.array_equal(c6.cpu().numpy(), O.pack_fp6(codes))
+        assert np.array_equal(unquad_fp6(c6.cpu().numpy()), O.pack_fp6(codes))
         assert torch.equal(s6, s8)
         if not rot:
             assert set(np.unique(codes[7])) == set(range(-7, 8))
@@ -106,7 +106,7 @@ def test_rmsnorm_prologue_fp6_layout(Q):
     c8, s8 = Q.rmsnorm_rotate_quantize_act(x, g, sc, sh, eps=1e-6, bits=4, layout="i8")
     c6, s6 = Q.rmsnorm_rotate_quantize_act(x, g, sc, sh, eps=1e-6, bits=4, layout="fp6")
     torch.cuda.synchronize()
-    assert np.array_equal(c6.cpu().numpy(), O.pack_fp6(c8.cpu().numpy()))
+    assert np.array_equal(unquad_fp6(c6.cpu().numpy()), O.pack_fp6(c8.cpu().numpy()))
     assert torch.equal(s6, s8)
 
 
@@ -139,7 +139,7 @@ def test_fp6_exact_sum_matches_oracle(Q, M, N, K):
     rng = np.random.default_rng(M * 5 + N + K)
     qa = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
     qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
-    a, w = to_dev(O.pack_fp6(qa)), to_dev(quad_fp6(O.pack_fp6(qw)))
+    a, w = to_dev(quad_fp6(O.pack_fp6(qa))), to_dev(quad_fp6(O.pack_fp6(qw)))
     one_a = torch.ones(M, dtype=torch.float32, device="cuda")
     one_w = torch.ones(N, dtype=torch.float32, device="cuda")
     out = Q.qgemm_w4a4_fp6(a, one_a, w, one_w, K, epilogue="i32")
@@ -159,7 +159,7 @@ def test_fp6_exact_sum_extremes(Q):
     qw[5] = 7
     one_a = torch.ones(M, dtype=torch.float32, device="cuda")
     one_w = torch.ones(N, dtype=torch.float32, device="cuda")
-    out = Q.qgemm_w4a4_fp6(to_dev(O.pack_fp6(qa)), one_a, to_dev(quad_fp6(O.pack_fp6(qw))), one_w, K, epilogue="i32")
+    out = Q.qgemm_w4a4_fp6(to_dev(quad_fp6(O.pack_fp6(qa))), one_a, to_dev(quad_fp6(O.pack_fp6(qw))), one_w, K, epilogue="i32")
     torch.cuda.synchronize()
     want = O.int_gemm(qa, qw)
     assert np.array_equal(out.cpu().numpy().astype(np.int64), want)
@@ -186,7 +186,7 @@ def test_fp6_epilogues_equal_int4_path(Q, M, N, K, mode):
     qa, qw, sa_h, sw_h = _same_codes_pair(M, N, K, M + N, mode)
     sa, sw = to_dev_scales(sa_h), to_dev_scales(sw_h)
     a8, w4 = to_dev(qa), to_dev(pair_w4(O.pack_int4(qw)))
-    a6, w6 = to_dev(O.pack_fp6(qa)), to_dev(quad_fp6(O.pack_fp6(qw)))
+    a6, w6 = to_dev(quad_fp6(O.pack_fp6(qa))), to_dev(quad_fp6(O.pack_fp6(qw)))
     bias = to_dev_bf16(_rand_bf16(M, (N,), 0.1))
     rows = np.unique(np.concatenate([np.arange(4), M - 1 - np.arange(4),
                                      np.random.default_rng(M).choice(M, 40, replace=False)]))
@@ -214,7 +214,7 @@ def test_fp6_strided_output_and_empty(Q):
     M, N, K = 4059, 5104, 512
     qa, qw, sa_h, sw_h = _same_codes_pair(M, N, K, 77, "row")
     sa, sw = to_dev_scales(sa_h), to_dev_scales(sw_h)
-    a6, w6 = to_dev(O.pack_fp6(qa)), to_dev(quad_fp6(O.pack_fp6(qw)))
+    a6, w6 = to_dev(quad_fp6(O.pack_fp6(qa))), to_dev(quad_fp6(O.pack_fp6(qw)))
     big = torch.zeros((M, N + 16), dtype=torch.bfloat16, device="cuda")
     out = Q.qgemm_w4a4_fp6(a6, sa, w6, sw, K, out=big[:, :N])
     ref = Q.qgemm_w4a4(to_dev(qa), sa, to_dev(pair_w4(O.pack_int4(qw))), sw, K)
@@ -249,7 +249,7 @@ def test_fp6_attention_projection_full_size(Q):
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
     rng = np.random.default_rng(9)
     rows = np.unique(np.concatenate([np.arange(4), M - 1 - np.arange(4), rng.choice(M, 24, replace=False)]))
-    qa = O.unpack_fp6(a6[rows].cpu().numpy())
+    qa = O.unpack_fp6(unquad_fp6(a6.cpu().numpy())[rows])
     assert np.array_equal(qa, a8[rows].cpu().numpy())
     qw = O.unpack_int4(unpair_w4(w4.cpu().numpy()))
     assert np.array_equal(acc[rows].cpu().numpy().astype(np.int64), O.int_gemm(qa, qw))
@@ -277,7 +277,7 @@ def test_fp6_group64_equals_int4_path(Q, M, N, K):
     qa, qw, sa_h, sw_h = _group_pair(M, N, K, M + 3 * N + K)
     sa, sw = to_dev_scales(sa_h), to_dev_scales(sw_h)
     a8, w4 = to_dev(qa), to_dev(pair_w4(O.pack_int4(qw)))
-    a6, w6 = to_dev(O.pack_fp6(qa)), to_dev(quad_fp6(O.pack_fp6(qw)))
+    a6, w6 = to_dev(quad_fp6(O.pack_fp6(qa))), to_dev(quad_fp6(O.pack_fp6(qw)))
     bias = to_dev_bf16(_rand_bf16(N, (N,), 0.1))
     for epi in ("bf16", "f32"):
         for bb in (None, bias):
@@ -317,7 +317,7 @@ def test_fp6_group64_lowrank_equals_int4_path(Q, rank, epi):
     lr = to_dev_bf16(_rand_bf16(6, (M, rank), 0.5)) if rank else None
     l2 = to_dev_l2(_rand_bf16(7, (rank, N), 0.05)) if rank else None
     ref = Q.qgemm_w4a4_lowrank(to_dev(qa), sa, to_dev(pair_w4(O.pack_int4(qw))), sw, K, lr=lr, l2=l2, epilogue=epi)
-    got = Q.qgemm_w4a4_fp6_lowrank(to_dev(O.pack_fp6(qa)), sa, to_dev(quad_fp6(O.pack_fp6(qw))), sw, K, lr=lr, l2=l2,
+    got = Q.qgemm_w4a4_fp6_lowrank(to_dev(quad_fp6(O.pack_fp6(qa))), sa, to_dev(quad_fp6(O.pack_fp6(qw))), sw, K, lr=lr, l2=l2,
                                    epilogue=epi)
     torch.cuda.synchronize()
     assert got.shape == ref.shape
@@ -337,7 +337,7 @@ def test_fp6_group64_rejections(Q):
 
     M, N, K = 32, 64, 256
     qa, qw, sa_h, sw_h = _group_pair(M, N, K, 1)
-    a6, w6 = to_dev(O.pack_fp6(qa)), to_dev(quad_fp6(O.pack_fp6(qw)))
+    a6, w6 = to_dev(quad_fp6(O.pack_fp6(qa))), to_dev(quad_fp6(O.pack_fp6(qw)))
     with pytest.raises(Q.QLinearError):   # group sums are rescaled: no exact I32 result
         Q.qgemm_w4a4_fp6(a6, to_dev_scales(sa_h), w6, to_dev_scales(sw_h), K, a_scale_mode="group64",
                          w_scale_mode="group64", epilogue="i32")
@@ -378,7 +378,7 @@ def test_fp6_group64_svdq_gateup_full_size(Q):
     fs = np.sort(rng.choice(N // 2, 192, replace=False))
     ns = np.concatenate([fs, N // 2 + fs])
     ri = torch.as_tensor(rows, device="cuda")
-    qa = O.QuantResult(O.unpack_fp6(a6[ri].cpu().numpy()), sa6[ri].cpu().numpy(), 4, "group64", None)
+    qa = O.QuantResult(O.unpack_fp6(unquad_fp6(a6.cpu().numpy())[rows]), sa6[ri].cpu().numpy(), 4, "group64", None)
     qw = O.QuantResult(O.unpack_fp6(unquad_fp6(w6.cpu().numpy())[ns]), sw6.cpu().numpy()[ns],
                        4, "group64", None)
     y, dy = P.linear_bound(qa, qw, bf16_bits(x[ri]), bf16_bits(l1), np.ascontiguousarray(bf16_bits(l2)[ns].T))
