@@ -970,6 +970,9 @@ def gemm_only_record(case, ops, dev, cold=True):
         rec["pct_int8_peak"] = round(100.0 * ops / (ms * 1e-3) / 1e12 / INT8_MFMA_PEAK_TOPS, 2)
         if case.peak != INT8_MFMA_PEAK_TOPS:
             rec["pct_own_peak"] = round(100.0 * ops / (ms * 1e-3) / 1e12 / case.peak, 2)
+    if case.valu_ops:   # VALU-bound group-64 rescale: fraction of the fp32 VALU issue rate
+        rec["pct_valu_peak"] = round(100.0 * case.valu_ops / case.gemm_launches / (rec["ms_per_launch"] * 1e-3)
+                                     / 1e12 / VALU_PEAK_TOPS, 2)
     if cold and not stack:
         cms = time_cold(fns, dev)
         rec["cold_ms"] = round(cms, 5)
@@ -1092,7 +1095,8 @@ def main(argv=None):
     other = None
     if args.workload == "attn_proj_w4a4" and not args.no_other_gemms:
         other = {}
-        for name in ("ffdown_w8a8", "svdq_gateup", "attn_proj_mxfp4", "svdq_gateup_mxfp4"):
+        for name in ("attn_proj_w4a4_fp6", "ffdown_w8a8", "svdq_gateup", "svdq_gateup_fp6", "attn_proj_mxfp4",
+                     "svdq_gateup_mxfp4"):
             oc = CASES[name](Q, W, dev)
             rec = gemm_only_record(oc, float(oc.ops), dev)
             rec["workload"] = oc.config["workload"]

@@ -247,10 +247,22 @@ struct AccOf { typedef v4i type; };
 template <>
 struct AccOf<true> { typedef v4f type; };
 
-// FP6 stage rows: 6 chunks of 16 bytes; chunk c of row r lives at
-// c ^ ((r >> 3) & 1), so rows r and r + 8 of a fragment read (16
-// consecutive rows at one chunk index) use different 16-byte bank groups.
-__device__ __forceinline__ int swz6(int r, int c) { return c ^ ((r >> 3) & 1); }
+// FP6 stage rows: 6 chunks of 16 bytes (96 bytes: 24 of the 32 4-byte
+// banks).  A b128 fragment read is served 8 lanes at a time, 8 consecutive
+// rows at one chunk index; rows r and r + 4 start on the same bank, so the
+// four low-part chunks 0..3 are XOR-ed with row bits 2..3, which gives the 8
+// rows 8 different 16-byte bank groups.  The high parts (chunks 4, 5, read
+// as b64 by 16 lanes) can only swap whole chunks, by row bit 3; their rows r
+// and r + 4 still share banks (a 2-way conflict the 16-byte loads cannot
+// split).  f depends on r & 15 only, so fragment rows 16 apart agree.
+// The group-64 kernel (M32) keeps the plain row-bit-3 swap of every chunk,
+// which measured 1.5 % faster there (its reads overlap the VALU-heavy
+// rescale); the 16x16x128 kernel gains 3 % from the bits-2..3 form.
+template <bool M32>
+__device__ __forceinline__ int swz6(int r, int c) {
+  if (M32) return c ^ ((r >> 3) & 1);
+  return c < 4 ? c ^ ((r >> 2) & 3) : c ^ ((r >> 3) & 1);
+}
 
 // Chunk position inside an LDS row of RB bytes: chunk c of row r lives at
 // c ^ f(r).  A fragment read (ds_read_b128) has 16 lanes on 16 consecutive
@@ -364,7 +376,7 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
     const int ci = (wave + C::NW * t) * 64 + lane;
     const int rl = C::F6 ? ci / CPR : (wave + C::NW * t) * (1024 / C::ARB) + lane / CPR;
     const int64_t gr = m0 + rl > p.M - 1 ? p.M - 1 : m0 + rl;
-    const int ch = C::F6 ? swz6(rl, ci % CPR) : swz<C::ARB, C::GROUP, C::MX == 8>(rl, lane % CPR);
+    const int ch = C::F6 ? swz6<C::M32>(rl, ci % CPR) : swz<C::ARB, C::GROUP, C::MX == 8>(rl, lane % CPR);
     a_vo[t] = (uint32_t)((gr - m0) * lda + (ch << 4));
     if constexpr (C::F6) {
       const bool quad = gr < (p.M & ~int64_t(3));
@@ -378,7 +390,7 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
     constexpr int CPR = C::WRB / 16;
     const int ci = (wave + C::NW * tw) * 64 + lane;
     const int rl = C::F6 ? ci / CPR : (wave + C::NW * tw) * (1024 / C::WRB) + lane / CPR;
-    const int ch = C::F6 ? swz6(rl, ci % CPR) : swz<C::WRB, C::GROUP, C::MX == 8>(rl, lane % CPR);
+    const int ch = C::F6 ? swz6<C::M32>(rl, ci % CPR) : swz<C::WRB, C::GROUP, C::MX == 8>(rl, lane % CPR);
     // packed INT4 weights: rows 2p, 2p + 1 interleaved per 128-channel stage
     // (64 bytes each), so a stage of two rows is one cache line
     const int64_t wr = w_row_of<C, SWIG>(p, n0, rl);
@@ -523,23 +535,23 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
   }
   // FP6: sub-block lg of a 96-byte row, low 16 bytes at chunk lg, high 8
   // bytes in chunk 4 + lg / 2 (half lg % 2); fragment rows differ by
-  // multiples of 16, which leaves the swizzle bit (row bit 3) unchanged.
-  const int a6_hi = a_row * 96 + (swz6(a_row, lg) << 4);
-  const int a6_lo = a_row * 96 + (swz6(a_row, 4 + (lg >> 1)) << 4) + 8 * (lg & 1);
-  const int w6_hi = w_row * 96 + (swz6(w_row, lg) << 4);
-  const int w6_lo = w_row * 96 + (swz6(w_row, 4 + (lg >> 1)) << 4) + 8 * (lg & 1);
+  // multiples of 16, which leaves the swizzle (row bits 2..3) unchanged.
+  const int a6_hi = a_row * 96 + (swz6<C::M32>(a_row, lg) << 4);
+  const int a6_lo = a_row * 96 + (swz6<C::M32>(a_row, 4 + (lg >> 1)) << 4) + 8 * (lg & 1);
+  const int w6_hi = w_row * 96 + (swz6<C::M32>(w_row, lg) << 4);
+  const int w6_lo = w_row * 96 + (swz6<C::M32>(w_row, 4 + (lg >> 1)) << 4) + 8 * (lg & 1);
   // M32: lane supplies row l32 (+ 32 per fragment) and the 32-channel
   // sub-block 2 kk + lane / 32 of group kk: 16 bytes at that chunk, 8 bytes
-  // in chunk 4 + kk (half lane / 32).  Rows + 32 keep the swizzle bit.
+  // in chunk 4 + kk (half lane / 32).  Rows + 32 keep the swizzle.
   const int l32 = lane & 31, h32 = lane >> 5;
   const int a32_row = wm * C::WM + l32, w32_row = wn * C::WN + l32;
   int a32_hi[2], a32_lo[2], w32_hi[2], w32_lo[2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
-    a32_hi[kk] = a32_row * 96 + (swz6(a32_row, 2 * kk + h32) << 4);
-    a32_lo[kk] = a32_row * 96 + (swz6(a32_row, 4 + kk) << 4) + 8 * h32;
-    w32_hi[kk] = w32_row * 96 + (swz6(w32_row, 2 * kk + h32) << 4);
-    w32_lo[kk] = w32_row * 96 + (swz6(w32_row, 4 + kk) << 4) + 8 * h32;
+    a32_hi[kk] = a32_row * 96 + (swz6<C::M32>(a32_row, 2 * kk + h32) << 4);
+    a32_lo[kk] = a32_row * 96 + (swz6<C::M32>(a32_row, 4 + kk) << 4) + 8 * h32;
+    w32_hi[kk] = w32_row * 96 + (swz6<C::M32>(w32_row, 2 * kk + h32) << 4);
+    w32_lo[kk] = w32_row * 96 + (swz6<C::M32>(w32_row, 4 + kk) << 4) + 8 * h32;
   }
   // M32 scales: the lane's four 32-row fragments' s_a as one b128 at
   // position wm WM + 4 l32; its 16 weight rows' s_w as four b128 at tile
