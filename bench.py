@@ -2,7 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--workload attn_proj_w4a4|attn_proj_w4a4_fp6|ffdown_w8a8|svdq_gateup|
-                                svdq_gateup_fp6|svdq_split_gateup|stack|stack_fused|stack_grouped]
+                                svdq_gateup_fp6|svdq_split_gateup|stack|stack_fp6|stack_fused|
+                                stack_grouped]
 
 Default workload (the headline line): one DiT attention projection at
 1024x1024 -- X bf16 [4096 x 5120] ~ N(0,1) with 1% outlier channels x30,
@@ -19,6 +20,8 @@ Other workloads (separate runs, same JSON shape):
   attn_proj_w4a4_fp6  the headline projection on the FP6 instruction
   stack         the 224 linears of a 28-block DiT at 2048x2048 (16384
                 tokens): 128 W4A4 + 96 W8A8, every activation resident
+  stack_fp6     the stack with its 128 W4A4 layers' INT4 codes in the FP6 layout
+                on the FP6 matrix instruction (same outputs bit for bit)
   stack_fused   the same 224 linears with each block's RMSNorm + modulation
                 fused into its prologues and one prepared activation per
                 shared input and precision (Q|gate int4, K|V int8, gate|up):
@@ -102,6 +105,7 @@ GEMM_KERNELS = {
     "svdq_gateup_fp6": ("qgemm_w4a4_lowrank_fp6", "4096x5120x40960", ["qgemm_pipe.hip"]),
     "stack": ("qgemm_stack", "224x16384", ["qgemm_pipe.hip"]),
     "stack_fused": ("qgemm_stack_fused", "224x16384", ["qgemm_pipe.hip"]),
+    "stack_fp6": ("qgemm_stack_fp6", "224x16384", ["qgemm_pipe.hip"]),
     "stack_grouped": ("qgemm_stack_grouped", "224x16384", ["qgemm_pipe.hip"]),
 }
 
@@ -674,11 +678,13 @@ def case_svdq(Q, W, dev, fp6=False):
     return c
 
 
-def case_stack(Q, W, dev):
+def case_stack(Q, W, dev, fp6=False):
     """224 linears of the 28-block stack at 2048^2.  Activations for every
     layer are drawn on the device (torch generator seeded 2l+1, N(0,1)) and
     kept resident; weights (seeded 2l, N(0,0.02)) are prepared offline and the
-    bf16 copies freed.  One codes buffer and one output buffer are reused."""
+    bf16 copies freed.  One codes buffer and one output buffer are reused.
+    fp6: the 128 W4A4 layers hold the same INT4 codes in the FP6 layout and
+    run on the FP6 matrix instruction (same outputs bit for bit)."""
     import torch
     M = 16384
     layers = W.stack_layers()
@@ -686,6 +692,7 @@ def case_stack(Q, W, dev):
     maxk = max(k for _, _, _, k, _ in layers)
     maxn = max(n for _, _, n, _, _ in layers)
     codes = torch.empty((M * maxk,), dtype=torch.int8, device=dev)
+    codes6 = torch.empty((M * maxk // 4 * 3,), dtype=torch.uint8, device=dev) if fp6 else None
     sa = torch.empty((M,), dtype=torch.float32, device=dev)
     out = torch.empty((M * maxn,), dtype=torch.bfloat16, device=dev)
     c = Case()
@@ -699,7 +706,17 @@ def case_stack(Q, W, dev):
         sw = torch.empty((n,), dtype=torch.float32, device=dev)
         cd = codes[: M * k].view(M, k)
         o = out[: M * n].view(M, n)
-        if bits == 4:
+        if bits == 4 and fp6:
+            wq = torch.empty((n, k // 4 * 3), dtype=torch.uint8, device=dev)
+            c6 = codes6[: M * k // 4 * 3].view(M, k // 4 * 3)
+            prep += _timed_prep(lambda: Q.pack_weight_fp6(w, packed=wq, scales=sw))
+            c.launches.append(("prologue", lambda x=x, c6=c6: Q.rotate_quantize_act(
+                x, bits=4, scale_mode="row", layout="fp6", codes=c6, scales=sa)))
+            c.launches.append(("gemm", lambda c6=c6, wq=wq, sw=sw, o=o, k=k: Q.qgemm_w4a4_fp6(
+                c6, sa, wq, sw, k, out=o)))
+            c.gemm_bytes += (M + n) * k // 4 * 3
+            n4 += 1
+        elif bits == 4:
             wq = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
             prep += _timed_prep(lambda: Q.pack_weight_int4(w, packed=wq, scales=sw))
             c.launches.append(("prologue", lambda x=x, cd=cd: Q.rotate_quantize_act(
@@ -725,11 +742,13 @@ def case_stack(Q, W, dev):
     torch.cuda.synchronize()
     c.prep_ms = prep
     c.metric = ("effective int TOPS + % int8 MFMA peak, mixed 224-linear DiT stack at 2048^2 "
-                "(16384 tokens, 128 W4A4 + 96 W8A8)")
-    c.dtype = "int8 MFMA (int4/int8 codes), int32 accumulate, bf16 out"
+                "(16384 tokens, 128 W4A4 + 96 W8A8)" + (", W4A4 layers on the FP6 instruction" if fp6 else ""))
+    c.dtype = ("FP6 e2m3 MFMA (exact int4 codes) for W4A4, int8 MFMA for W8A8, bf16 out" if fp6 else
+               "int8 MFMA (int4/int8 codes), int32 accumulate, bf16 out")
     c.config = {"workload": "28-block DiT linear stack at 2048^2: 16384 tokens, d=5120, ffn=20480, "
                             f"{len(layers)} linears ({n4} W4A4, {len(layers) - n4} W8A8), per-token / "
-                            "per-row scales, group-256 Hadamard, bf16 out, every activation resident",
+                            "per-row scales, group-256 Hadamard, bf16 out, every activation resident"
+                            + ("; W4A4 codes in the FP6 layout on the FP6 instruction" if fp6 else ""),
                 "M": M, "layers": len(layers), "global_batch": M, "parallelism": "single GPU"}
     return c
 
@@ -885,7 +904,8 @@ CASES = {"attn_proj_w4a4": case_attn, "attn_proj_w4a4_fp6": case_attn_fp6, "svdq
          "svdq_gateup_mxfp4": case_svdq_mx,
          "ffdown_w8a8": case_ffdown, "svdq_gateup": case_svdq,
          "svdq_gateup_fp6": lambda Q, W, dev: case_svdq(Q, W, dev, fp6=True),
-         "stack": case_stack, "stack_fused": case_stack_fused,
+         "stack": case_stack, "stack_fp6": lambda Q, W, dev: case_stack(Q, W, dev, fp6=True),
+         "stack_fused": case_stack_fused,
          "stack_grouped": lambda Q, W, dev: case_stack_fused(Q, W, dev, grouped=True)}
 
 
