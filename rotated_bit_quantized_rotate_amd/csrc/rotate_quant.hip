@@ -105,6 +105,8 @@ __device__ __forceinline__ uint32_t fp6_join4(uint32_t p) {
 // pair_k != 0 (packed weights): rows 2p and 2p + 1 interleaved per 128-channel
 // slice -- channel c of row r at byte (r / 2) K + 128 (c / 128) + 64 (r % 2)
 // + (c % 128) / 2 (K = pair_k); a lane's 16 channels never cross a slice.
+// FP6 (pair_k = K, rows = R): rows in fours per 128-channel block, the last
+// R % 4 rows plain (the QL_LAYOUT_FP6 row order).
 __device__ __forceinline__ void store_codes(void* codes, int64_t off_elems, int fmt, const uint32_t (&u)[16],
                                             int64_t pair_k = 0, int64_t rows = 0) {
   if (fmt == 2) {
@@ -124,9 +126,12 @@ __device__ __forceinline__ void store_codes(void* codes, int64_t off_elems, int 
     uint8_t* blk = static_cast<uint8_t*>(codes) + (off_elems >> 7) * 96;
     // rows 4q .. 4q + 3 interleaved per 128-channel slice (96 bytes each,
     // 384 bytes: three whole cache lines); the last rows % 4 rows stay plain
-    const int64_t r = off_elems / pair_k, cc = off_elems - r * pair_k;
-    if (r < (rows & ~int64_t(3)))
-      blk = static_cast<uint8_t*>(codes) + (r >> 2) * (pair_k / 128 * 384) + (cc >> 7) * 384 + (r & 3) * 96;
+    // (pair_k: the row length K; rows: the matrix's row count)
+    if (pair_k > 0) {
+      const int64_t r = off_elems / pair_k, cc = off_elems - r * pair_k;
+      if (r < (rows & ~int64_t(3)))
+        blk = static_cast<uint8_t*>(codes) + (r >> 2) * (pair_k / 128 * 384) + (cc >> 7) * 384 + (r & 3) * 96;
+    }
     const int g = (int)(c >> 5);
     if ((c & 16) == 0) *reinterpret_cast<uint4*>(blk + 16 * g) = make_uint4(d0, d1, d2, nd0);
     else *reinterpret_cast<uint2*>(blk + 64 + 8 * g) = make_uint2(d1, d2);
