@@ -1180,8 +1180,26 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
       }
     }
     lds_barrier();
+    constexpr int CH = C::BN / 8;  // 8-column chunks per row (16 bf16 bytes out)
+    constexpr int NIT = (2 * HR * CH + C::NT - 1) / C::NT;  // copy-out chunks per thread and round
 #pragma unroll
     for (int band = 0; band < NB / 2; ++band) {
+      // gated residual: the round's residual chunks are loaded before its
+      // bands are staged, so their memory latency passes during the staging
+      // (loaded inside the copy-out, each wave waited for them one at a time)
+      uint4 rres[F32 ? NIT : 1];
+      if constexpr (F32) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          const int c = tid + it * C::NT;
+          const int r = c / CH, ch = c % CH;
+          const int64_t m = m0 + (r < HR ? band * HR + r : C::BM / 2 + band * HR + (r - HR));
+          const int64_t n = n0 + ch * 8;
+          rres[it] = (c < 2 * HR * CH && m < p.M && n < p.N)
+                         ? *reinterpret_cast<const uint4*>(p.residual + m * p.ldo + n)
+                         : make_uint4(0, 0, 0, 0);
+        }
+      }
       // both wave rows stage at once: wave row wm its band wm * NB / 2 + band
       // (fragments i0 .. i0 + FPB - 1) into staging rows wm * HR + ...
       {
@@ -1223,8 +1241,10 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
       lds_barrier();
       // Output rows leave with nontemporal stores: nothing reads them in this
       // kernel, and streaming them past L2 allocation measured 3-4 % faster.
-      constexpr int CH = C::BN / 8;  // 8-column chunks per row (16 bf16 bytes out)
-      for (int c = tid; c < 2 * HR * CH; c += C::NT) {
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int c = tid + it * C::NT;
+        if (c >= 2 * HR * CH) break;
         const int r = c / CH, ch = c % CH;
         const int64_t m = m0 + (r < HR ? band * HR + r : C::BM / 2 + band * HR + (r - HR));
         const int64_t n = n0 + ch * 8;  // 16 | N: a chunk is wholly in or out
@@ -1233,7 +1253,7 @@ __device__ __forceinline__ void pipe_tile(const PArgs& p, int tile_m, int tile_n
         if (F32) {
           const float4 y0 = *reinterpret_cast<const float4*>(row_ptr(r) + ch * 32);
           const float4 y1 = *reinterpret_cast<const float4*>(row_ptr(r) + ch * 32 + 16);
-          const uint4 rr = *reinterpret_cast<const uint4*>(p.residual + m * p.ldo + n);
+          const uint4 rr = rres[F32 ? it : 0];
           const float4 g0 = *reinterpret_cast<const float4*>(sv + C::BM + 2 * C::BN + ch * 8);
           const float4 g1 = *reinterpret_cast<const float4*>(sv + C::BM + 2 * C::BN + ch * 8 + 4);
           const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
