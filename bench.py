@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--workload attn_proj_w4a4|attn_proj_w4a4_fp6|ffdown_w8a8|svdq_gateup|
                                 svdq_gateup_fp6|svdq_split_gateup|stack|stack_fp6|stack_fused|
-                                stack_grouped]
+                                stack_fused_fp6|stack_grouped]
 
 Default workload (the headline line): one DiT attention projection at
 1024x1024 -- X bf16 [4096 x 5120] ~ N(0,1) with 1% outlier channels x30,
@@ -26,6 +26,7 @@ Other workloads (separate runs, same JSON shape):
                 fused into its prologues and one prepared activation per
                 shared input and precision (Q|gate int4, K|V int8, gate|up):
                 5 prologues per block instead of 8
+  stack_fused_fp6  stack_fused with the W4A4 layers on the FP6 instruction
   stack_grouped stack_fused with each block's Q|K|V|gate projections in one
                 grouped launch (sigmoid on the gate; K, V in INT8) and its
                 gate|up projections in another: 4 GEMM launches per block
@@ -106,6 +107,7 @@ GEMM_KERNELS = {
     "stack": ("qgemm_stack", "224x16384", ["qgemm_pipe.hip"]),
     "stack_fused": ("qgemm_stack_fused", "224x16384", ["qgemm_pipe.hip"]),
     "stack_fp6": ("qgemm_stack_fp6", "224x16384", ["qgemm_pipe.hip"]),
+    "stack_fused_fp6": ("qgemm_stack_fused_fp6", "224x16384", ["qgemm_pipe.hip"]),
     "stack_grouped": ("qgemm_stack_grouped", "224x16384", ["qgemm_pipe.hip"]),
 }
 
@@ -753,7 +755,7 @@ def case_stack(Q, W, dev, fp6=False):
     return c
 
 
-def case_stack_fused(Q, W, dev, grouped=False):
+def case_stack_fused(Q, W, dev, grouped=False, fp6=False):
     """The stack's 224 linears (same weights) as a DiT block runs them when
     the block's RMSNorm + modulation live in the quantization prologue and one
     prepared activation serves every projection of the same input (model card
@@ -766,14 +768,18 @@ def case_stack_fused(Q, W, dev, grouped=False):
     seeds 10^7 + 8 b + i).  The attention input is prepared once as int4
     codes (wq, attn_gate) and once as int8 codes (wk, wv); the MLP input once
     (mlp_gate, mlp_up).  grouped: the block's Q|K|V|gate projections run as
-    one grouped launch (sigmoid on the gate) and gate|up as another."""
+    one grouped launch (sigmoid on the gate) and gate|up as another.  fp6:
+    the W4A4 layers' codes in the FP6 layout on the FP6 instruction (same
+    outputs bit for bit; separate launches)."""
     import torch
     M = 16384
     layers = W.stack_layers()
     g = torch.Generator(device=dev)
     maxk = max(k for _, _, _, k, _ in layers)
     maxn = max(n for _, _, n, _, _ in layers)
-    codes = {4: torch.empty((M * maxk,), dtype=torch.int8, device=dev),
+    assert not (fp6 and grouped), "the grouped GEMM takes int8-MFMA operands"
+    codes = {4: torch.empty((M * maxk // 4 * 3 if fp6 else M * maxk,), dtype=torch.uint8 if fp6 else torch.int8,
+                            device=dev),
              8: torch.empty((M * maxk,), dtype=torch.int8, device=dev)}
     sa = {4: torch.empty((M,), dtype=torch.float32, device=dev),
           8: torch.empty((M,), dtype=torch.float32, device=dev)}
@@ -789,12 +795,16 @@ def case_stack_fused(Q, W, dev, grouped=False):
         return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * std + mean).to(torch.bfloat16)
 
     def prologue(x, bits, norm):
-        cd = codes[bits][: M * x.shape[1]].view(M, x.shape[1])
+        f6 = fp6 and bits == 4
+        kc = x.shape[1] // 4 * 3 if f6 else x.shape[1]
+        cd = codes[bits][: M * kc].view(M, kc)
+        lay = "fp6" if f6 else "i8"
         if norm is None:
-            fn = lambda: Q.rotate_quantize_act(x, bits=bits, scale_mode="row", codes=cd, scales=sa[bits])
+            fn = lambda: Q.rotate_quantize_act(x, bits=bits, scale_mode="row", layout=lay, codes=cd,
+                                               scales=sa[bits])
         else:
             fn = lambda: Q.rmsnorm_rotate_quantize_act(x, *norm, eps=1e-6, bits=bits, scale_mode="row",
-                                                       codes=cd, scales=sa[bits])
+                                                       layout=lay, codes=cd, scales=sa[bits])
         c.launches.append(("prologue", fn))
         c.pro_bytes += M * x.shape[1] * 3 + M * 4
 
@@ -815,7 +825,11 @@ def case_stack_fused(Q, W, dev, grouped=False):
             bits = W.stack_precision(b, name)
             w = rnd(2 * li, (n, k), 0.02)
             sw = torch.empty((n,), dtype=torch.float32, device=dev)
-            if bits == 4:
+            if bits == 4 and fp6:
+                wq = torch.empty((n, k // 4 * 3), dtype=torch.uint8, device=dev)
+                prep += _timed_prep(lambda: Q.pack_weight_fp6(w, packed=wq, scales=sw))
+                n4 += 1
+            elif bits == 4:
                 wq = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
                 prep += _timed_prep(lambda: Q.pack_weight_int4(w, packed=wq, scales=sw))
                 n4 += 1
@@ -828,8 +842,15 @@ def case_stack_fused(Q, W, dev, grouped=False):
 
         def gemm(name):
             wq, sw, n, k, bits = lw[name]
-            cd = codes[bits][: M * k].view(M, k)
             o = out[: M * n].view(M, n)
+            if bits == 4 and fp6:
+                c6 = codes[4][: M * k // 4 * 3].view(M, k // 4 * 3)
+                c.launches.append(("gemm", lambda: Q.qgemm_w4a4_fp6(c6, sa[4], wq, sw, k, out=o)))
+                c.ops += 2 * M * n * k
+                c.gemm_bytes += (M + n) * k // 4 * 3 + M * 4 + n * 4 + M * n * 2  # FP6: 3/4 byte per code
+                c.gemm_launches += 1
+                return
+            cd = codes[bits][: M * k].view(M, k)
             if bits == 4:
                 fn = lambda: Q.qgemm_w4a4(cd, sa[4], wq, sw, k, out=o)
                 c.gemm_bytes += n * k // 2
@@ -884,15 +905,19 @@ def case_stack_fused(Q, W, dev, grouped=False):
     c.prep_ms = prep
     c.metric = ("effective int TOPS + % int8 MFMA peak, mixed 224-linear DiT stack at 2048^2 "
                 "(16384 tokens, 128 W4A4 + 96 W8A8), norm fused + prepared activations reused"
-                + (" + grouped Q|K|V|gate and gate|up GEMMs" if grouped else ""))
-    c.dtype = "int8 MFMA (int4/int8 codes), int32 accumulate, bf16 out"
+                + (" + grouped Q|K|V|gate and gate|up GEMMs" if grouped else "")
+                + (", W4A4 layers on the FP6 instruction" if fp6 else ""))
+    c.dtype = ("FP6 e2m3 MFMA (exact int4 codes) for W4A4, int8 MFMA for W8A8, bf16 out" if fp6 else
+               "int8 MFMA (int4/int8 codes), int32 accumulate, bf16 out")
     c.config = {"workload": "28-block DiT linear stack at 2048^2: 16384 tokens, d=5120, ffn=20480, "
                             f"{len(layers)} linears ({n4} W4A4, {len(layers) - n4} W8A8), per-token / "
                             "per-row scales, group-256 Hadamard, bf16 out; RMSNorm + adaLN modulation fused "
                             "into the attention and MLP prologues, one prepared activation per shared input "
                             "and precision (5 prologues per block)"
                             + ("; Q|K|V|gate (sigmoid gate, K/V INT8) and gate|up as grouped launches "
-                               "(4 GEMM launches per block)" if grouped else "") + ", every input resident",
+                               "(4 GEMM launches per block)" if grouped else "")
+                            + ("; W4A4 codes in the FP6 layout on the FP6 instruction" if fp6 else "")
+                            + ", every input resident",
                 "M": M, "layers": len(layers), "prologues": 5 * W.STACK_BLOCKS, "global_batch": M,
                 "parallelism": "single GPU"}
     return c
@@ -906,6 +931,7 @@ CASES = {"attn_proj_w4a4": case_attn, "attn_proj_w4a4_fp6": case_attn_fp6, "svdq
          "svdq_gateup_fp6": lambda Q, W, dev: case_svdq(Q, W, dev, fp6=True),
          "stack": case_stack, "stack_fp6": lambda Q, W, dev: case_stack(Q, W, dev, fp6=True),
          "stack_fused": case_stack_fused,
+         "stack_fused_fp6": lambda Q, W, dev: case_stack_fused(Q, W, dev, fp6=True),
          "stack_grouped": lambda Q, W, dev: case_stack_fused(Q, W, dev, grouped=True)}
 
 
