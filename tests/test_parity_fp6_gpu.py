@@ -256,6 +256,39 @@ def test_fp6_attention_projection_full_size(Q):
     assert bf16_bits(got).shape == (M, N)
 
 
+@pytest.mark.parametrize("N,K", [(6144, 5120), (20480, 5120), (5120, 6144)])
+def test_fp6_stack_shapes_full_size(Q, N, K):
+    """The W4A4 shapes of the 224-linear stack at 16384 tokens (Q / gate,
+    gate|up, wo) as the stack_fp6 workload runs them: the FP6 output equals
+    the INT4 path's bit for bit on the same codes, and the exact sums of
+    sampled rows and columns equal the oracle's integer product."""
+    import torch
+
+    M = 16384
+    torch.manual_seed(N + K)
+    x = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+    w = (torch.randn(N, K, device="cuda") * 0.02).to(torch.bfloat16)
+    a8, sa8, _ = Q.rotate_quantize_act(x, bits=4, scale_mode="row", layout="i8")
+    a6, sa6, _ = Q.rotate_quantize_act(x, bits=4, scale_mode="row", layout="fp6")
+    w4, sw4 = Q.pack_weight_int4(w, scale_mode="row")
+    w6, sw6 = Q.pack_weight_fp6(w, scale_mode="row")
+    ref = Q.qgemm_w4a4(a8, sa8, w4, sw4, K)
+    got = Q.qgemm_w4a4_fp6(a6, sa6, w6, sw6, K)
+    acc = Q.qgemm_w4a4_fp6(a6, sa6, w6, sw6, K, epilogue="i32")
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    rng = np.random.default_rng(N + K)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 10, replace=False)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 254, replace=False)]))
+    qa = O.unpack_fp6(unquad_fp6(a6.cpu().numpy())[rows])
+    assert np.array_equal(qa, a8[rows].cpu().numpy())
+    qw = O.unpack_fp6(unquad_fp6(w6.cpu().numpy())[cols])
+    assert np.array_equal(qw, O.unpack_int4(unpair_w4(w4.cpu().numpy()))[cols])
+    want = O.int_gemm(qa, qw)
+    assert np.array_equal(acc[torch.as_tensor(rows, device="cuda")][:, torch.as_tensor(cols, device="cuda")]
+                          .cpu().numpy().astype(np.int64), want)
+
+
 # ------------------------------------------------------- group-64 GEMM ------
 
 def _group_pair(M, N, K, seed):
