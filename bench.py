@@ -1142,7 +1142,7 @@ def main(argv=None):
     if args.workload == "attn_proj_w4a4" and not args.no_other_gemms:
         other = {}
         for name in ("attn_proj_w4a4_fp6", "ffdown_w8a8", "svdq_gateup", "svdq_gateup_fp6", "attn_proj_mxfp4",
-                     "svdq_gateup_mxfp4"):
+                     "svdq_gateup_mxfp4", "stack", "stack_fp6"):
             oc = CASES[name](Q, W, dev)
             rec = gemm_only_record(oc, float(oc.ops), dev)
             rec["workload"] = oc.config["workload"]
