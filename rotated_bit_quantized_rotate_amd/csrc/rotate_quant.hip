@@ -435,56 +435,120 @@ hipError_t dispatch_rq(const RqArgs& a, const Plan& p, int phase, hipStream_t s)
 // The product is skinny (rank <= 128) and bound by reading X once.  One
 // workgroup per 16 rows; its 8 waves split K into eighths, so a 4096-row X
 // gives 256 workgroups x 8 waves.  bf16 MFMA 16x16x32, fp32 accumulation:
-// the first operand is a 16-rank block of L1^T (each lane gathers 8
-// consecutive k of one L1 column straight from global memory; L1 is small
-// and stays in L2), the second the 16 rows of X (one 16-byte load per lane
-// per 32 channels).  The eight partial sums meet in LDS.
+// the first operand is a 16-rank block of L1^T (8 consecutive k of one L1
+// column per lane), the second the 16 rows of X (one 16-byte load per lane
+// per 32 channels).  A step's 32 L1 rows are one contiguous block of the
+// [K, rank] matrix: the wave loads it with coalesced 16-byte loads into its
+// own LDS slice and reads the columns back as 2-byte values (the four 8-row
+// groups sit 32 bytes apart, so one read's 64 lanes hit 32 distinct banks).
+// X is loaded four steps ahead and L1 two, so the loads of later steps are
+// in flight while a step computes.  The eight partial sums meet in LDS.
 // ---------------------------------------------------------------------------
 constexpr int kLrWaves = 8;
-constexpr int kLrMaxRank = 128;
 
+// 16-byte L1 loads of step st (clamped to the last step): the step's
+// 32 x rank block is contiguous; lane loads chunks lane + 64 i
+template <int NB>
+__device__ __forceinline__ void lr_load_l(v4u (&dst)[NB], const uint8_t* lb, int st, int nit, int lane) {
+  const int ss = st < nit ? st : nit - 1;
+  const uint8_t* b = lb + (int64_t)ss * 64 * (16 * NB);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) dst[i] = *reinterpret_cast<const v4u*>(b + (lane + 64 * i) * 16);
+}
+
+__device__ __forceinline__ v4u lr_load_x(const uint16_t* xp, int st, int nit) {
+  const int ss = st < nit ? st : nit - 1;
+  return *reinterpret_cast<const v4u*>(xp + (int64_t)ss * 32);
+}
+
+// one 32-channel step: L1 chunks (lcur) through the wave's LDS slice into
+// the MFMA's first operand, X fragment (xcur) as the second; lcur and xcur
+// then take the loads of steps st + 2 and st + 4.  The wave's LDS
+// operations run in order: the step's reads follow its writes, and the next
+// step's writes follow these reads.
+template <int NB>
+__device__ __forceinline__ void lr_step(v4u (&lcur)[NB], v4u& xcur, v4f (&acc)[NB], const int (&woff)[NB],
+                                        uint8_t* sl, int rbase, const uint8_t* lb, const uint16_t* xp, int st,
+                                        int nit, int lane) {
+  constexpr int rank = 16 * NB;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) *reinterpret_cast<v4u*>(sl + woff[i]) = lcur[i];
+  lr_load_l<NB>(lcur, lb, st + 2, nit, lane);
+  const v8bf xf = __builtin_bit_cast(v8bf, xcur);
+  xcur = lr_load_x(xp, st + 4, nit);
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const uint16_t* rp = reinterpret_cast<const uint16_t*>(sl + rbase + j * 32);
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)rp[(2 * e) * rank] | ((uint32_t)rp[(2 * e + 1) * rank] << 16);
+    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, make_uint4(w[0], w[1], w[2], w[3])),
+                                                     xf, acc[j], 0, 0, 0);
+  }
+}
+
+// NB = rank / 16
+template <int NB>
 __global__ __launch_bounds__(64 * kLrWaves) void lowrank_down_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, const uint16_t* __restrict__ l1,
-    int rank, uint16_t* __restrict__ lr) {
-  __shared__ float part[kLrWaves][16 * kLrMaxRank];
+    uint16_t* __restrict__ lr) {
+  constexpr int rank = 16 * NB;
+  constexpr int cpr = 2 * NB;                        // 16-byte chunks per L1 row
+  constexpr int kSlice = 32 * rank * 2 + 4 * 32;     // bytes of a wave's L1 block in LDS
+  __shared__ float part[kLrWaves][16 * rank];
+  __shared__ __align__(16) uint8_t slice[kLrWaves][kSlice];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int l16 = lane & 15;
   const int lg = lane >> 4;
-  const int nb = rank >> 4;
   const int64_t m0 = (int64_t)blockIdx.x * 16;
   int64_t arow = m0 + l16;
   if (arow > M - 1) arow = M - 1;
   const int64_t kw = K / kLrWaves;  // multiple of 32 (K is a multiple of 256)
   const int64_t kbeg = wave * kw;
+  const int nit = (int)(kw >> 5);
   const uint16_t* xp = x + arow * ldx + kbeg + lg * 8;
-  const uint16_t* lp = l1 + (kbeg + lg * 8) * rank + l16;
+  const uint8_t* lb = reinterpret_cast<const uint8_t*>(l1 + kbeg * rank);
+  uint8_t* sl = slice[wave];
+  // chunk q = lane + 64 i of a step's block: row q / cpr, chunk q % cpr
+  int woff[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int q = lane + 64 * i;
+    const int k = q / cpr;
+    woff[i] = k * 2 * rank + (k >> 3) * 32 + (q - k * cpr) * 16;
+  }
+  // lane reads rows 8 lg + t (t < 8) at rank 16 j + l16
+  const int rbase = lg * 8 * 2 * rank + lg * 32 + l16 * 2;
 
-  v4f acc[kLrMaxRank / 16];
+  v4f acc[NB];
 #pragma unroll
-  for (int j = 0; j < kLrMaxRank / 16; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  for (int64_t k0 = 0; k0 < kw; k0 += 32) {
-    const v8bf xf = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(xp + k0));
-    const uint16_t* lk = lp + k0 * rank;
-#pragma unroll
-    for (int j = 0; j < kLrMaxRank / 16; ++j) {
-      if (j < nb) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w[e] = (uint32_t)lk[(2 * e) * rank + j * 16] | ((uint32_t)lk[(2 * e + 1) * rank + j * 16] << 16);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(v8bf, make_uint4(w[0], w[1], w[2], w[3])), xf, acc[j], 0, 0, 0);
-      }
-    }
+  for (int j = 0; j < NB; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  v4u x0 = lr_load_x(xp, 0, nit), x1 = lr_load_x(xp, 1, nit), x2 = lr_load_x(xp, 2, nit),
+        x3 = lr_load_x(xp, 3, nit);
+  v4u la[NB], lc[NB];
+  lr_load_l<NB>(la, lb, 0, nit, lane);
+  lr_load_l<NB>(lc, lb, 1, nit, lane);
+  int s0 = 0;
+  for (; s0 + 4 <= nit; s0 += 4) {
+    lr_step<NB>(la, x0, acc, woff, sl, rbase, lb, xp, s0, nit, lane);
+    lr_step<NB>(lc, x1, acc, woff, sl, rbase, lb, xp, s0 + 1, nit, lane);
+    lr_step<NB>(la, x2, acc, woff, sl, rbase, lb, xp, s0 + 2, nit, lane);
+    lr_step<NB>(lc, x3, acc, woff, sl, rbase, lb, xp, s0 + 3, nit, lane);
+  }
+  // last nit % 4 steps: operands loaded in place (the ring's registers would
+  // need a step-dependent choice, which the compiler turns into scratch)
+  for (; s0 < nit; ++s0) {
+    v4u lt[NB];
+    lr_load_l<NB>(lt, lb, s0, nit, lane);
+    v4u xt = lr_load_x(xp, s0, nit);
+    lr_step<NB>(lt, xt, acc, woff, sl, rbase, lb, xp, s0, nit, lane);
   }
   // lane holds ranks 16 j + 4 lg + r of row m0 + l16
 #pragma unroll
-  for (int j = 0; j < kLrMaxRank / 16; ++j)
-    if (j < nb)
-      *reinterpret_cast<v4f*>(&part[wave][l16 * rank + j * 16 + lg * 4]) = acc[j];
+  for (int j = 0; j < NB; ++j) *reinterpret_cast<v4f*>(&part[wave][l16 * rank + j * 16 + lg * 4]) = acc[j];
   __syncthreads();
   for (int o = tid; o < 16 * rank; o += 64 * kLrWaves) {
     float sum = 0.f;
@@ -520,8 +584,15 @@ int launch_lowrank_down(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, co
                         int rank, uint16_t* lr, hipStream_t s) {
   if (M == 0) return OK;
   const unsigned blocks = (unsigned)((M + 15) / 16);
-  hipLaunchKernelGGL(lowrank_down_kernel, dim3(blocks), dim3(64 * kLrWaves), 0, s, x, M, K, ldx, l1, rank,
-                     lr);
+  switch (rank >> 4) {
+#define QL_LR_CASE(nb)                                                                                      \
+  case nb:                                                                                                  \
+    hipLaunchKernelGGL(lowrank_down_kernel<nb>, dim3(blocks), dim3(64 * kLrWaves), 0, s, x, M, K, ldx, l1, lr); \
+    break;
+    QL_LR_CASE(1) QL_LR_CASE(2) QL_LR_CASE(3) QL_LR_CASE(4) QL_LR_CASE(5) QL_LR_CASE(6) QL_LR_CASE(7) QL_LR_CASE(8)
+#undef QL_LR_CASE
+    default: return ERR_LAUNCH;  // the API admits ranks 16..128 in steps of 16 only
+  }
   return hipGetLastError() == hipSuccess ? OK : ERR_LAUNCH;
 }
 
